@@ -1,0 +1,262 @@
+"""CPU oracle for the Sparse-BitNet BitLinear forward.
+
+TEST INFRASTRUCTURE ONLY. This module is the plain, slow, obviously-correct statement of what the
+hot path computes. Only the test suite, the smoke check of the entry module and the benchmark's
+CPU-baseline leg may import it; the product path (the HIP library and its Python binding) never
+does, and it shares no code, table or helper with that path.
+
+Sources (page titles, with the section each step follows):
+  [BitNet-blog]   "Microsoft BitNet 1.58: The Era of 1-Bit Large Language Models",
+                  section "The BitLinear Layer" (five operations; the latent-weight paragraph
+                  after it) and "bitnet.cpp: Matrix-Free Inference" (four ternary values per byte).
+  [BitNet-index]  "BitNet b1.58: How Ternary Weights Cut LLM Memory by 82% Without Losing
+                  Accuracy", section "How ternary quantization works during training".
+  [Sparse-BitNet] "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to Semi-Structured
+                  Sparsity", Abstract (dynamic N:M sparsification jointly with 1.58-bit
+                  quantization), Figure 6 (per-block threshold = the (N+1)-th largest normalized
+                  magnitude, i.e. the N largest of each M-block are kept), Table 6 (N:8 sweep).
+  [8:16]          "From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights with
+                  Variance Correction", abstract / Core claim (8:16 pattern; 0.875 vs 0.75
+                  metadata bits per element).
+
+Readings taken where the pages are silent or disagree (each is also listed in the design notes):
+  * weights are divided by their mean absolute value (the index page says "divided"; the blog's
+    "multiply" would send every code to zero), then rounded to nearest and clamped to [-1, 1];
+  * rounding is round-half-to-even;
+  * the weight scale is one per tensor and is taken over the dense latent weights, before
+    selection (Figure 6 places the thresholds on normalized magnitudes);
+  * the activation scale is per token: absmax with a floor of 1e-5, symmetric 127 levels;
+  * the int8 code sequence is s = fl32(127 / a'), v = fl32(x * s), q = clamp(rne(v), -127, 127);
+  * the N:M groups are M consecutive weights along the reduction axis K of each output row;
+    selection keys on |w|; ties go to the lower index; kept weights that ternarize to 0 still
+    count as kept;
+  * the packed layout ("RPF") puts, per output row, a code bitstream (2n bits per group: the kept
+    codes in ascending position, 2-bit two's complement 00=0, 01=+1, 11=-1, LSB first) and, when
+    n < m, a mask bitstream (m bits per group, bit i <-> position i of the group, LSB first); each
+    stream is padded with zero bits to a whole byte per row;
+  * the output is fp32 y = fl32(fl32(fl32(acc) * gamma) * fl32(a' / 127)).
+
+Floating point follows the precision the path decides integers in (fp32 scale and product); the
+weight-scale sum is accumulated in fp64.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ABSMAX_FLOOR = np.float32(1e-5)
+QMAX = 127
+SUPPORTED_M = (4, 8, 16)
+
+
+# ----------------------------------------------------------------------------------------------
+# Activations: [BitNet-blog] "The BitLinear Layer", operation 2; [BitNet-index] per-token INT8.
+# ----------------------------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact: the bf16 pattern is the top half of the fp32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def act_absmax(x: np.ndarray) -> np.ndarray:
+    """a'_t = max(max_k |x[t, k]|, 1e-5) per token row (fp32; max is exact)."""
+    x = np.asarray(x, dtype=np.float32)
+    assert np.all(np.isfinite(x)), "activations must be finite"
+    if x.shape[1] == 0:
+        return np.full(x.shape[0], ABSMAX_FLOOR, dtype=np.float32)
+    return np.maximum(np.max(np.abs(x), axis=1), ABSMAX_FLOOR).astype(np.float32)
+
+
+def act_scale(a_prime: np.ndarray) -> np.ndarray:
+    """s_t = fl32(127 / a'_t), the correctly rounded fp32 quotient.
+
+    Computed as an fp64 quotient rounded once to fp32; for division that double rounding equals
+    the correctly rounded fp32 result because 53 >= 2*24 + 2.
+    """
+    return (np.float64(QMAX) / np.asarray(a_prime, dtype=np.float64)).astype(np.float32)
+
+
+def quantize_act(x_bf16: np.ndarray):
+    """Per-token absmax INT8 quantization.
+
+    Returns (q int8 [T][K], a_prime fp32 [T]).  v = fl32(x * s) is exact in fp64 before its single
+    rounding (an 8-bit by 24-bit significand product), so it is the fp32 product.
+    """
+    x = bf16_to_f32(x_bf16)
+    a_prime = act_absmax(x)
+    s = act_scale(a_prime)
+    v = (x.astype(np.float64) * s.astype(np.float64)[:, None]).astype(np.float32)
+    q = np.clip(np.rint(v), -QMAX, QMAX).astype(np.int8)
+    return q, a_prime
+
+
+# ----------------------------------------------------------------------------------------------
+# Weights: [BitNet-blog] operation 3 + [BitNet-index] absmean; [Sparse-BitNet] Abstract, Fig. 6.
+# ----------------------------------------------------------------------------------------------
+
+def absmean_gamma(w: np.ndarray) -> np.float32:
+    """gamma = fl32( (sum |w| in fp64) / (n_out * K) ), one scale per tensor over dense weights.
+
+    NumPy's fp64 sum (pairwise) is within ~1e-15 relative of the exact sum.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    assert np.all(np.isfinite(w)), "latent weights must be finite"
+    if w.size == 0:
+        return np.float32(0.0)
+    total = np.sum(np.abs(w.astype(np.float64)), dtype=np.float64)
+    return np.float32(total / np.float64(w.size))
+
+
+def check_pattern(n: int, m: int, k: int) -> None:
+    if m not in SUPPORTED_M:
+        raise ValueError(f"m must be one of {SUPPORTED_M}, got {m}")
+    if not 1 <= n <= m:
+        raise ValueError(f"need 1 <= n <= m, got n={n}, m={m}")
+    if k % m:
+        raise ValueError(f"K={k} is not a multiple of m={m}")
+
+
+def nm_keep_mask(w: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Keep mask (bool [n_out][K]): in each group of m consecutive weights along K, the n with the
+    largest |w|; equal magnitudes are ordered by position (lower index first)."""
+    w = np.asarray(w, dtype=np.float32)
+    n_out, k = w.shape
+    check_pattern(n, m, k)
+    mag = np.abs(w).reshape(n_out, k // m, m)
+    # A stable sort of -|w| lists equal magnitudes in ascending position.
+    order = np.argsort(-mag, axis=2, kind="stable")
+    keep = np.zeros(mag.shape, dtype=bool)
+    np.put_along_axis(keep, order[:, :, :n], True, axis=2)
+    return keep.reshape(n_out, k)
+
+
+def ternary_codes(w: np.ndarray, keep: np.ndarray, gamma: np.float32) -> np.ndarray:
+    """code = keep ? RoundClip(w / gamma, -1, 1) : 0, as int8 in {-1, 0, +1}.
+
+    With round-half-to-even, RoundClip(w / gamma) is nonzero exactly when |w| > gamma / 2, so the
+    code is taken by that exact comparison (gamma / 2 is exact in fp32) instead of a rounded
+    quotient.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    half = np.float32(0.5) * np.float32(gamma)
+    nonzero = np.abs(w) > half
+    return np.where(keep & nonzero, np.sign(w), 0).astype(np.int8)
+
+
+def rpf_row_bytes(n: int, m: int, k: int):
+    """(code bytes per row, mask bytes per row) of the packed layout."""
+    groups = k // m
+    code_bytes = (groups * 2 * n + 7) // 8
+    mask_bytes = (k + 7) // 8 if n < m else 0
+    return code_bytes, mask_bytes
+
+
+def rpf_pack(codes: np.ndarray, keep: np.ndarray, n: int, m: int):
+    """Packed layout: per row a code bitstream and (n < m) a mask bitstream, LSB first.
+
+    [BitNet-blog] "bitnet.cpp" packs four ternary values per byte (2 bits each); the per-group mask
+    is the index metadata.  Returns (code_bytes uint8 [n_out][cb], mask_bytes uint8 [n_out][mb]).
+    """
+    n_out, k = codes.shape
+    check_pattern(n, m, k)
+    groups = k // m
+    kept = codes.reshape(n_out, groups, m)[keep.reshape(n_out, groups, m)]
+    kept = kept.reshape(n_out, groups * n)
+    two_bit = kept.astype(np.int16) & 3  # two's complement: 0 -> 00, +1 -> 01, -1 -> 11
+    bits = np.empty((n_out, groups * n * 2), dtype=np.uint8)
+    bits[:, 0::2] = two_bit & 1
+    bits[:, 1::2] = two_bit >> 1
+    code_bytes = np.packbits(bits, axis=1, bitorder="little")
+    if n < m:
+        mask_bytes = np.packbits(keep.astype(np.uint8), axis=1, bitorder="little")
+    else:
+        mask_bytes = np.zeros((n_out, 0), dtype=np.uint8)
+    cb, mb = rpf_row_bytes(n, m, k)
+    assert code_bytes.shape == (n_out, cb) and mask_bytes.shape == (n_out, mb)
+    return code_bytes, mask_bytes
+
+
+def rpf_unpack(code_bytes: np.ndarray, mask_bytes: np.ndarray, n: int, m: int, k: int):
+    """Inverse of rpf_pack: (codes int8 [n_out][K], keep bool [n_out][K])."""
+    n_out = code_bytes.shape[0]
+    groups = k // m
+    bits = np.unpackbits(code_bytes, axis=1, bitorder="little")[:, : groups * n * 2]
+    two_bit = bits[:, 0::2].astype(np.int8) | (bits[:, 1::2].astype(np.int8) << 1)
+    values = np.where(two_bit == 3, -1, two_bit).astype(np.int8)  # 10 is never written
+    if n < m:
+        keep = np.unpackbits(mask_bytes, axis=1, bitorder="little")[:, :k].astype(bool)
+    else:
+        keep = np.ones((n_out, k), dtype=bool)
+    codes = np.zeros((n_out, k), dtype=np.int8)
+    codes[keep] = values.reshape(-1)
+    return codes, keep
+
+
+def pack_nm_ternary(w: np.ndarray, n: int, m: int) -> dict:
+    """absmean -> keep mask -> codes -> packed bytes, for one latent weight tensor."""
+    gamma = absmean_gamma(w)
+    keep = nm_keep_mask(w, n, m)
+    codes = ternary_codes(w, keep, gamma)
+    code_bytes, mask_bytes = rpf_pack(codes, keep, n, m)
+    return {"gamma": gamma, "keep": keep, "codes": codes,
+            "code_bytes": code_bytes, "mask_bytes": mask_bytes}
+
+
+# ----------------------------------------------------------------------------------------------
+# Matmul and dequantization: [BitNet-blog] operations 4 and 5.
+# ----------------------------------------------------------------------------------------------
+
+def int_matmul(q: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """acc[t, r] = sum_k q[t, k] * code[r, k], exact.
+
+    Every partial sum is an integer of magnitude <= 127 * K < 2^53, so the fp64 matrix product is
+    exact regardless of its blocking order.
+    """
+    acc = np.asarray(q, dtype=np.float64) @ np.asarray(codes, dtype=np.float64).T
+    assert np.all(np.abs(acc) < 2.0**31)
+    return acc.astype(np.int32)
+
+
+def dequantize(acc: np.ndarray, gamma: np.float32, a_prime: np.ndarray) -> np.ndarray:
+    """y[t, r] = fl32( fl32( fl32(acc) * gamma ) * fl32(a'_t / 127) )."""
+    acc_f = np.asarray(acc).astype(np.float32)  # exact: |acc| < 2^24
+    act_step = (np.asarray(a_prime, dtype=np.float32) / np.float32(QMAX)).astype(np.float32)
+    return ((acc_f * np.float32(gamma)).astype(np.float32) * act_step[:, None]).astype(np.float32)
+
+
+def bitlinear_forward(x_bf16: np.ndarray, w: np.ndarray, n: int, m: int) -> dict:
+    """Whole forward: quantize activations, pack weights, integer matmul, dequantize."""
+    q, a_prime = quantize_act(x_bf16)
+    packed = pack_nm_ternary(w, n, m)
+    acc = int_matmul(q, packed["codes"])
+    y = dequantize(acc, packed["gamma"], a_prime)
+    return dict(packed, q=q, a_prime=a_prime, acc=acc, y=y)
+
+
+# ----------------------------------------------------------------------------------------------
+# Metadata size: [8:16] abstract (0.875 vs 0.75 bits/element).
+# ----------------------------------------------------------------------------------------------
+
+def combinatorial_metadata_bits(n: int, m: int) -> float:
+    """Bits per element of the smallest fixed-width index of an n-of-m choice:
+    ceil(log2 C(m, n)) / m."""
+    return math.ceil(math.log2(math.comb(m, n))) / m
+
+
+def boundary_elements_act(x_bf16: np.ndarray, a_prime: np.ndarray, rel: float = 1e-6):
+    """Elements whose exact 127*x/a' lies within ``rel`` (relative) of a k + 0.5 rounding boundary.
+
+    Computed in fp64; used to count (not excuse silently) int8 mismatches near a boundary.
+    """
+    x = bf16_to_f32(x_bf16).astype(np.float64)
+    v = np.abs(x * (QMAX / np.asarray(a_prime, dtype=np.float64))[:, None])
+    frac = v - np.floor(v)
+    return (np.abs(frac - 0.5) <= rel * np.maximum(v, 1e-300)) & (v > 0)
+
+
+def boundary_elements_weight(w: np.ndarray, gamma: np.float32, rel: float = 1e-6):
+    """Weights with ||w| - gamma/2| <= rel * gamma/2 (codes there may legitimately flip)."""
+    half = np.float64(gamma) / 2.0
+    return np.abs(np.abs(np.asarray(w, dtype=np.float64)) - half) <= rel * half

@@ -1,0 +1,454 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU needed).
+
+Each test checks the oracle against something other than itself: the hand-derived worked example,
+the metadata sizes the pages print, a pure-Python brute force, closed-form zero fractions,
+invariants, special cases that reduce to textbook definitions, and symmetries.
+"""
+
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+from scipy import integrate, special
+
+import oracle
+from sparsity_sbn_quantize_amd import inputs
+from tests.conftest import GOLDEN
+
+PATTERNS = [(2, 4), (1, 4), (3, 4), (4, 4), (8, 8), (7, 8), (6, 8), (5, 8), (4, 8), (3, 8),
+            (2, 8), (1, 8), (8, 16), (4, 16), (12, 16), (16, 16), (1, 16)]
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------------------------
+# Worked example (hand-derived from the definitions; fixture carries the citation).
+# ---------------------------------------------------------------------------------------------
+
+def test_worked_example_2of4():
+    g = load("worked_example_2of4.json")
+    exp = g["expected"]
+    w = np.array([g["w"]], dtype=np.float32)
+    x = inputs.f32_to_bf16_bits(np.array([g["x"]], dtype=np.float32))
+    assert np.array_equal(inputs.bf16_bits_to_f32(x)[0], np.array(g["x"], np.float32)), \
+        "example activations must be exact in bf16"
+    r = oracle.bitlinear_forward(x, w, 2, 4)
+    assert r["gamma"] == np.float32(exp["gamma"])
+    assert r["a_prime"][0] == np.float32(exp["a_prime"])
+    assert r["q"][0].tolist() == exp["q"]
+    assert r["keep"][0].astype(int).tolist() == exp["keep_2of4"]
+    assert r["codes"][0].tolist() == exp["codes_2of4"]
+    assert r["code_bytes"][0].tolist() == exp["code_bytes_2of4"]
+    assert r["mask_bytes"][0].tolist() == exp["mask_bytes_2of4"]
+    assert int(r["acc"][0, 0]) == exp["acc_2of4"]
+    assert r["y"][0, 0] == np.float32(exp["y_2of4"])
+
+    d = oracle.bitlinear_forward(x, w, 4, 4)
+    assert d["codes"][0].tolist() == exp["codes_dense"]
+    assert d["code_bytes"][0].tolist() == exp["code_bytes_dense_4of4"]
+    assert d["mask_bytes"].shape == (1, 0)
+    assert int(d["acc"][0, 0]) == exp["acc_dense"]
+    assert d["y"][0, 0] == np.float32(exp["y_dense"])
+
+
+def test_metadata_bits_match_pages():
+    g = load("metadata_bits.json")["bits_per_element"]
+    assert oracle.combinatorial_metadata_bits(2, 4) == g["2:4"]
+    assert oracle.combinatorial_metadata_bits(8, 16) == g["8:16"]
+
+
+# ---------------------------------------------------------------------------------------------
+# Brute force: a pure-Python, loop-by-loop restatement on tiny shapes.
+# ---------------------------------------------------------------------------------------------
+
+def f32(v: float) -> float:
+    """Round a Python float (binary64) to the nearest binary32, ties to even."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def brute_forward(x_vals, w_vals, n, m):
+    """Plain loops over Python floats and ints; no NumPy arithmetic."""
+    T, K, N = len(x_vals), len(x_vals[0]), len(w_vals)
+    floor = f32(1e-5)
+    q, a_primes = [], []
+    for t in range(T):
+        a = 0.0
+        for k in range(K):
+            a = max(a, abs(x_vals[t][k]))
+        a = max(a, floor)
+        s = f32(127.0 / a)
+        row = []
+        for k in range(K):
+            v = f32(x_vals[t][k] * s)
+            r = round(v)  # Python rounds half to even
+            row.append(max(-127, min(127, r)))
+        q.append(row)
+        a_primes.append(a)
+    total = math.fsum(abs(w_vals[r][k]) for r in range(N) for k in range(K))
+    gamma = f32(total / (N * K)) if N * K else 0.0
+    half = f32(0.5 * gamma)
+    codes = [[0] * K for _ in range(N)]
+    keep = [[0] * K for _ in range(N)]
+    for r in range(N):
+        for g0 in range(0, K, m):
+            order = sorted(range(m), key=lambda i: (-abs(w_vals[r][g0 + i]), i))
+            for i in order[:n]:
+                keep[r][g0 + i] = 1
+                wv = w_vals[r][g0 + i]
+                if abs(wv) > half:
+                    codes[r][g0 + i] = 1 if wv > 0 else -1
+    acc = [[0] * N for _ in range(T)]
+    for t in range(T):
+        for r in range(N):
+            s = 0
+            for k in range(K):
+                s += q[t][k] * codes[r][k]
+            acc[t][r] = s
+    y = [[f32(f32(float(acc[t][r]) * gamma) * f32(a_primes[t] / 127.0)) for r in range(N)]
+         for t in range(T)]
+    # packed bytes, bit by bit
+    code_rows, mask_rows = [], []
+    for r in range(N):
+        bits = []
+        for g0 in range(0, K, m):
+            for i in range(m):
+                if keep[r][g0 + i]:
+                    c = codes[r][g0 + i] & 3
+                    bits += [c & 1, c >> 1]
+        code_rows.append(_bits_to_bytes(bits))
+        mask_rows.append(_bits_to_bytes(keep[r]) if n < m else [])
+    return dict(q=q, a_prime=a_primes, gamma=gamma, keep=keep, codes=codes, acc=acc, y=y,
+                code_bytes=code_rows, mask_bytes=mask_rows)
+
+
+def _bits_to_bytes(bits):
+    out = []
+    for b0 in range(0, len(bits), 8):
+        v = 0
+        for i, b in enumerate(bits[b0:b0 + 8]):
+            v |= b << i
+        out.append(v)
+    return out
+
+
+# Values with many exact ties, signed zeros and bf16 half-boundaries.
+_w_atoms = [0.0, -0.0, 0.125, -0.125, 0.25, -0.25, 0.375, 0.5, -0.5, 1.0, -1.0, 0.0625,
+            -0.03125, 2.0, 0.75]
+_x_atoms = [0.0, -0.0, 1.0, -1.0, 0.5, 0.25, -2.0, 1.984375, 0.9765625, 0.0078125, -1.0390625,
+            3.0, -0.75, 127.0, 1e-6]
+
+
+@st.composite
+def tiny_case(draw):
+    n, m = draw(st.sampled_from(PATTERNS))
+    groups = draw(st.integers(1, 4 if m < 16 else 2))
+    K = groups * m
+    T = draw(st.integers(1, 4))
+    N = draw(st.integers(1, 6))
+    wv = st.one_of(st.sampled_from(_w_atoms),
+                   st.floats(-0.125, 0.125, width=32, allow_subnormal=False))
+    xv = st.one_of(st.sampled_from(_x_atoms), st.floats(-8, 8, width=32, allow_subnormal=False))
+    w = np.array(draw(st.lists(st.lists(wv, min_size=K, max_size=K), min_size=N, max_size=N)),
+                 dtype=np.float32)
+    x = np.array(draw(st.lists(st.lists(xv, min_size=K, max_size=K), min_size=T, max_size=T)),
+                 dtype=np.float32)
+    return n, m, w, inputs.f32_to_bf16_bits(x)
+
+
+@settings(max_examples=300, deadline=None)
+@given(tiny_case())
+def test_oracle_matches_brute_force(case):
+    n, m, w, xb = case
+    r = oracle.bitlinear_forward(xb, w, n, m)
+    x_vals = inputs.bf16_bits_to_f32(xb).astype(np.float64).tolist()
+    b = brute_forward(x_vals, w.astype(np.float64).tolist(), n, m)
+    assert r["q"].tolist() == b["q"]
+    assert r["a_prime"].tolist() == b["a_prime"]
+    assert float(r["gamma"]) == b["gamma"]
+    assert r["keep"].astype(int).tolist() == b["keep"]
+    assert r["codes"].tolist() == b["codes"]
+    assert r["code_bytes"].tolist() == b["code_bytes"]
+    assert r["mask_bytes"].tolist() == b["mask_bytes"]
+    assert r["acc"].tolist() == b["acc"]
+    assert r["y"].tolist() == b["y"]
+
+
+def test_brute_force_random_shapes():
+    """Non-square shapes so a transposed operand cannot pass."""
+    rng = np.random.default_rng(7)
+    for (n, m) in [(2, 4), (6, 8), (8, 16), (3, 8)]:
+        T, K, N = 3, 3 * m, 5
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        xb = inputs.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+        r = oracle.bitlinear_forward(xb, w, n, m)
+        b = brute_forward(inputs.bf16_bits_to_f32(xb).astype(np.float64).tolist(),
+                          w.astype(np.float64).tolist(), n, m)
+        assert r["acc"].tolist() == b["acc"]
+        assert r["y"].tolist() == b["y"]
+        assert r["code_bytes"].tolist() == b["code_bytes"]
+
+
+# ---------------------------------------------------------------------------------------------
+# Closed forms: zero fraction of ternarized weights (dense and after n:m selection).
+# ---------------------------------------------------------------------------------------------
+
+def _gauss_abs(sigma):
+    F = lambda u: special.erf(u / (sigma * math.sqrt(2.0)))
+    f = lambda u: 2.0 * math.exp(-0.5 * (u / sigma) ** 2) / (sigma * math.sqrt(2.0 * math.pi))
+    return F, f
+
+
+def _laplace_abs(b):
+    return (lambda u: 1.0 - math.exp(-u / b)), (lambda u: math.exp(-u / b) / b)
+
+
+def masked_zero_fraction(F, f, half, n, m):
+    """1 - P(kept and |w| > half): an element of magnitude u is kept when fewer than n of the
+    other m-1 group members exceed it (continuous law, so no ties)."""
+    def integrand(u):
+        Fu = F(u)
+        return f(u) * sum(math.comb(m - 1, j) * (1 - Fu) ** j * Fu ** (m - 1 - j)
+                          for j in range(n))
+    val, _ = integrate.quad(integrand, half, np.inf, limit=200)
+    return 1.0 - val
+
+
+def test_closed_form_population_values():
+    """The closed forms at the population scale (gamma = E|w|) give the textbook constants."""
+    s = 1.0
+    F, f = _gauss_abs(s)
+    half = s * math.sqrt(2 / math.pi) / 2
+    assert abs(F(half) - special.erf(1 / (2 * math.sqrt(math.pi)))) < 1e-15
+    assert abs(F(half) - 0.310064) < 5e-7
+    Fl, fl = _laplace_abs(1.0)
+    assert abs(Fl(0.5) - (1 - math.exp(-0.5))) < 1e-15
+    assert abs(masked_zero_fraction(F, f, half, 2, 4) - 0.525188) < 5e-6
+    assert abs(masked_zero_fraction(F, f, half, 6, 8) - 0.345973) < 5e-6
+    assert abs(masked_zero_fraction(F, f, half, 8, 16) - 0.502719) < 5e-6
+    assert abs(masked_zero_fraction(Fl, fl, 0.5, 8, 16) - 0.512764) < 5e-6
+    # n = m keeps everything: the masked form reduces to the dense one.
+    assert abs(masked_zero_fraction(F, f, half, 8, 8) - F(half)) < 1e-9
+
+
+@pytest.mark.parametrize("dist,n,m", [("normal", 2, 4), ("normal", 6, 8), ("normal", 8, 16),
+                                      ("normal", 8, 8), ("laplace", 8, 16), ("laplace", 4, 4)])
+def test_zero_fraction_matches_closed_form(dist, n, m):
+    rng = np.random.default_rng(11)
+    N, K = 512, 2048
+    if dist == "normal":
+        sigma = 0.02
+        w = (rng.standard_normal((N, K)) * sigma).astype(np.float32)
+        F, f = _gauss_abs(sigma)
+    else:
+        b = 0.015
+        w = rng.laplace(0, b, (N, K)).astype(np.float32)
+        F, f = _laplace_abs(b)
+    p = oracle.pack_nm_ternary(w, n, m)
+    half = float(p["gamma"]) / 2.0  # realized scale
+    expected = masked_zero_fraction(F, f, half, n, m)
+    per_group = (p["codes"] == 0).reshape(-1, m).mean(axis=1)
+    se = per_group.std(ddof=1) / math.sqrt(per_group.size)
+    assert abs(per_group.mean() - expected) < 5 * se, (per_group.mean(), expected, se)
+
+
+def test_zero_fraction_rowscaled_gaussian():
+    """Per-row scale U(0.5, 2) on N(0, 0.02) with one per-tensor gamma (decode workload)."""
+    w = inputs.latent_weights(inputs.W_DECODE, 0, n_out=1024, k=2560)
+    p = oracle.pack_nm_ternary(w, 8, 8)
+    half = float(p["gamma"]) / 2.0
+    sig = 0.02
+    expected, _ = integrate.quad(
+        lambda s: special.erf(half / (sig * s * math.sqrt(2.0))) / 1.5, 0.5, 2.0)
+    per_row = (p["codes"] == 0).mean(axis=1)
+    se = per_row.std(ddof=1) / math.sqrt(per_row.size)
+    assert abs(per_row.mean() - expected) < 5 * se + 1e-4, (per_row.mean(), expected, se)
+
+
+# ---------------------------------------------------------------------------------------------
+# Invariants.
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_invariants(n, m):
+    rng = np.random.default_rng(n * 100 + m)
+    N, K = 37, 8 * m
+    # quantized magnitudes force many ties
+    w = (rng.integers(-6, 7, (N, K)) * 0.01).astype(np.float32)
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32) * 3)
+    r = oracle.bitlinear_forward(xb, w, n, m)
+    codes, keep = r["codes"], r["keep"]
+    assert set(np.unique(codes)).issubset({-1, 0, 1})
+    g_keep = keep.reshape(N, -1, m)
+    g_codes = codes.reshape(N, -1, m)
+    assert np.all(g_keep.sum(axis=2) == n)
+    assert np.all((g_codes != 0).sum(axis=2) <= n)
+    assert np.all(codes[~keep] == 0)
+    mag = np.abs(w).reshape(N, -1, m)
+    kept_min = np.where(g_keep, mag, np.inf).min(axis=2)
+    pruned_max = np.where(~g_keep, mag, -np.inf).max(axis=2)
+    assert np.all(kept_min >= pruned_max)
+    # ties resolved toward the lower index: no pruned element of equal magnitude precedes a kept one
+    for r_ in range(N):
+        for g in range(K // m):
+            for i in range(m):
+                for j in range(i):
+                    if mag[r_, g, i] == mag[r_, g, j] and g_keep[r_, g, i]:
+                        assert g_keep[r_, g, j]
+    q = r["q"].astype(int)
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    back_codes, back_keep = oracle.rpf_unpack(r["code_bytes"], r["mask_bytes"], n, m, K)
+    assert np.array_equal(back_codes, codes) and np.array_equal(back_keep, keep)
+    cb, mb = oracle.rpf_row_bytes(n, m, K)
+    assert r["code_bytes"].shape == (N, cb) and r["mask_bytes"].shape == (N, mb)
+    assert cb == K * 2 * n // (8 * m) and mb == (K // 8 if n < m else 0)
+
+
+def test_packed_bits_per_weight():
+    """Code + mask bits per weight: (2n + m)/m, or 2 when n = m (no mask)."""
+    for (n, m), bpw in {(2, 4): 2.0, (6, 8): 2.5, (8, 16): 2.0, (8, 8): 2.0, (4, 8): 2.0}.items():
+        cb, mb = oracle.rpf_row_bytes(n, m, 2560)
+        assert (cb + mb) * 8 / 2560 == bpw
+
+
+# ---------------------------------------------------------------------------------------------
+# Special cases that reduce to textbook definitions.
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m", [4, 8, 16])
+def test_dense_reduces_to_roundclip(m):
+    """n = m keeps every weight, so codes = RoundClip(W / gamma, -1, 1) with the quotient taken in
+    fp64 and rounded half-to-even (the BitNet b1.58 definition written directly)."""
+    rng = np.random.default_rng(m)
+    w = (rng.standard_normal((64, 16 * m)) * 0.02).astype(np.float32)
+    w[0, :4] = [0.0, -0.0, 1e-9, -1e-9]
+    p = oracle.pack_nm_ternary(w, m, m)
+    mean_abs = math.fsum(abs(float(v)) for v in w.ravel()) / w.size
+    assert p["gamma"] == np.float32(mean_abs)
+    ref = np.clip(np.rint(w.astype(np.float64) / np.float64(p["gamma"])), -1, 1).astype(np.int8)
+    assert np.array_equal(p["codes"], ref)
+    assert np.all(p["keep"])
+
+
+def test_exact_half_ties_round_to_zero():
+    """|w| == gamma/2 exactly rounds to 0 (half to even), |w| just above rounds to +-1."""
+    w = np.array([[0.5, 0.5, 0.5, 0.5, 1.5, 1.5, 1.5, 1.5]], np.float32)  # gamma = 1, half = 0.5
+    p = oracle.pack_nm_ternary(w, 8, 8)
+    assert p["gamma"] == 1.0
+    assert p["codes"][0].tolist() == [0, 0, 0, 0, 1, 1, 1, 1]
+    w2 = w.copy()
+    w2[0, 0] = np.nextafter(np.float32(0.5), np.float32(1))
+    w2[0, 4] = np.nextafter(np.float32(1.5), np.float32(0))  # keeps sum close; gamma now != 1
+    p2 = oracle.pack_nm_ternary(w2, 8, 8)
+    assert p2["codes"][0, 0] == (1 if w2[0, 0] > p2["gamma"] / 2 else 0)
+
+
+def test_identity_weights():
+    """W = I: dense codes are I, acc = q; 2:4 keeps the diagonal plus the lowest-index zero."""
+    K = 64
+    w = np.eye(K, dtype=np.float32)
+    rng = np.random.default_rng(3)
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((4, K)).astype(np.float32))
+    r = oracle.bitlinear_forward(xb, w, 4, 4)
+    assert np.array_equal(r["codes"], np.eye(K, dtype=np.int8))
+    assert np.array_equal(r["acc"], r["q"].astype(np.int32))
+    assert r["gamma"] == np.float32(1.0 / K)
+    s = oracle.pack_nm_ternary(w, 2, 4)
+    for row in range(K):
+        g0 = row - row % 4
+        kept = np.nonzero(s["keep"][row, g0:g0 + 4])[0].tolist()
+        lowest_zero = min(i for i in range(4) if g0 + i != row)
+        assert kept == sorted({row - g0, lowest_zero})
+
+
+def test_all_equal_weights_sum_rows():
+    """All-equal positive W (dense) gives acc = row sums of q."""
+    w = np.full((8, 32), 0.01, np.float32)
+    rng = np.random.default_rng(4)
+    xb = inputs.f32_to_bf16_bits(rng.standard_normal((3, 32)).astype(np.float32))
+    r = oracle.bitlinear_forward(xb, w, 8, 8)
+    assert np.all(r["codes"] == 1)
+    assert np.array_equal(r["acc"], np.repeat(r["q"].astype(np.int64).sum(1, keepdims=True),
+                                                8, axis=1))
+    # 2:4 on equal weights keeps positions 0, 1 of every group
+    s = oracle.pack_nm_ternary(w, 2, 4)
+    assert np.all(s["keep"].reshape(8, -1, 4)[:, :, :2]) and not s["keep"].reshape(8, -1, 4)[:, :, 2:].any()
+
+
+def test_zero_and_tiny_rows():
+    """An all-zero activation row gives a' = 1e-5 and q = 0; an all-zero W gives gamma = 0 and
+    all codes 0."""
+    x = np.zeros((2, 16), np.float32)
+    x[1, 3] = 1e-30
+    q, a = oracle.quantize_act(inputs.f32_to_bf16_bits(x))
+    assert a[0] == np.float32(1e-5) and np.all(q[0] == 0)
+    assert a[1] == np.float32(1e-5)
+    p = oracle.pack_nm_ternary(np.zeros((4, 16), np.float32), 2, 4)
+    assert p["gamma"] == 0 and np.all(p["codes"] == 0)
+    assert np.all(p["keep"].reshape(4, -1, 4)[:, :, :2])
+
+
+def test_empty_inputs():
+    q, a = oracle.quantize_act(np.zeros((0, 16), np.uint16))
+    assert q.shape == (0, 16) and a.shape == (0,)
+    p = oracle.pack_nm_ternary(np.zeros((0, 16), np.float32), 2, 4)
+    assert p["code_bytes"].shape == (0, 2) and p["mask_bytes"].shape == (0, 2)
+    acc = oracle.int_matmul(np.zeros((0, 16), np.int8), p["codes"])
+    assert acc.shape == (0, 0)
+
+
+def test_pattern_validation():
+    w = np.zeros((2, 12), np.float32)
+    with pytest.raises(ValueError):
+        oracle.nm_keep_mask(w, 2, 8)  # 12 % 8
+    with pytest.raises(ValueError):
+        oracle.nm_keep_mask(w, 0, 4)
+    with pytest.raises(ValueError):
+        oracle.nm_keep_mask(w, 5, 4)
+    with pytest.raises(ValueError):
+        oracle.nm_keep_mask(np.zeros((2, 12), np.float32), 2, 6)
+
+
+# ---------------------------------------------------------------------------------------------
+# Symmetries.
+# ---------------------------------------------------------------------------------------------
+
+def test_symmetries():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((16, 64)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    xb = inputs.f32_to_bf16_bits(x)
+    for n, m in [(2, 4), (6, 8), (8, 16)]:
+        p = oracle.pack_nm_ternary(w, n, m)
+        pn = oracle.pack_nm_ternary(-w, n, m)
+        assert np.array_equal(pn["keep"], p["keep"]) and np.array_equal(pn["codes"], -p["codes"])
+        p4 = oracle.pack_nm_ternary(w * np.float32(4.0), n, m)
+        assert np.array_equal(p4["codes"], p["codes"]) and p4["gamma"] == p["gamma"] * 4
+        # permuting whole groups along K (same permutation for x and w) leaves acc unchanged
+        perm_groups = rng.permutation(64 // m)
+        perm = (perm_groups[:, None] * m + np.arange(m)[None, :]).ravel()
+        r = oracle.bitlinear_forward(xb, w, n, m)
+        rp = oracle.bitlinear_forward(xb[:, perm], w[:, perm], n, m)
+        assert np.array_equal(rp["acc"], r["acc"])
+    q, a = oracle.quantize_act(xb)
+    qn, an = oracle.quantize_act(inputs.f32_to_bf16_bits(-x))
+    assert np.array_equal(qn, -q) and np.array_equal(an, a)
+    q2, a2 = oracle.quantize_act(inputs.f32_to_bf16_bits(x * 8))
+    assert np.array_equal(q2, q) and np.array_equal(a2, a * 8)
+
+
+def test_boundary_counters():
+    x = np.array([[1.984375, 0.9765625, 0.0078125, 0.25]], np.float32)  # s = 64: 62.5, 0.5 ties
+    xb = inputs.f32_to_bf16_bits(x)
+    q, a = oracle.quantize_act(xb)
+    b = oracle.boundary_elements_act(xb, a)
+    assert b[0].tolist() == [False, True, True, False]
+    w = np.array([[0.5, 0.5, 0.5, 0.5, 1.5, 1.5, 1.5, 1.5]], np.float32)
+    assert oracle.boundary_elements_weight(w, np.float32(1.0))[0].tolist() == [True] * 4 + [False] * 4
