@@ -1,0 +1,154 @@
+/*
+ * sbn.h - C ABI of the Sparse-BitNet BitLinear forward for AMD MI355X (gfx950).
+ *
+ * The forward of one BitLinear layer is split into three calls:
+ *   sbn_quantize_act     per-token absmax INT8 activation quantization
+ *   sbn_pack_nm_ternary  per-tensor absmean ternary quantization of fp32 latent weights with a
+ *                        dynamic n:m magnitude keep mask, packed as 2-bit codes + per-group mask
+ *   sbn_bitlinear_fwd    n:m-sparse ternary x INT8 matmul, int32 accumulation, fused dequant
+ * Sources: "Microsoft BitNet 1.58: The Era of 1-Bit Large Language Models", section "The BitLinear
+ * Layer" (the five operations of BitLinear; latent full-precision weights re-quantized on every
+ * forward) and section "bitnet.cpp: Matrix-Free Inference" (four 2-bit ternary values per byte,
+ * integer dot products); "BitNet b1.58: How Ternary Weights Cut LLM Memory by 82% Without Losing
+ * Accuracy", section "How ternary quantization works during training" (weights divided by their
+ * mean absolute value, rounded, clamped to [-1, 1]; INT8 activations with a per-token scale);
+ * "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to Semi-Structured Sparsity", Abstract
+ * (dynamic N:M sparsification applied jointly with 1.58-bit quantization), Figure 6 (the N largest
+ * normalized magnitudes of each M-block are kept) and Table 6 (the N:8 patterns); "From 2:4 to
+ * 8:16 sparsity patterns in LLMs for Outliers and Weights with Variance Correction", abstract
+ * (the 8:16 pattern and its per-group index metadata).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host). Device memory belongs to the caller,
+ *     except the packed-weight handle, which the library owns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue
+ *     work on it; none synchronizes the device (except sbn_free, see there).
+ *   - Arguments are validated on the host before any HIP call; a rejected call touches no GPU
+ *     state and returns a negative sbn_status. sbn_last_error() then holds a message.
+ *   - Shapes: T tokens, K input features (reduction axis), n_out output features. Leading
+ *     dimensions (ld_*) are in elements and must be >= the row length.
+ *   - NaN or Inf inputs give unspecified (but memory-safe) results.
+ *   - The handle's device must be the current device for every call that uses it.
+ */
+#ifndef SBN_H
+#define SBN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SBN_OK = 0,
+  SBN_ERR_INVALID_ARG = -1, /* null pointer, bad size, leading dimension or enum value */
+  SBN_ERR_UNSUPPORTED = -2, /* pattern or size outside what the kernels implement */
+  SBN_ERR_SHAPE = -3,       /* re-pack into a handle of another shape or pattern */
+  SBN_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  SBN_ERR_OOM = -5          /* device allocation failed */
+} sbn_status;
+
+typedef enum {
+  SBN_OUT_F32 = 0,    /* y fp32 = fl32(fl32(fl32(acc) * gamma) * fl32(a'_t / 127)) */
+  SBN_OUT_I32_ACC = 1 /* y int32 = acc, the raw integer accumulator */
+} sbn_out_kind;
+
+/* Opaque packed ternary weight, owned by the library. */
+typedef struct sbn_packed sbn_packed;
+
+/* Upper bound on K: keeps every accumulator |acc| <= 127*K below 2^24, so fl32(acc) is exact. */
+#define SBN_MAX_K (1 << 17)
+
+/*
+ * Per-token absmax INT8 activation quantization ("The BitLinear Layer", operation 2; per-token
+ * scale in "How ternary quantization works during training").
+ *   x_bf16    [T][ld_x] bf16 bit patterns (uint16), read only.
+ *   x_q       [T][ld_q] int8 out: q = clamp(rne(fl32(x * s_t)), -127, 127),
+ *             s_t = fl32(127 / a'_t) (correctly rounded fp32 division).
+ *   x_absmax  [T] fp32 out: a'_t = max(max_k |x[t,k]|, 1e-5), the scale kept for dequantization.
+ * Requires T >= 0, 1 <= K <= SBN_MAX_K, ld_x >= K, ld_q >= K; T == 0 is a no-op.
+ * Columns K..ld-1 of x_q are not written.
+ */
+sbn_status sbn_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K, int64_t ld_x,
+                            int8_t* x_q, int64_t ld_q, float* x_absmax, void* stream);
+
+/*
+ * Absmean ternary quantization with a dynamic n:m keep mask, packed ("The BitLinear Layer",
+ * operation 3, with the divide reading of "How ternary quantization works during training";
+ * Sparse-BitNet Abstract and Figure 6).
+ *   w_latent  [n_out][ld_w] fp32 latent weights (nn.Linear layout), read only.
+ *   gamma = fl32( sum|w| (fp64) / (n_out*K) ), one scale per tensor over the dense weights.
+ *   keep: in each group of m consecutive weights along K of a row, the n largest |w|, equal
+ *         magnitudes going to the lower position.
+ *   code  = keep ? (|w| > gamma/2 ? sign(w) : 0) : 0   (= RoundClip(w/gamma, -1, 1), ties to even)
+ *   *handle == NULL: a handle is allocated (hipMalloc; the only allocation the library makes)
+ *   and returned in *handle (host). Otherwise the existing handle is re-packed in place, with no
+ *   allocation; it must have been made with the same n_out, K, n_keep, m_group (else
+ *   SBN_ERR_SHAPE). Every call recomputes gamma and the mask from the current weights.
+ * Requires m_group in {4, 8, 16}, 1 <= n_keep <= m_group, K % m_group == 0,
+ * m_group <= K <= SBN_MAX_K, 0 <= n_out < 2^31, ld_w >= K.
+ */
+sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
+                               int n_keep, int m_group, sbn_packed** handle /* host */,
+                               void* stream);
+
+/*
+ * n:m-sparse ternary x INT8 matmul with int32 accumulation and fused dequantization
+ * ("The BitLinear Layer", operations 4 and 5).
+ *   x_q       [T][ld_q] int8 (from sbn_quantize_act), x_absmax [T] fp32 (a'_t).
+ *   acc[t][r] = sum_k x_q[t][k] * code[r][k]   (exact int32)
+ *   y         [T][ld_y] fp32 (SBN_OUT_F32) or int32 (SBN_OUT_I32_ACC); x_absmax may be NULL
+ *             for SBN_OUT_I32_ACC.
+ * Requires T >= 0, ld_q >= K, ld_y >= n_out; T == 0 is a no-op.
+ */
+sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_q,
+                             const float* x_absmax, int64_t T, void* y, int64_t ld_y,
+                             sbn_out_kind out_kind, void* stream);
+
+/*
+ * Releases a handle: waits for the last stream that used it, then frees its device memory.
+ * sbn_free(NULL) is a no-op.
+ */
+void sbn_free(sbn_packed* handle);
+
+/*
+ * Canonical export of a handle, for tests and checkpoints (enqueued on `stream`):
+ *   codes     [n_out][K] int8 in {-1, 0, +1} (0 where pruned), or NULL to skip
+ *   keep_mask [n_out][K] uint8 in {0, 1}, or NULL to skip
+ *   gamma     [1] fp32, or NULL to skip
+ */
+sbn_status sbn_packed_export(const sbn_packed* w, int8_t* codes, uint8_t* keep_mask, float* gamma,
+                             void* stream);
+
+/*
+ * Export of the packed bytes in the reference packed format (RPF): per row, a code bitstream
+ * (group g's n kept codes, ascending position, at bits [2n*g, 2n*(g+1)); 2-bit two's complement
+ * 00 = 0, 01 = +1, 11 = -1; LSB first) padded to code_row_bytes = ceil(K/m*2n/8), and, when
+ * n < m, a mask bitstream (bit i of group g <-> position g*m + i) of mask_row_bytes = ceil(K/8).
+ *   code_bytes [n_out][code_row_bytes] uint8, mask_bytes [n_out][mask_row_bytes] uint8
+ *   (mask_bytes may be NULL when n == m). Either may be NULL to skip it.
+ */
+sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8_t* mask_bytes,
+                                 void* stream);
+
+typedef struct {
+  int64_t n_out, K;
+  int n, m;
+  size_t code_row_bytes, mask_row_bytes; /* RPF row sizes */
+  size_t rpf_bytes;                      /* n_out * (code_row_bytes + mask_row_bytes) */
+  size_t packed_bytes;                   /* bytes the forward kernels stream (kernel layout) */
+  size_t device_bytes;                   /* all device memory the handle holds */
+} sbn_packed_desc;
+
+/* Describes a handle; `out` is a host pointer. */
+sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out /* host */);
+
+/* The message of the last failed call on this host thread ("" if none). */
+const char* sbn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBN_H */

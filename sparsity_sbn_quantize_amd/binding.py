@@ -1,0 +1,195 @@
+"""Thin Python binding of libsbn (ctypes): argument marshalling only.
+
+Every step of the forward runs in the HIP kernels behind the C ABI declared in include/sbn.h;
+PyTorch supplies device memory and the current stream. There is no CPU fallback: if the built
+library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsbn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "sbn.h")
+
+SBN_OUT_F32 = 0
+SBN_OUT_I32_ACC = 1
+STATUS = {0: "SBN_OK", -1: "SBN_ERR_INVALID_ARG", -2: "SBN_ERR_UNSUPPORTED", -3: "SBN_ERR_SHAPE",
+          -4: "SBN_ERR_HIP", -5: "SBN_ERR_OOM"}
+
+
+class SbnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class PackedDesc(ctypes.Structure):
+    _fields_ = [("n_out", ctypes.c_int64), ("K", ctypes.c_int64), ("n", ctypes.c_int),
+                ("m", ctypes.c_int), ("code_row_bytes", ctypes.c_size_t),
+                ("mask_row_bytes", ctypes.c_size_t), ("rpf_bytes", ctypes.c_size_t),
+                ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "sbn_quantize_act": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
+    "sbn_pack_nm_ternary": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_void_p), _P]),
+    "sbn_bitlinear_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _P]),
+    "sbn_free": (None, [_P]),
+    "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
+    "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
+    "sbn_last_error": (ctypes.c_char_p, []),
+}
+
+
+def header_symbols() -> list:
+    """Function names declared in include/sbn.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sbn_\w+)\s*\(", text, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libsbn.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def last_error() -> str:
+    return (lib().sbn_last_error() or b"").decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise SbnError(status, last_error())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+def quantize_act(x, out_q=None, out_absmax=None, stream=None):
+    """x: bf16 (or int16 bit patterns) [T][K] on the device -> (q int8 [T][K], a' fp32 [T])."""
+    import torch
+    _require_cuda(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("x must be bfloat16 (or int16 bf16 bit patterns)")
+    T, K = x.shape
+    q = out_q if out_q is not None else torch.empty((T, K), dtype=torch.int8, device=x.device)
+    a = out_absmax if out_absmax is not None else torch.empty((T,), dtype=torch.float32,
+                                                              device=x.device)
+    check(lib().sbn_quantize_act(_ptr(x), T, K, x.stride(0), _ptr(q), q.stride(0), _ptr(a),
+                                 _stream(stream)))
+    return q, a
+
+
+class PackedWeight:
+    """A packed n:m ternary weight (library-owned device memory)."""
+
+    def __init__(self, w, n: int, m: int, stream=None):
+        self._h = ctypes.c_void_p(0)
+        self.n, self.m = n, m
+        self.pack(w, stream)
+
+    def pack(self, w, stream=None):
+        """(Re-)packs from fp32 latent weights [n_out][K]; re-packing reuses the handle."""
+        import torch
+        _require_cuda(w, "w")
+        if w.dtype != torch.float32:
+            raise ValueError("w must be float32")
+        n_out, K = w.shape
+        check(lib().sbn_pack_nm_ternary(_ptr(w), n_out, K, w.stride(0), self.n, self.m,
+                                        ctypes.byref(self._h), _stream(stream)))
+        self.n_out, self.K = n_out, K
+        return self
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("handle was freed")
+        return self._h
+
+    def query(self) -> PackedDesc:
+        d = PackedDesc()
+        check(lib().sbn_packed_query(self.handle, ctypes.byref(d)))
+        return d
+
+    def export(self, stream=None):
+        """(codes int8 [n_out][K], keep uint8 [n_out][K], gamma fp32 [1]) on the device."""
+        import torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        codes = torch.empty((self.n_out, self.K), dtype=torch.int8, device=dev)
+        keep = torch.empty((self.n_out, self.K), dtype=torch.uint8, device=dev)
+        gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+        check(lib().sbn_packed_export(self.handle, _ptr(codes), _ptr(keep), _ptr(gamma),
+                                      _stream(stream)))
+        return codes, keep, gamma
+
+    def export_rpf(self, stream=None):
+        """(code_bytes uint8 [n_out][cb], mask_bytes uint8 [n_out][mb]) on the device."""
+        import torch
+        d = self.query()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        cb = torch.zeros((self.n_out, d.code_row_bytes), dtype=torch.uint8, device=dev)
+        mb = torch.zeros((self.n_out, d.mask_row_bytes), dtype=torch.uint8, device=dev)
+        check(lib().sbn_packed_export_rpf(self.handle, _ptr(cb),
+                                          _ptr(mb) if d.mask_row_bytes else ctypes.c_void_p(0),
+                                          _stream(stream)))
+        return cb, mb
+
+    def free(self):
+        if self._h:
+            lib().sbn_free(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def bitlinear(x_q, x_absmax, w: PackedWeight, out: str = "f32", y=None, stream=None):
+    """y [T][n_out] = dequant(x_q @ codes^T); out="i32" returns the raw int32 accumulators."""
+    import torch
+    _require_cuda(x_q, "x_q")
+    T = x_q.shape[0]
+    kind = SBN_OUT_F32 if out == "f32" else SBN_OUT_I32_ACC
+    if y is None:
+        y = torch.empty((T, w.n_out), dtype=torch.float32 if kind == SBN_OUT_F32 else torch.int32,
+                        device=x_q.device)
+    check(lib().sbn_bitlinear_fwd(w.handle, _ptr(x_q), x_q.stride(0), _ptr(x_absmax), T,
+                                  _ptr(y), y.stride(0), kind, _stream(stream)))
+    return y

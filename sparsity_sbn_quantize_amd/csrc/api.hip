@@ -1,0 +1,211 @@
+// C ABI of libsbn: argument validation, handle lifecycle and dispatch. Every argument check
+// happens before the first HIP call, so a rejected call leaves the GPU untouched.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "sbn_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sbn_status fail(sbn_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+sbn_status hip_fail(hipError_t e, const char* what) {
+  return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool pattern_ok(int n, int m) { return (m == 4 || m == 8 || m == 16) && n >= 1 && n <= m; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sbn_last_error(void) { return g_last_error; }
+
+sbn_status sbn_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K, int64_t ld_x,
+                            int8_t* x_q, int64_t ld_q, float* x_absmax, void* stream) {
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "sbn_quantize_act: T=%lld < 0", (long long)T);
+  if (K < 1 || K > SBN_MAX_K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_quantize_act: K=%lld outside [1, %d]", (long long)K,
+                SBN_MAX_K);
+  if (ld_x < K || ld_q < K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_quantize_act: ld_x=%lld / ld_q=%lld < K=%lld",
+                (long long)ld_x, (long long)ld_q, (long long)K);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_quantize_act: T too large");
+  if (T == 0) return SBN_OK;
+  if (!x_bf16 || !x_q || !x_absmax)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_quantize_act: null pointer");
+  hipError_t e = sbn::launch_quantize_act(x_bf16, T, K, ld_x, x_q, ld_q, x_absmax,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_quantize_act launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
+                               int n_keep, int m_group, sbn_packed** handle, void* stream) {
+  if (!handle) return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: handle is null");
+  if (!pattern_ok(n_keep, m_group))
+    return fail(SBN_ERR_UNSUPPORTED,
+                "sbn_pack_nm_ternary: pattern %d:%d (need m in {4,8,16}, 1 <= n <= m)", n_keep,
+                m_group);
+  if (K < m_group || K > SBN_MAX_K || K % m_group != 0)
+    return fail(SBN_ERR_INVALID_ARG,
+                "sbn_pack_nm_ternary: K=%lld must be a multiple of m=%d in [m, %d]",
+                (long long)K, m_group, SBN_MAX_K);
+  if (n_out < 0 || n_out > INT32_MAX)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: n_out=%lld outside [0, 2^31)",
+                (long long)n_out);
+  if (ld_w < K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: ld_w=%lld < K=%lld", (long long)ld_w,
+                (long long)K);
+  if (!w_latent && n_out > 0) return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: w is null");
+
+  sbn_packed* h = *handle;
+  hipStream_t s = (hipStream_t)stream;
+  if (h) {
+    if (h->L.n_out != n_out || h->L.K != K || h->L.n != n_keep || h->L.m != m_group)
+      return fail(SBN_ERR_SHAPE,
+                  "sbn_pack_nm_ternary: handle is %lldx%lld %d:%d, call asks %lldx%lld %d:%d",
+                  (long long)h->L.n_out, (long long)h->L.K, h->L.n, h->L.m, (long long)n_out,
+                  (long long)K, n_keep, m_group);
+  } else {
+    sbn::Layout L;
+    L.n_out = n_out;
+    L.K = K;
+    L.n = n_keep;
+    L.m = m_group;
+    L.code_brick_bytes = 16 * n_keep / m_group;
+    L.has_mask = n_keep < m_group ? 1 : 0;
+    L.row_blocks = (n_out + 15) / 16;
+    L.quads = ((K + sbn::kBrickK - 1) / sbn::kBrickK + 3) / 4;
+    if (16 * n_keep % m_group != 0)
+      return fail(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: pattern %d:%d", n_keep, m_group);
+    const size_t slots = (size_t)L.row_blocks * (size_t)L.quads * 64;
+    const int num_partials = sbn::absmean_blocks(n_out);
+    const size_t mask_bytes = L.has_mask ? slots * 8 : 0;
+    const size_t code_bytes = slots * (size_t)L.code_brick_bytes;
+    size_t off = 0;
+    const size_t off_mask = off;
+    off = align_up(off + mask_bytes, 256);
+    const size_t off_codes = off;
+    off = align_up(off + code_bytes, 256);
+    const size_t off_gamma = off;
+    off = align_up(off + sizeof(float), 256);
+    const size_t off_part = off;
+    off = align_up(off + sizeof(double) * num_partials, 256);
+
+    h = new (std::nothrow) sbn_packed;
+    if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
+    h->L = L;
+    h->code_row_bytes = (size_t)((K / m_group) * 2 * n_keep + 7) / 8;
+    h->mask_row_bytes = L.has_mask ? (size_t)(K + 7) / 8 : 0;
+    h->mask_plane_bytes = mask_bytes;
+    h->code_plane_bytes = code_bytes;
+    h->num_partials = num_partials;
+    h->base_bytes = off;
+    h->last_stream = s;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+      delete h;
+      return hip_fail(e, "sbn_pack_nm_ternary: hipGetDevice");
+    }
+    e = hipMalloc(&h->base, h->base_bytes);
+    if (e != hipSuccess) {
+      delete h;
+      (void)hipGetLastError();
+      return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: hipMalloc(%zu) failed", off);
+    }
+    // Padding bricks are never written by the pack kernel and must read as zero.
+    e = hipMemsetAsync(h->base, 0, h->base_bytes, s);
+    if (e != hipSuccess) {
+      (void)hipFree(h->base);
+      delete h;
+      return hip_fail(e, "sbn_pack_nm_ternary: hipMemsetAsync");
+    }
+    h->mask = L.has_mask ? h->base + off_mask : nullptr;
+    h->codes = h->base + off_codes;
+    h->gamma = reinterpret_cast<float*>(h->base + off_gamma);
+    h->partials = reinterpret_cast<double*>(h->base + off_part);
+    *handle = h;
+  }
+  h->last_stream = s;
+  hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
+  if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_q,
+                             const float* x_absmax, int64_t T, void* y, int64_t ld_y,
+                             sbn_out_kind out_kind, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: handle is null");
+  if (out_kind != SBN_OUT_F32 && out_kind != SBN_OUT_I32_ACC)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: out_kind=%d", (int)out_kind);
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: T=%lld < 0", (long long)T);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd: T too large");
+  if (ld_q < w->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: ld_q=%lld < K=%lld", (long long)ld_q,
+                (long long)w->L.K);
+  if (ld_y < w->L.n_out)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: ld_y=%lld < n_out=%lld",
+                (long long)ld_y, (long long)w->L.n_out);
+  if (T == 0) return SBN_OK;
+  if (!x_q || !y || (out_kind == SBN_OUT_F32 && !x_absmax))
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: null pointer");
+  const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
+  hipError_t e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd launch");
+  return SBN_OK;
+}
+
+void sbn_free(sbn_packed* handle) {
+  if (!handle) return;
+  (void)hipStreamSynchronize(handle->last_stream);
+  (void)hipFree(handle->base);
+  delete handle;
+}
+
+sbn_status sbn_packed_export(const sbn_packed* w, int8_t* codes, uint8_t* keep_mask, float* gamma,
+                             void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export: handle is null");
+  hipError_t e = sbn::launch_export(w, codes, keep_mask, gamma, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_export launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8_t* mask_bytes,
+                                 void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_rpf: handle is null");
+  hipError_t e = sbn::launch_export_rpf(w, code_bytes, mask_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_export_rpf launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
+  if (!w || !out) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_query: null pointer");
+  out->n_out = w->L.n_out;
+  out->K = w->L.K;
+  out->n = w->L.n;
+  out->m = w->L.m;
+  out->code_row_bytes = w->code_row_bytes;
+  out->mask_row_bytes = w->mask_row_bytes;
+  out->rpf_bytes = (size_t)w->L.n_out * (w->code_row_bytes + w->mask_row_bytes);
+  out->packed_bytes = w->mask_plane_bytes + w->code_plane_bytes;
+  out->device_bytes = w->base_bytes;
+  return SBN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// Per-token absmax INT8 activation quantization.
+//
+// "Microsoft BitNet 1.58: The Era of 1-Bit Large Language Models", section "The BitLinear
+// Layer", operation 2 (BF16 -> INT8 by absmax scaling, scale kept for dequantization); "BitNet
+// b1.58: How Ternary Weights Cut LLM Memory by 82% Without Losing Accuracy", section "How ternary
+// quantization works during training" (per-token scale).
+//
+//   a'_t = max(max_k |x[t,k]|, 1e-5)          (exact: a maximum of bf16 magnitudes)
+//   s_t  = fl32(127 / a'_t)                    (correctly rounded fp32 division)
+//   q    = clamp(rne(fl32(x * s_t)), -127, 127)
+//
+// HBM-bound: 2 bytes read + 1 byte written per element. Each row is held in registers between
+// the max pass and the quantize pass, so it is read from memory once. The max is taken on the
+// bf16 bit patterns with the sign cleared (order-preserving for finite values), two per 32-bit
+// lane op.
+#include "sbn_internal.hpp"
+
+namespace sbn {
+namespace {
+
+constexpr float kFloor = 1e-5f;
+
+__device__ __forceinline__ uint32_t max_abs_bf16x2(uint32_t acc, uint32_t w) {
+  // |hi| and |lo| as 15-bit magnitudes; compare halves independently.
+  const uint32_t a = w & 0x7FFF7FFFu;
+  const uint32_t lo = max(acc & 0xFFFFu, a & 0xFFFFu);
+  const uint32_t hi = max(acc >> 16, a >> 16);
+  return lo | (hi << 16);
+}
+
+__device__ __forceinline__ uint32_t quant4(uint32_t w01, uint32_t w23, float s) {
+  // Four bf16 (two per word) -> four int8 packed in a word.
+  const float f0 = __uint_as_float(w01 << 16), f1 = __uint_as_float(w01 & 0xFFFF0000u);
+  const float f2 = __uint_as_float(w23 << 16), f3 = __uint_as_float(w23 & 0xFFFF0000u);
+  const int i0 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f0 * s), -127.f, 127.f);
+  const int i1 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f1 * s), -127.f, 127.f);
+  const int i2 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f2 * s), -127.f, 127.f);
+  const int i3 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f3 * s), -127.f, 127.f);
+  return (uint32_t)(i0 & 0xFF) | ((uint32_t)(i1 & 0xFF) << 8) | ((uint32_t)(i2 & 0xFF) << 16) |
+         ((uint32_t)(i3 & 0xFF) << 24);
+}
+
+template <int TPR>
+__device__ __forceinline__ uint32_t row_max(uint32_t v, uint32_t* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  if constexpr (TPR > 64) {
+    const int wave = threadIdx.x >> 6, nw = TPR / 64;
+    const int first = (threadIdx.x / TPR) * nw;  // first wave of this row
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    for (int i = 0; i < nw; ++i) r = max(r, red[first + i]);
+    v = r;
+  }
+  return v;
+}
+
+// Vector path: x rows 16-byte aligned, K % 8 == 0, q rows 8-byte aligned.
+template <int TPR, int VPT>
+__global__ __launch_bounds__(256) void quantize_act_vec(const uint16_t* __restrict__ x, int64_t T,
+                                                        int64_t K, int64_t ld_x,
+                                                        int8_t* __restrict__ q, int64_t ld_q,
+                                                        float* __restrict__ absmax) {
+  constexpr int kRowsPerBlock = 256 / TPR;
+  __shared__ uint32_t red[4];
+  const int lt = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / TPR;
+  const bool active = row < T;
+  const int64_t nvec = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (active ? row : 0) * ld_x);
+  uint4 v[VPT];
+  uint32_t m2 = 0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t vi = lt + (int64_t)i * TPR;
+    v[i] = (active && vi < nvec) ? xr[vi] : make_uint4(0, 0, 0, 0);
+    m2 = max_abs_bf16x2(m2, v[i].x);
+    m2 = max_abs_bf16x2(m2, v[i].y);
+    m2 = max_abs_bf16x2(m2, v[i].z);
+    m2 = max_abs_bf16x2(m2, v[i].w);
+  }
+  uint32_t mb = max(m2 & 0xFFFFu, m2 >> 16);
+  mb = row_max<TPR>(mb, red);
+  const float a = fmaxf(__uint_as_float(mb << 16), kFloor);
+  const float s = 127.0f / a;
+  if (!active) return;
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ld_q);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t vi = lt + (int64_t)i * TPR;
+    if (vi < nvec) qr[vi] = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+  }
+  if (lt == 0) absmax[row] = a;
+}
+
+// General path: any alignment and K; the row is read twice (the second read hits cache).
+__global__ __launch_bounds__(256) void quantize_act_any(const uint16_t* __restrict__ x, int64_t T,
+                                                        int64_t K, int64_t ld_x,
+                                                        int8_t* __restrict__ q, int64_t ld_q,
+                                                        float* __restrict__ absmax) {
+  __shared__ uint32_t red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * ld_x;
+  uint32_t mb = 0;
+  for (int64_t k = threadIdx.x; k < K; k += 256) mb = max(mb, (uint32_t)(xr[k] & 0x7FFFu));
+  mb = row_max<256>(mb, red);
+  const float a = fmaxf(__uint_as_float(mb << 16), kFloor);
+  const float s = 127.0f / a;
+  int8_t* qr = q + row * ld_q;
+  for (int64_t k = threadIdx.x; k < K; k += 256) {
+    const float f = __uint_as_float((uint32_t)xr[k] << 16);
+    qr[k] = (int8_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(f * s), -127.f, 127.f);
+  }
+  if (threadIdx.x == 0) absmax[row] = a;
+}
+
+template <int TPR, int VPT>
+hipError_t launch_vec(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x, int8_t* q,
+                      int64_t ld_q, float* absmax, hipStream_t s) {
+  constexpr int rpb = 256 / TPR;
+  const int64_t blocks = (T + rpb - 1) / rpb;
+  hipLaunchKernelGGL((quantize_act_vec<TPR, VPT>), dim3((unsigned)blocks), dim3(256), 0, s, x, T,
+                     K, ld_x, q, ld_q, absmax);
+  return hipGetLastError();
+}
+
+template <int TPR>
+hipError_t dispatch_vpt(int vpt, const uint16_t* x, int64_t T, int64_t K, int64_t ld_x,
+                        int8_t* q, int64_t ld_q, float* absmax, hipStream_t s) {
+  switch (vpt) {
+    case 1: return launch_vec<TPR, 1>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 2: return launch_vec<TPR, 2>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 3: return launch_vec<TPR, 3>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 4: return launch_vec<TPR, 4>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 5: return launch_vec<TPR, 5>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 6: return launch_vec<TPR, 6>(x, T, K, ld_x, q, ld_q, absmax, s);
+    case 7: return launch_vec<TPR, 7>(x, T, K, ld_x, q, ld_q, absmax, s);
+    default: return launch_vec<TPR, 8>(x, T, K, ld_x, q, ld_q, absmax, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x, int8_t* q,
+                               int64_t ld_q, float* absmax, hipStream_t s) {
+  const bool aligned = ((uintptr_t)x % 16 == 0) && (ld_x % 8 == 0) && (K % 8 == 0) &&
+                       ((uintptr_t)q % 8 == 0) && (ld_q % 8 == 0);
+  const int64_t nvec = K / 8;
+  if (aligned && nvec <= 64 * 8) {
+    return dispatch_vpt<64>((int)((nvec + 63) / 64), x, T, K, ld_x, q, ld_q, absmax, s);
+  }
+  if (aligned && nvec <= 256 * 8) {
+    return dispatch_vpt<256>((int)((nvec + 255) / 256), x, T, K, ld_x, q, ld_q, absmax, s);
+  }
+  hipLaunchKernelGGL(quantize_act_any, dim3((unsigned)T), dim3(256), 0, s, x, T, K, ld_x, q,
+                     ld_q, absmax);
+  return hipGetLastError();
+}
+
+}  // namespace sbn

@@ -1,0 +1,42 @@
+// Host-side internals of libsbn: the packed-weight handle and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sbn.h"
+#include "sbn_common.hpp"
+
+struct sbn_packed {
+  sbn::Layout L;
+  size_t code_row_bytes, mask_row_bytes;  // reference packed format (RPF) row sizes
+  size_t mask_plane_bytes, code_plane_bytes;
+  int num_partials;    // absmean partial sums (one per block of the reduction kernel)
+  uint8_t* base;       // single device allocation holding everything below
+  size_t base_bytes;
+  uint8_t* mask;       // mask plane (brick fragments), or nullptr when n == m
+  uint8_t* codes;      // code plane (brick fragments)
+  float* gamma;        // device scalar
+  double* partials;    // device workspace [num_partials]
+  int device;
+  hipStream_t last_stream;
+};
+
+namespace sbn {
+
+// Number of blocks of the absmean reduction for a tensor with n_out rows (fixed per shape, so the
+// fp64 partial-sum order, and hence gamma, is reproducible run to run).
+int absmean_blocks(int64_t n_out);
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x, int8_t* q,
+                               int64_t ld_q, float* absmax, hipStream_t s);
+hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
+hipError_t launch_export(const sbn_packed* h, int8_t* codes, uint8_t* keep, float* gamma,
+                         hipStream_t s);
+hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* mask_bytes,
+                             hipStream_t s);
+hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
+                            const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
+                            hipStream_t s);
+
+}  // namespace sbn

@@ -1,0 +1,93 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on the host
+before any HIP call (no GPU needed: validation never reaches the runtime)."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+from sparsity_sbn_quantize_amd import binding as b
+
+ERR_INVALID, ERR_UNSUPPORTED, ERR_SHAPE = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.lib()
+
+
+def test_exports_match_header(lib):
+    declared = b.header_symbols()
+    assert set(declared) == {"sbn_quantize_act", "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
+                             "sbn_free", "sbn_packed_export", "sbn_packed_export_rpf",
+                             "sbn_packed_query", "sbn_last_error"}
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def _h():
+    return ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, -1, 8, 8, None, 8, None, None), ERR_INVALID),        # T < 0
+    ((None, 4, 0, 8, None, 8, None, None), ERR_INVALID),         # K = 0
+    ((None, 4, 1 << 18, 1 << 18, None, 1 << 18, None, None), ERR_INVALID),  # K > max
+    ((None, 4, 16, 8, None, 16, None, None), ERR_INVALID),       # ld_x < K
+    ((None, 4, 16, 16, None, 15, None, None), ERR_INVALID),      # ld_q < K
+    ((None, 4, 16, 16, None, 16, None, None), ERR_INVALID),      # null pointers
+])
+def test_quantize_validation(lib, args, code):
+    assert lib.sbn_quantize_act(*args) == code
+    assert b.last_error()
+
+
+def test_quantize_T0_is_noop(lib):
+    assert lib.sbn_quantize_act(None, 0, 16, 16, None, 16, None, None) == 0
+
+
+@pytest.mark.parametrize("n_out,K,ld,n,m,code", [
+    (16, 64, 64, 2, 6, ERR_UNSUPPORTED),    # m not in {4, 8, 16}
+    (16, 64, 64, 0, 4, ERR_UNSUPPORTED),    # n < 1
+    (16, 64, 64, 5, 4, ERR_UNSUPPORTED),    # n > m
+    (16, 60, 60, 6, 8, ERR_INVALID),        # K % m
+    (16, 8, 8, 8, 16, ERR_INVALID),         # K < m
+    (-1, 64, 64, 2, 4, ERR_INVALID),        # n_out < 0
+    (16, 64, 32, 2, 4, ERR_INVALID),        # ld_w < K
+    (16, 64, 64, 2, 4, ERR_INVALID),        # w null
+])
+def test_pack_validation(lib, n_out, K, ld, n, m, code):
+    h = _h()
+    assert lib.sbn_pack_nm_ternary(None, n_out, K, ld, n, m, ctypes.byref(h), None) == code
+    assert not h.value
+    assert b.last_error()
+
+
+def test_pack_null_handle_pointer(lib):
+    assert lib.sbn_pack_nm_ternary(None, 16, 64, 64, 2, 4, None, None) == ERR_INVALID
+
+
+def test_forward_and_misc_validation(lib):
+    assert lib.sbn_bitlinear_fwd(None, None, 0, None, 1, None, 0, 0, None) == ERR_INVALID
+    assert lib.sbn_packed_export(None, None, None, None, None) == ERR_INVALID
+    assert lib.sbn_packed_export_rpf(None, None, None, None) == ERR_INVALID
+    assert lib.sbn_packed_query(None, None) == ERR_INVALID
+    lib.sbn_free(None)  # no-op
+
+
+def test_error_message_is_per_call(lib):
+    lib.sbn_quantize_act(None, 4, 0, 8, None, 8, None, None)
+    assert "K=0" in b.last_error()
+    lib.sbn_bitlinear_fwd(None, None, 0, None, 1, None, 0, 0, None)
+    assert "handle" in b.last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        b.lib()
