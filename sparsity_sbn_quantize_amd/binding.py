@@ -96,8 +96,13 @@ def _ptr(t) -> ctypes.c_void_p:
 def _require_cuda(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+def _ld(t, width: int) -> int:
+    """Leading dimension of a 2-D tensor; for a single row (or none) torch may report any stride."""
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), width)
 
 
 def quantize_act(x, out_q=None, out_absmax=None, stream=None):
@@ -110,7 +115,7 @@ def quantize_act(x, out_q=None, out_absmax=None, stream=None):
     q = out_q if out_q is not None else torch.empty((T, K), dtype=torch.int8, device=x.device)
     a = out_absmax if out_absmax is not None else torch.empty((T,), dtype=torch.float32,
                                                               device=x.device)
-    check(lib().sbn_quantize_act(_ptr(x), T, K, x.stride(0), _ptr(q), q.stride(0), _ptr(a),
+    check(lib().sbn_quantize_act(_ptr(x), T, K, _ld(x, K), _ptr(q), _ld(q, K), _ptr(a),
                                  _stream(stream)))
     return q, a
 
@@ -130,7 +135,7 @@ class PackedWeight:
         if w.dtype != torch.float32:
             raise ValueError("w must be float32")
         n_out, K = w.shape
-        check(lib().sbn_pack_nm_ternary(_ptr(w), n_out, K, w.stride(0), self.n, self.m,
+        check(lib().sbn_pack_nm_ternary(_ptr(w), n_out, K, _ld(w, K), self.n, self.m,
                                         ctypes.byref(self._h), _stream(stream)))
         self.n_out, self.K = n_out, K
         return self
@@ -190,6 +195,6 @@ def bitlinear(x_q, x_absmax, w: PackedWeight, out: str = "f32", y=None, stream=N
     if y is None:
         y = torch.empty((T, w.n_out), dtype=torch.float32 if kind == SBN_OUT_F32 else torch.int32,
                         device=x_q.device)
-    check(lib().sbn_bitlinear_fwd(w.handle, _ptr(x_q), x_q.stride(0), _ptr(x_absmax), T,
-                                  _ptr(y), y.stride(0), kind, _stream(stream)))
+    check(lib().sbn_bitlinear_fwd(w.handle, _ptr(x_q), _ld(x_q, w.K), _ptr(x_absmax), T,
+                                  _ptr(y), _ld(y, w.n_out), kind, _stream(stream)))
     return y
