@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sparse-BitNet BitLinear forward on one MI355X (gfx950).
+
+A step is one pass of the hot path over one batch of synthetic input: per-token INT8 quantization
+of the activations, then the n:m-sparse ternary x INT8 matmul with fused dequantization (and, for
+the dynamic-sparsity training workload, the absmean + n:m re-pack of the latent weights). Steps
+are captured into one HIP graph and replayed, so host launch overhead is not measured; inputs are
+resident in HBM before the timed region starts.
+
+Default workload: decode GEMV, 6:8, K=2560 -> N=6912, one token, weights packed once; the packed
+weights rotate over enough distinct copies (>= 1 GiB) that every step streams them from HBM.
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA
+METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GEMV)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
+                  "sparsity_sbn_quantize_amd/csrc/sbn_common.hpp",
+                  "sparsity_sbn_quantize_amd/csrc/pack.hip",
+                  "sparsity_sbn_quantize_amd/csrc/quantize_act.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when missing or
+    taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------------------------
+# Algorithmic work per launch (what the method must move or compute).
+# ------------------------------------------------------------------------------------------------
+
+def rpf_bytes(n_out, K, n, m):
+    code_row = ((K // m) * 2 * n + 7) // 8
+    mask_row = (K + 7) // 8 if n < m else 0
+    return n_out * (code_row + mask_row)
+
+
+def quantize_bytes(T, K):
+    return 2 * T * K + T * K + 4 * T
+
+
+def forward_bytes(T, K, n_out, n, m):
+    return rpf_bytes(n_out, K, n, m) + T * K + 4 * T + 4 + 4 * T * n_out
+
+
+def pack_bytes(n_out, K, n, m):
+    return 4 * n_out * K + rpf_bytes(n_out, K, n, m) + 4
+
+
+# ------------------------------------------------------------------------------------------------
+# GPU helpers.
+# ------------------------------------------------------------------------------------------------
+
+class Gpu:
+    def __init__(self):
+        import torch
+        from sparsity_sbn_quantize_amd import binding
+        self.torch = torch
+        self.b = binding
+        binding.lib()  # fails loudly when the HIP library is missing
+        torch.cuda.set_device(0)
+
+    def bf16(self, bits):
+        import numpy as np
+        return self.torch.from_numpy(bits.view(np.int16)).cuda().view(self.torch.bfloat16)
+
+    def f32(self, a):
+        return self.torch.from_numpy(a).cuda()
+
+    def graph(self, fn, count):
+        """Captures fn(i) for i in range(count) into one HIP graph."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g):
+        """Milliseconds of one replay, between HIP events on the replaying stream."""
+        torch = self.torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        g.replay()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e)
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------------------------------------
+# Workloads.
+# ------------------------------------------------------------------------------------------------
+
+def run_decode(gpu, args, T=1, with_cpu=True):
+    """Decode GEMV: quantize T tokens + n:m forward on weights packed once."""
+    import numpy as np
+    from sparsity_sbn_quantize_amd import inputs
+    torch = gpu.torch
+    wl = inputs.W_DECODE
+    layer = wl.layers[0]
+    n, m = wl.patterns[0]
+    K, N = layer.k, layer.n_out
+    x_bits, w = inputs.layer_inputs(wl, 0, T)
+    xd, wd = gpu.bf16(x_bits), gpu.f32(w)
+    R = max(1, -(-args.rotate_bytes // rpf_bytes(N, K, n, m)))
+    pws = [gpu.b.PackedWeight(wd, n, m) for _ in range(R)]
+    q = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    a = torch.empty((T,), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+        gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
+
+    def gemv_only(i):
+        gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
+
+    def quant_only(i):
+        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+
+    step(0)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    gw = gpu.graph(step, args.warmup) if args.warmup > 0 else None
+    gs = gpu.graph(step, args.steps)
+    if gw is not None:
+        gw.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = gpu.time_graph(gs)
+    wall = time.perf_counter() - t0
+    assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
+    gk = gpu.graph(gemv_only, args.steps)
+    gk.replay()
+    gemv_ms = gpu.time_graph(gk) / args.steps
+    gq = gpu.graph(quant_only, args.steps)
+    gq.replay()
+    quant_ms = gpu.time_graph(gq) / args.steps
+
+    fb = forward_bytes(T, K, N, n, m)
+    step_bytes = fb + quantize_bytes(T, K)
+    ms_step = ms / args.steps
+    achieved = fb / (gemv_ms * 1e-3) / 1e9
+    res = {
+        "value": step_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms_step,
+        "wall_s": wall,
+        "config": {"workload": f"{wl.name}_T{T}", "pattern": f"{n}:{m}", "tokens": T, "K": K,
+                   "n_out": N, "weights": "packed once, rotated over %d copies" % R,
+                   "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "bitlinear_gemv", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"gemv_{n}of{m}_T{T}"),
+                     "bytes_per_launch": fb, "avg_launch_us": gemv_ms * 1e3},
+        "kernels_us": {"quantize_act": quant_ms * 1e3, "bitlinear_gemv": gemv_ms * 1e3},
+    }
+    if with_cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_decode(x_bits, w, n, m, step_bytes, args.cpu_seconds)
+    for p in pws:
+        p.free()
+    return res
+
+
+def cpu_decode(x_bits, w, n, m, step_bytes, seconds):
+    import oracle
+    packed = oracle.pack_nm_ternary(w, n, m)  # packed once, as on the GPU
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        q, a = oracle.quantize_act(x_bits)
+        acc = oracle.int_matmul(q, packed["codes"])
+        oracle.dequantize(acc, packed["gamma"], a)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and steps >= 3:
+            break
+    return {"value": step_bytes * steps / el / 1e9, "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"the full step (quantize + exact fp64 matmul + dequantize), {steps} steps "
+                      f"in {el:.1f} s"}
+
+
+def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True):
+    """Prefill GEMM: quantize 2048 tokens + 8:16 forward (weights packed once)."""
+    from sparsity_sbn_quantize_amd import inputs
+    torch = gpu.torch
+    wl = inputs.W_PREFILL
+    layer = wl.layers[layer_index]
+    n, m = wl.patterns[0]
+    T = wl.tokens[0]
+    K, N = layer.k, layer.n_out
+    steps = steps or args.steps
+    x_bits, w = inputs.layer_inputs(wl, layer_index, T)
+    xd, wd = gpu.bf16(x_bits), gpu.f32(w)
+    pw = gpu.b.PackedWeight(wd, n, m)
+    q = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    a = torch.empty((T,), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+        gpu.b.bitlinear(q, a, pw, out="f32", y=y)
+
+    def gemm_only(i):
+        gpu.b.bitlinear(q, a, pw, out="f32", y=y)
+
+    step(0)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    gs = gpu.graph(step, steps)
+    gs.replay()
+    ms = gpu.time_graph(gs) / steps
+    assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
+    gk = gpu.graph(gemm_only, steps)
+    gk.replay()
+    gemm_ms = gpu.time_graph(gk) / steps
+    ops = 2.0 * T * K * N
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    res = {
+        "value": ops / (ms * 1e-3) / 1e12, "unit": "TOPS", "ms_per_step": ms,
+        "config": {"workload": f"{wl.name}_{layer.name}", "pattern": f"{n}:{m}", "tokens": T,
+                   "K": K, "n_out": N, "ops": "dense-equivalent 2*T*K*N"},
+        "roofline": {"bound": "mfma", "kernel": "bitlinear_gemm", "achieved": achieved,
+                     "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": achieved / INT8_PEAK_TOPS,
+                     "traffic": measured_traffic(f"gemm_{n}of{m}_{layer.name}"),
+                     "avg_launch_us": gemm_ms * 1e3},
+    }
+    if with_cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_prefill(x_bits, w, n, m, K, N, args.cpu_seconds)
+    pw.free()
+    return res
+
+
+def cpu_prefill(x_bits, w, n, m, K, N, seconds):
+    import oracle
+    packed = oracle.pack_nm_ternary(w, n, m)
+    tok = 32
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        q, a = oracle.quantize_act(x_bits[:tok])
+        acc = oracle.int_matmul(q, packed["codes"])
+        oracle.dequantize(acc, packed["gamma"], a)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and steps >= 2:
+            break
+    ops = 2.0 * tok * K * N * steps
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": cpu_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"{tok} of the tokens per step (same weights, K, N), {steps} steps in "
+                      f"{el:.1f} s"}
+
+
+def profile_copy(gpu, args):
+    """A plain device copy of known size (for scaling HBM byte counters)."""
+    torch = gpu.torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode16", "prefill_up", "prefill_down"])
+    ap.add_argument("--rotate-bytes", type=int, default=1 << 30,
+                    help="distinct packed-weight bytes rotated through (cold HBM)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
+              "part of this build", file=sys.stderr)
+        sys.exit(2)
+    gpu = Gpu()
+    if args.profile_copy:
+        profile_copy(gpu, args)
+        return
+    if args.workload == "decode":
+        res = run_decode(gpu, args, T=1)
+    elif args.workload == "decode16":
+        res = run_decode(gpu, args, T=16)
+    else:
+        res = run_prefill(gpu, args, 0 if args.workload == "prefill_up" else 1,
+                          steps=min(args.steps, 200))
+    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+            "steps": args.steps if args.workload.startswith("decode") else min(args.steps, 200),
+            "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": res["config"], "roofline": res["roofline"],
+            "kernels_us": res.get("kernels_us")}
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
+    if not args.no_secondary and args.workload == "decode":
+        sec = []
+        r16 = run_decode(gpu, args, T=16, with_cpu=False)
+        sec.append({k: r16[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
+        for li in (0, 1):
+            rp = run_prefill(gpu, args, li, steps=50, with_cpu=False)
+            sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
+        line["secondary"] = sec
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -11,8 +11,10 @@
 // Each lane decodes one brick (64 K positions of one weight row) from its packed mask + codes
 // straight into the A operand of v_mfma_i32_16x16x64_i8: the brick's bytes [16j, 16j+16) feed
 // MFMA j of the 256-K fragment. The B operand (activations) uses the same K assignment, so the
-// products pair correctly whatever the instruction's internal K order. Decode is a lookup per
-// 4 positions in a 4096-entry nibble table held in LDS (index: mask nibble, next 8 code bits).
+// products pair correctly whatever the instruction's internal K order. Decode: the brick's codes
+// (plane order) become int8 bytes with shift/and/v_perm, and each 4 output positions are one
+// v_perm of those bytes with a selector taken from a 256-entry table keyed by a mask byte,
+// replicated per lane group in LDS so that the table reads are free of bank conflicts.
 //
 //   GEMV (T <= 16): one workgroup per 16-row fragment row, its 4 waves split K; activations are
 //   read straight from global memory (they are tiny and cache-resident).
@@ -25,17 +27,9 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-__device__ const NibbleTable g_nibble_table = make_nibble_table();
-
 __device__ __forceinline__ v4i mfma16(const uint32_t* a, v4i b, v4i c) {
   const v4i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void load_lut(uint32_t* lut) {
-  const uint4* src = reinterpret_cast<const uint4*>(g_nibble_table.v);
-  uint4* dst = reinterpret_cast<uint4*>(lut);
-  for (int i = threadIdx.x; i < 1024; i += blockDim.x) dst[i] = src[i];
 }
 
 // Loads one brick's mask (8 bytes) and code bytes. CBB > 0: compile-time code bytes per brick.
@@ -69,10 +63,10 @@ __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* __res
 }
 
 template <int N, int M>
-__device__ __forceinline__ void decode(const Layout& L, const uint32_t* lut, const uint32_t mask[2],
+__device__ __forceinline__ void decode(const Layout& L, const uint2* sel, const uint32_t mask[2],
                                        const uint32_t codes[4], uint32_t out[16]) {
   if constexpr (N > 0) {
-    decode_brick_lut<N, M>(lut, mask, codes, out);
+    decode_brick_sel<N, M>(sel, mask, codes, out);
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) out[i] = 0;
@@ -80,15 +74,30 @@ __device__ __forceinline__ void decode(const Layout& L, const uint32_t* lut, con
   }
 }
 
-// 16 activation bytes of one token row at K offset k (zero beyond K).
-__device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int64_t k, int64_t K,
-                                        int vec) {
-  if (vec && k + 16 <= K) return *reinterpret_cast<const v4i*>(row + k);
-  uint32_t w[4] = {0, 0, 0, 0};
-  for (int i = 0; i < 16; ++i) {
-    if (k + i < K) w[i >> 2] |= (uint32_t)(uint8_t)row[k + i] << (8 * (i & 3));
+// 16 activation bytes of one token row at K offset k (a multiple of 16), zero beyond K.
+// XVEC: rows are 16-byte aligned and K % 16 == 0, so a chunk is either whole or absent.
+template <bool XVEC>
+__device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int k, int K) {
+  if constexpr (XVEC) {
+    // Branch-free: the load address is clamped into the row (K >= 16 here), the value masked.
+    const v4i v = *reinterpret_cast<const v4i*>(row + min(k, K - 16));
+    return k < K ? v : v4i{0, 0, 0, 0};
+  } else {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      if (k + i < K) w[i >> 2] |= (uint32_t)(uint8_t)row[k + i] << (8 * (i & 3));
+    }
+    return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
   }
-  return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
+// 16 activation bytes at K offset k (a multiple of 16) with the address clamped into the row:
+// bytes at k >= K are arbitrary row data, which is harmless wherever the weights at those
+// positions are zero (bricks are zero-padded past K). XVEC rows only. No value select, so the
+// load's result is not needed until it is used (no wait right after the load).
+__device__ __forceinline__ v4i load_x16_clamped(const int8_t* __restrict__ row, int k, int K) {
+  return *reinterpret_cast<const v4i*>(row + min(k, K - 16));
 }
 
 __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, int64_t t,
@@ -101,143 +110,377 @@ __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, i
   }
 }
 
-template <int N, int M, int CBB>
+// GEMV (T <= 16): a workgroup owns RB 16-row fragment rows; its 4 waves split K (wave w takes
+// the 256-K steps w, w+4, ...). K is walked in chunks of 16 steps (4096 K): the chunk's bricks
+// are loaded first, then the chunk's activations are staged once in LDS (shared by all waves and
+// row fragments instead of being re-read from L2 by every wave), then bricks are decoded and
+// multiplied. Partial sums of the 4 waves are combined through LDS.
+constexpr int kGemvChunk = 4;                       // K steps per wave per chunk
+constexpr int kGemvChunkK = 4 * kGemvChunk * kQuadK;  // 4096
+constexpr int kGemvXStride = kGemvChunkK + 16;
+
+template <int N, int M, int CBB, bool XVEC, int RB>
 __global__ __launch_bounds__(256) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
-    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q, int xq_vec,
+    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
     const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
     int out_kind) {
-  __shared__ uint32_t lut[N > 0 ? 4096 : 1];
-  __shared__ v4i red[3][64];
+  constexpr bool kSel = N > 0 && N < M;  // sparse fast path: selector table in LDS
+  __shared__ uint2 sel_tab[kSel ? 4096 : 1];
+  __shared__ v4i red[3][RB][64];
+  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [T][kGemvXStride]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rb = blockIdx.x;
-  if constexpr (N > 0) {
-    load_lut(lut);
-    __syncthreads();
-  }
+  const int64_t rb0 = (int64_t)blockIdx.x * RB;
   const int t = lane & 15, g = lane >> 4;
-  const bool tok_ok = t < T;
-  const int8_t* xrow = xq + (tok_ok ? t : 0) * ld_q;
-  v4i acc = {0, 0, 0, 0};
-  for (int64_t q = wave; q < L.quads; q += 4) {
-    const int64_t slot = ((rb * L.quads + q) << 6) | lane;
-    uint32_t mask[2], codes[4], a[16];
-    load_brick<CBB>(L, mask_plane, code_plane, slot, mask, codes);
-    const int64_t kb = (q * 4 + g) * kBrickK;
-    v4i b[4];
+  const int Ti = (int)T;
+  const bool tok_ok = t < Ti;
+  v4i acc[RB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = tok_ok ? load_x16(xrow, kb + 16 * j, L.K, xq_vec) : v4i{0, 0, 0, 0};
-    decode<N, M>(L, lut, mask, codes, a);
+  for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
+  uint32_t mask[kGemvChunk][RB][2], codes[kGemvChunk][RB][4];
+
+  const int nchunks = (int)((L.quads + 4 * kGemvChunk - 1) / (4 * kGemvChunk));
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t qbase = (int64_t)c * 4 * kGemvChunk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[j], acc);
+    for (int i = 0; i < kGemvChunk; ++i) {
+      const int64_t q = qbase + wave + 4 * i;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (q < L.quads && rb0 + r < L.row_blocks) {
+          load_brick<CBB>(L, mask_plane, code_plane, (((rb0 + r) * L.quads + q) << 6) | lane,
+                          mask[i][r], codes[i][r]);
+        } else {
+          mask[i][r][0] = mask[i][r][1] = 0;
+          codes[i][r][0] = codes[i][r][1] = codes[i][r][2] = codes[i][r][3] = 0;
+        }
+      }
+    }
+    // Stage this chunk's activations: T rows x 4096 K in 16-byte pieces.
+    const int k0 = c * kGemvChunkK;
+    if (c > 0) __syncthreads();  // previous chunk's readers are done with xs
+    for (int e = threadIdx.x; e < Ti * (kGemvChunkK / 16); e += 256) {
+      const int tok = e / (kGemvChunkK / 16), ch = e % (kGemvChunkK / 16);
+      *reinterpret_cast<v4i*>(xs + tok * kGemvXStride + ch * 16) =
+          load_x16<XVEC>(xq + tok * ld_q, k0 + ch * 16, (int)L.K);
+    }
+    if constexpr (kSel) {
+      if (c == 0) fill_sel_table(sel_tab);
+    }
+    __syncthreads();
+    const uint2* sel = sel_tab + (lane & 15);
+    const int8_t* xb = xs + (tok_ok ? t : 0) * kGemvXStride + g * kBrickK;
+#pragma unroll
+    for (int i = 0; i < kGemvChunk; ++i) {
+      const int64_t q = qbase + wave + 4 * i;
+      if (q < L.quads) {
+        v4i b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = tok_ok ? *reinterpret_cast<const v4i*>(xb + (wave + 4 * i) * kQuadK + 16 * j)
+                        : v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          uint32_t a[16];
+          decode<N, M>(L, sel, mask[i][r], codes[i][r], a);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r] = mfma16(a + 4 * j, b[j], acc[r]);
+        }
+      }
+    }
   }
-  if (wave > 0) red[wave - 1][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    if (wave > 0) red[wave - 1][r][lane] = acc[r];
   __syncthreads();
-  if (wave != 0) return;
-  acc += red[0][lane] + red[1][lane] + red[2][lane];
-  if (!tok_ok) return;
+  if (wave != 0 || !tok_ok) return;
   const float gamma = gamma_p[0];
   const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = rb * 16 + 4 * g + i;
-    if (r < L.n_out) store_out(y, ld_y, out_kind, t, r, acc[i], gamma, step);
+  for (int r = 0; r < RB; ++r) {
+    const v4i sum = acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = (rb0 + r) * 16 + 4 * g + i;
+      if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+    }
   }
 }
 
-constexpr int kRF = 4;    // 16-row fragments per wave
-constexpr int kCF = 8;    // 16-token fragments per workgroup
-constexpr int kXStride = 272;  // bytes per staged token row (256 + 16 to spread LDS banks)
+// GEMM: a workgroup computes 256 rows x (16*CF) tokens; wave w owns 4 row fragments (64 rows).
+// The K loop (256 K per step) is software-pipelined three deep: while the MFMAs of step q run,
+// the bricks of step q+1 are decoded (one row fragment per MFMA group), the activation tile of
+// step q+1 is written to the other LDS buffer, and the global loads of step q+2 are in flight.
+// One barrier per step.
+constexpr int kRF = 4;         // 16-row fragments per wave
+constexpr int kGemmCF = 8;     // 16-token fragments per workgroup
+constexpr int kXStride = 272;  // bytes per staged token row (256 + 16 spreads the LDS banks)
 
-template <int N, int M, int CBB>
-__global__ __launch_bounds__(256) void bitlinear_gemm(
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). The linear block
+// id is remapped so that every XCD receives one contiguous run of tiles in a grouped order
+// (kTileGroup token tiles x all N tiles, N-major within the group): the tiles an XCD has in
+// flight then share activation rows and packed weights in its L2.
+constexpr int kXcds = 8;
+constexpr int kTileGroup = 4;
+
+__device__ __forceinline__ void xcd_tile(int nblocks, int bid, int tiles_n, int tiles_t,
+                                         int& tile_n, int& tile_t) {
+  const int xcd = bid % kXcds, j = bid / kXcds;
+  const int base = nblocks / kXcds, extra = nblocks % kXcds;
+  const int lin = xcd * base + min(xcd, extra) + j;  // position in the grouped order
+  const int per_group = kTileGroup * tiles_n;
+  const int group = lin / per_group, r = lin % per_group;
+  const int gsize = min(kTileGroup, tiles_t - group * kTileGroup);
+  tile_n = r / gsize;
+  tile_t = group * kTileGroup + r % gsize;
+}
+
+template <int N, int M, int CBB, int CF, bool XVEC>
+__global__ __launch_bounds__(256, 1) void bitlinear_gemm(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
-    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q, int xq_vec,
+    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
     const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
-    int out_kind) {
-  __shared__ uint32_t lut[N > 0 ? 4096 : 1];
-  __shared__ __attribute__((aligned(16))) int8_t xs[kCF * 16 * kXStride];
+    int out_kind, int tiles_n, int tiles_t) {
+  constexpr int kTok = CF * 16;
+  constexpr int kXChunks = kTok * 16 / 256;  // 16-byte activation chunks per thread per K step
+  constexpr bool kSel = N > 0 && N < M;      // sparse fast path: selector table in LDS
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint2* sel_tab = reinterpret_cast<uint2*>(smem);
+  int8_t* xs0 = reinterpret_cast<int8_t*>(smem + (kSel ? 32768 : 0));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rb0 = ((int64_t)blockIdx.x * 4 + wave) * kRF;  // this wave's first row fragment
-  const int64_t t0 = (int64_t)blockIdx.y * kCF * 16;
-  if constexpr (N > 0) load_lut(lut);
-  v4i acc[kRF][kCF];
+  int tile_n, tile_t;
+  xcd_tile((int)gridDim.x, (int)blockIdx.x, tiles_n, tiles_t, tile_n, tile_t);
+  const int64_t rb0 = ((int64_t)tile_n * 4 + wave) * kRF;
+  const int64_t t0 = (int64_t)tile_t * kTok;
+  const int64_t nq = L.quads;
+  const int K = (int)L.K;
+  // Rows past n_out and tokens past T read valid (clamped) data; their results are not stored,
+  // so the steady-state loop has no per-load branches.
+  const int cbb = CBB > 0 ? CBB : L.code_brick_bytes;  // code bytes per brick
+  const uint8_t* mrow[kRF];
+  const uint8_t* crow[kRF];
+#pragma unroll
+  for (int rf = 0; rf < kRF; ++rf) {
+    const int64_t rb = min(rb0 + rf, L.row_blocks - 1);
+    mrow[rf] = mask_plane + ((rb * nq) << 6 | lane) * 8;
+    crow[rf] = code_plane + ((rb * nq) << 6 | lane) * cbb;
+  }
+  if constexpr (kSel) fill_sel_table(sel_tab);
+  const uint2* sel = sel_tab + (lane & 15);
+  const int8_t* xrow[kXChunks];
+#pragma unroll
+  for (int i = 0; i < kXChunks; ++i) {
+    const int c = threadIdx.x + i * 256;
+    xrow[i] = xq + min<int64_t>(t0 + (c >> 4), T - 1) * ld_q + (c & 15) * 16;
+  }
+
+  typedef uint32_t Bricks[kRF][6];  // per row fragment: mask words 0-1, code words 2-5
+  typedef uint32_t Frags[kRF][16];  // decoded A operands
+  v4i xr[kXChunks];
+  auto load_step = [&](int64_t q, Bricks& bk) {
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      const int ch = (threadIdx.x + i * 256) & 15;
+      if constexpr (XVEC) {
+        xr[i] = load_x16_clamped(xrow[i] - ch * 16, (int)q * kQuadK + ch * 16, K);
+      } else {
+        xr[i] = load_x16<false>(xrow[i] - ch * 16, (int)q * kQuadK + ch * 16, K);
+      }
+    }
+#pragma unroll
+    for (int rf = 0; rf < kRF; ++rf) {
+      const int64_t off = q << 6;  // slots advance by 64 per K step
+      bk[rf][0] = bk[rf][1] = 0;
+      if (N > 0 ? N < M : L.has_mask) {
+        const uint2 m = *reinterpret_cast<const uint2*>(mrow[rf] + off * 8);
+        bk[rf][0] = m.x;
+        bk[rf][1] = m.y;
+      }
+      bk[rf][2] = bk[rf][3] = bk[rf][4] = bk[rf][5] = 0;
+      const uint8_t* c = crow[rf] + off * cbb;
+      if constexpr (CBB == 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(c);
+        bk[rf][2] = v.x; bk[rf][3] = v.y; bk[rf][4] = v.z; bk[rf][5] = v.w;
+      } else if constexpr (CBB == 12) {
+        const uint32_t* v = reinterpret_cast<const uint32_t*>(c);
+        bk[rf][2] = v[0]; bk[rf][3] = v[1]; bk[rf][4] = v[2];
+      } else if constexpr (CBB == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(c);
+        bk[rf][2] = v.x; bk[rf][3] = v.y;
+      } else {
+        for (int i = 0; i < cbb; ++i) bk[rf][2 + (i >> 2)] |= (uint32_t)c[i] << (8 * (i & 3));
+      }
+    }
+  };
+  auto store_x = [&](int buf) {
+    int8_t* xs = xs0 + buf * (kTok * kXStride);
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+      const int c = threadIdx.x + i * 256;
+      *reinterpret_cast<v4i*>(xs + (c >> 4) * kXStride + (c & 15) * 16) = xr[i];
+    }
+  };
+  auto decode_rf = [&](const Bricks& bk, int rf, uint32_t* out) {
+    const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
+    const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
+    decode<N, M>(L, sel, m, c, out);
+  };
+
+  v4i acc[kRF][CF];
 #pragma unroll
   for (int rf = 0; rf < kRF; ++rf)
 #pragma unroll
-    for (int cf = 0; cf < kCF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
-
-  for (int64_t q = 0; q < L.quads; ++q) {
-    // Stage the activation tile: tokens t0 + [0, 128), K = q*256 + [0, 256).
-    for (int c = threadIdx.x; c < kCF * 16 * 16; c += 256) {
-      const int tok = c >> 4, ch = c & 15;
-      const int64_t tt = t0 + tok;
-      v4i v = {0, 0, 0, 0};
-      if (tt < T) v = load_x16(xq + tt * ld_q, q * kQuadK + ch * 16, L.K, xq_vec);
-      *reinterpret_cast<v4i*>(xs + tok * kXStride + ch * 16) = v;
-    }
-    __syncthreads();
-    uint32_t a[kRF][16];
+    for (int cf = 0; cf < CF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
+  const int8_t* xlane = xs0 + (lane & 15) * kXStride + (lane >> 4) * kBrickK;
+  auto mfma_group = [&](const int8_t* xb, int j, const Frags& a) {
 #pragma unroll
-    for (int rf = 0; rf < kRF; ++rf) {
-      const int64_t rb = rb0 + rf;
-      if (rb < L.row_blocks) {
-        uint32_t mask[2], codes[4];
-        load_brick<CBB>(L, mask_plane, code_plane, ((rb * L.quads + q) << 6) | lane, mask, codes);
-        decode<N, M>(L, lut, mask, codes, a[rf]);
-      } else {
+    for (int cf = 0; cf < CF; ++cf) {
+      const v4i bv = *reinterpret_cast<const v4i*>(xb + cf * 16 * kXStride + 16 * j);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a[rf][i] = 0;
-      }
+      for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(a[rf] + 4 * j, bv, acc[rf][cf]);
     }
+  };
+  // One K step q: multiply with `acur`; decode step q+1 (bricks `bdec`) into `anext` between the
+  // MFMA groups; stage step q+1's activations; load step q+2 into `bload`.
+  auto step = [&](int64_t q, const Frags& acur, Frags& anext, const Bricks& bdec, Bricks& bload) {
+    const int8_t* xb = xlane + (q & 1) * (kTok * kXStride);
+    store_x((int)((q + 1) & 1));
+    load_step(min<int64_t>(q + 2, nq - 1), bload);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      mfma_group(xb, j, acur);
+      decode_rf(bdec, j, anext[j]);  // kRF == 4: one fragment per MFMA group
+      // Ask the scheduler to interleave: per activation fragment one LDS read, its kRF MFMAs,
+      // a share of the decode's VALU work and one selector read.
 #pragma unroll
-      for (int cf = 0; cf < kCF; ++cf) {
-        const v4i b = *reinterpret_cast<const v4i*>(xs + (cf * 16 + (lane & 15)) * kXStride +
-                                                    (lane >> 4) * kBrickK + 16 * j);
-#pragma unroll
-        for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(a[rf] + 4 * j, b, acc[rf][cf]);
+      for (int cf = 0; cf < CF; ++cf) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
       }
     }
     __syncthreads();
+  };
+  auto last_step = [&](int64_t q, const Frags& acur) {
+    const int8_t* xb = xlane + (q & 1) * (kTok * kXStride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mfma_group(xb, j, acur);
+  };
+
+  Bricks b0, b1;
+  Frags a0, a1;
+  load_step(0, b0);
+  store_x(0);
+  __syncthreads();
+#pragma unroll
+  for (int rf = 0; rf < kRF; ++rf) decode_rf(b0, rf, a0[rf]);
+  load_step(min<int64_t>(1, nq - 1), b1);
+  // Register sets alternate between consecutive steps, so nothing is copied.
+  int64_t q = 0;
+  for (; q + 2 < nq; q += 2) {
+    step(q, a0, a1, b1, b0);
+    step(q + 1, a1, a0, b0, b1);
   }
+  if (q + 1 < nq) {
+    step(q, a0, a1, b1, b0);
+    last_step(q + 1, a1);
+  } else {
+    last_step(q, a0);
+  }
+
   const float gamma = gamma_p[0];
   const int g = lane >> 4;
+  // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte store when the
+  // output rows are 16-byte aligned and all 4 rows exist.
+  const bool vec_out = (((uintptr_t)y | (uintptr_t)(ld_y * 4)) & 15) == 0;
 #pragma unroll
-  for (int cf = 0; cf < kCF; ++cf) {
+  for (int cf = 0; cf < CF; ++cf) {
     const int64_t t = t0 + cf * 16 + (lane & 15);
     if (t >= T) continue;
     const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
+      const int64_t r0 = (rb0 + rf) * 16 + 4 * g;
+      const v4i v = acc[rf][cf];
+      if (vec_out && r0 + 4 <= L.n_out) {
+        if (out_kind == SBN_OUT_I32_ACC) {
+          *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + r0) = v;
+        } else {
+          float4 f;
+          f.x = __fmul_rn(__fmul_rn((float)v[0], gamma), step);
+          f.y = __fmul_rn(__fmul_rn((float)v[1], gamma), step);
+          f.z = __fmul_rn(__fmul_rn((float)v[2], gamma), step);
+          f.w = __fmul_rn(__fmul_rn((float)v[3], gamma), step);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + r0) = f;
+        }
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = (rb0 + rf) * 16 + 4 * g + i;
-        if (r < L.n_out) store_out(y, ld_y, out_kind, t, r, acc[rf][cf][i], gamma, step);
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < L.n_out) store_out(y, ld_y, out_kind, t, r0 + i, v[i], gamma, step);
       }
     }
   }
 }
 
-template <int N, int M, int CBB>
-hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q, int xq_vec,
+
+template <int N, int M, int CF>
+constexpr size_t gemm_smem_bytes() {
+  return (N > 0 && N < M ? 32768 : 0) + 2 * (size_t)CF * 16 * kXStride;
+}
+
+// Raises a kernel's dynamic-LDS limit once per process (gfx950 has 160 KB of LDS per CU).
+template <typename K>
+hipError_t allow_smem(K kernel, size_t bytes) {
+  static size_t done = 0;
+  if (bytes <= done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done = bytes;
+  return e;
+}
+
+template <int N, int M, int CBB, bool XVEC>
+hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
   const Layout& L = h->L;
   if (T <= 16) {
-    hipLaunchKernelGGL((bitlinear_gemv<N, M, CBB>), dim3((unsigned)L.row_blocks), dim3(256), 0, s,
-                       h->mask, h->codes, L, h->gamma, xq, ld_q, xq_vec, absmax, T, y, ld_y,
-                       out_kind);
-  } else {
-    const int64_t gx = (L.row_blocks + 4 * kRF - 1) / (4 * kRF);
-    const int64_t gy = (T + kCF * 16 - 1) / (kCF * 16);
-    hipLaunchKernelGGL((bitlinear_gemm<N, M, CBB>), dim3((unsigned)gx, (unsigned)gy), dim3(256),
-                       0, s, h->mask, h->codes, L, h->gamma, xq, ld_q, xq_vec, absmax, T, y,
-                       ld_y, out_kind);
+    const size_t xs_bytes = (size_t)T * kGemvXStride;
+    if (T <= 4) {
+      hipError_t e = allow_smem(bitlinear_gemv<N, M, CBB, XVEC, 1>, xs_bytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((bitlinear_gemv<N, M, CBB, XVEC, 1>), dim3((unsigned)L.row_blocks),
+                         dim3(256), xs_bytes, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax,
+                         T, y, ld_y, out_kind);
+    } else {
+      hipError_t e = allow_smem(bitlinear_gemv<N, M, CBB, XVEC, 2>, xs_bytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((bitlinear_gemv<N, M, CBB, XVEC, 2>),
+                         dim3((unsigned)((L.row_blocks + 1) / 2)), dim3(256), xs_bytes, s, h->mask,
+                         h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y, out_kind);
+    }
+    return hipGetLastError();
   }
+  constexpr int CF = kGemmCF;
+  constexpr size_t smem = gemm_smem_bytes<N, M, CF>();
+  hipError_t e = allow_smem(bitlinear_gemm<N, M, CBB, CF, XVEC>, smem);
+  if (e != hipSuccess) return e;
+  const int64_t gx = (L.row_blocks + 4 * kRF - 1) / (4 * kRF);
+  const int64_t gy = (T + CF * 16 - 1) / (CF * 16);
+  hipLaunchKernelGGL((bitlinear_gemm<N, M, CBB, CF, XVEC>), dim3((unsigned)(gx * gy)), dim3(256),
+                     smem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
+                     out_kind, (int)gx, (int)gy);
   return hipGetLastError();
+}
+
+template <int N, int M, int CBB>
+hipError_t launch_pattern_x(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
+                            const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
+                            hipStream_t s) {
+  const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (h->L.K % 16 == 0);
+  if (xvec) return launch_pattern<N, M, CBB, true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern<N, M, CBB, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace
@@ -247,11 +490,10 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             hipStream_t s) {
   const Layout& L = h->L;
   if (L.n_out == 0 || T == 0) return hipSuccess;
-  const int xq_vec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0);
   const int n = L.n, m = L.m;
 #define SBN_CASE(NN, MM, CB)                                                                    \
   if (n == NN && m == MM)                                                                       \
-    return launch_pattern<NN, MM, CB>(h, xq, ld_q, xq_vec, absmax, T, y, ld_y, out_kind, s);
+    return launch_pattern_x<NN, MM, CB>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
   SBN_CASE(2, 4, 8)
   SBN_CASE(4, 4, 16)
   SBN_CASE(4, 8, 8)
@@ -260,7 +502,7 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   SBN_CASE(8, 16, 8)
   SBN_CASE(16, 16, 16)
 #undef SBN_CASE
-  return launch_pattern<0, 0, 0>(h, xq, ld_q, xq_vec, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern_x<0, 0, 0>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace sbn

@@ -114,9 +114,10 @@ __global__ __launch_bounds__(256) void pack_bricks(const float* __restrict__ w, 
   const int groups = (int)min<int64_t>(kBrickK / M, (L.K - k0) / M);
 
   uint64_t maskbits = 0;
-  uint64_t pend = 0;  // code bits not yet stored
+  uint64_t pend = 0;  // code bits not yet stored (sequence order)
   int npend = 0;
   uint8_t* cdst = code_plane + slot * L.code_brick_bytes;
+  const bool plane = plane_order(n, M);
   int cbyte = 0;
   for (int g = 0; g < groups; ++g) {
     uint32_t a[M], sgn[M];
@@ -126,8 +127,7 @@ __global__ __launch_bounds__(256) void pack_bricks(const float* __restrict__ w, 
       a[i] = u & 0x7FFFFFFFu;
       sgn[i] = u >> 31;
     }
-    const uint32_t keep = (n == M) ? ((M == 32) ? 0xFFFFFFFFu : ((1u << M) - 1u))
-                                   : keep_mask_group<M>(a, n);
+    const uint32_t keep = (n == M) ? ((1u << M) - 1u) : keep_mask_group<M>(a, n);
     maskbits |= (uint64_t)keep << (g * M);
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -137,13 +137,29 @@ __global__ __launch_bounds__(256) void pack_bricks(const float* __restrict__ w, 
         npend += 2;
       }
     }
-    while (npend >= 8) {
-      cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
-      pend >>= 8;
-      npend -= 8;
+    if (plane) {
+      // plane order: store whole 16-code words (the code plane is 4-byte aligned per brick)
+      while (npend >= 32) {
+        reinterpret_cast<uint32_t*>(cdst)[cbyte >> 2] = seq_to_plane((uint32_t)pend);
+        cbyte += 4;
+        pend >>= 32;
+        npend -= 32;
+      }
+    } else {
+      while (npend >= 8) {
+        cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
+        pend >>= 8;
+        npend -= 8;
+      }
     }
   }
-  if (npend > 0) cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
+  if (npend > 0) {
+    if (plane) {
+      reinterpret_cast<uint32_t*>(cdst)[cbyte >> 2] = seq_to_plane((uint32_t)pend);
+    } else {
+      cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
+    }
+  }
   if (L.has_mask) {
     uint2* mdst = reinterpret_cast<uint2*>(mask_plane + slot * 8);
     *mdst = make_uint2((uint32_t)maskbits, (uint32_t)(maskbits >> 32));
@@ -200,8 +216,16 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
   if (code_out) {
     const int64_t b0 = brick * L.code_brick_bytes;
     const int cnt = (int)min<int64_t>(L.code_brick_bytes, crb - b0);
-    for (int i = 0; i < cnt; ++i)
-      code_out[row * crb + b0 + i] = code_plane[slot * L.code_brick_bytes + i];
+    const uint8_t* src = code_plane + slot * L.code_brick_bytes;
+    if (plane_order(L.n, L.m)) {
+      for (int i = 0; i < cnt; i += 4) {
+        const uint32_t seq = plane_to_seq(*reinterpret_cast<const uint32_t*>(src + i));
+        for (int j = 0; j < 4 && i + j < cnt; ++j)
+          code_out[row * crb + b0 + i + j] = (uint8_t)(seq >> (8 * j));
+      }
+    } else {
+      for (int i = 0; i < cnt; ++i) code_out[row * crb + b0 + i] = src[i];
+    }
   }
   if (mask_out && L.has_mask) {
     const int64_t b0 = brick * 8;
