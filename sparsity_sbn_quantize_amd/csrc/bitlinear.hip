@@ -207,14 +207,20 @@ __global__ __launch_bounds__(256) void bitlinear_gemv(
   }
 }
 
-// GEMM: a workgroup computes 256 rows x (16*CF) tokens; wave w owns 4 row fragments (64 rows).
-// The K loop (256 K per step) is software-pipelined three deep: while the MFMAs of step q run,
-// the bricks of step q+1 are decoded (one row fragment per MFMA group), the activation tile of
-// step q+1 is written to the other LDS buffer, and the global loads of step q+2 are in flight.
-// One barrier per step.
-constexpr int kRF = 4;         // 16-row fragments per wave
-constexpr int kGemmCF = 8;     // 16-token fragments per workgroup
-constexpr int kXStride = 272;  // bytes per staged token row (256 + 16 spreads the LDS banks)
+// GEMM: a workgroup of 8 waves computes 256 rows x (16*CF) tokens; wave w owns 2 row fragments
+// (32 rows) and all tokens.
+// K advances 256 per step. Activation tiles go global -> LDS directly (global_load_lds, no
+// registers) into a 3-buffer ring, two steps ahead; each token row's 16-byte chunks are stored
+// XOR-swizzled (chunk c at position c ^ (token % 16)) so that the fragment reads of 16 tokens
+// hit distinct banks. Bricks of the next step are decoded K-slice by K-slice into the A
+// registers right after the MFMAs that last read that slice, and the scheduler is asked to
+// interleave that decode with the MFMAs. One barrier per step.
+constexpr int kGemmWaves = 8;   // waves per workgroup: two per SIMD, so that one wave's decode
+                                // and LDS traffic overlap the other's MFMAs
+constexpr int kRF = 2;          // 16-row fragments per wave (256 rows per workgroup)
+constexpr int kGemmCF = 8;      // 16-token fragments per workgroup (128 tokens)
+constexpr int kXBufs = 3;       // activation ring depth
+constexpr int kGemmThreads = kGemmWaves * 64;
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). The linear block
 // id is remapped so that every XCD receives one contiguous run of tiles in a grouped order
@@ -235,14 +241,22 @@ __device__ __forceinline__ void xcd_tile(int nblocks, int bid, int tiles_n, int 
   tile_t = group * kTileGroup + r % gsize;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt immediate that waits until at most `n` vector-memory operations are outstanding and
+// does not wait on LDS/scalar or export counters (gfx9 encoding: vmcnt split over bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
 template <int N, int M, int CBB, int CF, bool XVEC>
-__global__ __launch_bounds__(256, 1) void bitlinear_gemm(
+__global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
     const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
     int out_kind, int tiles_n, int tiles_t) {
   constexpr int kTok = CF * 16;
-  constexpr int kXChunks = kTok * 16 / 256;  // 16-byte activation chunks per thread per K step
+  constexpr int kTileBytes = kTok * kQuadK;  // one step's activation tile (no padding)
+  constexpr int kXLoads = kTok * 16 / kGemmThreads;  // 16-byte pieces per thread per step
   constexpr bool kSel = N > 0 && N < M;      // sparse fast path: selector table in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint2* sel_tab = reinterpret_cast<uint2*>(smem);
@@ -250,13 +264,17 @@ __global__ __launch_bounds__(256, 1) void bitlinear_gemm(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int tile_n, tile_t;
   xcd_tile((int)gridDim.x, (int)blockIdx.x, tiles_n, tiles_t, tile_n, tile_t);
-  const int64_t rb0 = ((int64_t)tile_n * 4 + wave) * kRF;
+  const int64_t rb0 = ((int64_t)tile_n * kGemmWaves + wave) * kRF;
   const int64_t t0 = (int64_t)tile_t * kTok;
   const int64_t nq = L.quads;
   const int K = (int)L.K;
-  // Rows past n_out and tokens past T read valid (clamped) data; their results are not stored,
-  // so the steady-state loop has no per-load branches.
+  const bool has_mask = N > 0 ? N < M : L.has_mask != 0;
   const int cbb = CBB > 0 ? CBB : L.code_brick_bytes;  // code bytes per brick
+
+  if constexpr (kSel) fill_sel_table(sel_tab);
+  const uint2* sel = sel_tab + (lane & 15);
+
+  // Brick addresses (rows past n_out are clamped: valid reads, results never stored).
   const uint8_t* mrow[kRF];
   const uint8_t* crow[kRF];
 #pragma unroll
@@ -265,33 +283,24 @@ __global__ __launch_bounds__(256, 1) void bitlinear_gemm(
     mrow[rf] = mask_plane + ((rb * nq) << 6 | lane) * 8;
     crow[rf] = code_plane + ((rb * nq) << 6 | lane) * cbb;
   }
-  if constexpr (kSel) fill_sel_table(sel_tab);
-  const uint2* sel = sel_tab + (lane & 15);
-  const int8_t* xrow[kXChunks];
+  // This thread's activation pieces: wave-instruction i covers 4 tokens (lane / 16) x 16 chunk
+  // positions (lane % 16); position p of token `tok` holds global chunk p ^ (tok % 16). Tokens
+  // past T are clamped (never stored).
+  const int8_t* xrow[kXLoads];
+  int xchunk[kXLoads];
 #pragma unroll
-  for (int i = 0; i < kXChunks; ++i) {
-    const int c = threadIdx.x + i * 256;
-    xrow[i] = xq + min<int64_t>(t0 + (c >> 4), T - 1) * ld_q + (c & 15) * 16;
+  for (int i = 0; i < kXLoads; ++i) {
+    const int tok = 4 * (wave * kXLoads + i) + (lane >> 4);
+    xchunk[i] = ((lane & 15) ^ (tok & 15)) * 16;
+    xrow[i] = xq + min<int64_t>(t0 + tok, T - 1) * ld_q;
   }
-
   typedef uint32_t Bricks[kRF][6];  // per row fragment: mask words 0-1, code words 2-5
-  typedef uint32_t Frags[kRF][16];  // decoded A operands
-  v4i xr[kXChunks];
-  auto load_step = [&](int64_t q, Bricks& bk) {
-#pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
-      const int ch = (threadIdx.x + i * 256) & 15;
-      if constexpr (XVEC) {
-        xr[i] = load_x16_clamped(xrow[i] - ch * 16, (int)q * kQuadK + ch * 16, K);
-      } else {
-        xr[i] = load_x16<false>(xrow[i] - ch * 16, (int)q * kQuadK + ch * 16, K);
-      }
-    }
+  auto load_bricks = [&](int64_t q, Bricks& bk) {
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
       const int64_t off = q << 6;  // slots advance by 64 per K step
       bk[rf][0] = bk[rf][1] = 0;
-      if (N > 0 ? N < M : L.has_mask) {
+      if (has_mask) {
         const uint2 m = *reinterpret_cast<const uint2*>(mrow[rf] + off * 8);
         bk[rf][0] = m.x;
         bk[rf][1] = m.y;
@@ -312,18 +321,34 @@ __global__ __launch_bounds__(256, 1) void bitlinear_gemm(
       }
     }
   };
-  auto store_x = [&](int buf) {
-    int8_t* xs = xs0 + buf * (kTok * kXStride);
+  auto load_x = [&](int64_t q) {  // step q's activation tile -> ring slot q % kXBufs
+    int8_t* dst = xs0 + (int)(q % kXBufs) * kTileBytes;
+    const int kq = (int)q * kQuadK;
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
-      const int c = threadIdx.x + i * 256;
-      *reinterpret_cast<v4i*>(xs + (c >> 4) * kXStride + (c & 15) * 16) = xr[i];
+    for (int i = 0; i < kXLoads; ++i) {
+      int8_t* d = dst + (wave * kXLoads + i) * 1024;
+      if constexpr (XVEC) {
+        // chunks past K read in-row data (K >= 16 here); the weights at those positions are 0
+        const int k = min(kq + xchunk[i], K - 16);
+        __builtin_amdgcn_global_load_lds((const void*)(xrow[i] + k), (lds_ptr)d, 16, 0, 0);
+      } else {
+        *reinterpret_cast<v4i*>(d + lane * 16) = load_x16<false>(xrow[i], kq + xchunk[i], K);
+      }
     }
   };
-  auto decode_rf = [&](const Bricks& bk, int rf, uint32_t* out) {
+  auto decode_slice = [&](const Bricks& bk, int rf, int j, uint32_t* out) {
     const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
     const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
-    decode<N, M>(L, sel, m, c, out);
+    if constexpr (N > 0) {
+      decode_slice_sel<N, M>(sel, m, c, j, out);
+    } else {
+      uint32_t tmp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmp[i] = 0;
+      decode_brick_plain(m, c, L.n, L.m, L.has_mask, tmp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = tmp[4 * j + i];
+    }
   };
 
   v4i acc[kRF][CF];
@@ -331,102 +356,123 @@ __global__ __launch_bounds__(256, 1) void bitlinear_gemm(
   for (int rf = 0; rf < kRF; ++rf)
 #pragma unroll
     for (int cf = 0; cf < CF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
-  const int8_t* xlane = xs0 + (lane & 15) * kXStride + (lane >> 4) * kBrickK;
-  auto mfma_group = [&](const int8_t* xb, int j, const Frags& a) {
+  // Fragment read offsets: token cf*16 + t (t = lane % 16), global chunk 4*(lane/16) + j.
+  const int t_l = lane & 15, g_l = lane >> 4;
+  int boff[4];
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) {
-      const v4i bv = *reinterpret_cast<const v4i*>(xb + cf * 16 * kXStride + 16 * j);
+  for (int j = 0; j < 4; ++j) boff[j] = t_l * kQuadK + (((4 * g_l + j) ^ t_l) * 16);
+  // Vector-memory operations issued per step (activation pieces + brick loads).
+  constexpr int kStepLoads = kXLoads + kRF * (N > 0 ? (N < M ? 2 : 1) : 0);
+
+  uint32_t a[kRF][16];
+  Bricks b0, b1;
+  load_bricks(0, b0);
+  load_x(0);
+  load_bricks(min<int64_t>(1, nq - 1), b1);
+  load_x(min<int64_t>(1, nq - 1));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // ring slots of steps 0 and 1 written
+  __syncthreads();
 #pragma unroll
-      for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(a[rf] + 4 * j, bv, acc[rf][cf]);
-    }
-  };
-  // One K step q: multiply with `acur`; decode step q+1 (bricks `bdec`) into `anext` between the
-  // MFMA groups; stage step q+1's activations; load step q+2 into `bload`.
-  auto step = [&](int64_t q, const Frags& acur, Frags& anext, const Bricks& bdec, Bricks& bload) {
-    const int8_t* xb = xlane + (q & 1) * (kTok * kXStride);
-    store_x((int)((q + 1) & 1));
-    load_step(min<int64_t>(q + 2, nq - 1), bload);
+  for (int rf = 0; rf < kRF; ++rf)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) decode_slice(b0, rf, j, a[rf] + 4 * j);
+
+  // Step q (its A slices 0-2 already decoded, its bricks in `bcur`):
+  //   MFMA group 0 while decoding slice 3 of step q (bcur); then the loads of step q+2 go out
+  //   (bricks into bcur, now free; activations into ring slot (q+2) % 3);
+  //   MFMA group j (j = 1..3) while decoding slice j-1 of step q+1 (bnext) into the registers
+  //   that group j-1 has finished with.
+  // Activation fragments are read one MFMA batch ahead. Before the closing barrier each wave
+  // waits for its own step-(q+1) activation pieces (issued during step q-1): only the kStepLoads
+  // operations issued in this step may still be in flight.
+  auto step = [&](int64_t q, Bricks& bcur, const Bricks& bnext, bool has_next) {
+    const int8_t* xt = xs0 + (int)(q % kXBufs) * kTileBytes;
+    const bool prefetch = q + 2 < nq;
+    v4i bv = *reinterpret_cast<const v4i*>(xt + boff[0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      mfma_group(xb, j, acur);
-      decode_rf(bdec, j, anext[j]);  // kRF == 4: one fragment per MFMA group
-      // Ask the scheduler to interleave: per activation fragment one LDS read, its kRF MFMAs,
-      // a share of the decode's VALU work and one selector read.
 #pragma unroll
       for (int cf = 0; cf < CF; ++cf) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);    // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        const int nj = cf + 1 < CF ? j : j + 1, ncf = cf + 1 < CF ? cf + 1 : 0;
+        v4i bn = bv;
+        if (nj < 4) bn = *reinterpret_cast<const v4i*>(xt + ncf * 16 * kQuadK + boff[nj]);
+#pragma unroll
+        for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(a[rf] + 4 * j, bv, acc[rf][cf]);
+        bv = bn;
       }
+      if (j == 0) {
+#pragma unroll
+        for (int rf = 0; rf < kRF; ++rf) decode_slice(bcur, rf, 3, a[rf] + 12);
+      } else if (has_next) {
+#pragma unroll
+        for (int rf = 0; rf < kRF; ++rf) decode_slice(bnext, rf, j - 1, a[rf] + 4 * (j - 1));
+      }
+#pragma unroll
+      for (int cf = 0; cf < CF; ++cf) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);        // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 + 2 * kRF, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // LDS read
+      }
+      if (j == 0 && prefetch) {
+        load_bricks(q + 2, bcur);
+        load_x(q + 2);
+      }
+    }
+    if (prefetch && N > 0 && XVEC) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepLoads));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     __syncthreads();
   };
-  auto last_step = [&](int64_t q, const Frags& acur) {
-    const int8_t* xb = xlane + (q & 1) * (kTok * kXStride);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mfma_group(xb, j, acur);
-  };
-
-  Bricks b0, b1;
-  Frags a0, a1;
-  load_step(0, b0);
-  store_x(0);
-  __syncthreads();
-#pragma unroll
-  for (int rf = 0; rf < kRF; ++rf) decode_rf(b0, rf, a0[rf]);
-  load_step(min<int64_t>(1, nq - 1), b1);
-  // Register sets alternate between consecutive steps, so nothing is copied.
   int64_t q = 0;
   for (; q + 2 < nq; q += 2) {
-    step(q, a0, a1, b1, b0);
-    step(q + 1, a1, a0, b0, b1);
+    step(q, b0, b1, true);
+    step(q + 1, b1, b0, true);
   }
   if (q + 1 < nq) {
-    step(q, a0, a1, b1, b0);
-    last_step(q + 1, a1);
+    step(q, b0, b1, true);
+    step(q + 1, b1, b0, false);
   } else {
-    last_step(q, a0);
+    step(q, b0, b1, false);
   }
 
   const float gamma = gamma_p[0];
-  const int g = lane >> 4;
   // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte store when the
   // output rows are 16-byte aligned and all 4 rows exist.
   const bool vec_out = (((uintptr_t)y | (uintptr_t)(ld_y * 4)) & 15) == 0;
 #pragma unroll
   for (int cf = 0; cf < CF; ++cf) {
-    const int64_t t = t0 + cf * 16 + (lane & 15);
+    const int64_t t = t0 + cf * 16 + t_l;
     if (t >= T) continue;
-    const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
+    const float step_t = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
-      const int64_t r0 = (rb0 + rf) * 16 + 4 * g;
+      const int64_t r0 = (rb0 + rf) * 16 + 4 * g_l;
       const v4i v = acc[rf][cf];
       if (vec_out && r0 + 4 <= L.n_out) {
         if (out_kind == SBN_OUT_I32_ACC) {
           *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + r0) = v;
         } else {
           float4 f;
-          f.x = __fmul_rn(__fmul_rn((float)v[0], gamma), step);
-          f.y = __fmul_rn(__fmul_rn((float)v[1], gamma), step);
-          f.z = __fmul_rn(__fmul_rn((float)v[2], gamma), step);
-          f.w = __fmul_rn(__fmul_rn((float)v[3], gamma), step);
+          f.x = __fmul_rn(__fmul_rn((float)v[0], gamma), step_t);
+          f.y = __fmul_rn(__fmul_rn((float)v[1], gamma), step_t);
+          f.z = __fmul_rn(__fmul_rn((float)v[2], gamma), step_t);
+          f.w = __fmul_rn(__fmul_rn((float)v[3], gamma), step_t);
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + r0) = f;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (r0 + i < L.n_out) store_out(y, ld_y, out_kind, t, r0 + i, v[i], gamma, step);
+          if (r0 + i < L.n_out) store_out(y, ld_y, out_kind, t, r0 + i, v[i], gamma, step_t);
       }
     }
   }
 }
 
-
 template <int N, int M, int CF>
 constexpr size_t gemm_smem_bytes() {
-  return (N > 0 && N < M ? 32768 : 0) + 2 * (size_t)CF * 16 * kXStride;
+  return (N > 0 && N < M ? 32768 : 0) + (size_t)kXBufs * CF * 16 * kQuadK;
 }
 
 // Raises a kernel's dynamic-LDS limit once per process (gfx950 has 160 KB of LDS per CU).
@@ -466,9 +512,10 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   constexpr size_t smem = gemm_smem_bytes<N, M, CF>();
   hipError_t e = allow_smem(bitlinear_gemm<N, M, CBB, CF, XVEC>, smem);
   if (e != hipSuccess) return e;
-  const int64_t gx = (L.row_blocks + 4 * kRF - 1) / (4 * kRF);
+  const int64_t gx = (L.row_blocks + kGemmWaves * kRF - 1) / (kGemmWaves * kRF);
   const int64_t gy = (T + CF * 16 - 1) / (CF * 16);
-  hipLaunchKernelGGL((bitlinear_gemm<N, M, CBB, CF, XVEC>), dim3((unsigned)(gx * gy)), dim3(256),
+  hipLaunchKernelGGL((bitlinear_gemm<N, M, CBB, CF, XVEC>), dim3((unsigned)(gx * gy)),
+                     dim3(kGemmThreads),
                      smem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
                      out_kind, (int)gx, (int)gy);
   return hipGetLastError();

@@ -175,6 +175,53 @@ __device__ __forceinline__ void decode_brick_sel(const uint2* __restrict__ sel,
   }
 }
 
+// Decodes K-slice j (positions 16j..16j+15, the A operand of MFMA j) of one brick for the fast
+// patterns; same arithmetic as decode_brick_sel, restricted to one slice so that a caller can
+// overwrite slice j of its A registers as soon as MFMA j has consumed them.
+template <int N, int M>
+__device__ __forceinline__ void decode_slice_sel(const uint2* __restrict__ sel,
+                                                 const uint32_t mask[2], const uint32_t codes[4],
+                                                 int j, uint32_t out[4]) {
+  auto conv = [&](int k) -> uint32_t {  // codes [4k, 4k+4) of the brick as int8 bytes
+    return __builtin_amdgcn_perm(0u, 0xFF000100u, (codes[k >> 2] >> (2 * (k & 3))) & 0x03030303u);
+  };
+  if constexpr (N == M) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = conv(4 * j + i);
+  } else if constexpr (M == 4 || (M == 8 && N == 4)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = 2 * j + hh;
+      const uint32_t m8 = (mask[h >> 2] >> (8 * (h & 3))) & 0xFFu;
+      const uint2 s = sel[m8 * 16];
+      const uint32_t c = conv(h);
+      out[2 * hh] = __builtin_amdgcn_perm(0u, c, s.x);
+      out[2 * hh + 1] = __builtin_amdgcn_perm(0u, c, s.y);
+    }
+  } else if constexpr (M == 8 && N == 6) {
+    const uint32_t c0 = conv(3 * j), c1 = conv(3 * j + 1), c2 = conv(3 * j + 2);
+    const int g0 = 2 * j, g1 = 2 * j + 1;
+    const uint2 s0 = sel[((mask[g0 >> 2] >> (8 * (g0 & 3))) & 0xFFu) * 16];
+    const uint2 s1 = sel[((mask[g1 >> 2] >> (8 * (g1 & 3))) & 0xFFu) * 16];
+    out[0] = __builtin_amdgcn_perm(c1, c0, s0.x);
+    out[1] = __builtin_amdgcn_perm(c1, c0, s0.y);
+    const uint32_t lo = __builtin_amdgcn_alignbyte(c2, c1, 2), hi = c2 >> 16;
+    out[2] = __builtin_amdgcn_perm(hi, lo, s1.x);
+    out[3] = __builtin_amdgcn_perm(hi, lo, s1.y);
+  } else if constexpr (M == 16 && N == 8) {
+    const uint32_t c0 = conv(2 * j), c1 = conv(2 * j + 1);
+    const uint32_t m16 = (mask[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t lo8 = m16 & 0xFFu, hi8 = m16 >> 8;
+    const uint2 sl = sel[lo8 * 16];
+    const uint2 sh = sel[hi8 * 16];
+    out[0] = __builtin_amdgcn_perm(c1, c0, sl.x);
+    out[1] = __builtin_amdgcn_perm(c1, c0, sl.y);
+    const uint64_t win = ((((uint64_t)c1 << 32) | c0) >> ((8 * __builtin_popcount(lo8)) & 63));
+    out[2] = __builtin_amdgcn_perm((uint32_t)(win >> 32), (uint32_t)win, sh.x);
+    out[3] = __builtin_amdgcn_perm((uint32_t)(win >> 32), (uint32_t)win, sh.y);
+  }
+}
+
 // Patterns decoded by decode_brick_sel.
 __host__ __device__ constexpr bool sel_fast_path(int n, int m) {
   return n == m || (m == 4 && n == 2) || (m == 8 && (n == 4 || n == 6)) || (m == 16 && n == 8);
