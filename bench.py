@@ -303,6 +303,98 @@ def cpu_prefill(x_bits, w, n, m, K, N, seconds):
                       f"{el:.1f} s"}
 
 
+def run_block(gpu, args, pattern, T, steps):
+    """2B-style block: Q, K, V, O, gate, up, down BitLinears at T tokens for one n:m pattern; one
+    step quantizes each distinct layer input and runs all seven forwards."""
+    from sparsity_sbn_quantize_amd import inputs
+    torch = gpu.torch
+    wl = inputs.W_BLOCK
+    n, m = pattern
+    layers = wl.layers
+    acts = {}
+    for layer in layers:
+        if layer.act_input not in acts:
+            xb = inputs.activations(wl, layer.act_input, T, layer.k)
+            acts[layer.act_input] = (gpu.bf16(xb),
+                                     torch.empty((T, layer.k), dtype=torch.int8, device="cuda"),
+                                     torch.empty((T,), dtype=torch.float32, device="cuda"))
+    wds = gpu.block_weights
+    ys = [torch.empty((T, l.n_out), dtype=torch.float32, device="cuda") for l in layers]
+    weight_bytes = sum(rpf_bytes(l.n_out, l.k, n, m) for l in layers)
+    # cold HBM for the memory-bound decode shapes: distinct packed copies of the whole block
+    R = max(1, -(-args.rotate_bytes // weight_bytes)) if T <= 16 else 1
+    packed = [[gpu.b.PackedWeight(wds[i], n, m) for i in range(len(layers))] for _ in range(R)]
+
+    def step(i):
+        pw = packed[i % len(packed)]
+        for (xd, q, a) in acts.values():
+            gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+        for li, layer in enumerate(layers):
+            _, q, a = acts[layer.act_input]
+            gpu.b.bitlinear(q, a, pw[li], out="f32", y=ys[li])
+
+    step(0)
+    g = gpu.graph(step, steps)
+    g.replay()
+    ms = gpu.time_graph(g) / steps
+    ops = sum(2.0 * T * l.k * l.n_out for l in layers)
+    fb = sum(forward_bytes(T, l.k, l.n_out, n, m) for l in layers)
+    qb = sum(quantize_bytes(T, layers[[l.act_input for l in layers].index(ai)].k) for ai in acts)
+    for pw in packed:
+        for p_ in pw:
+            p_.free()
+    return {"pattern": f"{n}:{m}", "tokens": T, "ms_per_step": ms,
+            "TOPS": ops / (ms * 1e-3) / 1e12, "GBps": (fb + qb) / (ms * 1e-3) / 1e9,
+            "weight_bytes": weight_bytes}
+
+
+def run_train(gpu, args, layer_index, pattern, steps):
+    """7B-style dynamic-sparsity training step, forward part: re-pack the fp32 latent weights
+    (absmean + n:m mask + ternary codes), quantize the 8192-token input, n:m GEMM."""
+    from sparsity_sbn_quantize_amd import inputs
+    torch = gpu.torch
+    wl = inputs.W_TRAIN
+    layer = wl.layers[layer_index]
+    n, m = pattern
+    T = wl.tokens[0]
+    K, N = layer.k, layer.n_out
+    x_bits, w = inputs.layer_inputs(wl, layer_index, T)
+    xd, wd = gpu.bf16(x_bits), gpu.f32(w)
+    del x_bits, w
+    pw = gpu.b.PackedWeight(wd, n, m)
+    q = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    a = torch.empty((T,), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        pw.pack(wd)
+        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+        gpu.b.bitlinear(q, a, pw, out="f32", y=y)
+
+    def pack_only(i):
+        pw.pack(wd)
+
+    def gemm_only(i):
+        gpu.b.bitlinear(q, a, pw, out="f32", y=y)
+
+    step(0)
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("step", step), ("pack", pack_only), ("gemm", gemm_only)):
+        g = gpu.graph(fn, steps)
+        g.replay()
+        res[name] = gpu.time_graph(g) / steps
+    pb = pack_bytes(N, K, n, m)
+    ops = 2.0 * T * K * N
+    pw.free()
+    return {"layer": layer.name, "pattern": f"{n}:{m}", "tokens": T, "K": K, "n_out": N,
+            "ms_per_step": res["step"], "pack_us": res["pack"] * 1e3,
+            "pack_GBps": pb / (res["pack"] * 1e-3) / 1e9,
+            "pack_frac_hbm": pb / (res["pack"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm_us": res["gemm"] * 1e3, "gemm_TOPS": ops / (res["gemm"] * 1e-3) / 1e12,
+            "gemm_frac_int8": ops / (res["gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+
+
 def profile_copy(gpu, args):
     """A plain device copy of known size (for scaling HBM byte counters)."""
     torch = gpu.torch
@@ -321,7 +413,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "decode16", "prefill_up", "prefill_down"])
+                    choices=["decode", "decode16", "prefill_up", "prefill_down", "block", "train"])
     ap.add_argument("--rotate-bytes", type=int, default=1 << 30,
                     help="distinct packed-weight bytes rotated through (cold HBM)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -336,6 +428,18 @@ def main():
     gpu = Gpu()
     if args.profile_copy:
         profile_copy(gpu, args)
+        return
+    if args.workload == "block":
+        from sparsity_sbn_quantize_amd import inputs
+        gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
+                             for i in range(len(inputs.W_BLOCK.layers))]
+        rows = [run_block(gpu, args, pat, T, 20 if T > 16 else min(args.steps, 500))
+                for pat in inputs.W_BLOCK.patterns for T in inputs.W_BLOCK.tokens]
+        print(json.dumps({"workload": inputs.W_BLOCK.name, "rows": rows}))
+        return
+    if args.workload == "train":
+        rows = [run_train(gpu, args, li, pat, 10) for pat in ((2, 4), (8, 16)) for li in (0, 1)]
+        print(json.dumps({"workload": "train_step_7b_ffn_T8192", "rows": rows}))
         return
     if args.workload == "decode":
         res = run_decode(gpu, args, T=1)
@@ -359,6 +463,8 @@ def main():
         for li in (0, 1):
             rp = run_prefill(gpu, args, li, steps=50, with_cpu=False)
             sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
+        for li, pat in ((0, (2, 4)), (1, (8, 16))):
+            sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
         line["secondary"] = sec
     print(json.dumps(line))
 
