@@ -87,7 +87,8 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     L.K = K;
     L.n = n_keep;
     L.m = m_group;
-    L.code_brick_bytes = 16 * n_keep / m_group;
+    L.positional = sbn::positional_codes(n_keep, m_group) ? 1 : 0;
+    L.code_brick_bytes = L.positional ? 16 : 16 * n_keep / m_group;
     L.has_mask = n_keep < m_group ? 1 : 0;
     L.row_blocks = (n_out + 15) / 16;
     L.quads = ((K + sbn::kBrickK - 1) / sbn::kBrickK + 3) / 4;
@@ -203,7 +204,8 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   out->code_row_bytes = w->code_row_bytes;
   out->mask_row_bytes = w->mask_row_bytes;
   out->rpf_bytes = (size_t)w->L.n_out * (w->code_row_bytes + w->mask_row_bytes);
-  out->packed_bytes = w->mask_plane_bytes + w->code_plane_bytes;
+  out->packed_bytes = w->L.positional ? w->code_plane_bytes
+                                      : w->mask_plane_bytes + w->code_plane_bytes;
   out->device_bytes = w->base_bytes;
   return SBN_OK;
 }

@@ -8,18 +8,17 @@
 //   acc[t][r] = sum_k q[t][k] * code[r][k]                          (exact int32)
 //   y[t][r]   = fl32( fl32( fl32(acc) * gamma ) * fl32(a'_t / 127) )
 //
-// Each lane decodes one brick (64 K positions of one weight row) from its packed mask + codes
-// straight into the A operand of v_mfma_i32_16x16x64_i8: the brick's bytes [16j, 16j+16) feed
-// MFMA j of the 256-K fragment. The B operand (activations) uses the same K assignment, so the
-// products pair correctly whatever the instruction's internal K order. Decode: the brick's codes
-// (plane order) become int8 bytes with shift/and/v_perm, and each 4 output positions are one
-// v_perm of those bytes with a selector taken from a 256-entry table keyed by a mask byte,
-// replicated per lane group in LDS so that the table reads are free of bank conflicts.
+// Each lane decodes one brick (64 K positions of one weight row) straight into the A operand of
+// v_mfma_i32_16x16x64_i8: the brick's K slice j (positions 16j .. 16j+15) feeds MFMA j of the
+// 256-K fragment. The B operand (activations) uses the same K assignment, so the products pair
+// correctly whatever the instruction's internal K order. With positional codes one slice is one
+// code word and becomes int8 bytes with nine ALU ops; the kept form (2n < m) is expanded with a
+// plain loop over its mask.
 //
-//   GEMV (T <= 16): one workgroup per 16-row fragment row, its 4 waves split K; activations are
-//   read straight from global memory (they are tiny and cache-resident).
+//   GEMV (T <= 16): one workgroup per one or two 16-row fragment rows, its 4 waves split K; the
+//   activations are staged once in LDS.
 //   GEMM (T > 16): a workgroup computes 256 rows x 128 tokens; the 128 x 256 activation tile of
-//   each K step is staged in LDS and shared by the 4 waves, each wave owning 64 weight rows.
+//   each K step is staged in LDS and shared by the waves.
 #include "sbn_internal.hpp"
 
 namespace sbn {
@@ -32,45 +31,38 @@ __device__ __forceinline__ v4i mfma16(const uint32_t* a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, c, 0, 0, 0);
 }
 
-// Loads one brick's mask (8 bytes) and code bytes. CBB > 0: compile-time code bytes per brick.
-template <int CBB>
+// Loads one brick: positional codes (16 bytes), or the kept form's mask (8 bytes) and code bytes.
+template <bool POS>
 __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* __restrict__ mask_plane,
                                            const uint8_t* __restrict__ code_plane, int64_t slot,
                                            uint32_t mask[2], uint32_t codes[4]) {
   mask[0] = mask[1] = 0;
-  if (L.has_mask) {
-    const uint2 m = *reinterpret_cast<const uint2*>(mask_plane + slot * 8);
-    mask[0] = m.x;
-    mask[1] = m.y;
-  }
   codes[0] = codes[1] = codes[2] = codes[3] = 0;
-  if constexpr (CBB == 16) {
+  if constexpr (POS) {
     const uint4 c = *reinterpret_cast<const uint4*>(code_plane + slot * 16);
     codes[0] = c.x; codes[1] = c.y; codes[2] = c.z; codes[3] = c.w;
-  } else if constexpr (CBB == 12) {
-    const uint32_t* c = reinterpret_cast<const uint32_t*>(code_plane + slot * 12);
-    codes[0] = c[0]; codes[1] = c[1]; codes[2] = c[2];
-  } else if constexpr (CBB == 8) {
-    const uint2 c = *reinterpret_cast<const uint2*>(code_plane + slot * 8);
-    codes[0] = c.x; codes[1] = c.y;
-  } else if constexpr (CBB == 4) {
-    codes[0] = *reinterpret_cast<const uint32_t*>(code_plane + slot * 4);
   } else {
+    if (L.has_mask) {
+      const uint2 m = *reinterpret_cast<const uint2*>(mask_plane + slot * 8);
+      mask[0] = m.x;
+      mask[1] = m.y;
+    }
     const int cbb = L.code_brick_bytes;
     const uint8_t* c = code_plane + slot * cbb;
     for (int i = 0; i < cbb; ++i) codes[i >> 2] |= (uint32_t)c[i] << (8 * (i & 3));
   }
 }
 
-template <int N, int M>
-__device__ __forceinline__ void decode(const Layout& L, const uint2* sel, const uint32_t mask[2],
+template <bool POS>
+__device__ __forceinline__ void decode(const Layout& L, const uint32_t mask[2],
                                        const uint32_t codes[4], uint32_t out[16]) {
-  if constexpr (N > 0) {
-    decode_brick_sel<N, M>(sel, mask, codes, out);
+  if constexpr (POS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[j], out + 4 * j);
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) out[i] = 0;
-    decode_brick_plain(mask, codes, L.n, L.m, L.has_mask, out);
+    decode_kept_brick(mask, codes, L.n, L.m, L.has_mask, out);
   }
 }
 
@@ -119,14 +111,12 @@ constexpr int kGemvChunk = 4;                       // K steps per wave per chun
 constexpr int kGemvChunkK = 4 * kGemvChunk * kQuadK;  // 4096
 constexpr int kGemvXStride = kGemvChunkK + 16;
 
-template <int N, int M, int CBB, bool XVEC, int RB>
+template <bool POS, bool XVEC, int RB>
 __global__ __launch_bounds__(256) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
     const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
     int out_kind) {
-  constexpr bool kSel = N > 0 && N < M;  // sparse fast path: selector table in LDS
-  __shared__ uint2 sel_tab[kSel ? 4096 : 1];
   __shared__ v4i red[3][RB][64];
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [T][kGemvXStride]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -148,7 +138,7 @@ __global__ __launch_bounds__(256) void bitlinear_gemv(
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         if (q < L.quads && rb0 + r < L.row_blocks) {
-          load_brick<CBB>(L, mask_plane, code_plane, (((rb0 + r) * L.quads + q) << 6) | lane,
+          load_brick<POS>(L, mask_plane, code_plane, (((rb0 + r) * L.quads + q) << 6) | lane,
                           mask[i][r], codes[i][r]);
         } else {
           mask[i][r][0] = mask[i][r][1] = 0;
@@ -164,11 +154,7 @@ __global__ __launch_bounds__(256) void bitlinear_gemv(
       *reinterpret_cast<v4i*>(xs + tok * kGemvXStride + ch * 16) =
           load_x16<XVEC>(xq + tok * ld_q, k0 + ch * 16, (int)L.K);
     }
-    if constexpr (kSel) {
-      if (c == 0) fill_sel_table(sel_tab);
-    }
     __syncthreads();
-    const uint2* sel = sel_tab + (lane & 15);
     const int8_t* xb = xs + (tok_ok ? t : 0) * kGemvXStride + g * kBrickK;
 #pragma unroll
     for (int i = 0; i < kGemvChunk; ++i) {
@@ -182,7 +168,7 @@ __global__ __launch_bounds__(256) void bitlinear_gemv(
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
           uint32_t a[16];
-          decode<N, M>(L, sel, mask[i][r], codes[i][r], a);
+          decode<POS>(L, mask[i][r], codes[i][r], a);
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[r] = mfma16(a + 4 * j, b[j], acc[r]);
         }
@@ -248,7 +234,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-template <int N, int M, int CBB, int CF, bool XVEC>
+template <bool POS, int CF, bool XVEC>
 __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
@@ -257,10 +243,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
   constexpr int kTok = CF * 16;
   constexpr int kTileBytes = kTok * kQuadK;  // one step's activation tile (no padding)
   constexpr int kXLoads = kTok * 16 / kGemmThreads;  // 16-byte pieces per thread per step
-  constexpr bool kSel = N > 0 && N < M;      // sparse fast path: selector table in LDS
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint2* sel_tab = reinterpret_cast<uint2*>(smem);
-  int8_t* xs0 = reinterpret_cast<int8_t*>(smem + (kSel ? 32768 : 0));
+  int8_t* xs0 = reinterpret_cast<int8_t*>(smem);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int tile_n, tile_t;
   xcd_tile((int)gridDim.x, (int)blockIdx.x, tiles_n, tiles_t, tile_n, tile_t);
@@ -268,11 +252,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
   const int64_t t0 = (int64_t)tile_t * kTok;
   const int64_t nq = L.quads;
   const int K = (int)L.K;
-  const bool has_mask = N > 0 ? N < M : L.has_mask != 0;
-  const int cbb = CBB > 0 ? CBB : L.code_brick_bytes;  // code bytes per brick
-
-  if constexpr (kSel) fill_sel_table(sel_tab);
-  const uint2* sel = sel_tab + (lane & 15);
+  const bool has_mask = !POS && L.has_mask != 0;
+  const int cbb = POS ? 16 : L.code_brick_bytes;  // code bytes per brick
 
   // Brick addresses (rows past n_out are clamped: valid reads, results never stored).
   const uint8_t* mrow[kRF];
@@ -307,15 +288,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
       }
       bk[rf][2] = bk[rf][3] = bk[rf][4] = bk[rf][5] = 0;
       const uint8_t* c = crow[rf] + off * cbb;
-      if constexpr (CBB == 16) {
+      if constexpr (POS) {
         const uint4 v = *reinterpret_cast<const uint4*>(c);
         bk[rf][2] = v.x; bk[rf][3] = v.y; bk[rf][4] = v.z; bk[rf][5] = v.w;
-      } else if constexpr (CBB == 12) {
-        const uint32_t* v = reinterpret_cast<const uint32_t*>(c);
-        bk[rf][2] = v[0]; bk[rf][3] = v[1]; bk[rf][4] = v[2];
-      } else if constexpr (CBB == 8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(c);
-        bk[rf][2] = v.x; bk[rf][3] = v.y;
       } else {
         for (int i = 0; i < cbb; ++i) bk[rf][2 + (i >> 2)] |= (uint32_t)c[i] << (8 * (i & 3));
       }
@@ -337,15 +312,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
     }
   };
   auto decode_slice = [&](const Bricks& bk, int rf, int j, uint32_t* out) {
-    const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
-    const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
-    if constexpr (N > 0) {
-      decode_slice_sel<N, M>(sel, m, c, j, out);
+    if constexpr (POS) {
+      exp_word_to_i8(bk[rf][2 + j], out);
     } else {
+      const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
+      const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
       uint32_t tmp[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmp[i] = 0;
-      decode_brick_plain(m, c, L.n, L.m, L.has_mask, tmp);
+      decode_kept_brick(m, c, L.n, L.m, L.has_mask, tmp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[i] = tmp[4 * j + i];
     }
@@ -362,7 +337,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
 #pragma unroll
   for (int j = 0; j < 4; ++j) boff[j] = t_l * kQuadK + (((4 * g_l + j) ^ t_l) * 16);
   // Vector-memory operations issued per step (activation pieces + brick loads).
-  constexpr int kStepLoads = kXLoads + kRF * (N > 0 ? (N < M ? 2 : 1) : 0);
+  constexpr int kStepLoads = kXLoads + kRF;
 
   uint32_t a[kRF][16];
   Bricks b0, b1;
@@ -418,7 +393,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
         load_x(q + 2);
       }
     }
-    if (prefetch && N > 0 && XVEC) {
+    if (prefetch && POS && XVEC) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepLoads));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -470,9 +445,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
   }
 }
 
-template <int N, int M, int CF>
+template <int CF>
 constexpr size_t gemm_smem_bytes() {
-  return (N > 0 && N < M ? 32768 : 0) + (size_t)kXBufs * CF * 16 * kQuadK;
+  return (size_t)kXBufs * CF * 16 * kQuadK;
 }
 
 // Raises a kernel's dynamic-LDS limit once per process (gfx950 has 160 KB of LDS per CU).
@@ -486,7 +461,7 @@ hipError_t allow_smem(K kernel, size_t bytes) {
   return e;
 }
 
-template <int N, int M, int CBB, bool XVEC>
+template <bool POS, bool XVEC>
 hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
@@ -494,40 +469,40 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   if (T <= 16) {
     const size_t xs_bytes = (size_t)T * kGemvXStride;
     if (T <= 4) {
-      hipError_t e = allow_smem(bitlinear_gemv<N, M, CBB, XVEC, 1>, xs_bytes);
+      hipError_t e = allow_smem(bitlinear_gemv<POS, XVEC, 1>, xs_bytes);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((bitlinear_gemv<N, M, CBB, XVEC, 1>), dim3((unsigned)L.row_blocks),
+      hipLaunchKernelGGL((bitlinear_gemv<POS, XVEC, 1>), dim3((unsigned)L.row_blocks),
                          dim3(256), xs_bytes, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax,
                          T, y, ld_y, out_kind);
     } else {
-      hipError_t e = allow_smem(bitlinear_gemv<N, M, CBB, XVEC, 2>, xs_bytes);
+      hipError_t e = allow_smem(bitlinear_gemv<POS, XVEC, 2>, xs_bytes);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((bitlinear_gemv<N, M, CBB, XVEC, 2>),
+      hipLaunchKernelGGL((bitlinear_gemv<POS, XVEC, 2>),
                          dim3((unsigned)((L.row_blocks + 1) / 2)), dim3(256), xs_bytes, s, h->mask,
                          h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y, out_kind);
     }
     return hipGetLastError();
   }
   constexpr int CF = kGemmCF;
-  constexpr size_t smem = gemm_smem_bytes<N, M, CF>();
-  hipError_t e = allow_smem(bitlinear_gemm<N, M, CBB, CF, XVEC>, smem);
+  constexpr size_t smem = gemm_smem_bytes<CF>();
+  hipError_t e = allow_smem(bitlinear_gemm<POS, CF, XVEC>, smem);
   if (e != hipSuccess) return e;
   const int64_t gx = (L.row_blocks + kGemmWaves * kRF - 1) / (kGemmWaves * kRF);
   const int64_t gy = (T + CF * 16 - 1) / (CF * 16);
-  hipLaunchKernelGGL((bitlinear_gemm<N, M, CBB, CF, XVEC>), dim3((unsigned)(gx * gy)),
+  hipLaunchKernelGGL((bitlinear_gemm<POS, CF, XVEC>), dim3((unsigned)(gx * gy)),
                      dim3(kGemmThreads),
                      smem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
                      out_kind, (int)gx, (int)gy);
   return hipGetLastError();
 }
 
-template <int N, int M, int CBB>
+template <bool POS>
 hipError_t launch_pattern_x(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s) {
   const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (h->L.K % 16 == 0);
-  if (xvec) return launch_pattern<N, M, CBB, true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
-  return launch_pattern<N, M, CBB, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  if (xvec) return launch_pattern<POS, true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern<POS, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace
@@ -537,19 +512,8 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             hipStream_t s) {
   const Layout& L = h->L;
   if (L.n_out == 0 || T == 0) return hipSuccess;
-  const int n = L.n, m = L.m;
-#define SBN_CASE(NN, MM, CB)                                                                    \
-  if (n == NN && m == MM)                                                                       \
-    return launch_pattern_x<NN, MM, CB>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
-  SBN_CASE(2, 4, 8)
-  SBN_CASE(4, 4, 16)
-  SBN_CASE(4, 8, 8)
-  SBN_CASE(6, 8, 12)
-  SBN_CASE(8, 8, 16)
-  SBN_CASE(8, 16, 8)
-  SBN_CASE(16, 16, 16)
-#undef SBN_CASE
-  return launch_pattern_x<0, 0, 0>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  if (L.positional) return launch_pattern_x<true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern_x<false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace sbn

@@ -73,97 +73,115 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
   if (threadIdx.x == 0) gamma[0] = count > 0.0 ? (float)(s / count) : 0.0f;
 }
 
-// Ranks of one m-group: keep[i] iff fewer than n group members precede i in the order
-// (|w| descending, position ascending). Magnitudes compare as their fp32 bit patterns.
+// Keep mask of one m-group a[0..M): i is kept iff fewer than n group members precede it in the
+// order (|w| descending, position ascending). Magnitudes compare as fp32 bit patterns. For each
+// pair i < j exactly one precedes the other, so rank_i = #{j > i: a_j > a_i} + #{j < i: a_j >= a_i}
+// is counted with one compare per pair.
 template <int M>
-__device__ __forceinline__ uint32_t keep_mask_group(const uint32_t (&a)[M], int n) {
-  uint32_t keep = 0;
+__device__ __forceinline__ uint32_t keep_mask_group(const uint32_t* a, int n) {
+  int rank[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) rank[i] = 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
-    int rank = 0;
 #pragma unroll
-    for (int j = 0; j < M; ++j) {
-      if (j < i) rank += (a[j] >= a[i]) ? 1 : 0;
-      if (j > i) rank += (a[j] > a[i]) ? 1 : 0;
+    for (int j = i + 1; j < M; ++j) {
+      const int c = a[j] > a[i] ? 1 : 0;
+      rank[i] += c;
+      rank[j] += 1 - c;
     }
-    keep |= (rank < n ? 1u : 0u) << i;
   }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) keep |= (rank[i] < n ? 1u : 0u) << i;
   return keep;
 }
 
-// One thread per brick slot (slot order, so each wave writes one contiguous block of bricks).
-template <int M>
-__global__ __launch_bounds__(256) void pack_bricks(const float* __restrict__ w, int64_t ld_w,
-                                                   Layout L, const float* __restrict__ gamma_p,
-                                                   uint8_t* __restrict__ mask_plane,
-                                                   uint8_t* __restrict__ code_plane) {
-  const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = L.row_blocks * L.quads * 64;
-  if (slot >= total) return;
-  const int lane = (int)(slot & 63);
-  const int64_t frag = slot >> 6;
+// One workgroup per fragment (16 rows x 256 K). Thread t handles 16 consecutive positions of one
+// row: brick slot lane t / 4 (row t/4 % 16, brick t/64) and positions 16 (t % 4) .. +15 of that
+// brick, so the four threads of a row read 64 contiguous weights and the workgroup writes the
+// fragment's code words (4 bytes per thread) and mask halves (2 bytes per thread) as one
+// contiguous block each. Padding rows and positions are written as zero.
+template <int M, bool POS>
+__global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ w, int64_t ld_w,
+                                                      int vec4, Layout L,
+                                                      const float* __restrict__ gamma_p,
+                                                      uint8_t* __restrict__ mask_plane,
+                                                      uint8_t* __restrict__ code_plane) {
+  const int64_t frag = blockIdx.x;
   const int64_t rb = frag / L.quads, bq = frag % L.quads;
-  const int64_t row = rb * 16 + (lane & 15);
-  const int64_t brick = bq * 4 + (lane >> 4);
-  const int64_t k0 = brick * kBrickK;
-  if (row >= L.n_out || k0 >= L.K) return;  // padding bricks stay zero
-  const float half = 0.5f * gamma_p[0];
-  const uint32_t half_bits = __float_as_uint(half);
-  const int n = L.n;
+  const int tid = threadIdx.x;
+  const int lane_slot = tid >> 2, word = tid & 3;
+  const int64_t row = rb * 16 + (lane_slot & 15);
+  const int64_t k0 = (bq * 4 + (lane_slot >> 4)) * kBrickK + 16 * word;
+  const int cnt = row < L.n_out ? (int)max<int64_t>(0, min<int64_t>(16, L.K - k0)) : 0;
   const float* wr = w + row * ld_w + k0;
-  const int groups = (int)min<int64_t>(kBrickK / M, (L.K - k0) / M);
-
-  uint64_t maskbits = 0;
-  uint64_t pend = 0;  // code bits not yet stored (sequence order)
-  int npend = 0;
-  uint8_t* cdst = code_plane + slot * L.code_brick_bytes;
-  const bool plane = plane_order(n, M);
-  int cbyte = 0;
-  for (int g = 0; g < groups; ++g) {
-    uint32_t a[M], sgn[M];
+  uint32_t u[16];
+  if (vec4 && cnt == 16) {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const uint32_t u = __float_as_uint(wr[g * M + i]);
-      a[i] = u & 0x7FFFFFFFu;
-      sgn[i] = u >> 31;
+    for (int v = 0; v < 4; ++v) {
+      const float4 f = reinterpret_cast<const float4*>(wr)[v];
+      u[4 * v] = __float_as_uint(f.x);
+      u[4 * v + 1] = __float_as_uint(f.y);
+      u[4 * v + 2] = __float_as_uint(f.z);
+      u[4 * v + 3] = __float_as_uint(f.w);
     }
-    const uint32_t keep = (n == M) ? ((1u << M) - 1u) : keep_mask_group<M>(a, n);
-    maskbits |= (uint64_t)keep << (g * M);
+  } else {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
+    for (int i = 0; i < 16; ++i) u[i] = i < cnt ? __float_as_uint(wr[i]) : 0u;
+  }
+  const uint32_t half_bits = __float_as_uint(0.5f * gamma_p[0]);
+  const int n = L.n;
+  uint32_t a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = u[i] & 0x7FFFFFFFu;
+  uint32_t keep = 0;
+#pragma unroll
+  for (int g = 0; g < 16 / M; ++g) {
+    uint32_t kg = (1u << M) - 1u;
+    if (n < M) kg = keep_mask_group<M>(a + g * M, n);
+    if (g * M < cnt) keep |= kg << (g * M);
+  }
+  // Ternary value of each kept position: |w| > gamma/2 (the rounding of |w|/gamma reaches 1).
+  uint32_t nz = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nz |= (a[i] > half_bits ? 1u : 0u) << i;
+  nz &= keep;
+  if constexpr (POS) {
+    uint32_t cw = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = ((nz >> i) & 1u) ? ((u[i] >> 31) ? 2u : 1u) : 0u;
+      cw |= c << (8 * (i & 3) + 2 * (i >> 2));
+    }
+    reinterpret_cast<uint32_t*>(code_plane)[frag * 256 + tid] = cw;
+  } else {
+    // Kept form: this thread's kept codes in ascending position, then the brick's four pieces
+    // are concatenated (each holds exactly 16n/M codes) by the thread of word 0.
+    uint32_t bits = 0;
+    int nb = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
       if ((keep >> i) & 1u) {
-        const uint32_t c = a[i] > half_bits ? (sgn[i] ? 3u : 1u) : 0u;
-        pend |= (uint64_t)c << npend;
-        npend += 2;
+        const uint32_t c = ((nz >> i) & 1u) ? ((u[i] >> 31) ? 3u : 1u) : 0u;
+        bits |= c << nb;
+        nb += 2;
       }
     }
-    if (plane) {
-      // plane order: store whole 16-code words (the code plane is 4-byte aligned per brick)
-      while (npend >= 32) {
-        reinterpret_cast<uint32_t*>(cdst)[cbyte >> 2] = seq_to_plane((uint32_t)pend);
-        cbyte += 4;
-        pend >>= 32;
-        npend -= 32;
-      }
-    } else {
-      while (npend >= 8) {
-        cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
-        pend >>= 8;
-        npend -= 8;
-      }
+    const int piece = 32 * n / M;  // bits per 16 positions
+    const int src = (int)(threadIdx.x & 63);
+    const uint64_t b1 = (uint32_t)__shfl(bits, src + 1, 64);
+    const uint64_t b2 = (uint32_t)__shfl(bits, src + 2, 64);
+    const uint64_t b3 = (uint32_t)__shfl(bits, src + 3, 64);
+    if (word == 0) {
+      const uint64_t all = bits | (b1 << piece) | (b2 << (2 * piece)) | (b3 << (3 * piece));
+      const int cbb = L.code_brick_bytes;
+      uint8_t* dst = code_plane + ((frag << 6) | lane_slot) * cbb;
+      for (int i = 0; i < cbb; ++i) dst[i] = (uint8_t)(all >> (8 * i));
     }
   }
-  if (npend > 0) {
-    if (plane) {
-      reinterpret_cast<uint32_t*>(cdst)[cbyte >> 2] = seq_to_plane((uint32_t)pend);
-    } else {
-      cdst[cbyte++] = (uint8_t)(pend & 0xFFu);
-    }
-  }
-  if (L.has_mask) {
-    uint2* mdst = reinterpret_cast<uint2*>(mask_plane + slot * 8);
-    *mdst = make_uint2((uint32_t)maskbits, (uint32_t)(maskbits >> 32));
-  }
+  if (L.has_mask)
+    reinterpret_cast<uint16_t*>(mask_plane)[frag * 256 + tid] = (uint16_t)keep;
 }
 
 __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* mask_plane,
@@ -192,7 +210,14 @@ __global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t*
   const int64_t slot = brick_slot(L, row, brick);
   uint32_t mask[2], codes[4], dec[16];
   load_brick(L, mask_plane, code_plane, slot, mask, codes);
-  decode_brick_plain(mask, codes, L.n, L.m, L.has_mask, dec);
+  if (L.positional) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[j], dec + 4 * j);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dec[i] = 0;
+    decode_kept_brick(mask, codes, L.n, L.m, L.has_mask, dec);
+  }
   const int64_t k0 = brick * kBrickK;
   const int cnt = (int)min<int64_t>(kBrickK, L.K - k0);
   for (int i = 0; i < cnt; ++i) {
@@ -203,7 +228,8 @@ __global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t*
 }
 
 // Reference packed format export: per row, code bytes [code_row_bytes] and mask bytes
-// [mask_row_bytes]; brick b's bits are the row stream's bytes [b*cbb, (b+1)*cbb) and [8b, 8b+8).
+// [mask_row_bytes]. Every brick holds whole groups, so brick b's kept codes are the row stream's
+// bytes [b*rcb, (b+1)*rcb) with rcb = 16n/m, and its mask the bytes [8b, 8b+8).
 __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_plane,
                                                   const uint8_t* code_plane, int64_t crb,
                                                   int64_t mrb, uint8_t* __restrict__ code_out,
@@ -214,17 +240,33 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
   const int64_t row = idx / nbricks, brick = idx % nbricks;
   const int64_t slot = brick_slot(L, row, brick);
   if (code_out) {
-    const int64_t b0 = brick * L.code_brick_bytes;
-    const int cnt = (int)min<int64_t>(L.code_brick_bytes, crb - b0);
-    const uint8_t* src = code_plane + slot * L.code_brick_bytes;
-    if (plane_order(L.n, L.m)) {
-      for (int i = 0; i < cnt; i += 4) {
-        const uint32_t seq = plane_to_seq(*reinterpret_cast<const uint32_t*>(src + i));
-        for (int j = 0; j < 4 && i + j < cnt; ++j)
-          code_out[row * crb + b0 + i + j] = (uint8_t)(seq >> (8 * j));
+    const int rcb = 16 * L.n / L.m;
+    const int64_t b0 = brick * rcb;
+    const int cnt = (int)min<int64_t>(rcb, crb - b0);
+    uint8_t* dst = code_out + row * crb + b0;
+    if (L.positional) {
+      uint32_t mask[2], codes[4];
+      load_brick(L, mask_plane, code_plane, slot, mask, codes);
+      const int npos = (int)min<int64_t>(kBrickK, L.K - brick * kBrickK);
+      uint32_t acc = 0;  // pending stream bits
+      int nacc = 0, out = 0;
+      for (int p = 0; p < npos; ++p) {
+        const uint32_t kept = L.has_mask ? ((mask[p >> 5] >> (p & 31)) & 1u) : 1u;
+        if (!kept) continue;
+        const int bit = pos_bit(p);
+        acc |= ref_code(pos_value((codes[bit >> 5] >> (bit & 31)) & 3u)) << nacc;
+        nacc += 2;
+        if (nacc == 8) {
+          if (out < cnt) dst[out] = (uint8_t)acc;
+          ++out;
+          acc = 0;
+          nacc = 0;
+        }
       }
+      if (nacc > 0 && out < cnt) dst[out] = (uint8_t)acc;
     } else {
-      for (int i = 0; i < cnt; ++i) code_out[row * crb + b0 + i] = src[i];
+      const uint8_t* src = code_plane + slot * L.code_brick_bytes;
+      for (int i = 0; i < cnt; ++i) dst[i] = src[i];
     }
   }
   if (mask_out && L.has_mask) {
@@ -254,22 +296,19 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
                      L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
-  const int64_t total = L.row_blocks * L.quads * 64;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  switch (L.m) {
-    case 4:
-      hipLaunchKernelGGL(pack_bricks<4>, grid, dim3(256), 0, s, w, ld_w, L, h->gamma, h->mask,
-                         h->codes);
-      break;
-    case 8:
-      hipLaunchKernelGGL(pack_bricks<8>, grid, dim3(256), 0, s, w, ld_w, L, h->gamma, h->mask,
-                         h->codes);
-      break;
-    default:
-      hipLaunchKernelGGL(pack_bricks<16>, grid, dim3(256), 0, s, w, ld_w, L, h->gamma, h->mask,
-                         h->codes);
-      break;
+  const dim3 grid((unsigned)(L.row_blocks * L.quads));
+#define SBN_PACK(MM, POS)                                                                     \
+  hipLaunchKernelGGL((pack_fragments<MM, POS>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
+                     h->mask, h->codes)
+  const bool pos = L.positional != 0;
+  if (L.m == 4) {
+    if (pos) SBN_PACK(4, true); else SBN_PACK(4, false);
+  } else if (L.m == 8) {
+    if (pos) SBN_PACK(8, true); else SBN_PACK(8, false);
+  } else {
+    if (pos) SBN_PACK(16, true); else SBN_PACK(16, false);
   }
+#undef SBN_PACK
   return hipGetLastError();
 }
 
