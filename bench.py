@@ -145,9 +145,18 @@ def cpu_model() -> str:
 # Workloads.
 # ------------------------------------------------------------------------------------------------
 
+FUSED_MAX_T = 4  # tokens up to which sbn_bitlinear_fwd_bf16 is a single kernel
+
+
+def fused_bytes(T, K, n_out, n, m):
+    """One-kernel decode step: bf16 x read, int8 x_q and a' written, packed weights and gamma
+    read, y written."""
+    return rpf_bytes(n_out, K, n, m) + 2 * T * K + T * K + 4 * T + 4 + 4 * T * n_out
+
+
 def run_decode(gpu, args, T=1, with_cpu=True):
-    """Decode GEMV: quantize T tokens + n:m forward on weights packed once."""
-    import numpy as np
+    """Decode: quantize T tokens + n:m forward on weights packed once (sbn_bitlinear_fwd_bf16:
+    one kernel for T <= 4, else the quantize kernel and the GEMV)."""
     from sparsity_sbn_quantize_amd import inputs
     torch = gpu.torch
     wl = inputs.W_DECODE
@@ -161,10 +170,10 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     q = torch.empty((T, K), dtype=torch.int8, device="cuda")
     a = torch.empty((T,), dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    fused = T <= FUSED_MAX_T
 
     def step(i):
-        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
-        gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
+        gpu.b.bitlinear_bf16(xd, pws[i % R], out="f32", y=y, x_q=q, x_absmax=a)
 
     def gemv_only(i):
         gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
@@ -172,8 +181,17 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     def quant_only(i):
         gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
 
+    def two_call(i):
+        gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+        gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
+
+    # the step equals the two-call path bit for bit
+    two_call(0)
+    torch.cuda.synchronize()
+    y_two = y.clone()
     step(0)
     torch.cuda.synchronize()
+    assert torch.equal(y, y_two), "one-call step differs from quantize + forward"
     y_eager = y.clone()
     gw = gpu.graph(step, args.warmup) if args.warmup > 0 else None
     gs = gpu.graph(step, args.steps)
@@ -184,28 +202,35 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     ms = gpu.time_graph(gs)
     wall = time.perf_counter() - t0
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
-    gk = gpu.graph(gemv_only, args.steps)
-    gk.replay()
-    gemv_ms = gpu.time_graph(gk) / args.steps
-    gq = gpu.graph(quant_only, args.steps)
-    gq.replay()
-    quant_ms = gpu.time_graph(gq) / args.steps
-
-    fb = forward_bytes(T, K, N, n, m)
-    step_bytes = fb + quantize_bytes(T, K)
+    timings = {}
+    for name, fn in (("bitlinear_gemv", gemv_only), ("quantize_act", quant_only),
+                     ("quantize_act+bitlinear_gemv", two_call)):
+        g = gpu.graph(fn, args.steps)
+        g.replay()
+        timings[name] = gpu.time_graph(g) / args.steps
     ms_step = ms / args.steps
-    achieved = fb / (gemv_ms * 1e-3) / 1e9
+    if fused:
+        step_bytes = fused_bytes(T, K, N, n, m)
+        kname, kbytes, kms = "bitlinear_gemv (quantize fused)", step_bytes, ms_step
+        tkey = f"gemv_fused_{n}of{m}_T{T}"
+        timings["bitlinear_gemv (quantize fused)"] = ms_step
+    else:
+        step_bytes = forward_bytes(T, K, N, n, m) + quantize_bytes(T, K)
+        kname, kbytes, kms = "bitlinear_gemv", forward_bytes(T, K, N, n, m), timings["bitlinear_gemv"]
+        tkey = f"gemv_{n}of{m}_T{T}"
+    achieved = kbytes / (kms * 1e-3) / 1e9
     res = {
         "value": step_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms_step,
         "wall_s": wall,
         "config": {"workload": f"{wl.name}_T{T}", "pattern": f"{n}:{m}", "tokens": T, "K": K,
                    "n_out": N, "weights": "packed once, rotated over %d copies" % R,
+                   "step": "one kernel (quantize fused)" if fused else "quantize + GEMV kernels",
                    "step_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "bitlinear_gemv", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(f"gemv_{n}of{m}_T{T}"),
-                     "bytes_per_launch": fb, "avg_launch_us": gemv_ms * 1e3},
-        "kernels_us": {"quantize_act": quant_ms * 1e3, "bitlinear_gemv": gemv_ms * 1e3},
+                     "traffic": measured_traffic(tkey),
+                     "bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3},
+        "kernels_us": {k: v * 1e3 for k, v in timings.items()},
     }
     if with_cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_decode(x_bits, w, n, m, step_bytes, args.cpu_seconds)

@@ -100,11 +100,26 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
  *   acc[t][r] = sum_k x_q[t][k] * code[r][k]   (exact int32)
  *   y         [T][ld_y] fp32 (SBN_OUT_F32) or int32 (SBN_OUT_I32_ACC); x_absmax may be NULL
  *             for SBN_OUT_I32_ACC.
- * Requires T >= 0, ld_q >= K, ld_y >= n_out; T == 0 is a no-op.
+ * Requires T >= 0, K <= ld_q <= 2^26, ld_y >= n_out; T == 0 or n_out == 0 is a no-op.
  */
 sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_q,
                              const float* x_absmax, int64_t T, void* y, int64_t ld_y,
                              sbn_out_kind out_kind, void* stream);
+
+/*
+ * Quantize-and-multiply in one call: the per-token absmax INT8 quantization of sbn_quantize_act
+ * followed by sbn_bitlinear_fwd ("The BitLinear Layer", operations 2, 4 and 5).
+ *   x_bf16    [T][ld_x] bf16 bit patterns (uint16), read only.
+ *   x_q       [T][ld_q] int8 out and x_absmax [T] fp32 out: exactly what sbn_quantize_act writes.
+ *   y         [T][ld_y] as for sbn_bitlinear_fwd.
+ * For T <= 4 and K <= 12288 the whole call is one kernel launch, in which every workgroup
+ * quantizes the activations it needs itself; otherwise it runs the two kernels in turn.
+ * Requires T >= 0, ld_x >= K, K <= ld_q <= 2^26, ld_y >= n_out; T == 0 is a no-op; y may be
+ * NULL when n_out == 0 (x_q and x_absmax are still written).
+ */
+sbn_status sbn_bitlinear_fwd_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
+                                  int64_t T, int8_t* x_q, int64_t ld_q, float* x_absmax, void* y,
+                                  int64_t ld_y, sbn_out_kind out_kind, void* stream);
 
 /*
  * Releases a handle: waits for the last stream that used it, then frees its device memory.

@@ -43,6 +43,8 @@ _SIGNATURES = {
     "sbn_pack_nm_ternary": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_void_p), _P]),
     "sbn_bitlinear_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _P]),
+    "sbn_bitlinear_fwd_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I64,
+                                              ctypes.c_int, _P]),
     "sbn_free": (None, [_P]),
     "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
@@ -198,3 +200,25 @@ def bitlinear(x_q, x_absmax, w: PackedWeight, out: str = "f32", y=None, stream=N
     check(lib().sbn_bitlinear_fwd(w.handle, _ptr(x_q), _ld(x_q, w.K), _ptr(x_absmax), T,
                                   _ptr(y), _ld(y, w.n_out), kind, _stream(stream)))
     return y
+
+
+def bitlinear_bf16(x, w: PackedWeight, out: str = "f32", y=None, x_q=None, x_absmax=None,
+                   stream=None):
+    """Quantize-and-multiply: x bf16 [T][K] -> (y, x_q int8 [T][K], a' fp32 [T])."""
+    import torch
+    _require_cuda(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("x must be bfloat16 (or int16 bf16 bit patterns)")
+    T = x.shape[0]
+    kind = SBN_OUT_F32 if out == "f32" else SBN_OUT_I32_ACC
+    if y is None:
+        y = torch.empty((T, w.n_out), dtype=torch.float32 if kind == SBN_OUT_F32 else torch.int32,
+                        device=x.device)
+    if x_q is None:
+        x_q = torch.empty((T, w.K), dtype=torch.int8, device=x.device)
+    if x_absmax is None:
+        x_absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    check(lib().sbn_bitlinear_fwd_bf16(w.handle, _ptr(x), _ld(x, w.K), T, _ptr(x_q),
+                                       _ld(x_q, w.K), _ptr(x_absmax), _ptr(y), _ld(y, w.n_out),
+                                       kind, _stream(stream)))
+    return y, x_q, x_absmax

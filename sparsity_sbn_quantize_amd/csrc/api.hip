@@ -29,6 +29,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool pattern_ok(int n, int m) { return (m == 4 || m == 8 || m == 16) && n >= 1 && n <= m; }
 
+// The matmul kernels form 32-bit offsets of up to 16 activation rows.
+constexpr int64_t kMaxLdQ = (int64_t)1 << 26;
+
 }  // namespace
 
 extern "C" {
@@ -91,10 +94,12 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     L.code_brick_bytes = L.positional ? 16 : 16 * n_keep / m_group;
     L.has_mask = n_keep < m_group ? 1 : 0;
     L.row_blocks = (n_out + 15) / 16;
+    L.row_blocks_pad = (L.row_blocks + sbn::kPadRowBlocks - 1) / sbn::kPadRowBlocks *
+                       sbn::kPadRowBlocks;
     L.quads = ((K + sbn::kBrickK - 1) / sbn::kBrickK + 3) / 4;
     if (16 * n_keep % m_group != 0)
       return fail(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: pattern %d:%d", n_keep, m_group);
-    const size_t slots = (size_t)L.row_blocks * (size_t)L.quads * 64;
+    const size_t slots = (size_t)L.row_blocks_pad * (size_t)L.quads * 64;
     const int num_partials = sbn::absmean_blocks(n_out);
     const size_t mask_bytes = L.has_mask ? slots * 8 : 0;
     const size_t code_bytes = slots * (size_t)L.code_brick_bytes;
@@ -159,16 +164,47 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
   if (ld_q < w->L.K)
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: ld_q=%lld < K=%lld", (long long)ld_q,
                 (long long)w->L.K);
+  if (ld_q > kMaxLdQ)
+    return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd: ld_q=%lld > %lld", (long long)ld_q,
+                (long long)kMaxLdQ);
   if (ld_y < w->L.n_out)
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: ld_y=%lld < n_out=%lld",
                 (long long)ld_y, (long long)w->L.n_out);
   if (T == 0) return SBN_OK;
+  if (w->L.n_out == 0) return SBN_OK;
   if (!x_q || !y || (out_kind == SBN_OUT_F32 && !x_absmax))
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: null pointer");
   const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
   hipError_t e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
                                        (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_bitlinear_fwd_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
+                                  int64_t T, int8_t* x_q, int64_t ld_q, float* x_absmax, void* y,
+                                  int64_t ld_y, sbn_out_kind out_kind, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: handle is null");
+  if (out_kind != SBN_OUT_F32 && out_kind != SBN_OUT_I32_ACC)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: out_kind=%d", (int)out_kind);
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: T=%lld < 0", (long long)T);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd_bf16: T too large");
+  if (ld_x < w->L.K || ld_q < w->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: ld_x=%lld / ld_q=%lld < K=%lld",
+                (long long)ld_x, (long long)ld_q, (long long)w->L.K);
+  if (ld_q > kMaxLdQ)
+    return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd_bf16: ld_q=%lld > %lld", (long long)ld_q,
+                (long long)kMaxLdQ);
+  if (ld_y < w->L.n_out)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: ld_y=%lld < n_out=%lld",
+                (long long)ld_y, (long long)w->L.n_out);
+  if (T == 0) return SBN_OK;
+  if (!x_bf16 || !x_q || !x_absmax || (!y && w->L.n_out > 0))
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: null pointer");
+  const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
+  hipError_t e = sbn::launch_bitlinear_bf16(w, x_bf16, ld_x, T, x_q, ld_q, x_absmax, y, ld_y,
+                                            (int)out_kind, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd_bf16 launch");
   return SBN_OK;
 }
 

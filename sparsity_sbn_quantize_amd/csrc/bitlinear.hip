@@ -19,6 +19,8 @@
 //   activations are staged once in LDS.
 //   GEMM (T > 16): a workgroup computes 256 rows x 128 tokens; the 128 x 256 activation tile of
 //   each K step is staged in LDS and shared by the waves.
+#include <algorithm>
+
 #include "sbn_internal.hpp"
 
 namespace sbn {
@@ -84,14 +86,6 @@ __device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int k, i
   }
 }
 
-// 16 activation bytes at K offset k (a multiple of 16) with the address clamped into the row:
-// bytes at k >= K are arbitrary row data, which is harmless wherever the weights at those
-// positions are zero (bricks are zero-padded past K). XVEC rows only. No value select, so the
-// load's result is not needed until it is used (no wait right after the load).
-__device__ __forceinline__ v4i load_x16_clamped(const int8_t* __restrict__ row, int k, int K) {
-  return *reinterpret_cast<const v4i*>(row + min(k, K - 16));
-}
-
 __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, int64_t t,
                                           int64_t r, int acc, float gamma, float step) {
   if (out_kind == SBN_OUT_I32_ACC) {
@@ -102,111 +96,202 @@ __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, i
   }
 }
 
-// GEMV (T <= 16): a workgroup owns RB 16-row fragment rows; its 4 waves split K (wave w takes
-// the 256-K steps w, w+4, ...). K is walked in chunks of 16 steps (4096 K): the chunk's bricks
-// are loaded first, then the chunk's activations are staged once in LDS (shared by all waves and
-// row fragments instead of being re-read from L2 by every wave), then bricks are decoded and
-// multiplied. Partial sums of the 4 waves are combined through LDS.
-constexpr int kGemvChunk = 4;                       // K steps per wave per chunk
-constexpr int kGemvChunkK = 4 * kGemvChunk * kQuadK;  // 4096
-constexpr int kGemvXStride = kGemvChunkK + 16;
+// GEMV (T <= 16): one workgroup per 16-row fragment row with W = min(16, quads) waves; wave w
+// takes the 256-K quads w, w + W, ... (at most kGemvMaxQ). Every wave first issues its brick
+// loads (HBM) and its activation loads (L2: every workgroup reads the same rows) straight into
+// MFMA operand registers, then decodes and multiplies; the partial sums of the waves are combined
+// through LDS once. Lane (t, g) supplies token t's 64 activation bytes at K offset 64g of each
+// quad, matching the K slices of the bricks.
+// FUSED (T <= 4): the activations are bf16. Every workgroup then computes the per-token absmax
+// over K itself (lane maxima, then wave maxima combined through LDS) and quantizes the pieces it
+// needs with the arithmetic of the quantize kernel, so the decode step is one launch with no int8
+// copy of the activations between two kernels; workgroup 0 also writes x_q and a' for the caller.
+// (For more tokens every workgroup would redo a quantization pass over all T x K activations;
+// there the quantize kernel followed by the GEMV is faster.)
+constexpr int kGemvMaxWaves = 16;
+constexpr int kGemvMaxQ = 3;  // quads per wave (template Q <= 3): K <= 16 * 3 * 256 = 12288
+constexpr int kFusedMaxT = 4;  // tokens of the one-kernel quantize-and-multiply path
 
-template <bool POS, bool XVEC, int RB>
-__global__ __launch_bounds__(256) void bitlinear_gemv(
-    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
-    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
-    const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
-    int out_kind) {
-  __shared__ v4i red[3][RB][64];
-  extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [T][kGemvXStride]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rb0 = (int64_t)blockIdx.x * RB;
-  const int t = lane & 15, g = lane >> 4;
-  const int Ti = (int)T;
-  const bool tok_ok = t < Ti;
-  v4i acc[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
-  uint32_t mask[kGemvChunk][RB][2], codes[kGemvChunk][RB][4];
-
-  const int nchunks = (int)((L.quads + 4 * kGemvChunk - 1) / (4 * kGemvChunk));
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t qbase = (int64_t)c * 4 * kGemvChunk;
-#pragma unroll
-    for (int i = 0; i < kGemvChunk; ++i) {
-      const int64_t q = qbase + wave + 4 * i;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (q < L.quads && rb0 + r < L.row_blocks) {
-          load_brick<POS>(L, mask_plane, code_plane, (((rb0 + r) * L.quads + q) << 6) | lane,
-                          mask[i][r], codes[i][r]);
-        } else {
-          mask[i][r][0] = mask[i][r][1] = 0;
-          codes[i][r][0] = codes[i][r][1] = codes[i][r][2] = codes[i][r][3] = 0;
-        }
-      }
-    }
-    // Stage this chunk's activations: T rows x 4096 K in 16-byte pieces.
-    const int k0 = c * kGemvChunkK;
-    if (c > 0) __syncthreads();  // previous chunk's readers are done with xs
-    for (int e = threadIdx.x; e < Ti * (kGemvChunkK / 16); e += 256) {
-      const int tok = e / (kGemvChunkK / 16), ch = e % (kGemvChunkK / 16);
-      *reinterpret_cast<v4i*>(xs + tok * kGemvXStride + ch * 16) =
-          load_x16<XVEC>(xq + tok * ld_q, k0 + ch * 16, (int)L.K);
-    }
-    __syncthreads();
-    const int8_t* xb = xs + (tok_ok ? t : 0) * kGemvXStride + g * kBrickK;
-#pragma unroll
-    for (int i = 0; i < kGemvChunk; ++i) {
-      const int64_t q = qbase + wave + 4 * i;
-      if (q < L.quads) {
-        v4i b[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = tok_ok ? *reinterpret_cast<const v4i*>(xb + (wave + 4 * i) * kQuadK + 16 * j)
-                        : v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          uint32_t a[16];
-          decode<POS>(L, mask[i][r], codes[i][r], a);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[r] = mfma16(a + 4 * j, b[j], acc[r]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-    if (wave > 0) red[wave - 1][r][lane] = acc[r];
-  __syncthreads();
-  if (wave != 0 || !tok_ok) return;
-  const float gamma = gamma_p[0];
-  const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const v4i sum = acc[r] + red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = (rb0 + r) * 16 + 4 * g + i;
-      if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
-    }
+__device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, const v4i& v) {
+  if (vec && k + 16 <= K) {
+    *reinterpret_cast<v4i*>(row + k) = v;
+  } else {
+    for (int i = 0; i < 16 && k + i < K; ++i) row[k + i] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
   }
 }
 
-// GEMM: a workgroup of 8 waves computes 256 rows x (16*CF) tokens; wave w owns 2 row fragments
-// (32 rows) and all tokens.
-// K advances 256 per step. Activation tiles go global -> LDS directly (global_load_lds, no
-// registers) into a 3-buffer ring, two steps ahead; each token row's 16-byte chunks are stored
-// XOR-swizzled (chunk c at position c ^ (token % 16)) so that the fragment reads of 16 tokens
-// hit distinct banks. Bricks of the next step are decoded K-slice by K-slice into the A
-// registers right after the MFMAs that last read that slice, and the scheduler is asked to
-// interleave that decode with the MFMAs. One barrier per step.
-constexpr int kGemmWaves = 8;   // waves per workgroup: two per SIMD, so that one wave's decode
-                                // and LDS traffic overlap the other's MFMAs
-constexpr int kRF = 2;          // 16-row fragments per wave (256 rows per workgroup)
-constexpr int kGemmCF = 8;      // 16-token fragments per workgroup (128 tokens)
-constexpr int kXBufs = 3;       // activation ring depth
+template <bool POS, bool FUSED, bool XVEC, int Q>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
+    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
+    const float* __restrict__ gamma_p, const void* __restrict__ xin, int64_t ld_x,
+    int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
+    void* __restrict__ y, int64_t ld_y, int out_kind) {
+  __shared__ v4i red[kGemvMaxWaves][64];
+  __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT];
+  __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
+  const int W = (int)(blockDim.x >> 6);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rb = blockIdx.x;
+  const int t = lane & 15, g = lane >> 4;
+  const bool tok_ok = t < (int)T;
+  const int K = (int)L.K, nq = (int)L.quads;
+
+  uint32_t mask[Q][2], codes[Q][4];
+  auto load_bricks = [&]() {
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int q = wave + i * W;
+      if (q < nq) {
+        load_brick<POS>(L, mask_plane, code_plane, ((rb * nq + q) << 6) | lane, mask[i],
+                        codes[i]);
+      } else {
+        mask[i][0] = mask[i][1] = 0;
+        codes[i][0] = codes[i][1] = codes[i][2] = codes[i][3] = 0;
+      }
+    }
+  };
+  v4i b[Q][4];  // B operands: 16 int8 activations per K slice
+  float a_t = 0.0f;     // a' of token t (FUSED)
+  if constexpr (!FUSED) {
+    load_bricks();
+    const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = (wave + i * W) * kQuadK + 64 * g + 16 * j;
+        b[i][j] = v4i{0, 0, 0, 0};
+        if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
+      }
+  } else {
+    // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
+    // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
+    // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
+    uint2 xv[Q][kFusedMaxT];
+    uint32_t m[kFusedMaxT];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt) m[tt] = 0;
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        const int k = (wave + i * W) * kQuadK + 4 * lane;
+        uint2 v = make_uint2(0, 0);
+        if (tt < (int)T && k < K) {
+          const uint16_t* row = xb + tt * ld_x;
+          if constexpr (XVEC) {
+            v = *reinterpret_cast<const uint2*>(row + k);
+          } else {
+            uint32_t w2[2] = {0, 0};
+            for (int u = 0; u < 4 && k + u < K; ++u) w2[u >> 1] |= (uint32_t)row[k + u] << (16 * (u & 1));
+            v = make_uint2(w2[0], w2[1]);
+          }
+        }
+        xv[i][tt] = v;
+        m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], v.x), v.y);
+      }
+    // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
+    // does not wait for the bricks: the quantization below overlaps the brick loads.
+    load_bricks();
+    const int Tn = (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+    // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
+    // over the waves through LDS.
+    uint32_t pk[kFusedMaxT / 2];
+#pragma unroll
+    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) {
+      pk[p2] = 0;
+      if (2 * p2 >= Tn) continue;
+      const uint32_t a0 = max(m[2 * p2] & 0xFFFFu, m[2 * p2] >> 16);
+      const uint32_t a1 = max(m[2 * p2 + 1] & 0xFFFFu, m[2 * p2 + 1] >> 16);
+      pk[p2] = wave_max_u16x2(a0 | (a1 << 16));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt)
+        wmax[wave][tt] = (pk[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
+    }
+    __syncthreads();
+    float s_t[kFusedMaxT];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt) {
+      s_t[tt] = 0.0f;
+      if (tt >= Tn) continue;
+      uint32_t am = 0;
+      for (int w = 0; w < W; ++w) am = max(am, wmax[w][tt]);
+      const float a = fmaxf(__uint_as_float(am << 16), kAbsmaxFloor);
+      s_t[tt] = 127.0f / a;
+      if (tt == t) a_t = a;
+    }
+    uint32_t* xs = xq_lds[wave];  // [kFusedMaxT][64] words
+    const bool vq = ((uintptr_t)xq_out % 4 == 0) && (ld_q % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int k = (wave + i * W) * kQuadK + 4 * lane;
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        if (tt >= Tn) continue;
+        const uint32_t qw = quant4(xv[i][tt].x, xv[i][tt].y, s_t[tt]);
+        xs[tt * 64 + lane] = qw;
+        if (rb == 0 && tt < (int)T && k < K) {
+          int8_t* dst = xq_out + tt * ld_q + k;
+          if (vq && k + 4 <= K) {
+            *reinterpret_cast<uint32_t*>(dst) = qw;
+          } else {
+            for (int u = 0; u < 4 && k + u < K; ++u) dst[u] = (int8_t)(qw >> (8 * u));
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[i][j] = t < kFusedMaxT && tok_ok
+                      ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 + 16 * g + 4 * j)
+                      : v4i{0, 0, 0, 0};
+    }
+    if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
+  }
+
+  v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    if (wave + i * W < nq) {
+      uint32_t a[16];
+      decode<POS>(L, mask[i], codes[i], a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || !tok_ok) return;
+  v4i sum = red[0][lane];
+  for (int w = 1; w < W; ++w) sum += red[w][lane];
+  const float gamma = gamma_p[0];
+  const float step = out_kind == SBN_OUT_F32 ? (FUSED ? a_t : absmax[t]) / 127.0f : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = rb * 16 + 4 * g + i;
+    if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+  }
+}
+
+// GEMM (T > 16): a workgroup of 4 waves computes 256 rows x 128 tokens; wave w owns 4 row
+// fragments (64 rows) and all 128 tokens. Two workgroups share a CU (two waves per SIMD), so one
+// wave's decode and LDS traffic overlap the other's MFMAs. K advances 256 per step. Each step's
+// 128 x 256 activation tile goes global -> LDS directly (global_load_lds, no registers) into a
+// 2-slot ring, one step ahead, laid out so that every fragment read is free of bank conflicts. K slice
+// j+1 of the wave's row fragments is decoded while the MFMAs of slice j run (two A register
+// sets); bricks are loaded one step ahead. One barrier per step.
+constexpr int kGemmWaves = 4;
+constexpr int kRF = 4;                                  // 16-row fragments per wave
+constexpr int kGemmCF = 8;                              // 16-token fragments per tile
+constexpr int kGemmTok = kGemmCF * 16;                  // 128 tokens per tile
+constexpr int kGemmRowBlocks = kGemmWaves * kRF;        // 16 row fragments (256 rows) per tile
+constexpr int kXBufs = 2;                               // activation ring depth
 constexpr int kGemmThreads = kGemmWaves * 64;
+constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile (32 KB)
+constexpr int kXLoads = kGemmTok * 16 / kGemmThreads;   // 16-byte pieces per thread per step
+constexpr size_t kGemmSmem = (size_t)kXBufs * kTileBytes;
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). The linear block
 // id is remapped so that every XCD receives one contiguous run of tiles in a grouped order
@@ -229,195 +314,204 @@ __device__ __forceinline__ void xcd_tile(int nblocks, int bid, int tiles_n, int 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no stride): offsets are
+// bytes and reads at or past num_records return zero.
+constexpr int kBufDword3 = 0x00020000;
+
 // s_waitcnt immediate that waits until at most `n` vector-memory operations are outstanding and
 // does not wait on LDS/scalar or export counters (gfx9 encoding: vmcnt split over bits 3:0 and
 // 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-template <bool POS, int CF, bool XVEC>
-__global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
-    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
-    const float* __restrict__ gamma_p, const int8_t* __restrict__ xq, int64_t ld_q,
-    const float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y,
-    int out_kind, int tiles_n, int tiles_t) {
-  constexpr int kTok = CF * 16;
-  constexpr int kTileBytes = kTok * kQuadK;  // one step's activation tile (no padding)
-  constexpr int kXLoads = kTok * 16 / kGemmThreads;  // 16-byte pieces per thread per step
+template <bool POS, bool XVEC>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
+                    Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
+                    int64_t ld_q, const float* __restrict__ absmax, int64_t T,
+                    void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t) {
+  constexpr int kBW = POS ? 4 : 6;  // brick words in registers: codes, or mask (2) + codes (4)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int8_t* xs0 = reinterpret_cast<int8_t*>(smem);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int8_t* const xs0 = reinterpret_cast<int8_t*>(smem);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+  const int lane = threadIdx.x & 63;
   int tile_n, tile_t;
   xcd_tile((int)gridDim.x, (int)blockIdx.x, tiles_n, tiles_t, tile_n, tile_t);
   const int64_t rb0 = ((int64_t)tile_n * kGemmWaves + wave) * kRF;
-  const int64_t t0 = (int64_t)tile_t * kTok;
-  const int64_t nq = L.quads;
+  const int64_t t0 = (int64_t)tile_t * kGemmTok;
+  const int nq = (int)L.quads;
   const int K = (int)L.K;
-  const bool has_mask = !POS && L.has_mask != 0;
-  const int cbb = POS ? 16 : L.code_brick_bytes;  // code bytes per brick
+  const int cbb = POS ? 16 : L.code_brick_bytes;
 
-  // Brick addresses (rows past n_out are clamped: valid reads, results never stored).
-  const uint8_t* mrow[kRF];
-  const uint8_t* crow[kRF];
-#pragma unroll
-  for (int rf = 0; rf < kRF; ++rf) {
-    const int64_t rb = min(rb0 + rf, L.row_blocks - 1);
-    mrow[rf] = mask_plane + ((rb * nq) << 6 | lane) * 8;
-    crow[rf] = code_plane + ((rb * nq) << 6 | lane) * cbb;
-  }
+  // Brick addresses: a wave-uniform base plus lane * (brick bytes); row fragment rf and step q are
+  // uniform offsets. Stored row fragments are padded to a multiple of 16, so every tile's rows
+  // exist (the padding is zero and its results are never stored).
+  const int64_t frag0 = rb0 * nq;
+  const uint8_t* const cbase = code_plane + (frag0 << 6) * cbb;
+  const uint8_t* const mbase = POS ? nullptr : mask_plane + (frag0 << 6) * 8;
+  const int64_t rf_stride = (int64_t)nq << 6;  // slots per row fragment
+  // Positional bricks go through a buffer resource (base in scalar registers, one 32-bit lane
+  // offset): every offset a tile uses is below kRF * nq * 1024 bytes <= 2 MB.
+  const __amdgpu_buffer_rsrc_t crsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, 0x7FFFFFFF, kBufDword3);
+  const int lane_c = lane * cbb;
   // This thread's activation pieces: wave-instruction i covers 4 tokens (lane / 16) x 16 chunk
-  // positions (lane % 16); position p of token `tok` holds global chunk p ^ (tok % 16). Tokens
-  // past T are clamped (never stored).
-  const int8_t* xrow[kXLoads];
-  int xchunk[kXLoads];
+  // positions (lane % 16); position p of token `tok` holds global chunk p ^ (tok % 16). Offsets
+  // are relative to the tile's first token row. The aligned path reads through a buffer resource
+  // whose range ends with the last activation row: pieces of tokens past T, or of the last row
+  // past K, read as zero (elsewhere a piece past K reads in-row data, harmless because the
+  // weights there are zero). Tokens past T are never stored.
+  const int8_t* const xt0 = xq + t0 * ld_q;
+  const int64_t x_extent = (T - 1 - t0) * ld_q + K;  // bytes from xt0 to the end of row T-1
+  // Activation tile layout in LDS: [16-token group cf][K chunk c (16 bytes)][token t], i.e. the
+  // 16-byte piece of token cf*16 + t at K chunk c sits at cf*4096 + c*256 + t*16. The fragment
+  // read of (slice j, group cf) then has the 16 lanes of each lane group g read 256 contiguous
+  // bytes (chunk 4g + j of tokens 0..15), which gfx950's LDS serves without bank conflicts. Wave
+  // instruction ii loads group ii / 4, chunks 4 (ii % 4) .. +3: lane l takes token l % 16, chunk
+  // 4 (ii % 4) + l / 16, i.e. 64 contiguous bytes of each of 16 token rows, and lands at
+  // 1 KB-block ii + 16 l as the layout requires. The per-instruction part of the address is
+  // uniform (folded into the instruction's buffer resource); the lane part is one offset.
+  const int xlane = (lane & 15) * (int)ld_q + (lane >> 4) * 16;
+  const int rlane = (lane >> 4) * 1024 + (lane & 15) * 16;  // fragment read offset
+  auto load_x = [&](int q, int slot) {  // step q's activation tile -> ring slot
+    int8_t* dst = xs0 + slot * kTileBytes + wave * (kXLoads * 1024);
+    const int kq = q * kQuadK;
 #pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    const int tok = 4 * (wave * kXLoads + i) + (lane >> 4);
-    xchunk[i] = ((lane & 15) ^ (tok & 15)) * 16;
-    xrow[i] = xq + min<int64_t>(t0 + tok, T - 1) * ld_q;
-  }
-  typedef uint32_t Bricks[kRF][6];  // per row fragment: mask words 0-1, code words 2-5
-  auto load_bricks = [&](int64_t q, Bricks& bk) {
+    for (int i = 0; i < kXLoads; ++i) {
+      const int ii = wave * kXLoads + i, cf = ii >> 2, c0 = (ii & 3) * 4;
+      if constexpr (XVEC) {
+        // Range ends with row T-1: pieces of tokens past T, or of the last row past K, read as
+        // zero (elsewhere a piece past K reads in-row data, harmless because the weights there
+        // are zero). Tokens past T are never stored.
+        const int64_t off0 = (int64_t)(cf * 16) * ld_q + kq + c0 * 16;  // uniform
+        const int64_t left = x_extent - off0;  // plain integer clamps keep this scalar
+        const int nrec = left <= 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(xt0 + off0), (short)0, nrec, kBufDword3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(dst + i * 1024), 16, xlane, 0, 0, 0);
+      } else {
+        const int tok = cf * 16 + (lane & 15), c = c0 + (lane >> 4);
+        const int8_t* row = xq + min<int64_t>(t0 + tok, T - 1) * ld_q;
+        *reinterpret_cast<v4i*>(dst + i * 1024 + lane * 16) = load_x16<false>(row, kq + c * 16, K);
+      }
+    }
+  };
+  typedef uint32_t Bricks[kRF][kBW];
+  auto load_bricks = [&](int q, Bricks& bk) {
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
-      const int64_t off = q << 6;  // slots advance by 64 per K step
-      bk[rf][0] = bk[rf][1] = 0;
-      if (has_mask) {
-        const uint2 m = *reinterpret_cast<const uint2*>(mrow[rf] + off * 8);
-        bk[rf][0] = m.x;
-        bk[rf][1] = m.y;
-      }
-      bk[rf][2] = bk[rf][3] = bk[rf][4] = bk[rf][5] = 0;
-      const uint8_t* c = crow[rf] + off * cbb;
+      const int64_t slot0 = rf * rf_stride + ((int64_t)q << 6);  // uniform
       if constexpr (POS) {
-        const uint4 v = *reinterpret_cast<const uint4*>(c);
-        bk[rf][2] = v.x; bk[rf][3] = v.y; bk[rf][4] = v.z; bk[rf][5] = v.w;
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(crsrc, lane_c, (int)(slot0 * 16), 0);
+        bk[rf][0] = (uint32_t)v[0]; bk[rf][1] = (uint32_t)v[1];
+        bk[rf][2] = (uint32_t)v[2]; bk[rf][3] = (uint32_t)v[3];
       } else {
+        bk[rf][0] = bk[rf][1] = 0;
+        if (L.has_mask) {
+          const uint2 m = *reinterpret_cast<const uint2*>(mbase + (slot0 + lane) * 8);
+          bk[rf][0] = m.x;
+          bk[rf][1] = m.y;
+        }
+        bk[rf][2] = bk[rf][3] = bk[rf][4] = bk[rf][5] = 0;
+        const uint8_t* c = cbase + slot0 * cbb + lane_c;
         for (int i = 0; i < cbb; ++i) bk[rf][2 + (i >> 2)] |= (uint32_t)c[i] << (8 * (i & 3));
       }
     }
   };
-  auto load_x = [&](int64_t q) {  // step q's activation tile -> ring slot q % kXBufs
-    int8_t* dst = xs0 + (int)(q % kXBufs) * kTileBytes;
-    const int kq = (int)q * kQuadK;
+  typedef uint32_t ASlice[kRF][4];
+  auto decode_slice = [&](const Bricks& bk, int j, ASlice& out) {
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-      int8_t* d = dst + (wave * kXLoads + i) * 1024;
-      if constexpr (XVEC) {
-        // chunks past K read in-row data (K >= 16 here); the weights at those positions are 0
-        const int k = min(kq + xchunk[i], K - 16);
-        __builtin_amdgcn_global_load_lds((const void*)(xrow[i] + k), (lds_ptr)d, 16, 0, 0);
+    for (int rf = 0; rf < kRF; ++rf) {
+      if constexpr (POS) {
+        exp_word_to_i8(bk[rf][j], out[rf]);
       } else {
-        *reinterpret_cast<v4i*>(d + lane * 16) = load_x16<false>(xrow[i], kq + xchunk[i], K);
+        const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
+        const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
+        uint32_t tmp[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmp[i] = 0;
+        decode_kept_brick(m, c, L.n, L.m, L.has_mask, tmp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[rf][i] = tmp[4 * j + i];
       }
     }
   };
-  auto decode_slice = [&](const Bricks& bk, int rf, int j, uint32_t* out) {
-    if constexpr (POS) {
-      exp_word_to_i8(bk[rf][2 + j], out);
-    } else {
-      const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
-      const uint32_t c[4] = {bk[rf][2], bk[rf][3], bk[rf][4], bk[rf][5]};
-      uint32_t tmp[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmp[i] = 0;
-      decode_kept_brick(m, c, L.n, L.m, L.has_mask, tmp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[i] = tmp[4 * j + i];
-    }
-  };
 
-  v4i acc[kRF][CF];
+  v4i acc[kRF][kGemmCF];
 #pragma unroll
   for (int rf = 0; rf < kRF; ++rf)
 #pragma unroll
-    for (int cf = 0; cf < CF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
-  // Fragment read offsets: token cf*16 + t (t = lane % 16), global chunk 4*(lane/16) + j.
+    for (int cf = 0; cf < kGemmCF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
   const int t_l = lane & 15, g_l = lane >> 4;
-  int boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) boff[j] = t_l * kQuadK + (((4 * g_l + j) ^ t_l) * 16);
-  // Vector-memory operations issued per step (activation pieces + brick loads).
-  constexpr int kStepLoads = kXLoads + kRF;
 
-  uint32_t a[kRF][16];
   Bricks b0, b1;
+  ASlice a0, a1;
   load_bricks(0, b0);
-  load_x(0);
-  load_bricks(min<int64_t>(1, nq - 1), b1);
-  load_x(min<int64_t>(1, nq - 1));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // ring slots of steps 0 and 1 written
+  load_x(0, 0);
+  load_bricks(min(1, nq - 1), b1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // ring slot of step 0 written
   __syncthreads();
-#pragma unroll
-  for (int rf = 0; rf < kRF; ++rf)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) decode_slice(b0, rf, j, a[rf] + 4 * j);
+  decode_slice(b0, 0, a0);
 
-  // Step q (its A slices 0-2 already decoded, its bricks in `bcur`):
-  //   MFMA group 0 while decoding slice 3 of step q (bcur); then the loads of step q+2 go out
-  //   (bricks into bcur, now free; activations into ring slot (q+2) % 3);
-  //   MFMA group j (j = 1..3) while decoding slice j-1 of step q+1 (bnext) into the registers
-  //   that group j-1 has finished with.
-  // Activation fragments are read one MFMA batch ahead. Before the closing barrier each wave
-  // waits for its own step-(q+1) activation pieces (issued during step q-1): only the kStepLoads
-  // operations issued in this step may still be in flight.
-  auto step = [&](int64_t q, Bricks& bcur, const Bricks& bnext, bool has_next) {
-    const int8_t* xt = xs0 + (int)(q % kXBufs) * kTileBytes;
-    const bool prefetch = q + 2 < nq;
-    v4i bv = *reinterpret_cast<const v4i*>(xt + boff[0]);
+  // Step q (slice 0 of its A already decoded into a0, its bricks in bcur, step q+1's in bnext):
+  // the activation tile of step q+1 goes out first; MFMA group j (slice j, 4 row fragments x 8
+  // token fragments) runs while slice j+1 is decoded into the other A set (slice 0 of step q+1
+  // during group 3); after group 3 the bricks of step q+2 are loaded into bcur. Before the
+  // closing barrier each wave waits for its step-(q+1) activation pieces: only the brick loads
+  // issued after them may still be in flight.
+  auto step = [&](int q, int slot, Bricks& bcur, const Bricks& bnext) {
+    // Unconditional, so that the step is straight-line code and the compiler's counter waits for
+    // the brick registers stay exact: past the last step the tile's range is empty (reads are
+    // zero) and the slot it fills is never read.
+    load_x(q + 1, slot ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // the tile loads go out before this step's MFMAs
+    const int8_t* xt = xs0 + slot * kTileBytes + rlane;
+    v4i bv = *reinterpret_cast<const v4i*>(xt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      ASlice& cur = (j & 1) ? a1 : a0;
+      ASlice& nxt = (j & 1) ? a0 : a1;
 #pragma unroll
-      for (int cf = 0; cf < CF; ++cf) {
-        const int nj = cf + 1 < CF ? j : j + 1, ncf = cf + 1 < CF ? cf + 1 : 0;
+      for (int cf = 0; cf < kGemmCF; ++cf) {
+        const int nj = cf + 1 < kGemmCF ? j : j + 1, ncf = cf + 1 < kGemmCF ? cf + 1 : 0;
         v4i bn = bv;
-        if (nj < 4) bn = *reinterpret_cast<const v4i*>(xt + ncf * 16 * kQuadK + boff[nj]);
+        if (nj < 4) bn = *reinterpret_cast<const v4i*>(xt + ncf * 4096 + nj * 256);
 #pragma unroll
-        for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(a[rf] + 4 * j, bv, acc[rf][cf]);
+        for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(cur[rf], bv, acc[rf][cf]);
         bv = bn;
       }
-      if (j == 0) {
-#pragma unroll
-        for (int rf = 0; rf < kRF; ++rf) decode_slice(bcur, rf, 3, a[rf] + 12);
-      } else if (has_next) {
-#pragma unroll
-        for (int rf = 0; rf < kRF; ++rf) decode_slice(bnext, rf, j - 1, a[rf] + 4 * (j - 1));
+      if (j < 3) {
+        decode_slice(bcur, j + 1, nxt);
+      } else {
+        decode_slice(bnext, 0, nxt);
       }
 #pragma unroll
-      for (int cf = 0; cf < CF; ++cf) {
-        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2 + 2 * kRF, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // LDS read
-      }
-      if (j == 0 && prefetch) {
-        load_bricks(q + 2, bcur);
-        load_x(q + 2);
+      for (int cf = 0; cf < kGemmCF; ++cf) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
       }
     }
-    if (prefetch && POS && XVEC) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kStepLoads));
+    load_bricks(min(q + 2, nq - 1), bcur);
+    if (POS && XVEC) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRF));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     __syncthreads();
   };
-  int64_t q = 0;
-  for (; q + 2 < nq; q += 2) {
-    step(q, b0, b1, true);
-    step(q + 1, b1, b0, true);
+  int q = 0;
+  for (; q + 1 < nq; q += 2) {
+    step(q, 0, b0, b1);
+    step(q + 1, 1, b1, b0);
   }
-  if (q + 1 < nq) {
-    step(q, b0, b1, true);
-    step(q + 1, b1, b0, false);
-  } else {
-    step(q, b0, b1, false);
-  }
+  if (q < nq) step(q, 0, b0, b1);
 
   const float gamma = gamma_p[0];
   // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte store when the
   // output rows are 16-byte aligned and all 4 rows exist.
   const bool vec_out = (((uintptr_t)y | (uintptr_t)(ld_y * 4)) & 15) == 0;
 #pragma unroll
-  for (int cf = 0; cf < CF; ++cf) {
+  for (int cf = 0; cf < kGemmCF; ++cf) {
     const int64_t t = t0 + cf * 16 + t_l;
     if (t >= T) continue;
     const float step_t = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
@@ -445,11 +539,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void bitlinear_gemm(
   }
 }
 
-template <int CF>
-constexpr size_t gemm_smem_bytes() {
-  return (size_t)kXBufs * CF * 16 * kQuadK;
-}
-
 // Raises a kernel's dynamic-LDS limit once per process (gfx950 has 160 KB of LDS per CU).
 template <typename K>
 hipError_t allow_smem(K kernel, size_t bytes) {
@@ -461,37 +550,44 @@ hipError_t allow_smem(K kernel, size_t bytes) {
   return e;
 }
 
+// Launches the GEMV with W = min(16, quads) waves and Q = ceil(quads / W) quads per wave.
+template <bool POS, bool FUSED, bool XVEC>
+hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
+                       int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
+                       int out_kind, hipStream_t s) {
+  const Layout& L = h->L;
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  const int Q = (int)((L.quads + W - 1) / W);
+#define SBN_GEMV(QQ)                                                                          \
+  hipLaunchKernelGGL((bitlinear_gemv<POS, FUSED, XVEC, QQ>), dim3((unsigned)L.row_blocks),    \
+                     dim3(64 * W), 0, s, h->mask, h->codes, L, h->gamma, x, ld_x, xq_out, ld_q, \
+                     absmax, T, y, ld_y, out_kind)
+  if (Q == 1) {
+    SBN_GEMV(1);
+  } else if (Q == 2) {
+    SBN_GEMV(2);
+  } else {
+    SBN_GEMV(3);
+  }
+#undef SBN_GEMV
+  return hipGetLastError();
+}
+
 template <bool POS, bool XVEC>
 hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
   const Layout& L = h->L;
-  if (T <= 16) {
-    const size_t xs_bytes = (size_t)T * kGemvXStride;
-    if (T <= 4) {
-      hipError_t e = allow_smem(bitlinear_gemv<POS, XVEC, 1>, xs_bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((bitlinear_gemv<POS, XVEC, 1>), dim3((unsigned)L.row_blocks),
-                         dim3(256), xs_bytes, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax,
-                         T, y, ld_y, out_kind);
-    } else {
-      hipError_t e = allow_smem(bitlinear_gemv<POS, XVEC, 2>, xs_bytes);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((bitlinear_gemv<POS, XVEC, 2>),
-                         dim3((unsigned)((L.row_blocks + 1) / 2)), dim3(256), xs_bytes, s, h->mask,
-                         h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y, out_kind);
-    }
-    return hipGetLastError();
+  if (T <= 16 && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
+    return launch_gemv<POS, false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax), T,
+                                         y, ld_y, out_kind, s);
   }
-  constexpr int CF = kGemmCF;
-  constexpr size_t smem = gemm_smem_bytes<CF>();
-  hipError_t e = allow_smem(bitlinear_gemm<POS, CF, XVEC>, smem);
+  hipError_t e = allow_smem(bitlinear_gemm<POS, XVEC>, kGemmSmem);
   if (e != hipSuccess) return e;
-  const int64_t gx = (L.row_blocks + kGemmWaves * kRF - 1) / (kGemmWaves * kRF);
-  const int64_t gy = (T + CF * 16 - 1) / (CF * 16);
-  hipLaunchKernelGGL((bitlinear_gemm<POS, CF, XVEC>), dim3((unsigned)(gx * gy)),
-                     dim3(kGemmThreads),
-                     smem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
+  const int64_t gx = (L.row_blocks + kGemmRowBlocks - 1) / kGemmRowBlocks;
+  const int64_t gy = (T + kGemmTok - 1) / kGemmTok;
+  hipLaunchKernelGGL((bitlinear_gemm<POS, XVEC>), dim3((unsigned)(gx * gy)), dim3(kGemmThreads),
+                     kGemmSmem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
                      out_kind, (int)gx, (int)gy);
   return hipGetLastError();
 }
@@ -505,7 +601,37 @@ hipError_t launch_pattern_x(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   return launch_pattern<POS, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
+template <bool POS, bool XVEC>
+hipError_t launch_gemv_fused(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
+                             int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
+                             int out_kind, hipStream_t s) {
+  return launch_gemv<POS, true, XVEC>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+}
+
 }  // namespace
+
+hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
+                                 int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
+                                 int out_kind, hipStream_t s) {
+  const Layout& L = h->L;
+  if (T == 0) return hipSuccess;
+  if (L.n_out > 0 && T <= kFusedMaxT && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
+    const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
+    if (L.positional) {
+      return xvec ? launch_gemv_fused<true, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
+                                                  out_kind, s)
+                  : launch_gemv_fused<true, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
+                                                   out_kind, s);
+    }
+    return xvec ? launch_gemv_fused<false, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
+                                                 out_kind, s)
+                : launch_gemv_fused<false, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
+                                                  out_kind, s);
+  }
+  hipError_t e = launch_quantize_act(x, T, L.K, ld_x, xq, ld_q, absmax, s);
+  if (e != hipSuccess) return e;
+  return launch_bitlinear(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+}
 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,

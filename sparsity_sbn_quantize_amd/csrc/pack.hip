@@ -296,7 +296,7 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
                      L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
-  const dim3 grid((unsigned)(L.row_blocks * L.quads));
+  const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
 #define SBN_PACK(MM, POS)                                                                     \
   hipLaunchKernelGGL((pack_fragments<MM, POS>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
                      h->mask, h->codes)

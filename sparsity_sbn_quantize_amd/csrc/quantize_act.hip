@@ -18,28 +18,6 @@
 namespace sbn {
 namespace {
 
-constexpr float kFloor = 1e-5f;
-
-__device__ __forceinline__ uint32_t max_abs_bf16x2(uint32_t acc, uint32_t w) {
-  // |hi| and |lo| as 15-bit magnitudes; compare halves independently.
-  const uint32_t a = w & 0x7FFF7FFFu;
-  const uint32_t lo = max(acc & 0xFFFFu, a & 0xFFFFu);
-  const uint32_t hi = max(acc >> 16, a >> 16);
-  return lo | (hi << 16);
-}
-
-__device__ __forceinline__ uint32_t quant4(uint32_t w01, uint32_t w23, float s) {
-  // Four bf16 (two per word) -> four int8 packed in a word.
-  const float f0 = __uint_as_float(w01 << 16), f1 = __uint_as_float(w01 & 0xFFFF0000u);
-  const float f2 = __uint_as_float(w23 << 16), f3 = __uint_as_float(w23 & 0xFFFF0000u);
-  const int i0 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f0 * s), -127.f, 127.f);
-  const int i1 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f1 * s), -127.f, 127.f);
-  const int i2 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f2 * s), -127.f, 127.f);
-  const int i3 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f3 * s), -127.f, 127.f);
-  return (uint32_t)(i0 & 0xFF) | ((uint32_t)(i1 & 0xFF) << 8) | ((uint32_t)(i2 & 0xFF) << 16) |
-         ((uint32_t)(i3 & 0xFF) << 24);
-}
-
 template <int TPR>
 __device__ __forceinline__ uint32_t row_max(uint32_t v, uint32_t* red) {
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
@@ -81,7 +59,7 @@ __global__ __launch_bounds__(256) void quantize_act_vec(const uint16_t* __restri
   }
   uint32_t mb = max(m2 & 0xFFFFu, m2 >> 16);
   mb = row_max<TPR>(mb, red);
-  const float a = fmaxf(__uint_as_float(mb << 16), kFloor);
+  const float a = fmaxf(__uint_as_float(mb << 16), kAbsmaxFloor);
   const float s = 127.0f / a;
   if (!active) return;
   uint2* qr = reinterpret_cast<uint2*>(q + row * ld_q);
@@ -104,7 +82,7 @@ __global__ __launch_bounds__(256) void quantize_act_any(const uint16_t* __restri
   uint32_t mb = 0;
   for (int64_t k = threadIdx.x; k < K; k += 256) mb = max(mb, (uint32_t)(xr[k] & 0x7FFFu));
   mb = row_max<256>(mb, red);
-  const float a = fmaxf(__uint_as_float(mb << 16), kFloor);
+  const float a = fmaxf(__uint_as_float(mb << 16), kAbsmaxFloor);
   const float s = 127.0f / a;
   int8_t* qr = q + row * ld_q;
   for (int64_t k = threadIdx.x; k < K; k += 256) {

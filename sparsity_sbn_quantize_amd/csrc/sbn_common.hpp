@@ -9,7 +9,7 @@
 // bits (8 bytes, absent when n == m) and its code bits. Bricks are stored fragment-major: 16 rows
 // x 4 bricks (one 16x16x64 MFMA A-operand tile over 256 K) form 64 bricks stored contiguously in
 // lane order (lane = row % 16 + 16 * (brick % 4)), so that one wave-wide load of one brick per lane
-// reads one contiguous block. Rows are padded to a multiple of 16 and bricks to a multiple of 4
+// reads one contiguous block. Rows are padded to a multiple of 256 and bricks to a multiple of 4
 // with zero bricks (all pruned, code 0). The mask plane and the code plane are separate arrays.
 //
 // Codes come in one of two forms:
@@ -41,8 +41,13 @@ struct Layout {
   int code_brick_bytes;  // positional ? 16 : 16 n / m
   int has_mask;          // n < m
   int64_t row_blocks;    // ceil(n_out / 16)
+  int64_t row_blocks_pad;  // row_blocks rounded up to kPadRowBlocks (stored, zero-filled)
   int64_t quads;         // ceil(ceil(K / 64) / 4)
 };
+
+// Stored row fragments are padded with zero bricks to a multiple of 16 (256 rows), so that a GEMM
+// tile never addresses past the planes.
+constexpr int kPadRowBlocks = 16;
 
 __host__ __device__ constexpr bool positional_codes(int n, int m) { return 2 * n >= m; }
 
@@ -101,6 +106,56 @@ __device__ inline void decode_kept_brick(const uint32_t mask[2], const uint32_t 
       out[d] = (out[d] & ~(0xFFu << s)) | (b << s);
     }
   }
+}
+
+// Per-token absmax INT8 quantization helpers, shared by the quantize kernel and the fused decode
+// forward so that both produce identical bytes:
+//   a' = max(max |x|, 1e-5); s = fl32(127 / a'); q = clamp(rne(fl32(x * s)), -127, 127).
+constexpr float kAbsmaxFloor = 1e-5f;
+
+// Running maximum of bf16 magnitudes, two per word (the sign cleared, 15-bit patterns compare
+// in the order of the values for finite inputs).
+__device__ __forceinline__ uint32_t max_abs_bf16x2(uint32_t acc, uint32_t w) {
+  const uint32_t a = w & 0x7FFF7FFFu;
+  const uint32_t lo = max(acc & 0xFFFFu, a & 0xFFFFu);
+  const uint32_t hi = max(acc >> 16, a >> 16);
+  return lo | (hi << 16);
+}
+
+// Four bf16 (two per word) -> four int8 packed in a word.
+__device__ __forceinline__ uint32_t quant4(uint32_t w01, uint32_t w23, float s) {
+  const float f0 = __uint_as_float(w01 << 16), f1 = __uint_as_float(w01 & 0xFFFF0000u);
+  const float f2 = __uint_as_float(w23 << 16), f3 = __uint_as_float(w23 & 0xFFFF0000u);
+  const int i0 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f0 * s), -127.f, 127.f);
+  const int i1 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f1 * s), -127.f, 127.f);
+  const int i2 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f2 * s), -127.f, 127.f);
+  const int i3 = (int)__builtin_amdgcn_fmed3f(__builtin_rintf(f3 * s), -127.f, 127.f);
+  return (uint32_t)(i0 & 0xFF) | ((uint32_t)(i1 & 0xFF) << 8) | ((uint32_t)(i2 & 0xFF) << 16) |
+         ((uint32_t)(i3 & 0xFF) << 24);
+}
+
+// Maximum over the 64 lanes of a wave of two packed 16-bit magnitudes (as max_abs_bf16x2), with
+// DPP lane moves (no LDS round trips): within quads (xor 1, 2), half rows and rows (mirrors), then
+// across rows (row broadcasts); lane 63 ends with the result, which is returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
+  auto dpp = [](uint32_t old, uint32_t x, int ctrl, int row_mask) -> uint32_t {
+    switch (ctrl) {  // the control word must be a constant expression
+      case 0xB1: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0xB1, 0xF, 0xF, false);
+      case 0x4E: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x4E, 0xF, 0xF, false);
+      case 0x141: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x141, 0xF, 0xF, false);
+      case 0x140: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x140, 0xF, 0xF, false);
+      case 0x142: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x142, 0xA, 0xF, false);
+      default: return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, 0x143, 0xC, 0xF, false);
+    }
+    (void)row_mask;
+  };
+  v = max_abs_bf16x2(v, dpp(v, v, 0xB1, 0xF));   // quad_perm [1,0,3,2]
+  v = max_abs_bf16x2(v, dpp(v, v, 0x4E, 0xF));   // quad_perm [2,3,0,1]
+  v = max_abs_bf16x2(v, dpp(v, v, 0x141, 0xF));  // row_half_mirror
+  v = max_abs_bf16x2(v, dpp(v, v, 0x140, 0xF));  // row_mirror
+  v = max_abs_bf16x2(v, dpp(v, v, 0x142, 0xA));  // row_bcast:15 into rows 1, 3
+  v = max_abs_bf16x2(v, dpp(v, v, 0x143, 0xC));  // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 }  // namespace sbn

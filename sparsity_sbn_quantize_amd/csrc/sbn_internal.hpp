@@ -38,5 +38,8 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
+hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
+                                 int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
+                                 int out_kind, hipStream_t s);
 
 }  // namespace sbn

@@ -19,7 +19,7 @@ def lib():
 def test_exports_match_header(lib):
     declared = b.header_symbols()
     assert set(declared) == {"sbn_quantize_act", "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
-                             "sbn_free", "sbn_packed_export", "sbn_packed_export_rpf",
+                             "sbn_bitlinear_fwd_bf16", "sbn_free", "sbn_packed_export", "sbn_packed_export_rpf",
                              "sbn_packed_query", "sbn_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -73,6 +73,8 @@ def test_pack_null_handle_pointer(lib):
 
 def test_forward_and_misc_validation(lib):
     assert lib.sbn_bitlinear_fwd(None, None, 0, None, 1, None, 0, 0, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_bf16(None, None, 0, 1, None, 0, None, None, 0, 0,
+                                      None) == ERR_INVALID
     assert lib.sbn_packed_export(None, None, None, None, None) == ERR_INVALID
     assert lib.sbn_packed_export_rpf(None, None, None, None) == ERR_INVALID
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
