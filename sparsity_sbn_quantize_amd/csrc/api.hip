@@ -112,6 +112,8 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     off = align_up(off + sizeof(float), 256);
     const size_t off_part = off;
     off = align_up(off + sizeof(double) * num_partials, 256);
+    const size_t off_sync = off;
+    off = align_up(off + sizeof(int) * sbn::kGemmSyncInts, 256);
 
     h = new (std::nothrow) sbn_packed;
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
@@ -145,6 +147,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     h->codes = h->base + off_codes;
     h->gamma = reinterpret_cast<float*>(h->base + off_gamma);
     h->partials = reinterpret_cast<double*>(h->base + off_part);
+    h->gemm_sync = reinterpret_cast<int*>(h->base + off_sync);
     *handle = h;
   }
   h->last_stream = s;

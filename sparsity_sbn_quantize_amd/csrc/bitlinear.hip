@@ -300,11 +300,27 @@ constexpr size_t kGemmSmem = (size_t)kXBufs * kTileBytes;
 constexpr int kXcds = 8;
 constexpr int kTileGroup = 4;
 
-__device__ __forceinline__ void xcd_tile(int nblocks, int bid, int tiles_n, int tiles_t,
-                                         int& tile_n, int& tile_t) {
+// Split-K (two workgroups per tile, each half of K) for launches with few tiles. The halves of a
+// tile are adjacent in the XCD order (same L2). Per tile and wave, the first half to finish
+// stores its int32 partial sums in the tile's region of y and raises a flag; the second waits
+// for the flag (a bounded spin: the first is already past its main loop, so it is running), adds
+// the partial and writes the result. Integer sums make the result independent of the order. The
+// two flag words per tile and wave live in the weight handle and are cleared by the second half,
+// so calls that share a handle must be ordered (one stream, or synchronized).
+constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
+constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
+static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
+
+// Position of block `bid` in the XCD-contiguous order.
+__device__ __forceinline__ int xcd_order(int nblocks, int bid) {
   const int xcd = bid % kXcds, j = bid / kXcds;
   const int base = nblocks / kXcds, extra = nblocks % kXcds;
-  const int lin = xcd * base + min(xcd, extra) + j;  // position in the grouped order
+  return xcd * base + min(xcd, extra) + j;
+}
+
+// Tile of position `lin` in the grouped order.
+__device__ __forceinline__ void grouped_tile(int lin, int tiles_n, int tiles_t, int& tile_n,
+                                             int& tile_t) {
   const int per_group = kTileGroup * tiles_n;
   const int group = lin / per_group, r = lin % per_group;
   const int gsize = min(kTileGroup, tiles_t - group * kTileGroup);
@@ -328,17 +344,21 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2,
 void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
                     Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
                     int64_t ld_q, const float* __restrict__ absmax, int64_t T,
-                    void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t) {
+                    void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t,
+                    int ksplit, int* __restrict__ sync) {
   constexpr int kBW = POS ? 4 : 6;  // brick words in registers: codes, or mask (2) + codes (4)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int8_t* const xs0 = reinterpret_cast<int8_t*>(smem);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   const int lane = threadIdx.x & 63;
+  const int lin = xcd_order((int)gridDim.x, (int)blockIdx.x);
+  const int tile_lin = lin / ksplit, half = lin % ksplit;
   int tile_n, tile_t;
-  xcd_tile((int)gridDim.x, (int)blockIdx.x, tiles_n, tiles_t, tile_n, tile_t);
+  grouped_tile(tile_lin, tiles_n, tiles_t, tile_n, tile_t);
   const int64_t rb0 = ((int64_t)tile_n * kGemmWaves + wave) * kRF;
   const int64_t t0 = (int64_t)tile_t * kGemmTok;
   const int nq = (int)L.quads;
+  const int qb = nq * half / ksplit, qe = nq * (half + 1) / ksplit;  // this workgroup's K steps
   const int K = (int)L.K;
   const int cbb = POS ? 16 : L.code_brick_bytes;
 
@@ -445,9 +465,9 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 
   Bricks b0, b1;
   ASlice a0, a1;
-  load_bricks(0, b0);
-  load_x(0, 0);
-  load_bricks(min(1, nq - 1), b1);
+  load_bricks(qb, b0);
+  load_x(qb, 0);
+  load_bricks(min(qb + 1, nq - 1), b1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // ring slot of step 0 written
   __syncthreads();
   decode_slice(b0, 0, a0);
@@ -499,17 +519,88 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     }
     __syncthreads();
   };
-  int q = 0;
-  for (; q + 1 < nq; q += 2) {
+  int q = qb;
+  for (; q + 1 < qe; q += 2) {
     step(q, 0, b0, b1);
     step(q + 1, 1, b1, b0);
   }
-  if (q < nq) step(q, 0, b0, b1);
+  if (q < qe) step(q, 0, b0, b1);
 
-  const float gamma = gamma_p[0];
-  // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte store when the
+  // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte access when the
   // output rows are 16-byte aligned and all 4 rows exist.
   const bool vec_out = (((uintptr_t)y | (uintptr_t)(ld_y * 4)) & 15) == 0;
+  int32_t* const yi = reinterpret_cast<int32_t*>(y);
+  if (ksplit > 1) {
+    // Every access of the handshake is coherent across the XCDs' L2 caches on its own (sc1:
+    // relaxed agent-scope atomics for the flags, sc1 buffer accesses for the partial sums);
+    // acquire/release fences would instead write back or invalidate whole L2s. Order: the
+    // partial sums are stored, the wave waits until its stores have completed, then raises the
+    // flag; the other half reads the partial sums only after it has seen the flag.
+    constexpr int kSc1 = 1 << 4;  // buffer cache-policy bit: sc1
+    int* const flag = sync + 2 * ((int64_t)tile_lin * kGemmWaves + wave);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(y, (short)0, 0x7FFFFFFF, kBufDword3);
+    int first = 0;
+    if (lane == 0)
+      first = __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+    first = __builtin_amdgcn_readfirstlane(first);
+    if (first) {
+#pragma unroll
+      for (int cf = 0; cf < kGemmCF; ++cf) {
+        const int64_t t = t0 + cf * 16 + t_l;
+        if (t >= T) continue;
+#pragma unroll
+        for (int rf = 0; rf < kRF; ++rf) {
+          const int64_t r0 = (rb0 + rf) * 16 + 4 * g_l;
+          const int off = (int)((t * ld_y + r0) * 4);
+          if (vec_out && r0 + 4 <= L.n_out) {
+            __builtin_amdgcn_raw_buffer_store_b128(acc[rf][cf], yr, off, 0, kSc1);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (r0 + i < L.n_out)
+                __builtin_amdgcn_raw_buffer_store_b32(acc[rf][cf][i], yr, off + 4 * i, 0, kSc1);
+          }
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);  // the partial sums have been written
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) __hip_atomic_store(flag + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (lane == 0) {
+      for (int it = 0; it < kSpinLimit; ++it) {
+        if (__hip_atomic_load(flag + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int cf = 0; cf < kGemmCF; ++cf) {
+      const int64_t t = t0 + cf * 16 + t_l;
+      if (t >= T) continue;
+#pragma unroll
+      for (int rf = 0; rf < kRF; ++rf) {
+        const int64_t r0 = (rb0 + rf) * 16 + 4 * g_l;
+        const int off = (int)((t * ld_y + r0) * 4);
+        if (vec_out && r0 + 4 <= L.n_out) {
+          acc[rf][cf] += __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, kSc1);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (r0 + i < L.n_out)
+              acc[rf][cf][i] += __builtin_amdgcn_raw_buffer_load_b32(yr, off + 4 * i, 0, kSc1);
+        }
+      }
+    }
+    if (lane == 0) {
+      __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  const float gamma = gamma_p[0];
 #pragma unroll
   for (int cf = 0; cf < kGemmCF; ++cf) {
     const int64_t t = t0 + cf * 16 + t_l;
@@ -586,9 +677,12 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   if (e != hipSuccess) return e;
   const int64_t gx = (L.row_blocks + kGemmRowBlocks - 1) / kGemmRowBlocks;
   const int64_t gy = (T + kGemmTok - 1) / kGemmTok;
-  hipLaunchKernelGGL((bitlinear_gemm<POS, XVEC>), dim3((unsigned)(gx * gy)), dim3(kGemmThreads),
-                     kGemmSmem, s, h->mask, h->codes, L, h->gamma, xq, ld_q, absmax, T, y, ld_y,
-                     out_kind, (int)gx, (int)gy);
+  // y offsets of the split-K handshake are 32-bit buffer offsets
+  const bool y_fits = (double)T * (double)ld_y * 4.0 < 2147483647.0;
+  const int ksplit = (gx * gy <= kSplitMaxTiles && L.quads >= 8 && y_fits) ? 2 : 1;
+  hipLaunchKernelGGL((bitlinear_gemm<POS, XVEC>), dim3((unsigned)(gx * gy * ksplit)),
+                     dim3(kGemmThreads), kGemmSmem, s, h->mask, h->codes, L, h->gamma, xq, ld_q,
+                     absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, ksplit, h->gemm_sync);
   return hipGetLastError();
 }
 

@@ -18,11 +18,15 @@ struct sbn_packed {
   uint8_t* codes;      // code plane (brick fragments)
   float* gamma;        // device scalar
   double* partials;    // device workspace [num_partials]
+  int* gemm_sync;      // split-K flags: kGemmSyncInts words, zero between calls
   int device;
   hipStream_t last_stream;
 };
 
 namespace sbn {
+
+// Words of split-K handshake flags a handle holds (2 per wave of up to 256 tiles x 4 waves).
+constexpr int kGemmSyncInts = 256 * 4 * 2;
 
 // Number of blocks of the absmean reduction for a tensor with n_out rows (fixed per shape, so the
 // fp64 partial-sum order, and hence gamma, is reproducible run to run).
