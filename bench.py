@@ -432,6 +432,59 @@ def profile_copy(gpu, args):
     print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
 
 
+# Counter runs behind profiles/traffic.json: tag -> (traffic key, kernel-name pattern). Each tag
+# names the bench workload that was run under `rocprofv3 --pmc FETCH_SIZE` and, separately,
+# `--pmc WRITE_SIZE`; the tag "copy" is `bench.py --profile-copy`.
+TRAFFIC_RUNS = {
+    "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<true, true"),
+    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv<true, false"),
+    "prefill_up": ("gemm_8of16_ffn_up", r"bitlinear_gemm<"),
+    "prefill_down": ("gemm_8of16_ffn_down", r"bitlinear_gemm<"),
+}
+
+
+def record_traffic(root):
+    """Writes profiles/traffic.json from rocprofv3 counter CSVs under `root`, laid out as
+    <tag>_<COUNTER>/run_counter_collection.csv. Bytes per launch = the median per-dispatch counter
+    value (KiB) x 1024 x the scale that maps the same counter onto a 1 GiB device copy."""
+    import csv
+    import re
+    import statistics
+
+    def per_dispatch(tag, counter, pattern):
+        path = os.path.join(root, f"{tag}_{counter}", "run_counter_collection.csv")
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"].startswith(counter) and re.search(pattern, r["Kernel_Name"]):
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(
+                        r["Counter_Value"])
+        return list(vals.values())
+
+    copy_bytes = 1 << 30
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = per_dispatch("copy", c, r".")
+        scale[c] = copy_bytes / (max(v) * 1024.0)
+    out = {"_note": "HBM bytes per launch = FETCH_SIZE x %.3f + WRITE_SIZE x %.3f (KiB x 1024); "
+                    "scales from a 1 GiB device copy; valid only for the kernel sources with this "
+                    "hash" % (scale["FETCH_SIZE"], scale["WRITE_SIZE"])}
+    for tag, (key, pattern) in TRAFFIC_RUNS.items():
+        try:
+            fetch = statistics.median(per_dispatch(tag, "FETCH_SIZE", pattern))
+            write = statistics.median(per_dispatch(tag, "WRITE_SIZE", pattern))
+        except (OSError, ValueError, statistics.StatisticsError):
+            continue
+        out[key] = {"bytes_per_launch": int(round((fetch * scale["FETCH_SIZE"] +
+                                                   write * scale["WRITE_SIZE"]) * 1024)),
+                    "fetch_bytes": int(round(fetch * scale["FETCH_SIZE"] * 1024)),
+                    "write_bytes": int(round(write * scale["WRITE_SIZE"] * 1024)),
+                    "source_hash": kernel_source_hash()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -445,7 +498,12 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 counter runs under DIR")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
               "part of this build", file=sys.stderr)
