@@ -1,6 +1,7 @@
 // C ABI of libsbn: argument validation, handle lifecycle and dispatch. Every argument check
 // happens before the first HIP call, so a rejected call leaves the GPU untouched.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -91,6 +92,11 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     L.n = n_keep;
     L.m = m_group;
     L.positional = sbn::positional_codes(n_keep, m_group) ? 1 : 0;
+    L.form = L.positional ? sbn::kFormPositional : sbn::kFormKept;
+    // 2:4 uses the structured-sparse MFMA operands unless SBN_NO_SMFMAC is set to a non-zero
+    // value (a diagnostic switch for comparing against the dense MFMA path).
+    const char* no_sp = getenv("SBN_NO_SMFMAC");
+    if (n_keep == 2 && m_group == 4 && !(no_sp && atoi(no_sp) != 0)) L.form = sbn::kFormSparse24;
     L.code_brick_bytes = L.positional ? 16 : 16 * n_keep / m_group;
     L.has_mask = n_keep < m_group ? 1 : 0;
     L.row_blocks = (n_out + 15) / 16;

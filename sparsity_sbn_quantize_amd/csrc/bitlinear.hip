@@ -28,19 +28,39 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ v4i mfma16(const uint32_t* a, v4i b, v4i c) {
   const v4i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, c, 0, 0, 0);
 }
 
+// Structured-sparse 2:4 MFMA over a 128-K block: a = the lane's 16 kept int8 weights, b = its 32
+// dense activation bytes (K chunks g and g + 4 of the block, g = lane / 16), idx = the kept
+// positions (2 bits per slot).
+__device__ __forceinline__ v4i smfmac16(const uint32_t* a, v4i b_lo, v4i b_hi, uint32_t idx,
+                                        v4i c) {
+  const v4i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+  const v8i bv = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
+  return __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, c, (int)idx, 0, 0);
+}
+
+// K chunk (16 bytes) of a 256-K quad that lane group g supplies as B operand piece j: slice j of
+// brick g for the dense MFMA (chunk 4g + j); for the sparse form, chunks g and g + 4 of block 0,
+// then of block 1 (chunk g + 4j).
+template <int FORM>
+__device__ __forceinline__ int b_chunk(int g, int j) {
+  return FORM == kFormSparse24 ? g + 4 * j : 4 * g + j;
+}
+
 // Loads one brick: positional codes (16 bytes), or the kept form's mask (8 bytes) and code bytes.
-template <bool POS>
+template <int FORM>
 __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* __restrict__ mask_plane,
                                            const uint8_t* __restrict__ code_plane, int64_t slot,
                                            uint32_t mask[2], uint32_t codes[4]) {
   mask[0] = mask[1] = 0;
   codes[0] = codes[1] = codes[2] = codes[3] = 0;
-  if constexpr (POS) {
+  if constexpr (FORM != kFormKept) {
     const uint4 c = *reinterpret_cast<const uint4*>(code_plane + slot * 16);
     codes[0] = c.x; codes[1] = c.y; codes[2] = c.z; codes[3] = c.w;
   } else {
@@ -55,10 +75,10 @@ __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* __res
   }
 }
 
-template <bool POS>
+template <int FORM>
 __device__ __forceinline__ void decode(const Layout& L, const uint32_t mask[2],
                                        const uint32_t codes[4], uint32_t out[16]) {
-  if constexpr (POS) {
+  if constexpr (FORM == kFormPositional) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[j], out + 4 * j);
   } else {
@@ -120,7 +140,7 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
   }
 }
 
-template <bool POS, bool FUSED, bool XVEC, int Q>
+template <int FORM, bool FUSED, bool XVEC, int Q>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const void* __restrict__ xin, int64_t ld_x,
@@ -142,8 +162,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     for (int i = 0; i < Q; ++i) {
       const int q = wave + i * W;
       if (q < nq) {
-        load_brick<POS>(L, mask_plane, code_plane, ((rb * nq + q) << 6) | lane, mask[i],
-                        codes[i]);
+        load_brick<FORM>(L, mask_plane, code_plane, ((rb * nq + q) << 6) | lane, mask[i],
+                         codes[i]);
       } else {
         mask[i][0] = mask[i][1] = 0;
         codes[i][0] = codes[i][1] = codes[i][2] = codes[i][3] = 0;
@@ -159,7 +179,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     for (int i = 0; i < Q; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = (wave + i * W) * kQuadK + 64 * g + 16 * j;
+        const int k = (wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
         b[i][j] = v4i{0, 0, 0, 0};
         if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
       }
@@ -245,7 +265,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         b[i][j] = t < kFusedMaxT && tok_ok
-                      ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 + 16 * g + 4 * j)
+                      ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 +
+                                                      4 * b_chunk<FORM>(g, j))
                       : v4i{0, 0, 0, 0};
     }
     if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
@@ -255,10 +276,19 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
 #pragma unroll
   for (int i = 0; i < Q; ++i) {
     if (wave + i * W < nq) {
-      uint32_t a[16];
-      decode<POS>(L, mask[i], codes[i], a);
+      if constexpr (FORM == kFormSparse24) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+        for (int blk = 0; blk < 2; ++blk) {
+          uint32_t a[4];
+          exp_word_to_i8(codes[i][2 * blk], a);
+          acc = smfmac16(a, b[i][2 * blk], b[i][2 * blk + 1], codes[i][2 * blk + 1], acc);
+        }
+      } else {
+        uint32_t a[16];
+        decode<FORM>(L, mask[i], codes[i], a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+      }
     }
   }
   red[wave][lane] = acc;
@@ -339,13 +369,15 @@ constexpr int kBufDword3 = 0x00020000;
 // 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-template <bool POS, bool XVEC>
+template <int FORM, bool XVEC>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
                     Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
                     int64_t ld_q, const float* __restrict__ absmax, int64_t T,
                     void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t,
                     int ksplit, int* __restrict__ sync) {
+  constexpr bool POS = FORM != kFormKept;  // 16 code bytes per lane and quad
+  constexpr bool SP = FORM == kFormSparse24;
   constexpr int kBW = POS ? 4 : 6;  // brick words in registers: codes, or mask (2) + codes (4)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int8_t* const xs0 = reinterpret_cast<int8_t*>(smem);
@@ -391,7 +423,9 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   // 1 KB-block ii + 16 l as the layout requires. The per-instruction part of the address is
   // uniform (folded into the instruction's buffer resource); the lane part is one offset.
   const int xlane = (lane & 15) * (int)ld_q + (lane >> 4) * 16;
-  const int rlane = (lane >> 4) * 1024 + (lane & 15) * 16;  // fragment read offset
+  // fragment read offset: chunk 4g (+ j) of token t for the dense MFMA; chunk g (+ 4, + 8 ...)
+  // for the sparse MFMA (g = lane / 16, t = lane % 16)
+  const int rlane = (lane >> 4) * (SP ? 256 : 1024) + (lane & 15) * 16;
   auto load_x = [&](int q, int slot) {  // step q's activation tile -> ring slot
     int8_t* dst = xs0 + slot * kTileBytes + wave * (kXLoads * 1024);
     const int kq = q * kQuadK;
@@ -438,10 +472,14 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     }
   };
   typedef uint32_t ASlice[kRF][4];
+  // A operand of MFMA slice j (dense forms) or of 128-K block j (sparse form: the block's kept
+  // weights; its index word stays in the brick registers).
   auto decode_slice = [&](const Bricks& bk, int j, ASlice& out) {
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
-      if constexpr (POS) {
+      if constexpr (SP) {
+        exp_word_to_i8(bk[rf][2 * j], out[rf]);
+      } else if constexpr (POS) {
         exp_word_to_i8(bk[rf][j], out[rf]);
       } else {
         const uint32_t m[2] = {bk[rf][0], bk[rf][1]};
@@ -519,12 +557,67 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     }
     __syncthreads();
   };
+  // Sparse 2:4 step: two 128-K blocks; block 0's 32 structured-sparse MFMAs run while block 1's
+  // kept weights are decoded, block 1's while the next step's block 0 is decoded. Each B operand
+  // is two 16-byte reads (chunks g and g + 4 of the block).
+  auto step_sp = [&](int q, int slot, Bricks& bcur, const Bricks& bnext) {
+    load_x(q + 1, slot ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // the tile loads go out before this step's MFMAs
+    const int8_t* xt = xs0 + slot * kTileBytes + rlane;
+    v4i blo = *reinterpret_cast<const v4i*>(xt);
+    v4i bhi = *reinterpret_cast<const v4i*>(xt + 1024);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      ASlice& cur = blk ? a1 : a0;
+      ASlice& nxt = blk ? a0 : a1;
+#pragma unroll
+      for (int cf = 0; cf < kGemmCF; ++cf) {
+        const int nb = cf + 1 < kGemmCF ? blk : blk + 1, ncf = cf + 1 < kGemmCF ? cf + 1 : 0;
+        v4i nlo = blo, nhi = bhi;
+        if (nb < 2) {
+          nlo = *reinterpret_cast<const v4i*>(xt + ncf * 4096 + nb * 2048);
+          nhi = *reinterpret_cast<const v4i*>(xt + ncf * 4096 + nb * 2048 + 1024);
+        }
+#pragma unroll
+        for (int rf = 0; rf < kRF; ++rf)
+          acc[rf][cf] = smfmac16(cur[rf], blo, bhi, bcur[rf][2 * blk + 1], acc[rf][cf]);
+        blo = nlo;
+        bhi = nhi;
+      }
+      if (blk == 0) {
+        decode_slice(bcur, 1, nxt);
+      } else {
+        decode_slice(bnext, 0, nxt);
+      }
+#pragma unroll
+      for (int cf = 0; cf < kGemmCF; ++cf) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS read
+      }
+    }
+    load_bricks(min(q + 2, nq - 1), bcur);
+    if (XVEC) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRF));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+  };
   int q = qb;
-  for (; q + 1 < qe; q += 2) {
-    step(q, 0, b0, b1);
-    step(q + 1, 1, b1, b0);
+  if constexpr (SP) {
+    for (; q + 1 < qe; q += 2) {
+      step_sp(q, 0, b0, b1);
+      step_sp(q + 1, 1, b1, b0);
+    }
+    if (q < qe) step_sp(q, 0, b0, b1);
+  } else {
+    for (; q + 1 < qe; q += 2) {
+      step(q, 0, b0, b1);
+      step(q + 1, 1, b1, b0);
+    }
+    if (q < qe) step(q, 0, b0, b1);
   }
-  if (q < qe) step(q, 0, b0, b1);
 
   // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte access when the
   // output rows are 16-byte aligned and all 4 rows exist.
@@ -642,7 +735,7 @@ hipError_t allow_smem(K kernel, size_t bytes) {
 }
 
 // Launches the GEMV with W = min(16, quads) waves and Q = ceil(quads / W) quads per wave.
-template <bool POS, bool FUSED, bool XVEC>
+template <int FORM, bool FUSED, bool XVEC>
 hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
                        int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
                        int out_kind, hipStream_t s) {
@@ -650,7 +743,7 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
   const int Q = (int)((L.quads + W - 1) / W);
 #define SBN_GEMV(QQ)                                                                          \
-  hipLaunchKernelGGL((bitlinear_gemv<POS, FUSED, XVEC, QQ>), dim3((unsigned)L.row_blocks),    \
+  hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ>), dim3((unsigned)L.row_blocks),   \
                      dim3(64 * W), 0, s, h->mask, h->codes, L, h->gamma, x, ld_x, xq_out, ld_q, \
                      absmax, T, y, ld_y, out_kind)
   if (Q == 1) {
@@ -664,42 +757,42 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   return hipGetLastError();
 }
 
-template <bool POS, bool XVEC>
+template <int FORM, bool XVEC>
 hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
   const Layout& L = h->L;
   if (T <= 16 && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
-    return launch_gemv<POS, false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax), T,
+    return launch_gemv<FORM, false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax), T,
                                          y, ld_y, out_kind, s);
   }
-  hipError_t e = allow_smem(bitlinear_gemm<POS, XVEC>, kGemmSmem);
+  hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC>, kGemmSmem);
   if (e != hipSuccess) return e;
   const int64_t gx = (L.row_blocks + kGemmRowBlocks - 1) / kGemmRowBlocks;
   const int64_t gy = (T + kGemmTok - 1) / kGemmTok;
   // y offsets of the split-K handshake are 32-bit buffer offsets
   const bool y_fits = (double)T * (double)ld_y * 4.0 < 2147483647.0;
   const int ksplit = (gx * gy <= kSplitMaxTiles && L.quads >= 8 && y_fits) ? 2 : 1;
-  hipLaunchKernelGGL((bitlinear_gemm<POS, XVEC>), dim3((unsigned)(gx * gy * ksplit)),
+  hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC>), dim3((unsigned)(gx * gy * ksplit)),
                      dim3(kGemmThreads), kGemmSmem, s, h->mask, h->codes, L, h->gamma, xq, ld_q,
                      absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, ksplit, h->gemm_sync);
   return hipGetLastError();
 }
 
-template <bool POS>
+template <int FORM>
 hipError_t launch_pattern_x(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s) {
   const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (h->L.K % 16 == 0);
-  if (xvec) return launch_pattern<POS, true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
-  return launch_pattern<POS, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  if (xvec) return launch_pattern<FORM, true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern<FORM, false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
-template <bool POS, bool XVEC>
+template <int FORM, bool XVEC>
 hipError_t launch_gemv_fused(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                              int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
                              int out_kind, hipStream_t s) {
-  return launch_gemv<POS, true, XVEC>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_gemv<FORM, true, XVEC>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace
@@ -711,16 +804,14 @@ hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t
   if (T == 0) return hipSuccess;
   if (L.n_out > 0 && T <= kFusedMaxT && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
-    if (L.positional) {
-      return xvec ? launch_gemv_fused<true, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
-                                                  out_kind, s)
-                  : launch_gemv_fused<true, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
-                                                   out_kind, s);
-    }
-    return xvec ? launch_gemv_fused<false, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
-                                                 out_kind, s)
-                : launch_gemv_fused<false, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y,
-                                                  out_kind, s);
+#define SBN_FUSED(FF)                                                                          \
+  return xvec ? launch_gemv_fused<FF, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind,  \
+                                            s)                                                 \
+              : launch_gemv_fused<FF, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind, s)
+    if (L.form == kFormSparse24) SBN_FUSED(kFormSparse24);
+    if (L.form == kFormPositional) SBN_FUSED(kFormPositional);
+    SBN_FUSED(kFormKept);
+#undef SBN_FUSED
   }
   hipError_t e = launch_quantize_act(x, T, L.K, ld_x, xq, ld_q, absmax, s);
   if (e != hipSuccess) return e;
@@ -732,8 +823,11 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             hipStream_t s) {
   const Layout& L = h->L;
   if (L.n_out == 0 || T == 0) return hipSuccess;
-  if (L.positional) return launch_pattern_x<true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
-  return launch_pattern_x<false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  if (L.form == kFormSparse24)
+    return launch_pattern_x<kFormSparse24>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  if (L.form == kFormPositional)
+    return launch_pattern_x<kFormPositional>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  return launch_pattern_x<kFormKept>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
 }  // namespace sbn

@@ -102,7 +102,12 @@ __device__ __forceinline__ uint32_t keep_mask_group(const uint32_t* a, int n) {
 // brick, so the four threads of a row read 64 contiguous weights and the workgroup writes the
 // fragment's code words (4 bytes per thread) and mask halves (2 bytes per thread) as one
 // contiguous block each. Padding rows and positions are written as zero.
-template <int M, bool POS>
+// Sparse 2:4 form (FORM == kFormSparse24, M == 4): thread t = 4s + w covers lane s and word w of
+// that lane's four (block b = w / 2, half h = w % 2): quad positions 128b + 32g + 16h .. +15 (g =
+// s / 16). It computes half of the block's code word and half of its index word; the thread pair
+// (h = 0, 1) exchanges halves, and thread h writes word 2b + h (codes, index), so the code plane
+// is still written as one contiguous block. Its mask halves go to the mask plane's brick layout.
+template <int M, int FORM>
 __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ w, int64_t ld_w,
                                                       int vec4, Layout L,
                                                       const float* __restrict__ gamma_p,
@@ -113,7 +118,11 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
   const int tid = threadIdx.x;
   const int lane_slot = tid >> 2, word = tid & 3;
   const int64_t row = rb * 16 + (lane_slot & 15);
-  const int64_t k0 = (bq * 4 + (lane_slot >> 4)) * kBrickK + 16 * word;
+  constexpr bool kSp24 = FORM == kFormSparse24;
+  // quad-relative first position of this thread's 16
+  const int qpos = kSp24 ? 128 * (word >> 1) + 32 * (lane_slot >> 4) + 16 * (word & 1)
+                         : kBrickK * (lane_slot >> 4) + 16 * word;
+  const int64_t k0 = bq * kQuadK + qpos;
   const int cnt = row < L.n_out ? (int)max<int64_t>(0, min<int64_t>(16, L.K - k0)) : 0;
   const float* wr = w + row * ld_w + k0;
   uint32_t u[16];
@@ -147,7 +156,29 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 16; ++i) nz |= (a[i] > half_bits ? 1u : 0u) << i;
   nz &= keep;
-  if constexpr (POS) {
+  if constexpr (kSp24) {
+    // slots 8h + 2q (lower kept) and 8h + 2q + 1 (higher kept) of group q of the 16 positions
+    const int h = word & 1;
+    uint32_t cw = 0, iw = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int slot = 8 * h + 2 * q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pidx = 4 * q + i;
+        if ((keep >> pidx) & 1u) {
+          const uint32_t c = ((nz >> pidx) & 1u) ? ((u[pidx] >> 31) ? 2u : 1u) : 0u;
+          cw |= c << sp24_code_bit(slot);
+          iw |= (uint32_t)i << (2 * slot);
+          ++slot;
+        }
+      }
+    }
+    const int src = (int)(threadIdx.x & 63);
+    const uint32_t ocw = (uint32_t)__shfl(cw, src ^ 1, 64);
+    const uint32_t oiw = (uint32_t)__shfl(iw, src ^ 1, 64);
+    reinterpret_cast<uint32_t*>(code_plane)[frag * 256 + tid] = h == 0 ? (cw | ocw) : (iw | oiw);
+  } else if constexpr (FORM == kFormPositional) {
     uint32_t cw = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -180,8 +211,15 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
       for (int i = 0; i < cbb; ++i) dst[i] = (uint8_t)(all >> (8 * i));
     }
   }
-  if (L.has_mask)
-    reinterpret_cast<uint16_t*>(mask_plane)[frag * 256 + tid] = (uint16_t)keep;
+  if (L.has_mask) {
+    if constexpr (kSp24) {
+      // mask plane in brick layout: brick qpos / 64 of the quad, bits (qpos % 64) .. +15
+      const int64_t mslot = (frag << 6) | ((lane_slot & 15) + 16 * (qpos >> 6));
+      reinterpret_cast<uint16_t*>(mask_plane)[mslot * 4 + ((qpos & 63) >> 4)] = (uint16_t)keep;
+    } else {
+      reinterpret_cast<uint16_t*>(mask_plane)[frag * 256 + tid] = (uint16_t)keep;
+    }
+  }
 }
 
 __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* mask_plane,
@@ -210,7 +248,23 @@ __global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t*
   const int64_t slot = brick_slot(L, row, brick);
   uint32_t mask[2], codes[4], dec[16];
   load_brick(L, mask_plane, code_plane, slot, mask, codes);
-  if (L.positional) {
+  if (L.form == kFormSparse24) {
+    // this brick's 64 positions are lane groups g0 and g0 + 1 of block b of its quad
+    const int64_t q = brick >> 2;
+    const int p0 = kBrickK * (int)(brick & 3);
+    const int b = p0 >> 7, g0 = (p0 & 127) >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dec[i] = 0;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int64_t s2 = (((row >> 4) * L.quads + q) << 6) | ((row & 15) + 16 * (g0 + hh));
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(code_plane + s2 * 16) + 2 * b;
+      for (int j = 0; j < 16; ++j) {
+        const int pos = 32 * hh + sp24_pos(w[1], j);
+        const uint32_t v = (uint32_t)pos_value((w[0] >> sp24_code_bit(j)) & 3u) & 0xFFu;
+        dec[pos >> 2] |= v << (8 * (pos & 3));
+      }
+    }
+  } else if (L.positional) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[j], dec + 4 * j);
   } else {
@@ -244,7 +298,22 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
     const int64_t b0 = brick * rcb;
     const int cnt = (int)min<int64_t>(rcb, crb - b0);
     uint8_t* dst = code_out + row * crb + b0;
-    if (L.positional) {
+    if (L.form == kFormSparse24) {
+      // 2:4: the brick's 32 kept codes are slots 0..15 of lane groups g0 and g0 + 1, in order
+      const int64_t q = brick >> 2;
+      const int p0 = kBrickK * (int)(brick & 3);
+      const int b = p0 >> 7, g0 = (p0 & 127) >> 5;
+      const int npos = (int)min<int64_t>(kBrickK, L.K - brick * kBrickK);
+      for (int hh = 0; hh < 2 && 32 * hh < npos; ++hh) {
+        const int64_t s2 = (((row >> 4) * L.quads + q) << 6) | ((row & 15) + 16 * (g0 + hh));
+        const uint32_t cw = reinterpret_cast<const uint32_t*>(code_plane + s2 * 16)[2 * b];
+        uint32_t bits = 0;
+        for (int j = 0; j < 16; ++j)
+          bits |= ref_code(pos_value((cw >> sp24_code_bit(j)) & 3u)) << (2 * j);
+        const int nbytes = min(4, (npos - 32 * hh + 7) / 8);  // 8 positions -> one code byte
+        for (int i = 0; i < nbytes && 4 * hh + i < cnt; ++i) dst[4 * hh + i] = (uint8_t)(bits >> (8 * i));
+      }
+    } else if (L.positional) {
       uint32_t mask[2], codes[4];
       load_brick(L, mask_plane, code_plane, slot, mask, codes);
       const int npos = (int)min<int64_t>(kBrickK, L.K - brick * kBrickK);
@@ -297,16 +366,17 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
-#define SBN_PACK(MM, POS)                                                                     \
-  hipLaunchKernelGGL((pack_fragments<MM, POS>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
+#define SBN_PACK(MM, FF)                                                                      \
+  hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
                      h->mask, h->codes)
-  const bool pos = L.positional != 0;
-  if (L.m == 4) {
-    if (pos) SBN_PACK(4, true); else SBN_PACK(4, false);
+  if (L.form == kFormSparse24) {
+    SBN_PACK(4, kFormSparse24);
+  } else if (L.m == 4) {
+    if (L.positional) SBN_PACK(4, kFormPositional); else SBN_PACK(4, kFormKept);
   } else if (L.m == 8) {
-    if (pos) SBN_PACK(8, true); else SBN_PACK(8, false);
+    if (L.positional) SBN_PACK(8, kFormPositional); else SBN_PACK(8, kFormKept);
   } else {
-    if (pos) SBN_PACK(16, true); else SBN_PACK(16, false);
+    if (L.positional) SBN_PACK(16, kFormPositional); else SBN_PACK(16, kFormKept);
   }
 #undef SBN_PACK
   return hipGetLastError();

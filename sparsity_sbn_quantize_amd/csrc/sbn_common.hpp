@@ -12,13 +12,19 @@
 // reads one contiguous block. Rows are padded to a multiple of 256 and bricks to a multiple of 4
 // with zero bricks (all pruned, code 0). The mask plane and the code plane are separate arrays.
 //
-// Codes come in one of two forms:
+// Codes come in one of three forms:
 //   - positional (2n >= m: 2:4, 4:8, 6:8, 8:16 and dense n == m). Every position of the brick has
 //     a 2-bit code, 0 where pruned: 16 bytes per brick, as many bits per weight as the reference
 //     format's kept codes plus mask when n == m/2 and fewer when n > m/2 (e.g. 2 vs 2.5 bits for
 //     6:8). The forward reads only this plane. Position p is at bits [8i + 2q, 8i + 2q + 2) of
 //     code word w, where p = 16w + 4q + i, with 00 = 0, 01 = +1, 10 = -1; so the sixteen
 //     positions of word w become int8 bytes with nine ALU ops (exp_word_to_i8).
+//   - sparse 2:4 (the operands of gfx950's structured-sparse MFMA v_smfmac_i32_16x16x128_i8):
+//     per lane (row r = lane % 16, lane group g = lane / 16) and 256-K quad, four words: for each
+//     128-K block b, a code word with the 16 kept codes of K [128b + 32g, 128b + 32g + 32) (slot j
+//     = the lower (j even) or higher (j odd) kept position of group j / 2 of 4; slot 4q + i at bits
+//     8i + 2q, positional values), then an index word (slot j's position in its group at bits
+//     [2j, 2j + 2)). 16 bytes per lane per quad, the same as positional codes.
 //   - kept (2n < m): the n kept codes of each group in ascending position, 2-bit two's complement
 //     (00 = 0, 01 = +1, 11 = -1), code i of the brick at bits [2i, 2i+2): exactly the reference
 //     bitstream, 16n/m bytes per brick. Decoded with decode_kept_brick.
@@ -34,11 +40,14 @@ constexpr int kFragRows = 16;       // rows per fragment
 constexpr int kFragBricks = 4;      // bricks per fragment (along K)
 constexpr int kQuadK = kBrickK * kFragBricks;  // 256 K positions per fragment
 
+enum CodeForm : int { kFormPositional = 0, kFormKept = 1, kFormSparse24 = 2 };
+
 struct Layout {
   int64_t n_out, K;
   int n, m;
-  int positional;        // 2n >= m: positional codes (16 bytes per brick)
-  int code_brick_bytes;  // positional ? 16 : 16 n / m
+  int form;              // CodeForm
+  int positional;        // form != kFormKept: 16 code bytes per lane and quad
+  int code_brick_bytes;  // 16, or 16 n / m for the kept form
   int has_mask;          // n < m
   int64_t row_blocks;    // ceil(n_out / 16)
   int64_t row_blocks_pad;  // row_blocks rounded up to kPadRowBlocks (stored, zero-filled)
@@ -50,6 +59,13 @@ struct Layout {
 constexpr int kPadRowBlocks = 16;
 
 __host__ __device__ constexpr bool positional_codes(int n, int m) { return 2 * n >= m; }
+
+// Sparse 2:4 form: dense positions (0..31 of the lane's 32) of the 16 slots of a code/index pair.
+__device__ __forceinline__ int sp24_pos(uint32_t index_word, int j) {
+  return 4 * (j >> 1) + (int)((index_word >> (2 * j)) & 3u);
+}
+// Slot j's code bits inside a code word (slot 4q + i at bits 8i + 2q).
+__host__ __device__ constexpr int sp24_code_bit(int j) { return 8 * (j & 3) + 2 * (j >> 2); }
 
 __host__ __device__ inline int64_t brick_slot(const Layout& L, int64_t row, int64_t brick) {
   const int64_t rb = row >> 4, bq = brick >> 2;

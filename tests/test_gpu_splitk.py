@@ -56,3 +56,27 @@ def test_split_k_repeated_calls_and_prefill_down():
     assert np.array_equal(ys[0][:, rows], acc_ref)
     pw.free()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 150, 300])
+def test_sparse_mfma_2of4_matches_dense_path(T, monkeypatch):
+    """2:4 handles use the structured-sparse MFMA (kept weights + position indices); with
+    SBN_NO_SMFMAC=1 they use positional codes and the dense MFMA. Both must give the same int32
+    accumulators, fp32 outputs and exports, equal to the oracle."""
+    import torch
+    x, w = _case(100 + T, T, 2560, 300)
+    res = {}
+    for flag in ("0", "1"):
+        monkeypatch.setenv("SBN_NO_SMFMAC", flag)
+        g = gu.gpu_forward(x, w, 2, 4)
+        gu.check_stages(g, x, w, 2, 4)
+        res[flag] = g
+        xd = gu.to_dev_bf16(x)
+        pw = binding.PackedWeight(gu.to_dev_f32(w), 2, 4)
+        y, _, _ = binding.bitlinear_bf16(xd, pw)
+        res[flag + "_bf16"] = y.cpu().numpy()
+        pw.free()
+    for key in ("acc", "y", "codes", "keep", "code_bytes", "mask_bytes"):
+        assert np.array_equal(res["0"][key], res["1"][key]), key
+    assert np.array_equal(res["0_bf16"], res["1_bf16"])
+    torch.cuda.synchronize()
