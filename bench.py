@@ -411,13 +411,34 @@ def run_train(gpu, args, layer_index, pattern, steps):
         res[name] = gpu.time_graph(g) / steps
     pb = pack_bytes(N, K, n, m)
     ops = 2.0 * T * K * N
+    out = {"layer": layer.name, "pattern": f"{n}:{m}", "tokens": T, "K": K, "n_out": N,
+           "ms_per_step": res["step"], "pack_us": res["pack"] * 1e3,
+           "pack_GBps": pb / (res["pack"] * 1e-3) / 1e9,
+           "pack_frac_hbm": pb / (res["pack"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "gemm_us": res["gemm"] * 1e3, "gemm_TOPS": ops / (res["gemm"] * 1e-3) / 1e12,
+           "gemm_frac_int8": ops / (res["gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    if (n, m) == (2, 4):
+        # 2:4 runs on the structured-sparse MFMA; time the dense-MFMA path on the same weights
+        # (positional codes) beside it, and check that both give the same output.
+        y_sp = y.clone()
+        os.environ["SBN_NO_SMFMAC"] = "1"
+        try:
+            pd = gpu.b.PackedWeight(wd, n, m)
+        finally:
+            del os.environ["SBN_NO_SMFMAC"]
+        yd = torch.empty_like(y)
+        gpu.b.bitlinear(q, a, pd, out="f32", y=yd)
+        torch.cuda.synchronize()
+        assert torch.equal(yd, y_sp), "dense and structured-sparse MFMA paths differ"
+        g = gpu.graph(lambda i: gpu.b.bitlinear(q, a, pd, out="f32", y=yd), steps)
+        g.replay()
+        dense_ms = gpu.time_graph(g) / steps
+        pd.free()
+        out["gemm"] = "structured-sparse MFMA (v_smfmac_i32_16x16x128_i8)"
+        out["gemm_dense_mfma_us"] = dense_ms * 1e3
+        out["gemm_dense_mfma_frac_int8"] = ops / (dense_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS
     pw.free()
-    return {"layer": layer.name, "pattern": f"{n}:{m}", "tokens": T, "K": K, "n_out": N,
-            "ms_per_step": res["step"], "pack_us": res["pack"] * 1e3,
-            "pack_GBps": pb / (res["pack"] * 1e-3) / 1e9,
-            "pack_frac_hbm": pb / (res["pack"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "gemm_us": res["gemm"] * 1e3, "gemm_TOPS": ops / (res["gemm"] * 1e-3) / 1e12,
-            "gemm_frac_int8": ops / (res["gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+    return out
 
 
 def profile_copy(gpu, args):

@@ -35,7 +35,10 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return r;  // valid in thread 0
 }
 
-// Stage 1: block b sums |w| over rows [b*n_out/B, (b+1)*n_out/B) in fp64.
+// Stage 1: block b sums |w| over rows [b*n_out/B, (b+1)*n_out/B) in fp64. When rows are
+// contiguous (ld_w == K) and 16-byte aligned, the block's rows are one flat float4 range read
+// with four loads in flight per thread into four accumulators, combined in a fixed order; the
+// grid is fixed per shape, so the sum (and gamma) is the same on every run.
 __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* __restrict__ w,
                                                                    int64_t n_out, int64_t K,
                                                                    int64_t ld_w, int vec4,
@@ -44,14 +47,29 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* 
   const int64_t B = gridDim.x;
   const int64_t r0 = n_out * blockIdx.x / B, r1 = n_out * (blockIdx.x + 1) / B;
   double acc = 0.0;
-  if (vec4) {
+  auto abs4 = [](const float4 f) -> double {
+    return (double)fabsf(f.x) + (double)fabsf(f.y) + (double)fabsf(f.z) + (double)fabsf(f.w);
+  };
+  if (vec4 && ld_w == K) {
+    const float4* base = reinterpret_cast<const float4*>(w + r0 * ld_w);
+    const int64_t n4 = (r1 - r0) * (K >> 2);
+    constexpr int kU = 4;
+    double a[kU] = {0.0, 0.0, 0.0, 0.0};
+    int64_t i = threadIdx.x;
+    for (; i + (kU - 1) * kAbsmeanThreads < n4; i += kU * kAbsmeanThreads) {
+      float4 f[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) f[u] = base[i + u * kAbsmeanThreads];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) a[u] += abs4(f[u]);
+    }
+    for (; i < n4; i += kAbsmeanThreads) a[0] += abs4(base[i]);
+    acc = (a[0] + a[1]) + (a[2] + a[3]);
+  } else if (vec4) {
     const int64_t kv = K >> 2;
     for (int64_t r = r0; r < r1; ++r) {
       const float4* row = reinterpret_cast<const float4*>(w + r * ld_w);
-      for (int64_t i = threadIdx.x; i < kv; i += kAbsmeanThreads) {
-        const float4 f = row[i];
-        acc += (double)fabsf(f.x) + (double)fabsf(f.y) + (double)fabsf(f.z) + (double)fabsf(f.w);
-      }
+      for (int64_t i = threadIdx.x; i < kv; i += kAbsmeanThreads) acc += abs4(row[i]);
     }
   } else {
     for (int64_t r = r0; r < r1; ++r) {
@@ -157,22 +175,25 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
   for (int i = 0; i < 16; ++i) nz |= (a[i] > half_bits ? 1u : 0u) << i;
   nz &= keep;
   if constexpr (kSp24) {
-    // slots 8h + 2q (lower kept) and 8h + 2q + 1 (higher kept) of group q of the 16 positions
+    // slots 8h + 2q (lower kept) and 8h + 2q + 1 (higher kept) of group q of the 16 positions:
+    // the two set bits of the group's keep nibble (none in padding groups: slots stay zero).
+    // The code of position p is nz_p << sign_p (0, 1 = +1, 2 = -1).
     const int h = word & 1;
+    uint32_t sgn = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sgn |= (u[i] >> 31) << i;
     uint32_t cw = 0, iw = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      int slot = 8 * h + 2 * q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pidx = 4 * q + i;
-        if ((keep >> pidx) & 1u) {
-          const uint32_t c = ((nz >> pidx) & 1u) ? ((u[pidx] >> 31) ? 2u : 1u) : 0u;
-          cw |= c << sp24_code_bit(slot);
-          iw |= (uint32_t)i << (2 * slot);
-          ++slot;
-        }
-      }
+      const uint32_t k4 = (keep >> (4 * q)) & 0xFu;
+      const uint32_t lo = k4 ? (uint32_t)__builtin_ctz(k4) : 0u;
+      const uint32_t hi = k4 ? 31u - (uint32_t)__builtin_clz(k4) : 0u;
+      const uint32_t plo = 4 * q + lo, phi = 4 * q + hi;
+      const uint32_t clo = k4 ? ((nz >> plo) & 1u) << ((sgn >> plo) & 1u) : 0u;
+      const uint32_t chi = k4 ? ((nz >> phi) & 1u) << ((sgn >> phi) & 1u) : 0u;
+      const int slot = 8 * h + 2 * q;
+      cw |= (clo << sp24_code_bit(slot)) | (chi << sp24_code_bit(slot + 1));
+      iw |= (lo << (2 * slot)) | (hi << (2 * slot + 2));
     }
     const int src = (int)(threadIdx.x & 63);
     const uint32_t ocw = (uint32_t)__shfl(cw, src ^ 1, 64);
