@@ -147,6 +147,16 @@ sbn_status sbn_packed_export(const sbn_packed* w, int8_t* codes, uint8_t* keep_m
 sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8_t* mask_bytes,
                                  void* stream);
 
+/*
+ * Keep-mask changes of the handle's last pack: the number of positions whose keep bit differs from
+ * the pack before it (the first pack of a handle compares against an empty mask, so it counts
+ * every kept position). flips / (n_out * K) is the mask flip rate r_t of Sparse-BitNet, Figure 3
+ * (b) (the equation's text is not on the page; this is its plainest reading). Always 0 when
+ * n == m. Enqueued on `stream`:
+ *   flips     [1] uint64 out (device).
+ */
+sbn_status sbn_packed_mask_flips(const sbn_packed* w, uint64_t* flips, void* stream);
+
 typedef struct {
   int64_t n_out, K;
   int n, m;

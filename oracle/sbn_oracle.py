@@ -14,7 +14,8 @@ Sources (page titles, with the section each step follows):
   [Sparse-BitNet] "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to Semi-Structured
                   Sparsity", Abstract (dynamic N:M sparsification jointly with 1.58-bit
                   quantization), Figure 6 (per-block threshold = the (N+1)-th largest normalized
-                  magnitude, i.e. the N largest of each M-block are kept), Table 6 (N:8 sweep).
+                  magnitude, i.e. the N largest of each M-block are kept), Table 6 (N:8 sweep),
+                  Figure 3 (b) (mask flip rate r_t between consecutive masks).
   [8:16]          "From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights with
                   Variance Correction", abstract / Core claim (8:16 pattern; 0.875 vs 0.75
                   metadata bits per element).
@@ -35,6 +36,8 @@ Readings taken where the pages are silent or disagree (each is also listed in th
     n < m, a mask bitstream (m bits per group, bit i <-> position i of the group, LSB first); each
     stream is padded with zero bits to a whole byte per row;
   * the output is fp32 y = fl32(fl32(fl32(acc) * gamma) * fl32(a' / 127)).
+  * the mask flip rate r_t counts positions whose keep bit differs between consecutive masks,
+    divided by the number of weights; a first mask is compared with one that keeps nothing.
 
 Floating point follows the precision the path decides integers in (fp32 scale and product); the
 weight-scale sum is accumulated in fp64.
@@ -233,6 +236,25 @@ def bitlinear_forward(x_bf16: np.ndarray, w: np.ndarray, n: int, m: int) -> dict
     acc = int_matmul(q, packed["codes"])
     y = dequantize(acc, packed["gamma"], a_prime)
     return dict(packed, q=q, a_prime=a_prime, acc=acc, y=y)
+
+
+# ----------------------------------------------------------------------------------------------
+# Mask flips between consecutive re-packs: [Sparse-BitNet] Figure 3 (b), the mask flip rate r_t.
+# The page plots r_t but does not print its formula; the plainest reading is the share of weight
+# positions whose keep decision differs between two consecutive masks.
+# ----------------------------------------------------------------------------------------------
+
+def mask_flips(keep_prev, keep_new) -> int:
+    """Number of positions whose keep bit differs between two masks of the same shape.
+
+    ``keep_prev`` may be None, which stands for a mask that keeps nothing (no earlier pack).
+    r_t = mask_flips(prev, new) / new.size.
+    """
+    new = np.asarray(keep_new, dtype=bool)
+    prev = np.zeros_like(new) if keep_prev is None else np.asarray(keep_prev, dtype=bool)
+    if prev.shape != new.shape:
+        raise ValueError(f"mask shapes differ: {prev.shape} vs {new.shape}")
+    return int(np.count_nonzero(prev != new))
 
 
 # ----------------------------------------------------------------------------------------------

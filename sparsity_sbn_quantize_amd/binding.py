@@ -49,6 +49,7 @@ _SIGNATURES = {
     "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
+    "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
     "sbn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -175,6 +176,14 @@ class PackedWeight:
                                           _ptr(mb) if d.mask_row_bytes else ctypes.c_void_p(0),
                                           _stream(stream)))
         return cb, mb
+
+    def mask_flips(self, stream=None):
+        """Keep bits changed by the last pack (int64 tensor [1] on the device)."""
+        import torch
+        dev = torch.device("cuda", torch.cuda.current_device())
+        out = torch.zeros((1,), dtype=torch.int64, device=dev)
+        check(lib().sbn_packed_mask_flips(self.handle, _ptr(out), _stream(stream)))
+        return out
 
     def free(self):
         if self._h:

@@ -83,8 +83,10 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* 
 
 // Stage 2: one block combines the partials in a fixed order and writes gamma.
 __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
-    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma) {
+    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma,
+    unsigned long long* __restrict__ flips) {
   __shared__ double red[kAbsmeanThreads / 64];
+  if (threadIdx.x == 0) flips[0] = 0;  // the pack that follows counts its mask changes here
   double acc = 0.0;
   for (int i = threadIdx.x; i < num; i += kAbsmeanThreads) acc += partials[i];
   const double s = block_sum_f64(acc, red);
@@ -130,7 +132,8 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
                                                       int vec4, Layout L,
                                                       const float* __restrict__ gamma_p,
                                                       uint8_t* __restrict__ mask_plane,
-                                                      uint8_t* __restrict__ code_plane) {
+                                                      uint8_t* __restrict__ code_plane,
+                                                      unsigned long long* __restrict__ flips) {
   const int64_t frag = blockIdx.x;
   const int64_t rb = frag / L.quads, bq = frag % L.quads;
   const int tid = threadIdx.x;
@@ -233,13 +236,21 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
     }
   }
   if (L.has_mask) {
+    // Mask flips (Sparse-BitNet, Figure 3 (b), the mask flip rate r_t): keep bits that differ
+    // from the previous pack's, read before they are overwritten; one atomic add per wave.
+    uint16_t* mp = reinterpret_cast<uint16_t*>(mask_plane) + frag * 256 + tid;
     if constexpr (kSp24) {
       // mask plane in brick layout: brick qpos / 64 of the quad, bits (qpos % 64) .. +15
       const int64_t mslot = (frag << 6) | ((lane_slot & 15) + 16 * (qpos >> 6));
-      reinterpret_cast<uint16_t*>(mask_plane)[mslot * 4 + ((qpos & 63) >> 4)] = (uint16_t)keep;
-    } else {
-      reinterpret_cast<uint16_t*>(mask_plane)[frag * 256 + tid] = (uint16_t)keep;
+      mp = reinterpret_cast<uint16_t*>(mask_plane) + mslot * 4 + ((qpos & 63) >> 4);
     }
+    const uint32_t changed = (uint32_t)__builtin_popcount((uint32_t)(*mp ^ (uint16_t)keep));
+    *mp = (uint16_t)keep;
+    uint32_t sum = changed;
+    for (int o = 32; o >= 1; o >>= 1) sum += (uint32_t)__shfl_xor((int)sum, o, 64);
+    if ((threadIdx.x & 63) == 0 && sum != 0)
+      __hip_atomic_fetch_add(flips, (unsigned long long)sum, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -367,6 +378,7 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
 }
 
 __global__ void copy_gamma(const float* src, float* dst) { dst[0] = src[0]; }
+__global__ void copy_u64(const unsigned long long* src, unsigned long long* dst) { dst[0] = src[0]; }
 
 }  // namespace
 
@@ -383,13 +395,14 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
                        L.n_out, L.K, ld_w, vec4, h->partials);
   }
   hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
-                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma);
+                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
+                     h->flips);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
 #define SBN_PACK(MM, FF)                                                                      \
   hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
-                     h->mask, h->codes)
+                     h->mask, h->codes, h->flips)
   if (L.form == kFormSparse24) {
     SBN_PACK(4, kFormSparse24);
   } else if (L.m == 4) {
@@ -429,4 +442,12 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
   return hipGetLastError();
 }
 
+}  // namespace sbn
+
+namespace sbn {
+hipError_t launch_copy_flips(const sbn_packed* h, uint64_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(copy_u64, dim3(1), dim3(1), 0, s, h->flips,
+                     reinterpret_cast<unsigned long long*>(out));
+  return hipGetLastError();
+}
 }  // namespace sbn

@@ -452,3 +452,54 @@ def test_boundary_counters():
     assert b[0].tolist() == [False, True, True, False]
     w = np.array([[0.5, 0.5, 0.5, 0.5, 1.5, 1.5, 1.5, 1.5]], np.float32)
     assert oracle.boundary_elements_weight(w, np.float32(1.0))[0].tolist() == [True] * 4 + [False] * 4
+
+
+# ---------------------------------------------------------------------------------------------
+# Mask flips between consecutive masks (Sparse-BitNet, Figure 3 (b), mask flip rate r_t).
+# ---------------------------------------------------------------------------------------------
+
+def test_mask_flips_hand_example():
+    """2:4 on one row of two groups. Group 0 reverses its magnitude order, so the kept pair
+    {0, 1} becomes {2, 3} (four positions change); group 1 keeps {2, 3} both times."""
+    w1 = np.array([[4, 3, 2, 1, 1, 2, 3, 4]], dtype=np.float32)
+    w2 = np.array([[1, 2, 3, 4, 1, 2, 3, 4]], dtype=np.float32)
+    k1, k2 = oracle.nm_keep_mask(w1, 2, 4), oracle.nm_keep_mask(w2, 2, 4)
+    assert k1.astype(int).tolist() == [[1, 1, 0, 0, 0, 0, 1, 1]]
+    assert k2.astype(int).tolist() == [[0, 0, 1, 1, 0, 0, 1, 1]]
+    assert oracle.mask_flips(k1, k2) == 4
+    assert oracle.mask_flips(None, k1) == 4  # first mask: every kept position counts
+
+
+def test_mask_flips_brute_force_and_metric():
+    """Against a pure-Python bit count; symmetric; zero only for equal masks; triangle
+    inequality; complement gives every position."""
+    rng = np.random.default_rng(5)
+    a, b, c = (rng.random((7, 24)) < 0.4 for _ in range(3))
+    brute = sum(1 for i in range(7) for j in range(24) if bool(a[i, j]) != bool(b[i, j]))
+    assert oracle.mask_flips(a, b) == brute
+    assert oracle.mask_flips(b, a) == brute
+    assert oracle.mask_flips(a, a) == 0
+    assert oracle.mask_flips(a, c) <= oracle.mask_flips(a, b) + oracle.mask_flips(b, c)
+    assert oracle.mask_flips(a, ~a) == a.size
+    with pytest.raises(ValueError):
+        oracle.mask_flips(a, b[:, :8])
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_mask_flips_nm_structure(n, m):
+    """Two n:m masks keep n per group each, so a group changes an even number of positions, at
+    most 2*min(n, m - n); a first mask counts n per group; positive scaling keeps the mask and
+    n == m never flips."""
+    rng = np.random.default_rng(31 * n + m)
+    N, K = 9, 4 * m
+    w1 = rng.standard_normal((N, K)).astype(np.float32)
+    w2 = (w1 + 0.7 * rng.standard_normal((N, K))).astype(np.float32)
+    k1, k2 = oracle.nm_keep_mask(w1, n, m), oracle.nm_keep_mask(w2, n, m)
+    per_group = (k1 != k2).reshape(N, -1, m).sum(axis=2)
+    assert np.all(per_group % 2 == 0)
+    assert np.all(per_group <= 2 * min(n, m - n))
+    assert oracle.mask_flips(k1, k2) == int(per_group.sum())
+    assert oracle.mask_flips(None, k1) == N * K * n // m
+    assert oracle.mask_flips(k1, oracle.nm_keep_mask(w1 * np.float32(3), n, m)) == 0
+    if n == m:
+        assert oracle.mask_flips(k1, k2) == 0
