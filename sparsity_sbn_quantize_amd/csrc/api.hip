@@ -121,7 +121,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     const size_t off_sync = off;
     off = align_up(off + sizeof(int) * sbn::kGemmSyncInts, 256);
     const size_t off_flips = off;
-    off = align_up(off + sizeof(unsigned long long), 256);
+    off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
 
     h = new (std::nothrow) sbn_packed;
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
@@ -156,7 +156,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     h->gamma = reinterpret_cast<float*>(h->base + off_gamma);
     h->partials = reinterpret_cast<double*>(h->base + off_part);
     h->gemm_sync = reinterpret_cast<int*>(h->base + off_sync);
-    h->flips = reinterpret_cast<unsigned long long*>(h->base + off_flips);
+    h->flip_parts = reinterpret_cast<uint32_t*>(h->base + off_flips);
     *handle = h;
   }
   h->last_stream = s;
@@ -245,7 +245,7 @@ sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8
 
 sbn_status sbn_packed_mask_flips(const sbn_packed* w, uint64_t* flips, void* stream) {
   if (!w || !flips) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_mask_flips: null pointer");
-  hipError_t e = sbn::launch_copy_flips(w, flips, (hipStream_t)stream);
+  hipError_t e = sbn::launch_sum_flips(w, flips, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_packed_mask_flips launch");
   return SBN_OK;
 }

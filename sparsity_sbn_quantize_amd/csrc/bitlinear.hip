@@ -622,7 +622,6 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   // Each lane holds 4 consecutive rows of one token per (rf, cf): one 16-byte access when the
   // output rows are 16-byte aligned and all 4 rows exist.
   const bool vec_out = (((uintptr_t)y | (uintptr_t)(ld_y * 4)) & 15) == 0;
-  int32_t* const yi = reinterpret_cast<int32_t*>(y);
   if (ksplit > 1) {
     // Every access of the handshake is coherent across the XCDs' L2 caches on its own (sc1:
     // relaxed agent-scope atomics for the flags, sc1 buffer accesses for the partial sums);

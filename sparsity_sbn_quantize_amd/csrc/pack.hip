@@ -83,10 +83,8 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* 
 
 // Stage 2: one block combines the partials in a fixed order and writes gamma.
 __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
-    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma,
-    unsigned long long* __restrict__ flips) {
+    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma) {
   __shared__ double red[kAbsmeanThreads / 64];
-  if (threadIdx.x == 0) flips[0] = 0;  // the pack that follows counts its mask changes here
   double acc = 0.0;
   for (int i = threadIdx.x; i < num; i += kAbsmeanThreads) acc += partials[i];
   const double s = block_sum_f64(acc, red);
@@ -133,7 +131,7 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
                                                       const float* __restrict__ gamma_p,
                                                       uint8_t* __restrict__ mask_plane,
                                                       uint8_t* __restrict__ code_plane,
-                                                      unsigned long long* __restrict__ flips) {
+                                                      uint32_t* __restrict__ flip_parts) {
   const int64_t frag = blockIdx.x;
   const int64_t rb = frag / L.quads, bq = frag % L.quads;
   const int tid = threadIdx.x;
@@ -145,6 +143,15 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
                          : kBrickK * (lane_slot >> 4) + 16 * word;
   const int64_t k0 = bq * kQuadK + qpos;
   const int cnt = row < L.n_out ? (int)max<int64_t>(0, min<int64_t>(16, L.K - k0)) : 0;
+  // This thread's 16 keep bits in the mask plane; the previous pack's bits are loaded first, so the
+  // load overlaps the weight loads.
+  uint16_t* mp = reinterpret_cast<uint16_t*>(mask_plane) + frag * 256 + tid;
+  if constexpr (kSp24) {
+    // mask plane in brick layout: brick qpos / 64 of the quad, bits (qpos % 64) .. +15
+    const int64_t mslot = (frag << 6) | ((lane_slot & 15) + 16 * (qpos >> 6));
+    mp = reinterpret_cast<uint16_t*>(mask_plane) + mslot * 4 + ((qpos & 63) >> 4);
+  }
+  const uint32_t old_keep = L.has_mask ? (uint32_t)*mp : 0u;
   const float* wr = w + row * ld_w + k0;
   uint32_t u[16];
   if (vec4 && cnt == 16) {
@@ -237,20 +244,11 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
   }
   if (L.has_mask) {
     // Mask flips (Sparse-BitNet, Figure 3 (b), the mask flip rate r_t): keep bits that differ
-    // from the previous pack's, read before they are overwritten; one atomic add per wave.
-    uint16_t* mp = reinterpret_cast<uint16_t*>(mask_plane) + frag * 256 + tid;
-    if constexpr (kSp24) {
-      // mask plane in brick layout: brick qpos / 64 of the quad, bits (qpos % 64) .. +15
-      const int64_t mslot = (frag << 6) | ((lane_slot & 15) + 16 * (qpos >> 6));
-      mp = reinterpret_cast<uint16_t*>(mask_plane) + mslot * 4 + ((qpos & 63) >> 4);
-    }
-    const uint32_t changed = (uint32_t)__builtin_popcount((uint32_t)(*mp ^ (uint16_t)keep));
+    // from the previous pack's. Each wave's count goes to its own slot (no atomics, no barrier);
+    // the slots are summed only when the count is asked for.
     *mp = (uint16_t)keep;
-    uint32_t sum = changed;
-    for (int o = 32; o >= 1; o >>= 1) sum += (uint32_t)__shfl_xor((int)sum, o, 64);
-    if ((threadIdx.x & 63) == 0 && sum != 0)
-      __hip_atomic_fetch_add(flips, (unsigned long long)sum, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t sum = wave_sum_u32((uint32_t)__builtin_popcount((old_keep ^ keep) & 0xFFFFu));
+    if ((tid & 63) == 0) flip_parts[frag * 4 + (tid >> 6)] = sum;
   }
 }
 
@@ -378,7 +376,21 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
 }
 
 __global__ void copy_gamma(const float* src, float* dst) { dst[0] = src[0]; }
-__global__ void copy_u64(const unsigned long long* src, unsigned long long* dst) { dst[0] = src[0]; }
+// Sum of the per-wave flip counts of the last pack (one workgroup; num may be 0).
+__global__ __launch_bounds__(1024) void sum_flips(const uint32_t* __restrict__ parts, int64_t num,
+                                                  unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long red[16];
+  unsigned long long acc = 0;
+  for (int64_t i = threadIdx.x; i < num; i += 1024) acc += parts[i];
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+    for (int i = 0; i < 16; ++i) t += red[i];
+    out[0] = t;
+  }
+}
 
 }  // namespace
 
@@ -395,14 +407,13 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
                        L.n_out, L.K, ld_w, vec4, h->partials);
   }
   hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
-                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
-                     h->flips);
+                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
 #define SBN_PACK(MM, FF)                                                                      \
   hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
-                     h->mask, h->codes, h->flips)
+                     h->mask, h->codes, h->flip_parts)
   if (L.form == kFormSparse24) {
     SBN_PACK(4, kFormSparse24);
   } else if (L.m == 4) {
@@ -445,8 +456,10 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 }  // namespace sbn
 
 namespace sbn {
-hipError_t launch_copy_flips(const sbn_packed* h, uint64_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(copy_u64, dim3(1), dim3(1), 0, s, h->flips,
+hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s) {
+  const Layout& L = h->L;
+  const int64_t num = (L.has_mask && L.n_out > 0) ? L.row_blocks_pad * L.quads * 4 : 0;
+  hipLaunchKernelGGL(sum_flips, dim3(1), dim3(1024), 0, s, h->flip_parts, num,
                      reinterpret_cast<unsigned long long*>(out));
   return hipGetLastError();
 }

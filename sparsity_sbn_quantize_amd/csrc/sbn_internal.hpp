@@ -19,7 +19,7 @@ struct sbn_packed {
   float* gamma;        // device scalar
   double* partials;    // device workspace [num_partials]
   int* gemm_sync;      // split-K flags: kGemmSyncInts words, zero between calls
-  unsigned long long* flips;  // keep bits changed by the last pack
+  uint32_t* flip_parts;  // keep bits changed by the last pack, one count per pack wave
   int device;
   hipStream_t last_stream;
 };
@@ -43,7 +43,7 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
-hipError_t launch_copy_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
+hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
                                  int out_kind, hipStream_t s);
