@@ -336,7 +336,10 @@ constexpr int kTileGroup = 4;
 // for the flag (a bounded spin: the first is already past its main loop, so it is running), adds
 // the partial and writes the result. Integer sums make the result independent of the order. The
 // two flag words per tile and wave live in the weight handle and are cleared by the second half,
-// so calls that share a handle must be ordered (one stream, or synchronized).
+// so calls that share a handle must be ordered (one stream, or synchronized). Sharing tiles more
+// widely (a contiguous share of all tiles' K steps for every resident workgroup, or three
+// workgroups per tile) was measured slower on the 2048- and 8192-token shapes: the partial sums
+// then move about as many bytes as the fp32 output, all at the same moment.
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
 constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
@@ -406,12 +409,10 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   const __amdgpu_buffer_rsrc_t crsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, 0x7FFFFFFF, kBufDword3);
   const int lane_c = lane * cbb;
-  // This thread's activation pieces: wave-instruction i covers 4 tokens (lane / 16) x 16 chunk
-  // positions (lane % 16); position p of token `tok` holds global chunk p ^ (tok % 16). Offsets
-  // are relative to the tile's first token row. The aligned path reads through a buffer resource
-  // whose range ends with the last activation row: pieces of tokens past T, or of the last row
-  // past K, read as zero (elsewhere a piece past K reads in-row data, harmless because the
-  // weights there are zero). Tokens past T are never stored.
+  // Activation pieces are read relative to the tile's first token row. The aligned path reads
+  // through buffer resources whose range ends with the last activation row: pieces of tokens past
+  // T, or of the last row past K, read as zero (elsewhere a piece past K reads in-row data,
+  // harmless because the weights there are zero). Tokens past T are never stored.
   const int8_t* const xt0 = xq + t0 * ld_q;
   const int64_t x_extent = (T - 1 - t0) * ld_q + K;  // bytes from xt0 to the end of row T-1
   // Activation tile layout in LDS: [16-token group cf][K chunk c (16 bytes)][token t], i.e. the
