@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GEMV)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
@@ -437,6 +438,28 @@ def run_train(gpu, args, layer_index, pattern, steps):
         out["gemm"] = "structured-sparse MFMA (v_smfmac_i32_16x16x128_i8)"
         out["gemm_dense_mfma_us"] = dense_ms * 1e3
         out["gemm_dense_mfma_frac_int8"] = ops / (dense_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS
+    # Straight-through data gradient on the same packed weights: dY bf16 [T][N] -> dX fp32 [T][K]
+    # on the bf16 MFMA. The first call after a pack also rebuilds the transposed code plane; the
+    # graph of pack + data gradient minus the two alone gives that kernel's time.
+    dy = gpu.bf16(inputs.grad_output(wl, layer_index, T))
+    dx = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    pw.pack(wd)
+    gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)
+    torch.cuda.synchronize()
+    dx_eager = dx.clone()
+    bw = {}
+    for name, fn in (("bwd", lambda i: gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)),
+                     ("pack_bwd", lambda i: (pw.pack(wd), gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)))):
+        g = gpu.graph(fn, steps)
+        g.replay()
+        bw[name] = gpu.time_graph(g) / steps
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_eager), "data-gradient graph replay differs from the eager call"
+    out["bwd_dx_us"] = bw["bwd"] * 1e3
+    out["bwd_dx_TFLOPS"] = ops / (bw["bwd"] * 1e-3) / 1e12
+    out["bwd_dx_frac_bf16"] = out["bwd_dx_TFLOPS"] / BF16_PEAK_TFLOPS
+    out["bwd_transpose_us"] = max(0.0, (bw["pack_bwd"] - bw["bwd"] - res["pack"]) * 1e3)
+    del dy, dx, dx_eager
     pw.free()
     return out
 

@@ -122,6 +122,22 @@ sbn_status sbn_bitlinear_fwd_bf16(const sbn_packed* w, const uint16_t* x_bf16, i
                                   int64_t ld_y, sbn_out_kind out_kind, void* stream);
 
 /*
+ * Data gradient of the layer under the straight-through estimator ("Microsoft BitNet 1.58: The
+ * Era of 1-Bit Large Language Models", section "Training with the Straight-Through Estimator":
+ * the backward pass treats both quantizers as the identity, so the gradient flows through the
+ * ternary weights gamma * C of the last pack).
+ *   dy_bf16   [T][ld_dy] bf16 bit patterns (uint16), the gradient of y, read only.
+ *   dx        [T][ld_dx] fp32 out: dx[t][k] = fl32( gamma * S ), S = sum_r dy[t][r] * code[r][k]
+ *             accumulated in fp32 (every product is exact; the order of the fp32 additions is
+ *             unspecified, so |S - exact| <= (n_out - 1) * 2^-24 * sum_r |dy[t][r] * code[r][k]|).
+ * The first call after a pack rebuilds the handle's transposed code plane (one extra kernel);
+ * later calls reuse it. n_out == 0 gives dx = 0.
+ * Requires T >= 0, n_out <= ld_dy <= 2^25, ld_dx >= K, n_out <= 2^27; T == 0 is a no-op.
+ */
+sbn_status sbn_bitlinear_bwd_dx(const sbn_packed* w, const uint16_t* dy_bf16, int64_t ld_dy,
+                                int64_t T, float* dx, int64_t ld_dx, void* stream);
+
+/*
  * Releases a handle: waits for the last stream that used it, then frees its device memory.
  * sbn_free(NULL) is a no-op.
  */

@@ -8,7 +8,9 @@ does, and it shares no code, table or helper with that path.
 Sources (page titles, with the section each step follows):
   [BitNet-blog]   "Microsoft BitNet 1.58: The Era of 1-Bit Large Language Models",
                   section "The BitLinear Layer" (five operations; the latent-weight paragraph
-                  after it) and "bitnet.cpp: Matrix-Free Inference" (four ternary values per byte).
+                  after it), "Training with the Straight-Through Estimator" (the backward pass
+                  treats the quantizers as the identity) and "bitnet.cpp: Matrix-Free Inference"
+                  (four ternary values per byte).
   [BitNet-index]  "BitNet b1.58: How Ternary Weights Cut LLM Memory by 82% Without Losing
                   Accuracy", section "How ternary quantization works during training".
   [Sparse-BitNet] "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to Semi-Structured
@@ -36,6 +38,8 @@ Readings taken where the pages are silent or disagree (each is also listed in th
     n < m, a mask bitstream (m bits per group, bit i <-> position i of the group, LSB first); each
     stream is padded with zero bits to a whole byte per row;
   * the output is fp32 y = fl32(fl32(fl32(acc) * gamma) * fl32(a' / 127)).
+  * the straight-through data gradient is dX = gamma * dY @ codes: both quantizers pass the
+    gradient unchanged, so only the ternary weights of the forward remain; dY is bf16, dX fp32;
   * the mask flip rate r_t counts positions whose keep bit differs between consecutive masks,
     divided by the number of weights; a first mask is compared with one that keeps nothing.
 
@@ -236,6 +240,31 @@ def bitlinear_forward(x_bf16: np.ndarray, w: np.ndarray, n: int, m: int) -> dict
     acc = int_matmul(q, packed["codes"])
     y = dequantize(acc, packed["gamma"], a_prime)
     return dict(packed, q=q, a_prime=a_prime, acc=acc, y=y)
+
+
+# ----------------------------------------------------------------------------------------------
+# Data gradient under the straight-through estimator: [BitNet-blog] "Training with the
+# Straight-Through Estimator" (the backward pass treats the quantizers as the identity) with the
+# forward of "The BitLinear Layer" (y from the ternary weights gamma * codes).
+# ----------------------------------------------------------------------------------------------
+
+def ste_dx(dy_bf16: np.ndarray, codes: np.ndarray, gamma: np.float32) -> np.ndarray:
+    """dX = gamma * dY @ codes (fp64, one rounding to fp32 at the end).
+
+    dy_bf16: bf16 bit patterns [T][n_out]; codes: ternary int8 [n_out][K]. Every product is a bf16
+    value or zero, and the fp64 sum of up to 2^20 of them is exact for gradients of ordinary range.
+    """
+    dy = bf16_to_f32(dy_bf16).astype(np.float64)
+    c = np.asarray(codes, dtype=np.float64)
+    return (np.float64(gamma) * (dy @ c)).astype(np.float32)
+
+
+def ste_dx_abs(dy_bf16: np.ndarray, codes: np.ndarray, gamma: np.float32) -> np.ndarray:
+    """gamma * |dY| @ |codes| (fp64): the magnitude that bounds the rounding error of any fp32
+    summation order of dX (recursive-summation bound)."""
+    dy = np.abs(bf16_to_f32(dy_bf16).astype(np.float64))
+    c = np.abs(np.asarray(codes, dtype=np.float64))
+    return np.float64(gamma) * (dy @ c)
 
 
 # ----------------------------------------------------------------------------------------------

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
     "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
+    "sbn_bitlinear_bwd_dx": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
     "sbn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -231,3 +232,17 @@ def bitlinear_bf16(x, w: PackedWeight, out: str = "f32", y=None, x_q=None, x_abs
                                        _ld(x_q, w.K), _ptr(x_absmax), _ptr(y), _ld(y, w.n_out),
                                        kind, _stream(stream)))
     return y, x_q, x_absmax
+
+
+def bitlinear_bwd_dx(dy, w: PackedWeight, dx=None, stream=None):
+    """Straight-through data gradient: dy bf16 [T][n_out] -> dx fp32 [T][K] = gamma * dy @ codes."""
+    import torch
+    _require_cuda(dy, "dy")
+    if dy.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("dy must be bfloat16 (or int16 bf16 bit patterns)")
+    T = dy.shape[0]
+    if dx is None:
+        dx = torch.empty((T, w.K), dtype=torch.float32, device=dy.device)
+    check(lib().sbn_bitlinear_bwd_dx(w.handle, _ptr(dy), _ld(dy, w.n_out), T, _ptr(dx),
+                                     _ld(dx, w.K), _stream(stream)))
+    return dx

@@ -122,6 +122,9 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     off = align_up(off + sizeof(int) * sbn::kGemmSyncInts, 256);
     const size_t off_flips = off;
     off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
+    const int64_t rq_count = (n_out + 127) / 128;
+    const size_t off_tplane = off;
+    off = align_up(off + (size_t)rq_count * (size_t)L.quads * 8192, 256);
 
     h = new (std::nothrow) sbn_packed;
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
@@ -157,9 +160,12 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     h->partials = reinterpret_cast<double*>(h->base + off_part);
     h->gemm_sync = reinterpret_cast<int*>(h->base + off_sync);
     h->flip_parts = reinterpret_cast<uint32_t*>(h->base + off_flips);
+    h->tplane = reinterpret_cast<uint32_t*>(h->base + off_tplane);
+    h->rq_count = rq_count;
     *handle = h;
   }
   h->last_stream = s;
+  h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
   hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
   if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
   return SBN_OK;
@@ -240,6 +246,33 @@ sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8
   if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_rpf: handle is null");
   hipError_t e = sbn::launch_export_rpf(w, code_bytes, mask_bytes, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_packed_export_rpf launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_bitlinear_bwd_dx(const sbn_packed* w, const uint16_t* dy_bf16, int64_t ld_dy,
+                                int64_t T, float* dx, int64_t ld_dx, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: handle is null");
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: T=%lld < 0", (long long)T);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_bwd_dx: T too large");
+  if (ld_dy < w->L.n_out)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: ld_dy=%lld < n_out=%lld",
+                (long long)ld_dy, (long long)w->L.n_out);
+  if (ld_dy > kMaxLdQ / 2)
+    return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_bwd_dx: ld_dy=%lld > %lld", (long long)ld_dy,
+                (long long)(kMaxLdQ / 2));
+  if (ld_dx < w->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: ld_dx=%lld < K=%lld",
+                (long long)ld_dx, (long long)w->L.K);
+  if (w->rq_count > (1 << 20))
+    return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_bwd_dx: n_out=%lld too large",
+                (long long)w->L.n_out);
+  if (T == 0) return SBN_OK;
+  if (!dx || (!dy_bf16 && w->L.n_out > 0))
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: null pointer");
+  sbn_packed* h = const_cast<sbn_packed*>(w);
+  h->last_stream = (hipStream_t)stream;
+  hipError_t e = sbn::launch_bwd_dx(h, dy_bf16, ld_dy, T, dx, ld_dx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_bwd_dx launch");
   return SBN_OK;
 }
 

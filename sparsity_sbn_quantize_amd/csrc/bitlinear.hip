@@ -26,8 +26,6 @@
 namespace sbn {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ v4i mfma16(const uint32_t* a, v4i b, v4i c) {
@@ -323,13 +321,6 @@ constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation
 constexpr int kXLoads = kGemmTok * 16 / kGemmThreads;   // 16-byte pieces per thread per step
 constexpr size_t kGemmSmem = (size_t)kXBufs * kTileBytes;
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2). The linear block
-// id is remapped so that every XCD receives one contiguous run of tiles in a grouped order
-// (kTileGroup token tiles x all N tiles, N-major within the group): the tiles an XCD has in
-// flight then share activation rows and packed weights in its L2.
-constexpr int kXcds = 8;
-constexpr int kTileGroup = 4;
-
 // Split-K (two workgroups per tile, each half of K) for launches with few tiles. The halves of a
 // tile are adjacent in the XCD order (same L2). Per tile and wave, the first half to finish
 // stores its int32 partial sums in the tile's region of y and raises a flag; the second waits
@@ -343,34 +334,6 @@ constexpr int kTileGroup = 4;
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
 constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
-
-// Position of block `bid` in the XCD-contiguous order.
-__device__ __forceinline__ int xcd_order(int nblocks, int bid) {
-  const int xcd = bid % kXcds, j = bid / kXcds;
-  const int base = nblocks / kXcds, extra = nblocks % kXcds;
-  return xcd * base + min(xcd, extra) + j;
-}
-
-// Tile of position `lin` in the grouped order.
-__device__ __forceinline__ void grouped_tile(int lin, int tiles_n, int tiles_t, int& tile_n,
-                                             int& tile_t) {
-  const int per_group = kTileGroup * tiles_n;
-  const int group = lin / per_group, r = lin % per_group;
-  const int gsize = min(kTileGroup, tiles_t - group * kTileGroup);
-  tile_n = r / gsize;
-  tile_t = group * kTileGroup + r % gsize;
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no stride): offsets are
-// bytes and reads at or past num_records return zero.
-constexpr int kBufDword3 = 0x00020000;
-
-// s_waitcnt immediate that waits until at most `n` vector-memory operations are outstanding and
-// does not wait on LDS/scalar or export counters (gfx9 encoding: vmcnt split over bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 template <int FORM, bool XVEC>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -721,17 +684,6 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
       }
     }
   }
-}
-
-// Raises a kernel's dynamic-LDS limit once per process (gfx950 has 160 KB of LDS per CU).
-template <typename K>
-hipError_t allow_smem(K kernel, size_t bytes) {
-  static size_t done = 0;
-  if (bytes <= done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done = bytes;
-  return e;
 }
 
 // Launches the GEMV with W = min(16, quads) waves and Q = ceil(quads / W) quads per wave.

@@ -266,17 +266,12 @@ __device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* mask_
   for (int i = 0; i < L.code_brick_bytes; ++i) codes[i >> 2] |= (uint32_t)c[i] << (8 * (i & 3));
 }
 
-// Canonical export: codes int8 [n_out][K], keep uint8 [n_out][K].
-__global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t* mask_plane,
-                                                        const uint8_t* code_plane,
-                                                        int8_t* __restrict__ codes_out,
-                                                        uint8_t* __restrict__ keep_out) {
-  const int64_t nbricks = (L.K + kBrickK - 1) / kBrickK;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= L.n_out * nbricks) return;
-  const int64_t row = idx / nbricks, brick = idx % nbricks;
+// The 64 int8 codes of brick `brick` of row `row` (position i at byte i % 4 of dec[i / 4]) and
+// its keep mask, for every code form.
+__device__ void decode_brick(const Layout& L, const uint8_t* mask_plane, const uint8_t* code_plane,
+                             int64_t row, int64_t brick, uint32_t mask[2], uint32_t dec[16]) {
   const int64_t slot = brick_slot(L, row, brick);
-  uint32_t mask[2], codes[4], dec[16];
+  uint32_t codes[4];
   load_brick(L, mask_plane, code_plane, slot, mask, codes);
   if (L.form == kFormSparse24) {
     // this brick's 64 positions are lane groups g0 and g0 + 1 of block b of its quad
@@ -302,6 +297,19 @@ __global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t*
     for (int i = 0; i < 16; ++i) dec[i] = 0;
     decode_kept_brick(mask, codes, L.n, L.m, L.has_mask, dec);
   }
+}
+
+// Canonical export: codes int8 [n_out][K], keep uint8 [n_out][K].
+__global__ __launch_bounds__(256) void export_canonical(Layout L, const uint8_t* mask_plane,
+                                                        const uint8_t* code_plane,
+                                                        int8_t* __restrict__ codes_out,
+                                                        uint8_t* __restrict__ keep_out) {
+  const int64_t nbricks = (L.K + kBrickK - 1) / kBrickK;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= L.n_out * nbricks) return;
+  const int64_t row = idx / nbricks, brick = idx % nbricks;
+  uint32_t mask[2], dec[16];
+  decode_brick(L, mask_plane, code_plane, row, brick, mask, dec);
   const int64_t k0 = brick * kBrickK;
   const int cnt = (int)min<int64_t>(kBrickK, L.K - k0);
   for (int i = 0; i < cnt; ++i) {
@@ -376,6 +384,54 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
 }
 
 __global__ void copy_gamma(const float* src, float* dst) { dst[0] = src[0]; }
+// Transposed code plane, read by the data-gradient matmul, whose reduction runs over the rows:
+// for every 16 columns cb and 128 rows rq, 64 lanes x 8 bytes at slot (cb * rq_count + rq) * 64
+// + lane. Lane l = c + 16 g holds column 16 cb + c of rows 128 rq + 32 g + (0..31); its word h
+// (0, 1) holds row 32 g + 16 h + 8 s + 2 p + e (s, e in {0, 1}, p in 0..3) at bits
+// 2 p + 8 s + 16 e, as 2-bit codes 0 = 0, 1 = +1, 2 = -1. One workgroup per 128 rows x 256
+// columns: its 512 bricks are decoded into LDS as 2-bit codes (row-major, 16 positions per
+// word), then every thread assembles 8 words of 8 columns. Rows past n_out are zero.
+__global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* mask_plane,
+                                                       const uint8_t* code_plane,
+                                                       int64_t rq_count,
+                                                       uint32_t* __restrict__ tplane) {
+  __shared__ uint32_t cw[128][17];  // row x 16 code words (+1 against bank conflicts)
+  const int64_t rq = blockIdx.x / L.quads, q = blockIdx.x % L.quads;
+  const int tid = threadIdx.x;
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, rl = idx >> 2, b = idx & 3;
+    const int64_t row = rq * 128 + rl;
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+    if (row < L.n_out) {
+      uint32_t mask[2], dec[16];
+      decode_brick(L, mask_plane, code_plane, row, q * kFragBricks + b, mask, dec);
+      for (int j = 0; j < kBrickK; ++j) {
+        const uint32_t v = (dec[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        w4[j >> 4] |= (v == 0xFFu ? 2u : v) << (2 * (j & 15));
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) cw[rl][4 * b + w] = w4[w];
+  }
+  __syncthreads();
+  const int task = tid >> 1, half = tid & 1;
+  const int cbl = task >> 3, g = (task >> 1) & 3, h = task & 1;
+  uint32_t rw[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) rw[rr] = cw[32 * g + 16 * h + rr][cbl];
+  const int64_t cb = q * 16 + cbl;
+  uint32_t* const dst = tplane + (cb * rq_count + rq) * 128;
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) {
+    const int c = 8 * half + cc;
+    uint32_t out = 0;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)  // rr = 8 s + 2 p + e
+      out |= ((rw[rr] >> (2 * c)) & 3u) << (2 * ((rr >> 1) & 3) + 8 * (rr >> 3) + 16 * (rr & 1));
+    dst[(c + 16 * g) * 2 + h] = out;
+  }
+}
+
 // Sum of the per-wave flip counts of the last pack (one workgroup; num may be 0).
 __global__ __launch_bounds__(1024) void sum_flips(const uint32_t* __restrict__ parts, int64_t num,
                                                   unsigned long long* __restrict__ out) {
@@ -456,6 +512,14 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 }  // namespace sbn
 
 namespace sbn {
+hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s) {
+  const Layout& L = h->L;
+  if (h->rq_count == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_codes, dim3((unsigned)(h->rq_count * L.quads)), dim3(256), 0, s, L,
+                     h->mask, h->codes, h->rq_count, h->tplane);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s) {
   const Layout& L = h->L;
   const int64_t num = (L.has_mask && L.n_out > 0) ? L.row_blocks_pad * L.quads * 4 : 0;

@@ -186,4 +186,42 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// GEMM tile order. Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// The linear block id is remapped so that every XCD receives one contiguous run of tiles in a
+// grouped order (kTileGroup token tiles x all N tiles, N-major within the group): the tiles an
+// XCD has in flight then share activation rows and packed weights in its L2.
+constexpr int kXcds = 8;
+constexpr int kTileGroup = 4;
+
+// Position of block `bid` in the XCD-contiguous order.
+__device__ __forceinline__ int xcd_order(int nblocks, int bid) {
+  const int xcd = bid % kXcds, j = bid / kXcds;
+  const int base = nblocks / kXcds, extra = nblocks % kXcds;
+  return xcd * base + min(xcd, extra) + j;
+}
+
+// Tile of position `lin` in the grouped order.
+__device__ __forceinline__ void grouped_tile(int lin, int tiles_n, int tiles_t, int& tile_n,
+                                             int& tile_t) {
+  const int per_group = kTileGroup * tiles_n;
+  const int group = lin / per_group, r = lin % per_group;
+  const int gsize = min(kTileGroup, tiles_t - group * kTileGroup);
+  tile_n = r / gsize;
+  tile_t = group * kTileGroup + r % gsize;
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no stride): offsets are
+// bytes and reads at or past num_records return zero.
+constexpr int kBufDword3 = 0x00020000;
+
+// s_waitcnt immediate that waits until at most `n` vector-memory operations are outstanding and
+// does not wait on LDS/scalar or export counters (gfx9 encoding: vmcnt split over bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
 }  // namespace sbn

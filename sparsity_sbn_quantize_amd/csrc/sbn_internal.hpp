@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "sbn.h"
 #include "sbn_common.hpp"
 
@@ -20,6 +24,9 @@ struct sbn_packed {
   double* partials;    // device workspace [num_partials]
   int* gemm_sync;      // split-K flags: kGemmSyncInts words, zero between calls
   uint32_t* flip_parts;  // keep bits changed by the last pack, one count per pack wave
+  uint32_t* tplane;     // transposed code plane (data-gradient matmul), 2 bits per weight
+  int64_t rq_count;     // 128-row groups of the transposed plane
+  bool tplane_valid;    // the transposed plane matches the last pack (host-side state)
   int device;
   hipStream_t last_stream;
 };
@@ -44,8 +51,29 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
 hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
+hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s);
+hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,
+                         float* dx, int64_t ld_dx, hipStream_t s);
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
                                  int out_kind, hipStream_t s);
+
+// Raises a kernel's dynamic-LDS limit once per process and kernel (gfx950 has 160 KB of LDS per
+// CU).
+inline hipError_t allow_smem_ptr(const void* kernel, size_t bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, size_t>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == kernel && d.second >= bytes) return hipSuccess;
+  hipError_t e =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, bytes);
+  return e;
+}
+template <typename K>
+hipError_t allow_smem(K kernel, size_t bytes) {
+  return allow_smem_ptr(reinterpret_cast<const void*>(kernel), bytes);
+}
 
 }  // namespace sbn

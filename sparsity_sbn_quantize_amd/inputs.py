@@ -22,6 +22,7 @@ import numpy as np
 # Tensor-kind tags in the spawn key.
 _ACT = 0
 _WEIGHT = 1
+_GRAD = 2
 
 
 @dataclass(frozen=True)
@@ -146,6 +147,14 @@ def latent_weights(wl: Workload, layer_index: int, n_out: int | None = None,
     else:
         raise ValueError(wl.weight_dist)
     return np.ascontiguousarray(w, dtype=np.float32)
+
+
+def grad_output(wl: Workload, layer_index: int, tokens: int) -> np.ndarray:
+    """bf16 bit patterns [tokens][n_out]: a standard-normal stand-in for the gradient of layer
+    ``layer_index``'s output (the pages give no gradient distribution)."""
+    layer = wl.layers[layer_index]
+    rng = _rng(wl.index, _GRAD, layer_index, tokens)
+    return f32_to_bf16_bits(rng.standard_normal((tokens, layer.n_out), dtype=np.float32))
 
 
 def layer_inputs(wl: Workload, layer_index: int, tokens: int):

@@ -19,8 +19,9 @@ def lib():
 def test_exports_match_header(lib):
     declared = b.header_symbols()
     assert set(declared) == {"sbn_quantize_act", "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
-                             "sbn_bitlinear_fwd_bf16", "sbn_free", "sbn_packed_export", "sbn_packed_export_rpf",
-                             "sbn_packed_query", "sbn_packed_mask_flips", "sbn_last_error"}
+                             "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_bwd_dx", "sbn_free",
+                             "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_query",
+                             "sbn_packed_mask_flips", "sbn_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -79,6 +80,7 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_export_rpf(None, None, None, None) == ERR_INVALID
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_bwd_dx(None, None, 0, 1, None, 0, None) == ERR_INVALID
     lib.sbn_free(None)  # no-op
 
 

@@ -503,3 +503,93 @@ def test_mask_flips_nm_structure(n, m):
     assert oracle.mask_flips(k1, oracle.nm_keep_mask(w1 * np.float32(3), n, m)) == 0
     if n == m:
         assert oracle.mask_flips(k1, k2) == 0
+
+
+# ---------------------------------------------------------------------------------------------
+# Straight-through data gradient (BitNet blog, "Training with the Straight-Through Estimator").
+# ---------------------------------------------------------------------------------------------
+
+def brute_ste_dx(dy_bits, codes, gamma):
+    """Pure-Python dX = fl32(gamma * fsum_r dy[t][r] * code[r][k])."""
+    dy = inputs.bf16_bits_to_f32(np.asarray(dy_bits)).astype(np.float64).tolist()
+    cl = np.asarray(codes).astype(int).tolist()
+    T, N, K = len(dy), len(cl), len(cl[0]) if cl else 0
+    out = []
+    for t in range(T):
+        row = []
+        for k in range(K):
+            s = math.fsum(dy[t][r] * cl[r][k] for r in range(N))
+            row.append(struct.unpack("f", struct.pack("f", float(gamma) * s))[0])
+        out.append(row)
+    return np.array(out, dtype=np.float32).reshape(T, K)
+
+
+def _ste_case(seed, T, N, K, n, m):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    p = oracle.pack_nm_ternary(w, n, m)
+    dy = inputs.f32_to_bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
+    return dy, p["codes"], p["gamma"], w
+
+
+def _ste_pins_fail(fn) -> bool:
+    """True when an implementation of dX disagrees with the brute force, the autograd adjoint or
+    the one-hot rows (used on the oracle and on planted mistakes)."""
+    import torch
+    cases = [(3, 8, 12, 2, 4), (2, 16, 8, 6, 8), (4, 5, 16, 8, 16), (3, 16, 16, 8, 16)]
+    for seed, (T, N, K, n, m) in enumerate(cases):
+        dy, codes, gamma, _ = _ste_case(seed, T, N, K, n, m)
+        got = fn(dy, codes, gamma)
+        if got.shape != (T, K) or not np.array_equal(got, brute_ste_dx(dy, codes, gamma)):
+            return True
+        # autograd of the forward definition y = x (gamma C)^T, in fp64
+        x = torch.zeros((T, K), dtype=torch.float64, requires_grad=True)
+        wt = torch.from_numpy(np.float64(gamma) * codes.astype(np.float64))
+        y = x @ wt.T
+        y.backward(torch.from_numpy(inputs.bf16_bits_to_f32(dy).astype(np.float64)))
+        if not np.allclose(got, x.grad.numpy(), rtol=2 ** -22, atol=0):
+            return True
+        # one-hot rows of dY select gamma times one code row
+        onehot = np.zeros((N, N), np.float32)
+        np.fill_diagonal(onehot, 1.0)
+        sel = fn(inputs.f32_to_bf16_bits(onehot), codes, gamma)
+        if not np.array_equal(sel, (np.float32(gamma) * codes.astype(np.float32))):
+            return True
+    return False
+
+
+def test_ste_dx_pins():
+    assert not _ste_pins_fail(oracle.ste_dx)
+
+
+@pytest.mark.parametrize("mutant", ["no_gamma", "transposed", "negated", "dy_truncated",
+                                    "codes_as_keep"])
+def test_ste_dx_mutants_caught(mutant):
+    """Plausible mistakes in the data gradient fail the pins."""
+    def f(dy, codes, gamma):
+        if mutant == "no_gamma":
+            return oracle.ste_dx(dy, codes, np.float32(1.0))
+        if mutant == "transposed":  # the codes' transpose (shape-compatible only when square)
+            d = inputs.bf16_bits_to_f32(dy).astype(np.float64)
+            c = codes.astype(np.float64)
+            if c.shape[0] != c.shape[1]:
+                return np.zeros((d.shape[0], c.shape[1]), np.float32)
+            return (np.float64(gamma) * (d @ c.T)).astype(np.float32)
+        if mutant == "negated":
+            return -oracle.ste_dx(dy, codes, gamma)
+        if mutant == "dy_truncated":  # dy taken as its integer part
+            d = np.trunc(inputs.bf16_bits_to_f32(dy)).astype(np.float32)
+            return oracle.ste_dx(inputs.f32_to_bf16_bits(d), codes, gamma)
+        return oracle.ste_dx(dy, (codes != 0).astype(np.int8), gamma)
+    assert _ste_pins_fail(f)
+
+
+def test_ste_dx_abs_bounds_value():
+    """|dX| <= gamma |dY| |C| elementwise, with equality where all terms share a sign."""
+    dy, codes, gamma, _ = _ste_case(9, 5, 24, 32, 6, 8)
+    dx = oracle.ste_dx(dy, codes, gamma).astype(np.float64)
+    ab = oracle.ste_dx_abs(dy, codes, gamma)
+    assert np.all(np.abs(dx) <= ab * (1 + 2 ** -23) + 1e-30)
+    pos = np.abs(inputs.f32_to_bf16_bits(np.ones((2, 24), np.float32)))
+    same = oracle.ste_dx(pos, np.abs(codes).astype(np.int8), gamma).astype(np.float64)
+    assert np.allclose(same, oracle.ste_dx_abs(pos, codes, gamma), rtol=2 ** -23)
