@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+LN_EPS = 1e-5             # LayerNorm epsilon of the timed LayerNorm variants
 METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GEMV)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
@@ -186,6 +187,14 @@ def run_decode(gpu, args, T=1, with_cpu=True):
         gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
         gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y)
 
+    # BitLinear operation 1 in front: the parameter-free LayerNorm, fused (one kernel for
+    # T <= 4) and as its own kernel
+    def ln_step(i):
+        gpu.b.bitlinear_bf16(xd, pws[i % R], out="f32", y=y, x_q=q, x_absmax=a, ln_eps=LN_EPS)
+
+    def ln_quant_only(i):
+        gpu.b.layernorm_quantize_act(xd, LN_EPS, out_q=q, out_absmax=a)
+
     # the step equals the two-call path bit for bit
     two_call(0)
     torch.cuda.synchronize()
@@ -205,7 +214,9 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
     timings = {}
     for name, fn in (("bitlinear_gemv", gemv_only), ("quantize_act", quant_only),
-                     ("quantize_act+bitlinear_gemv", two_call)):
+                     ("quantize_act+bitlinear_gemv", two_call),
+                     ("layernorm_quantize_act", ln_quant_only),
+                     ("bitlinear_gemv (layernorm + quantize fused)", ln_step)):
         g = gpu.graph(fn, args.steps)
         g.replay()
         timings[name] = gpu.time_graph(g) / args.steps
@@ -292,10 +303,21 @@ def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True):
     gk = gpu.graph(gemm_only, steps)
     gk.replay()
     gemm_ms = gpu.time_graph(gk) / steps
+    act_ms = {}
+    for name, fn in (("quantize_act", lambda i: gpu.b.quantize_act(xd, out_q=q, out_absmax=a)),
+                     ("layernorm_quantize_act",
+                      lambda i: gpu.b.layernorm_quantize_act(xd, LN_EPS, out_q=q, out_absmax=a))):
+        g = gpu.graph(fn, steps)
+        g.replay()
+        act_ms[name] = gpu.time_graph(g) / steps
+    act_bytes = 3.0 * T * K + 4.0 * T  # bf16 in, int8 + a' out
     ops = 2.0 * T * K * N
     achieved = ops / (gemm_ms * 1e-3) / 1e12
     res = {
         "value": ops / (ms * 1e-3) / 1e12, "unit": "TOPS", "ms_per_step": ms,
+        "activation_kernels": {k: {"us": v * 1e3, "GBps": act_bytes / (v * 1e-3) / 1e9,
+                                   "frac_hbm": act_bytes / (v * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                               for k, v in act_ms.items()},
         "config": {"workload": f"{wl.name}_{layer.name}", "pattern": f"{n}:{m}", "tokens": T,
                    "K": K, "n_out": N, "ops": "dense-equivalent 2*T*K*N"},
         "roofline": {"bound": "mfma", "kernel": "bitlinear_gemm", "achieved": achieved,
@@ -581,6 +603,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": res["config"], "roofline": res["roofline"],
             "kernels_us": res.get("kernels_us")}
+    if "activation_kernels" in res:
+        line["activation_kernels"] = res["activation_kernels"]
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
     if not args.no_secondary and args.workload == "decode":
@@ -589,7 +613,8 @@ def main():
         sec.append({k: r16[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
         for li in (0, 1):
             rp = run_prefill(gpu, args, li, steps=50, with_cpu=False)
-            sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
+            sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
+                                           "activation_kernels")})
         for li, pat in ((0, (2, 4)), (1, (8, 16))):
             sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
         line["secondary"] = sec

@@ -2,7 +2,8 @@
  * sbn.h - C ABI of the Sparse-BitNet BitLinear forward for AMD MI355X (gfx950).
  *
  * The forward of one BitLinear layer is split into three calls:
- *   sbn_quantize_act     per-token absmax INT8 activation quantization
+ *   sbn_quantize_act     per-token absmax INT8 activation quantization (sbn_layernorm_quantize_act
+ *                        runs the layer's parameter-free LayerNorm first)
  *   sbn_pack_nm_ternary  per-tensor absmean ternary quantization of fp32 latent weights with a
  *                        dynamic n:m magnitude keep mask, packed as 2-bit codes + per-group mask
  *   sbn_bitlinear_fwd    n:m-sparse ternary x INT8 matmul, int32 accumulation, fused dequant
@@ -74,6 +75,22 @@ sbn_status sbn_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K, int64_
                             int8_t* x_q, int64_t ld_q, float* x_absmax, void* stream);
 
 /*
+ * Parameter-free LayerNorm followed by sbn_quantize_act ("The BitLinear Layer", operations 1 and
+ * 2: activations are normalized without learned scale or shift, then quantized from BF16 to INT8).
+ * The page gives no formula or epsilon; this is the standard LayerNorm without affine terms:
+ *   mu = fl64(sum_k x[t,k] / K), var = fl64(sum_k (x - mu)^2 / K)  (biased; fp64 statistics)
+ *   r  = fl64(1 / sqrt(var + eps))
+ *   z[t,k] = bf16( fl32( fl32(x - fl32(mu)) * fl32(r) ) )           (round to nearest even)
+ * and x_q, x_absmax are exactly what sbn_quantize_act writes for the bf16 rows z.
+ *   x_bf16    [T][ld_x] bf16 bit patterns (uint16), read only.
+ *   eps       > 0 and finite (1e-5 is the usual choice).
+ * Requires T >= 0, 1 <= K <= SBN_MAX_K, ld_x >= K, ld_q >= K; T == 0 is a no-op.
+ */
+sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K,
+                                      int64_t ld_x, float eps, int8_t* x_q, int64_t ld_q,
+                                      float* x_absmax, void* stream);
+
+/*
  * Absmean ternary quantization with a dynamic n:m keep mask, packed ("The BitLinear Layer",
  * operation 3, with the divide reading of "How ternary quantization works during training";
  * Sparse-BitNet Abstract and Figure 6).
@@ -120,6 +137,19 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
 sbn_status sbn_bitlinear_fwd_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
                                   int64_t T, int8_t* x_q, int64_t ld_q, float* x_absmax, void* y,
                                   int64_t ld_y, sbn_out_kind out_kind, void* stream);
+
+/*
+ * The whole BitLinear forward on bf16 input: sbn_layernorm_quantize_act then sbn_bitlinear_fwd
+ * ("The BitLinear Layer", operations 1, 2, 4 and 5). x_q and x_absmax receive exactly what
+ * sbn_layernorm_quantize_act writes; y is as for sbn_bitlinear_fwd. For T <= 4 and K <= 12288
+ * the whole call is one kernel launch in which every workgroup normalizes and quantizes the rows
+ * it needs itself; otherwise it runs the two kernels in turn. Requirements as for
+ * sbn_bitlinear_fwd_bf16, with eps > 0 and finite.
+ */
+sbn_status sbn_bitlinear_fwd_ln_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
+                                     int64_t T, float eps, int8_t* x_q, int64_t ld_q,
+                                     float* x_absmax, void* y, int64_t ld_y,
+                                     sbn_out_kind out_kind, void* stream);
 
 /*
  * Data gradient of the layer under the straight-through estimator ("Microsoft BitNet 1.58: The

@@ -29,6 +29,9 @@ Readings taken where the pages are silent or disagree (each is also listed in th
   * the weight scale is one per tensor and is taken over the dense latent weights, before
     selection (Figure 6 places the thresholds on normalized magnitudes);
   * the activation scale is per token: absmax with a floor of 1e-5, symmetric 127 levels;
+  * the parameter-free LayerNorm (operation 1) is the standard one without affine terms: fp64
+    mean and biased variance, r = 1/sqrt(var + eps), z = bf16(fl32(fl32(x - mu) * r)) with mu and
+    r rounded to fp32; the quantizer then takes z (the page says BF16 is quantized to INT8);
   * the int8 code sequence is s = fl32(127 / a'), v = fl32(x * s), q = clamp(rne(v), -127, 127);
   * the N:M groups are M consecutive weights along the reduction axis K of each output row;
     selection keys on |w|; ties go to the lower index; kept weights that ternarize to 0 still
@@ -83,6 +86,34 @@ def act_scale(a_prime: np.ndarray) -> np.ndarray:
     the correctly rounded fp32 result because 53 >= 2*24 + 2.
     """
     return (np.float64(QMAX) / np.asarray(a_prime, dtype=np.float64)).astype(np.float32)
+
+
+def f32_to_bf16_rne(z: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, rounded to nearest even (finite inputs)."""
+    u = np.asarray(z, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def layernorm_bf16(x_bf16: np.ndarray, eps: float) -> np.ndarray:
+    """Parameter-free LayerNorm ([BitNet-blog] "The BitLinear Layer", operation 1), output bf16.
+
+    Statistics in fp64 (biased variance), normalization in fp32, one rounding to bf16:
+    z = bf16(fl32(fl32(x - fl32(mu)) * fl32(1 / sqrt(var + eps)))).
+    """
+    x = bf16_to_f32(x_bf16).astype(np.float64)
+    k = x.shape[1]
+    mu = x.sum(axis=1) / np.float64(k)
+    d = x - mu[:, None]
+    var = (d * d).sum(axis=1) / np.float64(k)
+    r = 1.0 / np.sqrt(var + np.float64(np.float32(eps)))
+    x32 = x.astype(np.float32)
+    z = (x32 - mu.astype(np.float32)[:, None]).astype(np.float32) * r.astype(np.float32)[:, None]
+    return f32_to_bf16_rne(z.astype(np.float32))
+
+
+def layernorm_quantize_act(x_bf16: np.ndarray, eps: float):
+    """LayerNorm, then the absmax INT8 quantization of its bf16 output: (q, a')."""
+    return quantize_act(layernorm_bf16(x_bf16, eps))
 
 
 def quantize_act(x_bf16: np.ndarray):

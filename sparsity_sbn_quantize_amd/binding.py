@@ -40,6 +40,8 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SIGNATURES = {
     "sbn_quantize_act": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
+    "sbn_layernorm_quantize_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_float, _P,
+                                                  _I64, _P, _P]),
     "sbn_pack_nm_ternary": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_void_p), _P]),
     "sbn_bitlinear_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _P]),
@@ -51,6 +53,8 @@ _SIGNATURES = {
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
     "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
     "sbn_bitlinear_bwd_dx": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
+    "sbn_bitlinear_fwd_ln_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _I64,
+                                                 _P, _P, _I64, ctypes.c_int, _P]),
     "sbn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -123,6 +127,20 @@ def quantize_act(x, out_q=None, out_absmax=None, stream=None):
                                  _stream(stream)))
     return q, a
 
+
+def layernorm_quantize_act(x, eps: float = 1e-5, out_q=None, out_absmax=None, stream=None):
+    """Parameter-free LayerNorm, then per-token absmax INT8: x bf16 [T][K] -> (q, a')."""
+    import torch
+    _require_cuda(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("x must be bfloat16 (or int16 bf16 bit patterns)")
+    T, K = x.shape
+    q = out_q if out_q is not None else torch.empty((T, K), dtype=torch.int8, device=x.device)
+    a = out_absmax if out_absmax is not None else torch.empty((T,), dtype=torch.float32,
+                                                              device=x.device)
+    check(lib().sbn_layernorm_quantize_act(_ptr(x), T, K, _ld(x, K), float(eps), _ptr(q),
+                                           _ld(q, K), _ptr(a), _stream(stream)))
+    return q, a
 
 class PackedWeight:
     """A packed n:m ternary weight (library-owned device memory)."""
@@ -213,8 +231,9 @@ def bitlinear(x_q, x_absmax, w: PackedWeight, out: str = "f32", y=None, stream=N
 
 
 def bitlinear_bf16(x, w: PackedWeight, out: str = "f32", y=None, x_q=None, x_absmax=None,
-                   stream=None):
-    """Quantize-and-multiply: x bf16 [T][K] -> (y, x_q int8 [T][K], a' fp32 [T])."""
+                   stream=None, ln_eps=None):
+    """Quantize-and-multiply: x bf16 [T][K] -> (y, x_q int8 [T][K], a' fp32 [T]). With ln_eps,
+    the parameter-free LayerNorm runs first (sbn_bitlinear_fwd_ln_bf16)."""
     import torch
     _require_cuda(x, "x")
     if x.dtype not in (torch.bfloat16, torch.int16):
@@ -228,9 +247,14 @@ def bitlinear_bf16(x, w: PackedWeight, out: str = "f32", y=None, x_q=None, x_abs
         x_q = torch.empty((T, w.K), dtype=torch.int8, device=x.device)
     if x_absmax is None:
         x_absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
-    check(lib().sbn_bitlinear_fwd_bf16(w.handle, _ptr(x), _ld(x, w.K), T, _ptr(x_q),
-                                       _ld(x_q, w.K), _ptr(x_absmax), _ptr(y), _ld(y, w.n_out),
-                                       kind, _stream(stream)))
+    if ln_eps is None:
+        check(lib().sbn_bitlinear_fwd_bf16(w.handle, _ptr(x), _ld(x, w.K), T, _ptr(x_q),
+                                           _ld(x_q, w.K), _ptr(x_absmax), _ptr(y),
+                                           _ld(y, w.n_out), kind, _stream(stream)))
+    else:
+        check(lib().sbn_bitlinear_fwd_ln_bf16(w.handle, _ptr(x), _ld(x, w.K), T, float(ln_eps),
+                                              _ptr(x_q), _ld(x_q, w.K), _ptr(x_absmax), _ptr(y),
+                                              _ld(y, w.n_out), kind, _stream(stream)))
     return y, x_q, x_absmax
 
 

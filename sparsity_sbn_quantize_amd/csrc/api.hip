@@ -33,6 +33,34 @@ bool pattern_ok(int n, int m) { return (m == 4 || m == 8 || m == 16) && n >= 1 &
 // The matmul kernels form 32-bit offsets of up to 16 activation rows.
 constexpr int64_t kMaxLdQ = (int64_t)1 << 26;
 
+// Shared body of the bf16-input forwards (ln_eps > 0: LayerNorm before the quantization).
+sbn_status fwd_bf16(const char* name, const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
+                    int64_t T, float ln_eps, int8_t* x_q, int64_t ld_q, float* x_absmax, void* y,
+                    int64_t ld_y, sbn_out_kind out_kind, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "%s: handle is null", name);
+  if (out_kind != SBN_OUT_F32 && out_kind != SBN_OUT_I32_ACC)
+    return fail(SBN_ERR_INVALID_ARG, "%s: out_kind=%d", name, (int)out_kind);
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "%s: T=%lld < 0", name, (long long)T);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "%s: T too large", name);
+  if (ld_x < w->L.K || ld_q < w->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "%s: ld_x=%lld / ld_q=%lld < K=%lld", name,
+                (long long)ld_x, (long long)ld_q, (long long)w->L.K);
+  if (ld_q > kMaxLdQ)
+    return fail(SBN_ERR_UNSUPPORTED, "%s: ld_q=%lld > %lld", name, (long long)ld_q,
+                (long long)kMaxLdQ);
+  if (ld_y < w->L.n_out)
+    return fail(SBN_ERR_INVALID_ARG, "%s: ld_y=%lld < n_out=%lld", name, (long long)ld_y,
+                (long long)w->L.n_out);
+  if (T == 0) return SBN_OK;
+  if (!x_bf16 || !x_q || !x_absmax || (!y && w->L.n_out > 0))
+    return fail(SBN_ERR_INVALID_ARG, "%s: null pointer", name);
+  const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
+  hipError_t e = sbn::launch_bitlinear_bf16(w, x_bf16, ld_x, T, x_q, ld_q, x_absmax, y, ld_y,
+                                            (int)out_kind, ln_eps, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return SBN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,6 +83,30 @@ sbn_status sbn_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K, int64_
   hipError_t e = sbn::launch_quantize_act(x_bf16, T, K, ld_x, x_q, ld_q, x_absmax,
                                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_quantize_act launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K,
+                                      int64_t ld_x, float eps, int8_t* x_q, int64_t ld_q,
+                                      float* x_absmax, void* stream) {
+  if (T < 0)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_layernorm_quantize_act: T=%lld < 0", (long long)T);
+  if (K < 1 || K > SBN_MAX_K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_layernorm_quantize_act: K=%lld outside [1, %d]",
+                (long long)K, SBN_MAX_K);
+  if (ld_x < K || ld_q < K)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_layernorm_quantize_act: ld_x=%lld / ld_q=%lld < K",
+                (long long)ld_x, (long long)ld_q);
+  if (!(eps > 0.0f) || eps > 3.0e38f)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_layernorm_quantize_act: eps=%g must be > 0 and finite",
+                (double)eps);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_layernorm_quantize_act: T too large");
+  if (T == 0) return SBN_OK;
+  if (!x_bf16 || !x_q || !x_absmax)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_layernorm_quantize_act: null pointer");
+  hipError_t e = sbn::launch_ln_quantize_act(x_bf16, T, K, ld_x, eps, x_q, ld_q, x_absmax,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_layernorm_quantize_act launch");
   return SBN_OK;
 }
 
@@ -202,28 +254,19 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
 sbn_status sbn_bitlinear_fwd_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
                                   int64_t T, int8_t* x_q, int64_t ld_q, float* x_absmax, void* y,
                                   int64_t ld_y, sbn_out_kind out_kind, void* stream) {
-  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: handle is null");
-  if (out_kind != SBN_OUT_F32 && out_kind != SBN_OUT_I32_ACC)
-    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: out_kind=%d", (int)out_kind);
-  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: T=%lld < 0", (long long)T);
-  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd_bf16: T too large");
-  if (ld_x < w->L.K || ld_q < w->L.K)
-    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: ld_x=%lld / ld_q=%lld < K=%lld",
-                (long long)ld_x, (long long)ld_q, (long long)w->L.K);
-  if (ld_q > kMaxLdQ)
-    return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_fwd_bf16: ld_q=%lld > %lld", (long long)ld_q,
-                (long long)kMaxLdQ);
-  if (ld_y < w->L.n_out)
-    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: ld_y=%lld < n_out=%lld",
-                (long long)ld_y, (long long)w->L.n_out);
-  if (T == 0) return SBN_OK;
-  if (!x_bf16 || !x_q || !x_absmax || (!y && w->L.n_out > 0))
-    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_bf16: null pointer");
-  const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
-  hipError_t e = sbn::launch_bitlinear_bf16(w, x_bf16, ld_x, T, x_q, ld_q, x_absmax, y, ld_y,
-                                            (int)out_kind, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd_bf16 launch");
-  return SBN_OK;
+  return fwd_bf16("sbn_bitlinear_fwd_bf16", w, x_bf16, ld_x, T, 0.0f, x_q, ld_q, x_absmax, y,
+                  ld_y, out_kind, stream);
+}
+
+sbn_status sbn_bitlinear_fwd_ln_bf16(const sbn_packed* w, const uint16_t* x_bf16, int64_t ld_x,
+                                     int64_t T, float eps, int8_t* x_q, int64_t ld_q,
+                                     float* x_absmax, void* y, int64_t ld_y,
+                                     sbn_out_kind out_kind, void* stream) {
+  if (!(eps > 0.0f) || eps > 3.0e38f)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd_ln_bf16: eps=%g must be > 0 and finite",
+                (double)eps);
+  return fwd_bf16("sbn_bitlinear_fwd_ln_bf16", w, x_bf16, ld_x, T, eps, x_q, ld_q, x_absmax, y,
+                  ld_y, out_kind, stream);
 }
 
 void sbn_free(sbn_packed* handle) {

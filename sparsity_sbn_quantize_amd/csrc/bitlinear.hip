@@ -143,9 +143,11 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const void* __restrict__ xin, int64_t ld_x,
     int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
-    void* __restrict__ y, int64_t ld_y, int out_kind) {
+    void* __restrict__ y, int64_t ld_y, int out_kind, float ln_eps) {
   __shared__ v4i red[kGemvMaxWaves][64];
   __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT];
+  __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
+  __shared__ double lndev[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
   __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
   const int W = (int)(blockDim.x >> 6);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -187,9 +189,6 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
     uint2 xv[Q][kFusedMaxT];
-    uint32_t m[kFusedMaxT];
-#pragma unroll
-    for (int tt = 0; tt < kFusedMaxT; ++tt) m[tt] = 0;
 #pragma unroll
     for (int i = 0; i < Q; ++i)
 #pragma unroll
@@ -207,12 +206,99 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
           }
         }
         xv[i][tt] = v;
-        m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], v.x), v.y);
       }
     // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
     // does not wait for the bricks: the quantization below overlaps the brick loads.
     load_bricks();
     const int Tn = (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+    if (ln_eps > 0.0f) {
+      // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
+      // and sum of squared deviations over the wave (DPP) and then the waves (LDS, fixed order);
+      // the lane's elements are replaced by their bf16 normalized values.
+      double ps[kFusedMaxT], pd[kFusedMaxT];
+      float mu32[kFusedMaxT], r32[kFusedMaxT];
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        ps[tt] = 0.0;
+        if (tt >= Tn) continue;
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+          const uint2 v = xv[i][tt];
+          ps[tt] += (double)__uint_as_float(v.x << 16) + (double)__uint_as_float(v.x & 0xFFFF0000u) +
+                    (double)__uint_as_float(v.y << 16) + (double)__uint_as_float(v.y & 0xFFFF0000u);
+        }
+        ps[tt] = wave_sum_f64(ps[tt]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) lnsum[wave][tt] = ps[tt];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        pd[tt] = 0.0;
+        ps[tt] = 0.0;
+        if (tt >= Tn) continue;
+        for (int w = 0; w < W; ++w) ps[tt] += lnsum[w][tt];
+        ps[tt] /= (double)K;  // the mean
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+          const int k = (wave + i * W) * kQuadK + 4 * lane;
+          const uint2 v = xv[i][tt];
+          const float f[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                              __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (k + u < K) {
+              const double e = (double)f[u] - ps[tt];
+              pd[tt] += e * e;
+            }
+          }
+        }
+        pd[tt] = wave_sum_f64(pd[tt]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) lndev[wave][tt] = pd[tt];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        mu32[tt] = 0.0f;
+        r32[tt] = 0.0f;
+        if (tt >= Tn) continue;
+        double d = 0.0;
+        for (int w = 0; w < W; ++w) d += lndev[w][tt];
+        mu32[tt] = (float)ps[tt];
+        r32[tt] = (float)(1.0 / sqrt(d / (double)K + (double)ln_eps));
+      }
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const int k = (wave + i * W) * kQuadK + 4 * lane;
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          if (tt >= Tn || k >= K) continue;
+          uint2 z = make_uint2(ln_pair(xv[i][tt].x, mu32[tt], r32[tt]),
+                               ln_pair(xv[i][tt].y, mu32[tt], r32[tt]));
+          // positions past K stay zero
+          if (k + 4 > K) {
+            const int keep = K - k;  // 1 .. 3 valid values
+            if (keep < 2) z.x &= 0xFFFFu;
+            if (keep < 3) z.y = 0u;
+            else z.y &= 0xFFFFu;
+          }
+          xv[i][tt] = z;
+        }
+      }
+    }
+    uint32_t m[kFusedMaxT];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt) {
+      m[tt] = 0;
+#pragma unroll
+      for (int i = 0; i < Q; ++i) m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], xv[i][tt].x),
+                                                         xv[i][tt].y);
+    }
     // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
     // over the waves through LDS.
     uint32_t pk[kFusedMaxT / 2];
@@ -690,14 +776,14 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 template <int FORM, bool FUSED, bool XVEC>
 hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
                        int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
-                       int out_kind, hipStream_t s) {
+                       int out_kind, float ln_eps, hipStream_t s) {
   const Layout& L = h->L;
   const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
   const int Q = (int)((L.quads + W - 1) / W);
 #define SBN_GEMV(QQ)                                                                          \
   hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ>), dim3((unsigned)L.row_blocks),   \
                      dim3(64 * W), 0, s, h->mask, h->codes, L, h->gamma, x, ld_x, xq_out, ld_q, \
-                     absmax, T, y, ld_y, out_kind)
+                     absmax, T, y, ld_y, out_kind, ln_eps)
   if (Q == 1) {
     SBN_GEMV(1);
   } else if (Q == 2) {
@@ -716,7 +802,7 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   const Layout& L = h->L;
   if (T <= 16 && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     return launch_gemv<FORM, false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax), T,
-                                         y, ld_y, out_kind, s);
+                                         y, ld_y, out_kind, 0.0f, s);
   }
   hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC>, kGemmSmem);
   if (e != hipSuccess) return e;
@@ -743,29 +829,32 @@ hipError_t launch_pattern_x(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
 template <int FORM, bool XVEC>
 hipError_t launch_gemv_fused(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                              int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
-                             int out_kind, hipStream_t s) {
-  return launch_gemv<FORM, true, XVEC>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+                             int out_kind, float ln_eps, hipStream_t s) {
+  return launch_gemv<FORM, true, XVEC>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y, out_kind, ln_eps,
+                                       s);
 }
 
 }  // namespace
 
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
-                                 int out_kind, hipStream_t s) {
+                                 int out_kind, float ln_eps, hipStream_t s) {
   const Layout& L = h->L;
   if (T == 0) return hipSuccess;
   if (L.n_out > 0 && T <= kFusedMaxT && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
 #define SBN_FUSED(FF)                                                                          \
   return xvec ? launch_gemv_fused<FF, true>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind,  \
-                                            s)                                                 \
-              : launch_gemv_fused<FF, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind, s)
+                                            ln_eps, s)                                         \
+              : launch_gemv_fused<FF, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind, \
+                                             ln_eps, s)
     if (L.form == kFormSparse24) SBN_FUSED(kFormSparse24);
     if (L.form == kFormPositional) SBN_FUSED(kFormPositional);
     SBN_FUSED(kFormKept);
 #undef SBN_FUSED
   }
-  hipError_t e = launch_quantize_act(x, T, L.K, ld_x, xq, ld_q, absmax, s);
+  hipError_t e = ln_eps > 0.0f ? launch_ln_quantize_act(x, T, L.K, ld_x, ln_eps, xq, ld_q, absmax, s)
+                               : launch_quantize_act(x, T, L.K, ld_x, xq, ld_q, absmax, s);
   if (e != hipSuccess) return e;
   return launch_bitlinear(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }

@@ -210,6 +210,46 @@ __device__ __forceinline__ void grouped_tile(int lin, int tiles_n, int tiles_t, 
   tile_t = group * kTileGroup + r % gsize;
 }
 
+// One DPP lane move of a double (both halves); lanes of rows outside RMASK read 0.0.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, RMASK, 0xF,
+                                                            false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                            RMASK, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum over the 64 lanes of a wave in fp64 (the lane moves of wave_sum_u32); every lane gets the
+// value of lane 63.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f64<0x140, 0xF>(v);  // row_mirror
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Round an fp32 value to a bf16 bit pattern, nearest even (finite values).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Parameter-free LayerNorm of two bf16 values (one word) with fp32 mean mu and 1/sigma r:
+// bf16(fl32(fl32(x - mu) * r)) each.
+__device__ __forceinline__ uint32_t ln_pair(uint32_t w, float mu, float r) {
+  const float z0 = __fmul_rn(__fsub_rn(__uint_as_float(w << 16), mu), r);
+  const float z1 = __fmul_rn(__fsub_rn(__uint_as_float(w & 0xFFFF0000u), mu), r);
+  return bf16_rne(z0) | (bf16_rne(z1) << 16);
+}
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 

@@ -42,6 +42,9 @@ int absmean_blocks(int64_t n_out);
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x, int8_t* q,
                                int64_t ld_q, float* absmax, hipStream_t s);
+hipError_t launch_ln_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x,
+                                  float eps, int8_t* q, int64_t ld_q, float* absmax,
+                                  hipStream_t s);
 hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
 hipError_t launch_export(const sbn_packed* h, int8_t* codes, uint8_t* keep, float* gamma,
                          hipStream_t s);
@@ -54,9 +57,10 @@ hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
 hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s);
 hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,
                          float* dx, int64_t ld_dx, hipStream_t s);
+// ln_eps > 0: parameter-free LayerNorm (with that epsilon) before the quantization.
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
-                                 int out_kind, hipStream_t s);
+                                 int out_kind, float ln_eps, hipStream_t s);
 
 // Raises a kernel's dynamic-LDS limit once per process and kernel (gfx950 has 160 KB of LDS per
 // CU).

@@ -18,8 +18,10 @@ def lib():
 
 def test_exports_match_header(lib):
     declared = b.header_symbols()
-    assert set(declared) == {"sbn_quantize_act", "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
-                             "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_bwd_dx", "sbn_free",
+    assert set(declared) == {"sbn_quantize_act", "sbn_layernorm_quantize_act",
+                             "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
+                             "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_fwd_ln_bf16",
+                             "sbn_bitlinear_bwd_dx", "sbn_free",
                              "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
@@ -81,6 +83,13 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
     assert lib.sbn_bitlinear_bwd_dx(None, None, 0, 1, None, 0, None) == ERR_INVALID
+    assert lib.sbn_layernorm_quantize_act(None, 1, 8, 8, 1e-5, None, 8, None, None) == ERR_INVALID
+    assert lib.sbn_layernorm_quantize_act(None, 1, 8, 8, 0.0, None, 8, None, None) == ERR_INVALID
+    assert lib.sbn_layernorm_quantize_act(None, 0, 8, 8, 1e-5, None, 8, None, None) == 0
+    assert lib.sbn_bitlinear_fwd_ln_bf16(None, None, 0, 1, 1e-5, None, 0, None, None, 0, 0,
+                                         None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_ln_bf16(None, None, 0, 1, 0.0, None, 0, None, None, 0, 0,
+                                         None) == ERR_INVALID
     lib.sbn_free(None)  # no-op
 
 

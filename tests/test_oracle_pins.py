@@ -593,3 +593,104 @@ def test_ste_dx_abs_bounds_value():
     pos = np.abs(inputs.f32_to_bf16_bits(np.ones((2, 24), np.float32)))
     same = oracle.ste_dx(pos, np.abs(codes).astype(np.int8), gamma).astype(np.float64)
     assert np.allclose(same, oracle.ste_dx_abs(pos, codes, gamma), rtol=2 ** -23)
+
+
+# ---------------------------------------------------------------------------------------------
+# Parameter-free LayerNorm before the quantizer (BitNet blog, "The BitLinear Layer", op 1).
+# ---------------------------------------------------------------------------------------------
+
+def _fl32(v: float) -> float:
+    return struct.unpack("f", struct.pack("f", v))[0]
+
+
+def _bf16_bits_py(v: float) -> int:
+    u = struct.unpack("I", struct.pack("f", v))[0]
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+
+
+def brute_layernorm(x_bits, eps):
+    """Pure Python: fsum statistics, fp32 normalization, bf16 rounding (bit patterns)."""
+    xs = inputs.bf16_bits_to_f32(np.asarray(x_bits)).astype(np.float64).tolist()
+    out = []
+    for row in xs:
+        k = len(row)
+        mu = math.fsum(row) / k
+        var = math.fsum((v - mu) ** 2 for v in row) / k
+        r = 1.0 / math.sqrt(var + float(np.float32(eps)))
+        mu32, r32 = _fl32(mu), _fl32(r)
+        out.append([_bf16_bits_py(_fl32(_fl32(_fl32(v) - mu32) * r32)) for v in row])
+    return np.array(out, dtype=np.uint16)
+
+
+def _ln_pins_fail(fn) -> bool:
+    import torch
+    rng = np.random.default_rng(77)
+    eps = 1e-5
+    for T, K, scale in ((3, 8, 3.0), (2, 16, 3.0), (4, 12, 3.0), (3, 16, 1e-3)):
+        # scale 1e-3 gives a variance below eps, where eps matters
+        x = inputs.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32) * scale)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            z = fn(x, eps)
+        if z.shape != (T, K) or not np.array_equal(z, brute_layernorm(x, eps)):
+            return True
+    # the library LayerNorm (no affine) in fp64, to bf16 precision
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((6, 64)).astype(np.float32) * 2 - 0.5)
+    ref = torch.nn.functional.layer_norm(
+        torch.from_numpy(inputs.bf16_bits_to_f32(x).astype(np.float64)), (64,), eps=eps).numpy()
+    z = inputs.bf16_bits_to_f32(fn(x, eps)).astype(np.float64)
+    if not np.all(np.abs(z - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6):
+        return True
+    # scaling x by 2^k and eps by 4^k leaves every bit of z unchanged
+    x2 = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x) * np.float32(8.0))
+    if not np.array_equal(fn(x2, eps * 64.0), fn(x, eps)):
+        return True
+    # a constant row normalizes to zero
+    c = inputs.f32_to_bf16_bits(np.full((2, 32), 1.75, np.float32))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        zc = fn(c, eps)
+    if not np.all(inputs.bf16_bits_to_f32(zc) == 0):
+        return True
+    return False
+
+
+def test_layernorm_pins():
+    assert not _ln_pins_fail(oracle.layernorm_bf16)
+
+
+def test_layernorm_quantize_zero_rows():
+    c = inputs.f32_to_bf16_bits(np.full((2, 32), -3.0, np.float32))
+    q, a = oracle.layernorm_quantize_act(c, 1e-5)
+    assert np.all(q == 0) and np.all(a == np.float32(1e-5))
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.default_rng(3)
+    z = np.concatenate([rng.standard_normal(5000).astype(np.float32),
+                        np.float32([0.0, -0.0, 1.0, 1.00390625, 1.005859375, 3.0e38, 1e-40])])
+    ours = oracle.f32_to_bf16_rne(z)
+    ref = torch.from_numpy(z).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+@pytest.mark.parametrize("mutant", ["unbiased", "no_eps", "var_not_std", "no_mean"])
+def test_layernorm_mutants_caught(mutant):
+    def f(x, eps):
+        xv = inputs.bf16_bits_to_f32(x).astype(np.float64)
+        k = xv.shape[1]
+        mu = xv.mean(axis=1)
+        d = xv - mu[:, None]
+        if mutant == "unbiased":
+            var = (d * d).sum(axis=1) / (k - 1)
+        else:
+            var = (d * d).sum(axis=1) / k
+        if mutant == "no_eps":
+            r = 1.0 / np.sqrt(var)
+        elif mutant == "var_not_std":
+            r = 1.0 / (var + eps)
+        else:
+            r = 1.0 / np.sqrt(var + eps)
+        m32 = np.zeros_like(mu, dtype=np.float32) if mutant == "no_mean" else mu.astype(np.float32)
+        z = (xv.astype(np.float32) - m32[:, None]).astype(np.float32) * r.astype(np.float32)[:, None]
+        return oracle.f32_to_bf16_rne(z.astype(np.float32))
+    assert _ln_pins_fail(f)
