@@ -24,7 +24,6 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kBwWaves = 4;
 constexpr int kBwCF = 4;                                 // 16-column fragments per wave

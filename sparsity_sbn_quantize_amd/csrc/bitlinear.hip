@@ -138,7 +138,12 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
   }
 }
 
-template <int FORM, bool FUSED, bool XVEC, int Q>
+// LN (bf16 input only): parameter-free LayerNorm before the quantization. XBUF (int8 input
+// only): brick and activation loads through buffer resources, straight-line; measured faster for
+// a few tokens (4.35 vs 4.58 us at T = 1 on the 2560 -> 6912 decode shape) and slower for 16
+// (6.35 vs 6.05 us), so the launcher picks it for T <= 4. The bf16-input kernel loads its bricks
+// through the buffer resource too (4.95 vs 5.06 us per one-kernel step at T = 1).
+template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
     const float* __restrict__ gamma_p, const void* __restrict__ xin, int64_t ld_x,
@@ -157,11 +162,23 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   const int K = (int)L.K, nq = (int)L.quads;
 
   uint32_t mask[Q][2], codes[Q][4];
+  // With FUSED or XBUF, positional and structured-sparse bricks come through a buffer resource
+  // over this row block's quads: a quad past the last reads as zero, so the loads are
+  // straight-line code and the compiler's wait counts stay exact (a wait for the activations then
+  // does not wait for the bricks behind them).
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(code_plane + ((rb * nq) << 6) * 16), (short)0, FORM != kFormKept ? nq * 1024 : 0,
+      kBufDword3);
   auto load_bricks = [&]() {
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
       const int q = wave + i * W;
-      if (q < nq) {
+      if constexpr (FORM != kFormKept && (FUSED || XBUF)) {
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, q * 1024, 0);
+        codes[i][0] = (uint32_t)c[0]; codes[i][1] = (uint32_t)c[1];
+        codes[i][2] = (uint32_t)c[2]; codes[i][3] = (uint32_t)c[3];
+        mask[i][0] = mask[i][1] = 0;
+      } else if (q < nq) {
         load_brick<FORM>(L, mask_plane, code_plane, ((rb * nq + q) << 6) | lane, mask[i],
                          codes[i]);
       } else {
@@ -174,15 +191,32 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   float a_t = 0.0f;     // a' of token t (FUSED)
   if constexpr (!FUSED) {
     load_bricks();
-    const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+    if constexpr (XVEC && XBUF) {
+      // One buffer resource over the T activation rows, straight-line loads: the lanes of a
+      // missing token take an offset past the range and read zero, as does the K tail of the last
+      // row; a piece past K in another row reads that row's padding or the next row, harmless
+      // because the weights there are zero. Offsets stay below 2^31: T <= 16, ld_x <= 2^26.
+      const int64_t ext = ((int64_t)T - 1) * ld_x + K;
+      const __amdgpu_buffer_rsrc_t xr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)xin, (short)0, (int)ext, kBufDword3);
 #pragma unroll
-    for (int i = 0; i < Q; ++i)
+      for (int i = 0; i < Q; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = (wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
-        b[i][j] = v4i{0, 0, 0, 0};
-        if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int voff = tok_ok ? t * (int)ld_x + 16 * b_chunk<FORM>(g, j) : (1 << 30);
+          b[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff, (wave + i * W) * kQuadK, 0);
+        }
+    } else {
+      const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = (wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
+          b[i][j] = v4i{0, 0, 0, 0};
+          if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
+        }
+    }
   } else {
     // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
     // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
@@ -211,7 +245,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     // does not wait for the bricks: the quantization below overlaps the brick loads.
     load_bricks();
     const int Tn = (int)T;  // <= kFusedMaxT; loops below stop at the real token count
-    if (ln_eps > 0.0f) {
+    if constexpr (LN) {
       // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
       // and sum of squared deviations over the wave (DPP) and then the waves (LDS, fixed order);
       // the lane's elements are replaced by their bf16 normalized values.
@@ -780,17 +814,24 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   const Layout& L = h->L;
   const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
   const int Q = (int)((L.quads + W - 1) / W);
-#define SBN_GEMV(QQ)                                                                          \
-  hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ>), dim3((unsigned)L.row_blocks),   \
-                     dim3(64 * W), 0, s, h->mask, h->codes, L, h->gamma, x, ld_x, xq_out, ld_q, \
-                     absmax, T, y, ld_y, out_kind, ln_eps)
-  if (Q == 1) {
-    SBN_GEMV(1);
-  } else if (Q == 2) {
-    SBN_GEMV(2);
-  } else {
-    SBN_GEMV(3);
+#define SBN_GEMV(QQ, LNV, XB)                                                                 \
+  hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ, LNV, XB>),                           \
+                     dim3((unsigned)L.row_blocks), dim3(64 * W), 0, s, h->mask, h->codes, L,     \
+                     h->gamma, x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
+#define SBN_GEMV_Q(QQ)                                                                        \
+  if (FUSED) {                                                                                \
+    if (ln_eps > 0.0f) SBN_GEMV(QQ, FUSED, false); else SBN_GEMV(QQ, false, false);          \
+  } else {                                                                                    \
+    if (T <= kFusedMaxT) SBN_GEMV(QQ, false, !FUSED); else SBN_GEMV(QQ, false, false);        \
   }
+  if (Q == 1) {
+    SBN_GEMV_Q(1);
+  } else if (Q == 2) {
+    SBN_GEMV_Q(2);
+  } else {
+    SBN_GEMV_Q(3);
+  }
+#undef SBN_GEMV_Q
 #undef SBN_GEMV
   return hipGetLastError();
 }

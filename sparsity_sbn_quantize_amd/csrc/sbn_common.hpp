@@ -251,6 +251,7 @@ __device__ __forceinline__ uint32_t ln_pair(uint32_t w, float mu, float r) {
 }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no stride): offsets are
