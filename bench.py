@@ -33,15 +33,22 @@ METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GE
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
                   "sparsity_sbn_quantize_amd/csrc/sbn_common.hpp",
+                  "sparsity_sbn_quantize_amd/csrc/backward.hip",
                   "sparsity_sbn_quantize_amd/csrc/pack.hip",
                   "sparsity_sbn_quantize_amd/csrc/quantize_act.hip"]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comment-only lines, trailing // comments and blank lines
+    are left out, so editing a comment does not invalidate measured traffic."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

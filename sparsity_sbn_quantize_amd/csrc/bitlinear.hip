@@ -15,10 +15,12 @@
 // code word and becomes int8 bytes with nine ALU ops; the kept form (2n < m) is expanded with a
 // plain loop over its mask.
 //
-//   GEMV (T <= 16): one workgroup per one or two 16-row fragment rows, its 4 waves split K; the
-//   activations are staged once in LDS.
+//   GEMV (T <= 16): one workgroup per 16-row fragment row, its waves split K (one to three
+//   256-K quads each); operands go straight from memory into MFMA registers and the waves' sums
+//   meet once in LDS. With bf16 input (T <= 4) every workgroup also quantizes (optionally after a
+//   parameter-free LayerNorm) the activations it needs.
 //   GEMM (T > 16): a workgroup computes 256 rows x 128 tokens; the 128 x 256 activation tile of
-//   each K step is staged in LDS and shared by the waves.
+//   each K step is staged in LDS and shared by the waves; 2:4 runs on the structured-sparse MFMA.
 #include <algorithm>
 
 #include "sbn_internal.hpp"
