@@ -110,6 +110,24 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
                                int n_keep, int m_group, sbn_packed** handle /* host */,
                                void* stream);
 
+/* Flags of sbn_pack_nm_ternary_ex. */
+#define SBN_PACK_VARIANCE_CORRECTION 1
+
+/*
+ * sbn_pack_nm_ternary with options. SBN_PACK_VARIANCE_CORRECTION ("From 2:4 to 8:16 sparsity
+ * patterns in LLMs for Outliers and Weights with Variance Correction", method summary: after
+ * pruning, the remaining weights are rescaled back to the dense variance): the codes and the mask
+ * are unchanged; the scale the matmuls use becomes gamma_out = fl32(gamma * sqrt(nd / ns)), with
+ * nd the nonzero codes of the dense (n = m) ternary weights and ns those of the n:m codes
+ * (gamma_out = gamma when ns == 0). The page gives no formula; this restores the mean square of
+ * the ternary weights gamma * code, per tensor like gamma. sbn_bitlinear_fwd, the bf16 forwards,
+ * sbn_bitlinear_bwd_dx and sbn_packed_export then use gamma_out. Each call may change the flags.
+ * flags = 0 is sbn_pack_nm_ternary; other bits give SBN_ERR_INVALID_ARG.
+ */
+sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
+                                  int n_keep, int m_group, int flags, sbn_packed** handle /* host */,
+                                  void* stream);
+
 /*
  * n:m-sparse ternary x INT8 matmul with int32 accumulation and fused dequantization
  * ("The BitLinear Layer", operations 4 and 5).
@@ -177,7 +195,8 @@ void sbn_free(sbn_packed* handle);
  * Canonical export of a handle, for tests and checkpoints (enqueued on `stream`):
  *   codes     [n_out][K] int8 in {-1, 0, +1} (0 where pruned), or NULL to skip
  *   keep_mask [n_out][K] uint8 in {0, 1}, or NULL to skip
- *   gamma     [1] fp32, or NULL to skip
+ *   gamma     [1] fp32, or NULL to skip (the scale the matmuls use: gamma, or the
+ *             variance-corrected gamma_out after a pack with SBN_PACK_VARIANCE_CORRECTION)
  */
 sbn_status sbn_packed_export(const sbn_packed* w, int8_t* codes, uint8_t* keep_mask, float* gamma,
                              void* stream);

@@ -41,6 +41,8 @@ Readings taken where the pages are silent or disagree (each is also listed in th
     n < m, a mask bitstream (m bits per group, bit i <-> position i of the group, LSB first); each
     stream is padded with zero bits to a whole byte per row;
   * the output is fp32 y = fl32(fl32(fl32(acc) * gamma) * fl32(a' / 127)).
+  * variance correction (optional) rescales the ternary weights gamma * codes to the mean square of
+    the dense ternary weights: gamma_out = fl32(gamma * sqrt(nd / ns)) per tensor;
   * the straight-through data gradient is dX = gamma * dY @ codes: both quantizers pass the
     gradient unchanged, so only the ternary weights of the forward remain; dY is bf16, dX fp32;
   * the mask flip rate r_t counts positions whose keep bit differs between consecutive masks,
@@ -271,6 +273,29 @@ def bitlinear_forward(x_bf16: np.ndarray, w: np.ndarray, n: int, m: int) -> dict
     acc = int_matmul(q, packed["codes"])
     y = dequantize(acc, packed["gamma"], a_prime)
     return dict(packed, q=q, a_prime=a_prime, acc=acc, y=y)
+
+
+# ----------------------------------------------------------------------------------------------
+# Variance correction: [8:16] method summary (after pruning, the remaining weights are rescaled
+# back to the dense variance). The page gives no formula; the reading applies it to the weights
+# the matmul uses, gamma * codes, per tensor like gamma: their mean square is gamma^2 times the
+# share of nonzero codes, so the factor is sqrt(nonzero dense codes / nonzero n:m codes).
+# ----------------------------------------------------------------------------------------------
+
+def variance_correction(w: np.ndarray, n: int, m: int) -> dict:
+    """gamma, the nonzero counts nd (dense ternary, n = m) and ns (n:m ternary), and the output
+    scale gamma_out = fl32(gamma * sqrt(nd / ns)) (gamma when ns == 0)."""
+    w = np.asarray(w, dtype=np.float32)
+    gamma = absmean_gamma(w)
+    dense = ternary_codes(w, np.ones(w.shape, dtype=bool), gamma)
+    sparse = ternary_codes(w, nm_keep_mask(w, n, m), gamma)
+    nd = int(np.count_nonzero(dense))
+    ns = int(np.count_nonzero(sparse))
+    if ns == 0:
+        gamma_out = np.float32(gamma)
+    else:
+        gamma_out = np.float32(np.float64(gamma) * np.sqrt(np.float64(nd) / np.float64(ns)))
+    return {"gamma": gamma, "nd": nd, "ns": ns, "gamma_out": gamma_out}
 
 
 # ----------------------------------------------------------------------------------------------

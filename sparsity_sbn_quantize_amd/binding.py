@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sbn.h")
 
 SBN_OUT_F32 = 0
 SBN_OUT_I32_ACC = 1
+SBN_PACK_VARIANCE_CORRECTION = 1
 STATUS = {0: "SBN_OK", -1: "SBN_ERR_INVALID_ARG", -2: "SBN_ERR_UNSUPPORTED", -3: "SBN_ERR_SHAPE",
           -4: "SBN_ERR_HIP", -5: "SBN_ERR_OOM"}
 
@@ -44,6 +45,8 @@ _SIGNATURES = {
                                                   _I64, _P, _P]),
     "sbn_pack_nm_ternary": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_void_p), _P]),
+    "sbn_pack_nm_ternary_ex": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), _P]),
     "sbn_bitlinear_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, ctypes.c_int, _P]),
     "sbn_bitlinear_fwd_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I64,
                                               ctypes.c_int, _P]),
@@ -145,20 +148,25 @@ def layernorm_quantize_act(x, eps: float = 1e-5, out_q=None, out_absmax=None, st
 class PackedWeight:
     """A packed n:m ternary weight (library-owned device memory)."""
 
-    def __init__(self, w, n: int, m: int, stream=None):
+    def __init__(self, w, n: int, m: int, stream=None, variance_correction: bool = False):
         self._h = ctypes.c_void_p(0)
         self.n, self.m = n, m
+        self.variance_correction = variance_correction
         self.pack(w, stream)
 
-    def pack(self, w, stream=None):
-        """(Re-)packs from fp32 latent weights [n_out][K]; re-packing reuses the handle."""
+    def pack(self, w, stream=None, variance_correction=None):
+        """(Re-)packs from fp32 latent weights [n_out][K]; re-packing reuses the handle. With
+        variance_correction, the matmuls use the variance-corrected scale (sbn_pack_nm_ternary_ex)."""
+        if variance_correction is not None:
+            self.variance_correction = variance_correction
         import torch
         _require_cuda(w, "w")
         if w.dtype != torch.float32:
             raise ValueError("w must be float32")
         n_out, K = w.shape
-        check(lib().sbn_pack_nm_ternary(_ptr(w), n_out, K, _ld(w, K), self.n, self.m,
-                                        ctypes.byref(self._h), _stream(stream)))
+        flags = SBN_PACK_VARIANCE_CORRECTION if self.variance_correction else 0
+        check(lib().sbn_pack_nm_ternary_ex(_ptr(w), n_out, K, _ld(w, K), self.n, self.m, flags,
+                                           ctypes.byref(self._h), _stream(stream)))
         self.n_out, self.K = n_out, K
         return self
 

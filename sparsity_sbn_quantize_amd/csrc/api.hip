@@ -112,6 +112,14 @@ sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t
 
 sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
                                int n_keep, int m_group, sbn_packed** handle, void* stream) {
+  return sbn_pack_nm_ternary_ex(w_latent, n_out, K, ld_w, n_keep, m_group, 0, handle, stream);
+}
+
+sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
+                                  int n_keep, int m_group, int flags, sbn_packed** handle,
+                                  void* stream) {
+  if ((flags & ~SBN_PACK_VARIANCE_CORRECTION) != 0)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: unknown flags 0x%x", flags);
   if (!handle) return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: handle is null");
   if (!pattern_ok(n_keep, m_group))
     return fail(SBN_ERR_UNSUPPORTED,
@@ -174,6 +182,10 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     off = align_up(off + sizeof(int) * sbn::kGemmSyncInts, 256);
     const size_t off_flips = off;
     off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
+    const size_t off_vc = off;
+    off = align_up(off + 2 * sizeof(uint32_t) * slots / 16, 256);
+    const size_t off_gamma_vc = off;
+    off = align_up(off + sizeof(float), 256);
     const int64_t rq_count = (n_out + 127) / 128;
     const size_t off_tplane = off;
     off = align_up(off + (size_t)rq_count * (size_t)L.quads * 8192, 256);
@@ -212,12 +224,16 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
     h->partials = reinterpret_cast<double*>(h->base + off_part);
     h->gemm_sync = reinterpret_cast<int*>(h->base + off_sync);
     h->flip_parts = reinterpret_cast<uint32_t*>(h->base + off_flips);
+    h->vc_parts = reinterpret_cast<uint32_t*>(h->base + off_vc);
+    h->gamma_vc = reinterpret_cast<float*>(h->base + off_gamma_vc);
+    h->vc = false;
     h->tplane = reinterpret_cast<uint32_t*>(h->base + off_tplane);
     h->rq_count = rq_count;
     *handle = h;
   }
   h->last_stream = s;
   h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
+  h->vc = (flags & SBN_PACK_VARIANCE_CORRECTION) != 0;
   hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
   if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
   return SBN_OK;

@@ -245,13 +245,13 @@ hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy,
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bitlinear_bwd_dx<true>, dim3((unsigned)(tiles_c * tiles_t)),
                        dim3(kBwThreads), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,
-                       h->gamma, dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
+                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
   } else {
     e = allow_smem(bitlinear_bwd_dx<false>, kBwSmem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bitlinear_bwd_dx<false>, dim3((unsigned)(tiles_c * tiles_t)),
                        dim3(kBwThreads), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,
-                       h->gamma, dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
+                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
   }
   return hipGetLastError();
 }

@@ -819,7 +819,7 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
 #define SBN_GEMV(QQ, LNV, XB)                                                                 \
   hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ, LNV, XB>),                           \
                      dim3((unsigned)L.row_blocks), dim3(64 * W), 0, s, h->mask, h->codes, L,     \
-                     h->gamma, x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
+                     h->gamma_out(), x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
 #define SBN_GEMV_Q(QQ)                                                                        \
   if (FUSED) {                                                                                \
     if (ln_eps > 0.0f) SBN_GEMV(QQ, FUSED, false); else SBN_GEMV(QQ, false, false);          \
@@ -855,8 +855,8 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   const bool y_fits = (double)T * (double)ld_y * 4.0 < 2147483647.0;
   const int ksplit = (gx * gy <= kSplitMaxTiles && L.quads >= 8 && y_fits) ? 2 : 1;
   hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC>), dim3((unsigned)(gx * gy * ksplit)),
-                     dim3(kGemmThreads), kGemmSmem, s, h->mask, h->codes, L, h->gamma, xq, ld_q,
-                     absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, ksplit, h->gemm_sync);
+                     dim3(kGemmThreads), kGemmSmem, s, h->mask, h->codes, L, h->gamma_out(), xq,
+                     ld_q, absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, ksplit, h->gemm_sync);
   return hipGetLastError();
 }
 

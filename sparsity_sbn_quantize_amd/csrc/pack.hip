@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
                                                       const float* __restrict__ gamma_p,
                                                       uint8_t* __restrict__ mask_plane,
                                                       uint8_t* __restrict__ code_plane,
-                                                      uint32_t* __restrict__ flip_parts) {
+                                                      uint32_t* __restrict__ flip_parts,
+                                                      uint32_t* __restrict__ vc_parts) {
   const int64_t frag = blockIdx.x;
   const int64_t rb = frag / L.quads, bq = frag % L.quads;
   const int tid = threadIdx.x;
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
   uint32_t nz = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) nz |= (a[i] > half_bits ? 1u : 0u) << i;
+  const uint32_t nz_dense = nz;  // the codes of the dense (n = m) ternary weights
   nz &= keep;
   if constexpr (kSp24) {
     // slots 8h + 2q (lower kept) and 8h + 2q + 1 (higher kept) of group q of the 16 positions:
@@ -249,6 +251,15 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
     *mp = (uint16_t)keep;
     const uint32_t sum = wave_sum_u32((uint32_t)__builtin_popcount((old_keep ^ keep) & 0xFFFFu));
     if ((tid & 63) == 0) flip_parts[frag * 4 + (tid >> 6)] = sum;
+  }
+  if (vc_parts) {
+    // Variance correction: nonzero counts of the dense and of the n:m ternary codes, per wave.
+    const uint32_t d = wave_sum_u32((uint32_t)__builtin_popcount(nz_dense));
+    const uint32_t sp = wave_sum_u32((uint32_t)__builtin_popcount(nz));
+    if ((tid & 63) == 0) {
+      vc_parts[(frag * 4 + (tid >> 6)) * 2] = d;
+      vc_parts[(frag * 4 + (tid >> 6)) * 2 + 1] = sp;
+    }
   }
 }
 
@@ -432,6 +443,40 @@ __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* 
   }
 }
 
+// Variance correction ("From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights with
+// Variance Correction", the method summary: the remaining weights are rescaled back to the dense
+// variance). The weights the matmul uses are gamma * codes, whose mean square is gamma^2 times the
+// share of nonzero codes, so the factor is sqrt(nonzero dense codes / nonzero n:m codes) and the
+// output scale is gamma_out = fl32(gamma * sqrt(nd / ns)) (gamma when ns == 0). One workgroup.
+__global__ __launch_bounds__(1024) void vc_finalize(const uint32_t* __restrict__ parts, int64_t num,
+                                                    const float* __restrict__ gamma,
+                                                    float* __restrict__ gamma_out) {
+  __shared__ unsigned long long red[2][16];
+  unsigned long long d = 0, sp = 0;
+  for (int64_t i = threadIdx.x; i < num; i += 1024) {
+    d += parts[2 * i];
+    sp += parts[2 * i + 1];
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    d += __shfl_xor(d, o, 64);
+    sp += __shfl_xor(sp, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = d;
+    red[1][threadIdx.x >> 6] = sp;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long td = 0, ts = 0;
+    for (int i = 0; i < 16; ++i) {
+      td += red[0][i];
+      ts += red[1][i];
+    }
+    const double g = (double)gamma[0];
+    gamma_out[0] = ts == 0 ? gamma[0] : (float)(g * sqrt((double)td / (double)ts));
+  }
+}
+
 // Sum of the per-wave flip counts of the last pack (one workgroup; num may be 0).
 __global__ __launch_bounds__(1024) void sum_flips(const uint32_t* __restrict__ parts, int64_t num,
                                                   unsigned long long* __restrict__ out) {
@@ -467,9 +512,10 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
+  uint32_t* const vc = h->vc ? h->vc_parts : nullptr;
 #define SBN_PACK(MM, FF)                                                                      \
   hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
-                     h->mask, h->codes, h->flip_parts)
+                     h->mask, h->codes, h->flip_parts, vc)
   if (L.form == kFormSparse24) {
     SBN_PACK(4, kFormSparse24);
   } else if (L.m == 4) {
@@ -480,6 +526,10 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
     if (L.positional) SBN_PACK(16, kFormPositional); else SBN_PACK(16, kFormKept);
   }
 #undef SBN_PACK
+  if (h->vc) {
+    hipLaunchKernelGGL(vc_finalize, dim3(1), dim3(1024), 0, s, h->vc_parts,
+                       L.row_blocks_pad * L.quads * 4, h->gamma, h->gamma_vc);
+  }
   return hipGetLastError();
 }
 
@@ -492,7 +542,7 @@ hipError_t launch_export(const sbn_packed* h, int8_t* codes, uint8_t* keep, floa
     hipLaunchKernelGGL(export_canonical, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        L, h->mask, h->codes, codes, keep);
   }
-  if (gamma) hipLaunchKernelGGL(copy_gamma, dim3(1), dim3(1), 0, s, h->gamma, gamma);
+  if (gamma) hipLaunchKernelGGL(copy_gamma, dim3(1), dim3(1), 0, s, h->gamma_out(), gamma);
   return hipGetLastError();
 }
 

@@ -24,11 +24,16 @@ struct sbn_packed {
   double* partials;    // device workspace [num_partials]
   int* gemm_sync;      // split-K flags: kGemmSyncInts words, zero between calls
   uint32_t* flip_parts;  // keep bits changed by the last pack, one count per pack wave
+  uint32_t* vc_parts;   // variance correction: nonzero counts (dense, n:m) per pack wave
+  float* gamma_vc;      // variance-corrected output scale (device scalar)
+  bool vc;              // the last pack applied the variance correction (host-side state)
   uint32_t* tplane;     // transposed code plane (data-gradient matmul), 2 bits per weight
   int64_t rq_count;     // 128-row groups of the transposed plane
   bool tplane_valid;    // the transposed plane matches the last pack (host-side state)
   int device;
   hipStream_t last_stream;
+  // Scale the matmuls multiply by: gamma, or the variance-corrected gamma.
+  float* gamma_out() const { return vc ? gamma_vc : gamma; }
 };
 
 namespace sbn {

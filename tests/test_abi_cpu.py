@@ -19,7 +19,7 @@ def lib():
 def test_exports_match_header(lib):
     declared = b.header_symbols()
     assert set(declared) == {"sbn_quantize_act", "sbn_layernorm_quantize_act",
-                             "sbn_pack_nm_ternary", "sbn_bitlinear_fwd",
+                             "sbn_pack_nm_ternary", "sbn_pack_nm_ternary_ex", "sbn_bitlinear_fwd",
                              "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_fwd_ln_bf16",
                              "sbn_bitlinear_bwd_dx", "sbn_free",
                              "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_query",
@@ -82,6 +82,11 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_export_rpf(None, None, None, None) == ERR_INVALID
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
+    h = ctypes.c_void_p(0)
+    for flags in (2, -1, 1 << 30):  # unknown flag bits are rejected before any device work
+        assert lib.sbn_pack_nm_ternary_ex(None, 16, 64, 64, 2, 4, flags, ctypes.byref(h),
+                                          None) == ERR_INVALID
+    assert lib.sbn_pack_nm_ternary_ex(None, 16, 64, 64, 2, 4, 1, None, None) == ERR_INVALID
     assert lib.sbn_bitlinear_bwd_dx(None, None, 0, 1, None, 0, None) == ERR_INVALID
     assert lib.sbn_layernorm_quantize_act(None, 1, 8, 8, 1e-5, None, 8, None, None) == ERR_INVALID
     assert lib.sbn_layernorm_quantize_act(None, 1, 8, 8, 0.0, None, 8, None, None) == ERR_INVALID

@@ -694,3 +694,60 @@ def test_layernorm_mutants_caught(mutant):
         z = (xv.astype(np.float32) - m32[:, None]).astype(np.float32) * r.astype(np.float32)[:, None]
         return oracle.f32_to_bf16_rne(z.astype(np.float32))
     assert _ln_pins_fail(f)
+
+
+# ---------------------------------------------------------------------------------------------
+# Variance correction (8:16 paper, method summary): gamma_out = gamma * sqrt(nd / ns).
+# ---------------------------------------------------------------------------------------------
+
+def _vc_pins_fail(fn) -> bool:
+    """fn(w, n, m) -> dict with gamma_out, nd, ns."""
+    g = load("worked_example_2of4.json")
+    w = np.array([g["w"]], np.float32)
+    r = fn(w, 2, 4)
+    # hand count: dense codes [+1,-1,+1,+1,0,0,+1,+1] (6 nonzero), 2:4 codes [+1,-1,0,0,0,0,+1,+1]
+    if r["nd"] != 6 or r["ns"] != 4:
+        return True
+    if r["gamma_out"] != np.float32(_fl32(0.48046875 * math.sqrt(6 / 4))):
+        return True
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    # n = m: nothing is pruned, the scale is unchanged
+    r = fn(w, 8, 8)
+    if r["gamma_out"] != oracle.absmean_gamma(w):
+        return True
+    # population closed form for Gaussian weights: nonzero shares 1 - F(gamma/2) (dense) and
+    # 1 - masked zero fraction (n:m) at the realized gamma
+    w = (np.random.default_rng(22).standard_normal((512, 2048)) * 0.02).astype(np.float32)
+    F, f = _gauss_abs(0.02)
+    for n, m in ((2, 4), (8, 16)):
+        r = fn(w, n, m)
+        half = float(oracle.absmean_gamma(w)) / 2
+        k2 = (1 - F(half)) / (1 - masked_zero_fraction(F, f, half, n, m))
+        if abs(r["gamma_out"] / oracle.absmean_gamma(w) - math.sqrt(k2)) > 2e-3:
+            return True
+    # a power-of-two scale of the weights scales gamma_out exactly
+    if fn(w * np.float32(4), 2, 4)["gamma_out"] != np.float32(4) * fn(w, 2, 4)["gamma_out"]:
+        return True
+    return False
+
+
+def test_variance_correction_pins():
+    assert not _vc_pins_fail(oracle.variance_correction)
+
+
+@pytest.mark.parametrize("mutant", ["inverted", "squared", "keep_count"])
+def test_variance_correction_mutants_caught(mutant):
+    def f(w, n, m):
+        r = dict(oracle.variance_correction(w, n, m))
+        g64 = np.float64(r["gamma"])
+        if mutant == "inverted":
+            r["gamma_out"] = np.float32(g64 * np.sqrt(r["ns"] / r["nd"])) if r["nd"] else r["gamma"]
+        elif mutant == "squared":
+            r["gamma_out"] = np.float32(g64 * (r["nd"] / r["ns"])) if r["ns"] else r["gamma"]
+        else:  # kept positions instead of nonzero codes
+            ns = int(oracle.nm_keep_mask(w, n, m).sum())
+            r["ns"] = ns
+            r["gamma_out"] = np.float32(g64 * np.sqrt(r["nd"] / ns))
+        return r
+    assert _vc_pins_fail(f)
