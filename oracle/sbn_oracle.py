@@ -46,7 +46,9 @@ Readings taken where the pages are silent or disagree (each is also listed in th
   * the straight-through data gradient is dX = gamma * dY @ codes: both quantizers pass the
     gradient unchanged, so only the ternary weights of the forward remain; dY is bf16, dX fp32;
   * the mask flip rate r_t counts positions whose keep bit differs between consecutive masks,
-    divided by the number of weights; a first mask is compared with one that keeps nothing.
+    divided by the number of weights; a first mask is compared with one that keeps nothing;
+  * the compact inference encoding keeps, per group, a nonzero mask (m bits) and n sign slots
+    for the nonzero codes in ascending position (1 = -1), m + n bits per group, LSB first.
 
 Floating point follows the precision the path decides integers in (fp32 scale and product); the
 weight-scale sum is accumulated in fp64.
@@ -340,6 +342,68 @@ def mask_flips(keep_prev, keep_new) -> int:
     if prev.shape != new.shape:
         raise ValueError(f"mask shapes differ: {prev.shape} vs {new.shape}")
     return int(np.count_nonzero(prev != new))
+
+
+# ----------------------------------------------------------------------------------------------
+# Compact inference encoding: [BitNet-blog] "Why 1.58 Bits?" (a ternary weight holds log2 3 bits)
+# and "bitnet.cpp: Matrix-Free Inference" (packed ternary weights are unpacked on chip);
+# [8:16] abstract (the per-group metadata cost of an n:m pattern). Once packed, the product needs
+# only which positions are nonzero and their signs: a pruned position and a kept zero both give 0.
+# ----------------------------------------------------------------------------------------------
+
+def compact_row_bytes(n: int, m: int, k: int) -> int:
+    """Bytes per row of the compact encoding: m + n bits per group, padded to a byte."""
+    return ((k // m) * (m + n) + 7) // 8
+
+
+def compact_pack(codes: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Compact encoding of n:m ternary codes, per row, LSB first.
+
+    Group g (positions g*m .. g*m+m-1) owns bits [g*(m+n), (g+1)*(m+n)) of the row stream:
+      bit i      (0 <= i < m): 1 when position g*m + i holds a nonzero code;
+      bit m + j  (0 <= j < n): 1 when the group's j-th nonzero code, counting by ascending
+                               position, is -1; slots past the group's nonzero count are 0.
+    Requires at most n nonzero codes per group (true of every n:m pack).  Returns uint8
+    [n_out][compact_row_bytes].
+    """
+    codes = np.asarray(codes, dtype=np.int8)
+    n_out, k = codes.shape
+    check_pattern(n, m, k)
+    groups = k // m
+    c = codes.reshape(n_out, groups, m)
+    nz = c != 0
+    if np.any(nz.sum(axis=2) > n):
+        raise ValueError("a group has more than n nonzero codes")
+    rank = np.cumsum(nz, axis=2) - 1  # index of each nonzero among its group's nonzeros
+    slots = np.zeros((n_out, groups, n), dtype=bool)
+    for j in range(n):
+        slots[:, :, j] = np.any(nz & (rank == j) & (c < 0), axis=2)
+    bits = np.concatenate([nz, slots], axis=2).reshape(n_out, groups * (m + n))
+    out = np.packbits(bits.astype(np.uint8), axis=1, bitorder="little")
+    assert out.shape == (n_out, compact_row_bytes(n, m, k))
+    return out
+
+
+def compact_unpack(data: np.ndarray, n: int, m: int, k: int) -> np.ndarray:
+    """Inverse of compact_pack: ternary codes int8 [n_out][K]. Rejects streams whose unused sign
+    slots or padding bits are not zero."""
+    data = np.asarray(data, dtype=np.uint8)
+    n_out = data.shape[0]
+    groups = k // m
+    allbits = np.unpackbits(data, axis=1, bitorder="little")
+    if np.any(allbits[:, groups * (m + n):]):
+        raise ValueError("nonzero padding bits")
+    bits = allbits[:, : groups * (m + n)].reshape(n_out, groups, m + n).astype(bool)
+    nz, slots = bits[:, :, :m], bits[:, :, m:]
+    count = nz.sum(axis=2)
+    if np.any(count > n):
+        raise ValueError("a group has more than n nonzero positions")
+    if np.any(slots & (np.arange(n) >= count[:, :, None])):
+        raise ValueError("a sign slot past the group's nonzero count is set")
+    rank = np.cumsum(nz, axis=2) - 1
+    neg = np.take_along_axis(slots, np.clip(rank, 0, n - 1), axis=2) & nz
+    codes = np.where(nz, np.where(neg, -1, 1), 0).astype(np.int8)
+    return codes.reshape(n_out, k)
 
 
 # ----------------------------------------------------------------------------------------------

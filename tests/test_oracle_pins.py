@@ -751,3 +751,134 @@ def test_variance_correction_mutants_caught(mutant):
             r["gamma_out"] = np.float32(g64 * np.sqrt(r["nd"] / ns))
         return r
     assert _vc_pins_fail(f)
+
+
+# ---------------------------------------------------------------------------------------------
+# Compact inference encoding: per group, m nonzero-mask bits then n sign slots (1 = -1) for the
+# nonzero codes in ascending position; m + n bits per group, LSB first.
+# ---------------------------------------------------------------------------------------------
+
+# Hand-encoded rows (codes, n, m, bytes). 2:4 [+1,-1,0,0 | 0,0,+1,+1] (the worked example's
+# sparse codes): group 0 mask 1100, slots (0, 1); group 1 mask 0011, slots (0, 0): bits
+# 110001 001100 -> 0x23 0x03. 6:8 [+1,0,-1,0,0,+1,-1,0]: mask 10100110, slots 0,1,0,1,0,0 ->
+# 0x65 0x0A. 2:4 [0,0,0,-1 | -1,0,+1,0]: group 0 has one nonzero (slots 1, 0), group 1 mask 1010,
+# slots (1, 0) -> bits 000110 101010 -> 0x58 0x05.
+COMPACT_HAND = [
+    ([1, -1, 0, 0, 0, 0, 1, 1], 2, 4, [0x23, 0x03]),
+    ([1, 0, -1, 0, 0, 1, -1, 0], 6, 8, [0x65, 0x0A]),
+    ([0, 0, 0, -1, -1, 0, 1, 0], 2, 4, [0x58, 0x05]),
+]
+
+
+def _compact_brute(codes, n, m):
+    """Bit-by-bit encoder in plain Python."""
+    out = []
+    for row in codes:
+        bits = []
+        for g in range(len(row) // m):
+            grp = [int(v) for v in row[g * m:(g + 1) * m]]
+            bits += [1 if v != 0 else 0 for v in grp]
+            signs = [1 if v < 0 else 0 for v in grp if v != 0]
+            bits += signs + [0] * (n - len(signs))
+        bits += [0] * (-len(bits) % 8)
+        out.append([sum(b << i for i, b in enumerate(bits[o:o + 8]))
+                    for o in range(0, len(bits), 8)])
+    return np.array(out, np.uint8)
+
+
+def _random_nm_codes(rng, n_out, k, n, m):
+    """Ternary codes with at most n nonzeros per group (some groups with fewer)."""
+    c = rng.integers(-1, 2, (n_out, k // m, m)).astype(np.int8)
+    for r in range(n_out):
+        for g in range(k // m):
+            nz = np.flatnonzero(c[r, g])
+            limit = rng.integers(0, n + 1)
+            if len(nz) > limit:
+                c[r, g, rng.choice(nz, len(nz) - limit, replace=False)] = 0
+    return c.reshape(n_out, k)
+
+
+def _compact_pins_fail(pack) -> bool:
+    for codes, n, m, expect in COMPACT_HAND:
+        if not np.array_equal(pack(np.array([codes], np.int8), n, m)[0], np.array(expect, np.uint8)):
+            return True
+    rng = np.random.default_rng(31)
+    for n, m in ((2, 4), (6, 8), (8, 16), (3, 8), (1, 4), (8, 8), (12, 16)):
+        c = _random_nm_codes(rng, 3, 4 * m, n, m)
+        if not np.array_equal(pack(c, n, m), _compact_brute(c, n, m)):
+            return True
+    return False
+
+
+def test_compact_pins():
+    assert not _compact_pins_fail(oracle.compact_pack)
+
+
+def test_compact_size():
+    """m + n bits per group: 1.5 bits per weight at 2:4 and 8:16, 1.75 at 6:8, 2 when dense."""
+    for (n, m), bpw in (((2, 4), 1.5), ((8, 16), 1.5), ((6, 8), 1.75), ((8, 8), 2.0),
+                        ((4, 8), 1.5), ((3, 8), 1.375)):
+        assert oracle.compact_row_bytes(n, m, 2560) * 8 == bpw * 2560
+    assert oracle.compact_row_bytes(6, 8, 8) == 2  # 14 bits -> 2 bytes
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 16), (3, 8), (1, 4), (8, 8), (16, 16)])
+def test_compact_roundtrip(n, m):
+    """unpack(pack(c)) == c for random codes and for the oracle's own n:m packs."""
+    rng = np.random.default_rng(n * 17 + m)
+    c = _random_nm_codes(rng, 5, 20 * m, n, m)
+    assert np.array_equal(oracle.compact_unpack(oracle.compact_pack(c, n, m), n, m, 20 * m), c)
+    w = (rng.standard_normal((7, 40 * m)) * 0.02).astype(np.float32)
+    p = oracle.pack_nm_ternary(w, n, m)
+    data = oracle.compact_pack(p["codes"], n, m)
+    assert np.array_equal(oracle.compact_unpack(data, n, m, 40 * m), p["codes"])
+    # the nonzero mask bits count the nonzero codes
+    bits = np.unpackbits(data, axis=1, bitorder="little")[:, : 40 * (m + n)].reshape(7, 40, m + n)
+    assert np.array_equal(bits[:, :, :m].sum(axis=2),
+                          (p["codes"].reshape(7, 40, m) != 0).sum(axis=2))
+
+
+def test_compact_rejects_bad_streams():
+    with pytest.raises(ValueError):
+        oracle.compact_pack(np.array([[1, 1, 1, 0]], np.int8), 2, 4)  # 3 nonzeros in a 2:4 group
+    with pytest.raises(ValueError):
+        oracle.compact_unpack(np.array([[0x21]], np.uint8), 2, 4, 4)  # slot 1 set, 1 nonzero
+    with pytest.raises(ValueError):
+        oracle.compact_unpack(np.array([[0x00, 0x10]], np.uint8), 2, 4, 8)  # padding bit set
+
+
+@pytest.mark.parametrize("mutant", ["polarity", "descending", "running_slots", "msb_mask"])
+def test_compact_mutants_caught(mutant):
+    def pack(codes, n, m):
+        c = np.asarray(codes, np.int8)
+        n_out, k = c.shape
+        rows = []
+        for row in c:
+            bits = []
+            run = []
+            for g in range(k // m):
+                grp = [int(v) for v in row[g * m:(g + 1) * m]]
+                mask = [1 if v != 0 else 0 for v in grp]
+                signs = [1 if v < 0 else 0 for v in grp if v != 0]
+                if mutant == "polarity":
+                    signs = [1 - s for s in signs]
+                elif mutant == "descending":
+                    signs = signs[::-1]
+                elif mutant == "msb_mask":
+                    mask = mask[::-1]
+                if mutant == "running_slots":  # sign slots shared by the whole row, not per group
+                    run += signs
+                    bits += mask + [0] * n
+                else:
+                    bits += mask + signs + [0] * (n - len(signs))
+            if mutant == "running_slots":
+                for g in range(k // m):
+                    for j in range(n):
+                        idx = g * n + j
+                        bits[g * (m + n) + m + j] = run[idx] if idx < len(run) else 0
+            bits += [0] * (-len(bits) % 8)
+            rows.append([sum(b << i for i, b in enumerate(bits[o:o + 8]))
+                         for o in range(0, len(bits), 8)])
+        return np.array(rows, np.uint8)
+
+    assert _compact_pins_fail(pack)
