@@ -112,6 +112,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
 
 /* Flags of sbn_pack_nm_ternary_ex. */
 #define SBN_PACK_VARIANCE_CORRECTION 1
+#define SBN_PACK_COMPACT 2
 
 /*
  * sbn_pack_nm_ternary with options. SBN_PACK_VARIANCE_CORRECTION ("From 2:4 to 8:16 sparsity
@@ -121,8 +122,15 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
  * nd the nonzero codes of the dense (n = m) ternary weights and ns those of the n:m codes
  * (gamma_out = gamma when ns == 0). The page gives no formula; this restores the mean square of
  * the ternary weights gamma * code, per tensor like gamma. sbn_bitlinear_fwd, the bf16 forwards,
- * sbn_bitlinear_bwd_dx and sbn_packed_export then use gamma_out. Each call may change the flags.
- * flags = 0 is sbn_pack_nm_ternary; other bits give SBN_ERR_INVALID_ARG.
+ * sbn_bitlinear_bwd_dx and sbn_packed_export then use gamma_out.
+ * SBN_PACK_COMPACT (inference encoding; "Why 1.58 Bits?" and "bitnet.cpp: Matrix-Free Inference"
+ * in "Microsoft BitNet 1.58": a ternary weight holds log2 3 bits, packed weights are unpacked on
+ * chip): the pack also writes a compact copy of the codes that keeps only which positions are
+ * nonzero and their signs, (m + n) / m bits per weight (1.5 at 2:4 and 8:16, 1.75 at 6:8, against
+ * 2 for the 2-bit codes), and every launch of the forwards with T <= 16 (the GEMV) reads it
+ * instead of the 2-bit codes. Results are identical; sbn_packed_export_compact exports it.
+ * Each call may change the flags. flags = 0 is sbn_pack_nm_ternary; other bits give
+ * SBN_ERR_INVALID_ARG.
  */
 sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
                                   int n_keep, int m_group, int flags, sbn_packed** handle /* host */,
@@ -213,6 +221,17 @@ sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8
                                  void* stream);
 
 /*
+ * Export of the compact form written by the last pack (which must have had SBN_PACK_COMPACT, else
+ * SBN_ERR_INVALID_ARG), enqueued on `stream`. Per row a bit stream, LSB first, padded to
+ * compact_row_bytes = ceil((K/m)(m + n)/8): group g (positions g*m .. g*m+m-1) at bits
+ * [g(m+n), (g+1)(m+n)); bit i < m is 1 when position g*m + i holds a nonzero code; bit m + j is 1
+ * when the group's j-th nonzero code, counting by ascending position, is -1 (slots past the
+ * group's nonzero count are 0).
+ *   bytes     [n_out][compact_row_bytes] uint8 out (device).
+ */
+sbn_status sbn_packed_export_compact(const sbn_packed* w, uint8_t* bytes, void* stream);
+
+/*
  * Keep-mask changes of the handle's last pack: the number of positions whose keep bit differs from
  * the pack before it (the first pack of a handle compares against an empty mask, so it counts
  * every kept position). flips / (n_out * K) is the mask flip rate r_t of Sparse-BitNet, Figure 3
@@ -229,6 +248,9 @@ typedef struct {
   size_t rpf_bytes;                      /* n_out * (code_row_bytes + mask_row_bytes) */
   size_t packed_bytes;                   /* bytes the forward kernels stream (kernel layout) */
   size_t device_bytes;                   /* all device memory the handle holds */
+  size_t compact_row_bytes;              /* compact export row size, ceil((K/m)(m+n)/8) */
+  size_t compact_bytes;                  /* bytes of the compact plane the GEMV streams */
+  int compact;                           /* the last pack wrote the compact form */
 } sbn_packed_desc;
 
 /* Describes a handle; `out` is a host pointer. */

@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sbn.h")
 SBN_OUT_F32 = 0
 SBN_OUT_I32_ACC = 1
 SBN_PACK_VARIANCE_CORRECTION = 1
+SBN_PACK_COMPACT = 2
 STATUS = {0: "SBN_OK", -1: "SBN_ERR_INVALID_ARG", -2: "SBN_ERR_UNSUPPORTED", -3: "SBN_ERR_SHAPE",
           -4: "SBN_ERR_HIP", -5: "SBN_ERR_OOM"}
 
@@ -32,7 +33,9 @@ class PackedDesc(ctypes.Structure):
     _fields_ = [("n_out", ctypes.c_int64), ("K", ctypes.c_int64), ("n", ctypes.c_int),
                 ("m", ctypes.c_int), ("code_row_bytes", ctypes.c_size_t),
                 ("mask_row_bytes", ctypes.c_size_t), ("rpf_bytes", ctypes.c_size_t),
-                ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t)]
+                ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t),
+                ("compact_row_bytes", ctypes.c_size_t), ("compact_bytes", ctypes.c_size_t),
+                ("compact", ctypes.c_int)]
 
 
 _lib = None
@@ -53,6 +56,7 @@ _SIGNATURES = {
     "sbn_free": (None, [_P]),
     "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
+    "sbn_packed_export_compact": (ctypes.c_int, [_P, _P, _P]),
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
     "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
     "sbn_bitlinear_bwd_dx": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
@@ -148,23 +152,29 @@ def layernorm_quantize_act(x, eps: float = 1e-5, out_q=None, out_absmax=None, st
 class PackedWeight:
     """A packed n:m ternary weight (library-owned device memory)."""
 
-    def __init__(self, w, n: int, m: int, stream=None, variance_correction: bool = False):
+    def __init__(self, w, n: int, m: int, stream=None, variance_correction: bool = False,
+                 compact: bool = False):
         self._h = ctypes.c_void_p(0)
         self.n, self.m = n, m
         self.variance_correction = variance_correction
+        self.compact = compact
         self.pack(w, stream)
 
-    def pack(self, w, stream=None, variance_correction=None):
+    def pack(self, w, stream=None, variance_correction=None, compact=None):
         """(Re-)packs from fp32 latent weights [n_out][K]; re-packing reuses the handle. With
-        variance_correction, the matmuls use the variance-corrected scale (sbn_pack_nm_ternary_ex)."""
+        variance_correction, the matmuls use the variance-corrected scale; with compact, the pack
+        also writes the compact form that the GEMV launches read (sbn_pack_nm_ternary_ex)."""
         if variance_correction is not None:
             self.variance_correction = variance_correction
+        if compact is not None:
+            self.compact = compact
         import torch
         _require_cuda(w, "w")
         if w.dtype != torch.float32:
             raise ValueError("w must be float32")
         n_out, K = w.shape
-        flags = SBN_PACK_VARIANCE_CORRECTION if self.variance_correction else 0
+        flags = ((SBN_PACK_VARIANCE_CORRECTION if self.variance_correction else 0) |
+                 (SBN_PACK_COMPACT if self.compact else 0))
         check(lib().sbn_pack_nm_ternary_ex(_ptr(w), n_out, K, _ld(w, K), self.n, self.m, flags,
                                            ctypes.byref(self._h), _stream(stream)))
         self.n_out, self.K = n_out, K
@@ -203,6 +213,15 @@ class PackedWeight:
                                           _ptr(mb) if d.mask_row_bytes else ctypes.c_void_p(0),
                                           _stream(stream)))
         return cb, mb
+
+    def export_compact(self, stream=None):
+        """The compact form's per-row bit streams (uint8 [n_out][compact_row_bytes], device)."""
+        import torch
+        d = self.query()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        out = torch.zeros((self.n_out, d.compact_row_bytes), dtype=torch.uint8, device=dev)
+        check(lib().sbn_packed_export_compact(self.handle, _ptr(out), _stream(stream)))
+        return out
 
     def mask_flips(self, stream=None):
         """Keep bits changed by the last pack (int64 tensor [1] on the device)."""

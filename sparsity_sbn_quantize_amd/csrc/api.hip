@@ -118,7 +118,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
 sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
                                   int n_keep, int m_group, int flags, sbn_packed** handle,
                                   void* stream) {
-  if ((flags & ~SBN_PACK_VARIANCE_CORRECTION) != 0)
+  if ((flags & ~(SBN_PACK_VARIANCE_CORRECTION | SBN_PACK_COMPACT)) != 0)
     return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: unknown flags 0x%x", flags);
   if (!handle) return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: handle is null");
   if (!pattern_ok(n_keep, m_group))
@@ -163,6 +163,7 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
     L.row_blocks_pad = (L.row_blocks + sbn::kPadRowBlocks - 1) / sbn::kPadRowBlocks *
                        sbn::kPadRowBlocks;
     L.quads = ((K + sbn::kBrickK - 1) / sbn::kBrickK + 3) / 4;
+    L.csb = sbn::kBrickK * n_keep / m_group;
     if (16 * n_keep % m_group != 0)
       return fail(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: pattern %d:%d", n_keep, m_group);
     const size_t slots = (size_t)L.row_blocks_pad * (size_t)L.quads * 64;
@@ -189,6 +190,11 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
     const int64_t rq_count = (n_out + 127) / 128;
     const size_t off_tplane = off;
     off = align_up(off + (size_t)rq_count * (size_t)L.quads * 8192, 256);
+    const size_t cplane_bytes =
+        (size_t)L.row_blocks_pad * (size_t)L.quads * (size_t)sbn::compact_quad_bytes(L.csb) +
+        sbn::kCompactSlack;
+    const size_t off_cplane = off;
+    off = align_up(off + cplane_bytes, 256);
 
     h = new (std::nothrow) sbn_packed;
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
@@ -229,11 +235,16 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
     h->vc = false;
     h->tplane = reinterpret_cast<uint32_t*>(h->base + off_tplane);
     h->rq_count = rq_count;
+    h->cplane = h->base + off_cplane;
+    h->cplane_bytes = cplane_bytes;
+    h->compact_row_bytes = (size_t)(((K / m_group) * (m_group + n_keep) + 7) / 8);
+    h->compact = false;
     *handle = h;
   }
   h->last_stream = s;
   h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
   h->vc = (flags & SBN_PACK_VARIANCE_CORRECTION) != 0;
+  h->compact = (flags & SBN_PACK_COMPACT) != 0;
   hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
   if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
   return SBN_OK;
@@ -342,6 +353,19 @@ sbn_status sbn_packed_mask_flips(const sbn_packed* w, uint64_t* flips, void* str
   return SBN_OK;
 }
 
+sbn_status sbn_packed_export_compact(const sbn_packed* w, uint8_t* bytes, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_compact: handle is null");
+  if (!w->compact)
+    return fail(SBN_ERR_INVALID_ARG,
+                "sbn_packed_export_compact: the last pack did not write the compact form "
+                "(SBN_PACK_COMPACT)");
+  if (!bytes && w->L.n_out > 0)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_compact: bytes is null");
+  hipError_t e = sbn::launch_export_compact(w, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_export_compact launch");
+  return SBN_OK;
+}
+
 sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   if (!w || !out) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_query: null pointer");
   out->n_out = w->L.n_out;
@@ -354,6 +378,9 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   out->packed_bytes = w->L.positional ? w->code_plane_bytes
                                       : w->mask_plane_bytes + w->code_plane_bytes;
   out->device_bytes = w->base_bytes;
+  out->compact_row_bytes = w->compact_row_bytes;
+  out->compact_bytes = w->cplane_bytes - sbn::kCompactSlack;
+  out->compact = w->compact ? 1 : 0;
   return SBN_OK;
 }
 

@@ -156,8 +156,13 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
   __shared__ double lndev[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
   __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
+  constexpr bool CMP = compact_form(FORM);
+  __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
   const int W = (int)(blockDim.x >> 6);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform; readfirstlane lets it feed the buffer loads' scalar offsets
+  // directly (otherwise each load sits in a loop over the lanes' distinct offsets)
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int64_t rb = blockIdx.x;
   const int t = lane & 15, g = lane >> 4;
   const bool tok_ok = t < (int)T;
@@ -167,15 +172,27 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   // With FUSED or XBUF, positional and structured-sparse bricks come through a buffer resource
   // over this row block's quads: a quad past the last reads as zero, so the loads are
   // straight-line code and the compiler's wait counts stay exact (a wait for the activations then
-  // does not wait for the bricks behind them).
+  // does not wait for the bricks behind them). The compact plane always comes this way: a quad
+  // takes cq = 512 + 8 csb bytes, and the range ends kCompactSlack bytes past the row block's
+  // last quad (the plane has that slack), which covers every lane's three-word sign load.
+  const int cq = CMP ? (int)compact_quad_bytes(L.csb) : 1024;
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(code_plane + ((rb * nq) << 6) * 16), (short)0, FORM != kFormKept ? nq * 1024 : 0,
-      kBufDword3);
+      (void*)(code_plane + rb * nq * cq), (short)0,
+      CMP ? nq * cq + kCompactSlack : (FORM != kFormKept ? nq * 1024 : 0), kBufDword3);
   auto load_bricks = [&]() {
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
       const int q = wave + i * W;
-      if constexpr (FORM != kFormKept && (FUSED || XBUF)) {
+      if constexpr (CMP) {
+        // the lane's nonzero mask, and the three words holding its csb sign bits
+        const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, q * cq, 0);
+        const int sbit = lane * L.csb;
+        const v3u sg = __builtin_amdgcn_raw_buffer_load_b96(
+            crs, kCompactMaskBytes + 4 * (sbit >> 5), q * cq, 0);
+        mask[i][0] = mk[0]; mask[i][1] = mk[1];
+        codes[i][0] = sg[0]; codes[i][1] = sg[1]; codes[i][2] = sg[2];
+        codes[i][3] = (uint32_t)(sbit & 31);
+      } else if constexpr (FORM != kFormKept && (FUSED || XBUF)) {
         const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, q * 1024, 0);
         codes[i][0] = (uint32_t)c[0]; codes[i][1] = (uint32_t)c[1];
         codes[i][2] = (uint32_t)c[2]; codes[i][3] = (uint32_t)c[3];
@@ -190,9 +207,17 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     }
   };
   v4i b[Q][4];  // B operands: 16 int8 activations per K slice
-  float a_t = 0.0f;     // a' of token t (FUSED)
+  float a_t = 0.0f;     // a' of token t (FUSED, else loaded with the operands)
+  // The scales are loaded up front, so the epilogue waits for no memory
+  const float gamma = gamma_p[0];
+  auto build_lut = [&]() {
+    if constexpr (CMP) {
+      for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
+    }
+  };
   if constexpr (!FUSED) {
     load_bricks();
+    build_lut();
     if constexpr (XVEC && XBUF) {
       // One buffer resource over the T activation rows, straight-line loads: the lanes of a
       // missing token take an offset past the range and read zero, as does the K tail of the last
@@ -219,6 +244,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
           if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
         }
     }
+    if (out_kind == SBN_OUT_F32 && tok_ok) a_t = absmax[t];
+    if constexpr (CMP) __syncthreads();  // the nibble table
   } else {
     // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
     // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
@@ -246,6 +273,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
     // does not wait for the bricks: the quantization below overlaps the brick loads.
     load_bricks();
+    build_lut();  // published by the barrier of the absmax reduction below
     const int Tn = (int)T;  // <= kFusedMaxT; loops below stop at the real token count
     if constexpr (LN) {
       // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
@@ -405,7 +433,14 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
         }
       } else {
         uint32_t a[16];
-        decode<FORM>(L, mask[i], codes[i], a);
+        if constexpr (CMP) {
+          const uint32_t sh = codes[i][3];
+          decode_compact<compact_m(FORM)>(mask[i], __builtin_amdgcn_alignbit(codes[i][1], codes[i][0], sh),
+                                          __builtin_amdgcn_alignbit(codes[i][2], codes[i][1], sh),
+                                          L.n, L.csb, clut, a);
+        } else {
+          decode<FORM>(L, mask[i], codes[i], a);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
       }
@@ -416,8 +451,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   if (wave != 0 || !tok_ok) return;
   v4i sum = red[0][lane];
   for (int w = 1; w < W; ++w) sum += red[w][lane];
-  const float gamma = gamma_p[0];
-  const float step = out_kind == SBN_OUT_F32 ? (FUSED ? a_t : absmax[t]) / 127.0f : 0.0f;
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = rb * 16 + 4 * g + i;
@@ -818,7 +852,8 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   const int Q = (int)((L.quads + W - 1) / W);
 #define SBN_GEMV(QQ, LNV, XB)                                                                 \
   hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ, LNV, XB>),                           \
-                     dim3((unsigned)L.row_blocks), dim3(64 * W), 0, s, h->mask, h->codes, L,     \
+                     dim3((unsigned)L.row_blocks), dim3(64 * W), 0, s, h->mask,                  \
+                     compact_form(FORM) ? h->cplane : h->codes, L,                                 \
                      h->gamma_out(), x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
 #define SBN_GEMV_Q(QQ)                                                                        \
   if (FUSED) {                                                                                \
@@ -838,12 +873,30 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   return hipGetLastError();
 }
 
+// The GEMV on the compact plane, by group size.
+template <bool FUSED, bool XVEC>
+hipError_t launch_gemv_compact(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
+                               int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
+                               int out_kind, float ln_eps, hipStream_t s) {
+  if (h->L.m == 4)
+    return launch_gemv<kFormCompact4, FUSED, XVEC>(h, x, ld_x, xq_out, ld_q, absmax, T, y, ld_y,
+                                                   out_kind, ln_eps, s);
+  if (h->L.m == 8)
+    return launch_gemv<kFormCompact8, FUSED, XVEC>(h, x, ld_x, xq_out, ld_q, absmax, T, y, ld_y,
+                                                   out_kind, ln_eps, s);
+  return launch_gemv<kFormCompact16, FUSED, XVEC>(h, x, ld_x, xq_out, ld_q, absmax, T, y, ld_y,
+                                                  out_kind, ln_eps, s);
+}
+
 template <int FORM, bool XVEC>
 hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
   const Layout& L = h->L;
   if (T <= 16 && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
+    if (h->compact)
+      return launch_gemv_compact<false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax),
+                                              T, y, ld_y, out_kind, 0.0f, s);
     return launch_gemv<FORM, false, XVEC>(h, xq, ld_q, nullptr, 0, const_cast<float*>(absmax), T,
                                          y, ld_y, out_kind, 0.0f, s);
   }
@@ -891,6 +944,12 @@ hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t
                                             ln_eps, s)                                         \
               : launch_gemv_fused<FF, false>(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind, \
                                              ln_eps, s)
+    if (h->compact) {
+      return xvec ? launch_gemv_compact<true, true>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y,
+                                                    out_kind, ln_eps, s)
+                  : launch_gemv_compact<true, false>(h, x, ld_x, xq, ld_q, absmax, T, y, ld_y,
+                                                     out_kind, ln_eps, s);
+    }
     if (L.form == kFormSparse24) SBN_FUSED(kFormSparse24);
     if (L.form == kFormPositional) SBN_FUSED(kFormPositional);
     SBN_FUSED(kFormKept);

@@ -395,6 +395,93 @@ __global__ __launch_bounds__(256) void export_rpf(Layout L, const uint8_t* mask_
 }
 
 __global__ void copy_gamma(const float* src, float* dst) { dst[0] = src[0]; }
+
+// Compact plane from the code planes: one wave per fragment quad (rb * quads + q); lane l encodes
+// brick 4q + l / 16 of row 16 rb + l % 16: its nonzero mask, and its signs into the slots of
+// their groups. The lanes' sign bits are merged into the quad's bit stream in LDS (a lane's csb
+// <= 64 bits span at most three words) and written out by the whole wave. Rows past n_out and
+// bricks past K encode as zero.
+__global__ __launch_bounds__(256) void build_compact(Layout L, const uint8_t* mask_plane,
+                                                     const uint8_t* code_plane, int64_t nfq,
+                                                     uint8_t* __restrict__ cplane) {
+  __shared__ uint32_t sb[4][130];  // 2 * 64 words of signs, +2 for the last lane's spill
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t fq = (int64_t)blockIdx.x * 4 + wave;
+  const int S = L.csb;
+  for (int i = lane; i < 130; i += 64) sb[wave][i] = 0u;
+  __syncthreads();
+  uint32_t nzm[2] = {0u, 0u};
+  if (fq < nfq) {
+    const int64_t row = (fq / L.quads) * 16 + (lane & 15);
+    const int64_t brick = (fq % L.quads) * kFragBricks + (lane >> 4);
+    unsigned long long sg = 0ull;
+    if (row < L.n_out) {
+      uint32_t mask[2], dec[16];
+      decode_brick(L, mask_plane, code_plane, row, brick, mask, dec);
+      int j = 0;  // nonzero codes seen so far in the current group
+      for (int p = 0; p < kBrickK; ++p) {
+        if (p % L.m == 0) j = 0;
+        const uint32_t v = (dec[p >> 2] >> (8 * (p & 3))) & 0xFFu;
+        if (v != 0u) {
+          nzm[p >> 5] |= 1u << (p & 31);
+          if (v == 0xFFu) sg |= 1ull << ((p / L.m) * L.n + j);
+          ++j;
+        }
+      }
+    }
+    const int bit = lane * S;
+    const int d = bit >> 5, sh = bit & 31;
+    const uint32_t lo = (uint32_t)sg, hi = (uint32_t)(sg >> 32);
+    const uint32_t w0 = lo << sh;
+    const uint32_t w1 = sh ? ((hi << sh) | (lo >> (32 - sh))) : hi;
+    const uint32_t w2 = sh ? (hi >> (32 - sh)) : 0u;
+    if (w0) atomicOr(&sb[wave][d], w0);
+    if (w1) atomicOr(&sb[wave][d + 1], w1);
+    if (w2) atomicOr(&sb[wave][d + 2], w2);
+  }
+  __syncthreads();
+  if (fq < nfq) {
+    uint8_t* dst = cplane + fq * compact_quad_bytes(S);
+    reinterpret_cast<uint2*>(dst)[lane] = make_uint2(nzm[0], nzm[1]);
+    uint32_t* sd = reinterpret_cast<uint32_t*>(dst + kCompactMaskBytes);
+    for (int i = lane; i < 2 * S; i += 64) sd[i] = sb[wave][i];
+  }
+}
+
+// Export of the compact plane as per-row bit streams: group g at bits [g (m + n), (g+1) (m + n)),
+// its m nonzero-mask bits first, then its n sign slots; LSB first, rows padded to a byte. One
+// thread per output byte, each bit read from the plane.
+__global__ __launch_bounds__(256) void export_compact(Layout L, const uint8_t* cplane, int64_t crb,
+                                                      uint8_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= L.n_out * crb) return;
+  const int64_t row = idx / crb, byte = idx % crb;
+  const int gbits = L.m + L.n;
+  const int64_t total = (L.K / L.m) * gbits;
+  const int S = L.csb;
+  uint32_t v = 0u;
+  for (int t = 0; t < 8; ++t) {
+    const int64_t B = byte * 8 + t;
+    if (B >= total) break;
+    const int64_t g = B / gbits;
+    const int p = (int)(B % gbits);
+    const int64_t pos0 = g * L.m, brick = pos0 >> 6;
+    const int lane = (int)((row & 15) | ((brick & 3) << 4));
+    const uint32_t* frag = reinterpret_cast<const uint32_t*>(
+        cplane + ((row >> 4) * L.quads + (brick >> 2)) * compact_quad_bytes(S));
+    uint32_t bv;
+    if (p < L.m) {
+      const int pb = (int)(pos0 & 63) + p;
+      bv = (frag[2 * lane + (pb >> 5)] >> (pb & 31)) & 1u;
+    } else {
+      const int gl = (int)((pos0 & 63) / L.m);
+      const int64_t sbit = (int64_t)lane * S + gl * L.n + (p - L.m);
+      bv = (frag[kCompactMaskBytes / 4 + (sbit >> 5)] >> (sbit & 31)) & 1u;
+    }
+    v |= bv << t;
+  }
+  out[row * crb + byte] = (uint8_t)v;
+}
 // Transposed code plane, read by the data-gradient matmul, whose reduction runs over the rows:
 // for every 16 columns cb and 128 rows rq, 64 lanes x 8 bytes at slot (cb * rq_count + rq) * 64
 // + lane. Lane l = c + 16 g holds column 16 cb + c of rows 128 rq + 32 g + (0..31); its word h
@@ -526,6 +613,11 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
     if (L.positional) SBN_PACK(16, kFormPositional); else SBN_PACK(16, kFormKept);
   }
 #undef SBN_PACK
+  if (h->compact) {
+    const int64_t nfq = L.row_blocks_pad * L.quads;
+    hipLaunchKernelGGL(build_compact, dim3((unsigned)((nfq + 3) / 4)), dim3(256), 0, s, L, h->mask,
+                       h->codes, nfq, h->cplane);
+  }
   if (h->vc) {
     hipLaunchKernelGGL(vc_finalize, dim3(1), dim3(1024), 0, s, h->vc_parts,
                        L.row_blocks_pad * L.quads * 4, h->gamma, h->gamma_vc);
@@ -562,6 +654,15 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 }  // namespace sbn
 
 namespace sbn {
+hipError_t launch_export_compact(const sbn_packed* h, uint8_t* out, hipStream_t s) {
+  const Layout& L = h->L;
+  const int64_t total = L.n_out * (int64_t)h->compact_row_bytes;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(export_compact, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, L,
+                     h->cplane, (int64_t)h->compact_row_bytes, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s) {
   const Layout& L = h->L;
   if (h->rq_count == 0) return hipSuccess;

@@ -28,6 +28,15 @@
 //   - kept (2n < m): the n kept codes of each group in ascending position, 2-bit two's complement
 //     (00 = 0, 01 = +1, 11 = -1), code i of the brick at bits [2i, 2i+2): exactly the reference
 //     bitstream, 16n/m bytes per brick. Decoded with decode_kept_brick.
+//
+// Compact plane (inference only; written next to the planes above when a pack asks for it and
+// read by the GEMV). A product needs only which positions are nonzero and their signs, so per
+// brick it holds a 64-bit nonzero mask (bit i <-> position i) and csb = 64n/m sign bits: group g
+// of the brick owns slots [g*n, g*n + n), slot g*n + j is 1 when the group's j-th nonzero code in
+// ascending position is -1, and unused slots are 0. A fragment quad stores its 64 lanes' masks (8
+// bytes each, lane order) and then the lanes' sign bits as one bit stream (lane l at stream bits
+// [l*csb, (l+1)*csb), little-endian words): 512 + 8*csb bytes per quad, (m + n)/m bits per weight
+// (1.5 at 2:4 and 8:16, 1.75 at 6:8).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,7 +49,25 @@ constexpr int kFragRows = 16;       // rows per fragment
 constexpr int kFragBricks = 4;      // bricks per fragment (along K)
 constexpr int kQuadK = kBrickK * kFragBricks;  // 256 K positions per fragment
 
-enum CodeForm : int { kFormPositional = 0, kFormKept = 1, kFormSparse24 = 2 };
+enum CodeForm : int {
+  kFormPositional = 0,
+  kFormKept = 1,
+  kFormSparse24 = 2,
+  // compact plane, by group size (kernel template forms only; Layout::form never holds these)
+  kFormCompact4 = 3,
+  kFormCompact8 = 4,
+  kFormCompact16 = 5
+};
+
+__host__ __device__ constexpr bool compact_form(int f) { return f >= kFormCompact4; }
+__host__ __device__ constexpr int compact_m(int f) {
+  return f == kFormCompact4 ? 4 : (f == kFormCompact8 ? 8 : 16);
+}
+constexpr int kCompactMaskBytes = 64 * 8;  // nonzero masks of one fragment quad
+constexpr int kCompactSlack = 16;          // zero bytes after the plane (3-word sign loads)
+__host__ __device__ constexpr int64_t compact_quad_bytes(int csb) {
+  return kCompactMaskBytes + 8 * (int64_t)csb;
+}
 
 struct Layout {
   int64_t n_out, K;
@@ -52,6 +79,7 @@ struct Layout {
   int64_t row_blocks;    // ceil(n_out / 16)
   int64_t row_blocks_pad;  // row_blocks rounded up to kPadRowBlocks (stored, zero-filled)
   int64_t quads;         // ceil(ceil(K / 64) / 4)
+  int csb;               // compact plane: sign bits per brick, 64 n / m
 };
 
 // Stored row fragments are padded with zero bricks to a multiple of 16 (256 rows), so that a GEMM
@@ -120,6 +148,49 @@ __device__ inline void decode_kept_brick(const uint32_t mask[2], const uint32_t 
       }
       const int d = pos >> 2, s = (pos & 3) * 8;
       out[d] = (out[d] & ~(0xFFu << s)) | (b << s);
+    }
+  }
+}
+
+// Compact nibble table: entry m4 | s << 4 holds the int8 codes of four positions whose nonzero
+// bits are m4, the nonzero ones taking their signs from the low bits of s in order (1 = -1).
+__host__ __device__ inline uint32_t compact_nibble_entry(uint32_t e) {
+  const uint32_t m4 = e & 15u, s = e >> 4;
+  uint32_t out = 0, k = 0;
+  for (int i = 0; i < 4; ++i) {
+    if ((m4 >> i) & 1u) {
+      out |= (((s >> k) & 1u) ? 0xFFu : 0x01u) << (8 * i);
+      ++k;
+    }
+  }
+  return out;
+}
+
+// Decodes one compact brick into 16 words of int8 codes (word d = positions 4d .. 4d+3).
+// mask: the brick's nonzero mask; sg_lo, sg_hi: its sign slots 0..63; n, csb: the pattern's n and
+// 64 n / m; lut: the 256-entry nibble table. Half h of the brick (positions 32h .. 32h+31) holds
+// whole groups whose slots are [h csb/2, (h+1) csb/2), at most 32 bits, so each half reads one
+// 32-bit window. Nibble j starts at slot off = its group's first slot plus the nonzero positions
+// before it in the group; off never passes the window's end except for a nibble with no nonzero
+// position (its group's slots are used up), whose table row is all zero for any s.
+template <int M>
+__device__ __forceinline__ void decode_compact(const uint32_t mask[2], uint32_t sg_lo,
+                                               uint32_t sg_hi, int n, int csb,
+                                               const uint32_t* lut, uint32_t out[16]) {
+  const int half_bits = csb >> 1;
+  const uint32_t w1 =
+      half_bits >= 32 ? sg_hi : __builtin_amdgcn_alignbit(sg_hi, sg_lo, (uint32_t)half_bits);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t mw = mask[h], sw = h ? w1 : sg_lo;
+    uint32_t off = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j % (M / 4) == 0) off = (uint32_t)((4 * j / M) * n);
+      const uint32_t m4 = (mw >> (4 * j)) & 15u;
+      const uint32_t s4 = __builtin_amdgcn_ubfe(sw, off, 4u);
+      out[8 * h + j] = lut[m4 | (s4 << 4)];
+      off += (uint32_t)__builtin_popcount(m4);
     }
   }
 }
@@ -252,6 +323,7 @@ __device__ __forceinline__ uint32_t ln_pair(uint32_t w, float mu, float r) {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, no stride): offsets are

@@ -30,6 +30,10 @@ struct sbn_packed {
   uint32_t* tplane;     // transposed code plane (data-gradient matmul), 2 bits per weight
   int64_t rq_count;     // 128-row groups of the transposed plane
   bool tplane_valid;    // the transposed plane matches the last pack (host-side state)
+  uint8_t* cplane;      // compact plane (nonzero masks + sign slots), read by the GEMV
+  size_t cplane_bytes;  // its size, the slack included
+  size_t compact_row_bytes;  // per-row bytes of the compact export stream
+  bool compact;         // the last pack wrote the compact plane (host-side state)
   int device;
   hipStream_t last_stream;
   // Scale the matmuls multiply by: gamma, or the variance-corrected gamma.
@@ -58,6 +62,7 @@ hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
+hipError_t launch_export_compact(const sbn_packed* h, uint8_t* out, hipStream_t s);
 hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
 hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s);
 hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,

@@ -22,7 +22,8 @@ def test_exports_match_header(lib):
                              "sbn_pack_nm_ternary", "sbn_pack_nm_ternary_ex", "sbn_bitlinear_fwd",
                              "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_fwd_ln_bf16",
                              "sbn_bitlinear_bwd_dx", "sbn_free",
-                             "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_query",
+                             "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_export_compact",
+                             "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -82,8 +83,9 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_export_rpf(None, None, None, None) == ERR_INVALID
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
+    assert lib.sbn_packed_export_compact(None, None, None) == ERR_INVALID
     h = ctypes.c_void_p(0)
-    for flags in (2, -1, 1 << 30):  # unknown flag bits are rejected before any device work
+    for flags in (4, -1, 1 << 30):  # unknown flag bits are rejected before any device work
         assert lib.sbn_pack_nm_ternary_ex(None, 16, 64, 64, 2, 4, flags, ctypes.byref(h),
                                           None) == ERR_INVALID
     assert lib.sbn_pack_nm_ternary_ex(None, 16, 64, 64, 2, 4, 1, None, None) == ERR_INVALID
