@@ -140,11 +140,14 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
   }
 }
 
-// LN (bf16 input only): parameter-free LayerNorm before the quantization. XBUF (int8 input
-// only): brick and activation loads through buffer resources, straight-line; measured faster for
-// a few tokens (4.35 vs 4.58 us at T = 1 on the 2560 -> 6912 decode shape) and slower for 16
-// (6.35 vs 6.05 us), so the launcher picks it for T <= 4. The bf16-input kernel loads its bricks
-// through the buffer resource too (4.95 vs 5.06 us per one-kernel step at T = 1).
+// LN (bf16 input only): parameter-free LayerNorm before the quantization. XBUF, int8 input: brick
+// and activation loads through buffer resources, straight-line; measured faster for a few tokens
+// (4.35 vs 4.58 us at T = 1 on the 2560 -> 6912 decode shape) and slower for 16 (6.35 vs 6.05 us),
+// so the launcher picks it for T <= 4. The bf16-input kernel loads its bricks through the buffer
+// resource too (4.95 vs 5.06 us per one-kernel step at T = 1). XBUF, bf16 input (T = 1, no
+// LayerNorm): the row comes through a buffer resource and the token count is a compile-time 1.
+// (Every wave taking the absmax over the whole row itself, with no barrier, was measured slower:
+// 6.3 vs 4.8 us, the 4320 waves' requests for the same few KB queue at a few L2 channels.)
 template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
     void* __restrict__ y, int64_t ld_y, int out_kind, float ln_eps) {
   __shared__ v4i red[kGemvMaxWaves][64];
-  __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT];
+  __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT / 2];  // token pairs, 16 bits each
   __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
   __shared__ double lndev[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
   __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
@@ -251,6 +254,11 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
     // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
+    // XBUF runs one token; the constant lets the compiler drop the other tokens' code
+    const int Tn = XBUF ? 1 : (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+    // One resource over the row (XBUF): loads are straight-line, positions past K read zero.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(xin), (short)0, XBUF ? K * 2 : 0, kBufDword3);
     uint2 xv[Q][kFusedMaxT];
 #pragma unroll
     for (int i = 0; i < Q; ++i)
@@ -258,7 +266,12 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
       for (int tt = 0; tt < kFusedMaxT; ++tt) {
         const int k = (wave + i * W) * kQuadK + 4 * lane;
         uint2 v = make_uint2(0, 0);
-        if (tt < (int)T && k < K) {
+        if constexpr (XBUF) {
+          if (tt == 0) {
+            const v2u r = __builtin_amdgcn_raw_buffer_load_b64(xr, k < K ? 2 * k : (1 << 30), 0, 0);
+            v = make_uint2(r[0], r[1]);
+          }
+        } else if (tt < Tn && k < K) {
           const uint16_t* row = xb + tt * ld_x;
           if constexpr (XVEC) {
             v = *reinterpret_cast<const uint2*>(row + k);
@@ -271,14 +284,16 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
         xv[i][tt] = v;
       }
     // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
-    // does not wait for the bricks: the quantization below overlaps the brick loads.
+    // does not wait for the bricks: the quantization below overlaps the brick loads. The
+    // scheduling barrier keeps the compiler from issuing the bricks first.
+    __builtin_amdgcn_sched_barrier(0);
     load_bricks();
-    build_lut();  // published by the barrier of the absmax reduction below
-    const int Tn = (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+    build_lut();  // published by a barrier below
     if constexpr (LN) {
       // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
-      // and sum of squared deviations over the wave (DPP) and then the waves (LDS, fixed order);
-      // the lane's elements are replaced by their bf16 normalized values.
+      // and sum of squared deviations over the wave (DPP), then over the waves (one LDS read per
+      // lane and a 16-lane DPP tree, a fixed order); the lane's elements are replaced by their
+      // bf16 normalized values.
       double ps[kFusedMaxT], pd[kFusedMaxT];
       float mu32[kFusedMaxT], r32[kFusedMaxT];
 #pragma unroll
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
         pd[tt] = 0.0;
         ps[tt] = 0.0;
         if (tt >= Tn) continue;
-        for (int w = 0; w < W; ++w) ps[tt] += lnsum[w][tt];
+        ps[tt] = row16_sum_f64(lane < W ? lnsum[lane][tt] : 0.0);
         ps[tt] /= (double)K;  // the mean
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
@@ -331,8 +346,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
         mu32[tt] = 0.0f;
         r32[tt] = 0.0f;
         if (tt >= Tn) continue;
-        double d = 0.0;
-        for (int w = 0; w < W; ++w) d += lndev[w][tt];
+        const double d = row16_sum_f64(lane < W ? lndev[lane][tt] : 0.0);
         mu32[tt] = (float)ps[tt];
         r32[tt] = (float)(1.0 / sqrt(d / (double)K + (double)ln_eps));
       }
@@ -364,7 +378,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
                                                          xv[i][tt].y);
     }
     // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
-    // over the waves through LDS.
+    // over the waves through LDS (one read per lane and a 16-lane DPP tree).
     uint32_t pk[kFusedMaxT / 2];
 #pragma unroll
     for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) {
@@ -376,17 +390,19 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     }
     if (lane == 0) {
 #pragma unroll
-      for (int tt = 0; tt < kFusedMaxT; ++tt)
-        wmax[wave][tt] = (pk[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
+      for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) wmax[wave][p2] = pk[p2];
     }
     __syncthreads();
+    uint32_t am2[kFusedMaxT / 2];
+#pragma unroll
+    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2)
+      am2[p2] = 2 * p2 < Tn ? row16_max_u16x2(lane < W ? wmax[lane][p2] : 0u) : 0u;
     float s_t[kFusedMaxT];
 #pragma unroll
     for (int tt = 0; tt < kFusedMaxT; ++tt) {
       s_t[tt] = 0.0f;
       if (tt >= Tn) continue;
-      uint32_t am = 0;
-      for (int w = 0; w < W; ++w) am = max(am, wmax[w][tt]);
+      const uint32_t am = (am2[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
       const float a = fmaxf(__uint_as_float(am << 16), kAbsmaxFloor);
       s_t[tt] = 127.0f / a;
       if (tt == t) a_t = a;
@@ -446,16 +462,32 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
       }
     }
   }
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0 || !tok_ok) return;
+  // (A fully unrolled sum over all 16 slots, masked, measured slower than this loop.)
   v4i sum = red[0][lane];
   for (int w = 1; w < W; ++w) sum += red[w][lane];
-  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
+  const int64_t row0 = rb * 16 + 4 * g;
+  const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < L.n_out;
+  if (vec) {  // the lane's four consecutive rows in one store
+    if (out_kind == SBN_OUT_I32_ACC) {
+      *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + row0) = sum;
+    } else {
+      float4 f;
+      f.x = __fmul_rn(__fmul_rn((float)sum[0], gamma), step);
+      f.y = __fmul_rn(__fmul_rn((float)sum[1], gamma), step);
+      f.z = __fmul_rn(__fmul_rn((float)sum[2], gamma), step);
+      f.w = __fmul_rn(__fmul_rn((float)sum[3], gamma), step);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + row0) = f;
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = rb * 16 + 4 * g + i;
-    if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + i;
+      if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+    }
   }
 }
 
@@ -857,7 +889,9 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
                      h->gamma_out(), x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
 #define SBN_GEMV_Q(QQ)                                                                        \
   if (FUSED) {                                                                                \
-    if (ln_eps > 0.0f) SBN_GEMV(QQ, FUSED, false); else SBN_GEMV(QQ, false, false);          \
+    if (ln_eps > 0.0f) SBN_GEMV(QQ, FUSED, false);                                            \
+    else if (XVEC && T == 1) SBN_GEMV(QQ, false, FUSED);                                      \
+    else SBN_GEMV(QQ, false, false);                                                          \
   } else {                                                                                    \
     if (T <= kFusedMaxT) SBN_GEMV(QQ, false, !FUSED); else SBN_GEMV(QQ, false, false);        \
   }

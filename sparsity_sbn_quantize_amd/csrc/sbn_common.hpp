@@ -307,6 +307,28 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// Combining one value per wave of a workgroup (at most 16 waves): lane w holds wave w's value
+// (0 for lanes past the last wave), and four DPP steps inside the first row of 16 lanes (two quad
+// permutations, then the half-row and row mirrors) leave the result in every lane of that row;
+// lane 0's copy is returned. One LDS read and a few ALU steps, instead of a read per wave.
+__device__ __forceinline__ uint32_t row16_max_u16x2(uint32_t v) {
+  v = max_abs_bf16x2(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max_abs_bf16x2(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max_abs_bf16x2(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = max_abs_bf16x2(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+}
+__device__ __forceinline__ double row16_sum_f64(double v) {
+  v += dpp_f64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f64<0x140, 0xF>(v);  // row_mirror
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 0);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 0);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 // Round an fp32 value to a bf16 bit pattern, nearest even (finite values).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
