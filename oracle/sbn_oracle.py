@@ -48,7 +48,9 @@ Readings taken where the pages are silent or disagree (each is also listed in th
   * the mask flip rate r_t counts positions whose keep bit differs between consecutive masks,
     divided by the number of weights; a first mask is compared with one that keeps nothing;
   * the compact inference encoding keeps, per group, a nonzero mask (m bits) and n sign slots
-    for the nonzero codes in ascending position (1 = -1), m + n bits per group, LSB first.
+    for the nonzero codes in ascending position (1 = -1), m + n bits per group, LSB first;
+  * structured outliers (optional): the k largest |w| of each 256-group along K are kept apart
+    as bf16 values; scale, selection and codes use the other weights (outlier positions as 0).
 
 Floating point follows the precision the path decides integers in (fp32 scale and product); the
 weight-scale sum is accumulated in fp64.
@@ -298,6 +300,74 @@ def variance_correction(w: np.ndarray, n: int, m: int) -> dict:
     else:
         gamma_out = np.float32(np.float64(gamma) * np.sqrt(np.float64(nd) / np.float64(ns)))
     return {"gamma": gamma, "nd": nd, "ns": ns, "gamma_out": gamma_out}
+
+
+# ----------------------------------------------------------------------------------------------
+# Structured outliers: [8:16] summary ("Summary", "Key points": salient weights kept in structured
+# 4:256, 8:256 or 16:256 patterns, about 1.5%, 3.1% and 6.25% of the weights). Reading: in each
+# group of 256 consecutive weights along K, the k of largest |w| (equal magnitudes: lower position
+# first) are kept apart as bf16 values; the ternary n:m path then sees the other weights only
+# (outlier positions read as 0 for the scale, the selection and the codes).
+# ----------------------------------------------------------------------------------------------
+
+OUTLIER_GROUP = 256
+
+
+def outlier_select(w: np.ndarray, k: int):
+    """(pos uint8 [n_out][K/256][k] ascending, val uint16 bf16 bits [n_out][K/256][k],
+    mask bool [n_out][K]) of the k largest |w| in each group of 256 along K."""
+    w = np.asarray(w, dtype=np.float32)
+    n_out, K = w.shape
+    if K % OUTLIER_GROUP != 0 or k not in (4, 8, 16):
+        raise ValueError("outliers need K % 256 == 0 and k in {4, 8, 16}")
+    groups = K // OUTLIER_GROUP
+    mag = np.abs(w).reshape(n_out, groups, OUTLIER_GROUP)
+    order = np.argsort(-mag, axis=2, kind="stable")  # equal magnitudes: ascending position
+    pos = np.sort(order[:, :, :k], axis=2)
+    vals = np.take_along_axis(w.reshape(n_out, groups, OUTLIER_GROUP), pos, axis=2)
+    mask = np.zeros((n_out, groups, OUTLIER_GROUP), dtype=bool)
+    np.put_along_axis(mask, pos, True, axis=2)
+    return (pos.astype(np.uint8), f32_to_bf16_rne(vals).astype(np.uint16),
+            mask.reshape(n_out, K))
+
+
+def pack_with_outliers(w: np.ndarray, n: int, m: int, k: int) -> dict:
+    """Outliers apart, then absmean / keep mask / codes of the remaining weights w' (w with the
+    outlier positions set to 0)."""
+    w = np.asarray(w, dtype=np.float32)
+    pos, val, omask = outlier_select(w, k)
+    w_rest = np.where(omask, np.float32(0.0), w).astype(np.float32)
+    gamma = absmean_gamma(w_rest)
+    keep = nm_keep_mask(w_rest, n, m)
+    codes = ternary_codes(w_rest, keep, gamma)
+    return {"gamma": gamma, "keep": keep, "codes": codes, "w_rest": w_rest,
+            "opos": pos, "oval": val, "omask": omask}
+
+
+def outlier_matrix(pos: np.ndarray, val: np.ndarray, K: int) -> np.ndarray:
+    """The outliers as a dense fp64 matrix [n_out][K] (zero elsewhere)."""
+    n_out, groups, k = pos.shape
+    dense = np.zeros((n_out, K), dtype=np.float64)
+    cols = pos.astype(np.int64) + OUTLIER_GROUP * np.arange(groups)[None, :, None]
+    rows = np.broadcast_to(np.arange(n_out)[:, None, None], cols.shape)
+    dense[rows, cols] = bf16_to_f32(val).astype(np.float64)
+    return dense
+
+
+def forward_with_outliers(q: np.ndarray, a_prime: np.ndarray, codes: np.ndarray,
+                          gamma: np.float32, pos: np.ndarray, val: np.ndarray) -> dict:
+    """y = (gamma * acc + o) * a'/127 in fp64, with acc the ternary accumulators and o = x_q @ O^T
+    the outlier term (exact: products of int8 and bf16 values summed in fp64). Also returns the
+    magnitude sum |gamma acc| + |x_q| @ |O|^T that bounds the fp32 evaluation's rounding."""
+    K = codes.shape[1]
+    acc = int_matmul(q, codes)
+    O = outlier_matrix(pos, val, K)
+    qf = np.asarray(q, dtype=np.float64)
+    o = qf @ O.T
+    step = np.asarray(a_prime, dtype=np.float64)[:, None] / 127.0
+    y = (np.float64(gamma) * acc.astype(np.float64) + o) * step
+    mag = (np.abs(np.float64(gamma) * acc.astype(np.float64)) + np.abs(qf) @ np.abs(O).T) * step
+    return {"acc": acc, "o": o, "y": y, "mag": mag}
 
 
 # ----------------------------------------------------------------------------------------------

@@ -882,3 +882,118 @@ def test_compact_mutants_caught(mutant):
         return np.array(rows, np.uint8)
 
     assert _compact_pins_fail(pack)
+
+
+# ---------------------------------------------------------------------------------------------
+# Structured k:256 outliers (8:16 paper, "Key points"): the k largest |w| of each 256-group along
+# K are kept apart as bf16; the ternary path sees the rest.
+# ---------------------------------------------------------------------------------------------
+
+def _outlier_hand_row():
+    """One 256-wide row: magnitude 2 at 200, a four-way tie of magnitude 1 at 10, 20, 30, 40, a
+    value 3 + 2^-7 (rounds to bf16 3.0) at 100 and small values elsewhere."""
+    w = np.full((1, 256), 0.01, np.float32)
+    w[0, 1::2] = -0.01
+    w[0, 200] = -2.0
+    w[0, [10, 20, 30, 40]] = [1.0, -1.0, 1.0, -1.0]
+    w[0, 100] = 3.0 + 2.0 ** -7
+    return w
+
+
+def _outlier_pins_fail(select, pack) -> bool:
+    w = _outlier_hand_row()
+    pos, val, mask = select(w, 4)
+    # k = 4: 100 (3.0078), 200 (2.0), then the tie of 1.0 broken toward the lower positions 10, 20
+    if pos.tolist() != [[[10, 20, 100, 200]]]:
+        return True
+    if oracle.bf16_to_f32(val).tolist() != [[[1.0, -1.0, 3.0, -2.0]]]:
+        return True
+    if int(mask.sum()) != 4 or not mask[0, 100] or mask[0, 30]:
+        return True
+    r = pack(w, 2, 4, 4)
+    rest = w.copy()
+    rest[0, [10, 20, 100, 200]] = 0
+    if r["gamma"] != np.float32(np.abs(rest.astype(np.float64)).sum() / 256):
+        return True
+    if np.any(r["codes"][0, [10, 20, 100, 200]] != 0):
+        return True
+    # the page's shares: k of every 256 weights (4:256 ~1.5%, 8:256 ~3.1%, 16:256 = 6.25%)
+    rng = np.random.default_rng(5)
+    w = rng.laplace(0, 0.02, (16, 1024)).astype(np.float32)
+    for k, share in ((4, 0.015625), (8, 0.03125), (16, 0.0625)):
+        pos, val, mask = select(w, k)
+        if mask.mean() != share:
+            return True
+        g = np.abs(w).reshape(16, 4, 256)
+        mk = mask.reshape(16, 4, 256)
+        if np.any(np.where(mk, g, np.inf).min(axis=2) < np.where(mk, -np.inf, g).max(axis=2)):
+            return True  # an outlier smaller than a weight left in the group
+        if not np.array_equal(val, oracle.f32_to_bf16_rne(np.take_along_axis(
+                w.reshape(16, 4, 256), pos.astype(np.int64), axis=2))):
+            return True
+    return False
+
+
+def test_outlier_pins():
+    assert not _outlier_pins_fail(oracle.outlier_select, oracle.pack_with_outliers)
+
+
+@pytest.mark.parametrize("mutant", ["ties_high", "magnitude_order", "smallest", "fp32_values",
+                                    "not_removed"])
+def test_outlier_mutants_caught(mutant):
+    def select(w, k):
+        pos, val, mask = oracle.outlier_select(w, k)
+        n_out, K = w.shape
+        g = K // 256
+        if mutant == "ties_high":
+            mag = np.abs(w).reshape(n_out, g, 256)[:, :, ::-1]
+            order = 255 - np.argsort(-mag, axis=2, kind="stable")[:, :, :k]
+            pos = np.sort(order, axis=2).astype(np.uint8)
+        elif mutant == "magnitude_order":
+            mag = np.abs(w).reshape(n_out, g, 256)
+            pos = np.argsort(-mag, axis=2, kind="stable")[:, :, :k].astype(np.uint8)
+        elif mutant == "smallest":
+            mag = np.abs(w).reshape(n_out, g, 256)
+            pos = np.sort(np.argsort(mag, axis=2, kind="stable")[:, :, :k], axis=2).astype(np.uint8)
+        vals = np.take_along_axis(w.reshape(n_out, g, 256), pos.astype(np.int64), axis=2)
+        val = oracle.f32_to_bf16_rne(vals).astype(np.uint16)
+        if mutant == "fp32_values":  # truncated instead of rounded
+            val = (vals.view(np.uint32) >> 16).astype(np.uint16)
+        mask = np.zeros((n_out, g, 256), bool)
+        np.put_along_axis(mask, pos.astype(np.int64), True, axis=2)
+        return pos, val, mask.reshape(n_out, K)
+
+    def pack(w, n, m, k):
+        if mutant == "not_removed":
+            r = dict(oracle.pack_with_outliers(w, n, m, k))
+            r["gamma"] = oracle.absmean_gamma(w)
+            r["codes"] = oracle.ternary_codes(w, oracle.nm_keep_mask(w, n, m), r["gamma"])
+            return r
+        return oracle.pack_with_outliers(w, n, m, k)
+
+    assert _outlier_pins_fail(select, pack)
+
+
+def test_outlier_forward_against_dense_product():
+    """The two-term forward equals x_q (gamma C + O)^T a'/127 formed as one dense fp64 matrix, and
+    a pure-Python loop on a tiny case."""
+    rng = np.random.default_rng(8)
+    w = rng.laplace(0, 0.02, (9, 512)).astype(np.float32)
+    x = oracle.f32_to_bf16_rne(rng.standard_normal((3, 512)).astype(np.float32))
+    q, a = oracle.quantize_act(x)
+    r = oracle.pack_with_outliers(w, 6, 8, 8)
+    f = oracle.forward_with_outliers(q, a, r["codes"], r["gamma"], r["opos"], r["oval"])
+    W_eff = np.float64(r["gamma"]) * r["codes"].astype(np.float64) + oracle.outlier_matrix(
+        r["opos"], r["oval"], 512)
+    y_dense = (q.astype(np.float64) @ W_eff.T) * (a.astype(np.float64)[:, None] / 127.0)
+    assert np.allclose(f["y"], y_dense, rtol=1e-12, atol=0)
+    # brute force, row 0 / token 0
+    t, rr = 0, 0
+    s = 0.0
+    for kk in range(512):
+        s += float(q[t, kk]) * float(r["gamma"]) * float(r["codes"][rr, kk])
+    for gi in range(2):
+        for j in range(8):
+            p = gi * 256 + int(r["opos"][rr, gi, j])
+            s += float(q[t, p]) * float(oracle.bf16_to_f32(r["oval"][rr, gi, j]))
+    assert math.isclose(f["y"][t, rr], s * float(a[t]) / 127.0, rel_tol=1e-12)
