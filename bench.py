@@ -227,6 +227,27 @@ def run_decode(gpu, args, T=1, with_cpu=True):
         g = gpu.graph(fn, args.steps)
         g.replay()
         timings[name] = gpu.time_graph(g) / args.steps
+    # Pack variants on the same weights: the compact plane (GEMV reads nonzero masks + signs)
+    # and 16:256 outliers (the step plus the outlier term); fewer rotated copies of each
+    variants = {}
+    for tag, kw in (("compact", {"compact": True}), ("outliers 16:256", {"outliers": 16})):
+        Rv = max(1, R // 2)
+        pv = [gpu.b.PackedWeight(wd, n, m, **kw) for _ in range(Rv)]
+
+        def vstep(i, pv=pv, Rv=Rv):
+            gpu.b.bitlinear_bf16(xd, pv[i % Rv], out="f32", y=y, x_q=q, x_absmax=a)
+
+        def vgemv(i, pv=pv, Rv=Rv):
+            gpu.b.bitlinear(q, a, pv[i % Rv], out="f32", y=y)
+
+        for name, fn in ((f"step ({tag})", vstep), (f"int8 forward ({tag})", vgemv)):
+            g = gpu.graph(fn, args.steps)
+            g.replay()
+            variants[name] = gpu.time_graph(g) / args.steps * 1e3
+        if tag == "compact":
+            variants["compact bytes per weight"] = pv[0].query().compact_bytes / (N * K)
+        for p in pv:
+            p.free()
     ms_step = ms / args.steps
     if fused:
         step_bytes = fused_bytes(T, K, N, n, m)
@@ -250,6 +271,7 @@ def run_decode(gpu, args, T=1, with_cpu=True):
                      "traffic": measured_traffic(tkey),
                      "bytes_per_launch": kbytes, "avg_launch_us": kms * 1e3},
         "kernels_us": {k: v * 1e3 for k, v in timings.items()},
+        "pack_variants_us": variants,
     }
     if with_cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_decode(x_bits, w, n, m, step_bytes, args.cpu_seconds)
@@ -610,6 +632,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": res["config"], "roofline": res["roofline"],
             "kernels_us": res.get("kernels_us")}
+    if res.get("pack_variants_us"):
+        line["pack_variants_us"] = res["pack_variants_us"]
     if "activation_kernels" in res:
         line["activation_kernels"] = res["activation_kernels"]
     if "cpu_baseline" in res:

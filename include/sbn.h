@@ -113,6 +113,7 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
 /* Flags of sbn_pack_nm_ternary_ex. */
 #define SBN_PACK_VARIANCE_CORRECTION 1
 #define SBN_PACK_COMPACT 2
+#define SBN_PACK_OUTLIERS(k) ((k) << 8) /* k in {4, 8, 16}: k:256 structured outliers */
 
 /*
  * sbn_pack_nm_ternary with options. SBN_PACK_VARIANCE_CORRECTION ("From 2:4 to 8:16 sparsity
@@ -129,6 +130,16 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
  * nonzero and their signs, (m + n) / m bits per weight (1.5 at 2:4 and 8:16, 1.75 at 6:8, against
  * 2 for the 2-bit codes), and every launch of the forwards with T <= 16 (the GEMV) reads it
  * instead of the 2-bit codes. Results are identical; sbn_packed_export_compact exports it.
+ * SBN_PACK_OUTLIERS(k), k in {4, 8, 16} ("From 2:4 to 8:16 sparsity patterns ...", summary:
+ * salient weights kept in structured k:256 patterns): in each group of 256 weights along K, the k
+ * of largest |w| (equal magnitudes: the lower position) are kept apart as bf16 values (round to
+ * nearest even); gamma, the keep mask, the codes and the variance-correction counts then use the
+ * other weights, with the outlier positions read as 0. The fp32 forwards add the outlier term:
+ * y = fl32(y_ternary + fl32(o * fl32(a'/127))), o = the fp32 sum, in a fixed order, of
+ * x_q[t][position] * value over the row's outliers (each product is exact). SBN_OUT_I32_ACC
+ * returns the ternary accumulators only; sbn_bitlinear_bwd_dx rejects such a handle
+ * (SBN_ERR_UNSUPPORTED: outliers are a post-training, inference-only variant). Needs
+ * K % 256 == 0 (else SBN_ERR_UNSUPPORTED).
  * Each call may change the flags. flags = 0 is sbn_pack_nm_ternary; other bits give
  * SBN_ERR_INVALID_ARG.
  */
@@ -221,6 +232,16 @@ sbn_status sbn_packed_export_rpf(const sbn_packed* w, uint8_t* code_bytes, uint8
                                  void* stream);
 
 /*
+ * Export of the k:256 outliers of the last pack (which must have had SBN_PACK_OUTLIERS(k), else
+ * SBN_ERR_INVALID_ARG), enqueued on `stream`:
+ *   positions [n_out][K/256][k] uint8, ascending within each group (position in the group)
+ *   values    [n_out][K/256][k] uint16, bf16 bit patterns
+ * Either may be NULL to skip it.
+ */
+sbn_status sbn_packed_export_outliers(const sbn_packed* w, uint8_t* positions, uint16_t* values,
+                                      void* stream);
+
+/*
  * Export of the compact form written by the last pack (which must have had SBN_PACK_COMPACT, else
  * SBN_ERR_INVALID_ARG), enqueued on `stream`. Per row a bit stream, LSB first, padded to
  * compact_row_bytes = ceil((K/m)(m + n)/8): group g (positions g*m .. g*m+m-1) at bits
@@ -251,6 +272,7 @@ typedef struct {
   size_t compact_row_bytes;              /* compact export row size, ceil((K/m)(m+n)/8) */
   size_t compact_bytes;                  /* bytes of the compact plane the GEMV streams */
   int compact;                           /* the last pack wrote the compact form */
+  int outlier_k;                         /* k of the last pack's k:256 outliers (0: none) */
 } sbn_packed_desc;
 
 /* Describes a handle; `out` is a host pointer. */

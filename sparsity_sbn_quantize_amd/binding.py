@@ -35,7 +35,7 @@ class PackedDesc(ctypes.Structure):
                 ("mask_row_bytes", ctypes.c_size_t), ("rpf_bytes", ctypes.c_size_t),
                 ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t),
                 ("compact_row_bytes", ctypes.c_size_t), ("compact_bytes", ctypes.c_size_t),
-                ("compact", ctypes.c_int)]
+                ("compact", ctypes.c_int), ("outlier_k", ctypes.c_int)]
 
 
 _lib = None
@@ -57,6 +57,7 @@ _SIGNATURES = {
     "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_export_compact": (ctypes.c_int, [_P, _P, _P]),
+    "sbn_packed_export_outliers": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
     "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
     "sbn_bitlinear_bwd_dx": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
@@ -153,28 +154,32 @@ class PackedWeight:
     """A packed n:m ternary weight (library-owned device memory)."""
 
     def __init__(self, w, n: int, m: int, stream=None, variance_correction: bool = False,
-                 compact: bool = False):
+                 compact: bool = False, outliers: int = 0):
         self._h = ctypes.c_void_p(0)
         self.n, self.m = n, m
         self.variance_correction = variance_correction
         self.compact = compact
+        self.outliers = outliers
         self.pack(w, stream)
 
-    def pack(self, w, stream=None, variance_correction=None, compact=None):
+    def pack(self, w, stream=None, variance_correction=None, compact=None, outliers=None):
         """(Re-)packs from fp32 latent weights [n_out][K]; re-packing reuses the handle. With
         variance_correction, the matmuls use the variance-corrected scale; with compact, the pack
-        also writes the compact form that the GEMV launches read (sbn_pack_nm_ternary_ex)."""
+        also writes the compact form that the GEMV launches read; with outliers = k (4, 8, 16),
+        the k largest |w| of every 256 along K are kept apart (sbn_pack_nm_ternary_ex)."""
         if variance_correction is not None:
             self.variance_correction = variance_correction
         if compact is not None:
             self.compact = compact
+        if outliers is not None:
+            self.outliers = outliers
         import torch
         _require_cuda(w, "w")
         if w.dtype != torch.float32:
             raise ValueError("w must be float32")
         n_out, K = w.shape
         flags = ((SBN_PACK_VARIANCE_CORRECTION if self.variance_correction else 0) |
-                 (SBN_PACK_COMPACT if self.compact else 0))
+                 (SBN_PACK_COMPACT if self.compact else 0) | (int(self.outliers) << 8))
         check(lib().sbn_pack_nm_ternary_ex(_ptr(w), n_out, K, _ld(w, K), self.n, self.m, flags,
                                            ctypes.byref(self._h), _stream(stream)))
         self.n_out, self.K = n_out, K
@@ -222,6 +227,16 @@ class PackedWeight:
         out = torch.zeros((self.n_out, d.compact_row_bytes), dtype=torch.uint8, device=dev)
         check(lib().sbn_packed_export_compact(self.handle, _ptr(out), _stream(stream)))
         return out
+
+    def export_outliers(self, stream=None):
+        """(positions uint8 [n_out][K/256][k], bf16 values as int16 [n_out][K/256][k]), device."""
+        import torch
+        k = self.query().outlier_k
+        dev = torch.device("cuda", torch.cuda.current_device())
+        pos = torch.zeros((self.n_out, self.K // 256, k), dtype=torch.uint8, device=dev)
+        val = torch.zeros((self.n_out, self.K // 256, k), dtype=torch.int16, device=dev)
+        check(lib().sbn_packed_export_outliers(self.handle, _ptr(pos), _ptr(val), _stream(stream)))
+        return pos, val
 
     def mask_flips(self, stream=None):
         """Keep bits changed by the last pack (int64 tensor [1] on the device)."""

@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsbn.so")
 
-SOURCES = ["api.hip", "quantize_act.hip", "pack.hip", "bitlinear.hip", "backward.hip"]
+SOURCES = ["api.hip", "quantize_act.hip", "pack.hip", "bitlinear.hip", "backward.hip",
+           "outliers.hip"]
 HEADERS = ["sbn_common.hpp", "sbn_internal.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -57,6 +57,9 @@ sbn_status fwd_bf16(const char* name, const sbn_packed* w, const uint16_t* x_bf1
   const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
   hipError_t e = sbn::launch_bitlinear_bf16(w, x_bf16, ld_x, T, x_q, ld_q, x_absmax, y, ld_y,
                                             (int)out_kind, ln_eps, (hipStream_t)stream);
+  if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
+    e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
+                                (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, name);
   return SBN_OK;
 }
@@ -118,8 +121,15 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
 sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t K, int64_t ld_w,
                                   int n_keep, int m_group, int flags, sbn_packed** handle,
                                   void* stream) {
-  if ((flags & ~(SBN_PACK_VARIANCE_CORRECTION | SBN_PACK_COMPACT)) != 0)
+  if ((flags & ~(SBN_PACK_VARIANCE_CORRECTION | SBN_PACK_COMPACT | SBN_PACK_OUTLIERS(0xFF))) != 0)
     return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: unknown flags 0x%x", flags);
+  const int outlier_k = (flags >> 8) & 0xFF;
+  if (outlier_k != 0 && outlier_k != 4 && outlier_k != 8 && outlier_k != 16)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: outliers per 256 must be 4, 8 or 16, not %d",
+                outlier_k);
+  if (outlier_k != 0 && K % 256 != 0)
+    return fail(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: k:256 outliers need K %% 256 == 0 (K=%lld)",
+                (long long)K);
   if (!handle) return fail(SBN_ERR_INVALID_ARG, "sbn_pack_nm_ternary: handle is null");
   if (!pattern_ok(n_keep, m_group))
     return fail(SBN_ERR_UNSUPPORTED,
@@ -195,6 +205,17 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
         sbn::kCompactSlack;
     const size_t off_cplane = off;
     off = align_up(off + cplane_bytes, 256);
+    // structured-outlier planes (for up to 16 per 256 weights), when K is a multiple of 256
+    const bool oplanes = K % 256 == 0;
+    const size_t ogroups = oplanes ? (size_t)n_out * (size_t)(K / 256) : 0;
+    const size_t off_opos = off;
+    off = align_up(off + ogroups * 16, 256);
+    const size_t off_oval = off;
+    off = align_up(off + ogroups * 16 * sizeof(uint16_t), 256);
+    const size_t off_omask = off;
+    off = align_up(off + (oplanes ? slots * 8 : 0), 256);
+    const size_t off_osum = off;
+    off = align_up(off + ogroups * sizeof(double), 256);
 
     h = new (std::nothrow) sbn_packed;
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
@@ -239,12 +260,19 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
     h->cplane_bytes = cplane_bytes;
     h->compact_row_bytes = (size_t)(((K / m_group) * (m_group + n_keep) + 7) / 8);
     h->compact = false;
+    h->outlier_k = 0;
+    h->outlier_planes = oplanes;
+    h->opos = h->base + off_opos;
+    h->oval = reinterpret_cast<uint16_t*>(h->base + off_oval);
+    h->omask = reinterpret_cast<unsigned long long*>(h->base + off_omask);
+    h->osum = reinterpret_cast<double*>(h->base + off_osum);
     *handle = h;
   }
   h->last_stream = s;
   h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
   h->vc = (flags & SBN_PACK_VARIANCE_CORRECTION) != 0;
   h->compact = (flags & SBN_PACK_COMPACT) != 0;
+  h->outlier_k = outlier_k;
   hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
   if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
   return SBN_OK;
@@ -274,6 +302,9 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
   const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
   hipError_t e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
                                        (hipStream_t)stream);
+  if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
+    e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
+                                (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd launch");
   return SBN_OK;
 }
@@ -336,6 +367,9 @@ sbn_status sbn_bitlinear_bwd_dx(const sbn_packed* w, const uint16_t* dy_bf16, in
   if (w->rq_count > (1 << 20))
     return fail(SBN_ERR_UNSUPPORTED, "sbn_bitlinear_bwd_dx: n_out=%lld too large",
                 (long long)w->L.n_out);
+  if (w->outlier_k > 0)
+    return fail(SBN_ERR_UNSUPPORTED,
+                "sbn_bitlinear_bwd_dx: the last pack kept k:256 outliers (forward only)");
   if (T == 0) return SBN_OK;
   if (!dx || (!dy_bf16 && w->L.n_out > 0))
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_bwd_dx: null pointer");
@@ -350,6 +384,17 @@ sbn_status sbn_packed_mask_flips(const sbn_packed* w, uint64_t* flips, void* str
   if (!w || !flips) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_mask_flips: null pointer");
   hipError_t e = sbn::launch_sum_flips(w, flips, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_packed_mask_flips launch");
+  return SBN_OK;
+}
+
+sbn_status sbn_packed_export_outliers(const sbn_packed* w, uint8_t* positions, uint16_t* values,
+                                      void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_outliers: handle is null");
+  if (w->outlier_k == 0)
+    return fail(SBN_ERR_INVALID_ARG,
+                "sbn_packed_export_outliers: the last pack kept no outliers (SBN_PACK_OUTLIERS)");
+  hipError_t e = sbn::launch_export_outliers(w, positions, values, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_export_outliers launch");
   return SBN_OK;
 }
 
@@ -381,6 +426,7 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   out->compact_row_bytes = w->compact_row_bytes;
   out->compact_bytes = w->cplane_bytes - sbn::kCompactSlack;
   out->compact = w->compact ? 1 : 0;
+  out->outlier_k = w->outlier_k;
   return SBN_OK;
 }
 

@@ -81,13 +81,22 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* 
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
-// Stage 2: one block combines the partials in a fixed order and writes gamma.
+// Stage 2: one block combines the partials in a fixed order and writes gamma. With structured
+// outliers (osum != nullptr), the sum of their |w| (nos group sums, also in a fixed order) is
+// taken off, so gamma is the absmean of the weights the ternary path sees.
 __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
-    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma) {
+    const double* __restrict__ partials, int num, double count, float* __restrict__ gamma,
+    const double* __restrict__ osum, int64_t nos) {
   __shared__ double red[kAbsmeanThreads / 64];
+  __shared__ double red2[kAbsmeanThreads / 64];
   double acc = 0.0;
   for (int i = threadIdx.x; i < num; i += kAbsmeanThreads) acc += partials[i];
-  const double s = block_sum_f64(acc, red);
+  double s = block_sum_f64(acc, red);
+  if (osum) {
+    double acc2 = 0.0;
+    for (int64_t i = threadIdx.x; i < nos; i += kAbsmeanThreads) acc2 += osum[i];
+    s -= block_sum_f64(acc2, red2);
+  }
   if (threadIdx.x == 0) gamma[0] = count > 0.0 ? (float)(s / count) : 0.0f;
 }
 
@@ -132,7 +141,8 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
                                                       uint8_t* __restrict__ mask_plane,
                                                       uint8_t* __restrict__ code_plane,
                                                       uint32_t* __restrict__ flip_parts,
-                                                      uint32_t* __restrict__ vc_parts) {
+                                                      uint32_t* __restrict__ vc_parts,
+                                                      const uint16_t* __restrict__ omask) {
   const int64_t frag = blockIdx.x;
   const int64_t rb = frag / L.quads, bq = frag % L.quads;
   const int tid = threadIdx.x;
@@ -153,6 +163,13 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
     mp = reinterpret_cast<uint16_t*>(mask_plane) + mslot * 4 + ((qpos & 63) >> 4);
   }
   const uint32_t old_keep = L.has_mask ? (uint32_t)*mp : 0u;
+  // Structured outliers: this thread's 16 outlier bits (same layout as its keep bits); those
+  // positions read as 0 below.
+  uint32_t obits = 0u;
+  if (omask) {
+    const int64_t oslot = (frag << 6) | ((lane_slot & 15) + 16 * (qpos >> 6));
+    obits = omask[oslot * 4 + ((qpos & 63) >> 4)];
+  }
   const float* wr = w + row * ld_w + k0;
   uint32_t u[16];
   if (vec4 && cnt == 16) {
@@ -168,6 +185,8 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] = i < cnt ? __float_as_uint(wr[i]) : 0u;
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = (obits >> i) & 1u ? 0u : u[i];
   const uint32_t half_bits = __float_as_uint(0.5f * gamma_p[0]);
   const int n = L.n;
   uint32_t a[16];
@@ -594,15 +613,22 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
     hipLaunchKernelGGL(absmean_partial, dim3(h->num_partials), dim3(kAbsmeanThreads), 0, s, w,
                        L.n_out, L.K, ld_w, vec4, h->partials);
   }
+  const bool outl = h->outlier_k > 0 && L.n_out > 0;
+  if (outl) {
+    hipError_t e = launch_outlier_select(w, ld_w, h, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
-                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma);
+                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
+                     outl ? h->osum : nullptr, outl ? L.n_out * (L.K >> 8) : (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
   uint32_t* const vc = h->vc ? h->vc_parts : nullptr;
 #define SBN_PACK(MM, FF)                                                                      \
   hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
-                     h->mask, h->codes, h->flip_parts, vc)
+                     h->mask, h->codes, h->flip_parts, vc,                                   \
+                     outl ? reinterpret_cast<const uint16_t*>(h->omask) : nullptr)
   if (L.form == kFormSparse24) {
     SBN_PACK(4, kFormSparse24);
   } else if (L.m == 4) {

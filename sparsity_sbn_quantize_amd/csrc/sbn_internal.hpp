@@ -34,6 +34,12 @@ struct sbn_packed {
   size_t cplane_bytes;  // its size, the slack included
   size_t compact_row_bytes;  // per-row bytes of the compact export stream
   bool compact;         // the last pack wrote the compact plane (host-side state)
+  int outlier_k;        // k of the last pack's k:256 outliers (0: none; host-side state)
+  bool outlier_planes;  // the planes below exist (K % 256 == 0)
+  uint8_t* opos;        // outlier positions [K/256][16][n_out] (k of the 16 slots used)
+  uint16_t* oval;       // outlier bf16 values, same layout
+  unsigned long long* omask;  // outlier positions as one 64-bit word per brick slot
+  double* osum;         // sum of each group's outlier |w| [n_out][K/256]
   int device;
   hipStream_t last_stream;
   // Scale the matmuls multiply by: gamma, or the variance-corrected gamma.
@@ -63,6 +69,12 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
 hipError_t launch_export_compact(const sbn_packed* h, uint8_t* out, hipStream_t s);
+hipError_t launch_outlier_select(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
+hipError_t launch_outlier_add(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
+                              const float* absmax, int64_t T, float* y, int64_t ld_y,
+                              hipStream_t s);
+hipError_t launch_export_outliers(const sbn_packed* h, uint8_t* pos, uint16_t* val,
+                                  hipStream_t s);
 hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
 hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s);
 hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,

@@ -23,6 +23,7 @@ def test_exports_match_header(lib):
                              "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_fwd_ln_bf16",
                              "sbn_bitlinear_bwd_dx", "sbn_free",
                              "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_export_compact",
+                             "sbn_packed_export_outliers",
                              "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
@@ -84,7 +85,13 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
     assert lib.sbn_packed_export_compact(None, None, None) == ERR_INVALID
+    assert lib.sbn_packed_export_outliers(None, None, None, None) == ERR_INVALID
     h = ctypes.c_void_p(0)
+    for k in (1, 3, 5, 32):  # outliers per 256 must be 4, 8 or 16
+        assert lib.sbn_pack_nm_ternary_ex(None, 16, 512, 512, 2, 4, k << 8, ctypes.byref(h),
+                                          None) == ERR_INVALID
+    assert lib.sbn_pack_nm_ternary_ex(None, 16, 320, 320, 2, 4, 4 << 8, ctypes.byref(h),
+                                      None) == -2  # K % 256 != 0
     for flags in (4, -1, 1 << 30):  # unknown flag bits are rejected before any device work
         assert lib.sbn_pack_nm_ternary_ex(None, 16, 64, 64, 2, 4, flags, ctypes.byref(h),
                                           None) == ERR_INVALID
