@@ -531,8 +531,9 @@ def profile_copy(gpu, args):
 # names the bench workload that was run under `rocprofv3 --pmc FETCH_SIZE` and, separately,
 # `--pmc WRITE_SIZE`; the tag "copy" is `bench.py --profile-copy`.
 TRAFFIC_RUNS = {
-    "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<\d+, true, \w+, \d+, false, false"),
-    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv<\d+, false"),
+    # positional codes (form 0) only: the compact variant's GEMV runs in the same workload
+    "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<0, true, \w+, \d+, false, \w+>"),
+    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv<0, false"),
     "prefill_up": ("gemm_8of16_ffn_up", r"bitlinear_gemm<"),
     "prefill_down": ("gemm_8of16_ffn_down", r"bitlinear_gemm<"),
 }

@@ -15,7 +15,8 @@
 //   opos  [G][k][n_out] uint8   positions within the group, ascending for each row and group
 //   oval  [G][k][n_out] uint16  bf16 bit patterns (round to nearest even of the latent fp32)
 //   omask brick layout of the mask plane (one 64-bit word per brick slot): the outlier positions
-//   osum  [n_out][G] fp64       sum of the group's outlier |w|, subtracted from the absmean sum
+//   osum  [ceil(n_out G / 256)]  fp64 sum of the outlier |w| of each selection workgroup (a fixed
+//                               order), subtracted from the absmean sum
 // (G = K / 256; entry (g, j) of all rows is contiguous, so the forward's loads coalesce.)
 #include "sbn_internal.hpp"
 
@@ -25,7 +26,8 @@ namespace {
 // One thread per (row, group). Every weight becomes a key (|w| bits, then 256 - position: larger
 // keys rank first, equal magnitudes rank the lower position first) and passes through a chain of
 // KO compare-and-swap steps that keeps the KO largest keys in order. The positions are then sorted
-// ascending and written out with their values, mask bits and |w| sum.
+// ascending and written out with their values and mask bits; the workgroup's outlier |w| sum goes
+// to osum[blockIdx.x].
 template <int KO>
 __global__ __launch_bounds__(256) void outlier_select(const float* __restrict__ w, int64_t ld_w,
                                                       int vec4, Layout L,
@@ -33,10 +35,11 @@ __global__ __launch_bounds__(256) void outlier_select(const float* __restrict__ 
                                                       uint16_t* __restrict__ oval,
                                                       unsigned long long* __restrict__ omask,
                                                       double* __restrict__ osum) {
+  __shared__ double red[4];
   const int64_t G = L.K >> 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= L.n_out * G) return;
-  const int64_t r = idx / G, g = idx % G;
+  const bool live = idx < L.n_out * G;
+  const int64_t r = live ? idx / G : 0, g = live ? idx % G : 0;
   const float* wr = w + r * ld_w + g * 256;
   unsigned long long key[KO];
 #pragma unroll
@@ -78,19 +81,25 @@ __global__ __launch_bounds__(256) void outlier_select(const float* __restrict__ 
   }
   unsigned long long bm[4] = {0ull, 0ull, 0ull, 0ull};
   double s = 0.0;
+  if (live) {
 #pragma unroll
-  for (int j = 0; j < KO; ++j) {
-    const int p = pos[j];
-    const float v = wr[p];
-    const int64_t o = (g * KO + j) * L.n_out + r;
-    opos[o] = (uint8_t)p;
-    oval[o] = (uint16_t)bf16_rne(v);
-    bm[p >> 6] |= 1ull << (p & 63);
-    s += (double)fabsf(v);
+    for (int j = 0; j < KO; ++j) {
+      const int p = pos[j];
+      const float v = wr[p];
+      const int64_t o = (g * KO + j) * L.n_out + r;
+      opos[o] = (uint8_t)p;
+      oval[o] = (uint16_t)bf16_rne(v);
+      bm[p >> 6] |= 1ull << (p & 63);
+      s += (double)fabsf(v);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) omask[brick_slot(L, r, g * 4 + b)] = bm[b];
   }
-  osum[idx] = s;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) omask[brick_slot(L, r, g * 4 + b)] = bm[b];
+  // workgroup sum in a fixed order: wave sums (DPP tree), then the four waves in order
+  s = wave_sum_f64(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) osum[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // Outlier term of the forward: a workgroup takes 256 / C rows and a tile of TT tokens, whose int8
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(256) void export_outliers(Layout L, int KO, const u
                                                        uint16_t* val_out) {
   const int64_t G = L.K >> 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (g, j, r), r fastest
-  if (idx >= G * KO * L.n_out) return;
+  if (idx >= G * KO * L.n_out) return;  // (g, j) entries of all rows
   const int64_t r = idx % L.n_out, gj = idx / L.n_out;
   const int64_t dst = r * G * KO + gj;
   if (pos_out) pos_out[dst] = opos[idx];

@@ -620,7 +620,8 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
   }
   hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
                      L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
-                     outl ? h->osum : nullptr, outl ? L.n_out * (L.K >> 8) : (int64_t)0);
+                     outl ? h->osum : nullptr,
+                     outl ? (L.n_out * (L.K >> 8) + 255) / 256 : (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.n_out == 0) return e;
   const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));

@@ -39,7 +39,7 @@ struct sbn_packed {
   uint8_t* opos;        // outlier positions [K/256][16][n_out] (k of the 16 slots used)
   uint16_t* oval;       // outlier bf16 values, same layout
   unsigned long long* omask;  // outlier positions as one 64-bit word per brick slot
-  double* osum;         // sum of each group's outlier |w| [n_out][K/256]
+  double* osum;         // outlier |w| sums, one per selection workgroup of 256 groups
   int device;
   hipStream_t last_stream;
   // Scale the matmuls multiply by: gamma, or the variance-corrected gamma.
