@@ -874,13 +874,19 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   }
 }
 
-// Launches the GEMV with W = min(16, quads) waves and Q = ceil(quads / W) quads per wave.
+// Launches the GEMV with W waves and Q = ceil(quads / W) quads per wave: W = min(16, quads) for
+// int8 input; W = ceil(quads / 3) for bf16 input, whose workgroup barriers then wait for fewer
+// waves (same-process A/B on the 2560 -> 6912 shape, one-kernel step at T = 1: 4.45 us at three
+// quads per wave, 4.72 at one, 4.60 at two, 4.65 at four, 4.93 at five; with the LayerNorm 6.46 vs
+// 7.56). The int8 kernel, which has no barrier before its products, is fastest at one quad per
+// wave (3.77 vs 3.85 us at two).
 template <int FORM, bool FUSED, bool XVEC>
 hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
                        int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
                        int out_kind, float ln_eps, hipStream_t s) {
   const Layout& L = h->L;
-  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  const int W =
+      (int)std::min<int64_t>(kGemvMaxWaves, FUSED ? (L.quads + kGemvMaxQ - 1) / kGemvMaxQ : L.quads);
   const int Q = (int)((L.quads + W - 1) / W);
 #define SBN_GEMV(QQ, LNV, XB)                                                                 \
   hipLaunchKernelGGL((bitlinear_gemv<FORM, FUSED, XVEC, QQ, LNV, XB>),                           \
