@@ -533,7 +533,7 @@ def profile_copy(gpu, args):
 TRAFFIC_RUNS = {
     # positional codes (form 0) only: the compact variant's GEMV runs in the same workload
     "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<0, true, \w+, \d+, false, \w+>"),
-    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv<0, false"),
+    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv_i8<0,"),
     "prefill_up": ("gemm_8of16_ffn_up", r"bitlinear_gemm<"),
     "prefill_down": ("gemm_8of16_ffn_down", r"bitlinear_gemm<"),
 }

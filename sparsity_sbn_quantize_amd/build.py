@@ -15,8 +15,11 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsbn.so")
 
 SOURCES = ["api.hip", "quantize_act.hip", "pack.hip", "bitlinear.hip", "backward.hip",
-           "outliers.hip"]
-HEADERS = ["sbn_common.hpp", "sbn_internal.hpp"]
+           "outliers.hip", "gemv_i8.hip"]
+HEADERS = ["sbn_common.hpp", "sbn_internal.hpp", "gemv.hpp"]
+# The int8-input GEMV entry takes its first loads' operands as leading scalar arguments, which
+# the firmware preloads into registers with this option.
+EXTRA_FLAGS = {"gemv_i8.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -30,7 +33,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

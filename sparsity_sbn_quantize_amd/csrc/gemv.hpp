@@ -1,0 +1,493 @@
+// Device code of the n:m-sparse ternary x INT8 GEMV and the helpers it shares with the GEMM;
+// included by bitlinear.hip (GEMM, bf16-input GEMV) and gemv_i8.hip (int8-input GEMV entry).
+//
+// "Microsoft BitNet 1.58: The Era of 1-Bit Large Language Models", section "The BitLinear
+// Layer", operations 4 and 5; section "bitnet.cpp: Matrix-Free Inference".
+#pragma once
+
+#include <algorithm>
+
+#include "sbn_internal.hpp"
+
+namespace sbn {
+namespace {
+
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4i mfma16(const uint32_t* a, v4i b, v4i c) {
+  const v4i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, c, 0, 0, 0);
+}
+
+// Structured-sparse 2:4 MFMA over a 128-K block: a = the lane's 16 kept int8 weights, b = its 32
+// dense activation bytes (K chunks g and g + 4 of the block, g = lane / 16), idx = the kept
+// positions (2 bits per slot).
+__device__ __forceinline__ v4i smfmac16(const uint32_t* a, v4i b_lo, v4i b_hi, uint32_t idx,
+                                        v4i c) {
+  const v4i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+  const v8i bv = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
+  return __builtin_amdgcn_smfmac_i32_16x16x128_i8(av, bv, c, (int)idx, 0, 0);
+}
+
+// K chunk (16 bytes) of a 256-K quad that lane group g supplies as B operand piece j: slice j of
+// brick g for the dense MFMA (chunk 4g + j); for the sparse form, chunks g and g + 4 of block 0,
+// then of block 1 (chunk g + 4j).
+template <int FORM>
+__device__ __forceinline__ int b_chunk(int g, int j) {
+  return FORM == kFormSparse24 ? g + 4 * j : 4 * g + j;
+}
+
+// Loads one brick: positional codes (16 bytes), or the kept form's mask (8 bytes) and code bytes.
+template <int FORM>
+__device__ __forceinline__ void load_brick(const Layout& L, const uint8_t* __restrict__ mask_plane,
+                                           const uint8_t* __restrict__ code_plane, int64_t slot,
+                                           uint32_t mask[2], uint32_t codes[4]) {
+  mask[0] = mask[1] = 0;
+  codes[0] = codes[1] = codes[2] = codes[3] = 0;
+  if constexpr (FORM != kFormKept) {
+    const uint4 c = *reinterpret_cast<const uint4*>(code_plane + slot * 16);
+    codes[0] = c.x; codes[1] = c.y; codes[2] = c.z; codes[3] = c.w;
+  } else {
+    if (L.has_mask) {
+      const uint2 m = *reinterpret_cast<const uint2*>(mask_plane + slot * 8);
+      mask[0] = m.x;
+      mask[1] = m.y;
+    }
+    const int cbb = L.code_brick_bytes;
+    const uint8_t* c = code_plane + slot * cbb;
+    for (int i = 0; i < cbb; ++i) codes[i >> 2] |= (uint32_t)c[i] << (8 * (i & 3));
+  }
+}
+
+template <int FORM>
+__device__ __forceinline__ void decode(const Layout& L, const uint32_t mask[2],
+                                       const uint32_t codes[4], uint32_t out[16]) {
+  if constexpr (FORM == kFormPositional) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[j], out + 4 * j);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = 0;
+    decode_kept_brick(mask, codes, L.n, L.m, L.has_mask, out);
+  }
+}
+
+// 16 activation bytes of one token row at K offset k (a multiple of 16), zero beyond K.
+// XVEC: rows are 16-byte aligned and K % 16 == 0, so a chunk is either whole or absent.
+template <bool XVEC>
+__device__ __forceinline__ v4i load_x16(const int8_t* __restrict__ row, int k, int K) {
+  if constexpr (XVEC) {
+    // Branch-free: the load address is clamped into the row (K >= 16 here), the value masked.
+    const v4i v = *reinterpret_cast<const v4i*>(row + min(k, K - 16));
+    return k < K ? v : v4i{0, 0, 0, 0};
+  } else {
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      if (k + i < K) w[i >> 2] |= (uint32_t)(uint8_t)row[k + i] << (8 * (i & 3));
+    }
+    return v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  }
+}
+
+__device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, int64_t t,
+                                          int64_t r, int acc, float gamma, float step) {
+  if (out_kind == SBN_OUT_I32_ACC) {
+    reinterpret_cast<int32_t*>(y)[t * ld_y + r] = acc;
+  } else {
+    const float v = __fmul_rn(__fmul_rn((float)acc, gamma), step);
+    reinterpret_cast<float*>(y)[t * ld_y + r] = v;
+  }
+}
+
+// GEMV (T <= 16): one workgroup per 16-row fragment row with W = min(16, quads) waves; wave w
+// takes the 256-K quads w, w + W, ... (at most kGemvMaxQ). Every wave first issues its brick
+// loads (HBM) and its activation loads (L2: every workgroup reads the same rows) straight into
+// MFMA operand registers, then decodes and multiplies; the partial sums of the waves are combined
+// through LDS once. Lane (t, g) supplies token t's 64 activation bytes at K offset 64g of each
+// quad, matching the K slices of the bricks.
+// FUSED (T <= 4): the activations are bf16. Every workgroup then computes the per-token absmax
+// over K itself (lane maxima, then wave maxima combined through LDS) and quantizes the pieces it
+// needs with the arithmetic of the quantize kernel, so the decode step is one launch with no int8
+// copy of the activations between two kernels; workgroup 0 also writes x_q and a' for the caller.
+// (For more tokens every workgroup would redo a quantization pass over all T x K activations;
+// there the quantize kernel followed by the GEMV is faster.)
+constexpr int kGemvMaxWaves = 16;
+constexpr int kGemvMaxQ = 3;  // quads per wave (template Q <= 3): K <= 16 * 3 * 256 = 12288
+constexpr int kFusedMaxT = 4;  // tokens of the one-kernel quantize-and-multiply path
+
+__device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, const v4i& v) {
+  if (vec && k + 16 <= K) {
+    *reinterpret_cast<v4i*>(row + k) = v;
+  } else {
+    for (int i = 0; i < 16 && k + i < K; ++i) row[k + i] = (int8_t)(v[i >> 2] >> (8 * (i & 3)));
+  }
+}
+
+// LN (bf16 input only): parameter-free LayerNorm before the quantization. XBUF, int8 input: brick
+// and activation loads through buffer resources, straight-line; measured faster for a few tokens
+// (4.35 vs 4.58 us at T = 1 on the 2560 -> 6912 decode shape) and slower for 16 (6.35 vs 6.05 us),
+// so the launcher picks it for T <= 4. The bf16-input kernel loads its bricks through the buffer
+// resource too (4.95 vs 5.06 us per one-kernel step at T = 1). XBUF, bf16 input (T = 1, no
+// LayerNorm): the row comes through a buffer resource and the token count is a compile-time 1.
+// (Every wave taking the absmax over the whole row itself, with no barrier, was measured slower:
+// 6.3 vs 4.8 us, the 4320 waves' requests for the same few KB queue at a few L2 channels.)
+template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
+__device__ __forceinline__ void gemv_body(
+    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
+    const Layout& L, const int K, const int nq, const float* __restrict__ gamma_p,
+    const void* __restrict__ xin, int64_t ld_x, int8_t* __restrict__ xq_out, int64_t ld_q,
+    float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y, int out_kind,
+    float ln_eps) {
+  __shared__ v4i red[kGemvMaxWaves][64];
+  __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT / 2];  // token pairs, 16 bits each
+  __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
+  __shared__ double lndev[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
+  __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
+  constexpr bool CMP = compact_form(FORM);
+  __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
+  const int W = (int)(blockDim.x >> 6);
+  // the wave index is uniform; readfirstlane lets it feed the buffer loads' scalar offsets
+  // directly (otherwise each load sits in a loop over the lanes' distinct offsets)
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t rb = blockIdx.x;
+  const int t = lane & 15, g = lane >> 4;
+  const bool tok_ok = t < (int)T;
+
+  uint32_t mask[Q][2], codes[Q][4];
+  // With FUSED or XBUF, positional and structured-sparse bricks come through a buffer resource
+  // over this row block's quads: a quad past the last reads as zero, so the loads are
+  // straight-line code and the compiler's wait counts stay exact (a wait for the activations then
+  // does not wait for the bricks behind them). The compact plane always comes this way: a quad
+  // takes cq = 512 + 8 csb bytes, and the range ends kCompactSlack bytes past the row block's
+  // last quad (the plane has that slack), which covers every lane's three-word sign load.
+  const int cq = CMP ? (int)compact_quad_bytes(L.csb) : 1024;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(code_plane + rb * nq * cq), (short)0,
+      CMP ? nq * cq + kCompactSlack : (FORM != kFormKept ? nq * 1024 : 0), kBufDword3);
+  auto load_bricks = [&]() {
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int q = wave + i * W;
+      if constexpr (CMP) {
+        // the lane's nonzero mask, and the three words holding its csb sign bits
+        const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, q * cq, 0);
+        const int sbit = lane * L.csb;
+        const v3u sg = __builtin_amdgcn_raw_buffer_load_b96(
+            crs, kCompactMaskBytes + 4 * (sbit >> 5), q * cq, 0);
+        mask[i][0] = mk[0]; mask[i][1] = mk[1];
+        codes[i][0] = sg[0]; codes[i][1] = sg[1]; codes[i][2] = sg[2];
+        codes[i][3] = (uint32_t)(sbit & 31);
+      } else if constexpr (FORM != kFormKept && (FUSED || XBUF)) {
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, q * 1024, 0);
+        codes[i][0] = (uint32_t)c[0]; codes[i][1] = (uint32_t)c[1];
+        codes[i][2] = (uint32_t)c[2]; codes[i][3] = (uint32_t)c[3];
+        mask[i][0] = mask[i][1] = 0;
+      } else if (q < nq) {
+        load_brick<FORM>(L, mask_plane, code_plane, ((rb * nq + q) << 6) | lane, mask[i],
+                         codes[i]);
+      } else {
+        mask[i][0] = mask[i][1] = 0;
+        codes[i][0] = codes[i][1] = codes[i][2] = codes[i][3] = 0;
+      }
+    }
+  };
+  v4i b[Q][4];  // B operands: 16 int8 activations per K slice
+  float a_t = 0.0f;     // a' of token t (FUSED, else loaded with the operands)
+  // The scales are loaded up front, so the epilogue waits for no memory
+  const float gamma = gamma_p[0];
+  auto build_lut = [&]() {
+    if constexpr (CMP) {
+      for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
+    }
+  };
+  if constexpr (!FUSED) {
+    load_bricks();
+    build_lut();
+    if constexpr (XVEC && XBUF) {
+      // One buffer resource over the T activation rows, straight-line loads: the lanes of a
+      // missing token take an offset past the range and read zero, as does the K tail of the last
+      // row; a piece past K in another row reads that row's padding or the next row, harmless
+      // because the weights there are zero. Offsets stay below 2^31: T <= 16, ld_x <= 2^26.
+      const int64_t ext = ((int64_t)T - 1) * ld_x + K;
+      const __amdgpu_buffer_rsrc_t xr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)xin, (short)0, (int)ext, kBufDword3);
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int voff = tok_ok ? t * (int)ld_x + 16 * b_chunk<FORM>(g, j) : (1 << 30);
+          b[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff, (wave + i * W) * kQuadK, 0);
+        }
+    } else {
+      const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = (wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
+          b[i][j] = v4i{0, 0, 0, 0};
+          if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
+        }
+    }
+    if (out_kind == SBN_OUT_F32 && tok_ok) a_t = absmax[t];
+    if constexpr (CMP) __syncthreads();  // the nibble table
+  } else {
+    // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
+    // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
+    // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
+    // XBUF runs one token; the constant lets the compiler drop the other tokens' code
+    const int Tn = XBUF ? 1 : (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+    // One resource over the row (XBUF): loads are straight-line, positions past K read zero.
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(xin), (short)0, XBUF ? K * 2 : 0, kBufDword3);
+    uint2 xv[Q][kFusedMaxT];
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        const int k = (wave + i * W) * kQuadK + 4 * lane;
+        uint2 v = make_uint2(0, 0);
+        if constexpr (XBUF) {
+          if (tt == 0) {
+            const v2u r = __builtin_amdgcn_raw_buffer_load_b64(xr, k < K ? 2 * k : (1 << 30), 0, 0);
+            v = make_uint2(r[0], r[1]);
+          }
+        } else if (tt < Tn && k < K) {
+          const uint16_t* row = xb + tt * ld_x;
+          if constexpr (XVEC) {
+            v = *reinterpret_cast<const uint2*>(row + k);
+          } else {
+            uint32_t w2[2] = {0, 0};
+            for (int u = 0; u < 4 && k + u < K; ++u) w2[u >> 1] |= (uint32_t)row[k + u] << (16 * (u & 1));
+            v = make_uint2(w2[0], w2[1]);
+          }
+        }
+        xv[i][tt] = v;
+      }
+    // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
+    // does not wait for the bricks: the quantization below overlaps the brick loads. The
+    // scheduling barrier keeps the compiler from issuing the bricks first.
+    __builtin_amdgcn_sched_barrier(0);
+    load_bricks();
+    build_lut();  // published by a barrier below
+    if constexpr (LN) {
+      // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
+      // and sum of squared deviations over the wave (DPP), then over the waves (one LDS read per
+      // lane and a 16-lane DPP tree, a fixed order); the lane's elements are replaced by their
+      // bf16 normalized values.
+      double ps[kFusedMaxT], pd[kFusedMaxT];
+      float mu32[kFusedMaxT], r32[kFusedMaxT];
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        ps[tt] = 0.0;
+        if (tt >= Tn) continue;
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+          const uint2 v = xv[i][tt];
+          ps[tt] += (double)__uint_as_float(v.x << 16) + (double)__uint_as_float(v.x & 0xFFFF0000u) +
+                    (double)__uint_as_float(v.y << 16) + (double)__uint_as_float(v.y & 0xFFFF0000u);
+        }
+        ps[tt] = wave_sum_f64(ps[tt]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) lnsum[wave][tt] = ps[tt];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        pd[tt] = 0.0;
+        ps[tt] = 0.0;
+        if (tt >= Tn) continue;
+        ps[tt] = row16_sum_f64(lane < W ? lnsum[lane][tt] : 0.0);
+        ps[tt] /= (double)K;  // the mean
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+          const int k = (wave + i * W) * kQuadK + 4 * lane;
+          const uint2 v = xv[i][tt];
+          const float f[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                              __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (k + u < K) {
+              const double e = (double)f[u] - ps[tt];
+              pd[tt] += e * e;
+            }
+          }
+        }
+        pd[tt] = wave_sum_f64(pd[tt]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) lndev[wave][tt] = pd[tt];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        mu32[tt] = 0.0f;
+        r32[tt] = 0.0f;
+        if (tt >= Tn) continue;
+        const double d = row16_sum_f64(lane < W ? lndev[lane][tt] : 0.0);
+        mu32[tt] = (float)ps[tt];
+        r32[tt] = (float)(1.0 / sqrt(d / (double)K + (double)ln_eps));
+      }
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const int k = (wave + i * W) * kQuadK + 4 * lane;
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          if (tt >= Tn || k >= K) continue;
+          uint2 z = make_uint2(ln_pair(xv[i][tt].x, mu32[tt], r32[tt]),
+                               ln_pair(xv[i][tt].y, mu32[tt], r32[tt]));
+          // positions past K stay zero
+          if (k + 4 > K) {
+            const int keep = K - k;  // 1 .. 3 valid values
+            if (keep < 2) z.x &= 0xFFFFu;
+            if (keep < 3) z.y = 0u;
+            else z.y &= 0xFFFFu;
+          }
+          xv[i][tt] = z;
+        }
+      }
+    }
+    uint32_t m[kFusedMaxT];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt) {
+      m[tt] = 0;
+#pragma unroll
+      for (int i = 0; i < Q; ++i) m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], xv[i][tt].x),
+                                                         xv[i][tt].y);
+    }
+    // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
+    // over the waves through LDS (one read per lane and a 16-lane DPP tree).
+    uint32_t pk[kFusedMaxT / 2];
+#pragma unroll
+    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) {
+      pk[p2] = 0;
+      if (2 * p2 >= Tn) continue;
+      const uint32_t a0 = max(m[2 * p2] & 0xFFFFu, m[2 * p2] >> 16);
+      const uint32_t a1 = max(m[2 * p2 + 1] & 0xFFFFu, m[2 * p2 + 1] >> 16);
+      pk[p2] = wave_max_u16x2(a0 | (a1 << 16));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) wmax[wave][p2] = pk[p2];
+    }
+    __syncthreads();
+    uint32_t am2[kFusedMaxT / 2];
+#pragma unroll
+    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2)
+      am2[p2] = 2 * p2 < Tn ? row16_max_u16x2(lane < W ? wmax[lane][p2] : 0u) : 0u;
+    float s_t[kFusedMaxT];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt) {
+      s_t[tt] = 0.0f;
+      if (tt >= Tn) continue;
+      const uint32_t am = (am2[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
+      const float a = fmaxf(__uint_as_float(am << 16), kAbsmaxFloor);
+      s_t[tt] = 127.0f / a;
+      if (tt == t) a_t = a;
+    }
+    uint32_t* xs = xq_lds[wave];  // [kFusedMaxT][64] words
+    const bool vq = ((uintptr_t)xq_out % 4 == 0) && (ld_q % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int k = (wave + i * W) * kQuadK + 4 * lane;
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        if (tt >= Tn) continue;
+        const uint32_t qw = quant4(xv[i][tt].x, xv[i][tt].y, s_t[tt]);
+        xs[tt * 64 + lane] = qw;
+        if (rb == 0 && tt < (int)T && k < K) {
+          int8_t* dst = xq_out + tt * ld_q + k;
+          if (vq && k + 4 <= K) {
+            *reinterpret_cast<uint32_t*>(dst) = qw;
+          } else {
+            for (int u = 0; u < 4 && k + u < K; ++u) dst[u] = (int8_t)(qw >> (8 * u));
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[i][j] = t < kFusedMaxT && tok_ok
+                      ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 +
+                                                      4 * b_chunk<FORM>(g, j))
+                      : v4i{0, 0, 0, 0};
+    }
+    if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
+  }
+
+  v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    if (wave + i * W < nq) {
+      if constexpr (FORM == kFormSparse24) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          uint32_t a[4];
+          exp_word_to_i8(codes[i][2 * blk], a);
+          acc = smfmac16(a, b[i][2 * blk], b[i][2 * blk + 1], codes[i][2 * blk + 1], acc);
+        }
+      } else {
+        uint32_t a[16];
+        if constexpr (CMP) {
+          const uint32_t sh = codes[i][3];
+          decode_compact<compact_m(FORM)>(mask[i], __builtin_amdgcn_alignbit(codes[i][1], codes[i][0], sh),
+                                          __builtin_amdgcn_alignbit(codes[i][2], codes[i][1], sh),
+                                          L.n, L.csb, clut, a);
+        } else {
+          decode<FORM>(L, mask[i], codes[i], a);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+      }
+    }
+  }
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || !tok_ok) return;
+  // (A fully unrolled sum over all 16 slots, masked, measured slower than this loop.)
+  v4i sum = red[0][lane];
+  for (int w = 1; w < W; ++w) sum += red[w][lane];
+  const int64_t row0 = rb * 16 + 4 * g;
+  const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < L.n_out;
+  if (vec) {  // the lane's four consecutive rows in one store
+    if (out_kind == SBN_OUT_I32_ACC) {
+      *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + row0) = sum;
+    } else {
+      float4 f;
+      f.x = __fmul_rn(__fmul_rn((float)sum[0], gamma), step);
+      f.y = __fmul_rn(__fmul_rn((float)sum[1], gamma), step);
+      f.z = __fmul_rn(__fmul_rn((float)sum[2], gamma), step);
+      f.w = __fmul_rn(__fmul_rn((float)sum[3], gamma), step);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + row0) = f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + i;
+      if (row < L.n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+    }
+  }
+}
+
+// Entry of the bf16-input kernels (and of the int8 kernels for other callers): the layout comes by
+// value and K and the quad count are read from it.
+template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
+    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
+    const float* __restrict__ gamma_p, const void* __restrict__ xin, int64_t ld_x,
+    int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
+    void* __restrict__ y, int64_t ld_y, int out_kind, float ln_eps) {
+  gemv_body<FORM, FUSED, XVEC, Q, LN, XBUF>(mask_plane, code_plane, L, (int)L.K, (int)L.quads,
+                                            gamma_p, xin, ld_x, xq_out, ld_q, absmax, T, y, ld_y,
+                                            out_kind, ln_eps);
+}
+
+}  // namespace
+}  // namespace sbn
