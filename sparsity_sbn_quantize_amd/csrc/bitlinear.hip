@@ -470,8 +470,7 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                           hipStream_t s) {
   const Layout& L = h->L;
-  if (T <= 16 && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ)
-    return launch_gemv_int8(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);  // gemv_i8.hip
+  if (T <= 16) return launch_gemv_int8(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);  // gemv_i8.hip
   hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC>, kGemmSmem);
   if (e != hipSuccess) return e;
   const int64_t gx = (L.row_blocks + kGemmRowBlocks - 1) / kGemmRowBlocks;

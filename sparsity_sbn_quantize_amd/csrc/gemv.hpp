@@ -101,8 +101,9 @@ __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, i
   }
 }
 
-// GEMV (T <= 16): one workgroup per 16-row fragment row with W = min(16, quads) waves; wave w
-// takes the 256-K quads w, w + W, ... (at most kGemvMaxQ). Every wave first issues its brick
+// GEMV (T <= 16): one workgroup per 16-row fragment row with W waves (set by the launcher); wave
+// w takes the 256-K quads w, w + W, ... (at most kGemvMaxQ per batch; with int8 input, further
+// batches of W * kGemvMaxQ quads follow for larger K). Every wave first issues its brick
 // loads (HBM) and its activation loads (L2: every workgroup reads the same rows) straight into
 // MFMA operand registers, then decodes and multiplies; the partial sums of the waves are combined
 // through LDS once. Lane (t, g) supplies token t's 64 activation bytes at K offset 64g of each
@@ -136,7 +137,7 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
 template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
 __device__ __forceinline__ void gemv_body(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
-    const Layout& L, const int K, const int nq, const float* __restrict__ gamma_p,
+    const Layout& L, const int K, const int nq, const int W, const float* __restrict__ gamma_p,
     const void* __restrict__ xin, int64_t ld_x, int8_t* __restrict__ xq_out, int64_t ld_q,
     float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y, int out_kind,
     float ln_eps) {
@@ -147,8 +148,8 @@ __device__ __forceinline__ void gemv_body(
   __shared__ uint32_t xq_lds[FUSED ? kGemvMaxWaves : 1][kFusedMaxT * 64];
   constexpr bool CMP = compact_form(FORM);
   __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
-  const int W = (int)(blockDim.x >> 6);
-  // the wave index is uniform; readfirstlane lets it feed the buffer loads' scalar offsets
+  // W: the workgroup's waves (blockDim.x / 64), an argument so that no load of the dispatch's
+  // group size delays the first loads; the wave index is uniform; readfirstlane lets it feed the buffer loads' scalar offsets
   // directly (otherwise each load sits in a loop over the lanes' distinct offsets)
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -167,10 +168,10 @@ __device__ __forceinline__ void gemv_body(
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(code_plane + rb * nq * cq), (short)0,
       CMP ? nq * cq + kCompactSlack : (FORM != kFormKept ? nq * 1024 : 0), kBufDword3);
-  auto load_bricks = [&]() {
+  auto load_bricks = [&](int qoff) {
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
-      const int q = wave + i * W;
+      const int q = qoff + wave + i * W;
       if constexpr (CMP) {
         // the lane's nonzero mask, and the three words holding its csb sign bits
         const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, q * cq, 0);
@@ -203,250 +204,261 @@ __device__ __forceinline__ void gemv_body(
       for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
     }
   };
-  if constexpr (!FUSED) {
-    load_bricks();
-    build_lut();
-    if constexpr (XVEC && XBUF) {
-      // One buffer resource over the T activation rows, straight-line loads: the lanes of a
-      // missing token take an offset past the range and read zero, as does the K tail of the last
-      // row; a piece past K in another row reads that row's padding or the next row, harmless
-      // because the weights there are zero. Offsets stay below 2^31: T <= 16, ld_x <= 2^26.
-      const int64_t ext = ((int64_t)T - 1) * ld_x + K;
-      const __amdgpu_buffer_rsrc_t xr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)xin, (short)0, (int)ext, kBufDword3);
+  v4i acc = v4i{0, 0, 0, 0};
+  // int8 input: the waves take batches of W * Q quads in turn, so any K fits; bf16 input (whose
+  // quantization needs the whole row first): one batch
+  const int nbatch = FUSED ? 1 : (nq + W * Q - 1) / (W * Q);
+  // The first batch is straight-line code (its loads go out first thing); further batches loop.
+  auto run_batch = [&](const int qoff, const bool first) {
+    if constexpr (!FUSED) {
+      load_bricks(qoff);
+      if (first) build_lut();
+      if constexpr (XVEC && XBUF) {
+        // One buffer resource over the T activation rows, straight-line loads: the lanes of a
+        // missing token take an offset past the range and read zero, as does the K tail of the last
+        // row; a piece past K in another row reads that row's padding or the next row, harmless
+        // because the weights there are zero. Offsets stay below 2^31: T <= 16, ld_x <= 2^26.
+        const int64_t ext = ((int64_t)T - 1) * ld_x + K;
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)xin, (short)0, (int)ext, kBufDword3);
 #pragma unroll
-      for (int i = 0; i < Q; ++i)
+        for (int i = 0; i < Q; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int voff = tok_ok ? t * (int)ld_x + 16 * b_chunk<FORM>(g, j) : (1 << 30);
-          b[i][j] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff, (wave + i * W) * kQuadK, 0);
-        }
+          for (int j = 0; j < 4; ++j) {
+            const int voff = tok_ok ? t * (int)ld_x + 16 * b_chunk<FORM>(g, j) : (1 << 30);
+            b[i][j] =
+                __builtin_amdgcn_raw_buffer_load_b128(xr, voff, (qoff + wave + i * W) * kQuadK, 0);
+          }
+      } else {
+        const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k = (qoff + wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
+            b[i][j] = v4i{0, 0, 0, 0};
+            if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
+          }
+      }
+      if (first) {
+        if (out_kind == SBN_OUT_F32 && tok_ok) a_t = absmax[t];
+        if constexpr (CMP) __syncthreads();  // the nibble table
+      }
     } else {
-      const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
+      // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
+      // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
+      // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
+      const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
+      // XBUF runs one token; the constant lets the compiler drop the other tokens' code
+      const int Tn = XBUF ? 1 : (int)T;  // <= kFusedMaxT; loops below stop at the real token count
+      // One resource over the row (XBUF): loads are straight-line, positions past K read zero.
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<void*>(xin), (short)0, XBUF ? K * 2 : 0, kBufDword3);
+      uint2 xv[Q][kFusedMaxT];
 #pragma unroll
       for (int i = 0; i < Q; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int k = (wave + i * W) * kQuadK + 16 * b_chunk<FORM>(g, j);
-          b[i][j] = v4i{0, 0, 0, 0};
-          if (tok_ok && k < K) b[i][j] = load_x16<XVEC>(xrow, k, K);
-        }
-    }
-    if (out_kind == SBN_OUT_F32 && tok_ok) a_t = absmax[t];
-    if constexpr (CMP) __syncthreads();  // the nibble table
-  } else {
-    // Lane l quantizes elements 4l .. 4l+3 of every token in each of its quads (one quant4 per
-    // token and quad, so no lane idles), then the bytes are regrouped through a wave-local LDS
-    // buffer into the B layout (lane (t, g) slice j = bytes 64g + 16j .. +15 of token t).
-    const uint16_t* xb = reinterpret_cast<const uint16_t*>(xin);
-    // XBUF runs one token; the constant lets the compiler drop the other tokens' code
-    const int Tn = XBUF ? 1 : (int)T;  // <= kFusedMaxT; loops below stop at the real token count
-    // One resource over the row (XBUF): loads are straight-line, positions past K read zero.
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(xin), (short)0, XBUF ? K * 2 : 0, kBufDword3);
-    uint2 xv[Q][kFusedMaxT];
-#pragma unroll
-    for (int i = 0; i < Q; ++i)
-#pragma unroll
-      for (int tt = 0; tt < kFusedMaxT; ++tt) {
-        const int k = (wave + i * W) * kQuadK + 4 * lane;
-        uint2 v = make_uint2(0, 0);
-        if constexpr (XBUF) {
-          if (tt == 0) {
-            const v2u r = __builtin_amdgcn_raw_buffer_load_b64(xr, k < K ? 2 * k : (1 << 30), 0, 0);
-            v = make_uint2(r[0], r[1]);
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          const int k = (wave + i * W) * kQuadK + 4 * lane;
+          uint2 v = make_uint2(0, 0);
+          if constexpr (XBUF) {
+            if (tt == 0) {
+              const v2u r = __builtin_amdgcn_raw_buffer_load_b64(xr, k < K ? 2 * k : (1 << 30), 0, 0);
+              v = make_uint2(r[0], r[1]);
+            }
+          } else if (tt < Tn && k < K) {
+            const uint16_t* row = xb + tt * ld_x;
+            if constexpr (XVEC) {
+              v = *reinterpret_cast<const uint2*>(row + k);
+            } else {
+              uint32_t w2[2] = {0, 0};
+              for (int u = 0; u < 4 && k + u < K; ++u) w2[u >> 1] |= (uint32_t)row[k + u] << (16 * (u & 1));
+              v = make_uint2(w2[0], w2[1]);
+            }
           }
-        } else if (tt < Tn && k < K) {
-          const uint16_t* row = xb + tt * ld_x;
-          if constexpr (XVEC) {
-            v = *reinterpret_cast<const uint2*>(row + k);
-          } else {
-            uint32_t w2[2] = {0, 0};
-            for (int u = 0; u < 4 && k + u < K; ++u) w2[u >> 1] |= (uint32_t)row[k + u] << (16 * (u & 1));
-            v = make_uint2(w2[0], w2[1]);
+          xv[i][tt] = v;
+        }
+      // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
+      // does not wait for the bricks: the quantization below overlaps the brick loads. The
+      // scheduling barrier keeps the compiler from issuing the bricks first.
+      __builtin_amdgcn_sched_barrier(0);
+      load_bricks(0);
+      build_lut();  // published by a barrier below
+      if constexpr (LN) {
+        // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
+        // and sum of squared deviations over the wave (DPP), then over the waves (one LDS read per
+        // lane and a 16-lane DPP tree, a fixed order); the lane's elements are replaced by their
+        // bf16 normalized values.
+        double ps[kFusedMaxT], pd[kFusedMaxT];
+        float mu32[kFusedMaxT], r32[kFusedMaxT];
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          ps[tt] = 0.0;
+          if (tt >= Tn) continue;
+#pragma unroll
+          for (int i = 0; i < Q; ++i) {
+            const uint2 v = xv[i][tt];
+            ps[tt] += (double)__uint_as_float(v.x << 16) + (double)__uint_as_float(v.x & 0xFFFF0000u) +
+                      (double)__uint_as_float(v.y << 16) + (double)__uint_as_float(v.y & 0xFFFF0000u);
           }
+          ps[tt] = wave_sum_f64(ps[tt]);
         }
-        xv[i][tt] = v;
-      }
-    // The bricks (HBM) go out after the activations (L2), so that waiting for the activations
-    // does not wait for the bricks: the quantization below overlaps the brick loads. The
-    // scheduling barrier keeps the compiler from issuing the bricks first.
-    __builtin_amdgcn_sched_barrier(0);
-    load_bricks();
-    build_lut();  // published by a barrier below
-    if constexpr (LN) {
-      // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
-      // and sum of squared deviations over the wave (DPP), then over the waves (one LDS read per
-      // lane and a 16-lane DPP tree, a fixed order); the lane's elements are replaced by their
-      // bf16 normalized values.
-      double ps[kFusedMaxT], pd[kFusedMaxT];
-      float mu32[kFusedMaxT], r32[kFusedMaxT];
+        if (lane == 0) {
 #pragma unroll
-      for (int tt = 0; tt < kFusedMaxT; ++tt) {
-        ps[tt] = 0.0;
-        if (tt >= Tn) continue;
-#pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          const uint2 v = xv[i][tt];
-          ps[tt] += (double)__uint_as_float(v.x << 16) + (double)__uint_as_float(v.x & 0xFFFF0000u) +
-                    (double)__uint_as_float(v.y << 16) + (double)__uint_as_float(v.y & 0xFFFF0000u);
+          for (int tt = 0; tt < kFusedMaxT; ++tt) lnsum[wave][tt] = ps[tt];
         }
-        ps[tt] = wave_sum_f64(ps[tt]);
-      }
-      if (lane == 0) {
+        __syncthreads();
 #pragma unroll
-        for (int tt = 0; tt < kFusedMaxT; ++tt) lnsum[wave][tt] = ps[tt];
-      }
-      __syncthreads();
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          pd[tt] = 0.0;
+          ps[tt] = 0.0;
+          if (tt >= Tn) continue;
+          ps[tt] = row16_sum_f64(lane < W ? lnsum[lane][tt] : 0.0);
+          ps[tt] /= (double)K;  // the mean
 #pragma unroll
-      for (int tt = 0; tt < kFusedMaxT; ++tt) {
-        pd[tt] = 0.0;
-        ps[tt] = 0.0;
-        if (tt >= Tn) continue;
-        ps[tt] = row16_sum_f64(lane < W ? lnsum[lane][tt] : 0.0);
-        ps[tt] /= (double)K;  // the mean
+          for (int i = 0; i < Q; ++i) {
+            const int k = (wave + i * W) * kQuadK + 4 * lane;
+            const uint2 v = xv[i][tt];
+            const float f[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                                __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (k + u < K) {
+                const double e = (double)f[u] - ps[tt];
+                pd[tt] += e * e;
+              }
+            }
+          }
+          pd[tt] = wave_sum_f64(pd[tt]);
+        }
+        if (lane == 0) {
+#pragma unroll
+          for (int tt = 0; tt < kFusedMaxT; ++tt) lndev[wave][tt] = pd[tt];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < kFusedMaxT; ++tt) {
+          mu32[tt] = 0.0f;
+          r32[tt] = 0.0f;
+          if (tt >= Tn) continue;
+          const double d = row16_sum_f64(lane < W ? lndev[lane][tt] : 0.0);
+          mu32[tt] = (float)ps[tt];
+          r32[tt] = (float)(1.0 / sqrt(d / (double)K + (double)ln_eps));
+        }
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
           const int k = (wave + i * W) * kQuadK + 4 * lane;
-          const uint2 v = xv[i][tt];
-          const float f[4] = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                              __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (k + u < K) {
-              const double e = (double)f[u] - ps[tt];
-              pd[tt] += e * e;
+          for (int tt = 0; tt < kFusedMaxT; ++tt) {
+            if (tt >= Tn || k >= K) continue;
+            uint2 z = make_uint2(ln_pair(xv[i][tt].x, mu32[tt], r32[tt]),
+                                 ln_pair(xv[i][tt].y, mu32[tt], r32[tt]));
+            // positions past K stay zero
+            if (k + 4 > K) {
+              const int keep = K - k;  // 1 .. 3 valid values
+              if (keep < 2) z.x &= 0xFFFFu;
+              if (keep < 3) z.y = 0u;
+              else z.y &= 0xFFFFu;
             }
+            xv[i][tt] = z;
           }
         }
-        pd[tt] = wave_sum_f64(pd[tt]);
+      }
+      uint32_t m[kFusedMaxT];
+#pragma unroll
+      for (int tt = 0; tt < kFusedMaxT; ++tt) {
+        m[tt] = 0;
+#pragma unroll
+        for (int i = 0; i < Q; ++i) m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], xv[i][tt].x),
+                                                           xv[i][tt].y);
+      }
+      // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
+      // over the waves through LDS (one read per lane and a 16-lane DPP tree).
+      uint32_t pk[kFusedMaxT / 2];
+#pragma unroll
+      for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) {
+        pk[p2] = 0;
+        if (2 * p2 >= Tn) continue;
+        const uint32_t a0 = max(m[2 * p2] & 0xFFFFu, m[2 * p2] >> 16);
+        const uint32_t a1 = max(m[2 * p2 + 1] & 0xFFFFu, m[2 * p2 + 1] >> 16);
+        pk[p2] = wave_max_u16x2(a0 | (a1 << 16));
       }
       if (lane == 0) {
 #pragma unroll
-        for (int tt = 0; tt < kFusedMaxT; ++tt) lndev[wave][tt] = pd[tt];
+        for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) wmax[wave][p2] = pk[p2];
       }
       __syncthreads();
+      uint32_t am2[kFusedMaxT / 2];
+#pragma unroll
+      for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2)
+        am2[p2] = 2 * p2 < Tn ? row16_max_u16x2(lane < W ? wmax[lane][p2] : 0u) : 0u;
+      float s_t[kFusedMaxT];
 #pragma unroll
       for (int tt = 0; tt < kFusedMaxT; ++tt) {
-        mu32[tt] = 0.0f;
-        r32[tt] = 0.0f;
+        s_t[tt] = 0.0f;
         if (tt >= Tn) continue;
-        const double d = row16_sum_f64(lane < W ? lndev[lane][tt] : 0.0);
-        mu32[tt] = (float)ps[tt];
-        r32[tt] = (float)(1.0 / sqrt(d / (double)K + (double)ln_eps));
+        const uint32_t am = (am2[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
+        const float a = fmaxf(__uint_as_float(am << 16), kAbsmaxFloor);
+        s_t[tt] = 127.0f / a;
+        if (tt == t) a_t = a;
       }
+      uint32_t* xs = xq_lds[wave];  // [kFusedMaxT][64] words
+      const bool vq = ((uintptr_t)xq_out % 4 == 0) && (ld_q % 4 == 0);
 #pragma unroll
       for (int i = 0; i < Q; ++i) {
         const int k = (wave + i * W) * kQuadK + 4 * lane;
 #pragma unroll
         for (int tt = 0; tt < kFusedMaxT; ++tt) {
-          if (tt >= Tn || k >= K) continue;
-          uint2 z = make_uint2(ln_pair(xv[i][tt].x, mu32[tt], r32[tt]),
-                               ln_pair(xv[i][tt].y, mu32[tt], r32[tt]));
-          // positions past K stay zero
-          if (k + 4 > K) {
-            const int keep = K - k;  // 1 .. 3 valid values
-            if (keep < 2) z.x &= 0xFFFFu;
-            if (keep < 3) z.y = 0u;
-            else z.y &= 0xFFFFu;
+          if (tt >= Tn) continue;
+          const uint32_t qw = quant4(xv[i][tt].x, xv[i][tt].y, s_t[tt]);
+          xs[tt * 64 + lane] = qw;
+          if (rb == 0 && tt < (int)T && k < K) {
+            int8_t* dst = xq_out + tt * ld_q + k;
+            if (vq && k + 4 <= K) {
+              *reinterpret_cast<uint32_t*>(dst) = qw;
+            } else {
+              for (int u = 0; u < 4 && k + u < K; ++u) dst[u] = (int8_t)(qw >> (8 * u));
+            }
           }
-          xv[i][tt] = z;
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[i][j] = t < kFusedMaxT && tok_ok
+                        ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 +
+                                                        4 * b_chunk<FORM>(g, j))
+                        : v4i{0, 0, 0, 0};
       }
+      if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
     }
-    uint32_t m[kFusedMaxT];
-#pragma unroll
-    for (int tt = 0; tt < kFusedMaxT; ++tt) {
-      m[tt] = 0;
-#pragma unroll
-      for (int i = 0; i < Q; ++i) m[tt] = max_abs_bf16x2(max_abs_bf16x2(m[tt], xv[i][tt].x),
-                                                         xv[i][tt].y);
-    }
-    // Per-token maxima: two tokens per word (16-bit halves), reduced over the wave (DPP), then
-    // over the waves through LDS (one read per lane and a 16-lane DPP tree).
-    uint32_t pk[kFusedMaxT / 2];
-#pragma unroll
-    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) {
-      pk[p2] = 0;
-      if (2 * p2 >= Tn) continue;
-      const uint32_t a0 = max(m[2 * p2] & 0xFFFFu, m[2 * p2] >> 16);
-      const uint32_t a1 = max(m[2 * p2 + 1] & 0xFFFFu, m[2 * p2 + 1] >> 16);
-      pk[p2] = wave_max_u16x2(a0 | (a1 << 16));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2) wmax[wave][p2] = pk[p2];
-    }
-    __syncthreads();
-    uint32_t am2[kFusedMaxT / 2];
-#pragma unroll
-    for (int p2 = 0; p2 < kFusedMaxT / 2; ++p2)
-      am2[p2] = 2 * p2 < Tn ? row16_max_u16x2(lane < W ? wmax[lane][p2] : 0u) : 0u;
-    float s_t[kFusedMaxT];
-#pragma unroll
-    for (int tt = 0; tt < kFusedMaxT; ++tt) {
-      s_t[tt] = 0.0f;
-      if (tt >= Tn) continue;
-      const uint32_t am = (am2[tt >> 1] >> (16 * (tt & 1))) & 0xFFFFu;
-      const float a = fmaxf(__uint_as_float(am << 16), kAbsmaxFloor);
-      s_t[tt] = 127.0f / a;
-      if (tt == t) a_t = a;
-    }
-    uint32_t* xs = xq_lds[wave];  // [kFusedMaxT][64] words
-    const bool vq = ((uintptr_t)xq_out % 4 == 0) && (ld_q % 4 == 0);
+
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
-      const int k = (wave + i * W) * kQuadK + 4 * lane;
+      if (qoff + wave + i * W < nq) {
+        if constexpr (FORM == kFormSparse24) {
 #pragma unroll
-      for (int tt = 0; tt < kFusedMaxT; ++tt) {
-        if (tt >= Tn) continue;
-        const uint32_t qw = quant4(xv[i][tt].x, xv[i][tt].y, s_t[tt]);
-        xs[tt * 64 + lane] = qw;
-        if (rb == 0 && tt < (int)T && k < K) {
-          int8_t* dst = xq_out + tt * ld_q + k;
-          if (vq && k + 4 <= K) {
-            *reinterpret_cast<uint32_t*>(dst) = qw;
-          } else {
-            for (int u = 0; u < 4 && k + u < K; ++u) dst[u] = (int8_t)(qw >> (8 * u));
+          for (int blk = 0; blk < 2; ++blk) {
+            uint32_t a[4];
+            exp_word_to_i8(codes[i][2 * blk], a);
+            acc = smfmac16(a, b[i][2 * blk], b[i][2 * blk + 1], codes[i][2 * blk + 1], acc);
           }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[i][j] = t < kFusedMaxT && tok_ok
-                      ? *reinterpret_cast<const v4i*>(xs + (t < kFusedMaxT ? t : 0) * 64 +
-                                                      4 * b_chunk<FORM>(g, j))
-                      : v4i{0, 0, 0, 0};
-    }
-    if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
-  }
-
-  v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < Q; ++i) {
-    if (wave + i * W < nq) {
-      if constexpr (FORM == kFormSparse24) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          uint32_t a[4];
-          exp_word_to_i8(codes[i][2 * blk], a);
-          acc = smfmac16(a, b[i][2 * blk], b[i][2 * blk + 1], codes[i][2 * blk + 1], acc);
-        }
-      } else {
-        uint32_t a[16];
-        if constexpr (CMP) {
-          const uint32_t sh = codes[i][3];
-          decode_compact<compact_m(FORM)>(mask[i], __builtin_amdgcn_alignbit(codes[i][1], codes[i][0], sh),
-                                          __builtin_amdgcn_alignbit(codes[i][2], codes[i][1], sh),
-                                          L.n, L.csb, clut, a);
         } else {
-          decode<FORM>(L, mask[i], codes[i], a);
-        }
+          uint32_t a[16];
+          if constexpr (CMP) {
+            const uint32_t sh = codes[i][3];
+            const uint32_t lo = __builtin_amdgcn_alignbit(codes[i][1], codes[i][0], sh);
+            const uint32_t hi = __builtin_amdgcn_alignbit(codes[i][2], codes[i][1], sh);
+            decode_compact<compact_m(FORM)>(mask[i], lo, hi, L.n, L.csb, clut, a);
+          } else {
+            decode<FORM>(L, mask[i], codes[i], a);
+          }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+          for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+        }
       }
     }
-  }
+  };
+  run_batch(0, true);
+  for (int qb = 1; qb < nbatch; ++qb) run_batch(qb * W * Q, false);
   const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
   red[wave][lane] = acc;
   __syncthreads();
@@ -485,8 +497,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
     void* __restrict__ y, int64_t ld_y, int out_kind, float ln_eps) {
   gemv_body<FORM, FUSED, XVEC, Q, LN, XBUF>(mask_plane, code_plane, L, (int)L.K, (int)L.quads,
-                                            gamma_p, xin, ld_x, xq_out, ld_q, absmax, T, y, ld_y,
-                                            out_kind, ln_eps);
+                                            (int)(blockDim.x >> 6), gamma_p, xin, ld_x, xq_out,
+                                            ld_q, absmax, T, y, ld_y, out_kind, ln_eps);
 }
 
 }  // namespace

@@ -2,7 +2,7 @@
 // Models", section "The BitLinear Layer", operations 4 and 5). The kernel body is the one the
 // bf16-input kernels use (gemv.hpp); this file is compiled with kernel-argument preloading, and
 // its entry takes the values its first loads need (code plane, activations, quad count, K, leading
-// dimension, token count, a') as leading scalar arguments, so those loads go out without waiting
+// dimension, token count, wave count, a', gamma) as leading scalar arguments, so those loads go out without waiting
 // for a scalar load of the argument block (3.77 -> 3.57 us at T = 1 and 5.64 -> 5.35 us at T = 16
 // on the 2560 -> 6912 shape). The bf16-input kernels keep their own argument order: moving their
 // arguments the same way made them slower.
@@ -14,28 +14,29 @@ namespace {
 template <int FORM, bool XVEC, int Q, bool XBUF>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
     const uint8_t* __restrict__ code_plane, const void* __restrict__ xin, int nq, int K, int ld_x,
-    int T, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
     const uint8_t* __restrict__ mask_plane, Layout L, void* __restrict__ y, int64_t ld_y,
     int out_kind) {
-  gemv_body<FORM, false, XVEC, Q, false, XBUF>(mask_plane, code_plane, L, K, nq, gamma_p, xin,
+  gemv_body<FORM, false, XVEC, Q, false, XBUF>(mask_plane, code_plane, L, K, nq, W, gamma_p, xin,
                                                (int64_t)ld_x, nullptr, 0,
                                                const_cast<float*>(absmax), (int64_t)T, y, ld_y,
                                                out_kind, 0.0f);
 }
 
-// W = min(16, quads) waves of Q = ceil(quads / W) quads; buffer-resource loads (XBUF) for T <= 4.
+// W = min(16, quads) waves of Q = min(3, ceil(quads / W)) quads; past 48 quads the waves take
+// batches of 48 in turn. Buffer-resource loads (XBUF) for T <= 4.
 template <int FORM, bool XVEC>
 hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
                      int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
   const Layout& L = h->L;
   const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
-  const int Q = (int)((L.quads + W - 1) / W);
+  const int Q = (int)std::min<int64_t>(kGemvMaxQ, (L.quads + W - 1) / W);
   const uint8_t* plane = compact_form(FORM) ? h->cplane : h->codes;
 #define SBN_I8(QQ, XB)                                                                         \
   hipLaunchKernelGGL((bitlinear_gemv_i8<FORM, XVEC, QQ, XB>), dim3((unsigned)L.row_blocks),     \
                      dim3(64 * W), 0, s, plane, static_cast<const void*>(xq), (int)L.quads,      \
-                     (int)L.K, (int)ld_q, (int)T, absmax, h->gamma_out(), h->mask, L, y, ld_y,   \
-                     out_kind)
+                     (int)L.K, (int)ld_q, (int)T, W, absmax, h->gamma_out(), h->mask, L, y,      \
+                     ld_y, out_kind)
 #define SBN_I8_Q(QQ)                                                                           \
   do {                                                                                         \
     if (T <= kFusedMaxT) SBN_I8(QQ, true); else SBN_I8(QQ, false);                             \

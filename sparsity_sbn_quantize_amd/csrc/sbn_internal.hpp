@@ -75,7 +75,7 @@ hipError_t launch_outlier_add(const sbn_packed* h, const int8_t* xq, int64_t ld_
                               hipStream_t s);
 hipError_t launch_export_outliers(const sbn_packed* h, uint8_t* pos, uint16_t* val,
                                   hipStream_t s);
-// The int8-input GEMV (T <= 16, quads <= 48), every code form.
+// The int8-input GEMV (T <= 16, any K), every code form.
 hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
