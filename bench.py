@@ -35,7 +35,10 @@ KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
                   "sparsity_sbn_quantize_amd/csrc/sbn_common.hpp",
                   "sparsity_sbn_quantize_amd/csrc/backward.hip",
                   "sparsity_sbn_quantize_amd/csrc/pack.hip",
-                  "sparsity_sbn_quantize_amd/csrc/quantize_act.hip"]
+                  "sparsity_sbn_quantize_amd/csrc/quantize_act.hip",
+                  "sparsity_sbn_quantize_amd/csrc/gemv.hpp",
+                  "sparsity_sbn_quantize_amd/csrc/gemv_i8.hip",
+                  "sparsity_sbn_quantize_amd/csrc/outliers.hip"]
 
 
 def kernel_source_hash() -> str:

@@ -115,7 +115,10 @@ __device__ __forceinline__ void store_out(void* y, int64_t ld_y, int out_kind, i
 // (For more tokens every workgroup would redo a quantization pass over all T x K activations;
 // there the quantize kernel followed by the GEMV is faster.)
 constexpr int kGemvMaxWaves = 16;
-constexpr int kGemvMaxQ = 3;  // quads per wave (template Q <= 3): K <= 16 * 3 * 256 = 12288
+// Quads per wave in one batch (template Q <= 3, so the operands fit in registers): one batch
+// covers K <= 16 * 3 * 256 = 12288; the int8-input GEMV runs ceil(quads / (3 W)) batches past that,
+// the one-kernel bf16 path stays at one batch.
+constexpr int kGemvMaxQ = 3;
 constexpr int kFusedMaxT = 4;  // tokens of the one-kernel quantize-and-multiply path
 
 __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, const v4i& v) {
