@@ -19,8 +19,8 @@
 //   256-K quads each); operands go straight from memory into MFMA registers and the waves' sums
 //   meet once in LDS. With bf16 input (T <= 4) every workgroup also quantizes (optionally after a
 //   parameter-free LayerNorm) the activations it needs.
-//   GEMM (T > 16): a workgroup computes 256 rows x 128 tokens; the 128 x 256 activation tile of
-//   each K step is staged in LDS and shared by the waves; 2:4 runs on the structured-sparse MFMA.
+//   GEMM (T > 16): a workgroup computes 256 rows x 128 (or 64) tokens; the activation tile of each
+//   K step is staged in LDS and shared by the waves; 2:4 runs on the structured-sparse MFMA.
 #include <algorithm>
 
 #include "gemv.hpp"
@@ -28,25 +28,25 @@
 namespace sbn {
 namespace {
 
-// GEMM (T > 16): a workgroup of 4 waves computes 256 rows x 128 tokens; wave w owns 4 row
-// fragments (64 rows) and all 128 tokens. Two workgroups share a CU (two waves per SIMD), so one
-// wave's decode and LDS traffic overlap the other's MFMAs. K advances 256 per step. Each step's
-// 128 x 256 activation tile goes global -> LDS directly (global_load_lds, no registers) into a
-// 2-slot ring, one step ahead, laid out so that every fragment read is free of bank conflicts. K slice
-// j+1 of the wave's row fragments is decoded while the MFMAs of slice j run (two A register
-// sets); bricks are loaded one step ahead. One barrier per step.
+// GEMM (T > 16): a workgroup of 4 waves computes 256 rows x 16 CF tokens (CF = 8: 128 tokens;
+// CF = 4: 64); wave w owns 4 row fragments (64 rows) and all the tile's tokens. Two workgroups
+// share a CU (two waves per SIMD), so one wave's decode and LDS traffic overlap the other's MFMAs.
+// K advances 256 per step. Each step's activation tile goes global -> LDS directly
+// (global_load_lds, no registers) into a 2-slot ring, one step ahead, laid out so that every
+// fragment read is free of bank conflicts. K slice j+1 of the wave's row fragments is decoded while
+// the MFMAs of slice j run (two A register sets); bricks are loaded one step ahead. One barrier per
+// step. CF = 8 reuses each decoded slice for twice as many MFMAs; CF = 4 doubles the tile count of
+// launches that would otherwise leave CUs idle (see the launcher).
 constexpr int kGemmWaves = 4;
 constexpr int kRF = 4;                                  // 16-row fragments per wave
-constexpr int kGemmCF = 8;                              // 16-token fragments per tile
-constexpr int kGemmTok = kGemmCF * 16;                  // 128 tokens per tile
 constexpr int kGemmRowBlocks = kGemmWaves * kRF;        // 16 row fragments (256 rows) per tile
 constexpr int kXBufs = 2;                               // activation ring depth
 constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile (32 KB)
-constexpr int kXLoads = kGemmTok * 16 / kGemmThreads;   // 16-byte pieces per thread per step
-constexpr size_t kGemmSmem = (size_t)kXBufs * kTileBytes;
 
-// Split-K (two workgroups per tile, each half of K) for launches with few tiles. The halves of a
+// LDS of a CF tile: the activation ring, then the tile's a'_t (one float per token).
+constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + cf * 16 * 4; }
+
+// Split-K (two workgroups per tile, each half of K) for launches that have few tiles even at CF = 4. The halves of a
 // tile are adjacent in the XCD order (same L2). Per tile and wave, the first half to finish
 // stores its int32 partial sums in the tile's region of y and raises a flag; the second waits
 // for the flag (a bounded spin: the first is already past its main loop, so it is running), adds
@@ -60,13 +60,18 @@ constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this m
 constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
 
-template <int FORM, bool XVEC>
+template <int FORM, bool XVEC, int CF>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
                     Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
                     int64_t ld_q, const float* __restrict__ absmax, int64_t T,
                     void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t,
                     int ksplit, int* __restrict__ sync) {
+  constexpr int kGemmCF = CF;                             // 16-token fragments per tile
+  constexpr int kGemmTok = CF * 16;                       // tokens per tile
+  constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile
+  constexpr int kXLoads = kGemmTok * 16 / kGemmThreads;   // 16-byte pieces per thread per step
+  constexpr size_t kRing = (size_t)kXBufs * kTileBytes;
   constexpr bool POS = FORM != kFormKept;  // 16 code bytes per lane and quad
   constexpr bool SP = FORM == kFormSparse24;
   constexpr int kBW = POS ? 4 : 6;  // brick words in registers: codes, or mask (2) + codes (4)
@@ -190,12 +195,20 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     for (int cf = 0; cf < kGemmCF; ++cf) acc[rf][cf] = v4i{0, 0, 0, 0};
   const int t_l = lane & 15, g_l = lane >> 4;
 
+  // The tile's activation scales go to LDS with the first operands. The epilogue reads them from
+  // there: a load from memory at that point would wait (vmcnt) for the stores already issued,
+  // which made each 16-token group's stores wait for the previous group's.
+  float* const am_s = reinterpret_cast<float*>(smem + kRing);
+  float am_v = 0.0f;
+  if (out_kind == SBN_OUT_F32 && (int)threadIdx.x < kGemmTok)
+    am_v = absmax[min<int64_t>(t0 + threadIdx.x, T - 1)];
   Bricks b0, b1;
   ASlice a0, a1;
   load_bricks(qb, b0);
   load_x(qb, 0);
   load_bricks(min(qb + 1, nq - 1), b1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // ring slot of step 0 written
+  if ((int)threadIdx.x < kGemmTok) am_s[threadIdx.x] = am_v;
   __syncthreads();
   decode_slice(b0, 0, a0);
 
@@ -234,7 +247,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int cf = 0; cf < kGemmCF; ++cf) {
         __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 40 / CF, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
       }
     }
@@ -281,7 +294,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int cf = 0; cf < kGemmCF; ++cf) {
         __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);    // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 24 / CF, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS read
       }
     }
@@ -386,7 +399,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   for (int cf = 0; cf < kGemmCF; ++cf) {
     const int64_t t = t0 + cf * 16 + t_l;
     if (t >= T) continue;
-    const float step_t = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
+    const float step_t = am_s[cf * 16 + t_l] / 127.0f;
 #pragma unroll
     for (int rf = 0; rf < kRF; ++rf) {
       const int64_t r0 = (rb0 + rf) * 16 + 4 * g_l;
@@ -471,16 +484,33 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           hipStream_t s) {
   const Layout& L = h->L;
   if (T <= 16) return launch_gemv_int8(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);  // gemv_i8.hip
-  hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC>, kGemmSmem);
-  if (e != hipSuccess) return e;
   const int64_t gx = (L.row_blocks + kGemmRowBlocks - 1) / kGemmRowBlocks;
-  const int64_t gy = (T + kGemmTok - 1) / kGemmTok;
+  // 128-token tiles (CF = 8) when they number more than kSplitMaxTiles; otherwise 64-token tiles,
+  // split over K as well if they are still that few. Same-process A/B, 2560 -> 6912 and
+  // 6912 -> 2560 at T = 2048 and the 7B FFN shapes at T = 8192: 64-token tiles are 5-10% slower
+  // where 128-token tiles fill the GPU, and 25% faster on 6912 -> 2560 (320 tiles, 52 us) than
+  // 128-token tiles split over K (320 workgroups, 69 us: the halves' partial-sum exchange alone
+  // cost 16 us).
+  const bool wide = gx * ((T + 127) / 128) > kSplitMaxTiles;
+  const int64_t gy = wide ? (T + 127) / 128 : (T + 63) / 64;
   // y offsets of the split-K handshake are 32-bit buffer offsets
   const bool y_fits = (double)T * (double)ld_y * 4.0 < 2147483647.0;
   const int ksplit = (gx * gy <= kSplitMaxTiles && L.quads >= 8 && y_fits) ? 2 : 1;
-  hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC>), dim3((unsigned)(gx * gy * ksplit)),
-                     dim3(kGemmThreads), kGemmSmem, s, h->mask, h->codes, L, h->gamma_out(), xq,
-                     ld_q, absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, ksplit, h->gemm_sync);
+#define SBN_GEMM(CF)                                                                           \
+  do {                                                                                         \
+    hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC, CF>, gemm_smem(CF));                  \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC, CF>), dim3((unsigned)(gx * gy * ksplit)),     \
+                       dim3(kGemmThreads), gemm_smem(CF), s, h->mask, h->codes, L,              \
+                       h->gamma_out(), xq, ld_q, absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, \
+                       ksplit, h->gemm_sync);                                                  \
+  } while (0)
+  if (wide) {
+    SBN_GEMM(8);
+  } else {
+    SBN_GEMM(4);
+  }
+#undef SBN_GEMM
   return hipGetLastError();
 }
 

@@ -1,0 +1,45 @@
+"""GPU parity of the GEMM's two tile widths (T > 16). Launches whose 128-token tiles number more
+than 256 use them; smaller launches use 64-token tiles (split over K as well while they still
+number at most 256). Integer accumulators equal the oracle's exactly; fp32 outputs follow it within
+the forward's tolerance; the fp32 scale of each token comes from the tile's LDS copy of a'_t."""
+
+import numpy as np
+import pytest
+
+from tests import gpu_util as gu
+from sparsity_sbn_quantize_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, T, K, N):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(4, (T, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    return inputs.f32_to_bf16_bits(x), w
+
+
+def tiles128(T, N):
+    return -(-N // 256) * -(-T // 128)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (3, 8), (8, 16)])
+@pytest.mark.parametrize("T", [1930, 1920])
+def test_tile_width_boundary(n, m, T):
+    """N = 4352 (17 row tiles): T = 1930 gives 272 tiles of 128 tokens, with a 10-token tail;
+    T = 1920 gives 255, so the launch takes 64-token tiles (510 of them, no split)."""
+    N, K = 4352, 1040 - 1040 % m
+    assert (tiles128(T, N) > 256) == (T == 1930)
+    x, w = _case(T + 31 * n + m, T, K, N)
+    g = gu.gpu_forward(x, w, n, m)
+    gu.check_stages(g, x, w, n, m)
+
+
+def test_wide_tiles_unaligned():
+    """128-token tiles with element-wise activation loads (odd leading dimensions of x, w and
+    x_q) and a ragged last row tile (4200 rows)."""
+    T, K, N = 2100, 528, 4200
+    assert tiles128(T, N) > 256
+    x, w = _case(5, T, K, N)
+    g = gu.gpu_forward(x, w, 6, 8, ld_x=K + 3, ld_w=K + 1, ld_q=K + 5)
+    gu.check_stages(g, x, w, 6, 8)

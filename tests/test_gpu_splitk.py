@@ -1,4 +1,4 @@
-"""GPU parity of the split-K GEMM (launches with at most 256 tiles of 256 rows x 128 tokens and
+"""GPU parity of the split-K GEMM (launches with at most 256 tiles of 256 rows x 64 tokens and
 at least 8 K steps run two workgroups per tile, one per half of K, combined through a handshake
 in y). Results must equal the oracle exactly (int32) and to 1e-5 (fp32), every call in a row."""
 
