@@ -56,6 +56,7 @@ constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + 
 // widely (a contiguous share of all tiles' K steps for every resident workgroup, or three
 // workgroups per tile) was measured slower on the 2048- and 8192-token shapes: the partial sums
 // then move about as many bytes as the fp32 output, all at the same moment.
+constexpr int kOutPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: output stores
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
 constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
@@ -395,6 +396,14 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   }
 
   const float gamma = gamma_p[0];
+  // Vector stores go through a buffer resource based at the tile's first token row (offsets below
+  // kGemmTok * ld_y * 4 < 2^31 whenever ld_y < 2^22; otherwise plain global stores), written
+  // through with the system-scope non-temporal policy. Same-process A/B against plain global
+  // stores: 2560 -> 6912 at T = 2048 42.1 -> 39.6 us (2:4: 35.5 -> 32.6), 6912 -> 2560 52.0 ->
+  // 50.6, the 7B FFN shapes at T = 8192 unchanged; without sc1 (sc0 nt) it was slower than plain.
+  const bool ybuf = ld_y < (int64_t{1} << 22);
+  const __amdgpu_buffer_rsrc_t yo = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<int32_t*>(y) + t0 * ld_y, (short)0, 0x7FFFFFFF, kBufDword3);
 #pragma unroll
   for (int cf = 0; cf < kGemmCF; ++cf) {
     const int64_t t = t0 + cf * 16 + t_l;
@@ -405,15 +414,17 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
       const int64_t r0 = (rb0 + rf) * 16 + 4 * g_l;
       const v4i v = acc[rf][cf];
       if (vec_out && r0 + 4 <= L.n_out) {
-        if (out_kind == SBN_OUT_I32_ACC) {
-          *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + r0) = v;
+        v4i o = v;
+        if (out_kind != SBN_OUT_I32_ACC) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = (int)__float_as_uint(__fmul_rn(__fmul_rn((float)v[i], gamma), step_t));
+        }
+        if (ybuf) {
+          __builtin_amdgcn_raw_buffer_store_b128(o, yo, (int)(((t - t0) * ld_y + r0) * 4), 0,
+                                                 kOutPolicy);
         } else {
-          float4 f;
-          f.x = __fmul_rn(__fmul_rn((float)v[0], gamma), step_t);
-          f.y = __fmul_rn(__fmul_rn((float)v[1], gamma), step_t);
-          f.z = __fmul_rn(__fmul_rn((float)v[2], gamma), step_t);
-          f.w = __fmul_rn(__fmul_rn((float)v[3], gamma), step_t);
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + r0) = f;
+          *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + r0) = o;
         }
       } else {
 #pragma unroll

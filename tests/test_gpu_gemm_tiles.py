@@ -43,3 +43,37 @@ def test_wide_tiles_unaligned():
     x, w = _case(5, T, K, N)
     g = gu.gpu_forward(x, w, 6, 8, ld_x=K + 3, ld_w=K + 1, ld_q=K + 5)
     gu.check_stages(g, x, w, 6, 8)
+
+
+@pytest.mark.parametrize("ld_y", [(1 << 22) - 4, (1 << 22) + 4])
+def test_output_row_stride_near_2_22(ld_y):
+    """The vector output stores address the tile's rows from its first token row with 32-bit
+    offsets while ld_y < 2^22 (here up to 127 rows x (2^22 - 4) floats, just under 2^31 bytes),
+    and fall back to plain stores from 2^22 on. 128-token tiles (33024 rows, T = 130: 258 tiles),
+    fp32 and int32 outputs, canaries right of n_out."""
+    import torch
+    from sparsity_sbn_quantize_amd import binding
+    import oracle
+    T, K, N = 130, 64, 33024
+    assert tiles128(T, N) > 256
+    x, w = _case(ld_y % 97, T, K, N)
+    xd = gu.to_dev_bf16(x)
+    q, a = binding.quantize_act(xd)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), 6, 8)
+    codes, _, g = pw.export()
+    acc_ref = oracle.int_matmul(q.cpu().numpy(), codes.cpu().numpy())
+    ybuf = torch.full((T, ld_y), -7.0, dtype=torch.float32, device="cuda")
+    binding.bitlinear(q, a, pw, out="f32", y=ybuf[:, :N])
+    y = ybuf[:, :N].cpu().numpy()
+    canary = ybuf[:, N:N + 64].cpu().numpy()
+    gu.assert_y_close(y, oracle.dequantize(acc_ref, np.float32(g.cpu().numpy()[0]),
+                                           a.cpu().numpy()))
+    assert np.all(canary == -7.0)
+    yi = ybuf.view(torch.int32)
+    yi.fill_(-7)
+    binding.bitlinear(q, a, pw, out="i32", y=yi[:, :N])
+    assert np.array_equal(yi[:, :N].cpu().numpy(), acc_ref)
+    assert np.all(yi[:, N:N + 64].cpu().numpy() == -7)
+    del ybuf, yi
+    pw.free()
+    torch.cuda.synchronize()
