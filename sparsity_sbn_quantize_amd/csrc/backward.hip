@@ -36,6 +36,7 @@ constexpr int kBwTileBytes = kBwTok * kBwStepRows * 2;   // dY tile of one step 
 constexpr int kBwXLoads = kBwTileBytes / 16 / kBwThreads;  // 16-byte pieces per thread per step
 constexpr size_t kBwSmem = 2 * (size_t)kBwTileBytes;
 // Lane offset that lies past every buffer range the dY loads use: such pieces read as zero.
+constexpr int kDxPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: dX stores
 constexpr int kOutOfRange = 0x7FFFFFF0;
 // Largest dY extent (bytes from a tile's first row to the end of the data) of the buffer path.
 constexpr int64_t kMaxBufExtent = 0x7FFF0000;
@@ -204,6 +205,13 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
   // Each lane holds 4 consecutive columns of one token per (cf, tf).
   const float gamma = gamma_p[0];
   const bool vec_out = (((uintptr_t)dx | (uintptr_t)(ld_dx * 4)) & 15) == 0;
+  // Vector stores: a buffer resource based at the tile's first token row (32-bit offsets while
+  // ld_dx < 2^22, plain global stores beyond), written through (sc0 nt sc1). Same-process A/B
+  // against plain global stores on the 7B FFN shapes at T = 8192: 562 -> 549 us (up), 580 -> 577
+  // us (down).
+  const bool dbuf = ld_dx < (int64_t{1} << 22);
+  const __amdgpu_buffer_rsrc_t dro =
+      __builtin_amdgcn_make_buffer_rsrc(dx + t0 * ld_dx, (short)0, 0x7FFFFFFF, kBufDword3);
 #pragma unroll
   for (int tf = 0; tf < kBwTF; ++tf) {
     const int64_t t = t0 + tf * 16 + (lane & 15);
@@ -214,8 +222,15 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
       const v4f v = acc[cf][tf];
       float* const o = dx + t * ld_dx + k0;
       if (vec_out && k0 + 4 <= K) {
-        *reinterpret_cast<float4*>(o) = make_float4(__fmul_rn(v[0], gamma), __fmul_rn(v[1], gamma),
-                                                    __fmul_rn(v[2], gamma), __fmul_rn(v[3], gamma));
+        v4i f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = (int)__float_as_uint(__fmul_rn(v[i], gamma));
+        if (dbuf) {
+          __builtin_amdgcn_raw_buffer_store_b128(f, dro, (int)(((t - t0) * ld_dx + k0) * 4), 0,
+                                                 kDxPolicy);
+        } else {
+          *reinterpret_cast<v4i*>(o) = f;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -150,3 +150,25 @@ def test_bwd_dx_7b_shapes_sampled():
         torch.cuda.synchronize()
         _check(dx, dy, codes.cpu().numpy(), np.float32(gamma.cpu().numpy()[0]), rows=rows)
         pw.free()
+
+
+@pytest.mark.parametrize("ld_dx", [(1 << 22) - 4, (1 << 22) + 4])
+def test_bwd_dx_row_stride_near_2_22(ld_dx):
+    """dX vector stores address the tile's rows from its first token row with 32-bit offsets while
+    ld_dx < 2^22 (here up to 127 rows x (2^22 - 4) floats, just under 2^31 bytes) and fall back to
+    plain stores from 2^22 on; canaries right of K stay untouched."""
+    import torch
+    T, N, K = 130, 264, 512
+    dy, w = _case(ld_dx % 89, T, N, K)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), 6, 8)
+    dxbuf = torch.full((T, ld_dx), 7.0, dtype=torch.float32, device="cuda")
+    binding.bitlinear_bwd_dx(gu.to_dev_bf16(dy), pw, dx=dxbuf[:, :K])
+    codes, _, gamma = pw.export()
+    torch.cuda.synchronize()
+    dx = dxbuf[:, :K].cpu().numpy()
+    canary = dxbuf[:, K:K + 64].cpu().numpy()
+    codes, gamma = codes.cpu().numpy(), np.float32(gamma.cpu().numpy()[0])
+    del dxbuf
+    pw.free()
+    assert np.all(canary == 7.0)
+    _check(dx, dy, codes, gamma)
