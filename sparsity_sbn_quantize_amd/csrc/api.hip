@@ -55,11 +55,9 @@ sbn_status fwd_bf16(const char* name, const sbn_packed* w, const uint16_t* x_bf1
   if (!x_bf16 || !x_q || !x_absmax || (!y && w->L.n_out > 0))
     return fail(SBN_ERR_INVALID_ARG, "%s: null pointer", name);
   const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
+  // (the outlier term, if any, is added inside: in the same launch for one token)
   hipError_t e = sbn::launch_bitlinear_bf16(w, x_bf16, ld_x, T, x_q, ld_q, x_absmax, y, ld_y,
                                             (int)out_kind, ln_eps, (hipStream_t)stream);
-  if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
-    e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
-                                (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, name);
   return SBN_OK;
 }

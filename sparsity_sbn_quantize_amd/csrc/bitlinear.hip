@@ -542,13 +542,72 @@ hipError_t launch_gemv_fused(const sbn_packed* h, const uint16_t* x, int64_t ld_
                                        s);
 }
 
+// The one-token step with the k:256 outlier term in the same launch (bitlinear_gemv_outl).
+template <int FORM>
+hipError_t launch_gemv_outl(const sbn_packed* h, const uint16_t* x, int8_t* xq, int64_t ld_q,
+                            float* absmax, float* y, hipStream_t s) {
+  const Layout& L = h->L;
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, (L.quads + kGemvMaxQ - 1) / kGemvMaxQ);
+  const int Q = (int)((L.quads + W - 1) / W);
+  const size_t smem = gemv_outl_smem(L.K, h->outlier_k);
+#define SBN_GEMV_OUTL(QQ)                                                                      \
+  do {                                                                                         \
+    hipError_t e = allow_smem(bitlinear_gemv_outl<FORM, QQ>, smem);                            \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_gemv_outl<FORM, QQ>), dim3((unsigned)L.row_blocks),            \
+                       dim3(64 * W), smem, s, h->mask, h->codes, L, h->gamma_out(), x, xq,       \
+                       ld_q, absmax, y, h->opos, h->oval, h->outlier_k);                       \
+  } while (0)
+  if (Q == 1) {
+    SBN_GEMV_OUTL(1);
+  } else if (Q == 2) {
+    SBN_GEMV_OUTL(2);
+  } else {
+    SBN_GEMV_OUTL(3);
+  }
+#undef SBN_GEMV_OUTL
+  return hipGetLastError();
+}
+
+hipError_t launch_bitlinear_bf16_plain(const sbn_packed* h, const uint16_t* x, int64_t ld_x,
+                                       int64_t T, int8_t* xq, int64_t ld_q, float* absmax,
+                                       void* y, int64_t ld_y, int out_kind, float ln_eps,
+                                       hipStream_t s);
+
 }  // namespace
 
+// The bf16-input forward, with the k:256 outlier term when the handle has one (fp32 output): in
+// the same launch for one token (no LayerNorm, positional or structured codes, n_out a multiple of
+// 16), otherwise by the outlier kernel after the forward.
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
                                  int out_kind, float ln_eps, hipStream_t s) {
   const Layout& L = h->L;
   if (T == 0) return hipSuccess;
+  const bool outl = h->outlier_k > 0 && out_kind == SBN_OUT_F32 && L.n_out > 0;
+  if (outl && T == 1 && ln_eps <= 0.0f && !h->compact && L.n_out % 16 == 0 &&
+      L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ && (uintptr_t)x % 8 == 0 &&
+      2.0 * (double)(L.K >> 8) * h->outlier_k * (double)L.n_out < 2147483647.0) {
+    float* yf = static_cast<float*>(y);
+    if (L.form == kFormSparse24) return launch_gemv_outl<kFormSparse24>(h, x, xq, ld_q, absmax, yf, s);
+    if (L.form == kFormPositional)
+      return launch_gemv_outl<kFormPositional>(h, x, xq, ld_q, absmax, yf, s);
+    return launch_gemv_outl<kFormKept>(h, x, xq, ld_q, absmax, yf, s);
+  }
+  hipError_t e = launch_bitlinear_bf16_plain(h, x, ld_x, T, xq, ld_q, absmax, y, ld_y, out_kind,
+                                             ln_eps, s);
+  if (e == hipSuccess && outl)
+    e = launch_outlier_add(h, xq, ld_q, absmax, T, static_cast<float*>(y), ld_y, s);
+  return e;
+}
+
+namespace {
+
+hipError_t launch_bitlinear_bf16_plain(const sbn_packed* h, const uint16_t* x, int64_t ld_x,
+                                       int64_t T, int8_t* xq, int64_t ld_q, float* absmax,
+                                       void* y, int64_t ld_y, int out_kind, float ln_eps,
+                                       hipStream_t s) {
+  const Layout& L = h->L;
   if (L.n_out > 0 && T <= kFusedMaxT && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
 #define SBN_FUSED(FF)                                                                          \
@@ -572,6 +631,8 @@ hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t
   if (e != hipSuccess) return e;
   return launch_bitlinear(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
+
+}  // namespace
 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,

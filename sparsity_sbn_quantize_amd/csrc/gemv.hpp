@@ -137,13 +137,23 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
 // LayerNorm): the row comes through a buffer resource and the token count is a compile-time 1.
 // (Every wave taking the absmax over the whole row itself, with no barrier, was measured slower:
 // 6.3 vs 4.8 us, the 4320 waves' requests for the same few KB queue at a few L2 channels.)
-template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
+//
+// OUTL (one-token bf16 step, fp32 output, n_out % 16 == 0): the row block's k:256 outliers are
+// added in the same launch, with the arithmetic of the separate outlier kernel (outliers.hip, 8
+// partial sums per row over groups c, c + 8, ..., position order within a group, partials added in
+// order c = 0 .. 7, then y = fl32(y0 + fl32(o * step))), so both paths give the same bits. The
+// quantized row and the block's outlier planes are staged in dynamic LDS: [K] x_q bytes, then
+// [G k][16] positions, [G k][16] bf16 values, [8][16] partial sums. Each thread issues three
+// straight-line loads for the planes with the bricks (G k <= 16 nq <= 64 W pieces of each).
+template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF, bool OUTL = false>
 __device__ __forceinline__ void gemv_body(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
     const Layout& L, const int K, const int nq, const int W, const float* __restrict__ gamma_p,
     const void* __restrict__ xin, int64_t ld_x, int8_t* __restrict__ xq_out, int64_t ld_q,
     float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y, int out_kind,
-    float ln_eps) {
+    float ln_eps, const uint8_t* __restrict__ opos = nullptr,
+    const uint16_t* __restrict__ oval = nullptr, int KO = 0) {
+  static_assert(!OUTL || (FUSED && XBUF && !LN), "outliers fused only into the one-token step");
   __shared__ v4i red[kGemvMaxWaves][64];
   __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT / 2];  // token pairs, 16 bits each
   __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
@@ -206,6 +216,25 @@ __device__ __forceinline__ void gemv_body(
     if constexpr (CMP) {
       for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
     }
+  };
+  // Outlier planes of this row block (OUTL): piece i of the positions is the 16 rows' bytes of
+  // (group, slot) i, pieces of the values are halves (8 rows) of theirs; out-of-range pieces read 0.
+  extern __shared__ __attribute__((aligned(16))) uint8_t gemv_dyn[];
+  const int G = K >> 8;
+  const int npos = OUTL ? G * KO : 0;
+  v4i opc[3];
+  auto load_outliers = [&]() {
+    const int64_t n_out = L.n_out;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(opos + rb * 16), (short)0, (int)(npos * n_out - rb * 16), kBufDword3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(oval + rb * 16), (short)0, (int)(2 * (npos * n_out - rb * 16)), kBufDword3);
+    const int p0 = threadIdx.x, p1 = threadIdx.x + 64 * W;
+    opc[0] = __builtin_amdgcn_raw_buffer_load_b128(pr, p0 < npos ? p0 * (int)n_out : (1 << 30), 0, 0);
+    opc[1] = __builtin_amdgcn_raw_buffer_load_b128(
+        vr, p0 < 2 * npos ? 2 * (p0 >> 1) * (int)n_out + 16 * (p0 & 1) : (1 << 30), 0, 0);
+    opc[2] = __builtin_amdgcn_raw_buffer_load_b128(
+        vr, p1 < 2 * npos ? 2 * (p1 >> 1) * (int)n_out + 16 * (p1 & 1) : (1 << 30), 0, 0);
   };
   v4i acc = v4i{0, 0, 0, 0};
   // int8 input: the waves take batches of W * Q quads in turn, so any K fits; bf16 input (whose
@@ -286,6 +315,7 @@ __device__ __forceinline__ void gemv_body(
       // scheduling barrier keeps the compiler from issuing the bricks first.
       __builtin_amdgcn_sched_barrier(0);
       load_bricks(0);
+      if constexpr (OUTL) load_outliers();
       build_lut();  // published by a barrier below
       if constexpr (LN) {
         // Parameter-free LayerNorm of every token row (as sbn_layernorm_quantize_act): fp64 sum
@@ -415,6 +445,9 @@ __device__ __forceinline__ void gemv_body(
           if (tt >= Tn) continue;
           const uint32_t qw = quant4(xv[i][tt].x, xv[i][tt].y, s_t[tt]);
           xs[tt * 64 + lane] = qw;
+          if constexpr (OUTL) {
+            if (k < K) reinterpret_cast<uint32_t*>(gemv_dyn)[k >> 2] = qw;  // K % 256 == 0
+          }
           if (rb == 0 && tt < (int)T && k < K) {
             int8_t* dst = xq_out + tt * ld_q + k;
             if (vq && k + 4 <= K) {
@@ -464,12 +497,57 @@ __device__ __forceinline__ void gemv_body(
   for (int qb = 1; qb < nbatch; ++qb) run_batch(qb * W * Q, false);
   const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
   red[wave][lane] = acc;
+  uint8_t* const pos_s = gemv_dyn + K;             // [G k][16]
+  uint16_t* const val_s = reinterpret_cast<uint16_t*>(pos_s + 16 * npos);  // [G k][16]
+  float* const part_s = reinterpret_cast<float*>(val_s + 16 * npos);       // [8][16]
+  if constexpr (OUTL) {
+    const int p0 = threadIdx.x, p1 = threadIdx.x + 64 * W;
+    if (p0 < npos) *reinterpret_cast<v4i*>(pos_s + 16 * p0) = opc[0];
+    if (p0 < 2 * npos) *reinterpret_cast<v4i*>(val_s + 8 * p0) = opc[1];
+    if (p1 < 2 * npos) *reinterpret_cast<v4i*>(val_s + 8 * p1) = opc[2];
+  }
   __syncthreads();
+  if constexpr (OUTL) {
+    // unit (c, r): partial sum c of row r of the block
+    for (int u = threadIdx.x; u < 128; u += 64 * W) {
+      const int r = u & 15, c = u >> 4;
+      float o = 0.0f;
+      for (int gg = c; gg < G; gg += 8) {
+        for (int j = 0; j < KO; ++j) {
+          const int gj = gg * KO + j;
+          const float v = __uint_as_float((uint32_t)val_s[16 * gj + r] << 16);
+          const int8_t xv8 = reinterpret_cast<const int8_t*>(gemv_dyn)[gg * 256 + pos_s[16 * gj + r]];
+          o = __fadd_rn(o, __fmul_rn((float)xv8, v));
+        }
+      }
+      part_s[c * 16 + r] = o;
+    }
+    __syncthreads();
+  }
   if (wave != 0 || !tok_ok) return;
   // (A fully unrolled sum over all 16 slots, masked, measured slower than this loop.)
   v4i sum = red[0][lane];
   for (int w = 1; w < W; ++w) sum += red[w][lane];
   const int64_t row0 = rb * 16 + 4 * g;
+  if constexpr (OUTL) {
+    // y = fl32( fl32(fl32(fl32(acc) * gamma) * step) + fl32(o * step) ), o summed as above
+    float* const yr = reinterpret_cast<float*>(y) + row0;
+    float f[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float o = part_s[4 * g + i];
+#pragma unroll
+      for (int cc = 1; cc < 8; ++cc) o = __fadd_rn(o, part_s[cc * 16 + 4 * g + i]);
+      f[i] = __fadd_rn(__fmul_rn(__fmul_rn((float)sum[i], gamma), step), __fmul_rn(o, step));
+    }
+    if (((uintptr_t)yr % 16) == 0) {
+      *reinterpret_cast<float4*>(yr) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yr[i] = f[i];
+    }
+    return;
+  }
   const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < L.n_out;
   if (vec) {  // the lane's four consecutive rows in one store
     if (out_kind == SBN_OUT_I32_ACC) {
@@ -502,6 +580,24 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
   gemv_body<FORM, FUSED, XVEC, Q, LN, XBUF>(mask_plane, code_plane, L, (int)L.K, (int)L.quads,
                                             (int)(blockDim.x >> 6), gamma_p, xin, ld_x, xq_out,
                                             ld_q, absmax, T, y, ld_y, out_kind, ln_eps);
+}
+
+// The one-token bf16 step with the k:256 outlier term (fp32 output; planes [G k][n_out]).
+template <int FORM, int Q>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_outl(
+    const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane, Layout L,
+    const float* __restrict__ gamma_p, const void* __restrict__ xin, int8_t* __restrict__ xq_out,
+    int64_t ld_q, float* __restrict__ absmax, void* __restrict__ y,
+    const uint8_t* __restrict__ opos, const uint16_t* __restrict__ oval, int KO) {
+  gemv_body<FORM, true, true, Q, false, true, true>(
+      mask_plane, code_plane, L, (int)L.K, (int)L.quads, (int)(blockDim.x >> 6), gamma_p, xin,
+      (int64_t)L.K, xq_out, ld_q, absmax, 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f, opos, oval,
+      KO);
+}
+
+// Dynamic LDS of bitlinear_gemv_outl.
+inline size_t gemv_outl_smem(int64_t K, int KO) {
+  return (size_t)K + (size_t)(K >> 8) * (size_t)KO * 48 + 8 * 16 * sizeof(float);
 }
 
 }  // namespace

@@ -184,3 +184,46 @@ def test_outlier_decode_shape():
     assert np.array_equal(r["codes"], ref["codes"])
     _check_y(r, 16, w.shape[1])
     assert np.array_equal(r["yb"], r["y"])
+
+
+@pytest.mark.parametrize("k", [4, 8, 16])
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (3, 8), (8, 16)])
+@pytest.mark.parametrize("N,K", [(64, 256), (304, 2560), (96, 12288), (48, 4096)])
+def test_outlier_term_in_the_one_token_step(k, n, m, N, K):
+    """One token, n_out a multiple of 16: the bf16-input step adds the outlier term in the same
+    launch (one to 48 quads, 1 to 16 waves, every code form). It sums in the outlier kernel's
+    order, so its output equals the int8 path's (forward, then the outlier kernel) bit for bit,
+    and both stay within the fp32 bound."""
+    w = _w(N * 3 + K + 7 * k + n, N, K)
+    x = _x(K + k, 1, K)
+    r = _fwd(w, x, n, m, k, 1)
+    q_ref, a_ref = oracle.quantize_act(x)
+    assert np.array_equal(r["q"], q_ref) and np.array_equal(r["a"], a_ref)
+    _check_y(r, k, K)
+    assert np.array_equal(r["yb"], r["y"])
+
+
+def test_outlier_term_in_the_one_token_step_unaligned_y_and_fallbacks():
+    """An output row 4 bytes off 16-byte alignment (element-wise stores in the one-kernel step),
+    n_out not a multiple of 16 and the LayerNorm step (both: forward, then the outlier kernel)."""
+    import torch
+    K, N, n, m, k = 1024, 160, 6, 8, 16
+    w = _w(77, N, K)
+    x = _x(78, 1, K)
+    xd = gu.to_dev_bf16(x)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m, outliers=k)
+    q, a = binding.quantize_act(xd)
+    y_ref = binding.bitlinear(q, a, pw, out="f32")
+    ybuf = torch.full((N + 1,), -7.0, dtype=torch.float32, device="cuda")
+    binding.bitlinear_bf16(xd, pw, y=ybuf[1:].view(1, N))
+    yl, ql, al = binding.bitlinear_bf16(xd, pw, ln_eps=1e-5)
+    yl_ref = binding.bitlinear(ql, al, pw, out="f32")
+    torch.cuda.synchronize()
+    assert ybuf[0].item() == -7.0
+    assert np.array_equal(ybuf[1:].cpu().numpy(), y_ref.cpu().numpy()[0])
+    assert np.array_equal(yl.cpu().numpy(), yl_ref.cpu().numpy())
+    pw.free()
+    w2 = _w(79, 72, K)
+    r = _fwd(w2, x, n, m, k, 1)
+    _check_y(r, k, K)
+    assert np.array_equal(r["yb"], r["y"])
