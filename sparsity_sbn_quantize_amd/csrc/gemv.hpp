@@ -120,6 +120,11 @@ constexpr int kGemvMaxWaves = 16;
 // the one-kernel bf16 path stays at one batch.
 constexpr int kGemvMaxQ = 3;
 constexpr int kFusedMaxT = 4;  // tokens of the one-kernel quantize-and-multiply path
+// Cache policy of the brick loads (read once per call): nt. Same-process A/B on the 2560 -> 6912
+// decode shape, against the default policy: one-kernel step 4.49 -> 4.16 us, with the LayerNorm
+// 6.58 -> 5.82 us, the int8 GEMV unchanged (3.34 us); sc1 alone changed nothing. The outlier
+// planes keep the default policy: nt there made the one-token outlier step slower (8.49 -> 9.06).
+constexpr int kPlaneLoad = 2;
 
 __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, const v4i& v) {
   if (vec && k + 16 <= K) {
@@ -187,15 +192,15 @@ __device__ __forceinline__ void gemv_body(
       const int q = qoff + wave + i * W;
       if constexpr (CMP) {
         // the lane's nonzero mask, and the three words holding its csb sign bits
-        const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, q * cq, 0);
+        const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, q * cq, kPlaneLoad);
         const int sbit = lane * L.csb;
         const v3u sg = __builtin_amdgcn_raw_buffer_load_b96(
-            crs, kCompactMaskBytes + 4 * (sbit >> 5), q * cq, 0);
+            crs, kCompactMaskBytes + 4 * (sbit >> 5), q * cq, kPlaneLoad);
         mask[i][0] = mk[0]; mask[i][1] = mk[1];
         codes[i][0] = sg[0]; codes[i][1] = sg[1]; codes[i][2] = sg[2];
         codes[i][3] = (uint32_t)(sbit & 31);
       } else if constexpr (FORM != kFormKept && (FUSED || XBUF)) {
-        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, q * 1024, 0);
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16, q * 1024, kPlaneLoad);
         codes[i][0] = (uint32_t)c[0]; codes[i][1] = (uint32_t)c[1];
         codes[i][2] = (uint32_t)c[2]; codes[i][3] = (uint32_t)c[3];
         mask[i][0] = mask[i][1] = 0;
