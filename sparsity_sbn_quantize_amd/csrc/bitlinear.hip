@@ -435,9 +435,9 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   }
 }
 
-// Launches the GEMV with W waves and Q = ceil(quads / W) quads per wave: W = min(16, quads) for
-// int8 input; W = ceil(quads / 3) for bf16 input, whose workgroup barriers then wait for fewer
-// waves (same-process A/B on the 2560 -> 6912 shape, one-kernel step at T = 1: 4.45 us at three
+// Launches the bf16-input GEMV (the int8-input GEMV is launched from gemv_i8.hip) with
+// W = ceil(quads / 3) waves and Q = ceil(quads / W) quads per wave, so that its workgroup barriers
+// wait for fewer waves (same-process A/B on the 2560 -> 6912 shape, one-kernel step at T = 1: 4.45 us at three
 // quads per wave, 4.72 at one, 4.60 at two, 4.65 at four, 4.93 at five; with the LayerNorm 6.46 vs
 // 7.56). The int8 kernel, which has no barrier before its products, is fastest at one quad per
 // wave (3.77 vs 3.85 us at two).
@@ -455,7 +455,7 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
                      compact_form(FORM) ? h->cplane : h->codes, L,                                 \
                      h->gamma_out(), x, ld_x, xq_out, ld_q, absmax, T, y, ld_y, out_kind, ln_eps)
 #define SBN_GEMV_Q(QQ)                                                                        \
-  if (FUSED) {                                                                                \
+  if constexpr (FUSED) {                                                                      \
     if (ln_eps > 0.0f) SBN_GEMV(QQ, FUSED, false);                                            \
     else if (XVEC && T == 1) SBN_GEMV(QQ, false, FUSED);                                      \
     else SBN_GEMV(QQ, false, false);                                                          \

@@ -24,7 +24,9 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
 }
 
 // W = min(16, quads) waves of Q = min(3, ceil(quads / W)) quads; past 48 quads the waves take
-// batches of 48 in turn. Buffer-resource loads (XBUF) for T <= 4.
+// batches of 48 in turn. Buffer-resource loads (XBUF) for every T <= 16: with non-temporal brick
+// loads they are faster at 16 tokens too (same-process A/B, 2560 -> 6912: 4.95 vs 5.60 us for the
+// branchy loads; before the nt policy the branchy loads had been faster there).
 template <int FORM, bool XVEC>
 hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
                      int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
@@ -37,10 +39,7 @@ hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const 
                      dim3(64 * W), 0, s, plane, static_cast<const void*>(xq), (int)L.quads,      \
                      (int)L.K, (int)ld_q, (int)T, W, absmax, h->gamma_out(), h->mask, L, y,      \
                      ld_y, out_kind)
-#define SBN_I8_Q(QQ)                                                                           \
-  do {                                                                                         \
-    if (T <= kFusedMaxT) SBN_I8(QQ, true); else SBN_I8(QQ, false);                             \
-  } while (0)
+#define SBN_I8_Q(QQ) SBN_I8(QQ, true)
   if (Q == 1) {
     SBN_I8_Q(1);
   } else if (Q == 2) {
