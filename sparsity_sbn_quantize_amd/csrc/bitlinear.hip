@@ -16,9 +16,10 @@
 // plain loop over its mask.
 //
 //   GEMV (T <= 16): one workgroup per 16-row fragment row, its waves split K (one to three
-//   256-K quads each); operands go straight from memory into MFMA registers and the waves' sums
-//   meet once in LDS. With bf16 input (T <= 4) every workgroup also quantizes (optionally after a
-//   parameter-free LayerNorm) the activations it needs.
+//   256-K quads each, in batches past 48 quads with int8 input); operands go straight from memory
+//   into MFMA registers and the waves' sums meet once in LDS. With bf16 input (T <= 4, K <= 12288)
+//   every workgroup also quantizes (optionally after a parameter-free LayerNorm) the activations
+//   it needs; for one token it can also add the k:256 outlier term.
 //   GEMM (T > 16): a workgroup computes 256 rows x 128 (or 64) tokens; the activation tile of each
 //   K step is staged in LDS and shared by the waves; 2:4 runs on the structured-sparse MFMA.
 #include <algorithm>
