@@ -137,8 +137,8 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
 // LN (bf16 input only): parameter-free LayerNorm before the quantization. XBUF, int8 input: brick
 // and activation loads through buffer resources, straight-line; measured faster for a few tokens
 // (4.35 vs 4.58 us at T = 1 on the 2560 -> 6912 decode shape), and with non-temporal brick loads
-// at 16 tokens too (4.95 vs 5.60 us), so the int8 launcher always takes it. The bf16-input kernel
-// loads its bricks through the buffer
+// at 16 tokens too when the launch is one batch (4.95 vs 5.60 us); the int8 launcher takes it for
+// T <= 4 and for one-batch launches. The bf16-input kernel loads its bricks through the buffer
 // resource too (4.95 vs 5.06 us per one-kernel step at T = 1). XBUF, bf16 input (T = 1, no
 // LayerNorm): the row comes through a buffer resource and the token count is a compile-time 1.
 // (Every wave taking the absmax over the whole row itself, with no barrier, was measured slower:

@@ -24,9 +24,13 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
 }
 
 // W = min(16, quads) waves of Q = min(3, ceil(quads / W)) quads; past 48 quads the waves take
-// batches of 48 in turn. Buffer-resource loads (XBUF) for every T <= 16: with non-temporal brick
-// loads they are faster at 16 tokens too (same-process A/B, 2560 -> 6912: 4.95 vs 5.60 us for the
-// branchy loads; before the nt policy the branchy loads had been faster there).
+// batches of 48 in turn. Buffer-resource loads (XBUF) for T <= 4, and for up to 16 tokens when the
+// launch is one batch; same-process A/B with non-temporal brick loads, T = 8 / 16 (us):
+//   6912 x 2560   XBUF 3.95 / 5.0   branchy 4.37 / 5.7
+//   2560 x 6912   XBUF 5.1  / 6.4   branchy 5.6  / 6.8
+//   4096 x 11008  XBUF 6.9  / 9.2   branchy 7.5  / 9.7
+//   5120 x 13824  XBUF 16.3 / 24.2  branchy 15.3 / 21.2   (two batches)
+//   8192 x 28672  XBUF 25.9 / 40.0  branchy 26.2 / 37.9   (three batches)
 template <int FORM, bool XVEC>
 hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
                      int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
@@ -39,7 +43,11 @@ hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const 
                      dim3(64 * W), 0, s, plane, static_cast<const void*>(xq), (int)L.quads,      \
                      (int)L.K, (int)ld_q, (int)T, W, absmax, h->gamma_out(), h->mask, L, y,      \
                      ld_y, out_kind)
-#define SBN_I8_Q(QQ) SBN_I8(QQ, true)
+  const bool xbuf = T <= kFusedMaxT || L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ;
+#define SBN_I8_Q(QQ)                                                                           \
+  do {                                                                                         \
+    if (xbuf) SBN_I8(QQ, true); else SBN_I8(QQ, false);                                        \
+  } while (0)
   if (Q == 1) {
     SBN_I8_Q(1);
   } else if (Q == 2) {
