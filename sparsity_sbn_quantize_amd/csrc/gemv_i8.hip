@@ -23,9 +23,9 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
                                                out_kind, 0.0f);
 }
 
-// W = min(16, quads) waves of Q = min(3, ceil(quads / W)) quads; past 48 quads the waves take
-// batches of 48 in turn. Buffer-resource loads (XBUF) for T <= 4, and for up to 16 tokens when the
-// launch is one batch; same-process A/B with non-temporal brick loads, T = 8 / 16 (us):
+// W waves (min(16, quads); for T > 4 see below) of Q = min(3, ceil(quads / W)) quads; past W Q
+// quads the waves take batches of W Q in turn. Buffer-resource loads (XBUF) for T <= 4, and for
+// up to 16 tokens when the launch is one batch; same-process A/B with non-temporal brick loads, T = 8 / 16 (us):
 //   6912 x 2560   XBUF 3.95 / 5.0   branchy 4.37 / 5.7
 //   2560 x 6912   XBUF 5.1  / 6.4   branchy 5.6  / 6.8
 //   4096 x 11008  XBUF 6.9  / 9.2   branchy 7.5  / 9.7
@@ -35,7 +35,15 @@ template <int FORM, bool XVEC>
 hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
                      int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
   const Layout& L = h->L;
-  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  // T > 4: the fewest quads per wave that fit (at most three), then the fewest waves at that
+  // count, so that few wave slots go empty. Same-process A/B at T = 8 / 16: 2560 x 6912 (27 quads;
+  // 14 waves of two instead of 16) 5.06 / 6.39 -> 4.78 / 5.96 us; 4096 x 11008 (43 quads; 15 waves
+  // of three instead of 16) 6.81 / 9.19 -> 6.64 / 8.87 us; unchanged for 10 quads and for batches.
+  int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  if (T > kFusedMaxT) {
+    const int64_t q = std::min<int64_t>(kGemvMaxQ, (L.quads + kGemvMaxWaves - 1) / kGemvMaxWaves);
+    W = (int)std::min<int64_t>(kGemvMaxWaves, (L.quads + q - 1) / q);
+  }
   const int Q = (int)std::min<int64_t>(kGemvMaxQ, (L.quads + W - 1) / W);
   const uint8_t* plane = compact_form(FORM) ? h->cplane : h->codes;
 #define SBN_I8(QQ, XB)                                                                         \
