@@ -440,8 +440,11 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 // W = ceil(quads / 3) waves and Q = ceil(quads / W) quads per wave, so that its workgroup barriers
 // wait for fewer waves (same-process A/B on the 2560 -> 6912 shape, one-kernel step at T = 1: 4.45 us at three
 // quads per wave, 4.72 at one, 4.60 at two, 4.65 at four, 4.93 at five; with the LayerNorm 6.46 vs
-// 7.56). The int8 kernel, which has no barrier before its products, is fastest at one quad per
-// wave (3.77 vs 3.85 us at two).
+// 7.56). Rechecked with non-temporal brick loads: three quads per wave stays fastest on the
+// decode shape (4.2 vs 4.4 at two, 4.6 at one) and on 6912 -> 2560; on 4096 -> 11008 at 2:4 (16
+// quads) two per wave measured faster (5.48 vs 5.85 us), so no single count fits every shape. The
+// int8 kernel, which has no barrier before its products, is fastest at one quad per wave (3.77 vs
+// 3.85 us at two).
 template <int FORM, bool FUSED, bool XVEC>
 hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
                        int64_t ld_q, float* absmax, int64_t T, void* y, int64_t ld_y,
