@@ -477,6 +477,105 @@ def compact_unpack(data: np.ndarray, n: int, m: int, k: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
+# Combinatorial mask rank: the metadata sizes the pages print (0.75 bits/element for 2:4, 0.875 for
+# 8:16; [8:16] abstract, Sparse-BitNet "Sparse-BitNet" section) are ceil(log2 C(m, n)) / m, the
+# width of a fixed-size index of the n-of-m choice. Each group's choice is written as its rank in
+# the combinatorial number system (colexicographic order of the kept positions, the textbook
+# bijection between n-subsets of {0..m-1} and 0 .. C(m, n) - 1), then its n kept codes.
+# ----------------------------------------------------------------------------------------------
+
+def rank_bits(n: int, m: int) -> int:
+    """Bits of a group's rank: ceil(log2 C(m, n)) (0 when n == m: one choice)."""
+    c = math.comb(m, n)
+    return (c - 1).bit_length()
+
+
+def rank_row_bytes(n: int, m: int, k: int) -> int:
+    """Bytes per row of the rank encoding: rank_bits + 2n bits per group, padded to a byte."""
+    return ((k // m) * (rank_bits(n, m) + 2 * n) + 7) // 8
+
+
+def mask_rank(positions) -> int:
+    """Rank of an n-subset (ascending positions c_0 < ... < c_{n-1}) in the combinatorial number
+    system: sum over i of C(c_i, i + 1)."""
+    return sum(math.comb(c, i + 1) for i, c in enumerate(positions))
+
+
+def mask_unrank(r: int, n: int, m: int) -> list:
+    """Inverse of mask_rank: the ascending positions of rank r (0 <= r < C(m, n)). Greedy from the
+    largest element: c_{i-1} is the largest c with C(c, i) <= the remaining rank."""
+    if not 0 <= r < math.comb(m, n):
+        raise ValueError("rank out of range")
+    out = []
+    for i in range(n, 0, -1):
+        c = i - 1
+        while c + 1 < m and math.comb(c + 1, i) <= r:
+            c += 1
+        r -= math.comb(c, i)
+        out.append(c)
+    return out[::-1]
+
+
+def rank_pack(codes: np.ndarray, keep: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Rank encoding of an n:m pack, per row, LSB first. Group g owns bits
+    [g (R + 2n), (g + 1)(R + 2n)), R = rank_bits(n, m): first the rank of its keep mask, then the
+    two's-complement low two bits of its n kept codes by ascending position (0 -> 00, +1 -> 01,
+    -1 -> 11, as in the 2-bit code stream of rpf_pack). Returns uint8 [n_out][rank_row_bytes]."""
+    codes = np.asarray(codes, dtype=np.int8)
+    keep = np.asarray(keep, dtype=bool)
+    n_out, k = codes.shape
+    check_pattern(n, m, k)
+    groups = k // m
+    R = rank_bits(n, m)
+    per = R + 2 * n
+    bits = np.zeros((n_out, groups * per), dtype=np.uint8)
+    for row in range(n_out):
+        for g in range(groups):
+            sel = np.flatnonzero(keep[row, g * m:(g + 1) * m])
+            if sel.size != n:
+                raise ValueError("a group does not keep exactly n positions")
+            r = mask_rank(sel.tolist())
+            base = g * per
+            for b in range(R):
+                bits[row, base + b] = (r >> b) & 1
+            for j, p in enumerate(sel):
+                two = int(codes[row, g * m + p]) & 3
+                bits[row, base + R + 2 * j] = two & 1
+                bits[row, base + R + 2 * j + 1] = two >> 1
+    out = np.packbits(bits, axis=1, bitorder="little")
+    if out.shape[1] < rank_row_bytes(n, m, k):  # k == 0
+        out = np.zeros((n_out, rank_row_bytes(n, m, k)), dtype=np.uint8)
+    return out
+
+
+def rank_unpack(data: np.ndarray, n: int, m: int, k: int):
+    """Inverse of rank_pack: (codes int8 [n_out][K], keep bool [n_out][K]). Rejects ranks out of
+    range, the code 10 and nonzero padding bits."""
+    data = np.asarray(data, dtype=np.uint8)
+    n_out = data.shape[0]
+    groups = k // m
+    R = rank_bits(n, m)
+    per = R + 2 * n
+    allbits = np.unpackbits(data, axis=1, bitorder="little")
+    if np.any(allbits[:, groups * per:]):
+        raise ValueError("nonzero padding bits")
+    codes = np.zeros((n_out, k), dtype=np.int8)
+    keep = np.zeros((n_out, k), dtype=bool)
+    for row in range(n_out):
+        for g in range(groups):
+            b = allbits[row, g * per:(g + 1) * per].astype(np.int64)
+            r = int(sum(int(b[i]) << i for i in range(R)))
+            pos = mask_unrank(r, n, m)
+            for j, p in enumerate(pos):
+                two = int(b[R + 2 * j]) | (int(b[R + 2 * j + 1]) << 1)
+                if two == 2:
+                    raise ValueError("code 10 is never written")
+                codes[row, g * m + p] = -1 if two == 3 else two
+                keep[row, g * m + p] = True
+    return codes, keep
+
+
+# ----------------------------------------------------------------------------------------------
 # Metadata size: [8:16] abstract (0.875 vs 0.75 bits/element).
 # ----------------------------------------------------------------------------------------------
 

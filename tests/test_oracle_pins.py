@@ -5,6 +5,7 @@ the metadata sizes the pages print, a pure-Python brute force, closed-form zero 
 invariants, special cases that reduce to textbook definitions, and symmetries.
 """
 
+import itertools
 import json
 import math
 import os
@@ -997,3 +998,125 @@ def test_outlier_forward_against_dense_product():
             p = gi * 256 + int(r["opos"][rr, gi, j])
             s += float(q[t, p]) * float(oracle.bf16_to_f32(r["oval"][rr, gi, j]))
     assert math.isclose(f["y"][t, rr], s * float(a[t]) / 127.0, rel_tol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# Combinatorial mask rank (the pages' metadata sizes: 0.75 bits/element for 2:4, 0.875 for 8:16)
+# ------------------------------------------------------------------------------------------------
+
+# The six 2-of-4 choices in colexicographic order (by largest position, then the next), written out
+# by hand: their ranks are 0 .. 5.
+RANK_2OF4 = [((0, 1), 0), ((0, 2), 1), ((1, 2), 2), ((0, 3), 3), ((1, 3), 4), ((2, 3), 5)]
+RANK_PATTERNS = [(2, 4), (1, 4), (3, 4), (4, 4), (6, 8), (3, 8), (4, 8), (8, 8), (8, 16), (5, 16),
+                 (12, 16), (16, 16)]
+
+
+def test_rank_bits_match_the_printed_metadata_sizes():
+    """ceil(log2 C(m, n)) / m reproduces the printed 0.75 (2:4) and 0.875 (8:16) bits per element;
+    with the 2-bit kept codes a group costs 1.75 and 1.875 bits per weight; a dense group needs no
+    rank."""
+    assert oracle.rank_bits(2, 4) / 4 == 0.75 and oracle.rank_bits(8, 16) / 16 == 0.875
+    assert oracle.rank_bits(2, 4) / 4 == oracle.combinatorial_metadata_bits(2, 4)
+    assert (oracle.rank_bits(2, 4) + 4) / 4 == 1.75 and (oracle.rank_bits(8, 16) + 16) / 16 == 1.875
+    for m in (4, 8, 16):
+        assert oracle.rank_bits(m, m) == 0
+    assert oracle.rank_row_bytes(8, 16, 32) == 8 and oracle.rank_row_bytes(2, 4, 8) == 2
+
+
+def _rank_pins_fail(rank, unrank) -> bool:
+    try:
+        for subset, r in RANK_2OF4:
+            if rank(list(subset)) != r or list(unrank(r, 2, 4)) != list(subset):
+                return True
+        for n, m in RANK_PATTERNS:
+            subsets = sorted(itertools.combinations(range(m), n), key=lambda c: c[::-1])  # colex
+            for r, c in enumerate(subsets):
+                if rank(list(c)) != r or list(unrank(r, n, m)) != list(c):
+                    return True
+    except (ValueError, IndexError):
+        return True
+    return False
+
+
+def test_rank_is_the_colex_bijection():
+    """Every n-of-m subset (up to 12870 for 8:16) gets its index in the colex-sorted list of all
+    subsets, and unrank inverts it."""
+    assert not _rank_pins_fail(oracle.mask_rank, oracle.mask_unrank)
+
+
+def _rank_brute(codes, keep, n, m):
+    """The rank stream built another way: each group's index in the colex-sorted subset list, then
+    its kept codes' low two bits, accumulated into one integer per row."""
+    n_out, k = codes.shape
+    R = (math.comb(m, n) - 1).bit_length()
+    subsets = {c: i for i, c in enumerate(sorted(itertools.combinations(range(m), n),
+                                                 key=lambda c: c[::-1]))}
+    nbytes = ((k // m) * (R + 2 * n) + 7) // 8
+    out = np.zeros((n_out, nbytes), dtype=np.uint8)
+    for row in range(n_out):
+        acc, shift = 0, 0
+        for g in range(k // m):
+            sel = tuple(int(i) for i in np.flatnonzero(keep[row, g * m:(g + 1) * m]))
+            acc |= subsets[sel] << shift
+            shift += R
+            for p in sel:
+                acc |= (int(codes[row, g * m + p]) & 3) << shift
+                shift += 2
+        out[row] = np.frombuffer(acc.to_bytes(nbytes, "little"), dtype=np.uint8)
+    return out
+
+
+def _rank_pack_pins_fail(pack) -> bool:
+    rng = np.random.default_rng(5)
+    for n, m in RANK_PATTERNS:
+        for k in (m, 3 * m, 64 + m):
+            w = rng.standard_normal((5, k)).astype(np.float32)
+            ref = oracle.pack_nm_ternary(w, n, m)
+            got = pack(ref["codes"], ref["keep"], n, m)
+            if got.shape != (5, oracle.rank_row_bytes(n, m, k)):
+                return True
+            if not np.array_equal(got, _rank_brute(ref["codes"], ref["keep"], n, m)):
+                return True
+    return False
+
+
+def test_rank_pack_against_brute_force_and_roundtrip():
+    assert not _rank_pack_pins_fail(oracle.rank_pack)
+    rng = np.random.default_rng(6)
+    for n, m in RANK_PATTERNS:
+        w = rng.standard_normal((7, 4 * m + 64)).astype(np.float32)
+        ref = oracle.pack_nm_ternary(w, n, m)
+        data = oracle.rank_pack(ref["codes"], ref["keep"], n, m)
+        codes, keep = oracle.rank_unpack(data, n, m, w.shape[1])
+        assert np.array_equal(codes, ref["codes"]) and np.array_equal(keep, ref["keep"])
+
+
+def test_rank_pins_catch_mutants():
+    """Lexicographic ranks, MSB-first rank bits and codes written before the rank all fail."""
+    def lex_rank(pos):
+        m = 16 if max(pos) >= 8 else (8 if max(pos) >= 4 else 4)
+        return list(itertools.combinations(range(m), len(pos))).index(tuple(pos))
+
+    assert _rank_pins_fail(lex_rank, oracle.mask_unrank)
+
+    def msb_first(codes, keep, n, m):
+        R = oracle.rank_bits(n, m)
+        data = oracle.rank_pack(codes, keep, n, m)
+        bits = np.unpackbits(data, axis=1, bitorder="little")
+        per = R + 2 * n
+        for g in range(codes.shape[1] // m):
+            bits[:, g * per:g * per + R] = bits[:, g * per:g * per + R][:, ::-1]
+        return np.packbits(bits, axis=1, bitorder="little")
+
+    def codes_first(codes, keep, n, m):
+        R = oracle.rank_bits(n, m)
+        data = oracle.rank_pack(codes, keep, n, m)
+        bits = np.unpackbits(data, axis=1, bitorder="little")
+        per = R + 2 * n
+        for g in range(codes.shape[1] // m):
+            seg = bits[:, g * per:(g + 1) * per].copy()
+            bits[:, g * per:(g + 1) * per] = np.concatenate([seg[:, R:], seg[:, :R]], axis=1)
+        return np.packbits(bits, axis=1, bitorder="little")
+
+    assert _rank_pack_pins_fail(msb_first)
+    assert _rank_pack_pins_fail(codes_first)
