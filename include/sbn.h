@@ -256,6 +256,21 @@ sbn_status sbn_packed_export_outliers(const sbn_packed* w, uint8_t* positions, u
 sbn_status sbn_packed_export_compact(const sbn_packed* w, uint8_t* bytes, void* stream);
 
 /*
+ * Export of the last pack's codes in the rank encoding, enqueued on `stream` (any handle, any
+ * code form). The pages print n:m metadata sizes of 0.75 bits per element for 2:4 and 0.875 for
+ * 8:16 ("From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights with Variance
+ * Correction", abstract): R = ceil(log2 C(m, n)) bits per group of m, the width of a fixed-size
+ * index of the group's n-of-m choice. Per row a bit stream, LSB first, padded to
+ * rank_row_bytes = ceil((K/m)(R + 2n)/8): group g at bits [g(R + 2n), (g+1)(R + 2n)) holds the
+ * rank of its keep mask in the combinatorial number system (colex order: the sum, over the i-th
+ * kept position c counted from 1 by ascending position, of C(c, i)), then the two's-complement
+ * low two bits of its n kept codes by ascending position (0 -> 00, +1 -> 01, -1 -> 11). 2:4 and
+ * 8:16 take 1.75 and 1.875 bits per weight. The GEMV does not read this form.
+ *   bytes     [n_out][rank_row_bytes] uint8 out (device); every byte is written.
+ */
+sbn_status sbn_packed_export_rank(const sbn_packed* w, uint8_t* bytes, void* stream);
+
+/*
  * Keep-mask changes of the handle's last pack: the number of positions whose keep bit differs from
  * the pack before it (the first pack of a handle compares against an empty mask, so it counts
  * every kept position). flips / (n_out * K) is the mask flip rate r_t of Sparse-BitNet, Figure 3
@@ -276,6 +291,7 @@ typedef struct {
   size_t compact_bytes;                  /* bytes of the compact plane the GEMV streams */
   int compact;                           /* the last pack wrote the compact form */
   int outlier_k;                         /* k of the last pack's k:256 outliers (0: none) */
+  size_t rank_row_bytes;                 /* rank export row size, ceil((K/m)(R + 2n)/8) */
 } sbn_packed_desc;
 
 /* Describes a handle; `out` is a host pointer. */

@@ -35,7 +35,8 @@ class PackedDesc(ctypes.Structure):
                 ("mask_row_bytes", ctypes.c_size_t), ("rpf_bytes", ctypes.c_size_t),
                 ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t),
                 ("compact_row_bytes", ctypes.c_size_t), ("compact_bytes", ctypes.c_size_t),
-                ("compact", ctypes.c_int), ("outlier_k", ctypes.c_int)]
+                ("compact", ctypes.c_int), ("outlier_k", ctypes.c_int),
+                ("rank_row_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -57,6 +58,7 @@ _SIGNATURES = {
     "sbn_packed_export": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "sbn_packed_export_rpf": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_export_compact": (ctypes.c_int, [_P, _P, _P]),
+    "sbn_packed_export_rank": (ctypes.c_int, [_P, _P, _P]),
     "sbn_packed_export_outliers": (ctypes.c_int, [_P, _P, _P, _P]),
     "sbn_packed_query": (ctypes.c_int, [_P, ctypes.POINTER(PackedDesc)]),
     "sbn_packed_mask_flips": (ctypes.c_int, [_P, _P, _P]),
@@ -226,6 +228,15 @@ class PackedWeight:
         dev = torch.device("cuda", torch.cuda.current_device())
         out = torch.zeros((self.n_out, d.compact_row_bytes), dtype=torch.uint8, device=dev)
         check(lib().sbn_packed_export_compact(self.handle, _ptr(out), _stream(stream)))
+        return out
+
+    def export_rank(self, stream=None):
+        """The codes in the rank encoding (uint8 [n_out][rank_row_bytes], device)."""
+        import torch
+        d = self.query()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        out = torch.full((self.n_out, d.rank_row_bytes), 0xA5, dtype=torch.uint8, device=dev)
+        check(lib().sbn_packed_export_rank(self.handle, _ptr(out), _stream(stream)))
         return out
 
     def export_outliers(self, stream=None):

@@ -409,6 +409,15 @@ sbn_status sbn_packed_export_compact(const sbn_packed* w, uint8_t* bytes, void* 
   return SBN_OK;
 }
 
+sbn_status sbn_packed_export_rank(const sbn_packed* w, uint8_t* bytes, void* stream) {
+  if (!w) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_rank: handle is null");
+  if (!bytes && w->L.n_out > 0)
+    return fail(SBN_ERR_INVALID_ARG, "sbn_packed_export_rank: bytes is null");
+  hipError_t e = sbn::launch_export_rank(w, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_export_rank launch");
+  return SBN_OK;
+}
+
 sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   if (!w || !out) return fail(SBN_ERR_INVALID_ARG, "sbn_packed_query: null pointer");
   out->n_out = w->L.n_out;
@@ -425,6 +434,9 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   out->compact_bytes = w->cplane_bytes - sbn::kCompactSlack;
   out->compact = w->compact ? 1 : 0;
   out->outlier_k = w->outlier_k;
+  out->rank_row_bytes =
+      (size_t)(((w->L.K / w->L.m) * (sbn::rank_bits((int)w->L.n, (int)w->L.m) + 2 * w->L.n) + 7) /
+               8);
   return SBN_OK;
 }
 

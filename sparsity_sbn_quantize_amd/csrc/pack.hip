@@ -652,6 +652,87 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
   return hipGetLastError();
 }
 
+// Rank encoding (export): per group, the rank of its keep mask in the combinatorial number system
+// (colex order of the kept positions: sum over the i-th kept position c of C(c, i), i from 1),
+// R = ceil(log2 C(m, n)) bits, then its n kept codes' low two bits by ascending position; rows LSB
+// first, padded to a byte. One thread per row and 128 positions (two bricks): its 128 / m groups
+// take (128 / m)(R + 2n) bits, a whole number of bytes for m in {4, 8, 16}, so threads write
+// disjoint bytes and the last thread of a row writes the padding.
+namespace {
+
+__device__ __forceinline__ uint32_t binom16(int c, int i) {
+  if (i > c) return 0u;
+  uint32_t r = 1u;
+  for (int j = 1; j <= i; ++j) r = r * (uint32_t)(c - i + j) / (uint32_t)j;  // exact, c < 16
+  return r;
+}
+
+__global__ __launch_bounds__(256) void export_rank(Layout L, const uint8_t* mask_plane,
+                                                   const uint8_t* code_plane, int R,
+                                                   int64_t row_bytes, uint8_t* __restrict__ out) {
+  const int64_t nchunks = (L.K + 127) / 128;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= L.n_out * nchunks) return;
+  const int64_t row = idx / nchunks, chunk = idx % nchunks;
+  const int m = L.m, n = L.n, per = R + 2 * n;
+  uint8_t* dst = out + row * row_bytes + chunk * (128 / m) * per / 8;
+  uint64_t acc = 0;
+  int nb = 0;
+  auto put = [&](uint32_t v, int bits) {  // bits <= 16
+    acc |= (uint64_t)v << nb;
+    nb += bits;
+    while (nb >= 8) {
+      *dst++ = (uint8_t)acc;
+      acc >>= 8;
+      nb -= 8;
+    }
+  };
+  for (int b = 0; b < 2; ++b) {
+    const int64_t brick = chunk * 2 + b;
+    const int64_t k0 = brick * kBrickK;
+    if (k0 >= L.K) break;
+    uint32_t mask[2], dec[16];
+    decode_brick(L, mask_plane, code_plane, row, brick, mask, dec);
+    const int groups = (int)(min<int64_t>(kBrickK, L.K - k0) / m);
+    for (int g = 0; g < groups; ++g) {
+      uint32_t r = 0u;
+      int i = 0;
+      for (int p = 0; p < m; ++p) {
+        const int pos = g * m + p;
+        if (!L.has_mask || ((mask[pos >> 5] >> (pos & 31)) & 1u)) r += binom16(p, ++i);
+      }
+      put(r, R);
+      for (int p = 0; p < m; ++p) {
+        const int pos = g * m + p;
+        if (!L.has_mask || ((mask[pos >> 5] >> (pos & 31)) & 1u))
+          put((dec[pos >> 2] >> (8 * (pos & 3))) & 3u, 2);
+      }
+    }
+  }
+  if (nb > 0) *dst = (uint8_t)acc;  // the row's last byte: padding bits are zero
+}
+
+}  // namespace
+
+int rank_bits(int n, int m) {
+  uint64_t c = 1;
+  for (int j = 1; j <= n; ++j) c = c * (uint64_t)(m - n + j) / (uint64_t)j;  // C(m, n)
+  int b = 0;
+  while ((uint64_t{1} << b) < c) ++b;
+  return b;
+}
+
+hipError_t launch_export_rank(const sbn_packed* h, uint8_t* out, hipStream_t s) {
+  const Layout& L = h->L;
+  const int64_t total = L.n_out * ((L.K + 127) / 128);
+  if (total == 0) return hipSuccess;
+  const int R = rank_bits((int)L.n, (int)L.m);
+  const int64_t row_bytes = ((L.K / L.m) * (R + 2 * L.n) + 7) / 8;
+  hipLaunchKernelGGL(export_rank, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, L,
+                     h->mask, h->codes, R, row_bytes, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_export(const sbn_packed* h, int8_t* codes, uint8_t* keep, float* gamma,
                          hipStream_t s) {
   const Layout& L = h->L;

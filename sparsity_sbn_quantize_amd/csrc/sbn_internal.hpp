@@ -69,6 +69,8 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s);
 hipError_t launch_export_compact(const sbn_packed* h, uint8_t* out, hipStream_t s);
+int rank_bits(int n, int m);  // ceil(log2 C(m, n))
+hipError_t launch_export_rank(const sbn_packed* h, uint8_t* out, hipStream_t s);
 hipError_t launch_outlier_select(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
 hipError_t launch_outlier_add(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                               const float* absmax, int64_t T, float* y, int64_t ld_y,

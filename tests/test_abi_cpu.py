@@ -23,6 +23,7 @@ def test_exports_match_header(lib):
                              "sbn_bitlinear_fwd_bf16", "sbn_bitlinear_fwd_ln_bf16",
                              "sbn_bitlinear_bwd_dx", "sbn_free",
                              "sbn_packed_export", "sbn_packed_export_rpf", "sbn_packed_export_compact",
+                             "sbn_packed_export_rank",
                              "sbn_packed_export_outliers",
                              "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error"}
@@ -85,6 +86,7 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_packed_query(None, None) == ERR_INVALID
     assert lib.sbn_packed_mask_flips(None, None, None) == ERR_INVALID
     assert lib.sbn_packed_export_compact(None, None, None) == ERR_INVALID
+    assert lib.sbn_packed_export_rank(None, None, None) == ERR_INVALID
     assert lib.sbn_packed_export_outliers(None, None, None, None) == ERR_INVALID
     h = ctypes.c_void_p(0)
     for k in (1, 3, 5, 32):  # outliers per 256 must be 4, 8 or 16
