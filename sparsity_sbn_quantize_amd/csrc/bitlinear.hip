@@ -220,6 +220,10 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   // during group 3); after group 3 the bricks of step q+2 are loaded into bcur. Before the
   // closing barrier each wave waits for its step-(q+1) activation pieces: only the brick loads
   // issued after them may still be in flight.
+  // Schedule of a dense step: per token fragment, its 4 MFMAs, 24 / CF VALU instructions of the
+  // next slice's decode, one LDS read. Same-process A/B of the VALU count per group (CF = 8):
+  // 3 against 5 took 6912 -> 2560 at T = 2048 from 50.5 to 49.0 us and the 7B down projection at
+  // T = 8192 from 275 to 273 us; 4, 6 and 8 were no better; the other shapes did not change.
   auto step = [&](int q, int slot, Bricks& bcur, const Bricks& bnext) {
     // Unconditional, so that the step is straight-line code and the compiler's counter waits for
     // the brick registers stay exact: past the last step the tile's range is empty (reads are
@@ -249,7 +253,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int cf = 0; cf < kGemmCF; ++cf) {
         __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 40 / CF, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 24 / CF, 0);  // VALU (A/B: 3 per group)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
       }
     }
