@@ -251,6 +251,20 @@ def run_decode(gpu, args, T=1, with_cpu=True):
             variants["compact bytes per weight"] = pv[0].query().compact_bytes / (N * K)
         for p in pv:
             p.free()
+    # The rank encoding (an export of the same packs, read by no kernel): time per export into one
+    # buffer, and its bytes per weight.
+    rrb = pws[0].query().rank_row_bytes
+    rank_out = gpu.torch.empty((N, rrb), dtype=gpu.torch.uint8, device="cuda")
+    lib = gpu.b.lib()
+
+    def rank_export(i):
+        gpu.b.check(lib.sbn_packed_export_rank(pws[i % R].handle, gpu.b._ptr(rank_out),
+                                               gpu.b._stream(None)))
+
+    g = gpu.graph(rank_export, args.steps)
+    g.replay()
+    variants["rank export"] = gpu.time_graph(g) / args.steps * 1e3
+    variants["rank bytes per weight"] = rrb * N / (N * K)
     ms_step = ms / args.steps
     if fused:
         step_bytes = fused_bytes(T, K, N, n, m)

@@ -660,12 +660,21 @@ hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStr
 // disjoint bytes and the last thread of a row writes the padding.
 namespace {
 
-__device__ __forceinline__ uint32_t binom16(int c, int i) {
-  if (i > c) return 0u;
-  uint32_t r = 1u;
-  for (int j = 1; j <= i; ++j) r = r * (uint32_t)(c - i + j) / (uint32_t)j;  // exact, c < 16
-  return r;
+// C(c, i) for c < 16, i <= 16 (Pascal's rule), in constant memory: the rank is a sum of table reads.
+struct BinomTable {
+  uint16_t v[16][17];
+};
+constexpr BinomTable make_binom_table() {
+  BinomTable t{};
+  for (int c = 0; c < 16; ++c) {
+    t.v[c][0] = 1;
+    for (int i = 1; i <= 16; ++i) t.v[c][i] = c == 0 ? 0 : (uint16_t)(t.v[c - 1][i - 1] + t.v[c - 1][i]);
+  }
+  return t;
 }
+__constant__ BinomTable kBinom = make_binom_table();
+
+__device__ __forceinline__ uint32_t binom16(int c, int i) { return kBinom.v[c][i]; }
 
 __global__ __launch_bounds__(256) void export_rank(Layout L, const uint8_t* mask_plane,
                                                    const uint8_t* code_plane, int R,
