@@ -618,8 +618,8 @@ def main():
         record_traffic(args.record_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
-              "part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     gpu = Gpu()
     if args.profile_copy:
