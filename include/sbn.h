@@ -138,8 +138,8 @@ sbn_status sbn_pack_nm_ternary(const float* w_latent, int64_t n_out, int64_t K, 
  * y = fl32(y_ternary + fl32(o * fl32(a'/127))), o = the fp32 sum, in a fixed order, of
  * x_q[t][position] * value over the row's outliers (each product is exact); the order is the same
  * on every path, so sbn_bitlinear_fwd and sbn_bitlinear_fwd_bf16 give the same bits. For one
- * token, no LayerNorm, n_out a multiple of 16 and no SBN_PACK_COMPACT, sbn_bitlinear_fwd_bf16 adds
- * the term in its single launch; otherwise a second launch adds it. SBN_OUT_I32_ACC
+ * token, n_out a multiple of 16, K <= 12288 and no SBN_PACK_COMPACT (and, for the bf16 entry, no
+ * LayerNorm), both forwards add the term in the GEMV's launch; otherwise a second launch adds it. SBN_OUT_I32_ACC
  * returns the ternary accumulators only; sbn_bitlinear_bwd_dx rejects such a handle
  * (SBN_ERR_UNSUPPORTED: outliers are a post-training, inference-only variant). Needs
  * K % 256 == 0 (else SBN_ERR_UNSUPPORTED).

@@ -298,11 +298,17 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
   if (!x_q || !y || (out_kind == SBN_OUT_F32 && !x_absmax))
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: null pointer");
   const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
-  hipError_t e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
-                                       (hipStream_t)stream);
-  if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
-    e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
-                                (hipStream_t)stream);
+  hipError_t e;
+  if (out_kind == SBN_OUT_F32 && sbn::gemv_int8_outl_fits(w, x_q, T)) {
+    // one token: the outlier term in the GEMV's launch
+    e = sbn::launch_gemv_int8_outl(w, x_q, x_absmax, static_cast<float*>(y), (hipStream_t)stream);
+  } else {
+    e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
+                              (hipStream_t)stream);
+    if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
+      e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
+                                  (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd launch");
   return SBN_OK;
 }

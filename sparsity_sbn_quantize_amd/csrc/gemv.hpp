@@ -144,11 +144,12 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
 // (Every wave taking the absmax over the whole row itself, with no barrier, was measured slower:
 // 6.3 vs 4.8 us, the 4320 waves' requests for the same few KB queue at a few L2 channels.)
 //
-// OUTL (one-token bf16 step, fp32 output, n_out % 16 == 0): the row block's k:256 outliers are
+// OUTL (one token, fp32 output, n_out % 16 == 0, one batch): the row block's k:256 outliers are
 // added in the same launch, with the arithmetic of the separate outlier kernel (outliers.hip, 8
 // partial sums per row over groups c, c + 8, ..., position order within a group, partials added in
 // order c = 0 .. 7, then y = fl32(y0 + fl32(o * step))), so both paths give the same bits. The
-// quantized row and the block's outlier planes are staged in dynamic LDS: [K] x_q bytes, then
+// quantized row (bf16 input: the quantized pieces; int8 input: the B operands of token 0, stored
+// after the products) and the block's outlier planes are staged in dynamic LDS: [K] x_q bytes, then
 // [G k][16] positions, [G k][16] bf16 values, [8][16] partial sums. Each thread issues three
 // straight-line loads for the planes with the bricks (G k <= 16 nq <= 64 W pieces of each).
 template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF, bool OUTL = false>
@@ -159,7 +160,7 @@ __device__ __forceinline__ void gemv_body(
     float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y, int out_kind,
     float ln_eps, const uint8_t* __restrict__ opos = nullptr,
     const uint16_t* __restrict__ oval = nullptr, int KO = 0) {
-  static_assert(!OUTL || (FUSED && XBUF && !LN), "outliers fused only into the one-token step");
+  static_assert(!OUTL || (XBUF && !LN && (FUSED || XVEC)), "outliers: one-token launches only");
   __shared__ v4i red[kGemvMaxWaves][64];
   __shared__ uint32_t wmax[kGemvMaxWaves][kFusedMaxT / 2];  // token pairs, 16 bits each
   __shared__ double lnsum[FUSED ? kGemvMaxWaves : 1][kFusedMaxT];
@@ -267,6 +268,8 @@ __device__ __forceinline__ void gemv_body(
             b[i][j] =
                 __builtin_amdgcn_raw_buffer_load_b128(xr, voff, (qoff + wave + i * W) * kQuadK, 0);
           }
+        // the outlier planes after the activations, so waiting for these waits for no plane
+        if constexpr (OUTL) load_outliers();
       } else {
         const int8_t* xrow = reinterpret_cast<const int8_t*>(xin) + (tok_ok ? t : 0) * ld_x;
 #pragma unroll
@@ -495,6 +498,20 @@ __device__ __forceinline__ void gemv_body(
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[i][j], acc);
+        }
+      }
+    }
+    if constexpr (OUTL && !FUSED) {
+      // token 0's activation bytes of this wave's quads into the row copy (one batch: qoff = 0)
+      if (t == 0) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+          const int q = wave + i * W;
+          if (q < nq) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<v4i*>(gemv_dyn + q * kQuadK + 16 * b_chunk<FORM>(g, j)) = b[i][j];
+          }
         }
       }
     }

@@ -23,6 +23,46 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
                                                out_kind, 0.0f);
 }
 
+// The one-token int8 GEMV with the k:256 outlier term in the same launch (fp32 output; planes
+// [G k][n_out]); the term's arithmetic is that of the separate outlier kernel (gemv.hpp, OUTL).
+template <int FORM, int Q>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_outl(
+    const uint8_t* __restrict__ code_plane, const void* __restrict__ xin, int nq, int K, int W,
+    const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    const uint8_t* __restrict__ mask_plane, Layout L, void* __restrict__ y,
+    const uint8_t* __restrict__ opos, const uint16_t* __restrict__ oval, int KO) {
+  gemv_body<FORM, false, true, Q, false, true, true>(
+      mask_plane, code_plane, L, K, nq, W, gamma_p, xin, (int64_t)K, nullptr, 0,
+      const_cast<float*>(absmax), 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f, opos, oval, KO);
+}
+
+template <int FORM>
+hipError_t launch_i8_outl(const sbn_packed* h, const int8_t* xq, const float* absmax, float* y,
+                          hipStream_t s) {
+  const Layout& L = h->L;
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  const int Q = (int)std::min<int64_t>(kGemvMaxQ, (L.quads + W - 1) / W);
+  const size_t smem = gemv_outl_smem(L.K, h->outlier_k);
+#define SBN_I8_OUTL(QQ)                                                                        \
+  do {                                                                                         \
+    hipError_t e = allow_smem(bitlinear_gemv_i8_outl<FORM, QQ>, smem);                         \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_gemv_i8_outl<FORM, QQ>), dim3((unsigned)L.row_blocks),         \
+                       dim3(64 * W), smem, s, h->codes, static_cast<const void*>(xq),          \
+                       (int)L.quads, (int)L.K, W, absmax, h->gamma_out(), h->mask, L,           \
+                       static_cast<void*>(y), h->opos, h->oval, h->outlier_k);                  \
+  } while (0)
+  if (Q == 1) {
+    SBN_I8_OUTL(1);
+  } else if (Q == 2) {
+    SBN_I8_OUTL(2);
+  } else {
+    SBN_I8_OUTL(3);
+  }
+#undef SBN_I8_OUTL
+  return hipGetLastError();
+}
+
 // W waves (min(16, quads); for T > 4 see below) of Q = min(3, ceil(quads / W)) quads; past W Q
 // quads the waves take batches of W Q in turn. Buffer-resource loads (XBUF) for T <= 4, and for
 // up to 16 tokens when the launch is one batch; same-process A/B with non-temporal brick loads, T = 8 / 16 (us):
@@ -86,6 +126,20 @@ hipError_t launch_i8_form(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
 }
 
 }  // namespace
+
+bool gemv_int8_outl_fits(const sbn_packed* h, const int8_t* xq, int64_t T) {
+  const Layout& L = h->L;
+  return h->outlier_k > 0 && T == 1 && !h->compact && L.n_out > 0 && L.n_out % 16 == 0 &&
+         L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ && (uintptr_t)xq % 16 == 0 &&
+         L.K % 16 == 0 && 2.0 * (double)(L.K >> 8) * h->outlier_k * (double)L.n_out < 2147483647.0;
+}
+
+hipError_t launch_gemv_int8_outl(const sbn_packed* h, const int8_t* xq, const float* absmax,
+                                 float* y, hipStream_t s) {
+  if (h->L.form == kFormSparse24) return launch_i8_outl<kFormSparse24>(h, xq, absmax, y, s);
+  if (h->L.form == kFormPositional) return launch_i8_outl<kFormPositional>(h, xq, absmax, y, s);
+  return launch_i8_outl<kFormKept>(h, xq, absmax, y, s);
+}
 
 hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,

@@ -70,6 +70,11 @@ hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             hipStream_t s);
 hipError_t launch_export_compact(const sbn_packed* h, uint8_t* out, hipStream_t s);
 int rank_bits(int n, int m);  // ceil(log2 C(m, n))
+// One-token int8 GEMV with the k:256 outlier term in the same launch (gemv_i8.hip), and whether a
+// call fits it (outliers, T = 1, fp32 output checked by the caller, n_out % 16 == 0, one batch).
+bool gemv_int8_outl_fits(const sbn_packed* h, const int8_t* xq, int64_t T);
+hipError_t launch_gemv_int8_outl(const sbn_packed* h, const int8_t* xq, const float* absmax,
+                                 float* y, hipStream_t s);
 hipError_t launch_export_rank(const sbn_packed* h, uint8_t* out, hipStream_t s);
 hipError_t launch_outlier_select(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
 hipError_t launch_outlier_add(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
