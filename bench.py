@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,6 +30,9 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0   # MI355X dense INT8 MFMA
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LN_EPS = 1e-5             # LayerNorm epsilon of the timed LayerNorm variants
+REPEATS = 5               # timed replays per measurement; the median is reported
+KERNEL_LAUNCHES = 200     # launches per graph when a kernel is timed on its own (>= 100)
+SLEEP_CYCLES = 2_000_000  # GPU busy wait before each timed replay (covers host enqueue latency)
 METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GEMV)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
@@ -121,16 +125,76 @@ class Gpu:
         torch.cuda.synchronize()
         return g
 
-    def time_graph(self, g):
-        """Milliseconds of one replay, between HIP events on the replaying stream."""
+    def time_graph(self, g, reps=REPEATS):
+        """Milliseconds of one replay, between HIP events on the replaying stream: the median of
+        `reps` replays. Before each, a GPU-side busy wait keeps the stream occupied while the host
+        enqueues the events and the replay, so that host launch latency is not timed."""
         torch = self.torch
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s.record()
+        times = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(SLEEP_CYCLES)
+            s.record()
+            g.replay()
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        return statistics.median(times)
+
+    def time_launches(self, fn, launches):
+        """Milliseconds per launch of fn: a graph of `launches` calls, replayed once untimed, then
+        the median of REPEATS timed replays divided by the launch count."""
+        g = self.graph(fn, launches)
         g.replay()
-        e.record()
-        e.synchronize()
-        return s.elapsed_time(e)
+        return self.time_graph(g) / launches
+
+
+def measure_ceilings(gpu, small_bytes):
+    """The box's own ceilings (include/sbn_ceilings.h): a streaming read of 2 GiB (HBM), a read of
+    `small_bytes` as one launch (the decode step's size; rotated over the 2 GiB buffer, so it comes
+    from HBM), an INT8 MFMA loop with no memory traffic, and an empty kernel's cost per launch in a
+    graph. Each is the median of REPEATS timed replays."""
+    import ctypes
+    torch, b = gpu.torch, gpu.b
+    lib = b.lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    big = 2 << 30
+    buf = torch.zeros(big // 4, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    small = (small_bytes + 4095) // 4096 * 4096
+    slots = big // small
+
+    def read_all(i):
+        b.check(lib.sbn_ceiling_stream_read(ctypes.c_void_p(base), big, 0xFFFFFFFF, b._ptr(sink),
+                                            b._stream(None)))
+
+    def read_small(i):
+        b.check(lib.sbn_ceiling_stream_read(ctypes.c_void_p(base + (i % slots) * small), small,
+                                            0xFFFFFFFF, b._ptr(sink), b._stream(None)))
+
+    ops = ctypes.c_double(0.0)
+    waves, iters = 256 * 8, 4096
+
+    def mfma(i):
+        b.check(lib.sbn_ceiling_mfma_i8(iters, waves, b._ptr(sink), ctypes.byref(ops),
+                                        b._stream(None)))
+
+    def empty(i):
+        b.check(lib.sbn_ceiling_empty(b._stream(None)))
+
+    read_ms = gpu.time_launches(read_all, 5)
+    small_ms = gpu.time_launches(read_small, KERNEL_LAUNCHES)
+    mfma_ms = gpu.time_launches(mfma, 5)
+    empty_ms = gpu.time_launches(empty, KERNEL_LAUNCHES)
+    del buf
+    return {"hbm_read_GBps": big / (read_ms * 1e-3) / 1e9, "hbm_read_bytes": big,
+            "small_read_us": small_ms * 1e3, "small_read_bytes": small,
+            "small_read_GBps": small / (small_ms * 1e-3) / 1e9,
+            "int8_mfma_TOPS": ops.value / (mfma_ms * 1e-3) / 1e12,
+            "empty_kernel_us": empty_ms * 1e3,
+            "note": "measured on this GPU: streaming read, one read launch of the decode step's "
+                    "size, INT8 MFMA loop, empty kernel (per launch in a graph)"}
 
 
 def cpu_threads() -> int:
@@ -214,12 +278,14 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     assert torch.equal(y, y_two), "one-call step differs from quantize + forward"
     y_eager = y.clone()
     gw = gpu.graph(step, args.warmup) if args.warmup > 0 else None
-    gs = gpu.graph(step, args.steps)
+    # Exactly K steps per timed replay; REPEATS graphs over disjoint runs of the rotated copies,
+    # so that no replay finds its weights in the last-level cache; the median is reported.
+    gss = [gpu.graph(lambda i, o=r * args.steps: step(o + i), args.steps) for r in range(REPEATS)]
     if gw is not None:
         gw.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = gpu.time_graph(gs)
+    ms = statistics.median(gpu.time_graph(g, reps=1) for g in gss)
     wall = time.perf_counter() - t0
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
     timings = {}
@@ -227,9 +293,7 @@ def run_decode(gpu, args, T=1, with_cpu=True):
                      ("quantize_act+bitlinear_gemv", two_call),
                      ("layernorm_quantize_act", ln_quant_only),
                      ("bitlinear_gemv (layernorm + quantize fused)", ln_step)):
-        g = gpu.graph(fn, args.steps)
-        g.replay()
-        timings[name] = gpu.time_graph(g) / args.steps
+        timings[name] = gpu.time_launches(fn, max(args.steps, KERNEL_LAUNCHES))
     # Pack variants on the same weights: the compact plane (GEMV reads nonzero masks + signs)
     # and 16:256 outliers (the step plus the outlier term); fewer rotated copies of each
     variants = {}
@@ -244,9 +308,7 @@ def run_decode(gpu, args, T=1, with_cpu=True):
             gpu.b.bitlinear(q, a, pv[i % Rv], out="f32", y=y)
 
         for name, fn in ((f"step ({tag})", vstep), (f"int8 forward ({tag})", vgemv)):
-            g = gpu.graph(fn, args.steps)
-            g.replay()
-            variants[name] = gpu.time_graph(g) / args.steps * 1e3
+            variants[name] = gpu.time_launches(fn, max(args.steps, KERNEL_LAUNCHES)) * 1e3
         if tag == "compact":
             variants["compact bytes per weight"] = pv[0].query().compact_bytes / (N * K)
         for p in pv:
@@ -261,16 +323,15 @@ def run_decode(gpu, args, T=1, with_cpu=True):
         gpu.b.check(lib.sbn_packed_export_rank(pws[i % R].handle, gpu.b._ptr(rank_out),
                                                gpu.b._stream(None)))
 
-    g = gpu.graph(rank_export, args.steps)
-    g.replay()
-    variants["rank export"] = gpu.time_graph(g) / args.steps * 1e3
+    variants["rank export"] = gpu.time_launches(rank_export, max(args.steps, KERNEL_LAUNCHES)) * 1e3
     variants["rank bytes per weight"] = rrb * N / (N * K)
     ms_step = ms / args.steps
     if fused:
         step_bytes = fused_bytes(T, K, N, n, m)
-        kname, kbytes, kms = "bitlinear_gemv (quantize fused)", step_bytes, ms_step
+        kms = gpu.time_launches(step, max(args.steps, KERNEL_LAUNCHES))
+        kname, kbytes = "bitlinear_gemv (quantize fused)", step_bytes
         tkey = f"gemv_fused_{n}of{m}_T{T}"
-        timings["bitlinear_gemv (quantize fused)"] = ms_step
+        timings["bitlinear_gemv (quantize fused)"] = kms
     else:
         step_bytes = forward_bytes(T, K, N, n, m) + quantize_bytes(T, K)
         kname, kbytes, kms = "bitlinear_gemv", forward_bytes(T, K, N, n, m), timings["bitlinear_gemv"]
@@ -342,20 +403,14 @@ def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True):
     step(0)
     torch.cuda.synchronize()
     y_eager = y.clone()
-    gs = gpu.graph(step, steps)
-    gs.replay()
-    ms = gpu.time_graph(gs) / steps
+    ms = gpu.time_launches(step, max(steps, KERNEL_LAUNCHES))
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
-    gk = gpu.graph(gemm_only, steps)
-    gk.replay()
-    gemm_ms = gpu.time_graph(gk) / steps
+    gemm_ms = gpu.time_launches(gemm_only, max(steps, KERNEL_LAUNCHES))
     act_ms = {}
     for name, fn in (("quantize_act", lambda i: gpu.b.quantize_act(xd, out_q=q, out_absmax=a)),
                      ("layernorm_quantize_act",
                       lambda i: gpu.b.layernorm_quantize_act(xd, LN_EPS, out_q=q, out_absmax=a))):
-        g = gpu.graph(fn, steps)
-        g.replay()
-        act_ms[name] = gpu.time_graph(g) / steps
+        act_ms[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
     act_bytes = 3.0 * T * K + 4.0 * T  # bf16 in, int8 + a' out
     ops = 2.0 * T * K * N
     achieved = ops / (gemm_ms * 1e-3) / 1e12
@@ -428,9 +483,7 @@ def run_block(gpu, args, pattern, T, steps):
             gpu.b.bitlinear(q, a, pw[li], out="f32", y=ys[li])
 
     step(0)
-    g = gpu.graph(step, steps)
-    g.replay()
-    ms = gpu.time_graph(g) / steps
+    ms = gpu.time_launches(step, max(steps, KERNEL_LAUNCHES))
     ops = sum(2.0 * T * l.k * l.n_out for l in layers)
     fb = sum(forward_bytes(T, l.k, l.n_out, n, m) for l in layers)
     qb = sum(quantize_bytes(T, layers[[l.act_input for l in layers].index(ai)].k) for ai in acts)
@@ -475,9 +528,7 @@ def run_train(gpu, args, layer_index, pattern, steps):
     torch.cuda.synchronize()
     res = {}
     for name, fn in (("step", step), ("pack", pack_only), ("gemm", gemm_only)):
-        g = gpu.graph(fn, steps)
-        g.replay()
-        res[name] = gpu.time_graph(g) / steps
+        res[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
     pb = pack_bytes(N, K, n, m)
     ops = 2.0 * T * K * N
     out = {"layer": layer.name, "pattern": f"{n}:{m}", "tokens": T, "K": K, "n_out": N,
@@ -499,9 +550,7 @@ def run_train(gpu, args, layer_index, pattern, steps):
         gpu.b.bitlinear(q, a, pd, out="f32", y=yd)
         torch.cuda.synchronize()
         assert torch.equal(yd, y_sp), "dense and structured-sparse MFMA paths differ"
-        g = gpu.graph(lambda i: gpu.b.bitlinear(q, a, pd, out="f32", y=yd), steps)
-        g.replay()
-        dense_ms = gpu.time_graph(g) / steps
+        dense_ms = gpu.time_launches(lambda i: gpu.b.bitlinear(q, a, pd, out="f32", y=yd), max(steps, KERNEL_LAUNCHES))
         pd.free()
         out["gemm"] = "structured-sparse MFMA (v_smfmac_i32_16x16x128_i8)"
         out["gemm_dense_mfma_us"] = dense_ms * 1e3
@@ -518,9 +567,7 @@ def run_train(gpu, args, layer_index, pattern, steps):
     bw = {}
     for name, fn in (("bwd", lambda i: gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)),
                      ("pack_bwd", lambda i: (pw.pack(wd), gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)))):
-        g = gpu.graph(fn, steps)
-        g.replay()
-        bw[name] = gpu.time_graph(g) / steps
+        bw[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
     torch.cuda.synchronize()
     assert torch.equal(dx, dx_eager), "data-gradient graph replay differs from the eager call"
     out["bwd_dx_us"] = bw["bwd"] * 1e3
@@ -656,6 +703,16 @@ def main():
         line["activation_kernels"] = res["activation_kernels"]
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
+    ceil = measure_ceilings(gpu, res["roofline"].get("bytes_per_launch", 1 << 22))
+    line["ceilings"] = ceil
+    rl = line["roofline"]
+    if rl["bound"] == "hbm":
+        rl["measured_peak"] = ceil["hbm_read_GBps"]
+        rl["frac_measured"] = rl["achieved"] / ceil["hbm_read_GBps"]
+        rl["frac_small_read"] = rl["achieved"] / ceil["small_read_GBps"]
+    else:
+        rl["measured_peak"] = ceil["int8_mfma_TOPS"]
+        rl["frac_measured"] = rl["achieved"] / ceil["int8_mfma_TOPS"]
     if not args.no_secondary and args.workload == "decode":
         sec = []
         r16 = run_decode(gpu, args, T=16, with_cpu=False)

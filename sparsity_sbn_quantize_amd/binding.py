@@ -13,7 +13,8 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsbn.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "sbn.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADERS = [os.path.join(INCLUDE, h) for h in ("sbn.h", "sbn_ceilings.h")]
 
 SBN_OUT_F32 = 0
 SBN_OUT_I32_ACC = 1
@@ -66,14 +67,20 @@ _SIGNATURES = {
     "sbn_bitlinear_fwd_ln_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _I64,
                                                  _P, _P, _I64, ctypes.c_int, _P]),
     "sbn_last_error": (ctypes.c_char_p, []),
+    "sbn_ceiling_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_uint32, _P, _P]),
+    "sbn_ceiling_mfma_i8": (ctypes.c_int, [_I64, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "sbn_ceiling_empty": (ctypes.c_int, [_P]),
 }
 
 
 def header_symbols() -> list:
-    """Function names declared in include/sbn.h."""
-    with open(HEADER) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sbn_\w+)\s*\(", text, re.M)))
+    """Function names declared in the headers under include/."""
+    names = set()
+    for path in HEADERS:
+        with open(path) as f:
+            text = f.read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sbn_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def lib() -> ctypes.CDLL:

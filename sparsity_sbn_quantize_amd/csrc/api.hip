@@ -22,6 +22,20 @@ sbn_status fail(sbn_status code, const char* fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+namespace sbn {
+sbn_status set_error(sbn_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace sbn
+
+namespace {
+
 sbn_status hip_fail(hipError_t e, const char* what) {
   return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }

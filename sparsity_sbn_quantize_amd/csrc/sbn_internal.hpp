@@ -48,6 +48,9 @@ struct sbn_packed {
 
 namespace sbn {
 
+// Sets the calling thread's sbn_last_error() message (printf format) and returns `code`.
+sbn_status set_error(sbn_status code, const char* fmt, ...);
+
 // Words of split-K handshake flags a handle holds (2 per wave of up to 256 tiles x 4 waves).
 constexpr int kGemmSyncInts = 256 * 4 * 2;
 

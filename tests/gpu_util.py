@@ -31,8 +31,11 @@ def to_dev_f32(w: np.ndarray, ld: int | None = None):
     return torch.from_numpy(buf).cuda()[:, :K]
 
 
-def gpu_forward(x_bits, w, n, m, ld_x=None, ld_w=None, ld_q=None, outs=("f32", "i32")):
-    """Runs quantize -> pack -> forward on the GPU; returns host arrays of every stage."""
+def gpu_forward(x_bits, w, n, m, ld_x=None, ld_w=None, ld_q=None, outs=("f32", "i32"),
+                bf16_step=False):
+    """Runs quantize -> pack -> forward on the GPU; returns host arrays of every stage. With
+    bf16_step, the quantize-and-multiply entry (sbn_bitlinear_fwd_bf16) also runs on the same
+    packed weights, and its outputs are returned under "bf16_*"."""
     import torch
     T, K = x_bits.shape
     xd = to_dev_bf16(x_bits, ld_x)
@@ -46,6 +49,11 @@ def gpu_forward(x_bits, w, n, m, ld_x=None, ld_w=None, ld_q=None, outs=("f32", "
     res = {}
     for kind in outs:
         res[kind] = binding.bitlinear(q, a, pw, out=kind)
+    if bf16_step:
+        for kind in outs:
+            yb, qb, ab = binding.bitlinear_bf16(xd, pw, out=kind)
+            res["bf16_" + kind] = yb
+        res["bf16_q"], res["bf16_a"] = qb, ab
     codes, keep, gamma = pw.export()
     cb, mb = pw.export_rpf()
     torch.cuda.synchronize()
@@ -57,6 +65,9 @@ def gpu_forward(x_bits, w, n, m, ld_x=None, ld_w=None, ld_q=None, outs=("f32", "
         out["y"] = res["f32"].cpu().numpy()
     if "i32" in res:
         out["acc"] = res["i32"].cpu().numpy()
+    for k, v in res.items():
+        if k.startswith("bf16_"):
+            out[k] = v.cpu().numpy()
     pw.free()
     return out
 
@@ -94,15 +105,25 @@ def gamma_matches(got, w) -> bool:
     return abs(mean - mid) <= 1e-9 * abs(mean)
 
 
-def check_stages(g, x_bits, w, n, m, acc_tokens=None, acc_rows=None):
+def check_stages(g, x_bits, w, n, m, acc_tokens=None, acc_rows=None, p=None):
     """Compares every stage of a GPU run `g` with the oracle. The int32 accumulators and fp32
     outputs are compared in full, or, when samples are given, on the sampled tokens (all rows)
-    and the sampled rows (all tokens)."""
+    and the sampled rows (all tokens). `p` may carry the oracle's pack of (w, n, m) computed
+    before. Outputs of the quantize-and-multiply entry (gpu_forward's bf16_step) must equal the
+    two-call path's bit for bit."""
+    if "bf16_q" in g:
+        assert np.array_equal(g["bf16_q"], g["q"]), "bf16 entry: x_q differs from the quantizer"
+        assert np.array_equal(g["bf16_a"], g["a_prime"]), "bf16 entry: a' differs"
+        if "acc" in g:
+            assert np.array_equal(g["bf16_i32"], g["acc"]), "bf16 entry: int32 accumulators differ"
+        if "y" in g:
+            assert np.array_equal(g["bf16_f32"], g["y"]), "bf16 entry: fp32 output differs"
     q_ref, a_ref = oracle.quantize_act(x_bits)
     assert np.array_equal(g["a_prime"], a_ref), "absmax"
     assert_int_exact_except_boundary(g["q"], q_ref, oracle.boundary_elements_act(x_bits, a_ref),
                                      "int8 activations")
-    p = oracle.pack_nm_ternary(w, n, m)
+    if p is None:
+        p = oracle.pack_nm_ternary(w, n, m)
     assert gamma_matches(g["gamma"], w), (g["gamma"], p["gamma"])
     assert np.array_equal(g["keep"], p["keep"]), "keep mask"
     assert_int_exact_except_boundary(g["codes"], p["codes"],

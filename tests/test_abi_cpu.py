@@ -26,7 +26,8 @@ def test_exports_match_header(lib):
                              "sbn_packed_export_rank",
                              "sbn_packed_export_outliers",
                              "sbn_packed_query",
-                             "sbn_packed_mask_flips", "sbn_last_error"}
+                             "sbn_packed_mask_flips", "sbn_last_error",
+                             "sbn_ceiling_stream_read", "sbn_ceiling_mfma_i8", "sbn_ceiling_empty"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -107,6 +108,14 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_bitlinear_fwd_ln_bf16(None, None, 0, 1, 0.0, None, 0, None, None, 0, 0,
                                          None) == ERR_INVALID
     lib.sbn_free(None)  # no-op
+    sink = ctypes.c_void_p(16)
+    ops = ctypes.c_double(0)
+    assert lib.sbn_ceiling_stream_read(None, 1024, 1, sink, None) == ERR_INVALID
+    assert lib.sbn_ceiling_stream_read(ctypes.c_void_p(64), 1000, 1, sink, None) == ERR_INVALID
+    assert lib.sbn_ceiling_stream_read(ctypes.c_void_p(8), 1024, 1, sink, None) == ERR_INVALID
+    assert lib.sbn_ceiling_mfma_i8(0, 1024, sink, ctypes.byref(ops), None) == ERR_INVALID
+    assert lib.sbn_ceiling_mfma_i8(100, 6, sink, ctypes.byref(ops), None) == ERR_INVALID
+    assert lib.sbn_ceiling_mfma_i8(100, 1024, sink, None, None) == ERR_INVALID
 
 
 def test_error_message_is_per_call(lib):

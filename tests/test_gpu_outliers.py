@@ -188,12 +188,12 @@ def test_outlier_decode_shape():
 
 @pytest.mark.parametrize("k", [4, 8, 16])
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (3, 8), (8, 16)])
-@pytest.mark.parametrize("N,K", [(64, 256), (304, 2560), (96, 12288), (48, 4096)])
+@pytest.mark.parametrize("N,K", [(64, 256), (304, 2560), (96, 12288), (48, 4096), (64, 6912)])
 def test_outlier_term_in_the_one_token_step(k, n, m, N, K):
-    """One token, n_out a multiple of 16: the bf16-input step adds the outlier term in the same
-    launch (one to 48 quads, 1 to 16 waves, every code form). It sums in the outlier kernel's
-    order, so its output equals the int8 path's (forward, then the outlier kernel) bit for bit,
-    and both stay within the fp32 bound."""
+    """One token, n_out a multiple of 16: both the bf16-input step and the int8 forward add the
+    outlier term in the GEMV's launch (one to 48 quads, 1 to 16 waves, one to three quads per
+    wave: K = 6912 has 27 quads, two per wave; every code form). Both stay within the fp32 bound
+    and give the same bits."""
     w = _w(N * 3 + K + 7 * k + n, N, K)
     x = _x(K + k, 1, K)
     r = _fwd(w, x, n, m, k, 1)
@@ -201,6 +201,31 @@ def test_outlier_term_in_the_one_token_step(k, n, m, N, K):
     assert np.array_equal(r["q"], q_ref) and np.array_equal(r["a"], a_ref)
     _check_y(r, k, K)
     assert np.array_equal(r["yb"], r["y"])
+
+
+@pytest.mark.parametrize("k", [4, 16])
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (3, 8), (8, 16)])
+@pytest.mark.parametrize("K", [2560, 12288])
+def test_one_token_outlier_launch_equals_two_launch_order(k, n, m, K):
+    """The one-token launches sum the outlier term in the order of the separate outlier kernel
+    (eight partial sums per row over groups c, c + 8, ..., added in order c = 0 .. 7). The same
+    token as row 0 of a two-token call (GEMV, then the outlier kernel) must give row 0 of the
+    one-token output bit for bit, here with G = 10 and 48 groups of 256, more than the eight
+    partial sums, so the cross-group order is exercised."""
+    import torch
+    N = 96
+    w = _w(K + 11 * k + n, N, K)
+    x2 = _x(K + 3 * k + m, 2, K)
+    xd2 = gu.to_dev_bf16(x2)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m, outliers=k)
+    q2, a2 = binding.quantize_act(xd2)
+    y2 = binding.bitlinear(q2, a2, pw, out="f32")          # GEMV + outlier kernel
+    y1 = binding.bitlinear(q2[:1], a2[:1], pw, out="f32")  # one launch, int8 input
+    yb = binding.bitlinear_bf16(xd2[:1], pw)[0]            # one launch, bf16 input
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy()[0], y2.cpu().numpy()[0])
+    assert np.array_equal(yb.cpu().numpy()[0], y2.cpu().numpy()[0])
+    pw.free()
 
 
 def test_outlier_term_in_the_one_token_step_unaligned_y_and_fallbacks():
