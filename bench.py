@@ -376,7 +376,7 @@ def cpu_decode(x_bits, w, n, m, step_bytes, seconds):
                       f"in {el:.1f} s"}
 
 
-def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True):
+def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True, cpu_seconds=None):
     """Prefill GEMM: quantize 2048 tokens + 8:16 forward (weights packed once)."""
     from sparsity_sbn_quantize_amd import inputs
     torch = gpu.torch
@@ -424,10 +424,14 @@ def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True):
         "roofline": {"bound": "mfma", "kernel": "bitlinear_gemm", "achieved": achieved,
                      "peak": INT8_PEAK_TOPS, "unit": "TOP/s", "frac": achieved / INT8_PEAK_TOPS,
                      "traffic": measured_traffic(f"gemm_{n}of{m}_{layer.name}"),
-                     "avg_launch_us": gemm_ms * 1e3},
+                     "avg_launch_us": gemm_ms * 1e3,
+                     # the method's own work: the kept weights' multiply-adds, T*K*N*n/m
+                     "algorithmic_macs": T * K * N * n / m,
+                     "algorithmic_TMACs_per_s": T * K * N * n / m / (gemm_ms * 1e-3) / 1e12},
     }
     if with_cpu and not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_prefill(x_bits, w, n, m, K, N, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_prefill(x_bits, w, n, m, K, N,
+                                          cpu_seconds if cpu_seconds else args.cpu_seconds)
     pw.free()
     return res
 
@@ -452,9 +456,21 @@ def cpu_prefill(x_bits, w, n, m, K, N, seconds):
                       f"{el:.1f} s"}
 
 
+# The block's grouped launches: members that read the same input share one launch.
+BLOCK_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))  # Q/K/V, O, gate/up, down
+
+
 def run_block(gpu, args, pattern, T, steps):
-    """2B-style block: Q, K, V, O, gate, up, down BitLinears at T tokens for one n:m pattern; one
-    step quantizes each distinct layer input and runs all seven forwards."""
+    """2B-style block: Q, K, V, O, gate, up, down BitLinears at T tokens for one n:m pattern.
+
+    A block step quantizes each of the four distinct layer inputs and runs all seven forwards.
+    Grouped (the block total): Q/K/V and gate/up each run as one grouped launch; for T <= 4 each
+    of the four groups is one kernel that also quantizes its input (sbn_bitlinear_fwd_group_bf16),
+    for T = 16 the quantize kernel and the grouped GEMV, for T > 16 the quantize kernel and one GEMM
+    per layer. Ungrouped (for comparison): four quantize kernels and seven forwards. Per layer: the
+    forward alone on int8 input, and for T <= 4 the one-kernel step of that layer alone. Decode token
+    counts rotate over distinct packed copies of the whole block (>= 1 GiB), so weights stream
+    from HBM."""
     from sparsity_sbn_quantize_amd import inputs
     torch = gpu.torch
     wl = inputs.W_BLOCK
@@ -470,29 +486,95 @@ def run_block(gpu, args, pattern, T, steps):
     wds = gpu.block_weights
     ys = [torch.empty((T, l.n_out), dtype=torch.float32, device="cuda") for l in layers]
     weight_bytes = sum(rpf_bytes(l.n_out, l.k, n, m) for l in layers)
-    # cold HBM for the memory-bound decode shapes: distinct packed copies of the whole block
     R = max(1, -(-args.rotate_bytes // weight_bytes)) if T <= 16 else 1
     packed = [[gpu.b.PackedWeight(wds[i], n, m) for i in range(len(layers))] for _ in range(R)]
+    b = gpu.b
 
-    def step(i):
-        pw = packed[i % len(packed)]
+    def ungrouped(i):
+        pw = packed[i % R]
         for (xd, q, a) in acts.values():
-            gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
+            b.quantize_act(xd, out_q=q, out_absmax=a)
         for li, layer in enumerate(layers):
             _, q, a = acts[layer.act_input]
-            gpu.b.bitlinear(q, a, pw[li], out="f32", y=ys[li])
+            b.bitlinear(q, a, pw[li], out="f32", y=ys[li])
 
-    step(0)
-    ms = gpu.time_launches(step, max(steps, KERNEL_LAUNCHES))
+    def grouped(i):
+        pw = packed[i % R]
+        for grp in BLOCK_GROUPS:
+            xd, q, a = acts[layers[grp[0]].act_input]
+            members = [pw[li] for li in grp]
+            outs = [ys[li] for li in grp]
+            if T <= FUSED_MAX_T:
+                b.bitlinear_group_bf16(xd, members, out="f32", ys=outs, x_q=q, x_absmax=a)
+            else:
+                b.quantize_act(xd, out_q=q, out_absmax=a)
+                b.bitlinear_group(q, a, members, out="f32", ys=outs)
+
+    # the grouped step equals the ungrouped one bit for bit
+    ungrouped(0)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    grouped(0)
+    torch.cuda.synchronize()
+    assert all(torch.equal(y, r) for y, r in zip(ys, ref)), "grouped block differs"
+    nl = max(steps, KERNEL_LAUNCHES) if T <= 16 else max(steps, 20)
+    ms_g = gpu.time_launches(grouped, nl)
+    ms_u = gpu.time_launches(ungrouped, nl)
+    per_layer = []
+    if T <= 16:
+        for li, layer in enumerate(layers):
+            xd, q, a = acts[layer.act_input]
+            fwd_ms = gpu.time_launches(
+                lambda i, li=li, q=q, a=a: b.bitlinear(q, a, packed[i % R][li], out="f32",
+                                                       y=ys[li]), nl)
+            row = {"layer": layer.name, "K": layer.k, "n_out": layer.n_out,
+                   "forward_us": fwd_ms * 1e3,
+                   "forward_GBps": forward_bytes(T, layer.k, layer.n_out, n, m) /
+                   (fwd_ms * 1e-3) / 1e9}
+            if T <= FUSED_MAX_T:
+                st_ms = gpu.time_launches(
+                    lambda i, li=li, xd=xd, q=q, a=a: b.bitlinear_bf16(
+                        xd, packed[i % R][li], out="f32", y=ys[li], x_q=q, x_absmax=a), nl)
+                row["step_us"] = st_ms * 1e3
+                row["step_GBps"] = fused_bytes(T, layer.k, layer.n_out, n, m) / (st_ms * 1e-3) / 1e9
+            per_layer.append(row)
+        groups = []
+        for grp in BLOCK_GROUPS:
+            if len(grp) < 2:
+                continue
+            xd, q, a = acts[layers[grp[0]].act_input]
+            outs = [ys[li] for li in grp]
+            if T <= FUSED_MAX_T:
+                fn = (lambda i, grp=grp, xd=xd, q=q, a=a, outs=outs: b.bitlinear_group_bf16(
+                    xd, [packed[i % R][li] for li in grp], out="f32", ys=outs, x_q=q, x_absmax=a))
+                gbytes = sum(rpf_bytes(layers[li].n_out, layers[li].k, n, m) + 4 * T *
+                             layers[li].n_out + 4 for li in grp) + \
+                    quantize_bytes(T, layers[grp[0]].k)
+            else:
+                fn = (lambda i, grp=grp, q=q, a=a, outs=outs: b.bitlinear_group(
+                    q, a, [packed[i % R][li] for li in grp], out="f32", ys=outs))
+                gbytes = sum(rpf_bytes(layers[li].n_out, layers[li].k, n, m) + 4 * T *
+                             layers[li].n_out + 4 for li in grp) + T * layers[grp[0]].k + 4 * T
+            g_ms = gpu.time_launches(fn, nl)
+            groups.append({"layers": "/".join(layers[li].name for li in grp), "us": g_ms * 1e3,
+                           "bytes": gbytes, "GBps": gbytes / (g_ms * 1e-3) / 1e9,
+                           "frac_hbm": gbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
     ops = sum(2.0 * T * l.k * l.n_out for l in layers)
     fb = sum(forward_bytes(T, l.k, l.n_out, n, m) for l in layers)
     qb = sum(quantize_bytes(T, layers[[l.act_input for l in layers].index(ai)].k) for ai in acts)
     for pw in packed:
         for p_ in pw:
             p_.free()
-    return {"pattern": f"{n}:{m}", "tokens": T, "ms_per_step": ms,
-            "TOPS": ops / (ms * 1e-3) / 1e12, "GBps": (fb + qb) / (ms * 1e-3) / 1e9,
-            "weight_bytes": weight_bytes}
+    out = {"pattern": f"{n}:{m}", "tokens": T, "ms_per_step": ms_g,
+           "ungrouped_ms_per_step": ms_u, "TOPS": ops / (ms_g * 1e-3) / 1e12,
+           "GBps": (fb + qb) / (ms_g * 1e-3) / 1e9,
+           "frac_hbm": (fb + qb) / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "weight_bytes": weight_bytes,
+           "launches": 4 if T <= FUSED_MAX_T else (8 if T <= 16 else 11)}
+    if per_layer:
+        out["per_layer"] = per_layer
+        out["grouped_launches"] = groups
+    return out
 
 
 def run_train(gpu, args, layer_index, pattern, steps):
@@ -508,18 +590,22 @@ def run_train(gpu, args, layer_index, pattern, steps):
     x_bits, w = inputs.layer_inputs(wl, layer_index, T)
     xd, wd = gpu.bf16(x_bits), gpu.f32(w)
     del x_bits, w
+    # The re-pack reads the latent weights from HBM: the timed packs rotate over distinct copies of
+    # them (>= 1 GiB in all, beyond the 256 MB last-level cache), each re-packed into one handle.
+    RL = max(1, -(-args.rotate_bytes // (4 * N * K)))
+    wds = [wd] + [wd.clone() for _ in range(RL - 1)]
     pw = gpu.b.PackedWeight(wd, n, m)
     q = torch.empty((T, K), dtype=torch.int8, device="cuda")
     a = torch.empty((T,), dtype=torch.float32, device="cuda")
     y = torch.empty((T, N), dtype=torch.float32, device="cuda")
 
     def step(i):
-        pw.pack(wd)
+        pw.pack(wds[i % RL])
         gpu.b.quantize_act(xd, out_q=q, out_absmax=a)
         gpu.b.bitlinear(q, a, pw, out="f32", y=y)
 
     def pack_only(i):
-        pw.pack(wd)
+        pw.pack(wds[i % RL])
 
     def gemm_only(i):
         gpu.b.bitlinear(q, a, pw, out="f32", y=y)
@@ -535,8 +621,10 @@ def run_train(gpu, args, layer_index, pattern, steps):
            "ms_per_step": res["step"], "pack_us": res["pack"] * 1e3,
            "pack_GBps": pb / (res["pack"] * 1e-3) / 1e9,
            "pack_frac_hbm": pb / (res["pack"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "pack_latent_copies": RL,
            "gemm_us": res["gemm"] * 1e3, "gemm_TOPS": ops / (res["gemm"] * 1e-3) / 1e12,
-           "gemm_frac_int8": ops / (res["gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS}
+           "gemm_frac_int8": ops / (res["gemm"] * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+           "gemm_algorithmic_TMACs_per_s": T * K * N * n / m / (res["gemm"] * 1e-3) / 1e12}
     if (n, m) == (2, 4):
         # 2:4 runs on the structured-sparse MFMA; time the dense-MFMA path on the same weights
         # (positional codes) beside it, and check that both give the same output.
@@ -566,7 +654,8 @@ def run_train(gpu, args, layer_index, pattern, steps):
     dx_eager = dx.clone()
     bw = {}
     for name, fn in (("bwd", lambda i: gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)),
-                     ("pack_bwd", lambda i: (pw.pack(wd), gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)))):
+                     ("pack_bwd", lambda i: (pw.pack(wds[i % RL]),
+                                              gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)))):
         bw[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
     torch.cuda.synchronize()
     assert torch.equal(dx, dx_eager), "data-gradient graph replay differs from the eager call"
@@ -574,7 +663,7 @@ def run_train(gpu, args, layer_index, pattern, steps):
     out["bwd_dx_TFLOPS"] = ops / (bw["bwd"] * 1e-3) / 1e12
     out["bwd_dx_frac_bf16"] = out["bwd_dx_TFLOPS"] / BF16_PEAK_TFLOPS
     out["pack_transpose_bwd_us"] = bw["pack_bwd"] * 1e3
-    del dy, dx, dx_eager
+    del dy, dx, dx_eager, wds
     pw.free()
     return out
 
@@ -718,11 +807,20 @@ def main():
         r16 = run_decode(gpu, args, T=16, with_cpu=False)
         sec.append({k: r16[k] for k in ("value", "unit", "ms_per_step", "config", "roofline")})
         for li in (0, 1):
-            rp = run_prefill(gpu, args, li, steps=50, with_cpu=False)
+            rp = run_prefill(gpu, args, li, steps=50, with_cpu=not args.no_cpu_baseline,
+                             cpu_seconds=min(args.cpu_seconds, 5.0))
             sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
-                                           "activation_kernels")})
+                                           "activation_kernels", "cpu_baseline") if k in rp})
         for li, pat in ((0, (2, 4)), (1, (8, 16))):
             sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
+        from sparsity_sbn_quantize_amd import inputs
+        gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
+                             for i in range(len(inputs.W_BLOCK.layers))]
+        for T in (1, 16):
+            for pat in inputs.W_BLOCK.patterns:
+                print(f"[bench] block {pat[0]}:{pat[1]} T={T}", file=sys.stderr, flush=True)
+                sec.append({"block": run_block(gpu, args, pat, T, args.steps)})
+        del gpu.block_weights
         line["secondary"] = sec
     print(json.dumps(line))
 

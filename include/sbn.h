@@ -191,6 +191,47 @@ sbn_status sbn_bitlinear_fwd_ln_bf16(const sbn_packed* w, const uint16_t* x_bf16
                                      float* x_absmax, void* y, int64_t ld_y,
                                      sbn_out_kind out_kind, void* stream);
 
+/* Most weights one grouped call takes. */
+#define SBN_MAX_GROUP 8
+
+/*
+ * Grouped forward: several packed weights that read the same activations, for instance the Q, K
+ * and V projections of a block, or its gate and up projections ("The BitLinear Layer", operations
+ * 4 and 5, for each weight). The result is exactly that of sbn_bitlinear_fwd on each member in
+ * turn with the same x_q and x_absmax:
+ *   ws        [count] (host) packed weights, all with the same K (else SBN_ERR_SHAPE);
+ *             1 <= count <= SBN_MAX_GROUP; a handle may appear more than once.
+ *   ys        [count] (host) output pointers, member i's y [T][ld_ys[i]] as for sbn_bitlinear_fwd.
+ *   ld_ys     [count] (host) leading dimensions, ld_ys[i] >= member i's n_out.
+ * For T <= 16, when the members share the pattern and code form, none holds the compact form, and
+ * (for SBN_OUT_F32) none has k:256 outliers, all members run in one kernel launch (one workgroup
+ * per 16 output rows of every member); otherwise the members run one after another.
+ * Requires T >= 0, K <= ld_q <= 2^26; T == 0 is a no-op. The outputs must not overlap.
+ */
+sbn_status sbn_bitlinear_fwd_group(const sbn_packed* const* ws /* host */, int count,
+                                   const int8_t* x_q, int64_t ld_q, const float* x_absmax,
+                                   int64_t T, void* const* ys /* host */,
+                                   const int64_t* ld_ys /* host */, sbn_out_kind out_kind,
+                                   void* stream);
+
+/*
+ * Grouped quantize-and-multiply: the activation quantization of sbn_quantize_act (after the
+ * parameter-free LayerNorm of sbn_layernorm_quantize_act when ln_eps > 0; ln_eps == 0: none),
+ * then sbn_bitlinear_fwd_group on the result ("The BitLinear Layer", operations 1, 2, 4 and 5).
+ * x_q and x_absmax receive exactly what the quantizer writes; the outputs are exactly those of
+ * sbn_bitlinear_fwd_group. For T <= 4 and K <= 12288, under the one-launch conditions of
+ * sbn_bitlinear_fwd_group, the whole call is one kernel launch in which every workgroup quantizes
+ * the activations it needs itself; otherwise the first member runs as sbn_bitlinear_fwd_bf16
+ * (or sbn_bitlinear_fwd_ln_bf16) and the others read its x_q and x_absmax.
+ * Requires ld_x >= K, ln_eps >= 0 and finite, and the requirements of sbn_bitlinear_fwd_group.
+ */
+sbn_status sbn_bitlinear_fwd_group_bf16(const sbn_packed* const* ws /* host */, int count,
+                                        const uint16_t* x_bf16, int64_t ld_x, int64_t T,
+                                        float ln_eps, int8_t* x_q, int64_t ld_q, float* x_absmax,
+                                        void* const* ys /* host */,
+                                        const int64_t* ld_ys /* host */, sbn_out_kind out_kind,
+                                        void* stream);
+
 /*
  * Data gradient of the layer under the straight-through estimator ("Microsoft BitNet 1.58: The
  * Era of 1-Bit Large Language Models", section "Training with the Straight-Through Estimator":

@@ -67,6 +67,11 @@ _SIGNATURES = {
     "sbn_bitlinear_fwd_ln_bf16": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _I64,
                                                  _P, _P, _I64, ctypes.c_int, _P]),
     "sbn_last_error": (ctypes.c_char_p, []),
+    "sbn_bitlinear_fwd_group": (ctypes.c_int, [_P, ctypes.c_int, _P, _I64, _P, _I64, _P, _P,
+                                               ctypes.c_int, _P]),
+    "sbn_bitlinear_fwd_group_bf16": (ctypes.c_int, [_P, ctypes.c_int, _P, _I64, _I64,
+                                                    ctypes.c_float, _P, _I64, _P, _P, _P,
+                                                    ctypes.c_int, _P]),
     "sbn_ceiling_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_uint32, _P, _P]),
     "sbn_ceiling_mfma_i8": (ctypes.c_int, [_I64, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "sbn_ceiling_empty": (ctypes.c_int, [_P]),
@@ -330,3 +335,55 @@ def bitlinear_bwd_dx(dy, w: PackedWeight, dx=None, stream=None):
     check(lib().sbn_bitlinear_bwd_dx(w.handle, _ptr(dy), _ld(dy, w.n_out), T, _ptr(dx),
                                      _ld(dx, w.K), _stream(stream)))
     return dx
+
+
+def _group_arrays(ws, ys):
+    n = len(ws)
+    handles = (ctypes.c_void_p * n)(*[w.handle.value for w in ws])
+    outs = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    lds = (ctypes.c_int64 * n)(*[_ld(y, w.n_out) for w, y in zip(ws, ys)])
+    return handles, outs, lds
+
+
+def _group_outputs(ws, T, kind, ys, device):
+    import torch
+    if ys is not None:
+        return list(ys)
+    dt = torch.float32 if kind == SBN_OUT_F32 else torch.int32
+    return [torch.empty((T, w.n_out), dtype=dt, device=device) for w in ws]
+
+
+def bitlinear_group(x_q, x_absmax, ws, out: str = "f32", ys=None, stream=None):
+    """Grouped forward of several packed weights on the same x_q (sbn_bitlinear_fwd_group):
+    returns the list of outputs [T][n_out_i]."""
+    _require_cuda(x_q, "x_q")
+    T = x_q.shape[0]
+    kind = SBN_OUT_F32 if out == "f32" else SBN_OUT_I32_ACC
+    ys = _group_outputs(ws, T, kind, ys, x_q.device)
+    handles, outs, lds = _group_arrays(ws, ys)
+    check(lib().sbn_bitlinear_fwd_group(handles, len(ws), _ptr(x_q), _ld(x_q, ws[0].K),
+                                        _ptr(x_absmax), T, outs, lds, kind, _stream(stream)))
+    return ys
+
+
+def bitlinear_group_bf16(x, ws, out: str = "f32", ys=None, x_q=None, x_absmax=None,
+                         ln_eps: float = 0.0, stream=None):
+    """Grouped quantize-and-multiply (sbn_bitlinear_fwd_group_bf16): x bf16 [T][K] ->
+    (list of outputs, x_q, a'). ln_eps > 0 runs the parameter-free LayerNorm first."""
+    import torch
+    _require_cuda(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.int16):
+        raise ValueError("x must be bfloat16 (or int16 bf16 bit patterns)")
+    T = x.shape[0]
+    K = ws[0].K
+    kind = SBN_OUT_F32 if out == "f32" else SBN_OUT_I32_ACC
+    ys = _group_outputs(ws, T, kind, ys, x.device)
+    if x_q is None:
+        x_q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    if x_absmax is None:
+        x_absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    handles, outs, lds = _group_arrays(ws, ys)
+    check(lib().sbn_bitlinear_fwd_group_bf16(handles, len(ws), _ptr(x), _ld(x, K), T,
+                                             float(ln_eps), _ptr(x_q), _ld(x_q, K),
+                                             _ptr(x_absmax), outs, lds, kind, _stream(stream)))
+    return ys, x_q, x_absmax

@@ -76,11 +76,123 @@ sbn_status fwd_bf16(const char* name, const sbn_packed* w, const uint16_t* x_bf1
   return SBN_OK;
 }
 
+// The int8-input forward of one weight (the dispatch of sbn_bitlinear_fwd after validation).
+hipError_t fwd_int8(const sbn_packed* w, const int8_t* x_q, int64_t ld_q, const float* x_absmax,
+                    int64_t T, void* y, int64_t ld_y, sbn_out_kind out_kind, hipStream_t s) {
+  if (w->L.n_out == 0) return hipSuccess;
+  const_cast<sbn_packed*>(w)->last_stream = s;
+  if (out_kind == SBN_OUT_F32 && sbn::gemv_int8_outl_fits(w, x_q, T))
+    return sbn::launch_gemv_int8_outl(w, x_q, x_absmax, static_cast<float*>(y), s);
+  hipError_t e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind, s);
+  if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
+    e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y, s);
+  return e;
+}
+
+// Shared validation of the grouped forwards; ok_single is set when one grouped launch can serve
+// them (same pattern and code form, no compact plane, no outlier term in the output, every member
+// with rows).
+sbn_status check_group(const char* name, const sbn_packed* const* ws, int count, int64_t T,
+                       int64_t ld_q, void* const* ys, const int64_t* ld_ys, sbn_out_kind out_kind,
+                       bool& ok_single) {
+  if (!ws || !ys || !ld_ys) return fail(SBN_ERR_INVALID_ARG, "%s: null host array", name);
+  if (count < 1 || count > SBN_MAX_GROUP)
+    return fail(SBN_ERR_INVALID_ARG, "%s: count=%d outside [1, %d]", name, count, SBN_MAX_GROUP);
+  if (out_kind != SBN_OUT_F32 && out_kind != SBN_OUT_I32_ACC)
+    return fail(SBN_ERR_INVALID_ARG, "%s: out_kind=%d", name, (int)out_kind);
+  if (T < 0) return fail(SBN_ERR_INVALID_ARG, "%s: T=%lld < 0", name, (long long)T);
+  if (T > INT32_MAX) return fail(SBN_ERR_UNSUPPORTED, "%s: T too large", name);
+  for (int i = 0; i < count; ++i)
+    if (!ws[i]) return fail(SBN_ERR_INVALID_ARG, "%s: ws[%d] is null", name, i);
+  const sbn_packed* w0 = ws[0];
+  ok_single = true;
+  for (int i = 0; i < count; ++i) {
+    const sbn_packed* w = ws[i];
+    if (w->L.K != w0->L.K)
+      return fail(SBN_ERR_SHAPE, "%s: ws[%d] has K=%lld, ws[0] K=%lld", name, i,
+                  (long long)w->L.K, (long long)w0->L.K);
+    if (ld_ys[i] < w->L.n_out)
+      return fail(SBN_ERR_INVALID_ARG, "%s: ld_ys[%d]=%lld < n_out=%lld", name, i,
+                  (long long)ld_ys[i], (long long)w->L.n_out);
+    if (T > 0 && w->L.n_out > 0 && !ys[i])
+      return fail(SBN_ERR_INVALID_ARG, "%s: ys[%d] is null", name, i);
+    if (w->L.n != w0->L.n || w->L.m != w0->L.m || w->L.form != w0->L.form || w->compact ||
+        (w->outlier_k > 0 && out_kind == SBN_OUT_F32) || w->L.n_out == 0)
+      ok_single = false;
+  }
+  if (ld_q < w0->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "%s: ld_q=%lld < K=%lld", name, (long long)ld_q,
+                (long long)w0->L.K);
+  if (ld_q > kMaxLdQ)
+    return fail(SBN_ERR_UNSUPPORTED, "%s: ld_q=%lld > %lld", name, (long long)ld_q,
+                (long long)kMaxLdQ);
+  return SBN_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* sbn_last_error(void) { return g_last_error; }
+
+sbn_status sbn_bitlinear_fwd_group(const sbn_packed* const* ws, int count, const int8_t* x_q,
+                                   int64_t ld_q, const float* x_absmax, int64_t T,
+                                   void* const* ys, const int64_t* ld_ys, sbn_out_kind out_kind,
+                                   void* stream) {
+  const char* name = "sbn_bitlinear_fwd_group";
+  bool single = false;
+  sbn_status st = check_group(name, ws, count, T, ld_q, ys, ld_ys, out_kind, single);
+  if (st != SBN_OK) return st;
+  if (T == 0) return SBN_OK;
+  if (!x_q || (out_kind == SBN_OUT_F32 && !x_absmax))
+    return fail(SBN_ERR_INVALID_ARG, "%s: null pointer", name);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (single && T <= 16) {
+    for (int i = 0; i < count; ++i) const_cast<sbn_packed*>(ws[i])->last_stream = s;
+    e = sbn::launch_gemv_int8_group(ws, count, x_q, ld_q, x_absmax, T, ys, ld_ys, (int)out_kind, s);
+  } else {
+    for (int i = 0; i < count && e == hipSuccess; ++i)
+      e = fwd_int8(ws[i], x_q, ld_q, x_absmax, T, ys[i], ld_ys[i], out_kind, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, name);
+  return SBN_OK;
+}
+
+sbn_status sbn_bitlinear_fwd_group_bf16(const sbn_packed* const* ws, int count,
+                                        const uint16_t* x_bf16, int64_t ld_x, int64_t T,
+                                        float ln_eps, int8_t* x_q, int64_t ld_q, float* x_absmax,
+                                        void* const* ys, const int64_t* ld_ys,
+                                        sbn_out_kind out_kind, void* stream) {
+  const char* name = "sbn_bitlinear_fwd_group_bf16";
+  bool single = false;
+  sbn_status st = check_group(name, ws, count, T, ld_q, ys, ld_ys, out_kind, single);
+  if (st != SBN_OK) return st;
+  if (ld_x < ws[0]->L.K)
+    return fail(SBN_ERR_INVALID_ARG, "%s: ld_x=%lld < K=%lld", name, (long long)ld_x,
+                (long long)ws[0]->L.K);
+  if (!(ln_eps >= 0.0f) || ln_eps > 3.0e38f)
+    return fail(SBN_ERR_INVALID_ARG, "%s: ln_eps=%g must be 0 or positive and finite", name,
+                (double)ln_eps);
+  if (T == 0) return SBN_OK;
+  if (!x_bf16 || !x_q || !x_absmax) return fail(SBN_ERR_INVALID_ARG, "%s: null pointer", name);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (single && sbn::gemv_group_fused_fits(ws[0], x_bf16, ld_x, T)) {
+    for (int i = 0; i < count; ++i) const_cast<sbn_packed*>(ws[i])->last_stream = s;
+    e = sbn::launch_gemv_group_bf16(ws, count, x_bf16, ld_x, T, x_q, ld_q, x_absmax, ys, ld_ys,
+                                    (int)out_kind, ln_eps, s);
+  } else {
+    // the first member quantizes (one kernel where it can), the others read its x_q and a'
+    const_cast<sbn_packed*>(ws[0])->last_stream = s;
+    e = sbn::launch_bitlinear_bf16(ws[0], x_bf16, ld_x, T, x_q, ld_q, x_absmax, ys[0], ld_ys[0],
+                                   (int)out_kind, ln_eps, s);
+    for (int i = 1; i < count && e == hipSuccess; ++i)
+      e = fwd_int8(ws[i], x_q, ld_q, x_absmax, T, ys[i], ld_ys[i], out_kind, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, name);
+  return SBN_OK;
+}
 
 sbn_status sbn_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t K, int64_t ld_x,
                             int8_t* x_q, int64_t ld_q, float* x_absmax, void* stream) {
@@ -311,18 +423,8 @@ sbn_status sbn_bitlinear_fwd(const sbn_packed* w, const int8_t* x_q, int64_t ld_
   if (w->L.n_out == 0) return SBN_OK;
   if (!x_q || !y || (out_kind == SBN_OUT_F32 && !x_absmax))
     return fail(SBN_ERR_INVALID_ARG, "sbn_bitlinear_fwd: null pointer");
-  const_cast<sbn_packed*>(w)->last_stream = (hipStream_t)stream;
-  hipError_t e;
-  if (out_kind == SBN_OUT_F32 && sbn::gemv_int8_outl_fits(w, x_q, T)) {
-    // one token: the outlier term in the GEMV's launch
-    e = sbn::launch_gemv_int8_outl(w, x_q, x_absmax, static_cast<float*>(y), (hipStream_t)stream);
-  } else {
-    e = sbn::launch_bitlinear(w, x_q, ld_q, x_absmax, T, y, ld_y, (int)out_kind,
-                              (hipStream_t)stream);
-    if (e == hipSuccess && w->outlier_k > 0 && out_kind == SBN_OUT_F32)
-      e = sbn::launch_outlier_add(w, x_q, ld_q, x_absmax, T, static_cast<float*>(y), ld_y,
-                                  (hipStream_t)stream);
-  }
+  // (one token with outliers: the outlier term in the GEMV's launch)
+  hipError_t e = fwd_int8(w, x_q, ld_q, x_absmax, T, y, ld_y, out_kind, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "sbn_bitlinear_fwd launch");
   return SBN_OK;
 }

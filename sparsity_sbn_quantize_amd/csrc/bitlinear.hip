@@ -482,6 +482,37 @@ hipError_t launch_gemv(const sbn_packed* h, const void* x, int64_t ld_x, int8_t*
   return hipGetLastError();
 }
 
+// The grouped one-kernel step (members as in bitlinear_gemv_group), with the wave and quad counts
+// of launch_gemv's one-kernel step.
+template <int FORM, bool XVEC>
+hipError_t launch_gemv_group_fused(const GemvGroup& G, int blocks, const Layout& L,
+                                   const uint16_t* x, int64_t ld_x, int8_t* xq_out, int64_t ld_q,
+                                   float* absmax, int64_t T, int out_kind, float ln_eps,
+                                   hipStream_t s) {
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, (L.quads + kGemvMaxQ - 1) / kGemvMaxQ);
+  const int Q = (int)((L.quads + W - 1) / W);
+#define SBN_GEMVG(QQ, LNV, XB)                                                                \
+  hipLaunchKernelGGL((bitlinear_gemv_group<FORM, true, XVEC, QQ, LNV, XB>), dim3((unsigned)blocks), \
+                     dim3(64 * W), 0, s, G, L, static_cast<const void*>(x), ld_x, xq_out, ld_q,  \
+                     absmax, T, out_kind, ln_eps)
+#define SBN_GEMVG_Q(QQ)                                                                       \
+  do {                                                                                        \
+    if (ln_eps > 0.0f) SBN_GEMVG(QQ, true, false);                                            \
+    else if (XVEC && T == 1) SBN_GEMVG(QQ, false, true);                                      \
+    else SBN_GEMVG(QQ, false, false);                                                         \
+  } while (0)
+  if (Q == 1) {
+    SBN_GEMVG_Q(1);
+  } else if (Q == 2) {
+    SBN_GEMVG_Q(2);
+  } else {
+    SBN_GEMVG_Q(3);
+  }
+#undef SBN_GEMVG_Q
+#undef SBN_GEMVG
+  return hipGetLastError();
+}
+
 // The GEMV on the compact plane, by group size.
 template <bool FUSED, bool XVEC>
 hipError_t launch_gemv_compact(const sbn_packed* h, const void* x, int64_t ld_x, int8_t* xq_out,
@@ -641,6 +672,31 @@ hipError_t launch_bitlinear_bf16_plain(const sbn_packed* h, const uint16_t* x, i
 }
 
 }  // namespace
+
+bool gemv_group_fused_fits(const sbn_packed* h0, const uint16_t* x, int64_t ld_x, int64_t T) {
+  (void)x;
+  (void)ld_x;
+  return T <= kFusedMaxT && h0->L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ;
+}
+
+hipError_t launch_gemv_group_bf16(const sbn_packed* const* hs, int count, const uint16_t* x,
+                                  int64_t ld_x, int64_t T, int8_t* xq, int64_t ld_q,
+                                  float* absmax, void* const* ys, const int64_t* ld_ys,
+                                  int out_kind, float ln_eps, hipStream_t s) {
+  GemvGroup G;
+  const int blocks = make_group(hs, count, ys, ld_ys, G);
+  const Layout& L = hs[0]->L;
+  const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
+#define SBN_GF(FF)                                                                             \
+  return xvec ? launch_gemv_group_fused<FF, true>(G, blocks, L, x, ld_x, xq, ld_q, absmax, T,   \
+                                                  out_kind, ln_eps, s)                         \
+              : launch_gemv_group_fused<FF, false>(G, blocks, L, x, ld_x, xq, ld_q, absmax, T,  \
+                                                   out_kind, ln_eps, s)
+  if (L.form == kFormSparse24) SBN_GF(kFormSparse24);
+  if (L.form == kFormPositional) SBN_GF(kFormPositional);
+  SBN_GF(kFormKept);
+#undef SBN_GF
+}
 
 hipError_t launch_bitlinear(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,

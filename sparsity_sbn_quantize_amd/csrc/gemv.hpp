@@ -152,13 +152,16 @@ __device__ __forceinline__ void store16(int8_t* row, int k, int K, bool vec, con
 // after the products) and the block's outlier planes are staged in dynamic LDS: [K] x_q bytes, then
 // [G k][16] positions, [G k][16] bf16 values, [8][16] partial sums. Each thread issues three
 // straight-line loads for the planes with the bricks (G k <= 16 nq <= 64 W pieces of each).
+//
+// rb: the row block this workgroup computes (of the weight whose planes, scale and output are
+// passed); xq_writer: this workgroup writes x_q and a' (FUSED; exactly one workgroup of a launch).
 template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF, bool OUTL = false>
 __device__ __forceinline__ void gemv_body(
     const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
     const Layout& L, const int K, const int nq, const int W, const float* __restrict__ gamma_p,
     const void* __restrict__ xin, int64_t ld_x, int8_t* __restrict__ xq_out, int64_t ld_q,
     float* __restrict__ absmax, int64_t T, void* __restrict__ y, int64_t ld_y, int out_kind,
-    float ln_eps, const uint8_t* __restrict__ opos = nullptr,
+    float ln_eps, const int64_t rb, const bool xq_writer, const uint8_t* __restrict__ opos = nullptr,
     const uint16_t* __restrict__ oval = nullptr, int KO = 0) {
   static_assert(!OUTL || (XBUF && !LN && (FUSED || XVEC)), "outliers: one-token launches only");
   __shared__ v4i red[kGemvMaxWaves][64];
@@ -173,7 +176,6 @@ __device__ __forceinline__ void gemv_body(
   // directly (otherwise each load sits in a loop over the lanes' distinct offsets)
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int64_t rb = blockIdx.x;
   const int t = lane & 15, g = lane >> 4;
   const bool tok_ok = t < (int)T;
 
@@ -457,7 +459,7 @@ __device__ __forceinline__ void gemv_body(
           if constexpr (OUTL) {
             if (k < K) reinterpret_cast<uint32_t*>(gemv_dyn)[k >> 2] = qw;  // K % 256 == 0
           }
-          if (rb == 0 && tt < (int)T && k < K) {
+          if (xq_writer && tt < (int)T && k < K) {
             int8_t* dst = xq_out + tt * ld_q + k;
             if (vq && k + 4 <= K) {
               *reinterpret_cast<uint32_t*>(dst) = qw;
@@ -473,7 +475,7 @@ __device__ __forceinline__ void gemv_body(
                                                         4 * b_chunk<FORM>(g, j))
                         : v4i{0, 0, 0, 0};
       }
-      if (rb == 0 && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
+      if (xq_writer && wave == 0 && g == 0 && tok_ok) absmax[t] = a_t;
     }
 
 #pragma unroll
@@ -602,7 +604,70 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv(
     void* __restrict__ y, int64_t ld_y, int out_kind, float ln_eps) {
   gemv_body<FORM, FUSED, XVEC, Q, LN, XBUF>(mask_plane, code_plane, L, (int)L.K, (int)L.quads,
                                             (int)(blockDim.x >> 6), gamma_p, xin, ld_x, xq_out,
-                                            ld_q, absmax, T, y, ld_y, out_kind, ln_eps);
+                                            ld_q, absmax, T, y, ld_y, out_kind, ln_eps,
+                                            (int64_t)blockIdx.x, blockIdx.x == 0);
+}
+
+// Grouped GEMV: several packed weights that share K, the pattern and the code form, and read the
+// same activations (e.g. the Q, K and V projections of a block, or its gate and up projections),
+// in one launch. The workgroups of member i are [rb_end[i-1], rb_end[i]); each computes one row
+// block of its member with that member's planes, scale and output, exactly as a launch on that
+// weight alone would.
+constexpr int kMaxGroup = 8;
+struct GemvMember {
+  const uint8_t* codes;  // code plane (or compact plane) of the member
+  const uint8_t* mask;   // mask plane (kept form), or nullptr
+  const float* gamma;    // the scale the matmul multiplies by
+  void* y;               // output [T][ld_y]
+  int64_t ld_y;
+  int64_t n_out;
+  int rb_end;            // one past the member's last workgroup
+};
+struct GemvGroup {
+  GemvMember m[kMaxGroup];
+  int count;
+};
+
+// Fills a group from packed weights that share K, the pattern and the code form (not the compact
+// plane); returns the launch's workgroup count.
+inline int make_group(const sbn_packed* const* hs, int count, void* const* ys,
+                      const int64_t* ld_ys, GemvGroup& G) {
+  int end = 0;
+  for (int i = 0; i < kMaxGroup; ++i) {
+    GemvMember& m = G.m[i];
+    if (i < count) {
+      end += (int)hs[i]->L.row_blocks;
+      m = GemvMember{hs[i]->codes, hs[i]->mask, hs[i]->gamma_out(), ys[i], ld_ys[i],
+                     hs[i]->L.n_out, end};
+    } else {
+      m = GemvMember{nullptr, nullptr, nullptr, nullptr, 0, 0, end};
+    }
+  }
+  G.count = count;
+  return end;
+}
+
+// The member of workgroup b (uniform) and its row block within that member.
+__device__ __forceinline__ int group_member(const GemvGroup& G, int b, int64_t& rb) {
+  int i = 0;
+  while (i + 1 < G.count && b >= G.m[i].rb_end) ++i;
+  rb = b - (i > 0 ? G.m[i - 1].rb_end : 0);
+  return i;
+}
+
+template <int FORM, bool FUSED, bool XVEC, int Q, bool LN, bool XBUF>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_group(
+    GemvGroup G, Layout L, const void* __restrict__ xin, int64_t ld_x,
+    int8_t* __restrict__ xq_out, int64_t ld_q, float* __restrict__ absmax, int64_t T,
+    int out_kind, float ln_eps) {
+  int64_t rb;
+  const int i = group_member(G, (int)blockIdx.x, rb);
+  Layout Lm = L;
+  Lm.n_out = G.m[i].n_out;
+  gemv_body<FORM, FUSED, XVEC, Q, LN, XBUF>(G.m[i].mask, G.m[i].codes, Lm, (int)L.K,
+                                            (int)L.quads, (int)(blockDim.x >> 6), G.m[i].gamma,
+                                            xin, ld_x, xq_out, ld_q, absmax, T, G.m[i].y,
+                                            G.m[i].ld_y, out_kind, ln_eps, rb, blockIdx.x == 0);
 }
 
 // The one-token bf16 step with the k:256 outlier term (fp32 output; planes [G k][n_out]).
@@ -614,8 +679,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_outl(
     const uint8_t* __restrict__ opos, const uint16_t* __restrict__ oval, int KO) {
   gemv_body<FORM, true, true, Q, false, true, true>(
       mask_plane, code_plane, L, (int)L.K, (int)L.quads, (int)(blockDim.x >> 6), gamma_p, xin,
-      (int64_t)L.K, xq_out, ld_q, absmax, 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f, opos, oval,
-      KO);
+      (int64_t)L.K, xq_out, ld_q, absmax, 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f,
+      (int64_t)blockIdx.x, blockIdx.x == 0, opos, oval, KO);
 }
 
 // Dynamic LDS of bitlinear_gemv_outl.

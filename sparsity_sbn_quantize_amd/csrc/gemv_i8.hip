@@ -20,7 +20,22 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8(
   gemv_body<FORM, false, XVEC, Q, false, XBUF>(mask_plane, code_plane, L, K, nq, W, gamma_p, xin,
                                                (int64_t)ld_x, nullptr, 0,
                                                const_cast<float*>(absmax), (int64_t)T, y, ld_y,
-                                               out_kind, 0.0f);
+                                               out_kind, 0.0f, (int64_t)blockIdx.x, false);
+}
+
+// The grouped int8 GEMV (members as in bitlinear_gemv_group, gemv.hpp).
+template <int FORM, bool XVEC, int Q, bool XBUF>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_group(
+    const void* __restrict__ xin, int nq, int K, int ld_x, int T, int W,
+    const float* __restrict__ absmax, GemvGroup G, Layout L, int out_kind) {
+  int64_t rb;
+  const int i = group_member(G, (int)blockIdx.x, rb);
+  Layout Lm = L;
+  Lm.n_out = G.m[i].n_out;
+  gemv_body<FORM, false, XVEC, Q, false, XBUF>(G.m[i].mask, G.m[i].codes, Lm, K, nq, W,
+                                               G.m[i].gamma, xin, (int64_t)ld_x, nullptr, 0,
+                                               const_cast<float*>(absmax), (int64_t)T, G.m[i].y,
+                                               G.m[i].ld_y, out_kind, 0.0f, rb, false);
 }
 
 // The one-token int8 GEMV with the k:256 outlier term in the same launch (fp32 output; planes
@@ -33,7 +48,8 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_outl(
     const uint8_t* __restrict__ opos, const uint16_t* __restrict__ oval, int KO) {
   gemv_body<FORM, false, true, Q, false, true, true>(
       mask_plane, code_plane, L, K, nq, W, gamma_p, xin, (int64_t)K, nullptr, 0,
-      const_cast<float*>(absmax), 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f, opos, oval, KO);
+      const_cast<float*>(absmax), 1, y, (int64_t)L.n_out, SBN_OUT_F32, 0.0f, (int64_t)blockIdx.x,
+      false, opos, oval, KO);
 }
 
 template <int FORM>
@@ -71,27 +87,33 @@ hipError_t launch_i8_outl(const sbn_packed* h, const int8_t* xq, const float* ab
 //   4096 x 11008  XBUF 6.9  / 9.2   branchy 7.5  / 9.7
 //   5120 x 13824  XBUF 16.3 / 24.2  branchy 15.3 / 21.2   (two batches)
 //   8192 x 28672  XBUF 25.9 / 40.0  branchy 26.2 / 37.9   (three batches)
-template <int FORM, bool XVEC>
-hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
-                     int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
-  const Layout& L = h->L;
-  // T > 4: the fewest quads per wave that fit (at most three), then the fewest waves at that
-  // count, so that few wave slots go empty. Same-process A/B at T = 8 / 16: 2560 x 6912 (27 quads;
-  // 14 waves of two instead of 16) 5.06 / 6.39 -> 4.78 / 5.96 us; 4096 x 11008 (43 quads; 15 waves
-  // of three instead of 16) 6.81 / 9.19 -> 6.64 / 8.87 us; unchanged for 10 quads and for batches.
-  int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+// T > 4: the fewest quads per wave that fit (at most three), then the fewest waves at that
+// count, so that few wave slots go empty. Same-process A/B at T = 8 / 16: 2560 x 6912 (27 quads;
+// 14 waves of two instead of 16) 5.06 / 6.39 -> 4.78 / 5.96 us; 4096 x 11008 (43 quads; 15 waves
+// of three instead of 16) 6.81 / 9.19 -> 6.64 / 8.87 us; unchanged for 10 quads and for batches.
+void i8_shape(const Layout& L, int64_t T, int& W, int& Q, bool& xbuf) {
+  W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
   if (T > kFusedMaxT) {
     const int64_t q = std::min<int64_t>(kGemvMaxQ, (L.quads + kGemvMaxWaves - 1) / kGemvMaxWaves);
     W = (int)std::min<int64_t>(kGemvMaxWaves, (L.quads + q - 1) / q);
   }
-  const int Q = (int)std::min<int64_t>(kGemvMaxQ, (L.quads + W - 1) / W);
+  Q = (int)std::min<int64_t>(kGemvMaxQ, (L.quads + W - 1) / W);
+  xbuf = T <= kFusedMaxT || L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ;
+}
+
+template <int FORM, bool XVEC>
+hipError_t launch_i8(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
+                     int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
+  const Layout& L = h->L;
+  int W, Q;
+  bool xbuf;
+  i8_shape(L, T, W, Q, xbuf);
   const uint8_t* plane = compact_form(FORM) ? h->cplane : h->codes;
 #define SBN_I8(QQ, XB)                                                                         \
   hipLaunchKernelGGL((bitlinear_gemv_i8<FORM, XVEC, QQ, XB>), dim3((unsigned)L.row_blocks),     \
                      dim3(64 * W), 0, s, plane, static_cast<const void*>(xq), (int)L.quads,      \
                      (int)L.K, (int)ld_q, (int)T, W, absmax, h->gamma_out(), h->mask, L, y,      \
                      ld_y, out_kind)
-  const bool xbuf = T <= kFusedMaxT || L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ;
 #define SBN_I8_Q(QQ)                                                                           \
   do {                                                                                         \
     if (xbuf) SBN_I8(QQ, true); else SBN_I8(QQ, false);                                        \
@@ -125,7 +147,56 @@ hipError_t launch_i8_form(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   return launch_i8<kFormKept, XVEC>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }
 
+template <int FORM, bool XVEC>
+hipError_t launch_i8_group(const GemvGroup& G, int blocks, const Layout& L, const int8_t* xq,
+                           int64_t ld_q, const float* absmax, int64_t T, int out_kind,
+                           hipStream_t s) {
+  int W, Q;
+  bool xbuf;
+  i8_shape(L, T, W, Q, xbuf);
+#define SBN_I8G(QQ, XB)                                                                        \
+  hipLaunchKernelGGL((bitlinear_gemv_i8_group<FORM, XVEC, QQ, XB>), dim3((unsigned)blocks),     \
+                     dim3(64 * W), 0, s, static_cast<const void*>(xq), (int)L.quads, (int)L.K,   \
+                     (int)ld_q, (int)T, W, absmax, G, L, out_kind)
+#define SBN_I8G_Q(QQ)                                                                          \
+  do {                                                                                         \
+    if (xbuf) SBN_I8G(QQ, true); else SBN_I8G(QQ, false);                                      \
+  } while (0)
+  if (Q == 1) {
+    SBN_I8G_Q(1);
+  } else if (Q == 2) {
+    SBN_I8G_Q(2);
+  } else {
+    SBN_I8G_Q(3);
+  }
+#undef SBN_I8G_Q
+#undef SBN_I8G
+  return hipGetLastError();
+}
+
+template <bool XVEC>
+hipError_t launch_i8_group_form(const GemvGroup& G, int blocks, const Layout& L,
+                                const int8_t* xq, int64_t ld_q, const float* absmax, int64_t T,
+                                int out_kind, hipStream_t s) {
+  if (L.form == kFormSparse24)
+    return launch_i8_group<kFormSparse24, XVEC>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
+  if (L.form == kFormPositional)
+    return launch_i8_group<kFormPositional, XVEC>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
+  return launch_i8_group<kFormKept, XVEC>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
+}
+
 }  // namespace
+
+hipError_t launch_gemv_int8_group(const sbn_packed* const* hs, int count, const int8_t* xq,
+                                  int64_t ld_q, const float* absmax, int64_t T, void* const* ys,
+                                  const int64_t* ld_ys, int out_kind, hipStream_t s) {
+  GemvGroup G;
+  const int blocks = make_group(hs, count, ys, ld_ys, G);
+  const Layout& L = hs[0]->L;
+  const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (L.K % 16 == 0);
+  if (xvec) return launch_i8_group_form<true>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
+  return launch_i8_group_form<false>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
+}
 
 bool gemv_int8_outl_fits(const sbn_packed* h, const int8_t* xq, int64_t T) {
   const Layout& L = h->L;

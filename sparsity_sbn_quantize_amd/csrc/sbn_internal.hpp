@@ -98,6 +98,18 @@ hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
                                  int out_kind, float ln_eps, hipStream_t s);
 
+// Grouped launches over weights that share K, the pattern and the code form (no compact plane,
+// no outlier term; checked by the caller): the int8 GEMV (T <= 16) and the one-kernel bf16 step
+// (gemv_group_fused_fits). ys, ld_ys: host arrays of the members' outputs.
+hipError_t launch_gemv_int8_group(const sbn_packed* const* hs, int count, const int8_t* xq,
+                                  int64_t ld_q, const float* absmax, int64_t T, void* const* ys,
+                                  const int64_t* ld_ys, int out_kind, hipStream_t s);
+bool gemv_group_fused_fits(const sbn_packed* h0, const uint16_t* x, int64_t ld_x, int64_t T);
+hipError_t launch_gemv_group_bf16(const sbn_packed* const* hs, int count, const uint16_t* x,
+                                  int64_t ld_x, int64_t T, int8_t* xq, int64_t ld_q,
+                                  float* absmax, void* const* ys, const int64_t* ld_ys,
+                                  int out_kind, float ln_eps, hipStream_t s);
+
 // Raises a kernel's dynamic-LDS limit once per process and kernel (gfx950 has 160 KB of LDS per
 // CU).
 inline hipError_t allow_smem_ptr(const void* kernel, size_t bytes) {

@@ -27,6 +27,7 @@ def test_exports_match_header(lib):
                              "sbn_packed_export_outliers",
                              "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error",
+                             "sbn_bitlinear_fwd_group", "sbn_bitlinear_fwd_group_bf16",
                              "sbn_ceiling_stream_read", "sbn_ceiling_mfma_i8", "sbn_ceiling_empty"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -108,6 +109,16 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_bitlinear_fwd_ln_bf16(None, None, 0, 1, 0.0, None, 0, None, None, 0, 0,
                                          None) == ERR_INVALID
     lib.sbn_free(None)  # no-op
+    one = (ctypes.c_void_p * 1)(None)
+    ld1 = (ctypes.c_int64 * 1)(16)
+    assert lib.sbn_bitlinear_fwd_group(None, 1, None, 16, None, 1, one, ld1, 0, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_group(one, 1, None, 16, None, 1, one, ld1, 0, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_group(one, 0, None, 16, None, 1, one, ld1, 0, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_group(one, 9, None, 16, None, 1, one, ld1, 0, None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_group_bf16(one, 1, None, 16, 1, 0.0, None, 16, None, one, ld1, 0,
+                                            None) == ERR_INVALID
+    assert lib.sbn_bitlinear_fwd_group_bf16(None, 1, None, 16, 1, 0.0, None, 16, None, one, ld1,
+                                            0, None) == ERR_INVALID
     sink = ctypes.c_void_p(16)
     ops = ctypes.c_double(0)
     assert lib.sbn_ceiling_stream_read(None, 1024, 1, sink, None) == ERR_INVALID
