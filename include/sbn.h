@@ -23,13 +23,17 @@
  *   - Pointers are DEVICE pointers unless marked (host). Device memory belongs to the caller,
  *     except the packed-weight handle, which the library owns.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls only enqueue
- *     work on it; none synchronizes the device (except sbn_free, see there).
+ *     work on it; none synchronizes the device (except sbn_packed_query and, on devices without
+ *     memory pools, sbn_free; see there).
  *   - Arguments are validated on the host before any HIP call; a rejected call touches no GPU
  *     state and returns a negative sbn_status. sbn_last_error() then holds a message.
  *   - Shapes: T tokens, K input features (reduction axis), n_out output features. Leading
  *     dimensions (ld_*) are in elements and must be >= the row length.
  *   - NaN or Inf inputs give unspecified (but memory-safe) results.
  *   - The handle's device must be the current device for every call that uses it.
+ *   - Calls that use one handle must be ordered (one stream, or synchronized by the caller): a
+ *     forward that splits K over two workgroups per tile keeps its handshake words in the handle,
+ *     and a re-pack rewrites the planes a forward reads.
  */
 #ifndef SBN_H
 #define SBN_H
@@ -99,8 +103,8 @@ sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t
  *   keep: in each group of m consecutive weights along K of a row, the n largest |w|, equal
  *         magnitudes going to the lower position.
  *   code  = keep ? (|w| > gamma/2 ? sign(w) : 0) : 0   (= RoundClip(w/gamma, -1, 1), ties to even)
- *   *handle == NULL: a handle is allocated (hipMalloc; the only allocation the library makes)
- *   and returned in *handle (host). Otherwise the existing handle is re-packed in place, with no
+ *   *handle == NULL: a handle is allocated (stream-ordered on `stream` where the device has memory
+ *   pools; with sbn_free, the only allocations the library makes) and returned in *handle (host). Otherwise the existing handle is re-packed in place, with no
  *   allocation; it must have been made with the same n_out, K, n_keep, m_group (else
  *   SBN_ERR_SHAPE). Every call recomputes gamma and the mask from the current weights.
  * Requires m_group in {4, 8, 16}, 1 <= n_keep <= m_group, K % m_group == 0,
@@ -249,7 +253,10 @@ sbn_status sbn_bitlinear_bwd_dx(const sbn_packed* w, const uint16_t* dy_bf16, in
                                 int64_t T, float* dx, int64_t ld_dx, void* stream);
 
 /*
- * Releases a handle: waits for the last stream that used it, then frees its device memory.
+ * Releases a handle. Where the device supports memory pools (MI355X does), its device memory was
+ * allocated stream-ordered and is released stream-ordered on the last stream that used the handle,
+ * without blocking the host; otherwise this waits for that stream, then frees. Work on other
+ * streams that still uses the handle must be ordered before that stream by the caller.
  * sbn_free(NULL) is a no-op.
  */
 void sbn_free(sbn_packed* handle);
@@ -333,9 +340,16 @@ typedef struct {
   int compact;                           /* the last pack wrote the compact form */
   int outlier_k;                         /* k of the last pack's k:256 outliers (0: none) */
   size_t rank_row_bytes;                 /* rank export row size, ceil((K/m)(R + 2n)/8) */
+  uint32_t splitk_giveups;               /* split-K waits that gave up (0 in a correct run) */
 } sbn_packed_desc;
 
-/* Describes a handle; `out` is a host pointer. */
+/*
+ * Describes a handle; `out` is a host pointer. To read splitk_giveups it waits for the handle's
+ * last stream. A forward that runs two workgroups per output tile (each half of K; launches with
+ * few tiles) passes partial sums through a handshake whose waiting half spins a bounded time; if
+ * it ever gives up, that tile is wrong and this counter, kept in the handle's device memory, says
+ * how many times it happened.
+ */
 sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out /* host */);
 
 /* The message of the last failed call on this host thread ("" if none). */

@@ -37,7 +37,7 @@ class PackedDesc(ctypes.Structure):
                 ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t),
                 ("compact_row_bytes", ctypes.c_size_t), ("compact_bytes", ctypes.c_size_t),
                 ("compact", ctypes.c_int), ("outlier_k", ctypes.c_int),
-                ("rank_row_bytes", ctypes.c_size_t)]
+                ("rank_row_bytes", ctypes.c_size_t), ("splitk_giveups", ctypes.c_uint32)]
 
 
 _lib = None
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
     """Loads libsbn.so (built in-tree); raises if it is missing."""
     global _lib
     if _lib is None:
+        # torch first: the process then holds torch's HIP runtime, which libsbn.so binds to (a
+        # library loaded before torch would bring in another copy of the runtime)
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it first "
                               "(python -c 'import __graft_entry__ as g; g.build()')")
@@ -387,3 +390,4 @@ def bitlinear_group_bf16(x, ws, out: str = "f32", ys=None, x_q=None, x_absmax=No
                                              float(ln_eps), _ptr(x_q), _ld(x_q, K),
                                              _ptr(x_absmax), outs, lds, kind, _stream(stream)))
     return ys, x_q, x_absmax
+

@@ -25,6 +25,9 @@ sbn_status fail(sbn_status code, const char* fmt, ...) {
 }  // namespace
 
 namespace sbn {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
 sbn_status set_error(sbn_status code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -32,6 +35,119 @@ sbn_status set_error(sbn_status code, const char* fmt, ...) {
   va_end(ap);
   return code;
 }
+
+sbn_status make_plan(int64_t n_out, int64_t K, int n, int m, Plan& p) {
+  Layout& L = p.L;
+  L.n_out = n_out;
+  L.K = K;
+  L.n = n;
+  L.m = m;
+  L.positional = positional_codes(n, m) ? 1 : 0;
+  L.form = L.positional ? kFormPositional : kFormKept;
+  // 2:4 uses the structured-sparse MFMA operands unless SBN_NO_SMFMAC is set to a non-zero value
+  // (a diagnostic switch for comparing against the dense MFMA path).
+  const char* no_sp = getenv("SBN_NO_SMFMAC");
+  if (n == 2 && m == 4 && !(no_sp && atoi(no_sp) != 0)) L.form = kFormSparse24;
+  L.code_brick_bytes = L.positional ? 16 : 16 * n / m;
+  L.has_mask = n < m ? 1 : 0;
+  L.row_blocks = (n_out + 15) / 16;
+  L.row_blocks_pad = (L.row_blocks + kPadRowBlocks - 1) / kPadRowBlocks * kPadRowBlocks;
+  L.quads = ((K + kBrickK - 1) / kBrickK + 3) / 4;
+  L.csb = kBrickK * n / m;
+  if (16 * n % m != 0)
+    return set_error(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: pattern %d:%d", n, m);
+  const size_t slots = (size_t)L.row_blocks_pad * (size_t)L.quads * 64;
+  p.num_partials = absmean_blocks(n_out);
+  p.mask_bytes = L.has_mask ? slots * 8 : 0;
+  p.code_bytes = slots * (size_t)L.code_brick_bytes;
+  size_t off = 0;
+  p.off_mask = off;
+  off = align_up(off + p.mask_bytes, 256);
+  p.off_codes = off;
+  off = align_up(off + p.code_bytes, 256);
+  p.off_gamma = off;
+  off = align_up(off + sizeof(float), 256);
+  p.off_part = off;
+  off = align_up(off + sizeof(double) * p.num_partials, 256);
+  p.off_sync = off;
+  off = align_up(off + sizeof(uint32_t) * (kGemmSyncInts + 1), 256);
+  p.off_flips = off;
+  off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
+  p.off_vc = off;
+  off = align_up(off + 2 * sizeof(uint32_t) * slots / 16, 256);
+  p.off_gamma_vc = off;
+  off = align_up(off + sizeof(float), 256);
+  p.forward_bytes = off;  // everything the pack and the forward use
+  p.rq_count = (n_out + 127) / 128;
+  p.off_tplane = off;
+  off = align_up(off + (size_t)p.rq_count * (size_t)L.quads * 8192, 256);
+  p.cplane_bytes =
+      (size_t)L.row_blocks_pad * (size_t)L.quads * (size_t)compact_quad_bytes(L.csb) +
+      kCompactSlack;
+  p.off_cplane = off;
+  off = align_up(off + p.cplane_bytes, 256);
+  // structured-outlier planes (for up to 16 per 256 weights), when K is a multiple of 256
+  p.oplanes = K % 256 == 0;
+  const size_t ogroups = p.oplanes ? (size_t)n_out * (size_t)(K / 256) : 0;
+  p.off_opos = off;
+  off = align_up(off + ogroups * 16, 256);
+  p.off_oval = off;
+  off = align_up(off + ogroups * 16 * sizeof(uint16_t), 256);
+  p.off_omask = off;
+  off = align_up(off + (p.oplanes ? slots * 8 : 0), 256);
+  p.off_osum = off;
+  off = align_up(off + ogroups * sizeof(double), 256);
+  p.total_bytes = off;
+  return SBN_OK;
+}
+
+void bind_planes(sbn_packed& h, const Plan& p, uint8_t* base) {
+  const Layout& L = p.L;
+  h.L = L;
+  h.code_row_bytes = (size_t)((L.K / L.m) * 2 * L.n + 7) / 8;
+  h.mask_row_bytes = L.has_mask ? (size_t)(L.K + 7) / 8 : 0;
+  h.mask_plane_bytes = p.mask_bytes;
+  h.code_plane_bytes = p.code_bytes;
+  h.num_partials = p.num_partials;
+  h.base = base;
+  h.base_bytes = p.total_bytes;
+  h.mask = L.has_mask ? base + p.off_mask : nullptr;
+  h.codes = base + p.off_codes;
+  h.gamma = reinterpret_cast<float*>(base + p.off_gamma);
+  h.partials = reinterpret_cast<double*>(base + p.off_part);
+  h.gemm_sync = reinterpret_cast<uint32_t*>(base + p.off_sync);
+  h.flip_parts = reinterpret_cast<uint32_t*>(base + p.off_flips);
+  h.vc_parts = reinterpret_cast<uint32_t*>(base + p.off_vc);
+  h.gamma_vc = reinterpret_cast<float*>(base + p.off_gamma_vc);
+  h.vc = false;
+  h.tplane = reinterpret_cast<uint32_t*>(base + p.off_tplane);
+  h.rq_count = p.rq_count;
+  h.cplane = base + p.off_cplane;
+  h.cplane_bytes = p.cplane_bytes;
+  h.compact_row_bytes = (size_t)(((L.K / L.m) * (L.m + L.n) + 7) / 8);
+  h.compact = false;
+  h.outlier_k = 0;
+  h.outlier_planes = p.oplanes;
+  h.opos = base + p.off_opos;
+  h.oval = reinterpret_cast<uint16_t*>(base + p.off_oval);
+  h.omask = reinterpret_cast<unsigned long long*>(base + p.off_omask);
+  h.osum = reinterpret_cast<double*>(base + p.off_osum);
+  h.splitk_spin_limit = kSplitSpinLimit;
+  h.splitk_publish = 1;
+}
+
+void splitk_settings(int& spin_limit, int& publish) {
+  // Test settings of the split-K handshake: SBN_SPLITK_SPIN_LIMIT (s_sleep rounds a waiting half
+  // spins before it gives up) and SBN_SPLITK_WITHHOLD=1 (the first half never publishes, so every
+  // waiting half gives up: exercises the give-up counter with every kernel exiting normally).
+  spin_limit = kSplitSpinLimit;
+  publish = 1;
+  const char* lim = getenv("SBN_SPLITK_SPIN_LIMIT");
+  if (lim && atoi(lim) > 0) spin_limit = atoi(lim);
+  const char* wh = getenv("SBN_SPLITK_WITHHOLD");
+  if (wh && atoi(wh) != 0) publish = 0;
+}
+
 }  // namespace sbn
 
 namespace {
@@ -39,8 +155,6 @@ namespace {
 sbn_status hip_fail(hipError_t e, const char* what) {
   return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
-
-size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool pattern_ok(int n, int m) { return (m == 4 || m == 8 || m == 16) && n >= 1 && n <= m; }
 
@@ -280,118 +394,42 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
                   (long long)h->L.n_out, (long long)h->L.K, h->L.n, h->L.m, (long long)n_out,
                   (long long)K, n_keep, m_group);
   } else {
-    sbn::Layout L;
-    L.n_out = n_out;
-    L.K = K;
-    L.n = n_keep;
-    L.m = m_group;
-    L.positional = sbn::positional_codes(n_keep, m_group) ? 1 : 0;
-    L.form = L.positional ? sbn::kFormPositional : sbn::kFormKept;
-    // 2:4 uses the structured-sparse MFMA operands unless SBN_NO_SMFMAC is set to a non-zero
-    // value (a diagnostic switch for comparing against the dense MFMA path).
-    const char* no_sp = getenv("SBN_NO_SMFMAC");
-    if (n_keep == 2 && m_group == 4 && !(no_sp && atoi(no_sp) != 0)) L.form = sbn::kFormSparse24;
-    L.code_brick_bytes = L.positional ? 16 : 16 * n_keep / m_group;
-    L.has_mask = n_keep < m_group ? 1 : 0;
-    L.row_blocks = (n_out + 15) / 16;
-    L.row_blocks_pad = (L.row_blocks + sbn::kPadRowBlocks - 1) / sbn::kPadRowBlocks *
-                       sbn::kPadRowBlocks;
-    L.quads = ((K + sbn::kBrickK - 1) / sbn::kBrickK + 3) / 4;
-    L.csb = sbn::kBrickK * n_keep / m_group;
-    if (16 * n_keep % m_group != 0)
-      return fail(SBN_ERR_UNSUPPORTED, "sbn_pack_nm_ternary: pattern %d:%d", n_keep, m_group);
-    const size_t slots = (size_t)L.row_blocks_pad * (size_t)L.quads * 64;
-    const int num_partials = sbn::absmean_blocks(n_out);
-    const size_t mask_bytes = L.has_mask ? slots * 8 : 0;
-    const size_t code_bytes = slots * (size_t)L.code_brick_bytes;
-    size_t off = 0;
-    const size_t off_mask = off;
-    off = align_up(off + mask_bytes, 256);
-    const size_t off_codes = off;
-    off = align_up(off + code_bytes, 256);
-    const size_t off_gamma = off;
-    off = align_up(off + sizeof(float), 256);
-    const size_t off_part = off;
-    off = align_up(off + sizeof(double) * num_partials, 256);
-    const size_t off_sync = off;
-    off = align_up(off + sizeof(int) * sbn::kGemmSyncInts, 256);
-    const size_t off_flips = off;
-    off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
-    const size_t off_vc = off;
-    off = align_up(off + 2 * sizeof(uint32_t) * slots / 16, 256);
-    const size_t off_gamma_vc = off;
-    off = align_up(off + sizeof(float), 256);
-    const int64_t rq_count = (n_out + 127) / 128;
-    const size_t off_tplane = off;
-    off = align_up(off + (size_t)rq_count * (size_t)L.quads * 8192, 256);
-    const size_t cplane_bytes =
-        (size_t)L.row_blocks_pad * (size_t)L.quads * (size_t)sbn::compact_quad_bytes(L.csb) +
-        sbn::kCompactSlack;
-    const size_t off_cplane = off;
-    off = align_up(off + cplane_bytes, 256);
-    // structured-outlier planes (for up to 16 per 256 weights), when K is a multiple of 256
-    const bool oplanes = K % 256 == 0;
-    const size_t ogroups = oplanes ? (size_t)n_out * (size_t)(K / 256) : 0;
-    const size_t off_opos = off;
-    off = align_up(off + ogroups * 16, 256);
-    const size_t off_oval = off;
-    off = align_up(off + ogroups * 16 * sizeof(uint16_t), 256);
-    const size_t off_omask = off;
-    off = align_up(off + (oplanes ? slots * 8 : 0), 256);
-    const size_t off_osum = off;
-    off = align_up(off + ogroups * sizeof(double), 256);
-
-    h = new (std::nothrow) sbn_packed;
+    sbn::Plan p;
+    sbn_status st = sbn::make_plan(n_out, K, n_keep, m_group, p);
+    if (st != SBN_OK) return st;
+    h = new (std::nothrow) sbn_packed();
     if (!h) return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: host allocation failed");
-    h->L = L;
-    h->code_row_bytes = (size_t)((K / m_group) * 2 * n_keep + 7) / 8;
-    h->mask_row_bytes = L.has_mask ? (size_t)(K + 7) / 8 : 0;
-    h->mask_plane_bytes = mask_bytes;
-    h->code_plane_bytes = code_bytes;
-    h->num_partials = num_partials;
-    h->base_bytes = off;
-    h->last_stream = s;
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) {
       delete h;
       return hip_fail(e, "sbn_pack_nm_ternary: hipGetDevice");
     }
-    e = hipMalloc(&h->base, h->base_bytes);
+    // Stream-ordered allocation where the device has memory pools (released by sbn_free on the
+    // handle's last stream without blocking the host); a plain allocation otherwise.
+    int pools = 0;
+    (void)hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, h->device);
+    uint8_t* base = nullptr;
+    h->async_alloc = pools != 0;
+    e = h->async_alloc ? hipMallocAsync(reinterpret_cast<void**>(&base), p.total_bytes, s)
+                       : hipMalloc(reinterpret_cast<void**>(&base), p.total_bytes);
     if (e != hipSuccess) {
       delete h;
       (void)hipGetLastError();
-      return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: hipMalloc(%zu) failed", off);
+      return fail(SBN_ERR_OOM, "sbn_pack_nm_ternary: device allocation of %zu bytes failed",
+                  p.total_bytes);
     }
-    // Padding bricks are never written by the pack kernel and must read as zero.
-    e = hipMemsetAsync(h->base, 0, h->base_bytes, s);
+    // Padding bricks are never written by the pack kernel and must read as zero; the split-K
+    // words start at zero.
+    e = hipMemsetAsync(base, 0, p.total_bytes, s);
     if (e != hipSuccess) {
-      (void)hipFree(h->base);
+      if (h->async_alloc) (void)hipFreeAsync(base, s); else (void)hipFree(base);
       delete h;
       return hip_fail(e, "sbn_pack_nm_ternary: hipMemsetAsync");
     }
-    h->mask = L.has_mask ? h->base + off_mask : nullptr;
-    h->codes = h->base + off_codes;
-    h->gamma = reinterpret_cast<float*>(h->base + off_gamma);
-    h->partials = reinterpret_cast<double*>(h->base + off_part);
-    h->gemm_sync = reinterpret_cast<int*>(h->base + off_sync);
-    h->flip_parts = reinterpret_cast<uint32_t*>(h->base + off_flips);
-    h->vc_parts = reinterpret_cast<uint32_t*>(h->base + off_vc);
-    h->gamma_vc = reinterpret_cast<float*>(h->base + off_gamma_vc);
-    h->vc = false;
-    h->tplane = reinterpret_cast<uint32_t*>(h->base + off_tplane);
-    h->rq_count = rq_count;
-    h->cplane = h->base + off_cplane;
-    h->cplane_bytes = cplane_bytes;
-    h->compact_row_bytes = (size_t)(((K / m_group) * (m_group + n_keep) + 7) / 8);
-    h->compact = false;
-    h->outlier_k = 0;
-    h->outlier_planes = oplanes;
-    h->opos = h->base + off_opos;
-    h->oval = reinterpret_cast<uint16_t*>(h->base + off_oval);
-    h->omask = reinterpret_cast<unsigned long long*>(h->base + off_omask);
-    h->osum = reinterpret_cast<double*>(h->base + off_osum);
+    sbn::bind_planes(*h, p, base);
     *handle = h;
   }
+  sbn::splitk_settings(h->splitk_spin_limit, h->splitk_publish);
   h->last_stream = s;
   h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
   h->vc = (flags & SBN_PACK_VARIANCE_CORRECTION) != 0;
@@ -449,8 +487,12 @@ sbn_status sbn_bitlinear_fwd_ln_bf16(const sbn_packed* w, const uint16_t* x_bf16
 
 void sbn_free(sbn_packed* handle) {
   if (!handle) return;
-  (void)hipStreamSynchronize(handle->last_stream);
-  (void)hipFree(handle->base);
+  if (handle->async_alloc) {
+    (void)hipFreeAsync(handle->base, handle->last_stream);
+  } else {
+    (void)hipStreamSynchronize(handle->last_stream);
+    (void)hipFree(handle->base);
+  }
   delete handle;
 }
 
@@ -559,6 +601,14 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
   out->rank_row_bytes =
       (size_t)(((w->L.K / w->L.m) * (sbn::rank_bits((int)w->L.n, (int)w->L.m) + 2 * w->L.n) + 7) /
                8);
+  // the split-K give-up counter, read after the handle's last stream has drained
+  uint32_t giveups = 0;
+  hipError_t e = hipStreamSynchronize(w->last_stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(&giveups, w->gemm_sync + sbn::kGemmSyncInts, sizeof(giveups),
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "sbn_packed_query");
+  out->splitk_giveups = giveups;
   return SBN_OK;
 }
 

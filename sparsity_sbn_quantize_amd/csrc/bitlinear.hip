@@ -49,18 +49,23 @@ constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + 
 
 // Split-K (two workgroups per tile, each half of K) for launches that have few tiles even at CF = 4. The halves of a
 // tile are adjacent in the XCD order (same L2). Per tile and wave, the first half to finish
-// stores its int32 partial sums in the tile's region of y and raises a flag; the second waits
-// for the flag (a bounded spin: the first is already past its main loop, so it is running), adds
-// the partial and writes the result. Integer sums make the result independent of the order. The
-// two flag words per tile and wave live in the weight handle and are cleared by the second half,
-// so calls that share a handle must be ordered (one stream, or synchronized). Sharing tiles more
+// stores its int32 partial sums in the tile's region of y and publishes them; the second waits
+// (a bounded spin: the first is already past its main loop, so it is running), adds the partial
+// and writes the result. Integer sums make the result independent of the order. Each (tile, wave)
+// slot has two words in the weight handle, never reset: an arrival counter (each launch adds 2,
+// so the old value's parity says which half came first and its half is the slot's launch count)
+// and the launch count the partial sums were last published for; the second half waits for its
+// own launch's count, so a value left by an earlier launch (or by a half that gave up waiting)
+// never matches, and graph replays need no host-side state. A half that gives up adds 1 to the
+// handle's give-up counter (sbn_packed_query) and stores a wrong tile. Arrivals of two launches
+// that share a handle must not interleave, so such calls must be ordered (one stream, or
+// synchronized). Sharing tiles more
 // widely (a contiguous share of all tiles' K steps for every resident workgroup, or three
 // workgroups per tile) was measured slower on the 2048- and 8192-token shapes: the partial sums
 // then move about as many bytes as the fp32 output, all at the same moment.
 constexpr int kOutPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: output stores
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
-constexpr int kSpinLimit = 1 << 24;    // s_sleep rounds before a waiting half gives up
-static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K flags of the handle");
+static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K words of the handle");
 
 template <int FORM, bool XVEC, int CF>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -68,7 +73,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
                     Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
                     int64_t ld_q, const float* __restrict__ absmax, int64_t T,
                     void* __restrict__ y, int64_t ld_y, int out_kind, int tiles_n, int tiles_t,
-                    int ksplit, int* __restrict__ sync) {
+                    int ksplit, uint32_t* __restrict__ sync, int spin_limit, int publish) {
   constexpr int kGemmCF = CF;                             // 16-token fragments per tile
   constexpr int kGemmTok = CF * 16;                       // tokens per tile
   constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile
@@ -334,17 +339,20 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     // Every access of the handshake is coherent across the XCDs' L2 caches on its own (sc1:
     // relaxed agent-scope atomics for the flags, sc1 buffer accesses for the partial sums);
     // acquire/release fences would instead write back or invalidate whole L2s. Order: the
-    // partial sums are stored, the wave waits until its stores have completed, then raises the
-    // flag; the other half reads the partial sums only after it has seen the flag.
+    // partial sums are stored, the wave waits until its stores have completed, then publishes
+    // its launch count; the other half reads the partial sums only after it has seen that count.
     constexpr int kSc1 = 1 << 4;  // buffer cache-policy bit: sc1
-    int* const flag = sync + 2 * ((int64_t)tile_lin * kGemmWaves + wave);
+    uint32_t* const arrive = sync + 2 * ((int64_t)tile_lin * kGemmWaves + wave);
+    uint32_t* const ready = arrive + 1;
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(y, (short)0, 0x7FFFFFFF, kBufDword3);
-    int first = 0;
+    uint32_t old = 0;
     if (lane == 0)
-      first = __hip_atomic_fetch_add(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
-    first = __builtin_amdgcn_readfirstlane(first);
-    if (first) {
+      old = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = (uint32_t)__builtin_amdgcn_readfirstlane((int)old);
+    // this launch's count on the slot (>= 1); the first arrival found an even count of arrivals
+    const uint32_t gen = (old >> 1) + 1u;
+    if ((old & 1u) == 0) {
 #pragma unroll
       for (int cf = 0; cf < kGemmCF; ++cf) {
         const int64_t t = t0 + cf * 16 + t_l;
@@ -366,14 +374,19 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);  // the partial sums have been written
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (lane == 0) __hip_atomic_store(flag + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0 && publish)
+        __hip_atomic_store(ready, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     if (lane == 0) {
-      for (int it = 0; it < kSpinLimit; ++it) {
-        if (__hip_atomic_load(flag + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+      int it = 0;
+      for (; it < spin_limit; ++it) {
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) break;
         __builtin_amdgcn_s_sleep(2);
       }
+      if (it == spin_limit)
+        __hip_atomic_fetch_add(sync + kGemmSyncInts, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
@@ -393,10 +406,6 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
               acc[rf][cf][i] += __builtin_amdgcn_raw_buffer_load_b32(yr, off + 4 * i, 0, kSc1);
         }
       }
-    }
-    if (lane == 0) {
-      __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(flag + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -553,7 +562,7 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
     hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC, CF>), dim3((unsigned)(gx * gy * ksplit)),     \
                        dim3(kGemmThreads), gemm_smem(CF), s, h->mask, h->codes, L,              \
                        h->gamma_out(), xq, ld_q, absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, \
-                       ksplit, h->gemm_sync);                                                  \
+                       ksplit, h->gemm_sync, h->splitk_spin_limit, h->splitk_publish);        \
   } while (0)
   if (wide) {
     SBN_GEMM(8);

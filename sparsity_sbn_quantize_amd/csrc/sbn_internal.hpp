@@ -5,8 +5,6 @@
 #include <stdint.h>
 
 #include <mutex>
-#include <utility>
-#include <vector>
 
 #include "sbn.h"
 #include "sbn_common.hpp"
@@ -22,7 +20,10 @@ struct sbn_packed {
   uint8_t* codes;      // code plane (brick fragments)
   float* gamma;        // device scalar
   double* partials;    // device workspace [num_partials]
-  int* gemm_sync;      // split-K flags: kGemmSyncInts words, zero between calls
+  uint32_t* gemm_sync;  // split-K words: kGemmSyncInts (two per slot, never reset), then the
+                        // give-up counter
+  int splitk_spin_limit;  // s_sleep rounds before a waiting split-K half gives up
+  int splitk_publish;     // 1; 0 only in the test mode that withholds the partial sums
   uint32_t* flip_parts;  // keep bits changed by the last pack, one count per pack wave
   uint32_t* vc_parts;   // variance correction: nonzero counts (dense, n:m) per pack wave
   float* gamma_vc;      // variance-corrected output scale (device scalar)
@@ -41,6 +42,7 @@ struct sbn_packed {
   unsigned long long* omask;  // outlier positions as one 64-bit word per brick slot
   double* osum;         // outlier |w| sums, one per selection workgroup of 256 groups
   int device;
+  bool async_alloc;     // base came from hipMallocAsync (released with hipFreeAsync)
   hipStream_t last_stream;
   // Scale the matmuls multiply by: gamma, or the variance-corrected gamma.
   float* gamma_out() const { return vc ? gamma_vc : gamma; }
@@ -51,8 +53,32 @@ namespace sbn {
 // Sets the calling thread's sbn_last_error() message (printf format) and returns `code`.
 sbn_status set_error(sbn_status code, const char* fmt, ...);
 
-// Words of split-K handshake flags a handle holds (2 per wave of up to 256 tiles x 4 waves).
+// Words of split-K handshake a handle holds (2 per wave of up to 256 tiles x 4 waves); the
+// give-up counter follows them.
 constexpr int kGemmSyncInts = 256 * 4 * 2;
+// s_sleep rounds a waiting split-K half spins before it gives up (its partner is already past its
+// main loop, so this is never reached in a correct run).
+constexpr int kSplitSpinLimit = 1 << 24;
+
+// The device memory layout of a handle for an (n_out, K, n:m) weight: offsets of the planes and
+// words in one allocation. The regions below forward_bytes are all that the pack (without the
+// compact or outlier options) and the forward use.
+struct Plan {
+  Layout L;
+  int num_partials;
+  int64_t rq_count;
+  bool oplanes;
+  size_t mask_bytes, code_bytes, cplane_bytes;
+  size_t off_mask, off_codes, off_gamma, off_part, off_sync, off_flips, off_vc, off_gamma_vc,
+      off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum;
+  size_t forward_bytes, total_bytes;
+};
+size_t align_up(size_t v, size_t a);
+sbn_status make_plan(int64_t n_out, int64_t K, int n, int m, Plan& p);
+// Points the handle's planes into `base` (laid out by the plan) and sets its defaults.
+void bind_planes(sbn_packed& h, const Plan& p, uint8_t* base);
+// The split-K test settings from the environment (SBN_SPLITK_SPIN_LIMIT, SBN_SPLITK_WITHHOLD).
+void splitk_settings(int& spin_limit, int& publish);
 
 // Number of blocks of the absmean reduction for a tensor with n_out rows (fixed per shape, so the
 // fp64 partial-sum order, and hence gamma, is reproducible run to run).
@@ -112,15 +138,24 @@ hipError_t launch_gemv_group_bf16(const sbn_packed* const* hs, int count, const 
 
 // Raises a kernel's dynamic-LDS limit once per process and kernel (gfx950 has 160 KB of LDS per
 // CU).
+// A fixed table (no heap allocation: the launchers also serve the entry point that allocates
+// nothing); a kernel past the table's end just sets its attribute on every launch.
 inline hipError_t allow_smem_ptr(const void* kernel, size_t bytes) {
   static std::mutex mu;
-  static std::vector<std::pair<const void*, size_t>> done;
+  constexpr int kSlots = 256;
+  static const void* done_k[kSlots];
+  static size_t done_b[kSlots];
+  static int count = 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (const auto& d : done)
-    if (d.first == kernel && d.second >= bytes) return hipSuccess;
+  for (int i = 0; i < count; ++i)
+    if (done_k[i] == kernel && done_b[i] >= bytes) return hipSuccess;
   hipError_t e =
       hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done.emplace_back(kernel, bytes);
+  if (e == hipSuccess && count < kSlots) {
+    done_k[count] = kernel;
+    done_b[count] = bytes;
+    ++count;
+  }
   return e;
 }
 template <typename K>

@@ -37,7 +37,7 @@ def test_split_k_unaligned():
 
 
 def test_split_k_repeated_calls_and_prefill_down():
-    """The handshake flags are reset by every call: twenty calls in a row on the 6912 -> 2560
+    """The handshake words carry over from call to call: twenty calls in a row on the 6912 -> 2560
     prefill shape give identical outputs, equal to the oracle on sampled tokens and rows."""
     import torch
     wl = inputs.W_PREFILL
@@ -56,6 +56,67 @@ def test_split_k_repeated_calls_and_prefill_down():
     assert np.array_equal(ys[0][:, rows], acc_ref)
     pw.free()
     torch.cuda.synchronize()
+
+
+def test_split_k_giveup_is_counted_and_does_not_leak(monkeypatch):
+    """A waiting half that never sees its partner's partial sums (the first halves withhold them
+    in a test mode set at pack time) gives up after a bounded spin, counts it in the handle and
+    exits normally. A re-pack of the same handle in the normal mode then gives correct results:
+    the words left by the launch that gave up never match a later launch. A handle packed
+    normally counts no give-ups."""
+    import torch
+    x, w = _case(11, 150, 2048, 300)  # 2 x 3 tiles of 256 rows x 64 tokens, 8 K steps: split
+    xd = gu.to_dev_bf16(x)
+    q, a = binding.quantize_act(xd)
+    monkeypatch.setenv("SBN_SPLITK_SPIN_LIMIT", "64")
+    monkeypatch.setenv("SBN_SPLITK_WITHHOLD", "1")
+    pw = binding.PackedWeight(gu.to_dev_f32(w), 8, 16)
+    binding.bitlinear(q, a, pw, out="i32")
+    torch.cuda.synchronize()
+    assert pw.query().splitk_giveups == 6 * 4  # every (tile, wave) pair
+    monkeypatch.delenv("SBN_SPLITK_WITHHOLD")
+    monkeypatch.delenv("SBN_SPLITK_SPIN_LIMIT")
+    pw.pack(gu.to_dev_f32(w))
+    codes = pw.export()[0].cpu().numpy()
+    acc_ref = oracle.int_matmul(q.cpu().numpy(), codes)
+    for _ in range(3):
+        acc = binding.bitlinear(q, a, pw, out="i32")
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert pw.query().splitk_giveups == 6 * 4
+    pw.free()
+    pw2 = binding.PackedWeight(gu.to_dev_f32(w), 8, 16)
+    acc = binding.bitlinear(q, a, pw2, out="i32")
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert pw2.query().splitk_giveups == 0
+    pw2.free()
+
+
+def test_split_k_graph_replays():
+    """The handshake keeps no host-side state: a captured split-K forward replayed several times,
+    with eager work and synchronizations between the replays, gives the eager result every time."""
+    import torch
+    x, w = _case(12, 150, 2048, 300)
+    xd = gu.to_dev_bf16(x)
+    q, a = binding.quantize_act(xd)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), 6, 8)
+    y = torch.empty((150, 300), dtype=torch.int32, device="cuda")
+    binding.bitlinear(q, a, pw, out="i32", y=y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.bitlinear(q, a, pw, out="i32", y=y)
+    for _ in range(4):
+        y.zero_()
+        binding.bitlinear(q, a, pw, out="i32")  # eager work on the same handle between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+    assert pw.query().splitk_giveups == 0
+    pw.free()
 
 
 @pytest.mark.parametrize("T", [1, 3, 16, 150, 300])
