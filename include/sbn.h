@@ -236,6 +236,32 @@ sbn_status sbn_bitlinear_fwd_group_bf16(const sbn_packed* const* ws /* host */, 
                                         const int64_t* ld_ys /* host */, sbn_out_kind out_kind,
                                         void* stream);
 
+/* Bytes of device workspace sbn_bitlinear_fwd_latent_static holds on each device it runs on. */
+#define SBN_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the pack of sbn_pack_nm_ternary (flags 0) of the
+ * latent weights followed by sbn_bitlinear_fwd, with the same results, but with the packed planes,
+ * the absmean partial sums and the split-K words in a fixed library-owned device workspace of
+ * SBN_STATIC_WORKSPACE_BYTES instead of a handle. The call allocates nothing (no hipMalloc or
+ * hipFree, no allocating library routine); it enqueues a fill kernel that clears the workspace
+ * regions that must start at zero, the pack kernels and the forward.
+ *   Arguments as for sbn_pack_nm_ternary (w_latent, n_out, K, ld_w, n_keep, m_group) and
+ *   sbn_bitlinear_fwd (x_q, ld_q, x_absmax, T, y, ld_y, out_kind).
+ * A weight whose planes do not fit the workspace gives SBN_ERR_UNSUPPORTED (the 7B-style
+ * 4096 x 11008 layers at 2:4 or 8:16 take about 17 MB; the limit is about 88M weights at 2:4).
+ * Every call on a device shares that device's workspace, which keeps the last call's contents:
+ * calls that overlap on one device (two streams, or two host threads) race and give wrong
+ * results; order them. No handle exists, so nothing is exported and no mask flips are counted.
+ * T == 0 or n_out == 0 is a no-op.
+ */
+sbn_status sbn_bitlinear_fwd_latent_static(const float* w_latent, int64_t n_out, int64_t K,
+                                           int64_t ld_w, int n_keep, int m_group,
+                                           const int8_t* x_q, int64_t ld_q, const float* x_absmax,
+                                           int64_t T, void* y, int64_t ld_y,
+                                           sbn_out_kind out_kind, void* stream);
+
 /*
  * Data gradient of the layer under the straight-through estimator ("Microsoft BitNet 1.58: The
  * Era of 1-Bit Large Language Models", section "Training with the Straight-Through Estimator":

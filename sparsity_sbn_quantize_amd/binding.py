@@ -72,6 +72,9 @@ _SIGNATURES = {
     "sbn_bitlinear_fwd_group_bf16": (ctypes.c_int, [_P, ctypes.c_int, _P, _I64, _I64,
                                                     ctypes.c_float, _P, _I64, _P, _P, _P,
                                                     ctypes.c_int, _P]),
+    "sbn_bitlinear_fwd_latent_static": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.c_int,
+                                                       ctypes.c_int, _P, _I64, _P, _I64, _P, _I64,
+                                                       ctypes.c_int, _P]),
     "sbn_ceiling_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_uint32, _P, _P]),
     "sbn_ceiling_mfma_i8": (ctypes.c_int, [_I64, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "sbn_ceiling_empty": (ctypes.c_int, [_P]),
@@ -391,3 +394,22 @@ def bitlinear_group_bf16(x, ws, out: str = "f32", ys=None, x_q=None, x_absmax=No
                                              _ptr(x_absmax), outs, lds, kind, _stream(stream)))
     return ys, x_q, x_absmax
 
+
+def bitlinear_latent_static(w, n: int, m: int, x_q, x_absmax, out: str = "f32", y=None,
+                            stream=None):
+    """Pack of the latent weights w fp32 [n_out][K] and forward on x_q, with no device allocation
+    in the library (sbn_bitlinear_fwd_latent_static: its fixed workspace holds the packed planes).
+    Returns y [T][n_out]."""
+    import torch
+    _require_cuda(w, "w")
+    _require_cuda(x_q, "x_q")
+    n_out, K = w.shape
+    T = x_q.shape[0]
+    kind = SBN_OUT_F32 if out == "f32" else SBN_OUT_I32_ACC
+    if y is None:
+        y = torch.empty((T, n_out), dtype=torch.float32 if kind == SBN_OUT_F32 else torch.int32,
+                        device=x_q.device)
+    check(lib().sbn_bitlinear_fwd_latent_static(_ptr(w), n_out, K, _ld(w, K), n, m, _ptr(x_q),
+                                                _ld(x_q, K), _ptr(x_absmax), T, _ptr(y),
+                                                _ld(y, n_out), kind, _stream(stream)))
+    return y

@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsbn.so")
 
 SOURCES = ["api.hip", "quantize_act.hip", "pack.hip", "bitlinear.hip", "backward.hip",
-           "outliers.hip", "gemv_i8.hip", "ceilings.hip"]
+           "outliers.hip", "gemv_i8.hip", "ceilings.hip", "static_ws.hip"]
 HEADERS = ["sbn_common.hpp", "sbn_internal.hpp", "gemv.hpp"]
 # The int8-input GEMV entry takes its first loads' operands as leading scalar arguments, which
 # the firmware preloads into registers with this option.

@@ -28,6 +28,7 @@ def test_exports_match_header(lib):
                              "sbn_packed_query",
                              "sbn_packed_mask_flips", "sbn_last_error",
                              "sbn_bitlinear_fwd_group", "sbn_bitlinear_fwd_group_bf16",
+                             "sbn_bitlinear_fwd_latent_static",
                              "sbn_ceiling_stream_read", "sbn_ceiling_mfma_i8", "sbn_ceiling_empty"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
