@@ -12,7 +12,8 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsbn.so")
+# SBN_LIB names another build of the library to load (the host-sanitizer build, for instance)
+LIB_PATH = os.environ.get("SBN_LIB") or os.path.join(HERE, "libsbn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 HEADERS = [os.path.join(INCLUDE, h) for h in ("sbn.h", "sbn_ceilings.h")]
 
