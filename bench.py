@@ -142,6 +142,44 @@ class Gpu:
             times.append(s.elapsed_time(e))
         return statistics.median(times)
 
+    def sleep_seconds_per_cycle(self):
+        """Seconds per cycle of the GPU busy wait (torch.cuda._sleep), measured once."""
+        if getattr(self, "_spc", None) is None:
+            torch = self.torch
+            n = 4_000_000
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            torch.cuda._sleep(n)
+            e.record()
+            e.synchronize()
+            self._spc = s.elapsed_time(e) * 1e-3 / n
+        return self._spc
+
+    def time_eager(self, run, reps=REPEATS):
+        """Milliseconds of run(r) (a fixed number of launches, eagerly enqueued) between HIP events,
+        the median over r = 0 .. reps-1. A GPU busy wait ahead of each timed region, longer than
+        three times the host's measured enqueue time of one run, keeps the host ahead of the GPU,
+        so the region times the kernels back to back, not the host."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(0)
+        host = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        cycles = int(max(SLEEP_CYCLES, 3.0 * host / self.sleep_seconds_per_cycle()))
+        times = []
+        for r in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(cycles)
+            s.record()
+            run(r)
+            e.record()
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        return statistics.median(times)
+
     def time_launches(self, fn, launches):
         """Milliseconds per launch of fn: a graph of `launches` calls, replayed once untimed, then
         the median of REPEATS timed replays divided by the launch count."""
@@ -278,16 +316,28 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     assert torch.equal(y, y_two), "one-call step differs from quantize + forward"
     y_eager = y.clone()
     gw = gpu.graph(step, args.warmup) if args.warmup > 0 else None
-    # Exactly K steps per timed replay; REPEATS graphs over disjoint runs of the rotated copies,
-    # so that no replay finds its weights in the last-level cache; the median is reported.
+    # Exactly K steps per timed region, the median of REPEATS regions over disjoint runs of the
+    # rotated copies (no region finds its weights in the last-level cache). Two ways to launch
+    # them, both reported: one K-step HIP graph per region, and K eager launches behind a GPU busy
+    # wait. A graph replay carries a fixed cost (about 10 us) that K = 20 steps do not amortize,
+    # and the host cannot enqueue eager launches as fast as the GPU runs them beyond about 100;
+    # the step time is the eager one for K <= 64, the graph one above.
     gss = [gpu.graph(lambda i, o=r * args.steps: step(o + i), args.steps) for r in range(REPEATS)]
     if gw is not None:
         gw.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = statistics.median(gpu.time_graph(g, reps=1) for g in gss)
-    wall = time.perf_counter() - t0
+    ms_graph = statistics.median(gpu.time_graph(g, reps=1) for g in gss)
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
+
+    def eager_run(r):
+        for i in range(args.steps):
+            step(r * args.steps + i)
+
+    ms_eager = gpu.time_eager(eager_run)
+    wall = time.perf_counter() - t0
+    assert torch.equal(y, y_eager), "eager steps differ from the first forward"
+    ms = ms_eager if args.steps <= 64 else ms_graph
     timings = {}
     for name, fn in (("bitlinear_gemv", gemv_only), ("quantize_act", quant_only),
                      ("quantize_act+bitlinear_gemv", two_call),
@@ -340,6 +390,9 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     res = {
         "value": step_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "ms_per_step": ms_step,
         "wall_s": wall,
+        "step_timing": {"method": "eager launches" if args.steps <= 64 else "HIP graph",
+                        "graph_ms_per_step": ms_graph / args.steps,
+                        "eager_ms_per_step": ms_eager / args.steps},
         "config": {"workload": f"{wl.name}_T{T}", "pattern": f"{n}:{m}", "tokens": T, "K": K,
                    "n_out": N, "weights": "packed once, rotated over %d copies" % R,
                    "step": "one kernel (quantize fused)" if fused else "quantize + GEMV kernels",
@@ -786,6 +839,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": res["config"], "roofline": res["roofline"],
             "kernels_us": res.get("kernels_us")}
+    if res.get("step_timing"):
+        line["step_timing"] = res["step_timing"]
     if res.get("pack_variants_us"):
         line["pack_variants_us"] = res["pack_variants_us"]
     if "activation_kernels" in res:
