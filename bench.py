@@ -411,6 +411,38 @@ def run_decode(gpu, args, T=1, with_cpu=True):
     return res
 
 
+# Decode shapes with a larger K than the configured workloads (70B- and 13B-style down
+# projections), where one launch streams tens of MB of weights: int8 GEMV, weights N(0, 0.02).
+LARGE_DECODE = ((8192, 28672, 8, 16), (5120, 13824, 6, 8))
+
+
+def run_decode_large(gpu, args):
+    torch = gpu.torch
+    rows = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    for (N, K, n, m) in LARGE_DECODE:
+        w = torch.randn((N, K), device="cuda", generator=gen) * 0.02
+        R = max(1, -(-args.rotate_bytes // rpf_bytes(N, K, n, m)))
+        pws = [gpu.b.PackedWeight(w, n, m) for _ in range(R)]
+        del w
+        for T in (1, 16):
+            x = (torch.randn((T, K), device="cuda", generator=gen)).to(torch.bfloat16)
+            q, a = gpu.b.quantize_act(x)
+            y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+            us = gpu.time_launches(lambda i: gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y),
+                                   max(args.steps, 100)) * 1e3
+            fb = forward_bytes(T, K, N, n, m)
+            rows.append({"n_out": N, "K": K, "pattern": f"{n}:{m}", "tokens": T, "us": us,
+                         "bytes": fb, "GBps": fb / us / 1e3,
+                         "frac_hbm": fb / us / 1e3 / HBM_PEAK_GBS})
+        for p in pws:
+            p.free()
+        torch.cuda.empty_cache()
+    return {"workload": "decode_gemv_large_k (int8 GEMV; extra shapes, N(0, 0.02) weights)",
+            "rows": rows}
+
+
 def cpu_decode(x_bits, w, n, m, step_bytes, seconds):
     import oracle
     packed = oracle.pack_nm_ternary(w, n, m)  # packed once, as on the GPU
@@ -815,6 +847,7 @@ def main():
         profile_copy(gpu, args)
         return
     if args.workload == "block":
+        sec.append({"decode_large_k": run_decode_large(gpu, args)})
         from sparsity_sbn_quantize_amd import inputs
         gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
                              for i in range(len(inputs.W_BLOCK.layers))]
@@ -868,6 +901,7 @@ def main():
                                            "activation_kernels", "cpu_baseline") if k in rp})
         for li, pat in ((0, (2, 4)), (1, (8, 16))):
             sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
+        sec.append({"decode_large_k": run_decode_large(gpu, args)})
         from sparsity_sbn_quantize_amd import inputs
         gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
                              for i in range(len(inputs.W_BLOCK.layers))]

@@ -6,6 +6,8 @@
 // for a scalar load of the argument block (3.77 -> 3.57 us at T = 1 and 5.64 -> 5.35 us at T = 16
 // on the 2560 -> 6912 shape). The bf16-input kernels keep their own argument order: moving their
 // arguments the same way made them slower.
+#include <stdlib.h>
+
 #include "gemv.hpp"
 
 namespace sbn {
@@ -36,6 +38,162 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_group(
                                                G.m[i].gamma, xin, (int64_t)ld_x, nullptr, 0,
                                                const_cast<float*>(absmax), (int64_t)T, G.m[i].y,
                                                G.m[i].ld_y, out_kind, 0.0f, rb, false);
+}
+
+// The int8 GEMV for K past one batch of the kernel above (more than 48 quads; e.g. 8192 x 28672,
+// 112 quads): every wave issues the brick loads of all its quads at once (up to kDeepMaxQ, so one
+// pass covers K <= 32768) instead of taking batches of three in turn, then streams its activation
+// pieces two quads ahead of the products. Its loads return in order, so the activations of quad i
+// are in once the bricks are; the products of quad i then overlap the activation loads of quads
+// i + 1 and i + 2. Only the lanes of present tokens load activations (the others are masked
+// off, so a one-token launch does not move 60 lanes' worth of empty pieces through the address
+// units). Positional and 2:4 codes; rows of x_q 16-byte aligned, ld_q % 16 == 0, K % 16 == 0 (the
+// launcher checks). Same-process A/B against the batched kernel (us): 8192 x 28672 at 8:16, one
+// token 20.9 -> 18.2, sixteen 38.3 -> 34.5; 5120 x 13824 at 6:8, 11.0 -> 9.9 and 21.3 -> 18.7.
+// (Without the masking the new kernel was slower at one token: 24.2 us.)
+constexpr int kDeepMaxQ = 8;
+
+// RB row blocks per workgroup share the activation loads (each wave's B operands serve RB sets of
+// bricks): with 16 tokens the activation pieces outweigh the bricks, and RB = 2 halves them.
+template <int FORM, int Q, int RB>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
+    const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
+    int ld_q, int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind) {
+  static_assert(FORM == kFormPositional || FORM == kFormSparse24, "positional or 2:4 codes");
+  __shared__ v4i red[RB][kGemvMaxWaves][64];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t rb0 = (int64_t)blockIdx.x * RB;
+  const int t = lane & 15, g = lane >> 4;
+  const bool tok_ok = t < T;
+  // The RB row blocks' quads are consecutive in the plane; stored row blocks are padded to a
+  // multiple of 16, so a last block past n_out exists (zero bricks; its rows are not stored).
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(code_plane + rb0 * nq * 1024), (short)0, RB * nq * 1024, kBufDword3);
+  uint32_t codes[RB][Q][4];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int q = wave + i * W;
+      const v4i c = __builtin_amdgcn_raw_buffer_load_b128(
+          crs, lane * 16, q < nq ? (r * nq + q) * 1024 : RB * nq * 1024, kPlaneLoad);
+      codes[r][i][0] = (uint32_t)c[0]; codes[r][i][1] = (uint32_t)c[1];
+      codes[r][i][2] = (uint32_t)c[2]; codes[r][i][3] = (uint32_t)c[3];
+    }
+  // one resource over the T activation rows: quads past the last read zero (offsets past the
+  // range); (T - 1) ld_q + K < 2^31 (T <= 16, ld_q <= 2^26)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(xq), (short)0, (int)((int64_t)(T - 1) * ld_q + K), kBufDword3);
+  auto load_x = [&](int i, v4i (&b)[4]) {
+    const int q = wave + i * W;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int voff = q < nq ? t * ld_q + 16 * b_chunk<FORM>(g, j) : 0x7FFFFFF0;
+      if (tok_ok) {
+        b[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff, q < nq ? q * kQuadK : 0, 0);
+      } else {
+        b[j] = v4i{0, 0, 0, 0};
+      }
+    }
+  };
+  const float gamma = gamma_p[0];
+  const float a_t = out_kind == SBN_OUT_F32 && tok_ok ? absmax[t] : 0.0f;
+  v4i bx[3][4];
+  load_x(0, bx[0]);
+  if (Q > 1) load_x(1, bx[1]);
+  v4i acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    if (i + 2 < Q) load_x(i + 2, bx[(i + 2) % 3]);
+    v4i(&b)[4] = bx[i % 3];
+    if (wave + i * W < nq) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if constexpr (FORM == kFormSparse24) {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            uint32_t a[4];
+            exp_word_to_i8(codes[r][i][2 * blk], a);
+            acc[r] = smfmac16(a, b[2 * blk], b[2 * blk + 1], codes[r][i][2 * blk + 1], acc[r]);
+          }
+        } else {
+          uint32_t a[16];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[r][i][j], a + 4 * j);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r] = mfma16(a + 4 * j, b[j], acc[r]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r) red[r][wave][lane] = acc[r];
+  __syncthreads();
+  // wave r sums row block r (wave 0 takes all of them when the workgroup has fewer waves)
+  if (wave >= RB || !tok_ok) return;
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
+  for (int r = wave; r < RB; r += W) {
+    v4i sum = red[r][0][lane];
+    for (int w = 1; w < W; ++w) sum += red[r][w][lane];
+    const int64_t row0 = (rb0 + r) * 16 + 4 * g;
+    const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < n_out;
+    if (vec) {
+      if (out_kind == SBN_OUT_I32_ACC) {
+        *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + row0) = sum;
+      } else {
+        float4 f;
+        f.x = __fmul_rn(__fmul_rn((float)sum[0], gamma), step);
+        f.y = __fmul_rn(__fmul_rn((float)sum[1], gamma), step);
+        f.z = __fmul_rn(__fmul_rn((float)sum[2], gamma), step);
+        f.w = __fmul_rn(__fmul_rn((float)sum[3], gamma), step);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + row0) = f;
+      }
+    } else {
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = row0 + i;
+        if (row < n_out) store_out(y, ld_y, out_kind, t, row, sum[i], gamma, step);
+      }
+    }
+  }
+}
+
+template <int FORM, int RB>
+hipError_t launch_i8_deep(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
+                          const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
+                          hipStream_t s) {
+  const Layout& L = h->L;
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  const int Q = (int)((L.quads + W - 1) / W);
+  const unsigned blocks = (unsigned)((L.row_blocks + RB - 1) / RB);
+#define SBN_DEEP(QQ)                                                                           \
+  hipLaunchKernelGGL((bitlinear_gemv_i8_deep<FORM, QQ, RB>), dim3(blocks), dim3(64 * W), 0, s, \
+                     h->codes, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, W, absmax,         \
+                     h->gamma_out(), y, ld_y, L.n_out, out_kind)
+  if constexpr (RB > 1) {  // (launched for one batch only: Q <= kGemvMaxQ)
+    switch (Q) {
+      case 1: SBN_DEEP(1); break;
+      case 2: SBN_DEEP(2); break;
+      default: SBN_DEEP(3); break;
+    }
+  } else {
+    switch (Q) {
+      case 1: SBN_DEEP(1); break;
+      case 2: SBN_DEEP(2); break;
+      case 3: SBN_DEEP(3); break;
+      case 4: SBN_DEEP(4); break;
+      case 5: SBN_DEEP(5); break;
+      case 6: SBN_DEEP(6); break;
+      case 7: SBN_DEEP(7); break;
+      default: SBN_DEEP(8); break;
+    }
+  }
+#undef SBN_DEEP
+  return hipGetLastError();
 }
 
 // The one-token int8 GEMV with the k:256 outlier term in the same launch (fp32 output; planes
@@ -216,6 +374,25 @@ hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                             const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
                             hipStream_t s) {
   const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (h->L.K % 16 == 0);
+  const Layout& L = h->L;
+  const bool deep_form = xvec && !h->compact &&
+                         (L.form == kFormSparse24 || L.form == kFormPositional) &&
+                         L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ;
+  if (deep_form && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ) {
+    if (L.form == kFormSparse24)
+      return launch_i8_deep<kFormSparse24, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    return launch_i8_deep<kFormPositional, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  }
+  // More than four tokens, one quad per wave and many row blocks: two row blocks per workgroup.
+  // Same-process A/B against the kernel above (us, T = 8 / 16): 6912 x 2560 3.96 / 4.98 ->
+  // 3.68 / 4.22, 11008 x 4096 7.09 / 8.88 -> 5.83 / 7.18; slower with two or three quads per wave
+  // (2560 x 6912 4.81 / 6.10 -> 5.69 / 6.93) or few row blocks (2560 x 2560 3.12 / 3.52 ->
+  // 3.25 / 3.68).
+  if (deep_form && T > kFusedMaxT && L.quads <= kGemvMaxWaves && L.row_blocks >= 320) {
+    if (L.form == kFormSparse24)
+      return launch_i8_deep<kFormSparse24, 2>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    return launch_i8_deep<kFormPositional, 2>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  }
   if (xvec) return launch_i8_form<true>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
   return launch_i8_form<false>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
 }

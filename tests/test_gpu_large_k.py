@@ -1,5 +1,7 @@
-"""GPU parity of the GEMV on large K (T <= 16): past 48 quads (K > 12288) the waves take batches
-of 48 quads in turn, so decode on e.g. 13B- and 70B-style down projections stays a GEMV. Integer
+"""GPU parity of the GEMV on large K (T <= 16): past 48 quads (K > 12288) each wave loads the bricks
+of all its quads at once (up to 128 quads, K <= 32768; positional and 2:4 codes, aligned int8
+rows), otherwise the waves take batches of 48 quads in turn, so decode on e.g. 13B- and 70B-style
+down projections stays a GEMV. Integer
 accumulators are exact; fp32 outputs follow the oracle within the forward's tolerance."""
 
 import numpy as np
@@ -40,9 +42,11 @@ def _run(x, w, n, m, ld_q=None, **pack_kw):
 
 @pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16), (3, 8)])
 @pytest.mark.parametrize("T", [1, 3, 16])
-@pytest.mark.parametrize("K", [12544, 13824, 28672])
+@pytest.mark.parametrize("K", [12544, 13824, 28672, 32768, 33024])
 def test_large_k_gemv(n, m, T, K):
-    """49, 54 and 112 quads: two and three batches, a ragged last batch; every code form."""
+    """49 to 128 quads: the kernel that loads all of a wave's quads at once (four to eight per wave;
+    positional and 2:4 codes) and, for the kept form (3:8), batches of 48 quads in turn; 129 quads:
+    batches for every form (three, the last ragged)."""
     x, w = _case(K + 7 * T + n, T, 72, K)
     r = _run(x, w, n, m)
     q_ref, a_ref = oracle.quantize_act(x)
@@ -71,6 +75,22 @@ def test_large_k_70b_shape():
     x, w = _case(70, 16, 8192, 28672)
     r = _run(x, w, 8, 16)
     q_ref, a_ref = oracle.quantize_act(x)
+    acc_ref = oracle.int_matmul(q_ref, r["codes"])
+    assert np.array_equal(r["acc"], acc_ref)
+    gu.assert_y_close(r["y"], oracle.dequantize(acc_ref, r["gamma"], a_ref))
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 16)])
+@pytest.mark.parametrize("T", [5, 9, 16])
+@pytest.mark.parametrize("N,K,ld_q", [(5200, 1040, None), (5104, 4096, 4112), (6912, 2560, None)])
+def test_two_row_blocks_per_workgroup(n, m, T, N, K, ld_q):
+    """More than four tokens, at most 16 quads and at least 320 row blocks: one workgroup takes two
+    row blocks (5200 rows: 325 blocks, the last workgroup's second block is padding; K = 1040: a
+    K tail inside the last quad; a padded x_q row pitch). All outputs against the oracle."""
+    x, w = _case(N + K + T + n, T, N, K)
+    r = _run(x, w, n, m, ld_q=ld_q)
+    q_ref, a_ref = oracle.quantize_act(x)
+    assert np.array_equal(r["q"], q_ref) and np.array_equal(r["a"], a_ref)
     acc_ref = oracle.int_matmul(q_ref, r["codes"])
     assert np.array_equal(r["acc"], acc_ref)
     gu.assert_y_close(r["y"], oracle.dequantize(acc_ref, r["gamma"], a_ref))
