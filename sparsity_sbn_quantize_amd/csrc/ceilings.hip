@@ -36,16 +36,25 @@ __global__ __launch_bounds__(256) void ceiling_mfma(int iters, uint32_t* __restr
   const int lane = threadIdx.x & 63;
   const v4i_t a = {lane, lane * 3, lane * 5, lane * 7};
   const v4i_t b = {lane * 11, lane * 13, lane * 17, lane * 19};
-  v4i_t c[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) c[j] = v4i_t{j, 0, 0, 0};
+  // eight separate accumulators, each updated in place (with the builtin the compiler gave each
+  // instruction a new destination and copied it back, an extra register move per product)
+  v4i_t c0 = {0, 0, 0, 0}, c1 = {1, 0, 0, 0}, c2 = {2, 0, 0, 0}, c3 = {3, 0, 0, 0};
+  v4i_t c4 = {4, 0, 0, 0}, c5 = {5, 0, 0, 0}, c6 = {6, 0, 0, 0}, c7 = {7, 0, 0, 0};
   for (int i = 0; i < iters; ++i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[j], 0, 0, 0);
+    asm volatile(
+        "v_mfma_i32_16x16x64_i8 %0, %8, %9, %0\n\t"
+        "v_mfma_i32_16x16x64_i8 %1, %8, %9, %1\n\t"
+        "v_mfma_i32_16x16x64_i8 %2, %8, %9, %2\n\t"
+        "v_mfma_i32_16x16x64_i8 %3, %8, %9, %3\n\t"
+        "v_mfma_i32_16x16x64_i8 %4, %8, %9, %4\n\t"
+        "v_mfma_i32_16x16x64_i8 %5, %8, %9, %5\n\t"
+        "v_mfma_i32_16x16x64_i8 %6, %8, %9, %6\n\t"
+        "v_mfma_i32_16x16x64_i8 %7, %8, %9, %7"
+        : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3), "+a"(c4), "+a"(c5), "+a"(c6), "+a"(c7)
+        : "v"(a), "v"(b));
   }
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) s ^= c[j][0] ^ c[j][1] ^ c[j][2] ^ c[j][3];
+  const v4i_t x = c0 ^ c1 ^ c2 ^ c3 ^ c4 ^ c5 ^ c6 ^ c7;
+  const int s = x[0] ^ x[1] ^ x[2] ^ x[3];
   if (s == 0x7FFFFFFF && threadIdx.x == 0) sink[0] = (uint32_t)s;
 }
 
