@@ -343,11 +343,14 @@ def run_decode(gpu, args, T=1, with_cpu=True):
                      ("quantize_act+bitlinear_gemv", two_call),
                      ("layernorm_quantize_act", ln_quant_only),
                      ("bitlinear_gemv (layernorm + quantize fused)", ln_step)):
+        if args.lean and name != "bitlinear_gemv":
+            continue
         timings[name] = gpu.time_launches(fn, max(args.steps, KERNEL_LAUNCHES))
     # Pack variants on the same weights: the compact plane (GEMV reads nonzero masks + signs)
     # and 16:256 outliers (the step plus the outlier term); fewer rotated copies of each
     variants = {}
-    for tag, kw in (("compact", {"compact": True}), ("outliers 16:256", {"outliers": 16})):
+    for tag, kw in (() if args.lean else
+                    (("compact", {"compact": True}), ("outliers 16:256", {"outliers": 16}))):
         Rv = max(1, R // 2)
         pv = [gpu.b.PackedWeight(wd, n, m, **kw) for _ in range(Rv)]
 
@@ -365,7 +368,7 @@ def run_decode(gpu, args, T=1, with_cpu=True):
             p.free()
     # The rank encoding (an export of the same packs, read by no kernel): time per export into one
     # buffer, and its bytes per weight.
-    rrb = pws[0].query().rank_row_bytes
+    rrb = pws[0].query().rank_row_bytes if not args.lean else 0
     rank_out = gpu.torch.empty((N, rrb), dtype=gpu.torch.uint8, device="cuda")
     lib = gpu.b.lib()
 
@@ -373,8 +376,10 @@ def run_decode(gpu, args, T=1, with_cpu=True):
         gpu.b.check(lib.sbn_packed_export_rank(pws[i % R].handle, gpu.b._ptr(rank_out),
                                                gpu.b._stream(None)))
 
-    variants["rank export"] = gpu.time_launches(rank_export, max(args.steps, KERNEL_LAUNCHES)) * 1e3
-    variants["rank bytes per weight"] = rrb * N / (N * K)
+    if not args.lean:
+        variants["rank export"] = gpu.time_launches(rank_export,
+                                                    max(args.steps, KERNEL_LAUNCHES)) * 1e3
+        variants["rank bytes per weight"] = rrb * N / (N * K)
     ms_step = ms / args.steps
     if fused:
         step_bytes = fused_bytes(T, K, N, n, m)
@@ -492,9 +497,11 @@ def run_prefill(gpu, args, layer_index=0, steps=None, with_cpu=True, cpu_seconds
     assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
     gemm_ms = gpu.time_launches(gemm_only, max(steps, KERNEL_LAUNCHES))
     act_ms = {}
-    for name, fn in (("quantize_act", lambda i: gpu.b.quantize_act(xd, out_q=q, out_absmax=a)),
-                     ("layernorm_quantize_act",
-                      lambda i: gpu.b.layernorm_quantize_act(xd, LN_EPS, out_q=q, out_absmax=a))):
+    for name, fn in (() if args.lean else
+                     (("quantize_act", lambda i: gpu.b.quantize_act(xd, out_q=q, out_absmax=a)),
+                      ("layernorm_quantize_act",
+                       lambda i: gpu.b.layernorm_quantize_act(xd, LN_EPS, out_q=q,
+                                                              out_absmax=a)))):
         act_ms[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
     act_bytes = 3.0 * T * K + 4.0 * T  # bf16 in, int8 + a' out
     ops = 2.0 * T * K * N
@@ -771,7 +778,7 @@ def profile_copy(gpu, args):
 TRAFFIC_RUNS = {
     # positional codes (form 0) only: the compact variant's GEMV runs in the same workload
     "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<0, true, \w+, \d+, false, \w+>"),
-    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv_i8<0,"),
+    "decode16": ("gemv_6of8_T16", r"bitlinear_gemv_i8_deep<0,"),
     "prefill_up": ("gemm_8of16_ffn_up", r"bitlinear_gemm<"),
     "prefill_down": ("gemm_8of16_ffn_down", r"bitlinear_gemm<"),
 }
@@ -832,9 +839,15 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-copy", action="store_true")
+    ap.add_argument("--lean", action="store_true",
+                    help="only the workload's step and its dominant kernel (for profiler runs): no "
+                         "variants, secondary lines, ceilings or CPU baseline")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write profiles/traffic.json from rocprofv3 counter runs under DIR")
     args = ap.parse_args()
+    if args.lean:
+        args.no_secondary = True
+        args.no_cpu_baseline = True
     if args.record_traffic:
         record_traffic(args.record_traffic)
         return
@@ -880,10 +893,13 @@ def main():
         line["activation_kernels"] = res["activation_kernels"]
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
-    ceil = measure_ceilings(gpu, res["roofline"].get("bytes_per_launch", 1 << 22))
+    ceil = (measure_ceilings(gpu, res["roofline"].get("bytes_per_launch", 1 << 22))
+            if not args.lean else None)
     line["ceilings"] = ceil
     rl = line["roofline"]
-    if rl["bound"] == "hbm":
+    if ceil is None:
+        pass
+    elif rl["bound"] == "hbm":
         rl["measured_peak"] = ceil["hbm_read_GBps"]
         rl["frac_measured"] = rl["achieved"] / ceil["hbm_read_GBps"]
         rl["frac_small_read"] = rl["achieved"] / ceil["small_read_GBps"]
