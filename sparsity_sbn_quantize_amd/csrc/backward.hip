@@ -45,12 +45,13 @@ constexpr int64_t kMaxBufExtent = 0x7FFF0000;
 // the slice. The 2-bit codes (0, 1 = +1, 2 = -1) become selectors: x = (c0 | c1 << 16),
 // x * 0x101 + 0x40004 = bytes [c0 + 4, c0, c1 + 4, c1], which v_perm maps to the low bytes
 // {0x00, 0x80, 0x80} and high bytes {0x00, 0x3F, 0xBF} of bf16 {0, +1, -1}.
+__device__ __forceinline__ uint32_t tdecode1(uint32_t w, int s, int p) {
+  const uint32_t x = (w >> (8 * s + 2 * p)) & 0x00030003u;
+  return __builtin_amdgcn_perm(0x00808000u, 0x00BF3F00u, x * 0x0101u + 0x00040004u);
+}
 __device__ __forceinline__ void tdecode(uint32_t w, int s, uint32_t out[4]) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t x = (w >> (8 * s + 2 * p)) & 0x00030003u;
-    out[p] = __builtin_amdgcn_perm(0x00808000u, 0x00BF3F00u, x * 0x0101u + 0x00040004u);
-  }
+  for (int p = 0; p < 4; ++p) out[p] = tdecode1(w, s, p);
 }
 
 __device__ __forceinline__ v4f mfma_bf16(const uint32_t a[4], v4i b, v4f c) {
@@ -161,10 +162,15 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* xt = smem + slot * kBwTileBytes + rlane;
       v4i bv = *reinterpret_cast<const v4i*>(xt);
+      // Fenced groups (as the forward GEMM): group (j, tf) issues the LDS read of the next
+      // group's dY first, then its 4 MFMAs, then its two of the next slice's 16 decoded words, and
+      // nothing crosses the fence after it, so every read is one group ahead of its MFMAs.
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ASlice& cur = (j & 1) ? a1 : a0;
         ASlice& nxt = (j & 1) ? a0 : a1;
+        const TBricks& src = j < 3 ? bcur : bnext;
+        const int sj = j < 3 ? j + 1 : 0;
 #pragma unroll
         for (int tf = 0; tf < kBwTF; ++tf) {
           const int nj = tf + 1 < kBwTF ? j : j + 1, ntf = tf + 1 < kBwTF ? tf + 1 : 0;
@@ -172,20 +178,14 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
           if (nj < 4) bn = *reinterpret_cast<const v4i*>(xt + ntf * 4096 + nj * 256);
 #pragma unroll
           for (int cf = 0; cf < kBwCF; ++cf) acc[cf][tf] = mfma_bf16(cur[cf], bv, acc[cf][tf]);
-          bv = bn;
-        }
-        if (j < 3) {
-          decode_slice(bcur, j + 1, nxt);
-        } else {
-          decode_slice(bnext, 0, nxt);
-        }
 #pragma unroll
-        for (int tf = 0; tf < kBwTF; ++tf) {
-          __builtin_amdgcn_sched_group_barrier(0x008, kBwCF, 0);  // MFMA
-          // 4 VALU per group: same-process A/B of 2, 3, 4, 5, 7 and 10, 4 best (7B FFN shapes
-          // at T = 8192 1-2% and 6912 x 2560 at T = 2048 4% faster than the earlier 7)
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+          for (int e = tf * 4 * kBwCF / kBwTF; e < (tf + 1) * 4 * kBwCF / kBwTF; ++e)
+            nxt[e >> 2][e & 3] = tdecode1(src[e >> 2][sj >> 1], sj & 1, e & 3);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, kBwCF, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);     // VALU
+          __builtin_amdgcn_sched_barrier(0);
+          bv = bn;
         }
       }
       load_t(rq + 2 < rq_count ? rq + 2 : rq_count - 1, bcur);

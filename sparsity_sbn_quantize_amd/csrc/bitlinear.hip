@@ -237,6 +237,35 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     __builtin_amdgcn_sched_barrier(0);  // the tile loads go out before this step's MFMAs
     const int8_t* xt = xs0 + slot * kTileBytes + rlane;
     v4i bv = *reinterpret_cast<const v4i*>(xt);
+    if constexpr (POS) {
+      // Fenced groups: group (j, cf) issues the LDS read of the next group's B first, then its 4
+      // MFMAs, then its share of the next slice's decode (2 kRF half-words over CF groups), and
+      // nothing crosses the fence after it, so every B read is one group ahead of its MFMAs.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ASlice& cur = (j & 1) ? a1 : a0;
+        ASlice& nxt = (j & 1) ? a0 : a1;
+        const Bricks& src = j < 3 ? bcur : bnext;
+        const int sj = j < 3 ? j + 1 : 0;
+#pragma unroll
+        for (int cf = 0; cf < kGemmCF; ++cf) {
+          const int nj = cf + 1 < kGemmCF ? j : j + 1, ncf = cf + 1 < kGemmCF ? cf + 1 : 0;
+          v4i bn = bv;
+          if (nj < 4) bn = *reinterpret_cast<const v4i*>(xt + ncf * 4096 + nj * 256);
+#pragma unroll
+          for (int rf = 0; rf < kRF; ++rf) acc[rf][cf] = mfma16(cur[rf], bv, acc[rf][cf]);
+#pragma unroll
+          for (int p = cf * 2 * kRF / kGemmCF; p < (cf + 1) * 2 * kRF / kGemmCF; ++p)
+            exp_word_half_to_i8(src[p >> 1][sj], p & 1, nxt[p >> 1][2 * (p & 1)],
+                                nxt[p >> 1][2 * (p & 1) + 1]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // VALU
+          __builtin_amdgcn_sched_barrier(0);
+          bv = bn;
+        }
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ASlice& cur = (j & 1) ? a1 : a0;
@@ -262,6 +291,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
       }
     }
+    }
     load_bricks(min(q + 2, nq - 1), bcur);
     if (POS && XVEC) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRF));
@@ -283,6 +313,8 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     for (int blk = 0; blk < 2; ++blk) {
       ASlice& cur = blk ? a1 : a0;
       ASlice& nxt = blk ? a0 : a1;
+      const Bricks& src = blk == 0 ? bcur : bnext;
+      const int sj = blk == 0 ? 1 : 0;
 #pragma unroll
       for (int cf = 0; cf < kGemmCF; ++cf) {
         const int nb = cf + 1 < kGemmCF ? blk : blk + 1, ncf = cf + 1 < kGemmCF ? cf + 1 : 0;
@@ -294,19 +326,18 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
         for (int rf = 0; rf < kRF; ++rf)
           acc[rf][cf] = smfmac16(cur[rf], blo, bhi, bcur[rf][2 * blk + 1], acc[rf][cf]);
+        // fenced as the dense step: next group's B reads first, then the MFMAs, then this group's
+        // share of the next block's decode
+#pragma unroll
+        for (int p = cf * 2 * kRF / kGemmCF; p < (cf + 1) * 2 * kRF / kGemmCF; ++p)
+          exp_word_half_to_i8(src[p >> 1][2 * sj], p & 1, nxt[p >> 1][2 * (p & 1)],
+                              nxt[p >> 1][2 * (p & 1) + 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // VALU
+        __builtin_amdgcn_sched_barrier(0);
         blo = nlo;
         bhi = nhi;
-      }
-      if (blk == 0) {
-        decode_slice(bcur, 1, nxt);
-      } else {
-        decode_slice(bnext, 0, nxt);
-      }
-#pragma unroll
-      for (int cf = 0; cf < kGemmCF; ++cf) {
-        __builtin_amdgcn_sched_group_barrier(0x008, kRF, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 24 / CF, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // LDS read
       }
     }
     load_bricks(min(q + 2, nq - 1), bcur);

@@ -127,6 +127,14 @@ __device__ __forceinline__ void exp_word_to_i8(uint32_t w, uint32_t out[4]) {
   out[3] = __builtin_amdgcn_perm(1u, 0x00008000u, w4 & 0x0C0C0C0Cu);
 }
 
+// Half h of exp_word_to_i8: its output words 2h and 2h + 1 (for spreading a decode over the MFMA
+// groups it overlaps).
+__device__ __forceinline__ void exp_word_half_to_i8(uint32_t w, int h, uint32_t& o0, uint32_t& o1) {
+  const uint32_t v = h ? w >> 4 : w;
+  o0 = __builtin_amdgcn_perm(0u, 0x00FF0100u, v & 0x03030303u);
+  o1 = __builtin_amdgcn_perm(1u, 0x00008000u, v & 0x0C0C0C0Cu);
+}
+
 // Plain decode of one kept-form brick into 16 dwords of int8 weights: dword p holds positions
 // 4p..4p+3. Works for any n:m; used by export and by the forward for the kept form.
 __device__ inline void decode_kept_brick(const uint32_t mask[2], const uint32_t codes[4], int n,
