@@ -860,13 +860,13 @@ def main():
         profile_copy(gpu, args)
         return
     if args.workload == "block":
-        sec.append({"decode_large_k": run_decode_large(gpu, args)})
+        large = run_decode_large(gpu, args)
         from sparsity_sbn_quantize_amd import inputs
         gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
                              for i in range(len(inputs.W_BLOCK.layers))]
         rows = [run_block(gpu, args, pat, T, 20 if T > 16 else min(args.steps, 500))
                 for pat in inputs.W_BLOCK.patterns for T in inputs.W_BLOCK.tokens]
-        print(json.dumps({"workload": inputs.W_BLOCK.name, "rows": rows}))
+        print(json.dumps({"workload": inputs.W_BLOCK.name, "rows": rows, "decode_large_k": large}))
         return
     if args.workload == "train":
         rows = [run_train(gpu, args, li, pat, 10) for pat in ((2, 4), (8, 16)) for li in (0, 1)]

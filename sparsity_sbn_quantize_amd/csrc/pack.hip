@@ -578,13 +578,35 @@ __global__ __launch_bounds__(256) void export_compact(Layout L, const uint8_t* c
 // + lane. Lane l = c + 16 g holds column 16 cb + c of rows 128 rq + 32 g + (0..31); its word h
 // (0, 1) holds row 32 g + 16 h + 8 s + 2 p + e (s, e in {0, 1}, p in 0..3) at bits
 // 2 p + 8 s + 16 e, as 2-bit codes 0 = 0, 1 = +1, 2 = -1. One workgroup per 128 rows x 256
-// columns: its 512 bricks are decoded into LDS as 2-bit codes (row-major, 16 positions per
-// word), then every thread assembles 8 words of 8 columns. Rows past n_out are zero.
+// columns: its 512 bricks are decoded into LDS as 2-bit codes (16 positions per word), every
+// thread assembles 8 transposed words of 8 columns into an LDS copy of the workgroup's 16 output
+// blocks, and the blocks (512 contiguous bytes each) are written with 16-byte stores. Rows past
+// n_out are zero.
+//
+// LDS layouts, chosen so that no access has bank conflicts on gfx950's 64 four-byte banks:
+//   code words: row r's 16 words start at 16 r + 16 (r >> 4), word c at c ^ 4 ((r >> 6) & 3).
+//     The decode writes a row's 4 words of one brick with one 16-byte store (a wave covers 16
+//     consecutive rows: 1 KB in 16 row segments); the assembly reads rows 32 g + 16 h + rr (fixed
+//     rr) of 4 columns per wave, 32 distinct words that this layout puts in 32 distinct banks.
+//   output blocks: word i of block cbl at 128 cbl + (i ^ 4 ((i >> 6) & 1) ^ 2 (cbl & 1)
+//     ^ 8 ((cbl >> 1) & 1)). An assembly store (fixed column step) writes words 2 c + 32 g + h,
+//     which would fold onto 16 banks; the block bits spread them over 64. The final read takes
+//     each thread's 8 words as two 16-byte reads: the XORs keep 4-word groups whole (bit 1 only
+//     swaps their halves, undone in registers), and bit 6 of i moved to bit 2 puts the 16 groups
+//     of a quarter wave on 16 distinct 4-bank sets.
+__device__ __forceinline__ int tc_cw_at(int r, int c) {
+  return r * 16 + 16 * (r >> 4) + (c ^ (4 * ((r >> 6) & 3)));
+}
+__device__ __forceinline__ int tc_ow_at(int cbl, int i) {
+  return cbl * 128 + (i ^ (((i >> 6) & 1) << 2) ^ ((cbl & 1) << 1) ^ (((cbl >> 1) & 1) << 3));
+}
+
 __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* mask_plane,
                                                        const uint8_t* code_plane,
                                                        int64_t rq_count,
                                                        uint32_t* __restrict__ tplane) {
-  __shared__ uint32_t cw[128][17];  // row x 16 code words (+1 against bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint32_t cw[128 * 16 + 7 * 16];
+  __shared__ __attribute__((aligned(16))) uint32_t ow[16 * 128];
   const int64_t rq = blockIdx.x / L.quads, q = blockIdx.x % L.quads;
   const int tid = threadIdx.x;
   for (int i = 0; i < 2; ++i) {
@@ -599,17 +621,14 @@ __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* 
         w4[j >> 4] |= (v == 0xFFu ? 2u : v) << (2 * (j & 15));
       }
     }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) cw[rl][4 * b + w] = w4[w];
+    *reinterpret_cast<uint4*>(&cw[tc_cw_at(rl, 4 * b)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
   __syncthreads();
   const int task = tid >> 1, half = tid & 1;
   const int cbl = task >> 3, g = (task >> 1) & 3, h = task & 1;
   uint32_t rw[16];
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) rw[rr] = cw[32 * g + 16 * h + rr][cbl];
-  const int64_t cb = q * 16 + cbl;
-  uint32_t* const dst = tplane + (cb * rq_count + rq) * 128;
+  for (int rr = 0; rr < 16; ++rr) rw[rr] = cw[tc_cw_at(32 * g + 16 * h + rr, cbl)];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
     const int c = 8 * half + cc;
@@ -617,7 +636,17 @@ __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* 
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)  // rr = 8 s + 2 p + e
       out |= ((rw[rr] >> (2 * c)) & 3u) << (2 * ((rr >> 1) & 3) + 8 * (rr >> 3) + 16 * (rr & 1));
-    dst[(c + 16 * g) * 2 + h] = out;
+    ow[tc_ow_at(cbl, (c + 16 * g) * 2 + h)] = out;
+  }
+  __syncthreads();
+  // 16 threads per output block, 8 consecutive words (32 bytes) each
+  const int ob = tid >> 4, part = tid & 15;
+  uint4* const dst = reinterpret_cast<uint4*>(tplane + ((q * 16 + ob) * rq_count + rq) * 128 +
+                                              8 * part);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint4 v = *reinterpret_cast<const uint4*>(&ow[tc_ow_at(ob, 8 * part + 4 * k) & ~3]);
+    dst[k] = (ob & 1) ? make_uint4(v.z, v.w, v.x, v.y) : v;
   }
 }
 
