@@ -428,21 +428,29 @@ def run_decode_large(gpu, args):
     gen.manual_seed(0)
     for (N, K, n, m) in LARGE_DECODE:
         w = torch.randn((N, K), device="cuda", generator=gen) * 0.02
-        R = max(1, -(-args.rotate_bytes // rpf_bytes(N, K, n, m)))
-        pws = [gpu.b.PackedWeight(w, n, m) for _ in range(R)]
-        del w
-        for T in (1, 16):
-            x = (torch.randn((T, K), device="cuda", generator=gen)).to(torch.bfloat16)
-            q, a = gpu.b.quantize_act(x)
-            y = torch.empty((T, N), dtype=torch.float32, device="cuda")
-            us = gpu.time_launches(lambda i: gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y),
-                                   max(args.steps, 100)) * 1e3
-            fb = forward_bytes(T, K, N, n, m)
-            rows.append({"n_out": N, "K": K, "pattern": f"{n}:{m}", "tokens": T, "us": us,
-                         "bytes": fb, "GBps": fb / us / 1e3,
-                         "frac_hbm": fb / us / 1e3 / HBM_PEAK_GBS})
-        for p in pws:
-            p.free()
+        xs = [(torch.randn((T, K), device="cuda", generator=gen)).to(torch.bfloat16)
+              for T in (1, 16)]
+        # the positional plane (2 bits per weight), then the compact plane ((m + n) / m bits per
+        # weight), each over enough packed copies that the weights stream from HBM
+        for plane, kw, bits in (("positional", {}, 2.0), ("compact", {"compact": True},
+                                                          (m + n) / m)):
+            R = max(1, -(-args.rotate_bytes // int(N * K * bits / 8)))
+            pws = [gpu.b.PackedWeight(w, n, m, **kw) for _ in range(R)]
+            for x in xs:
+                T = x.shape[0]
+                q, a = gpu.b.quantize_act(x)
+                y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+                us = gpu.time_launches(
+                    lambda i: gpu.b.bitlinear(q, a, pws[i % R], out="f32", y=y),
+                    max(args.steps, 100)) * 1e3
+                fb = forward_bytes(T, K, N, n, m)
+                rows.append({"n_out": N, "K": K, "pattern": f"{n}:{m}", "tokens": T,
+                             "plane": plane, "plane_bits_per_weight": bits, "us": us,
+                             "bytes": fb, "GBps": fb / us / 1e3,
+                             "frac_hbm": fb / us / 1e3 / HBM_PEAK_GBS})
+            for p in pws:
+                p.free()
+        del w, xs
         torch.cuda.empty_cache()
     return {"workload": "decode_gemv_large_k (int8 GEMV; extra shapes, N(0, 0.02) weights)",
             "rows": rows}

@@ -59,9 +59,12 @@ template <int FORM, int Q, int RB>
 __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
     const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
     int ld_q, int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
-    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind) {
-  static_assert(FORM == kFormPositional || FORM == kFormSparse24, "positional or 2:4 codes");
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int cn, int csb) {
+  constexpr bool CMP = compact_form(FORM);
+  static_assert(FORM == kFormPositional || FORM == kFormSparse24 || (CMP && RB == 1),
+                "positional, 2:4 or (one row block) compact codes");
   __shared__ v4i red[RB][kGemvMaxWaves][64];
+  __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
@@ -69,19 +72,42 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
   const bool tok_ok = t < T;
   // The RB row blocks' quads are consecutive in the plane; stored row blocks are padded to a
   // multiple of 16, so a last block past n_out exists (zero bricks; its rows are not stored).
+  // Compact plane: a quad takes cq = 512 + 8 csb bytes (the lanes' nonzero masks, then their sign
+  // slots as one bit stream); the range ends kCompactSlack bytes past the row block's last quad
+  // (the plane has that slack), which covers every lane's three-word sign load.
+  const int cq = CMP ? (int)compact_quad_bytes(csb) : 1024;
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(code_plane + rb0 * nq * 1024), (short)0, RB * nq * 1024, kBufDword3);
+      const_cast<uint8_t*>(code_plane + rb0 * nq * cq), (short)0,
+      RB * nq * cq + (CMP ? kCompactSlack : 0), kBufDword3);
   uint32_t codes[RB][Q][4];
+  uint32_t cmask[CMP ? Q : 1][2];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
       const int q = wave + i * W;
-      const v4i c = __builtin_amdgcn_raw_buffer_load_b128(
-          crs, lane * 16, q < nq ? (r * nq + q) * 1024 : RB * nq * 1024, kPlaneLoad);
-      codes[r][i][0] = (uint32_t)c[0]; codes[r][i][1] = (uint32_t)c[1];
-      codes[r][i][2] = (uint32_t)c[2]; codes[r][i][3] = (uint32_t)c[3];
+      if constexpr (CMP) {
+        // the lane's nonzero mask and the three words holding its csb sign bits; quads past the
+        // last read zero (an offset past the range)
+        const int qo = q < nq ? q * cq : nq * cq + kCompactSlack;
+        const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, qo, kPlaneLoad);
+        const int sbit = lane * csb;
+        const v3u sg = __builtin_amdgcn_raw_buffer_load_b96(
+            crs, kCompactMaskBytes + 4 * (sbit >> 5), qo, kPlaneLoad);
+        cmask[i][0] = mk[0]; cmask[i][1] = mk[1];
+        codes[r][i][0] = sg[0]; codes[r][i][1] = sg[1]; codes[r][i][2] = sg[2];
+        codes[r][i][3] = (uint32_t)(sbit & 31);
+      } else {
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(
+            crs, lane * 16, q < nq ? (r * nq + q) * 1024 : RB * nq * 1024, kPlaneLoad);
+        codes[r][i][0] = (uint32_t)c[0]; codes[r][i][1] = (uint32_t)c[1];
+        codes[r][i][2] = (uint32_t)c[2]; codes[r][i][3] = (uint32_t)c[3];
+      }
     }
+  if constexpr (CMP) {
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
+    __syncthreads();  // the table, after the plane loads went out
+  }
   // one resource over the T activation rows: quads past the last read zero (offsets past the
   // range); (T - 1) ld_q + K < 2^31 (T <= 16, ld_q <= 2^26)
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
@@ -120,6 +146,14 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
             exp_word_to_i8(codes[r][i][2 * blk], a);
             acc[r] = smfmac16(a, b[2 * blk], b[2 * blk + 1], codes[r][i][2 * blk + 1], acc[r]);
           }
+        } else if constexpr (CMP) {
+          uint32_t a[16];
+          const uint32_t sh = codes[r][i][3];
+          const uint32_t lo = __builtin_amdgcn_alignbit(codes[r][i][1], codes[r][i][0], sh);
+          const uint32_t hi = __builtin_amdgcn_alignbit(codes[r][i][2], codes[r][i][1], sh);
+          decode_compact<compact_m(FORM)>(cmask[i], lo, hi, cn, csb, clut, a);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r] = mfma16(a + 4 * j, b[j], acc[r]);
         } else {
           uint32_t a[16];
 #pragma unroll
@@ -170,10 +204,11 @@ hipError_t launch_i8_deep(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
   const int Q = (int)((L.quads + W - 1) / W);
   const unsigned blocks = (unsigned)((L.row_blocks + RB - 1) / RB);
+  const uint8_t* plane = compact_form(FORM) ? h->cplane : h->codes;
 #define SBN_DEEP(QQ)                                                                           \
   hipLaunchKernelGGL((bitlinear_gemv_i8_deep<FORM, QQ, RB>), dim3(blocks), dim3(64 * W), 0, s, \
-                     h->codes, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, W, absmax,         \
-                     h->gamma_out(), y, ld_y, L.n_out, out_kind)
+                     plane, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, W, absmax,            \
+                     h->gamma_out(), y, ld_y, L.n_out, out_kind, L.n, L.csb)
   if constexpr (RB > 1) {  // (launched for one batch only: Q <= kGemvMaxQ)
     switch (Q) {
       case 1: SBN_DEEP(1); break;
@@ -378,6 +413,13 @@ hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   const bool deep_form = xvec && !h->compact &&
                          (L.form == kFormSparse24 || L.form == kFormPositional) &&
                          L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ;
+  // The compact plane past one batch takes the same kernel (one row block per workgroup).
+  if (xvec && h->compact && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ &&
+      L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ) {
+    if (L.m == 4) return launch_i8_deep<kFormCompact4, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    if (L.m == 8) return launch_i8_deep<kFormCompact8, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    return launch_i8_deep<kFormCompact16, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  }
   if (deep_form && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     if (L.form == kFormSparse24)
       return launch_i8_deep<kFormSparse24, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);

@@ -94,3 +94,21 @@ def test_two_row_blocks_per_workgroup(n, m, T, N, K, ld_q):
     acc_ref = oracle.int_matmul(q_ref, r["codes"])
     assert np.array_equal(r["acc"], acc_ref)
     gu.assert_y_close(r["y"], oracle.dequantize(acc_ref, r["gamma"], a_ref))
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16), (4, 8)])
+@pytest.mark.parametrize("T", [1, 3, 16])
+@pytest.mark.parametrize("K", [12544, 28672, 32768])
+def test_large_k_compact_plane(n, m, T, K):
+    """The compact plane past one batch (49 to 128 quads) in the kernel that loads all of a wave's
+    quads at once: masks and sign slots per lane, the nibble table in LDS; every output equals the
+    oracle and the positional plane's."""
+    x, w = _case(K + 5 * T + m, T, 72, K)
+    r = _run(x, w, n, m, compact=True)
+    q_ref, a_ref = oracle.quantize_act(x)
+    acc_ref = oracle.int_matmul(q_ref, oracle.pack_nm_ternary(w, n, m)["codes"])
+    assert np.array_equal(r["acc"], acc_ref)
+    gu.assert_y_close(r["y"], oracle.dequantize(acc_ref, r["gamma"], a_ref))
+    assert np.array_equal(r["yb"], r["y"])
+    rp = _run(x, w, n, m)
+    assert np.array_equal(rp["y"].view(np.uint32), r["y"].view(np.uint32))
