@@ -196,6 +196,183 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
   }
 }
 
+// One to four tokens past one batch (49 to 128 quads): the workgroup first copies the activation
+// rows into LDS (1 KB pieces, global -> LDS directly, issued before the brick loads so they come
+// back first), and the waves read their B operands from there. The waves then keep no activation
+// registers (64 or fewer VGPRs against about 100 in bitlinear_gemv_i8_deep), so two workgroups of
+// 16 waves fit a CU and a launch of 512 row blocks runs in one round instead of two, and quad i is
+// multiplied as soon as its bricks land. XC: LDS pieces per wave (the launcher's round-up of
+// T * Kp / 1 KB / W); pieces past the rows go to a dummy KB past them. Same-box A/B against
+// bitlinear_gemv_i8_deep at one token (us): 8192 x 28672 8:16 18.2 -> 13.9 (4.2 TB/s), 2:4
+// 17.0 -> 13.1, 5120 x 13824 6:8 9.9 -> 7.5; the compact plane 23.0 -> 23.0 (8:16) and
+// 13.1 -> 11.2 (6:8).
+template <int FORM, int Q, int XC>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep_xl(
+    const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
+    int ld_q, int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int cn, int csb) {
+  constexpr bool CMP = compact_form(FORM);
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl_s[];  // T rows of Kp bytes, dummy KB
+  __shared__ v4i red[kGemvMaxWaves][64];
+  __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t rb0 = blockIdx.x;
+  const int t = lane & 15, g = lane >> 4;
+  const bool tok_ok = t < T;
+  const int kc = (K + 1023) >> 10, Kp = kc << 10;  // 1 KB pieces per row, padded row length
+  // Activation pieces: piece c = wave + i W is row c / kc, bytes (c % kc) KB .. +1 KB (past K:
+  // zero, the resource ends with the row); pieces past the T rows read nothing and land in the
+  // dummy KB at T Kp.
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int c = wave + i * W;
+    const bool real = c < T * kc;
+    const int tt = real ? c / kc : 0, cc = real ? c % kc : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(xq + (int64_t)tt * ld_q + cc * 1024), (short)0,
+        real ? K - cc * 1024 : 0, kBufDword3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr)(xl_s + (real ? tt * Kp + cc * 1024 : T * Kp)), 16, lane * 16, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the pieces go out before the bricks
+  const int cq = CMP ? (int)compact_quad_bytes(csb) : 1024;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(code_plane + rb0 * nq * cq), (short)0,
+      nq * cq + (CMP ? kCompactSlack : 0), kBufDword3);
+  uint32_t codes[Q][4];
+  uint32_t cmask[CMP ? Q : 1][2];
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    const int q = wave + i * W;
+    if constexpr (CMP) {
+      const int qo = q < nq ? q * cq : nq * cq + kCompactSlack;
+      const v2u mk = __builtin_amdgcn_raw_buffer_load_b64(crs, lane * 8, qo, kPlaneLoad);
+      const int sbit = lane * csb;
+      const v3u sg = __builtin_amdgcn_raw_buffer_load_b96(
+          crs, kCompactMaskBytes + 4 * (sbit >> 5), qo, kPlaneLoad);
+      cmask[i][0] = mk[0]; cmask[i][1] = mk[1];
+      codes[i][0] = sg[0]; codes[i][1] = sg[1]; codes[i][2] = sg[2];
+      codes[i][3] = (uint32_t)(sbit & 31);
+    } else {
+      const v4i c = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16,
+                                                          q < nq ? q * 1024 : nq * 1024, kPlaneLoad);
+      codes[i][0] = (uint32_t)c[0]; codes[i][1] = (uint32_t)c[1];
+      codes[i][2] = (uint32_t)c[2]; codes[i][3] = (uint32_t)c[3];
+    }
+  }
+  // The activation pieces went out first and return first: waiting until only the brick loads
+  // (Q, or 2 Q for the compact plane) are in flight means this wave's pieces are in LDS.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(CMP ? 2 * Q : Q));
+  __builtin_amdgcn_sched_barrier(0);
+  const float gamma = gamma_p[0];
+  const float a_t = out_kind == SBN_OUT_F32 && tok_ok ? absmax[t] : 0.0f;
+  if constexpr (CMP) {
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) clut[e] = compact_nibble_entry(e);
+  }
+  __syncthreads();  // every wave's pieces (and the nibble table)
+  v4i acc = v4i{0, 0, 0, 0};
+  const uint8_t* const xrow = xl_s + t * Kp;
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    const int q = wave + i * W;
+    if (q < nq) {
+      v4i b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = tok_ok ? *reinterpret_cast<const v4i*>(xrow + q * kQuadK + 16 * b_chunk<FORM>(g, j))
+                      : v4i{0, 0, 0, 0};
+      if constexpr (FORM == kFormSparse24) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          uint32_t a[4];
+          exp_word_to_i8(codes[i][2 * blk], a);
+          acc = smfmac16(a, b[2 * blk], b[2 * blk + 1], codes[i][2 * blk + 1], acc);
+        }
+      } else if constexpr (CMP) {
+        uint32_t a[16];
+        const uint32_t sh = codes[i][3];
+        const uint32_t lo = __builtin_amdgcn_alignbit(codes[i][1], codes[i][0], sh);
+        const uint32_t hi = __builtin_amdgcn_alignbit(codes[i][2], codes[i][1], sh);
+        decode_compact<compact_m(FORM)>(cmask[i], lo, hi, cn, csb, clut, a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[j], acc);
+      } else {
+        uint32_t a[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[i][j], a + 4 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[j], acc);
+      }
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || !tok_ok) return;
+  v4i sum = red[0][lane];
+  for (int w = 1; w < W; ++w) sum += red[w][lane];
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
+  const int64_t row0 = rb0 * 16 + 4 * g;
+  const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < n_out;
+  if (vec) {
+    if (out_kind == SBN_OUT_I32_ACC) {
+      *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + row0) = sum;
+    } else {
+      float4 f;
+      f.x = __fmul_rn(__fmul_rn((float)sum[0], gamma), step);
+      f.y = __fmul_rn(__fmul_rn((float)sum[1], gamma), step);
+      f.z = __fmul_rn(__fmul_rn((float)sum[2], gamma), step);
+      f.w = __fmul_rn(__fmul_rn((float)sum[3], gamma), step);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + row0) = f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (row0 + i < n_out) store_out(y, ld_y, out_kind, t, row0 + i, sum[i], gamma, step);
+  }
+}
+
+template <int FORM>
+hipError_t launch_i8_deep_xl(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
+                             const float* absmax, int64_t T, void* y, int64_t ld_y,
+                             int out_kind, hipStream_t s) {
+  const Layout& L = h->L;
+  const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+  const int Q = (int)((L.quads + W - 1) / W);
+  const int64_t kc = (L.K + 1023) >> 10;
+  const int64_t pieces = (T * kc + W - 1) / W;  // per wave
+  const size_t smem = (size_t)(T * kc + 1) * 1024;
+  const uint8_t* plane = compact_form(FORM) ? h->cplane : h->codes;
+#define SBN_XL(QQ, XX)                                                                         \
+  do {                                                                                         \
+    hipError_t e = allow_smem(bitlinear_gemv_i8_deep_xl<FORM, QQ, XX>, smem);                  \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_gemv_i8_deep_xl<FORM, QQ, XX>), dim3((unsigned)L.row_blocks), \
+                       dim3(64 * W), smem, s, plane, xq, (int)L.quads, (int)L.K, (int)ld_q,      \
+                       (int)T, W, absmax, h->gamma_out(), y, ld_y, L.n_out, out_kind, L.n,      \
+                       L.csb);                                                                 \
+  } while (0)
+#define SBN_XL_Q(XX)                                                                           \
+  switch (Q) {                                                                                 \
+    case 4: SBN_XL(4, XX); break;                                                              \
+    case 5: SBN_XL(5, XX); break;                                                              \
+    case 6: SBN_XL(6, XX); break;                                                              \
+    case 7: SBN_XL(7, XX); break;                                                              \
+    default: SBN_XL(8, XX); break;                                                             \
+  }
+  if (pieces <= 2) {
+    SBN_XL_Q(2);
+  } else if (pieces <= 4) {
+    SBN_XL_Q(4);
+  } else {
+    SBN_XL_Q(8);
+  }
+#undef SBN_XL_Q
+#undef SBN_XL
+  return hipGetLastError();
+}
+
 template <int FORM, int RB>
 hipError_t launch_i8_deep(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                           const float* absmax, int64_t T, void* y, int64_t ld_y, int out_kind,
@@ -413,6 +590,18 @@ hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   const bool deep_form = xvec && !h->compact &&
                          (L.form == kFormSparse24 || L.form == kFormPositional) &&
                          L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ;
+  // One to four tokens past one batch: activations staged in LDS (any code form but the kept one)
+  if (xvec && T <= kFusedMaxT && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ &&
+      L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ && L.form != kFormKept) {
+    if (h->compact) {
+      if (L.m == 4) return launch_i8_deep_xl<kFormCompact4>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+      if (L.m == 8) return launch_i8_deep_xl<kFormCompact8>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+      return launch_i8_deep_xl<kFormCompact16>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    }
+    if (L.form == kFormSparse24)
+      return launch_i8_deep_xl<kFormSparse24>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    return launch_i8_deep_xl<kFormPositional>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  }
   // The compact plane past one batch takes the same kernel (one row block per workgroup).
   if (xvec && h->compact && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ &&
       L.quads <= (int64_t)kGemvMaxWaves * kDeepMaxQ) {

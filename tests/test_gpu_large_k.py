@@ -1,8 +1,9 @@
 """GPU parity of the GEMV on large K (T <= 16): past 48 quads (K > 12288) each wave loads the bricks
-of all its quads at once (up to 128 quads, K <= 32768; positional and 2:4 codes, aligned int8
-rows), otherwise the waves take batches of 48 quads in turn, so decode on e.g. 13B- and 70B-style
-down projections stays a GEMV. Integer
-accumulators are exact; fp32 outputs follow the oracle within the forward's tolerance."""
+of all its quads at once (up to 128 quads, K <= 32768; positional, 2:4 and compact codes, aligned
+int8 rows; for one to four tokens the activation rows are first staged in LDS), otherwise the waves
+take batches of 48 quads in turn, so decode on e.g. 13B- and 70B-style down projections stays a
+GEMV. Integer accumulators are exact; fp32 outputs follow the oracle within the forward's
+tolerance."""
 
 import numpy as np
 import pytest
