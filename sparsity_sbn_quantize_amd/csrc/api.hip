@@ -69,14 +69,20 @@ sbn_status make_plan(int64_t n_out, int64_t K, int n, int m, Plan& p) {
   off = align_up(off + sizeof(float), 256);
   p.off_part = off;
   off = align_up(off + sizeof(double) * p.num_partials, 256);
+  // large-K GEMV split over K: its counters follow the split-K words (zeroed together)
+  const bool kx = L.quads >= kKxMinQuads && L.quads <= kKxMaxQuads && L.form != kFormKept;
+  p.kx_chunks = kx ? (int)((L.quads + kKxQuads - 1) / kKxQuads) : 0;
+  const int64_t kx_groups = kx ? kx_row_groups(L.row_blocks) : 0;
   p.off_sync = off;
-  off = align_up(off + sizeof(uint32_t) * (kGemmSyncInts + 1), 256);
+  off = align_up(off + sizeof(uint32_t) * (kGemmSyncInts + 1 + kx_groups), 256);
   p.off_flips = off;
   off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
   p.off_vc = off;
   off = align_up(off + 2 * sizeof(uint32_t) * slots / 16, 256);
   p.off_gamma_vc = off;
   off = align_up(off + sizeof(float), 256);
+  p.off_kx = off;
+  off = align_up(off + (size_t)kx_groups * p.kx_chunks * 16 * 1024, 256);
   p.forward_bytes = off;  // everything the pack and the forward use
   p.rq_count = (n_out + 127) / 128;
   p.off_tplane = off;
@@ -116,6 +122,9 @@ void bind_planes(sbn_packed& h, const Plan& p, uint8_t* base) {
   h.gamma = reinterpret_cast<float*>(base + p.off_gamma);
   h.partials = reinterpret_cast<double*>(base + p.off_part);
   h.gemm_sync = reinterpret_cast<uint32_t*>(base + p.off_sync);
+  h.kx_count = h.gemm_sync + kGemmSyncInts + 1;
+  h.kx_part = base + p.off_kx;
+  h.kx_chunks = p.kx_chunks;
   h.flip_parts = reinterpret_cast<uint32_t*>(base + p.off_flips);
   h.vc_parts = reinterpret_cast<uint32_t*>(base + p.off_vc);
   h.gamma_vc = reinterpret_cast<float*>(base + p.off_gamma_vc);

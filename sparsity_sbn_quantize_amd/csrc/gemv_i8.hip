@@ -333,6 +333,164 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep_xl(
   }
 }
 
+// Five to sixteen tokens past one batch (49 to 128 quads, positional or 2:4 codes): every row
+// block of the kernels above re-reads all T activation rows (235 MB from L2 for 8192 x 28672 at
+// T = 16, against 58.7 MB of codes). Here a workgroup takes 16 row blocks (256 rows, one per wave)
+// and one K chunk of kKxQuads quads: the chunk's T x 1.75 KB of activations go to LDS once and serve
+// all 16 waves, and the K chunks of a row group meet through int32 partial sums. At most 64 VGPRs,
+// so two workgroups share a CU (8192 x 28672: 32 row groups x 16 chunks, one round). Same-box
+// A/B at T = 16 against bitlinear_gemv_i8_deep (us): 8192 x 28672 8:16 34.8 -> 28.3, 2:4 33.2 ->
+// 26.4, 5120 x 13824 6:8 18.8 -> 16.2 (8-quad chunks at 70 VGPRs, one workgroup per CU: 31.8,
+// 31.9, 16.6). Each workgroup
+// stores its waves' partial sums (16 KB) in the handle, waits for them, and counts its arrival on
+// the row group's counter; the last arrival of the group (the C - 1-th after the others') adds
+// the other chunks' partial sums to its own (integer sums: any order gives the same result),
+// writes y and resets the counter. No workgroup waits for another. A row group's chunks run on one
+// XCD (the grid is padded so that every XCD's contiguous run of the grouped order holds whole
+// row groups; padding workgroups exit at once), so their partial sums and counter meet in that
+// XCD's L2; the last arrival reads them past its L1.
+template <int FORM, int XC>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void bitlinear_gemv_i8_kx(
+    const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
+    int ld_q, int T, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int C, int RG,
+    uint8_t* __restrict__ part, uint32_t* __restrict__ count) {
+  constexpr int KQ = kKxQuads;
+  constexpr int kCk = KQ * kQuadK;  // activation bytes of one row in a chunk
+  constexpr int kRow = 2048;        // their LDS row: two 1 KB pieces (KQ <= 8)
+  static_assert(kCk <= kRow, "two pieces per row");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[17 * kRow];  // 16 rows, a dummy row
+  __shared__ int last_s;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int lin = xcd_order((int)gridDim.x, (int)blockIdx.x);
+  const int grp = lin / C, c = lin % C;
+  if (grp >= RG) return;  // padding (the whole workgroup)
+  const int64_t rb = (int64_t)grp * 16 + wave;
+  const int t = lane & 15, g = lane >> 4;
+  const bool tok_ok = t < T;
+  // activation pieces: piece p = wave + i 16 of the chunk is row p / 2, bytes (p % 2) KB .. +1 KB
+  // from the chunk's start (past K: zero; past the chunk: the next chunk's bytes, unused); pieces
+  // past the T rows land in the dummy row
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int pc = wave + i * kGemvMaxWaves;
+    const bool real = pc < 2 * T;
+    const int tt = real ? pc >> 1 : 0, hb = real ? pc & 1 : 0;
+    const int64_t k0 = (int64_t)c * kCk + hb * 1024;
+    const int64_t left = K - k0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(xq + (int64_t)tt * ld_q + k0), (short)0,
+        real && left > 0 ? (int)left : 0, kBufDword3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr)(xs + (real ? tt * kRow + hb * 1024 : 16 * kRow)), 16, lane * 16, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the pieces go out before the bricks
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(code_plane + rb * nq * 1024), (short)0, nq * 1024, kBufDword3);
+  uint32_t codes[KQ][4];
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) {
+    const int q = c * KQ + i;
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(crs, lane * 16,
+                                                        q < nq ? q * 1024 : nq * 1024, kPlaneLoad);
+    codes[i][0] = (uint32_t)v[0]; codes[i][1] = (uint32_t)v[1];
+    codes[i][2] = (uint32_t)v[2]; codes[i][3] = (uint32_t)v[3];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(KQ));  // only the brick loads are still in flight
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();  // every wave's pieces are in LDS
+  v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) {
+    v4i b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = tok_ok ? *reinterpret_cast<const v4i*>(xs + t * kRow + i * kQuadK +
+                                                    16 * b_chunk<FORM>(g, j))
+                    : v4i{0, 0, 0, 0};
+    if constexpr (FORM == kFormSparse24) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        uint32_t a[4];
+        exp_word_to_i8(codes[i][2 * blk], a);
+        acc = smfmac16(a, b[2 * blk], b[2 * blk + 1], codes[i][2 * blk + 1], acc);
+      }
+    } else {
+      uint32_t a[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) exp_word_to_i8(codes[i][j], a + 4 * j);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma16(a + 4 * j, b[j], acc);
+    }
+  }
+  // this chunk's partial sums: 16 waves x 64 lanes x 16 bytes at (group, chunk)
+  uint8_t* const pg = part + (int64_t)grp * C * 16384;
+  *reinterpret_cast<v4i*>(pg + c * 16384 + wave * 1024 + lane * 16) = acc;
+  __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(count + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = old == (uint32_t)(C - 1);
+  }
+  __syncthreads();
+  if (!last_s) return;
+  constexpr int kGlc = 1;  // buffer cache-policy bit sc0: read past L1
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(pg, (short)0, C * 16384, kBufDword3);
+  for (int cc = 0; cc < C; ++cc)
+    if (cc != c) acc += __builtin_amdgcn_raw_buffer_load_b128(pr, wave * 1024 + lane * 16,
+                                                              cc * 16384, kGlc);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(count + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!tok_ok) return;
+  const float gamma = gamma_p[0];
+  const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
+  const int64_t row0 = rb * 16 + 4 * g;
+  const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < n_out;
+  if (vec) {
+    if (out_kind == SBN_OUT_I32_ACC) {
+      *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(y) + t * ld_y + row0) = acc;
+    } else {
+      float4 f;
+      f.x = __fmul_rn(__fmul_rn((float)acc[0], gamma), step);
+      f.y = __fmul_rn(__fmul_rn((float)acc[1], gamma), step);
+      f.z = __fmul_rn(__fmul_rn((float)acc[2], gamma), step);
+      f.w = __fmul_rn(__fmul_rn((float)acc[3], gamma), step);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * ld_y + row0) = f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (row0 + i < n_out) store_out(y, ld_y, out_kind, t, row0 + i, acc[i], gamma, step);
+  }
+}
+
+template <int FORM>
+hipError_t launch_i8_kx(const sbn_packed* h, const int8_t* xq, int64_t ld_q, const float* absmax,
+                        int64_t T, void* y, int64_t ld_y, int out_kind, hipStream_t s) {
+  const Layout& L = h->L;
+  const int C = h->kx_chunks;
+  const int64_t RG = (L.row_blocks + 15) / 16, RGp = kx_row_groups(L.row_blocks);
+  const unsigned blocks = (unsigned)(RGp * C);
+  // activation pieces per wave: 2 T over 16 waves
+  if (T <= 8) {
+    hipLaunchKernelGGL((bitlinear_gemv_i8_kx<FORM, 1>), dim3(blocks), dim3(64 * kGemvMaxWaves), 0,
+                       s, h->codes, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, absmax,
+                       h->gamma_out(), y, ld_y, L.n_out, out_kind, C, (int)RG, h->kx_part,
+                       h->kx_count);
+  } else {
+    hipLaunchKernelGGL((bitlinear_gemv_i8_kx<FORM, 2>), dim3(blocks), dim3(64 * kGemvMaxWaves), 0,
+                       s, h->codes, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, absmax,
+                       h->gamma_out(), y, ld_y, L.n_out, out_kind, C, (int)RG, h->kx_part,
+                       h->kx_count);
+  }
+  return hipGetLastError();
+}
+
 template <int FORM>
 hipError_t launch_i8_deep_xl(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                              const float* absmax, int64_t T, void* y, int64_t ld_y,
@@ -601,6 +759,13 @@ hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
     if (L.form == kFormSparse24)
       return launch_i8_deep_xl<kFormSparse24>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
     return launch_i8_deep_xl<kFormPositional>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+  }
+  // Five to sixteen tokens past one batch: split over K, activations shared through LDS
+  if (xvec && T > kFusedMaxT && !h->compact && h->kx_chunks > 0 && L.quads >= kKxMinQuads &&
+      L.quads <= kKxMaxQuads && (L.form == kFormPositional || L.form == kFormSparse24)) {
+    if (L.form == kFormSparse24)
+      return launch_i8_kx<kFormSparse24>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    return launch_i8_kx<kFormPositional>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
   }
   // The compact plane past one batch takes the same kernel (one row block per workgroup).
   if (xvec && h->compact && L.quads > (int64_t)kGemvMaxWaves * kGemvMaxQ &&

@@ -22,6 +22,10 @@ struct sbn_packed {
   double* partials;    // device workspace [num_partials]
   uint32_t* gemm_sync;  // split-K words: kGemmSyncInts (two per slot, never reset), then the
                         // give-up counter
+  uint32_t* kx_count;   // large-K GEMV split over K: one arrival counter per 256-row group (in
+                        // the split-K words' region, reset by each group's last arrival)
+  uint8_t* kx_part;     // its int32 partial sums, 16 KB per (row group, K chunk)
+  int kx_chunks;        // K chunks of that split (0: the layout has none)
   int splitk_spin_limit;  // s_sleep rounds before a waiting split-K half gives up
   int splitk_publish;     // 1; 0 only in the test mode that withholds the partial sums
   uint32_t* flip_parts;  // keep bits changed by the last pack, one count per pack wave
@@ -56,6 +60,11 @@ sbn_status set_error(sbn_status code, const char* fmt, ...);
 // Words of split-K handshake a handle holds (2 per wave of up to 256 tiles x 4 waves); the
 // give-up counter follows them.
 constexpr int kGemmSyncInts = 256 * 4 * 2;
+// Large-K GEMV split over K (5 to 16 tokens, 49 to 128 quads): quads per K chunk, and the row
+// groups (16 row blocks each) rounded up to a multiple of the 8 XCDs.
+constexpr int kKxQuads = 7;
+constexpr int kKxMinQuads = 49, kKxMaxQuads = 128;
+inline int64_t kx_row_groups(int64_t row_blocks) { return ((row_blocks + 15) / 16 + 7) / 8 * 8; }
 // s_sleep rounds a waiting split-K half spins before it gives up (its partner is already past its
 // main loop, so this is never reached in a correct run).
 constexpr int kSplitSpinLimit = 1 << 24;
@@ -70,7 +79,8 @@ struct Plan {
   bool oplanes;
   size_t mask_bytes, code_bytes, cplane_bytes;
   size_t off_mask, off_codes, off_gamma, off_part, off_sync, off_flips, off_vc, off_gamma_vc,
-      off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum;
+      off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum, off_kx;
+  int kx_chunks;
   size_t forward_bytes, total_bytes;
 };
 size_t align_up(size_t v, size_t a);

@@ -113,3 +113,29 @@ def test_large_k_compact_plane(n, m, T, K):
     assert np.array_equal(r["yb"], r["y"])
     rp = _run(x, w, n, m)
     assert np.array_equal(rp["y"].view(np.uint32), r["y"].view(np.uint32))
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16)])
+@pytest.mark.parametrize("T", [5, 9, 12])
+@pytest.mark.parametrize("K,N", [(12544, 72), (28672, 520), (32768, 264)])
+def test_large_k_split_over_k(n, m, T, K, N):
+    """Five to sixteen tokens past one batch: workgroups of 16 row blocks and one 8-quad K chunk,
+    the chunk's activations shared through LDS, the chunks' int32 partial sums met by the row
+    group's last arrival (which resets the group's counter). Three calls in a row on one handle
+    give the oracle's integers each time (a counter left over would merge the wrong chunks);
+    ragged row groups (72, 520 and 264 rows) and a ragged last K chunk (K = 12544: 49 quads)."""
+    import torch
+    x, w = _case(K + 11 * T + n, T, N, K)
+    xd = gu.to_dev_bf16(x)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m)
+    q, a = binding.quantize_act(xd)
+    q_ref, a_ref = oracle.quantize_act(x)
+    acc_ref = oracle.int_matmul(q_ref, oracle.pack_nm_ternary(w, n, m)["codes"])
+    g = np.float32(pw.export()[2].cpu().numpy()[0])
+    for _ in range(3):
+        acc = binding.bitlinear(q, a, pw, out="i32")
+        y = binding.bitlinear(q, a, pw, out="f32")
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), acc_ref)
+        gu.assert_y_close(y.cpu().numpy(), oracle.dequantize(acc_ref, g, a_ref))
+    pw.free()
