@@ -107,6 +107,13 @@ sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t
  *   pools; with sbn_free, the only allocations the library makes) and returned in *handle (host). Otherwise the existing handle is re-packed in place, with no
  *   allocation; it must have been made with the same n_out, K, n_keep, m_group (else
  *   SBN_ERR_SHAPE). Every call recomputes gamma and the mask from the current weights.
+ *   Reads of w_latent: the first pack of a handle reads it twice (gamma must be known before a
+ *   code is written). A re-pack with flags 0 of the patterns 2:4, 4:8, 6:8, 8:16 and n = m reads
+ *   it once: the previous gamma brackets the new threshold (gamma / 2 within 2^-7 of the old
+ *   one), the few 16-weight pieces with a kept magnitude inside the bracket are finished after
+ *   the new gamma is known, and if the threshold left the bracket the codes are rewritten from a
+ *   second read. The result is the same in every case; sbn_packed_desc.single_pass says which
+ *   path the last pack took.
  * Requires m_group in {4, 8, 16}, 1 <= n_keep <= m_group, K % m_group == 0,
  * m_group <= K <= SBN_MAX_K, 0 <= n_out < 2^31, ld_w >= K.
  */
@@ -367,6 +374,7 @@ typedef struct {
   int outlier_k;                         /* k of the last pack's k:256 outliers (0: none) */
   size_t rank_row_bytes;                 /* rank export row size, ceil((K/m)(R + 2n)/8) */
   uint32_t splitk_giveups;               /* split-K waits that gave up (0 in a correct run) */
+  int single_pass;                       /* the last pack was a single-read re-pack */
 } sbn_packed_desc;
 
 /*

@@ -38,7 +38,8 @@ class PackedDesc(ctypes.Structure):
                 ("packed_bytes", ctypes.c_size_t), ("device_bytes", ctypes.c_size_t),
                 ("compact_row_bytes", ctypes.c_size_t), ("compact_bytes", ctypes.c_size_t),
                 ("compact", ctypes.c_int), ("outlier_k", ctypes.c_int),
-                ("rank_row_bytes", ctypes.c_size_t), ("splitk_giveups", ctypes.c_uint32)]
+                ("rank_row_bytes", ctypes.c_size_t), ("splitk_giveups", ctypes.c_uint32),
+                ("single_pass", ctypes.c_int)]
 
 
 _lib = None

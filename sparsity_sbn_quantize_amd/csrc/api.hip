@@ -103,6 +103,10 @@ sbn_status make_plan(int64_t n_out, int64_t K, int n, int m, Plan& p) {
   off = align_up(off + (p.oplanes ? slots * 8 : 0), 256);
   p.off_osum = off;
   off = align_up(off + ogroups * sizeof(double), 256);
+  // single-pass re-pack: per-fragment partial sums, listed-piece counts and lists, the bracket
+  const size_t frags = (size_t)L.row_blocks_pad * (size_t)L.quads;
+  p.off_band = off;
+  off = align_up(off + frags * (sizeof(double) + kBandRecBytes) + 512 + kBandSlots * 128, 256);
   p.total_bytes = off;
   return SBN_OK;
 }
@@ -141,6 +145,17 @@ void bind_planes(sbn_packed& h, const Plan& p, uint8_t* base) {
   h.oval = reinterpret_cast<uint16_t*>(base + p.off_oval);
   h.omask = reinterpret_cast<unsigned long long*>(base + p.off_omask);
   h.osum = reinterpret_cast<double*>(base + p.off_osum);
+  {
+    const size_t frags = (size_t)L.row_blocks_pad * (size_t)L.quads;
+    uint8_t* b = base + p.off_band;
+    h.band_part = reinterpret_cast<double*>(b);
+    h.band_seg = b + frags * sizeof(double);
+    h.band_lim = reinterpret_cast<uint32_t*>(b + frags * (sizeof(double) + kBandRecBytes));
+    h.band_slots = reinterpret_cast<unsigned long long*>(
+        base + align_up(p.off_band + frags * (sizeof(double) + kBandRecBytes) + 256, 128));
+  }
+  h.gamma_valid = false;
+  h.single_pass = false;
   h.splitk_spin_limit = kSplitSpinLimit;
   h.splitk_publish = 1;
 }
@@ -446,6 +461,7 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
   h->outlier_k = outlier_k;
   hipError_t e = sbn::launch_pack(w_latent, ld_w, h, s);
   if (e != hipSuccess) return hip_fail(e, "sbn_pack_nm_ternary launch");
+  h->gamma_valid = true;  // the next pack of this handle may bracket its threshold with gamma
   return SBN_OK;
 }
 
@@ -618,6 +634,7 @@ sbn_status sbn_packed_query(const sbn_packed* w, sbn_packed_desc* out) {
                   hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "sbn_packed_query");
   out->splitk_giveups = giveups;
+  out->single_pass = w->single_pass ? 1 : 0;
   return SBN_OK;
 }
 

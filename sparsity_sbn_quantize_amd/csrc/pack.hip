@@ -17,6 +17,9 @@
 // so it is identical run to run. The pack kernel reads gamma from device memory (no host sync).
 #include "sbn_internal.hpp"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace sbn {
 namespace {
 
@@ -351,6 +354,581 @@ __global__ __launch_bounds__(256) void pack_fragments(const float* __restrict__ 
       vc_parts[(frag * 4 + (tid >> 6)) * 2] = d;
       vc_parts[(frag * 4 + (tid >> 6)) * 2 + 1] = sp;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Lean piece encoder and the single-pass re-pack.
+//
+// The same thread mapping as pack_fragments (one workgroup per fragment, thread t takes 16
+// consecutive positions of one row), with the keep mask and the codes built for fixed n:m
+// patterns (2:4, 4:8, 6:8, 8:16 and n = m) with fewer vector instructions: the n-th largest
+// magnitude of a group comes from a sorting network without run-time selects, the 16 predicate
+// bits of a thread are shifted in one per compare (the compare's lane mask is the carry of an
+// add), and the positional code word is two bit spreads of the nonzero and sign masks.
+//
+// Single pass. gamma must be known before a code can be written, so the first pack of a handle
+// reads the latent weights twice (absmean, then the codes). A re-pack instead takes the previous
+// pack's gamma g' and the bracket [T_lo, T_hi] = g'/2 (1 -+ 2^-7) around its threshold: every
+// kept magnitude above T_hi is nonzero and every one at or below T_lo is zero for any new
+// threshold inside the bracket, so one read writes the codes, the keep mask and gamma's partial
+// sums, and lists the pieces that hold a kept magnitude inside the bracket (their codes are
+// written as zero there). After the absmean is finalized, pack_fix checks that the new threshold
+// lies in the bracket and sets the listed pieces' nonzero codes; if it does not (gamma moved by
+// more than 2^-7), or a fragment listed more pieces than it has room for, pack_fix rewrites those
+// fragments' codes from the latent weights and the stored keep bits. The result is the same
+// planes as the two-pass pack in every case.
+constexpr float kBandHalfWidth = 0.0078125f;  // 2^-7
+
+// acc * 2 + predicate: a compare into VCC and an add with carry (one vector instruction each).
+__device__ __forceinline__ uint32_t shl_gt(uint32_t acc, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cmp_gt_u32_e32 vcc, %1, %2\n\tv_addc_co_u32_e32 %0, vcc, %3, %3, vcc"
+      : "=v"(r) : "v"(a), "v"(b), "v"(acc) : "vcc");
+  return r;
+}
+__device__ __forceinline__ uint32_t shl_ge(uint32_t acc, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cmp_ge_u32_e32 vcc, %1, %2\n\tv_addc_co_u32_e32 %0, vcc, %3, %3, vcc"
+      : "=v"(r) : "v"(a), "v"(b), "v"(acc) : "vcc");
+  return r;
+}
+__device__ __forceinline__ uint32_t shl_neg(uint32_t acc, uint32_t x) {
+  uint32_t r;
+  asm("v_cmp_gt_i32_e32 vcc, 0, %1\n\tv_addc_co_u32_e32 %0, vcc, %2, %2, vcc"
+      : "=v"(r) : "v"(x), "v"(acc) : "vcc");
+  return r;
+}
+
+// Position whose bit lands at bit k of a transposed mask: bit 4b + a holds position 4a + b, the
+// order of the positional code word (position i at bits 8 (i & 3) + 2 (i >> 2)).
+__device__ __forceinline__ constexpr int tpos(int k) { return 4 * (k & 3) + (k >> 2); }
+// Natural 16-bit mask (bit i = position i) to the transposed order.
+__device__ __forceinline__ uint32_t transpose4x4(uint32_t x) {
+  uint32_t t = (x ^ (x >> 3)) & 0x0A0Au;
+  x ^= t ^ (t << 3);
+  t = (x ^ (x >> 6)) & 0x00CCu;
+  x ^= t ^ (t << 6);
+  return x;
+}
+// Bit k to bit 2k.
+__device__ __forceinline__ uint32_t spread2(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  x = (x | (x << 1)) & 0x55555555u;
+  return x;
+}
+
+// The patterns with a lean encoder; N == M stands for every dense pattern.
+__host__ __device__ constexpr bool lean_pattern(int n, int m) {
+  return n == m || (m == 4 && n == 2) || (m == 8 && (n == 4 || n == 6)) || (m == 16 && n == 8);
+}
+
+// The n-th largest magnitude of each group (16 / M groups of the thread's 16).
+template <int M, int N>
+__device__ __forceinline__ void group_nth(const uint32_t* a, uint32_t* v) {
+  if constexpr (M == 4 && N == 2) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t* x = a + 4 * g;
+      const uint32_t h01 = max(x[0], x[1]), l01 = min(x[0], x[1]);
+      const uint32_t h23 = max(x[2], x[3]), l23 = min(x[2], x[3]);
+      v[g] = max(min(h01, h23), max(l01, l23));
+    }
+  } else if constexpr (M == 8) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      uint32_t s[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = a[8 * g + i];
+      sort8_desc(s);
+      v[g] = s[N - 1];
+    }
+  } else {
+    static_assert(M == 16, "lean patterns");
+    uint32_t A[8], B[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      A[i] = a[i];
+      B[i] = a[8 + i];
+    }
+    sort8_desc(A);
+    sort8_desc(B);
+    // n-th largest of the union of two descending lists: max over the split i (i from A, n - i
+    // from B) of the smaller of the two last elements taken
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i <= 8; ++i) {
+      const int j = N - i;
+      if (j < 0 || j > 8) continue;
+      const uint32_t x = i > 0 ? A[i - 1] : 0xFFFFFFFFu;
+      const uint32_t y = j > 0 ? B[j - 1] : 0xFFFFFFFFu;
+      r = max(r, min(x, y));
+    }
+    v[0] = r;
+  }
+}
+
+// Keep mask of the thread's 16 positions (bit i = position i), the rule of keep_mask_group: the
+// n largest magnitudes of each group, equal magnitudes to the lower position. Without ties the
+// positions at or above each group's n-th largest are exactly n per group; otherwise the group
+// takes those above it and the lowest positions equal to it. Groups starting at or past cnt are
+// empty. v receives the groups' n-th largest magnitudes.
+template <int M, int N>
+__device__ __forceinline__ uint32_t lean_keep(const uint32_t* a, int cnt, uint32_t* v) {
+  constexpr int G = 16 / M;
+  uint32_t keep;
+  if constexpr (N == M) {
+    keep = 0xFFFFu;
+  } else {
+    group_nth<M, N>(a, v);
+    uint32_t ge = 0;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) ge = shl_ge(ge, a[i], v[i / M]);
+    keep = ge;
+    if (__builtin_popcount(ge) != G * N) {
+      keep = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        uint32_t gt = 0;
+#pragma unroll
+        for (int i = 0; i < M; ++i) gt |= (a[g * M + i] > v[g] ? 1u : 0u) << i;
+        uint32_t eq = ((ge >> (g * M)) & ((1u << M) - 1u)) & ~gt;
+        uint32_t kept = gt;
+        for (int r = N - __builtin_popcount(gt); r > 0; --r) {
+          const uint32_t low = eq & (~eq + 1u);
+          kept |= low;
+          eq ^= low;
+        }
+        keep |= kept << (g * M);
+      }
+    }
+  }
+  if (cnt < 16) {
+    uint32_t live = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) live |= (g * M < cnt ? (1u << M) - 1u : 0u) << (g * M);
+    keep &= live;
+  }
+  return keep;
+}
+
+// Where a thread's 16 positions live: its fragment, row and K range, and its slots in the planes.
+struct PieceAt {
+  int64_t row, k0;
+  int cnt;        // positions inside the weight (0 for padding rows)
+  int lane_slot, word;
+};
+template <int FORM>
+__device__ __forceinline__ PieceAt piece_at(const Layout& L, int64_t frag, int tid) {
+  PieceAt p;
+  const int64_t rb = frag / L.quads, bq = frag % L.quads;
+  p.lane_slot = tid >> 2;
+  p.word = tid & 3;
+  p.row = rb * 16 + (p.lane_slot & 15);
+  const int qpos = FORM == kFormSparse24
+                       ? 128 * (p.word >> 1) + 32 * (p.lane_slot >> 4) + 16 * (p.word & 1)
+                       : kBrickK * (p.lane_slot >> 4) + 16 * p.word;
+  p.k0 = bq * kQuadK + qpos;
+  p.cnt = p.row < L.n_out ? (int)max<int64_t>(0, min<int64_t>(16, L.K - p.k0)) : 0;
+  return p;
+}
+// The thread's 16 keep bits in the mask plane (brick layout for the 2:4 form).
+template <int FORM>
+__device__ __forceinline__ uint16_t* piece_mask(uint8_t* mask_plane, int64_t frag, int tid,
+                                                const PieceAt& p) {
+  if constexpr (FORM == kFormSparse24) {
+    const int qpos = 128 * (p.word >> 1) + 32 * (p.lane_slot >> 4) + 16 * (p.word & 1);
+    const int64_t mslot = (frag << 6) | ((p.lane_slot & 15) + 16 * (qpos >> 6));
+    return reinterpret_cast<uint16_t*>(mask_plane) + mslot * 4 + ((qpos & 63) >> 4);
+  } else {
+    return reinterpret_cast<uint16_t*>(mask_plane) + frag * 256 + tid;
+  }
+}
+__device__ __forceinline__ void load_piece(const float* w, int64_t ld_w, int vec4,
+                                           const PieceAt& p, uint32_t* u) {
+  const float* wr = w + p.row * ld_w + p.k0;
+  if (vec4 && p.cnt == 16) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 f = reinterpret_cast<const float4*>(wr)[v];
+      u[4 * v] = __float_as_uint(f.x);
+      u[4 * v + 1] = __float_as_uint(f.y);
+      u[4 * v + 2] = __float_as_uint(f.z);
+      u[4 * v + 3] = __float_as_uint(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = i < p.cnt ? __float_as_uint(wr[i]) : 0u;
+  }
+}
+
+// Writes the thread's code word from its keep mask, the nonzero cut (a kept magnitude above it
+// is nonzero) and the signs. Positional: one word per thread. 2:4: the thread pair (h = 0, 1)
+// exchanges halves and thread h writes word 2b + h (codes, index). All 64 lanes of the wave call
+// it together.
+template <int FORM>
+__device__ __forceinline__ void lean_codes(const uint32_t* u, const uint32_t* a, uint32_t keep,
+                                           uint32_t cut, uint32_t* code_word, int word) {
+  if constexpr (FORM == kFormPositional) {
+    uint32_t nzt = 0, sgt = 0;
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+      nzt = shl_gt(nzt, a[tpos(k)], cut);
+      sgt = shl_neg(sgt, u[tpos(k)]);
+    }
+    const uint32_t nt = nzt & transpose4x4(keep);
+    *code_word = spread2(nt) + spread2(nt & sgt);
+  } else {
+    static_assert(FORM == kFormSparse24, "lean forms");
+    uint32_t nz = 0, sgn = 0;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      nz = shl_gt(nz, a[i], cut);
+      sgn = shl_neg(sgn, u[i]);
+    }
+    nz &= keep;
+    const int h = word & 1;
+    uint32_t cw = 0, iw = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t k4 = (keep >> (4 * q)) & 0xFu;
+      const uint32_t lo = k4 ? (uint32_t)__builtin_ctz(k4) : 0u;
+      const uint32_t hi = k4 ? 31u - (uint32_t)__builtin_clz(k4) : 0u;
+      const uint32_t plo = 4 * q + lo, phi = 4 * q + hi;
+      const uint32_t clo = k4 ? ((nz >> plo) & 1u) << ((sgn >> plo) & 1u) : 0u;
+      const uint32_t chi = k4 ? ((nz >> phi) & 1u) << ((sgn >> phi) & 1u) : 0u;
+      const int slot = 8 * h + 2 * q;
+      cw |= (clo << sp24_code_bit(slot)) | (chi << sp24_code_bit(slot + 1));
+      iw |= (lo << (2 * slot)) | (hi << (2 * slot + 2));
+    }
+    const int src = (int)(threadIdx.x & 63);
+    const uint32_t ocw = (uint32_t)__shfl(cw, src ^ 1, 64);
+    const uint32_t oiw = (uint32_t)__shfl(iw, src ^ 1, 64);
+    *code_word = h == 0 ? (cw | ocw) : (iw | oiw);
+  }
+}
+
+// Workspace of the single pass: gamma's partial sum per fragment, a record per fragment (the
+// number of pieces it listed, then up to kBandSegCap piece indices), and the bracket [T_lo, T_hi]
+// the pass used (as fp32 bit patterns).
+struct BandWs {
+  double* part;
+  uint8_t* seg;
+  uint32_t* lim;
+  unsigned long long* slots;
+};
+
+// gamma's sum in fixed point: the pass adds each fragment's fp64 partial, scaled by 2^(50 - e)
+// where 2^e > the previous pack's total sum |w| (so the new total is about 2^50 units) and
+// rounded to an integer, to one of kBandSlots counters. Integer sums do not depend on the order
+// of the additions, so gamma is the same on every run; its rounding error (half a unit per
+// fragment) is below 2^-36 of the total. A fragment above 2^62 / frags units (the total could
+// overflow), or a previous sum of 0 or not finite, sets the overflow flag, and the fix-up kernel
+// then adds the fp64 partials in a fixed order instead.
+__device__ __forceinline__ double band_scale(float gamma_prev, double count) {
+  const double tot = (double)gamma_prev * count;
+  if (!(tot > 0.0) || !isfinite(tot)) return 0.0;
+  int e;
+  frexp(tot, &e);
+  return ldexp(1.0, 50 - e);
+}
+
+// One workgroup per fragment. SINGLE = false: the second read of the two-pass pack (gamma_p is
+// this pack's gamma; optional variance-correction counts and structured outliers). SINGLE =
+// true: the single pass of a re-pack (gamma_p is the previous pack's gamma).
+template <int M, int N, int FORM, bool SINGLE>
+__global__ __launch_bounds__(256) void pack_lean(const float* __restrict__ w, int64_t ld_w,
+                                                 int vec4, Layout L,
+                                                 const float* __restrict__ gamma_p,
+                                                 uint8_t* __restrict__ mask_plane,
+                                                 uint8_t* __restrict__ code_plane,
+                                                 uint32_t* __restrict__ flip_parts,
+                                                 uint32_t* __restrict__ vc_parts,
+                                                 const uint16_t* __restrict__ omask, BandWs band,
+                                                 double count) {
+  const int64_t frag = blockIdx.x;
+  const int tid = threadIdx.x;
+  const PieceAt p = piece_at<FORM>(L, frag, tid);
+  uint16_t* mp = L.has_mask ? piece_mask<FORM>(mask_plane, frag, tid, p) : nullptr;
+  const uint32_t old_keep = L.has_mask ? (uint32_t)*mp : 0u;
+  uint32_t obits = 0u;
+  if (!SINGLE && omask) {
+    const int qpos = (int)(p.k0 - (frag % L.quads) * kQuadK);
+    const int64_t oslot = (frag << 6) | ((p.lane_slot & 15) + 16 * (qpos >> 6));
+    obits = omask[oslot * 4 + ((qpos & 63) >> 4)];
+  }
+  uint32_t u[16];
+  load_piece(w, ld_w, vec4, p, u);
+  if (!SINGLE && omask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = (obits >> i) & 1u ? 0u : u[i];
+  }
+  uint32_t a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = u[i] & 0x7FFFFFFFu;
+  const float half = 0.5f * gamma_p[0];
+  const uint32_t hbits = __float_as_uint(half);
+  uint32_t t_lo = hbits, t_hi = hbits;
+  if constexpr (SINGLE) {
+    t_lo = __float_as_uint(half * (1.0f - kBandHalfWidth));
+    t_hi = __float_as_uint(half * (1.0f + kBandHalfWidth));
+  }
+  uint32_t v[16 / M];
+  const uint32_t keep = lean_keep<M, N>(a, p.cnt, v);
+  uint32_t cw;
+  lean_codes<FORM>(u, a, keep, t_hi, &cw, p.word);
+  reinterpret_cast<uint32_t*>(code_plane)[frag * 256 + tid] = cw;
+  if (L.has_mask) {
+    *mp = (uint16_t)keep;
+    const uint32_t sum = wave_sum_u32((uint32_t)__builtin_popcount((old_keep ^ keep) & 0xFFFFu));
+    if ((tid & 63) == 0) flip_parts[frag * 4 + (tid >> 6)] = sum;
+  }
+  if constexpr (!SINGLE) {
+    if (vc_parts) {
+      uint32_t nzd = 0;
+#pragma unroll
+      for (int i = 15; i >= 0; --i) nzd = shl_gt(nzd, a[i], hbits);
+      const uint32_t d = wave_sum_u32((uint32_t)__builtin_popcount(nzd));
+      const uint32_t sp = wave_sum_u32((uint32_t)__builtin_popcount(nzd & keep));
+      if ((tid & 63) == 0) {
+        vc_parts[(frag * 4 + (tid >> 6)) * 2] = d;
+        vc_parts[(frag * 4 + (tid >> 6)) * 2 + 1] = sp;
+      }
+    }
+  } else {
+    // A kept magnitude inside (T_lo, T_hi]: kept ones are at or above their group's n-th
+    // largest, so the test runs over [max(T_lo + 1, v_g), T_hi] per group, as one unsigned
+    // compare of 2a - 2 lo against 2 (T_hi - lo) (a value below lo wraps past it).
+    bool inband = false;
+#pragma unroll
+    for (int g = 0; g < 16 / M; ++g) {
+      uint32_t lo = t_lo + 1u;
+      if constexpr (N != M) lo = max(lo, v[g]);
+      if (lo <= t_hi) {
+        const uint32_t c = 0u - 2u * lo;
+        uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < M; ++i) mn = min(mn, (u[g * M + i] << 1) + c);
+        inband |= mn <= 2u * (t_hi - lo) && g * M < p.cnt;
+      }
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += (double)__uint_as_float(a[i]);
+    s = wave_sum_f64(s);
+    const uint64_t bal = __ballot(inband);
+    __shared__ uint32_t wcount[4];
+    __shared__ double wsum[4];
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) {
+      wcount[wave] = (uint32_t)__popcll(bal);
+      wsum[wave] = s;
+    }
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) base += i < wave ? wcount[i] : 0u;
+    const uint32_t pos =
+        base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    uint8_t* const rec = band.seg + frag * kBandRecBytes;
+    if (inband && pos < (uint32_t)kBandSegCap) rec[4 + pos] = (uint8_t)tid;
+    if (tid == 0) {
+      *reinterpret_cast<uint32_t*>(rec) = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+      const double part = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+      band.part[frag] = part;
+      const double sc = band_scale(gamma_p[0], count);
+      const double q = part * sc;
+      if (sc > 0.0 && q < ldexp(1.0, 62) / (double)gridDim.x)
+        atomicAdd(band.slots + 16 * (frag % kBandSlots), (unsigned long long)llrint(q));
+      else
+        atomicOr(band.lim + 2, 1u);
+      if (frag == 0) {
+        band.lim[0] = t_lo;
+        band.lim[1] = t_hi;
+        *reinterpret_cast<double*>(band.lim + 4) = sc;
+      }
+    }
+  }
+}
+
+// The fix-up kernel of the single pass (after it in the stream). Every workgroup first adds the
+// pass's per-fragment partial sums in one fixed order (thread t takes partials t, t + 1024, ...,
+// then the waves' sums in wave order), so each computes the same gamma, and workgroup 0 stores it.
+// With the new threshold H inside the pass's bracket, each listed piece re-reads its 16 weights
+// and ORs in the nonzero codes of its kept magnitudes in (T_lo, T_hi] that exceed H (they were
+// written as zero). A fragment that listed more pieces than its record holds, or every fragment
+// when H left the bracket, has its code words rewritten from the weights and the stored keep
+// bits. Workgroup b takes fragments b, b + G, ... (at most kFixFrags): their records and the
+// partial sums are loaded together, then the listed pieces are spread over the threads.
+constexpr int kFixFrags = 448;
+template <int M, int N, int FORM>
+__global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, int64_t ld_w,
+                                                 int vec4, Layout L, float* __restrict__ gamma_out,
+                                                 uint8_t* __restrict__ mask_plane,
+                                                 uint8_t* __restrict__ code_plane, BandWs band,
+                                                 int64_t frags, double count) {
+  constexpr int kWords = kBandRecBytes / 4;
+  __shared__ uint32_t rec[kFixFrags][kWords];
+  __shared__ uint32_t start[kFixFrags + 1];
+  __shared__ uint32_t whole[kFixFrags];  // fragments rewritten whole (their k), nwhole of them
+  __shared__ uint32_t wwhole[16];
+  __shared__ uint32_t nwhole;
+  __shared__ double wsum[16];
+  __shared__ uint32_t wtot[16];
+  __shared__ float gsh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t G = gridDim.x;
+  const int nf = (int)min<int64_t>(kFixFrags, (frags - blockIdx.x + G - 1) / G);
+  // records (16 bytes per load) and partial sums, loads in flight together
+  constexpr int kRecVec = kBandRecBytes / 16;
+#pragma unroll 4
+  for (int j = tid; j < nf * kRecVec; j += 1024) {
+    const int k = j / kRecVec, q = j % kRecVec;
+    *reinterpret_cast<uint4*>(&rec[k][4 * q]) = reinterpret_cast<const uint4*>(
+        band.seg + (blockIdx.x + (int64_t)k * G) * kBandRecBytes)[q];
+  }
+  // gamma: the fixed-point counters, or the fp64 partials if the pass flagged an overflow
+  const bool fixed = band.lim[2] == 0u;
+  if (fixed) {
+    if (wave == 0) {
+      const unsigned long long v = band.slots[16 * lane];
+      // the 64 counters add up below 2^63
+      unsigned long long sum = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) {
+        const double sc = *reinterpret_cast<const double*>(band.lim + 4);  // the pass's scale
+        gsh = count > 0.0 ? (float)(((double)sum / sc) / count) : 0.0f;
+      }
+    }
+  } else {
+    double acc = 0.0;
+    for (int64_t i0 = 0; i0 < frags; i0 += 16 * 1024) {
+      double v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int64_t i = i0 + tid + u * 1024;
+        v[u] = i < frags ? band.part[i] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += v[u];
+    }
+    acc = wave_sum_f64(acc);
+    if (lane == 0) wsum[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      double s = 0.0;
+      for (int k = 0; k < 16; ++k) s += wsum[k];
+      gsh = count > 0.0 ? (float)(s / count) : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (blockIdx.x == 0) gamma_out[0] = gsh;
+    // the last workgroup to have read the counters clears them for the next pass
+    const uint32_t old = __hip_atomic_fetch_add(band.lim + 3, 1u, __ATOMIC_RELEASE,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)G - 1) {
+      __atomic_thread_fence(__ATOMIC_ACQUIRE);
+      for (int k = 0; k < kBandSlots; ++k) band.slots[16 * k] = 0ull;
+      band.lim[2] = 0u;
+      band.lim[3] = 0u;
+    }
+  }
+  const uint32_t hbits = __float_as_uint(0.5f * gsh);
+  const uint32_t t_lo = band.lim[0], t_hi = band.lim[1];
+  const bool in_bracket = t_lo <= hbits && hbits <= t_hi;
+  // listed pieces per fragment (0 for a fragment rewritten whole), exclusive prefix sums
+  uint32_t c = 0;
+  bool w_all = false;
+  if (tid < nf) {
+    const uint32_t r = rec[tid][0];
+    w_all = !in_bracket || r > (uint32_t)kBandSegCap;
+    c = w_all ? 0u : r;
+  }
+  // the fragments rewritten whole, listed in order
+  {
+    const uint64_t bal = __ballot(w_all);
+    if (lane == 0) wwhole[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    uint32_t off = 0;
+    for (int k = 0; k < wave; ++k) off += wwhole[k];
+    if (w_all)
+      whole[off + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] = tid;
+    if (tid == 0) {
+      uint32_t s = 0;
+      for (int k = 0; k < 16; ++k) s += wwhole[k];
+      nwhole = s;
+    }
+  }
+  uint32_t x = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  uint32_t woff = 0;
+  for (int k = 0; k < wave; ++k) woff += wtot[k];
+  if (tid < nf) start[tid] = woff + x - c;
+  if (tid == nf - 1) start[nf] = woff + x;
+  __syncthreads();
+  uint32_t* const words = reinterpret_cast<uint32_t*>(code_plane);
+  const uint32_t total = start[nf];
+  for (uint32_t e = tid; e < total; e += 1024) {
+    int lo = 0, hi = nf - 1;  // the fragment k with start[k] <= e < start[k + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    const int k = lo;
+    const int64_t frag = blockIdx.x + (int64_t)k * G;
+    const int t = reinterpret_cast<const uint8_t*>(rec[k])[4 + (e - start[k])];
+    const PieceAt p = piece_at<FORM>(L, frag, t);
+    uint32_t u[16];
+    load_piece(w, ld_w, vec4, p, u);
+    const uint32_t keep =
+        L.has_mask ? (uint32_t)*piece_mask<FORM>(mask_plane, frag, t, p) : 0xFFFFu;
+    uint32_t orw = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t ai = u[i] & 0x7FFFFFFFu;
+      if (!((keep >> i) & 1u) || ai <= t_lo || ai > t_hi || ai <= hbits) continue;
+      const uint32_t neg = u[i] >> 31;
+      if constexpr (FORM == kFormPositional) {
+        orw |= (1u + neg) << (8 * (i & 3) + 2 * (i >> 2));
+      } else {
+        const int q = i >> 2;
+        const uint32_t k4 = (keep >> (4 * q)) & 0xFu;
+        const int hb = 31 - __builtin_clz(k4);
+        const int slot = 8 * (p.word & 1) + 2 * q + ((i & 3) == hb ? 1 : 0);
+        orw |= (1u << neg) << sp24_code_bit(slot);
+      }
+    }
+    if (orw) atomicOr(words + frag * 256 + (FORM == kFormSparse24 ? (t & ~1) : t), orw);
+  }
+  // fragments rewritten whole: four at a time, 256 threads each
+  const int sub = tid >> 8, st = tid & 255;
+  const int nw = (int)nwhole;
+  for (int j0 = 0; j0 < nw; j0 += 4) {
+    const int j = j0 + sub;
+    if (j >= nw) continue;  // uniform over each group of 256 threads
+    const int64_t frag = blockIdx.x + (int64_t)whole[j] * G;
+    const PieceAt p = piece_at<FORM>(L, frag, st);
+    uint32_t u[16], a[16];
+    load_piece(w, ld_w, vec4, p, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = u[i] & 0x7FFFFFFFu;
+    const uint32_t keep =
+        L.has_mask ? (uint32_t)*piece_mask<FORM>(mask_plane, frag, st, p) : 0xFFFFu;
+    uint32_t cw;
+    lean_codes<FORM>(u, a, keep, hbits, &cw, p.word);
+    words[frag * 256 + st] = cw;
   }
 }
 
@@ -707,40 +1285,92 @@ int absmean_blocks(int64_t n_out) {
   return (int)std::min<int64_t>(n_out, kMaxAbsmeanBlocks);
 }
 
-hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s) {
+// Lean kernels of a pattern and form: calls FN(M, N, FORM) for the template arguments, or
+// returns false when the pattern has none (the kept form, and patterns outside the lean set).
+template <typename Fn>
+bool with_lean(const Layout& L, Fn&& fn) {
+  if (L.form == kFormKept || !lean_pattern(L.n, L.m)) return false;
+  if (L.form == kFormSparse24) {
+    fn(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{},
+       std::integral_constant<int, kFormSparse24>{});
+  } else if (L.n == L.m) {
+    fn(std::integral_constant<int, 16>{}, std::integral_constant<int, 16>{},
+       std::integral_constant<int, kFormPositional>{});
+  } else if (L.m == 4) {
+    fn(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{},
+       std::integral_constant<int, kFormPositional>{});
+  } else if (L.m == 8 && L.n == 4) {
+    fn(std::integral_constant<int, 8>{}, std::integral_constant<int, 4>{},
+       std::integral_constant<int, kFormPositional>{});
+  } else if (L.m == 8) {
+    fn(std::integral_constant<int, 8>{}, std::integral_constant<int, 6>{},
+       std::integral_constant<int, kFormPositional>{});
+  } else {
+    fn(std::integral_constant<int, 16>{}, std::integral_constant<int, 8>{},
+       std::integral_constant<int, kFormPositional>{});
+  }
+  return true;
+}
+
+hipError_t launch_pack(const float* w, int64_t ld_w, sbn_packed* h, hipStream_t s) {
   const Layout& L = h->L;
   const int vec4 = ((uintptr_t)w % 16 == 0) && (ld_w % 4 == 0) && (L.K % 4 == 0);
-  if (L.n_out > 0) {
-    hipLaunchKernelGGL(absmean_partial, dim3(h->num_partials), dim3(kAbsmeanThreads), 0, s, w,
-                       L.n_out, L.K, ld_w, vec4, h->partials);
-  }
   const bool outl = h->outlier_k > 0 && L.n_out > 0;
-  if (outl) {
-    hipError_t e = launch_outlier_select(w, ld_w, h, s);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
-                     L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
-                     outl ? h->osum : nullptr,
-                     outl ? (L.n_out * (L.K >> 8) + 255) / 256 : (int64_t)0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || L.n_out == 0) return e;
-  const dim3 grid((unsigned)(L.row_blocks_pad * L.quads));
-  uint32_t* const vc = h->vc ? h->vc_parts : nullptr;
+  const int64_t frags = L.row_blocks_pad * L.quads;
+  const BandWs band{h->band_part, h->band_seg, h->band_lim, h->band_slots};
+  // A re-pack without outliers or variance correction reads the latent weights once.
+  const bool single = h->gamma_valid && h->band_part != nullptr && !outl && !h->vc &&
+                      L.n_out > 0 && L.form != kFormKept && lean_pattern(L.n, L.m);
+  h->single_pass = single;
+  if (single) {
+    with_lean(L, [&](auto MM, auto NN, auto FF) {
+      hipLaunchKernelGGL((pack_lean<decltype(MM)::value, decltype(NN)::value, decltype(FF)::value, true>), dim3((unsigned)frags), dim3(256), 0,
+                         s, w, ld_w, vec4, L, h->gamma, h->mask, h->codes, h->flip_parts,
+                         nullptr, nullptr, band, (double)L.n_out * (double)L.K);
+      // 64 workgroups (fewer for few fragments), more if one would take over kFixFrags
+      const int64_t fix_blocks = std::max<int64_t>(std::min<int64_t>(64, (frags + 3) / 4),
+                                                   (frags + kFixFrags - 1) / kFixFrags);
+      hipLaunchKernelGGL((pack_fix<decltype(MM)::value, decltype(NN)::value, decltype(FF)::value>),
+                         dim3((unsigned)fix_blocks), dim3(1024), 0, s, w, ld_w, vec4, L, h->gamma,
+                         h->mask, h->codes, band, frags, (double)L.n_out * (double)L.K);
+    });
+  } else {
+    if (L.n_out > 0) {
+      hipLaunchKernelGGL(absmean_partial, dim3(h->num_partials), dim3(kAbsmeanThreads), 0, s, w,
+                         L.n_out, L.K, ld_w, vec4, h->partials);
+    }
+    if (outl) {
+      hipError_t e = launch_outlier_select(w, ld_w, h, s);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
+                       L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
+                       outl ? h->osum : nullptr,
+                       outl ? (L.n_out * (L.K >> 8) + 255) / 256 : (int64_t)0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || L.n_out == 0) return e;
+    uint32_t* const vc = h->vc ? h->vc_parts : nullptr;
+    const uint16_t* const om = outl ? reinterpret_cast<const uint16_t*>(h->omask) : nullptr;
+    const bool lean = with_lean(L, [&](auto MM, auto NN, auto FF) {
+      hipLaunchKernelGGL((pack_lean<decltype(MM)::value, decltype(NN)::value, decltype(FF)::value, false>), dim3((unsigned)frags), dim3(256), 0,
+                         s, w, ld_w, vec4, L, h->gamma, h->mask, h->codes, h->flip_parts, vc, om,
+                         band, 0.0);
+    });
+    if (!lean) {
+      const dim3 grid((unsigned)frags);
 #define SBN_PACK(MM, FF)                                                                      \
   hipLaunchKernelGGL((pack_fragments<MM, FF>), grid, dim3(256), 0, s, w, ld_w, vec4, L, h->gamma, \
-                     h->mask, h->codes, h->flip_parts, vc,                                   \
-                     outl ? reinterpret_cast<const uint16_t*>(h->omask) : nullptr)
-  if (L.form == kFormSparse24) {
-    SBN_PACK(4, kFormSparse24);
-  } else if (L.m == 4) {
-    if (L.positional) SBN_PACK(4, kFormPositional); else SBN_PACK(4, kFormKept);
-  } else if (L.m == 8) {
-    if (L.positional) SBN_PACK(8, kFormPositional); else SBN_PACK(8, kFormKept);
-  } else {
-    if (L.positional) SBN_PACK(16, kFormPositional); else SBN_PACK(16, kFormKept);
-  }
+                     h->mask, h->codes, h->flip_parts, vc, om)
+      if (L.m == 4) {
+        if (L.positional) SBN_PACK(4, kFormPositional); else SBN_PACK(4, kFormKept);
+      } else if (L.m == 8) {
+        if (L.positional) SBN_PACK(8, kFormPositional); else SBN_PACK(8, kFormKept);
+      } else {
+        if (L.positional) SBN_PACK(16, kFormPositional); else SBN_PACK(16, kFormKept);
+      }
 #undef SBN_PACK
+    }
+  }
   if (h->compact) {
     const int64_t nfq = L.row_blocks_pad * L.quads;
     hipLaunchKernelGGL(build_compact, dim3((unsigned)((nfq + 3) / 4)), dim3(256), 0, s, L, h->mask,

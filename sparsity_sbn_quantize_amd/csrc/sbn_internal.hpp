@@ -45,6 +45,14 @@ struct sbn_packed {
   uint16_t* oval;       // outlier bf16 values, same layout
   unsigned long long* omask;  // outlier positions as one 64-bit word per brick slot
   double* osum;         // outlier |w| sums, one per selection workgroup of 256 groups
+  double* band_part;     // single-pass re-pack: gamma's partial sum per fragment
+  uint8_t* band_seg;     // per fragment: the count of listed pieces (kept magnitudes near the
+                         // old threshold), then the pieces (kBandRecBytes per fragment)
+  uint32_t* band_lim;    // the bracket [T_lo, T_hi] the pass used (fp32 bit patterns), the
+                         // fixed-point overflow flag, the fix-up kernel's arrival counter
+  unsigned long long* band_slots;  // gamma's fixed-point sum, kBandSlots counters 128 B apart
+  bool gamma_valid;      // gamma holds a previous pack's value (host-side state)
+  bool single_pass;      // the last pack read the latent weights once (host-side state)
   int device;
   bool async_alloc;     // base came from hipMallocAsync (released with hipFreeAsync)
   hipStream_t last_stream;
@@ -68,6 +76,12 @@ inline int64_t kx_row_groups(int64_t row_blocks) { return ((row_blocks + 15) / 1
 // s_sleep rounds a waiting split-K half spins before it gives up (its partner is already past its
 // main loop, so this is never reached in a correct run).
 constexpr int kSplitSpinLimit = 1 << 24;
+// Single-pass re-pack: bytes of a fragment's record (the listed-piece count, then the pieces)
+// and the pieces it can list for the fix-up kernel.
+constexpr int kBandRecBytes = 128;
+constexpr int kBandSegCap = kBandRecBytes - 4;
+// Counters of the single pass's fixed-point absmean sum (fragment f adds to counter f % 64).
+constexpr int kBandSlots = 64;
 
 // The device memory layout of a handle for an (n_out, K, n:m) weight: offsets of the planes and
 // words in one allocation. The regions below forward_bytes are all that the pack (without the
@@ -79,7 +93,7 @@ struct Plan {
   bool oplanes;
   size_t mask_bytes, code_bytes, cplane_bytes;
   size_t off_mask, off_codes, off_gamma, off_part, off_sync, off_flips, off_vc, off_gamma_vc,
-      off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum, off_kx;
+      off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum, off_kx, off_band;
   int kx_chunks;
   size_t forward_bytes, total_bytes;
 };
@@ -99,7 +113,7 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t 
 hipError_t launch_ln_quantize_act(const uint16_t* x, int64_t T, int64_t K, int64_t ld_x,
                                   float eps, int8_t* q, int64_t ld_q, float* absmax,
                                   hipStream_t s);
-hipError_t launch_pack(const float* w, int64_t ld_w, const sbn_packed* h, hipStream_t s);
+hipError_t launch_pack(const float* w, int64_t ld_w, sbn_packed* h, hipStream_t s);
 hipError_t launch_export(const sbn_packed* h, int8_t* codes, uint8_t* keep, float* gamma,
                          hipStream_t s);
 hipError_t launch_export_rpf(const sbn_packed* h, uint8_t* code_bytes, uint8_t* mask_bytes,

@@ -118,6 +118,11 @@ extern "C" sbn_status sbn_bitlinear_fwd_latent_static(
   h.oval = nullptr;
   h.omask = nullptr;
   h.osum = nullptr;
+  h.band_part = nullptr;  // a fresh handle: the two-pass pack
+  h.band_seg = nullptr;
+  h.band_lim = nullptr;
+  h.band_slots = nullptr;
+  h.gamma_valid = false;
   h.last_stream = s;
   // The planes' padding bricks must read as zero and the split-K words start at zero; the
   // workspace holds whatever the last call on this device left.
