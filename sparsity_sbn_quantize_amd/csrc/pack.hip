@@ -589,20 +589,26 @@ __device__ __forceinline__ void lean_codes(const uint32_t* u, const uint32_t* a,
       sgn = shl_neg(sgn, u[i]);
     }
     nz &= keep;
+    // 2-bit code of every position (bits 2i, 2i + 1: 0, 1 = +1, 2 = -1), then per group the
+    // codes at its lowest and highest kept positions (none in padding groups: slots stay zero)
+    const uint32_t cn = spread2(nz) + spread2(nz & sgn);
+    // built for half h = 0 (constant shifts); half 1's slots are 8 further on, which moves the
+    // code bits up by 4 and the index bits up by 16
     const int h = word & 1;
     uint32_t cw = 0, iw = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t k4 = (keep >> (4 * q)) & 0xFu;
-      const uint32_t lo = k4 ? (uint32_t)__builtin_ctz(k4) : 0u;
-      const uint32_t hi = k4 ? 31u - (uint32_t)__builtin_clz(k4) : 0u;
-      const uint32_t plo = 4 * q + lo, phi = 4 * q + hi;
-      const uint32_t clo = k4 ? ((nz >> plo) & 1u) << ((sgn >> plo) & 1u) : 0u;
-      const uint32_t chi = k4 ? ((nz >> phi) & 1u) << ((sgn >> phi) & 1u) : 0u;
-      const int slot = 8 * h + 2 * q;
-      cw |= (clo << sp24_code_bit(slot)) | (chi << sp24_code_bit(slot + 1));
-      iw |= (lo << (2 * slot)) | (hi << (2 * slot + 2));
+      // lowest and highest kept position (0 and 0 in padding groups, where k4 == 0)
+      const uint32_t lo = (uint32_t)__builtin_ctz(k4 | 0x10u) & 3u;
+      const uint32_t hi = 31u - (uint32_t)__builtin_clz(k4 | 1u);
+      const uint32_t clo = (cn >> (8 * q + 2 * lo)) & 3u;  // 0 when k4 == 0 (nz is 0 there)
+      const uint32_t chi = (cn >> (8 * q + 2 * hi)) & 3u;
+      cw |= (clo << sp24_code_bit(2 * q)) | (chi << sp24_code_bit(2 * q + 1));
+      iw |= (lo << (4 * q)) | (hi << (4 * q + 2));
     }
+    cw <<= 4 * h;
+    iw <<= 16 * h;
     const int src = (int)(threadIdx.x & 63);
     const uint32_t ocw = (uint32_t)__shfl(cw, src ^ 1, 64);
     const uint32_t oiw = (uint32_t)__shfl(iw, src ^ 1, 64);
@@ -706,13 +712,11 @@ __global__ __launch_bounds__(256) void pack_lean(const float* __restrict__ w, in
     for (int g = 0; g < 16 / M; ++g) {
       uint32_t lo = t_lo + 1u;
       if constexpr (N != M) lo = max(lo, v[g]);
-      if (lo <= t_hi) {
-        const uint32_t c = 0u - 2u * lo;
-        uint32_t mn = 0xFFFFFFFFu;
+      const uint32_t c = 0u - 2u * lo;
+      uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < M; ++i) mn = min(mn, (u[g * M + i] << 1) + c);
-        inband |= mn <= 2u * (t_hi - lo) && g * M < p.cnt;
-      }
+      for (int i = 0; i < M; ++i) mn = min(mn, (u[g * M + i] << 1) + c);
+      inband |= lo <= t_hi && mn <= 2u * (t_hi - lo) && g * M < p.cnt;
     }
     double s = 0.0;
 #pragma unroll
