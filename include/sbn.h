@@ -112,7 +112,9 @@ sbn_status sbn_layernorm_quantize_act(const uint16_t* x_bf16, int64_t T, int64_t
  *   it once: the previous gamma brackets the new threshold (gamma / 2 within 2^-7 of the old
  *   one), the few 16-weight pieces with a kept magnitude inside the bracket are finished after
  *   the new gamma is known, and if the threshold left the bracket the codes are rewritten from a
- *   second read. The result is the same in every case; sbn_packed_desc.single_pass says which
+ *   second read. The planes are the same in every case; gamma is summed there in fixed point
+ *   (2^50 units for the previous total, error below 2^-36 of the sum, so it rounds to the same
+ *   fp32 value except that close to a rounding midpoint). sbn_packed_desc.single_pass says which
  *   path the last pack took.
  * Requires m_group in {4, 8, 16}, 1 <= n_keep <= m_group, K % m_group == 0,
  * m_group <= K <= SBN_MAX_K, 0 <= n_out < 2^31, ld_w >= K.
