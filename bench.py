@@ -235,6 +235,28 @@ def measure_ceilings(gpu, small_bytes):
                     "size, INT8 MFMA loop, empty kernel (per launch in a graph)"}
 
 
+def read_launch_ms(gpu, nbytes, launches):
+    """Time of one plain read launch of `nbytes` (the ceiling kernel over a 1 GiB buffer, rotated so
+    that it comes from HBM): the floor of any single launch that moves those bytes."""
+    import ctypes
+    torch, b = gpu.torch, gpu.b
+    lib = b.lib()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    big = 1 << 30
+    buf = torch.zeros(big // 4, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    size = (nbytes + 4095) // 4096 * 4096
+    slots = big // size
+
+    def read(i):
+        b.check(lib.sbn_ceiling_stream_read(ctypes.c_void_p(base + (i % slots) * size), size,
+                                            0xFFFFFFFF, b._ptr(sink), b._stream(None)))
+
+    ms = gpu.time_launches(read, launches)
+    del buf
+    return ms
+
+
 def cpu_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -656,9 +678,11 @@ def run_block(gpu, args, pattern, T, steps):
                 gbytes = sum(rpf_bytes(layers[li].n_out, layers[li].k, n, m) + 4 * T *
                              layers[li].n_out + 4 for li in grp) + T * layers[grp[0]].k + 4 * T
             g_ms = gpu.time_launches(fn, nl)
+            r_ms = read_launch_ms(gpu, gbytes, nl)
             groups.append({"layers": "/".join(layers[li].name for li in grp), "us": g_ms * 1e3,
                            "bytes": gbytes, "GBps": gbytes / (g_ms * 1e-3) / 1e9,
-                           "frac_hbm": gbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+                           "frac_hbm": gbytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "read_launch_us": r_ms * 1e3, "of_read_launch": r_ms / g_ms})
     ops = sum(2.0 * T * l.k * l.n_out for l in layers)
     fb = sum(forward_bytes(T, l.k, l.n_out, n, m) for l in layers)
     qb = sum(quantize_bytes(T, layers[[l.act_input for l in layers].index(ai)].k) for ai in acts)
@@ -692,8 +716,13 @@ def run_train(gpu, args, layer_index, pattern, steps):
     del x_bits, w
     # The re-pack reads the latent weights from HBM: the timed packs rotate over distinct copies of
     # them (>= 1 GiB in all, beyond the 256 MB last-level cache), each re-packed into one handle.
+    # Each copy carries its own small update (N(0, 1e-4), half a percent of the weights' scale),
+    # as consecutive training steps would: masks flip, gamma moves a little.
     RL = max(1, -(-args.rotate_bytes // (4 * N * K)))
-    wds = [wd] + [wd.clone() for _ in range(RL - 1)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + layer_index)
+    wds = [wd] + [wd + 1e-4 * torch.randn(wd.shape, device="cuda", generator=gen)
+                  for _ in range(RL - 1)]
     pw = gpu.b.PackedWeight(wd, n, m)
     q = torch.empty((T, K), dtype=torch.int8, device="cuda")
     a = torch.empty((T,), dtype=torch.float32, device="cuda")
@@ -728,6 +757,8 @@ def run_train(gpu, args, layer_index, pattern, steps):
     if (n, m) == (2, 4):
         # 2:4 runs on the structured-sparse MFMA; time the dense-MFMA path on the same weights
         # (positional codes) beside it, and check that both give the same output.
+        pw.pack(wd)
+        gpu.b.bitlinear(q, a, pw, out="f32", y=y)
         y_sp = y.clone()
         os.environ["SBN_NO_SMFMAC"] = "1"
         try:
@@ -752,13 +783,13 @@ def run_train(gpu, args, layer_index, pattern, steps):
     gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)
     torch.cuda.synchronize()
     dx_eager = dx.clone()
-    bw = {}
-    for name, fn in (("bwd", lambda i: gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)),
-                     ("pack_bwd", lambda i: (pw.pack(wds[i % RL]),
-                                              gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)))):
-        bw[name] = gpu.time_launches(fn, max(steps, KERNEL_LAUNCHES))
+    bw = {"bwd": gpu.time_launches(lambda i: gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx),
+                                   max(steps, KERNEL_LAUNCHES))}
     torch.cuda.synchronize()
     assert torch.equal(dx, dx_eager), "data-gradient graph replay differs from the eager call"
+    bw["pack_bwd"] = gpu.time_launches(lambda i: (pw.pack(wds[i % RL]),
+                                                  gpu.b.bitlinear_bwd_dx(dy, pw, dx=dx)),
+                                       max(steps, KERNEL_LAUNCHES))
     out["bwd_dx_us"] = bw["bwd"] * 1e3
     out["bwd_dx_TFLOPS"] = ops / (bw["bwd"] * 1e-3) / 1e12
     out["bwd_dx_frac_bf16"] = out["bwd_dx_TFLOPS"] / BF16_PEAK_TFLOPS
