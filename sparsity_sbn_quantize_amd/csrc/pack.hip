@@ -705,19 +705,22 @@ __global__ __launch_bounds__(256) void pack_lean(const float* __restrict__ w, in
     }
   } else {
     // A kept magnitude inside (T_lo, T_hi]: kept ones are at or above their group's n-th
-    // largest, so the test runs over [max(T_lo + 1, v_g), T_hi] per group, as one unsigned
-    // compare of 2a - 2 lo against 2 (T_hi - lo) (a value below lo wraps past it).
-    bool inband = false;
+    // largest, so the test runs over [max(T_lo + 1, v), T_hi], as one unsigned compare of
+    // 2a - 2 lo against 2 (T_hi - lo) (a value below lo wraps past it).
+    // (One range for the thread's 16, from the smallest group threshold: a superset of the kept
+    // ones. Positions past the row's end hold 0 and wrap, so they never count.)
+    uint32_t lo = t_lo + 1u;
+    if constexpr (N != M) {
+      uint32_t vmin = v[0];
 #pragma unroll
-    for (int g = 0; g < 16 / M; ++g) {
-      uint32_t lo = t_lo + 1u;
-      if constexpr (N != M) lo = max(lo, v[g]);
-      const uint32_t c = 0u - 2u * lo;
-      uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < M; ++i) mn = min(mn, (u[g * M + i] << 1) + c);
-      inband |= lo <= t_hi && mn <= 2u * (t_hi - lo) && g * M < p.cnt;
+      for (int g = 1; g < 16 / M; ++g) vmin = min(vmin, v[g]);
+      lo = max(lo, vmin);
     }
+    const uint32_t c = 0u - 2u * lo;
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mn = min(mn, (u[i] << 1) + c);
+    const bool inband = lo <= t_hi && mn <= 2u * (t_hi - lo);
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s += (double)__uint_as_float(a[i]);
