@@ -35,14 +35,11 @@ KERNEL_LAUNCHES = 200     # launches per graph when a kernel is timed on its own
 SLEEP_CYCLES = 2_000_000  # GPU busy wait before each timed replay (covers host enqueue latency)
 METRIC = "N:M ternary BitLinear dense-equiv TOPS (prefill) + HBM GB/s (decode GEMV)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# The sources of the kernels whose HBM traffic is recorded (the decode GEMVs and the prefill GEMM)
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
                   "sparsity_sbn_quantize_amd/csrc/sbn_common.hpp",
-                  "sparsity_sbn_quantize_amd/csrc/backward.hip",
-                  "sparsity_sbn_quantize_amd/csrc/pack.hip",
-                  "sparsity_sbn_quantize_amd/csrc/quantize_act.hip",
                   "sparsity_sbn_quantize_amd/csrc/gemv.hpp",
-                  "sparsity_sbn_quantize_amd/csrc/gemv_i8.hip",
-                  "sparsity_sbn_quantize_amd/csrc/outliers.hip"]
+                  "sparsity_sbn_quantize_amd/csrc/gemv_i8.hip"]
 
 
 def kernel_source_hash() -> str:
