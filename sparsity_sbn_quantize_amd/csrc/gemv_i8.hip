@@ -70,6 +70,10 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
   const int t = lane & 15, g = lane >> 4;
   const bool tok_ok = t < T;
+  // row blocks of this workgroup inside the stored (padded) plane: with RB = 3 the last
+  // workgroup can reach past it, and its missing row blocks read zero
+  const int64_t rb_pad = ((n_out + 15) / 16 + kPadRowBlocks - 1) / kPadRowBlocks * kPadRowBlocks;
+  const int rb_in = (int)min<int64_t>(RB, rb_pad - rb0);
   // The RB row blocks' quads are consecutive in the plane; stored row blocks are padded to a
   // multiple of 16, so a last block past n_out exists (zero bricks; its rows are not stored).
   // Compact plane: a quad takes cq = 512 + 8 csb bytes (the lanes' nonzero masks, then their sign
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
   const int cq = CMP ? (int)compact_quad_bytes(csb) : 1024;
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(code_plane + rb0 * nq * cq), (short)0,
-      RB * nq * cq + (CMP ? kCompactSlack : 0), kBufDword3);
+      rb_in * nq * cq + (CMP ? kCompactSlack : 0), kBufDword3);
   uint32_t codes[RB][Q][4];
   uint32_t cmask[CMP ? Q : 1][2];
 #pragma unroll
@@ -779,12 +783,19 @@ hipError_t launch_gemv_int8(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
       return launch_i8_deep<kFormSparse24, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
     return launch_i8_deep<kFormPositional, 1>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
   }
-  // More than four tokens, one quad per wave and many row blocks: two row blocks per workgroup.
-  // Same-process A/B against the kernel above (us, T = 8 / 16): 6912 x 2560 3.96 / 4.98 ->
-  // 3.68 / 4.22, 11008 x 4096 7.09 / 8.88 -> 5.83 / 7.18; slower with two or three quads per wave
-  // (2560 x 6912 4.81 / 6.10 -> 5.69 / 6.93) or few row blocks (2560 x 2560 3.12 / 3.52 ->
-  // 3.25 / 3.68).
+  // More than four tokens, one quad per wave and many row blocks: two row blocks per workgroup,
+  // three from 640 row blocks on (about 220-230 workgroups either way). Same-process A/B against
+  // the kernel above (us, T = 8 / 16): 6912 x 2560 3.96 / 4.98 -> 3.68 / 4.22, 11008 x 4096
+  // 7.09 / 8.88 -> 5.83 / 7.18; slower with two or three quads per wave (2560 x 6912 4.81 / 6.10
+  // -> 5.69 / 6.93) or few row blocks (2560 x 2560 3.12 / 3.52 -> 3.25 / 3.68). Three row blocks
+  // against two: 11008 x 4096 6.05 / 7.70 -> 5.39 / 6.20, 6912 x 2560 3.73 / 4.26 -> 3.97 / 4.48
+  // (four: 5.75 / 6.40 and 4.27 / 4.77).
   if (deep_form && T > kFusedMaxT && L.quads <= kGemvMaxWaves && L.row_blocks >= 320) {
+    if (L.row_blocks >= 640) {
+      if (L.form == kFormSparse24)
+        return launch_i8_deep<kFormSparse24, 3>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+      return launch_i8_deep<kFormPositional, 3>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
+    }
     if (L.form == kFormSparse24)
       return launch_i8_deep<kFormSparse24, 2>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);
     return launch_i8_deep<kFormPositional, 2>(h, xq, ld_q, absmax, T, y, ld_y, out_kind, s);

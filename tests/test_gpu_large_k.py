@@ -139,3 +139,21 @@ def test_large_k_split_over_k(n, m, T, K, N):
         assert np.array_equal(acc.cpu().numpy(), acc_ref)
         gu.assert_y_close(y.cpu().numpy(), oracle.dequantize(acc_ref, g, a_ref))
     pw.free()
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16)])
+@pytest.mark.parametrize("T", [5, 16])
+@pytest.mark.parametrize("N,K", [(10480, 1024), (10256, 2560)])
+def test_many_row_blocks_three_per_workgroup(n, m, T, N, K):
+    """Five to sixteen tokens, at most 16 quads and 640 or more row blocks: three row blocks per
+    workgroup. 10480 rows are 655 row blocks (656 stored), so the last workgroup's third row block
+    lies past the plane and must read zero; 10256 rows end inside a row block."""
+    x, w = _case(N + K + 3 * T + n, T, N, K)
+    r = _run(x, w, n, m)
+    q_ref, a_ref = oracle.quantize_act(x)
+    assert np.array_equal(r["q"], q_ref) and np.array_equal(r["a"], a_ref)
+    ref = oracle.pack_nm_ternary(w, n, m)
+    assert np.array_equal(r["codes"], ref["codes"])
+    acc_ref = oracle.int_matmul(q_ref, ref["codes"])
+    assert np.array_equal(r["acc"], acc_ref)
+    gu.assert_y_close(r["y"], oracle.dequantize(acc_ref, r["gamma"], a_ref))
