@@ -634,14 +634,15 @@ struct GemvGroup {
 };
 
 // Fills a group from packed weights that share K, the pattern and the code form (not the compact
-// plane); returns the launch's workgroup count.
+// plane), each workgroup taking rb_per_wg row blocks of one member; returns the launch's workgroup
+// count.
 inline int make_group(const sbn_packed* const* hs, int count, void* const* ys,
-                      const int64_t* ld_ys, GemvGroup& G) {
+                      const int64_t* ld_ys, GemvGroup& G, int rb_per_wg = 1) {
   int end = 0;
   for (int i = 0; i < kMaxGroup; ++i) {
     GemvMember& m = G.m[i];
     if (i < count) {
-      end += (int)hs[i]->L.row_blocks;
+      end += (int)((hs[i]->L.row_blocks + rb_per_wg - 1) / rb_per_wg);
       m = GemvMember{hs[i]->codes, hs[i]->mask, hs[i]->gamma_out(), ys[i], ld_ys[i],
                      hs[i]->L.n_out, end};
     } else {

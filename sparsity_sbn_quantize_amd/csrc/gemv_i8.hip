@@ -55,11 +55,14 @@ constexpr int kDeepMaxQ = 8;
 
 // RB row blocks per workgroup share the activation loads (each wave's B operands serve RB sets of
 // bricks): with 16 tokens the activation pieces outweigh the bricks, and RB = 2 halves them.
+// The workgroup computes row blocks rb0 .. rb0 + RB - 1 of the weight whose code plane, scale and
+// output are passed.
 template <int FORM, int Q, int RB>
-__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
+__device__ __forceinline__ void deep_body(
     const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
     int ld_q, int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
-    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int cn, int csb) {
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int cn, int csb,
+    const int64_t rb0) {
   constexpr bool CMP = compact_form(FORM);
   static_assert(FORM == kFormPositional || FORM == kFormSparse24 || (CMP && RB == 1),
                 "positional, 2:4 or (one row block) compact codes");
@@ -67,7 +70,6 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
   __shared__ uint32_t clut[CMP ? 256 : 1];  // compact nibble table
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int64_t rb0 = (int64_t)blockIdx.x * RB;
   const int t = lane & 15, g = lane >> 4;
   const bool tok_ok = t < T;
   // row blocks of this workgroup inside the stored (padded) plane: with RB = 3 the last
@@ -198,6 +200,28 @@ __global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
       }
     }
   }
+}
+
+template <int FORM, int Q, int RB>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep(
+    const uint8_t* __restrict__ code_plane, const int8_t* __restrict__ xq, int nq, int K,
+    int ld_q, int T, int W, const float* __restrict__ absmax, const float* __restrict__ gamma_p,
+    void* __restrict__ y, int64_t ld_y, int64_t n_out, int out_kind, int cn, int csb) {
+  deep_body<FORM, Q, RB>(code_plane, xq, nq, K, ld_q, T, W, absmax, gamma_p, y, ld_y, n_out,
+                         out_kind, cn, csb, (int64_t)blockIdx.x * RB);
+}
+
+// The grouped launch of the kernel above (members as in bitlinear_gemv_i8_group, their row blocks
+// taken RB at a time: member i's workgroups are [rb_end[i-1], rb_end[i]), ceil(row blocks / RB)
+// of them).
+template <int FORM, int Q, int RB>
+__global__ __launch_bounds__(kGemvMaxWaves * 64) void bitlinear_gemv_i8_deep_group(
+    const int8_t* __restrict__ xq, int nq, int K, int ld_q, int T, int W,
+    const float* __restrict__ absmax, GemvGroup G, int out_kind) {
+  int64_t wg;
+  const int i = group_member(G, (int)blockIdx.x, wg);
+  deep_body<FORM, Q, RB>(G.m[i].codes, xq, nq, K, ld_q, T, W, absmax, G.m[i].gamma, G.m[i].y,
+                         G.m[i].ld_y, G.m[i].n_out, out_kind, 0, 0, wg * RB);
 }
 
 // One to four tokens past one batch (49 to 128 quads): the workgroup first copies the activation
@@ -723,9 +747,35 @@ hipError_t launch_gemv_int8_group(const sbn_packed* const* hs, int count, const 
                                   int64_t ld_q, const float* absmax, int64_t T, void* const* ys,
                                   const int64_t* ld_ys, int out_kind, hipStream_t s) {
   GemvGroup G;
-  const int blocks = make_group(hs, count, ys, ld_ys, G);
   const Layout& L = hs[0]->L;
   const bool xvec = ((uintptr_t)xq % 16 == 0) && (ld_q % 16 == 0) && (L.K % 16 == 0);
+  // More than four tokens, at most 16 quads, many row blocks in all: the kernel that shares each
+  // wave's activation pieces among two (three from 640 row blocks on) row blocks of a member, as
+  // for one weight.
+  int64_t rbs = 0;
+  bool compact = false;
+  for (int i = 0; i < count; ++i) {
+    rbs += hs[i]->L.row_blocks;
+    compact = compact || hs[i]->compact;
+  }
+  if (xvec && T > kFusedMaxT && !compact && L.quads <= kGemvMaxWaves && rbs >= 320 &&
+      (L.form == kFormPositional || L.form == kFormSparse24)) {
+    const int W = (int)std::min<int64_t>(kGemvMaxWaves, L.quads);
+#define SBN_DG(FF, RB)                                                                          \
+  do {                                                                                          \
+    const int blocks = make_group(hs, count, ys, ld_ys, G, RB);                                \
+    hipLaunchKernelGGL((bitlinear_gemv_i8_deep_group<FF, 1, RB>), dim3((unsigned)blocks),          \
+                       dim3(64 * W), 0, s, xq, (int)L.quads, (int)L.K, (int)ld_q, (int)T, W,     \
+                       absmax, G, out_kind);                                                    \
+    return hipGetLastError();                                                                   \
+  } while (0)
+    if (L.form == kFormSparse24) {
+      if (rbs >= 640) SBN_DG(kFormSparse24, 3); else SBN_DG(kFormSparse24, 2);
+    }
+    if (rbs >= 640) SBN_DG(kFormPositional, 3); else SBN_DG(kFormPositional, 2);
+#undef SBN_DG
+  }
+  const int blocks = make_group(hs, count, ys, ld_ys, G);
   if (xvec) return launch_i8_group_form<true>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
   return launch_i8_group_form<false>(G, blocks, L, xq, ld_q, absmax, T, out_kind, s);
 }

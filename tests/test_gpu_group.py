@@ -180,3 +180,23 @@ def test_group_block_shapes(n, m, T):
             gu.assert_y_close(y.cpu().numpy()[:, rows], oracle.dequantize(acc_ref, g, ah))
         for p_ in pws:
             p_.free()
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16)])
+@pytest.mark.parametrize("T", [5, 16])
+@pytest.mark.parametrize("shapes", [[2560, 2570, 1000], [5000, 4000, 1336]])
+def test_group_int8_shared_activation_pieces(n, m, T, shapes):
+    """Five to sixteen tokens with 320 or more row blocks in all: each workgroup takes two (from
+    640 on, three) row blocks of one member and shares its activation pieces among them. Ragged
+    members (their last workgroup reaches past the stored plane), outputs equal to the single
+    forwards and to the oracle."""
+    K = 1024
+    ws = [_w(31 * i + n + m + T, N, K) for i, N in enumerate(shapes)]
+    pws = [binding.PackedWeight(gu.to_dev_f32(w), n, m) for w in ws]
+    xd = gu.to_dev_bf16(_x(5 * T + m, T, K))
+    q, a = binding.quantize_act(xd)
+    for kind in ("f32", "i32"):
+        ys = binding.bitlinear_group(q, a, pws, out=kind)
+        _check_members(pws, ys, q, a, kind)
+    for p in pws:
+        p.free()
