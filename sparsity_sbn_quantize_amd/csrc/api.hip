@@ -320,6 +320,16 @@ sbn_status sbn_bitlinear_fwd_group_bf16(const sbn_packed* const* ws, int count,
     for (int i = 0; i < count; ++i) const_cast<sbn_packed*>(ws[i])->last_stream = s;
     e = sbn::launch_gemv_group_bf16(ws, count, x_bf16, ld_x, T, x_q, ld_q, x_absmax, ys, ld_ys,
                                     (int)out_kind, ln_eps, s);
+  } else if (single && T <= 16) {
+    // the quantizer, then the grouped int8 GEMV
+    for (int i = 0; i < count; ++i) const_cast<sbn_packed*>(ws[i])->last_stream = s;
+    e = ln_eps > 0.0f ? sbn::launch_ln_quantize_act(x_bf16, T, ws[0]->L.K, ld_x, ln_eps, x_q, ld_q,
+                                                    x_absmax, s)
+                      : sbn::launch_quantize_act(x_bf16, T, ws[0]->L.K, ld_x, x_q, ld_q, x_absmax,
+                                                 s);
+    if (e == hipSuccess)
+      e = sbn::launch_gemv_int8_group(ws, count, x_q, ld_q, x_absmax, T, ys, ld_ys, (int)out_kind,
+                                      s);
   } else {
     // the first member quantizes (one kernel where it can), the others read its x_q and a'
     const_cast<sbn_packed*>(ws[0])->last_stream = s;

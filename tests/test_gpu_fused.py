@@ -150,3 +150,24 @@ def test_fused_validation():
     assert f(pw.handle, P(xd), 256, 2, P(q), 256, P(a), P(y), 32, 7, s) == -1  # out_kind
     assert f(pw.handle, P(xd), 256, 0, P(q), 256, P(a), P(y), 32, 0, s) == 0   # T == 0
     pw.free()
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16)])
+@pytest.mark.parametrize("T", [5, 9, 16])
+@pytest.mark.parametrize("N,K", [(10480, 1024), (5130, 4096), (6912, 2560)])
+def test_fused_wide_5_to_16_tokens(n, m, T, N, K):
+    """Five to sixteen tokens on layers of 320 or more row blocks and at most 16 quads: the
+    quantize kernel, then the row-block-sharing GEMV (two row blocks per workgroup, three from
+    640 on; 10480 rows end past the stored plane's last workgroup, 5130 inside a row block).
+    x_q and a' equal sbn_quantize_act's, outputs the two-call path's."""
+    x, w = _case(2000 + 3 * T + N + K + n, T, K, N)
+    _check(_run(x, w, n, m), x, K)
+
+
+def test_fused_wide_padded_and_unaligned():
+    """The same shapes with x_q rows wider than K (nothing written past K) and x leading
+    dimensions wider than K."""
+    x, w = _case(51, 16, 2560, 5136)
+    _check(_run(x, w, 6, 8, ld_q=2576), x, 2560)
+    _check(_run(x, w, 6, 8, ld_x=2568), x, 2560)
+    _check(_run(x, w, 6, 8, ld_x=2570), x, 2560)

@@ -200,3 +200,26 @@ def test_group_int8_shared_activation_pieces(n, m, T, shapes):
         _check_members(pws, ys, q, a, kind)
     for p in pws:
         p.free()
+
+
+@pytest.mark.parametrize("n,m", [(6, 8), (2, 4), (8, 16)])
+@pytest.mark.parametrize("T", [5, 16])
+@pytest.mark.parametrize("shapes", [[2560, 2570, 1000], [5000, 4000, 1336]])
+def test_group_bf16_wide_5_to_16_tokens(n, m, T, shapes):
+    """The grouped bf16 entry for five to sixteen tokens on wide members: the quantize kernel,
+    then the row-block-sharing grouped GEMV. x_q and a' equal sbn_quantize_act's, every member
+    equals its single forward and the oracle."""
+    import torch
+    K = 1024
+    ws = [_w(17 * i + n + m + T, N, K) for i, N in enumerate(shapes)]
+    pws = [binding.PackedWeight(gu.to_dev_f32(w), n, m) for w in ws]
+    xd = gu.to_dev_bf16(_x(3 * T + n, T, K))
+    q2, a2 = binding.quantize_act(xd)
+    for kind in ("f32", "i32"):
+        ys, q, a = binding.bitlinear_group_bf16(xd, pws, out=kind)
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), q2.cpu().numpy())
+        assert np.array_equal(a.cpu().numpy(), a2.cpu().numpy())
+        _check_members(pws, ys, q2, a2, kind)
+    for p in pws:
+        p.free()
