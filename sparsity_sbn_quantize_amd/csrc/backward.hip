@@ -102,17 +102,19 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
   const int ylane = (lane & 15) * (int)row_bytes + (lane >> 4) * 16;
   auto load_dy = [&](int rq, int slot) {
     uint8_t* dst = smem + slot * kBwTileBytes + wave * (kBwXLoads * 1024);
+    // One buffer resource per step (based at the step's first row of the tile's first token);
+    // the piece's place in the tile is a lane offset, below T ld_dy 2 < kMaxBufExtent.
+    const int64_t left = y_extent - (int64_t)rq * 256;
+    const int nrec = left <= 0 ? 0 : (int)left;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(y0 + (int64_t)rq * 256), (short)0, nrec, kBufDword3);
+    const int rowb = (int)row_bytes;
 #pragma unroll
     for (int i = 0; i < kBwXLoads; ++i) {
       const int ii = wave * kBwXLoads + i, tg = ii >> 2, c0 = (ii & 3) * 4;
       const int64_t r_first = (int64_t)rq * kBwStepRows + 8 * (c0 + (lane >> 4));
       if constexpr (XVEC) {
-        const int64_t off0 = (int64_t)(tg * 16) * row_bytes + (int64_t)rq * 256 + c0 * 16;
-        const int64_t left = y_extent - off0;
-        const int nrec = left <= 0 ? 0 : (int)left;
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(y0 + off0), (short)0, nrec, kBufDword3);
-        const int voff = r_first < n_out ? ylane : kOutOfRange;
+        const int voff = r_first < n_out ? ylane + tg * 16 * rowb + c0 * 16 : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(dst + i * 1024), 16, voff, 0, 0,
                                                  0);
       } else {
