@@ -1165,10 +1165,11 @@ __global__ __launch_bounds__(256) void export_compact(Layout L, const uint8_t* c
 // + lane. Lane l = c + 16 g holds column 16 cb + c of rows 128 rq + 32 g + (0..31); its word h
 // (0, 1) holds row 32 g + 16 h + 8 s + 2 p + e (s, e in {0, 1}, p in 0..3) at bits
 // 2 p + 8 s + 16 e, as 2-bit codes 0 = 0, 1 = +1, 2 = -1. One workgroup per 128 rows x 256
-// columns: its 512 bricks are decoded into LDS as 2-bit codes (16 positions per word), every
-// thread assembles 8 transposed words of 8 columns into an LDS copy of the workgroup's 16 output
-// blocks, and the blocks (512 contiguous bytes each) are written with 16-byte stores. Rows past
-// n_out are zero.
+// columns: its 512 bricks go to LDS as 2-bit codes in the positional word layout (16 positions
+// per word; positional bricks are copied as they are, 2:4 slots are moved to their positions,
+// kept-form bricks are decoded), every thread assembles 8 transposed words of 8 columns into an
+// LDS copy of the workgroup's 16 output blocks, and the blocks (512 contiguous bytes each) are
+// written with 16-byte stores. Rows past n_out are zero.
 //
 // LDS layouts, chosen so that no access has bank conflicts on gfx950's 64 four-byte banks:
 //   code words: row r's 16 words start at 16 r + 16 (r >> 4), word c at c ^ 4 ((r >> 6) & 3).
@@ -1201,11 +1202,37 @@ __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* 
     const int64_t row = rq * 128 + rl;
     uint32_t w4[4] = {0u, 0u, 0u, 0u};
     if (row < L.n_out) {
-      uint32_t mask[2], dec[16];
-      decode_brick(L, mask_plane, code_plane, row, q * kFragBricks + b, mask, dec);
-      for (int j = 0; j < kBrickK; ++j) {
-        const uint32_t v = (dec[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        w4[j >> 4] |= (v == 0xFFu ? 2u : v) << (2 * (j & 15));
+      const int64_t brick = q * kFragBricks + b;
+      if (L.form == kFormSparse24) {
+        // the brick's 64 positions are lane groups 2 (b & 1) + hh of block b >> 1 of the quad:
+        // slot j of a lane group's code word (bits 8 (j & 3) + 2 (j >> 2)) goes to position
+        // 4 (j >> 1) + index_j of its 32, i.e. word j >> 3, bits 8 index_j + 2 ((j >> 1) & 3)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t s2 =
+              (((row >> 4) * L.quads + q) << 6) | ((row & 15) + 16 * (2 * (b & 1) + hh));
+          const uint2 ci = *reinterpret_cast<const uint2*>(code_plane + s2 * 16 + 8 * (b >> 1));
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t c = (ci.x >> sp24_code_bit(j)) & 3u, p = (ci.y >> (2 * j)) & 3u;
+            w4[2 * hh + (j >> 3)] |= c << (8 * p + 2 * ((j >> 1) & 3));
+          }
+        }
+      } else if (L.positional) {
+        // already 2-bit codes in the layout below
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(code_plane + brick_slot(L, row, brick) * 16);
+        w4[0] = v.x;
+        w4[1] = v.y;
+        w4[2] = v.z;
+        w4[3] = v.w;
+      } else {
+        uint32_t mask[2], dec[16];
+        decode_brick(L, mask_plane, code_plane, row, brick, mask, dec);
+        for (int j = 0; j < kBrickK; ++j) {
+          const uint32_t v = (dec[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+          w4[j >> 4] |= (v == 0xFFu ? 2u : v) << pos_bit(j & 15);
+        }
       }
     }
     *reinterpret_cast<uint4*>(&cw[tc_cw_at(rl, 4 * b)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
@@ -1218,12 +1245,13 @@ __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* 
   for (int rr = 0; rr < 16; ++rr) rw[rr] = cw[tc_cw_at(32 * g + 16 * h + rr, cbl)];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) {
-    const int c = 8 * half + cc;
+    // column c = 8 half + cc of the word's 16 sits at bits 8 (c & 3) + 2 (c >> 2)
+    const int sh = 8 * (cc & 3) + 4 * half + 2 * (cc >> 2);
     uint32_t out = 0;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)  // rr = 8 s + 2 p + e
-      out |= ((rw[rr] >> (2 * c)) & 3u) << (2 * ((rr >> 1) & 3) + 8 * (rr >> 3) + 16 * (rr & 1));
-    ow[tc_ow_at(cbl, (c + 16 * g) * 2 + h)] = out;
+      out |= ((rw[rr] >> sh) & 3u) << (2 * ((rr >> 1) & 3) + 8 * (rr >> 3) + 16 * (rr & 1));
+    ow[tc_ow_at(cbl, (8 * half + cc + 16 * g) * 2 + h)] = out;
   }
   __syncthreads();
   // 16 threads per output block, 8 consecutive words (32 bytes) each

@@ -66,6 +66,16 @@ def test_bwd_dx_patterns(n, m, T, N, K):
     _check(dx, dy, codes, gamma)
 
 
+@pytest.mark.parametrize("T,N,K", [(64, 256, 256), (130, 300, 520)])
+def test_bwd_dx_24_positional(T, N, K, monkeypatch):
+    """2:4 packed in the positional form (SBN_NO_SMFMAC=1 at pack time): the transposed plane is
+    built from positional words, as for 6:8 and 8:16, not from the structured-sparse slots."""
+    monkeypatch.setenv("SBN_NO_SMFMAC", "1")
+    dy, w = _case(7 * T + N + K, T, N, K)
+    dx, codes, gamma = _run(dy, w, 2, 4)
+    _check(dx, dy, codes, gamma)
+
+
 def test_bwd_dx_repack_rebuilds_transposed_plane():
     """A re-pack with a different mask is seen by the next data gradient."""
     import torch
