@@ -188,8 +188,8 @@ class Gpu:
 def measure_ceilings(gpu, small_bytes):
     """The box's own ceilings (include/sbn_ceilings.h): a streaming read of 2 GiB (HBM), a read of
     `small_bytes` as one launch (the decode step's size; rotated over the 2 GiB buffer, so it comes
-    from HBM), an INT8 MFMA loop with no memory traffic, and an empty kernel's cost per launch in a
-    graph. Each is the median of REPEATS timed replays."""
+    from HBM), INT8 dense and structured-sparse MFMA loops with no memory traffic, and an empty
+    kernel's cost per launch in a graph. Each is the median of REPEATS timed replays."""
     import ctypes
     torch, b = gpu.torch, gpu.b
     lib = b.lib()
@@ -215,21 +215,30 @@ def measure_ceilings(gpu, small_bytes):
         b.check(lib.sbn_ceiling_mfma_i8(iters, waves, b._ptr(sink), ctypes.byref(ops),
                                         b._stream(None)))
 
+    sops = ctypes.c_double(0.0)
+
+    def smfmac(i):
+        b.check(lib.sbn_ceiling_smfmac_i8(iters, waves, b._ptr(sink), ctypes.byref(sops),
+                                          b._stream(None)))
+
     def empty(i):
         b.check(lib.sbn_ceiling_empty(b._stream(None)))
 
     read_ms = gpu.time_launches(read_all, 5)
     small_ms = gpu.time_launches(read_small, KERNEL_LAUNCHES)
     mfma_ms = gpu.time_launches(mfma, 5)
+    smfmac_ms = gpu.time_launches(smfmac, 5)
     empty_ms = gpu.time_launches(empty, KERNEL_LAUNCHES)
     del buf
     return {"hbm_read_GBps": big / (read_ms * 1e-3) / 1e9, "hbm_read_bytes": big,
             "small_read_us": small_ms * 1e3, "small_read_bytes": small,
             "small_read_GBps": small / (small_ms * 1e-3) / 1e9,
             "int8_mfma_TOPS": ops.value / (mfma_ms * 1e-3) / 1e12,
+            "int8_smfmac_dense_equiv_TOPS": sops.value / (smfmac_ms * 1e-3) / 1e12,
             "empty_kernel_us": empty_ms * 1e3,
             "note": "measured on this GPU: streaming read, one read launch of the decode step's "
-                    "size, INT8 MFMA loop, empty kernel (per launch in a graph)"}
+                    "size, INT8 MFMA loop, structured-sparse INT8 MFMA loop (2:4, counted "
+                    "dense-equivalent), empty kernel (per launch in a graph)"}
 
 
 def read_launch_ms(gpu, nbytes, launches):

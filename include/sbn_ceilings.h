@@ -42,6 +42,15 @@ sbn_status sbn_ceiling_stream_read(const void* buf, size_t bytes, uint32_t senti
 sbn_status sbn_ceiling_mfma_i8(int64_t iters, int64_t waves, uint32_t* sink, double* ops /* host */,
                                void* stream);
 
+/*
+ * The same loop on the structured-sparse v_smfmac_i32_16x16x128_i8 (the instruction of the 2:4
+ * GEMM): eight independent chains per wave, each instruction counted as its dense-equivalent
+ * 2 * 16 * 16 * 128 = 65536 integer operations (it multiplies the 64 kept weights of each 128-K
+ * row slice); *ops (host) receives waves * iters * 8 * 65536. Same argument limits.
+ */
+sbn_status sbn_ceiling_smfmac_i8(int64_t iters, int64_t waves, uint32_t* sink,
+                                 double* ops /* host */, void* stream);
+
 /* Enqueues one launch of an empty kernel (one workgroup of one wave). */
 sbn_status sbn_ceiling_empty(void* stream);
 

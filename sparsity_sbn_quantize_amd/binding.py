@@ -79,6 +79,8 @@ _SIGNATURES = {
                                                        ctypes.c_int, _P]),
     "sbn_ceiling_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_uint32, _P, _P]),
     "sbn_ceiling_mfma_i8": (ctypes.c_int, [_I64, _I64, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "sbn_ceiling_smfmac_i8": (ctypes.c_int, [_I64, _I64, _P, ctypes.POINTER(ctypes.c_double),
+                                             _P]),
     "sbn_ceiling_empty": (ctypes.c_int, [_P]),
 }
 

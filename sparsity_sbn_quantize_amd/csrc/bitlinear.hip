@@ -29,9 +29,13 @@
 namespace sbn {
 namespace {
 
-// GEMM (T > 16): a workgroup of 4 waves computes 256 rows x 16 CF tokens (CF = 8: 128 tokens;
+// GEMM (T > 16): a workgroup of W = 4 waves computes 256 rows x 16 CF tokens (CF = 8: 128 tokens;
 // CF = 4: 64); wave w owns 4 row fragments (64 rows) and all the tile's tokens. Two workgroups
 // share a CU (two waves per SIMD), so one wave's decode and LDS traffic overlap the other's MFMAs.
+// Launches with many 128-token tiles take W = 8 waves on 512 rows instead (one workgroup per
+// CU, still two waves per SIMD): each step's activation tile then goes to LDS once for 512 rows
+// instead of once per 256, and the global -> LDS transfers of the activation tiles were what
+// bounded the K loop (timing copies with half of those transfers left out ran 9-18% faster).
 // K advances 256 per step. Each step's activation tile goes global -> LDS directly
 // (global_load_lds, no registers) into a 2-slot ring, one step ahead, laid out so that every
 // fragment read is free of bank conflicts. K slice j+1 of the wave's row fragments is decoded while
@@ -42,7 +46,6 @@ constexpr int kGemmWaves = 4;
 constexpr int kRF = 4;                                  // 16-row fragments per wave
 constexpr int kGemmRowBlocks = kGemmWaves * kRF;        // 16 row fragments (256 rows) per tile
 constexpr int kXBufs = 2;                               // activation ring depth
-constexpr int kGemmThreads = kGemmWaves * 64;
 
 // LDS of a CF tile: the activation ring, then the tile's a'_t (one float per token).
 constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + cf * 16 * 4; }
@@ -65,10 +68,11 @@ constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + 
 // then move about as many bytes as the fp32 output, all at the same moment.
 constexpr int kOutPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: output stores
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
+constexpr int kWideMinTiles = 200;     // 512-row tiles when a launch has at least this many
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K words of the handle");
 
-template <int FORM, bool XVEC, int CF>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int FORM, bool XVEC, int CF, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __restrict__ code_plane,
                     Layout L, const float* __restrict__ gamma_p, const int8_t* __restrict__ xq,
                     int64_t ld_q, const float* __restrict__ absmax, int64_t T,
@@ -77,7 +81,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   constexpr int kGemmCF = CF;                             // 16-token fragments per tile
   constexpr int kGemmTok = CF * 16;                       // tokens per tile
   constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile
-  constexpr int kXLoads = kGemmTok * 16 / kGemmThreads;   // 16-byte pieces per thread per step
+  constexpr int kXLoads = kGemmTok * 16 / (W * 64);       // 16-byte pieces per thread per step
   constexpr size_t kRing = (size_t)kXBufs * kTileBytes;
   constexpr bool POS = FORM != kFormKept;  // 16 code bytes per lane and quad
   constexpr bool SP = FORM == kFormSparse24;
@@ -90,7 +94,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   const int tile_lin = lin / ksplit, half = lin % ksplit;
   int tile_n, tile_t;
   grouped_tile(tile_lin, tiles_n, tiles_t, tile_n, tile_t);
-  const int64_t rb0 = ((int64_t)tile_n * kGemmWaves + wave) * kRF;
+  const int64_t rb0 = ((int64_t)tile_n * W + wave) * kRF;
   const int64_t t0 = (int64_t)tile_t * kGemmTok;
   const int nq = (int)L.quads;
   const int qb = nq * half / ksplit, qe = nq * (half + 1) / ksplit;  // this workgroup's K steps
@@ -105,9 +109,11 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   const uint8_t* const mbase = POS ? nullptr : mask_plane + (frag0 << 6) * 8;
   const int64_t rf_stride = (int64_t)nq << 6;  // slots per row fragment
   // Positional bricks go through a buffer resource (base in scalar registers, one 32-bit lane
-  // offset): every offset a tile uses is below kRF * nq * 1024 bytes <= 2 MB.
-  const __amdgpu_buffer_rsrc_t crsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, 0x7FFFFFFF, kBufDword3);
+  // offset): every offset a tile uses is below kRF * nq * 1024 bytes <= 2 MB. The stored plane
+  // ends at a multiple of 256 rows; with 512-row tiles the waves of a last tile's second half lie
+  // wholly past it, and their resource is empty (every brick reads zero).
+  const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)cbase, (short)0, rb0 < L.row_blocks_pad ? 0x7FFFFFFF : 0, kBufDword3);
   const int lane_c = lane * cbb;
   // Activation pieces are read relative to the tile's first token row. The aligned path reads
   // through buffer resources whose range ends with the last activation row: pieces of tokens past
@@ -382,7 +388,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
     // partial sums are stored, the wave waits until its stores have completed, then publishes
     // its launch count; the other half reads the partial sums only after it has seen that count.
     constexpr int kSc1 = 1 << 4;  // buffer cache-policy bit: sc1
-    uint32_t* const arrive = sync + 2 * ((int64_t)tile_lin * kGemmWaves + wave);
+    uint32_t* const arrive = sync + 2 * ((int64_t)tile_lin * W + wave);
     uint32_t* const ready = arrive + 1;
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(y, (short)0, 0x7FFFFFFF, kBufDword3);
@@ -595,19 +601,29 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   // y offsets of the split-K handshake are 32-bit buffer offsets
   const bool y_fits = (double)T * (double)ld_y * 4.0 < 2147483647.0;
   const int ksplit = (gx * gy <= kSplitMaxTiles && L.quads >= 8 && y_fits) ? 2 : 1;
-#define SBN_GEMM(CF)                                                                           \
+  // 512-row tiles (8 waves, one workgroup per CU) where they still number kWideMinTiles: the
+  // activation tile of a K step then feeds twice the MFMAs (see the kernel's header).
+  const int64_t gx8 = (L.row_blocks + 2 * kGemmRowBlocks - 1) / (2 * kGemmRowBlocks);
+  const bool w8 = wide && gx8 * gy >= kWideMinTiles;
+#define SBN_GEMM(CF, WW, GX)                                                                   \
   do {                                                                                         \
-    hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC, CF>, gemm_smem(CF));                  \
+    hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC, CF, WW>, gemm_smem(CF));              \
     if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC, CF>), dim3((unsigned)(gx * gy * ksplit)),     \
-                       dim3(kGemmThreads), gemm_smem(CF), s, h->mask, h->codes, L,              \
-                       h->gamma_out(), xq, ld_q, absmax, T, y, ld_y, out_kind, (int)gx, (int)gy, \
+    hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC, CF, WW>), dim3((unsigned)(GX * gy * ksplit)), \
+                       dim3(WW * 64), gemm_smem(CF), s, h->mask, h->codes, L,                   \
+                       h->gamma_out(), xq, ld_q, absmax, T, y, ld_y, out_kind, (int)GX, (int)gy, \
                        ksplit, h->gemm_sync, h->splitk_spin_limit, h->splitk_publish);        \
   } while (0)
+  if constexpr (XVEC && FORM != kFormKept) {  // positional bricks through a bounded resource
+    if (w8) {
+      SBN_GEMM(8, 8, gx8);
+      return hipGetLastError();
+    }
+  }
   if (wide) {
-    SBN_GEMM(8);
+    SBN_GEMM(8, 4, gx);
   } else {
-    SBN_GEMM(4);
+    SBN_GEMM(4, 4, gx);
   }
 #undef SBN_GEMM
   return hipGetLastError();

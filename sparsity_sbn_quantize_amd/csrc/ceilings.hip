@@ -1,5 +1,5 @@
-// Measured ceilings of the GPU: a streaming read, a loop of INT8 MFMA instructions and an empty
-// kernel, so that the library's rates can be reported against what this chip delivers beside its
+// Measured ceilings of the GPU: a streaming read, loops of dense and structured-sparse INT8 MFMA
+// instructions and an empty kernel, so that the library's rates can be reported against what this chip delivers beside its
 // published peaks. Declared in include/sbn_ceilings.h.
 #include "sbn_ceilings.h"
 #include "sbn_internal.hpp"
@@ -58,6 +58,36 @@ __global__ __launch_bounds__(256) void ceiling_mfma(int iters, uint32_t* __restr
   if (s == 0x7FFFFFFF && threadIdx.x == 0) sink[0] = (uint32_t)s;
 }
 
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// The same loop on the structured-sparse instruction (2:4 kept weights of 128 K per row in the A
+// operand, a 2-bit position index per kept weight): 16 x 16 x 128 dense-equivalent products each.
+__global__ __launch_bounds__(256) void ceiling_smfmac(int iters, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const v4i_t a = {lane, lane * 3, lane * 5, lane * 7};
+  const v8i_t b = {lane * 11, lane * 13, lane * 17, lane * 19, lane * 23, lane * 29, lane * 31,
+                   lane * 37};
+  const int idx = (int)0xE4E4E4E4u;  // positions 0, 1, 2, 3 ... of each group of 4 (valid pairs)
+  v4i_t c0 = {0, 0, 0, 0}, c1 = {1, 0, 0, 0}, c2 = {2, 0, 0, 0}, c3 = {3, 0, 0, 0};
+  v4i_t c4 = {4, 0, 0, 0}, c5 = {5, 0, 0, 0}, c6 = {6, 0, 0, 0}, c7 = {7, 0, 0, 0};
+  for (int i = 0; i < iters; ++i) {
+    asm volatile(
+        "v_smfmac_i32_16x16x128_i8 %0, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %1, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %2, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %3, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %4, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %5, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %6, %8, %9, %10\n\t"
+        "v_smfmac_i32_16x16x128_i8 %7, %8, %9, %10"
+        : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+        : "v"(a), "v"(b), "v"(idx));
+  }
+  const v4i_t x = c0 ^ c1 ^ c2 ^ c3 ^ c4 ^ c5 ^ c6 ^ c7;
+  const int s = x[0] ^ x[1] ^ x[2] ^ x[3];
+  if (s == 0x7FFFFFFF && threadIdx.x == 0) sink[0] = (uint32_t)s;
+}
+
 __global__ void ceiling_empty() {}
 
 }  // namespace
@@ -95,6 +125,22 @@ sbn_status sbn_ceiling_mfma_i8(int64_t iters, int64_t waves, uint32_t* sink, dou
   if (e != hipSuccess)
     return sbn::set_error(SBN_ERR_HIP, "sbn_ceiling_mfma_i8 launch: %s", hipGetErrorString(e));
   *ops = (double)waves * (double)iters * 8.0 * 32768.0;
+  return SBN_OK;
+}
+
+sbn_status sbn_ceiling_smfmac_i8(int64_t iters, int64_t waves, uint32_t* sink, double* ops,
+                                 void* stream) {
+  if (!sink || !ops)
+    return sbn::set_error(SBN_ERR_INVALID_ARG, "sbn_ceiling_smfmac_i8: null pointer");
+  if (iters < 1 || iters > (1 << 24) || waves < 4 || waves > (1 << 20) || waves % 4 != 0)
+    return sbn::set_error(SBN_ERR_INVALID_ARG, "sbn_ceiling_smfmac_i8: iters=%lld waves=%lld",
+                          (long long)iters, (long long)waves);
+  hipLaunchKernelGGL(sbn::ceiling_smfmac, dim3((unsigned)(waves / 4)), dim3(256), 0,
+                     (hipStream_t)stream, (int)iters, sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return sbn::set_error(SBN_ERR_HIP, "sbn_ceiling_smfmac_i8 launch: %s", hipGetErrorString(e));
+  *ops = (double)waves * (double)iters * 8.0 * 65536.0;
   return SBN_OK;
 }
 

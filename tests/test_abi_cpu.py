@@ -29,7 +29,8 @@ def test_exports_match_header(lib):
                              "sbn_packed_mask_flips", "sbn_last_error",
                              "sbn_bitlinear_fwd_group", "sbn_bitlinear_fwd_group_bf16",
                              "sbn_bitlinear_fwd_latent_static",
-                             "sbn_ceiling_stream_read", "sbn_ceiling_mfma_i8", "sbn_ceiling_empty"}
+                             "sbn_ceiling_stream_read", "sbn_ceiling_mfma_i8", "sbn_ceiling_smfmac_i8",
+                             "sbn_ceiling_empty"}
     out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -128,6 +129,9 @@ def test_forward_and_misc_validation(lib):
     assert lib.sbn_ceiling_mfma_i8(0, 1024, sink, ctypes.byref(ops), None) == ERR_INVALID
     assert lib.sbn_ceiling_mfma_i8(100, 6, sink, ctypes.byref(ops), None) == ERR_INVALID
     assert lib.sbn_ceiling_mfma_i8(100, 1024, sink, None, None) == ERR_INVALID
+    assert lib.sbn_ceiling_smfmac_i8(0, 1024, sink, ctypes.byref(ops), None) == ERR_INVALID
+    assert lib.sbn_ceiling_smfmac_i8(100, 6, sink, ctypes.byref(ops), None) == ERR_INVALID
+    assert lib.sbn_ceiling_smfmac_i8(100, 1024, None, ctypes.byref(ops), None) == ERR_INVALID
 
 
 def test_error_message_is_per_call(lib):

@@ -1,7 +1,8 @@
-"""GPU parity of the GEMM's two tile widths (T > 16). Launches whose 128-token tiles number more
-than 256 use them; smaller launches use 64-token tiles (split over K as well while they still
-number at most 256). Integer accumulators equal the oracle's exactly; fp32 outputs follow it within
-the forward's tolerance; the fp32 scale of each token comes from the tile's LDS copy of a'_t."""
+"""GPU parity of the GEMM's tile shapes (T > 16). Launches whose 128-token tiles number more
+than 256 use them (on 512 rows with 8 waves when those tiles number at least 200); smaller
+launches use 64-token tiles (split over K as well while they still number at most 256). Integer
+accumulators equal the oracle's exactly; fp32 outputs follow it within the forward's tolerance;
+the fp32 scale of each token comes from the tile's LDS copy of a'_t."""
 
 import numpy as np
 import pytest
@@ -31,6 +32,23 @@ def test_tile_width_boundary(n, m, T):
     N, K = 4352, 1040 - 1040 % m
     assert (tiles128(T, N) > 256) == (T == 1930)
     x, w = _case(T + 31 * n + m, T, K, N)
+    g = gu.gpu_forward(x, w, n, m)
+    gu.check_stages(g, x, w, n, m)
+
+
+def tiles512(T, N):
+    return -(-N // 512) * -(-T // 128)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 16), (3, 8)])
+def test_512_row_tiles(n, m):
+    """Launches with at least 200 tiles of 512 rows x 128 tokens run 8-wave workgroups (the
+    positional and 2:4 forms): N = 4352 makes the last row tile half empty (its waves past the
+    stored plane read zero bricks and store nothing), T = 2900 a 84-token tail. 3:8 (kept form)
+    keeps 256-row tiles at the same size."""
+    T, N, K = 2900, 4352, 1040 - 1040 % m
+    assert tiles512(T, N) >= 200
+    x, w = _case(7 * n + m, T, K, N)
     g = gu.gpu_forward(x, w, n, m)
     gu.check_stages(g, x, w, n, m)
 
