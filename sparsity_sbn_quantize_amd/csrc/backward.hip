@@ -12,8 +12,9 @@
 //
 // The reduction runs over the weight rows, so the A operand needs, per lane, 8 consecutive rows
 // of one column: the transposed code plane (pack.hip) stores exactly that, 2 bits per weight.
-// A workgroup computes 256 columns x 128 tokens; wave w owns 4 column fragments (64 columns) and
-// all 128 tokens. Each step covers 128 rows: the 128 x 128 bf16 dY tile goes global -> LDS
+// A workgroup of W = 4 waves computes 256 columns x 128 tokens (W = 8: 512 columns, for launches
+// with many tiles, so that each dY tile below serves twice the MFMAs); wave w owns 4 column
+// fragments (64 columns) and all 128 tokens. Each step covers 128 rows: the 128 x 128 bf16 dY tile goes global -> LDS
 // directly into a 2-slot ring one step ahead (the same [token group][16-byte chunk][token] layout
 // as the forward's activations, free of bank conflicts), the transposed bricks come one step
 // ahead into registers, and slice j+1 (32 rows) is decoded to bf16 while the MFMAs of slice j run.
@@ -25,15 +26,12 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBwWaves = 4;
 constexpr int kBwCF = 4;                                 // 16-column fragments per wave
 constexpr int kBwTF = 8;                                 // 16-token fragments per tile
 constexpr int kBwTok = kBwTF * 16;                       // 128 tokens per tile
-constexpr int kBwCols = kBwWaves * kBwCF * 16;           // 256 columns per tile
-constexpr int kBwThreads = kBwWaves * 64;
 constexpr int kBwStepRows = 128;                         // rows per step (4 MFMA slices of 32)
 constexpr int kBwTileBytes = kBwTok * kBwStepRows * 2;   // dY tile of one step (32 KB)
-constexpr int kBwXLoads = kBwTileBytes / 16 / kBwThreads;  // 16-byte pieces per thread per step
+constexpr int kBwWideMinTiles = 200;  // 8-wave tiles (512 columns) when there are this many
 constexpr size_t kBwSmem = 2 * (size_t)kBwTileBytes;
 // Lane offset that lies past every buffer range the dY loads use: such pieces read as zero.
 constexpr int kDxPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: dX stores
@@ -60,8 +58,8 @@ __device__ __forceinline__ v4f mfma_bf16(const uint32_t a[4], v4i b, v4f c) {
                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-template <bool XVEC>
-__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool XVEC, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t n_out, int64_t K,
                       const float* __restrict__ gamma_p, const uint16_t* __restrict__ dy,
                       int64_t ld_dy, int64_t T, float* __restrict__ dx, int64_t ld_dx,
@@ -72,13 +70,19 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
   const int lin = xcd_order((int)gridDim.x, (int)blockIdx.x);
   int tile_c, tile_t;
   grouped_tile(lin, tiles_c, tiles_t, tile_c, tile_t);
-  const int64_t cb0 = (int64_t)tile_c * (kBwCols / 16) + wave * kBwCF;  // first column fragment
+  constexpr int kBwXLoads = kBwTileBytes / 16 / (W * 64);  // 16-byte pieces per thread per step
+  const int64_t cb0 = (int64_t)tile_c * (W * kBwCF) + wave * kBwCF;  // first column fragment
   const int64_t t0 = (int64_t)tile_t * kBwTok;
 
   // Transposed bricks: slot (cb * rq_count + rq) * 64 + lane, 8 bytes; the wave's 4 column
   // fragments are rq_count * 512 bytes apart.
+  // The plane holds the column fragments of whole 256-column quads; with 512-column tiles the
+  // waves of a last tile's second half may lie wholly past it: their resource is empty (every
+  // brick reads zero) and their columns are never stored.
+  const int64_t plane_cf = (K + 255) / 256 * 16;
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(tplane + cb0 * rq_count * 128), (short)0, 0x7FFFFFFF, kBufDword3);
+      (void*)(tplane + cb0 * rq_count * 128), (short)0, cb0 < plane_cf ? 0x7FFFFFFF : 0,
+      kBufDword3);
   const int cf_bytes = rq_count * 512;
   typedef uint32_t TBricks[kBwCF][2];
   auto load_t = [&](int rq, TBricks& tw) {
@@ -254,24 +258,30 @@ hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy,
     if (e != hipSuccess) return e;
   }
   const_cast<sbn_packed*>(h)->tplane_valid = true;
-  const int64_t tiles_c = L.quads;  // 256 columns per tile
   const int64_t tiles_t = (T + kBwTok - 1) / kBwTok;
   const bool xvec = ((uintptr_t)dy % 16 == 0) && (ld_dy % 8 == 0) && (L.n_out % 8 == 0) &&
                     (double)T * (double)ld_dy * 2.0 < (double)kMaxBufExtent;
-  hipError_t e;
-  if (xvec) {
-    e = allow_smem(bitlinear_bwd_dx<true>, kBwSmem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bitlinear_bwd_dx<true>, dim3((unsigned)(tiles_c * tiles_t)),
-                       dim3(kBwThreads), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,
-                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
+  // 512 columns per tile (8 waves) when such tiles number kBwWideMinTiles: each step's dY tile
+  // then goes to LDS once for 512 columns instead of once per 256 (as the forward GEMM)
+  const int64_t tiles_c8 = (L.quads + 1) / 2;
+  const bool w8 = xvec && tiles_c8 * tiles_t >= kBwWideMinTiles;
+  const int64_t tiles_c = w8 ? tiles_c8 : L.quads;
+#define SBN_BWD(XV, WW)                                                                        \
+  do {                                                                                         \
+    hipError_t e = allow_smem(bitlinear_bwd_dx<XV, WW>, kBwSmem);                              \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_bwd_dx<XV, WW>), dim3((unsigned)(tiles_c * tiles_t)),          \
+                       dim3(WW * 64), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,     \
+                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);    \
+  } while (0)
+  if (w8) {
+    SBN_BWD(true, 8);
+  } else if (xvec) {
+    SBN_BWD(true, 4);
   } else {
-    e = allow_smem(bitlinear_bwd_dx<false>, kBwSmem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bitlinear_bwd_dx<false>, dim3((unsigned)(tiles_c * tiles_t)),
-                       dim3(kBwThreads), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,
-                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);
+    SBN_BWD(false, 4);
   }
+#undef SBN_BWD
   return hipGetLastError();
 }
 

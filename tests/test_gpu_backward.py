@@ -143,9 +143,22 @@ def test_bwd_dx_validation():
     pw.free()
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (3, 8)])
+def test_bwd_dx_512_column_tiles(n, m):
+    """Launches with at least 200 tiles of 512 columns x 128 tokens run 8-wave workgroups: K = 3328
+    (13 quads) leaves the last tile's second half past the transposed plane (its waves read zero
+    bricks and store nothing), T = 3900 a 60-token tail, n_out = 300 a ragged last row step;
+    canaries right of K."""
+    T, N, K = 3900, 300, 3328
+    assert -(-K // 512) * -(-T // 128) >= 200
+    dy, w = _case(500 + 7 * n + m, T, N, K)
+    dx, codes, gamma = _run(dy, w, n, m, ld_dx=K + 4)
+    _check(dx, dy, codes, gamma)
+
+
 def test_bwd_dx_7b_shapes_sampled():
-    """The 7B FFN shapes at T = 8192 (the launch the benchmark times), 2:4 and 8:16; the oracle
-    on 24 sampled tokens."""
+    """The 7B FFN shapes at T = 8192 (the launch the benchmark times: 512-column tiles, the last
+    one half past the plane for K = 11008), 2:4 and 8:16; the oracle on 24 sampled tokens."""
     import torch
     wl = inputs.W_TRAIN
     rows = np.random.default_rng(0).choice(8192, 24, replace=False)
