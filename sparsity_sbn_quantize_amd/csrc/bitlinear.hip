@@ -69,6 +69,7 @@ constexpr size_t gemm_smem(int cf) { return (size_t)kXBufs * cf * 16 * kQuadK + 
 constexpr int kOutPolicy = 1 | 2 | 16;  // buffer cache-policy bits sc0 | nt | sc1: output stores
 constexpr int kSplitMaxTiles = 256;    // split when a launch has at most this many tiles
 constexpr int kWideMinTiles = 200;     // 512-row tiles when a launch has at least this many
+constexpr int kOneRoundTiles = 256;    // 8-wave workgroups that run at once (one per CU)
 static_assert(kGemmSyncInts >= kSplitMaxTiles * 4 * 2, "split-K words of the handle");
 
 template <int FORM, bool XVEC, int CF, int W>
@@ -81,7 +82,11 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   constexpr int kGemmCF = CF;                             // 16-token fragments per tile
   constexpr int kGemmTok = CF * 16;                       // tokens per tile
   constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile
-  constexpr int kXLoads = kGemmTok * 16 / (W * 64);       // 16-byte pieces per thread per step
+  // A step's activation tile is 4 CF wave loads of 1 KB (16 tokens x 64 bytes each), spread over
+  // the W waves; when W does not divide them (CF = 3 on 8 waves) the last waves issue fewer.
+  constexpr int kXInstr = 4 * CF;
+  constexpr int kXLoads = (kXInstr + W - 1) / W;          // wave loads per wave and step
+  constexpr bool kXRagged = kXInstr % W != 0;
   constexpr size_t kRing = (size_t)kXBufs * kTileBytes;
   constexpr bool POS = FORM != kFormKept;  // 16 code bytes per lane and quad
   constexpr bool SP = FORM == kFormSparse24;
@@ -152,6 +157,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i) {
         const int ii = wave * kXLoads + i, cf = ii >> 2, c0 = (ii & 3) * 4;
+        if (kXRagged && ii >= kXInstr) break;  // wave-uniform
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(dst + i * 1024), 16,
                                                  xlane + cf * 16 * ldq + c0 * 16, 0, 0, 0);
       }
@@ -159,6 +165,7 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i) {
         const int ii = wave * kXLoads + i, cf = ii >> 2, c0 = (ii & 3) * 4;
+        if (kXRagged && ii >= kXInstr) break;  // wave-uniform
         const int tok = cf * 16 + (lane & 15), c = c0 + (lane >> 4);
         const int8_t* row = xq + min<int64_t>(t0 + tok, T - 1) * ld_q;
         *reinterpret_cast<v4i*>(dst + i * 1024 + lane * 16) = load_x16<false>(row, kq + c * 16, K);
@@ -615,6 +622,31 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
                        ksplit, h->gemm_sync, h->splitk_spin_limit, h->splitk_publish);        \
   } while (0)
   if constexpr (XVEC && FORM != kFormKept) {  // positional bricks through a bounded resource
+    // One round of 512-row tiles that fills at least kWideMinTiles of the CUs: the widest token
+    // tile (128, 96, 64 or 48 tokens) whose tile count lies in [kWideMinTiles, kOneRoundTiles].
+    // Same-box A/B at T = 4096: 2560 -> 2560 38.8 -> 28.2 us and 6912 -> 2560 81.5 -> 60.4 us
+    // with 96-token tiles (215 tiles) against 128-token tiles of 256 rows (320 tiles, two per CU
+    // on 64 CUs); 2560 -> 6912 at T = 2048 keeps 128-token tiles (224).
+    auto one_round = [&](int cf) {
+      const int64_t tiles = gx8 * ((T + 16 * cf - 1) / (16 * cf));
+      return tiles >= kWideMinTiles && tiles <= kOneRoundTiles;
+    };
+#define SBN_GEMM8(CF)                                                                          \
+  do {                                                                                         \
+    const int64_t gyc = (T + 16 * CF - 1) / (16 * CF);                                         \
+    hipError_t e = allow_smem(bitlinear_gemm<FORM, XVEC, CF, 8>, gemm_smem(CF));               \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((bitlinear_gemm<FORM, XVEC, CF, 8>), dim3((unsigned)(gx8 * gyc)),        \
+                       dim3(8 * 64), gemm_smem(CF), s, h->mask, h->codes, L, h->gamma_out(),    \
+                       xq, ld_q, absmax, T, y, ld_y, out_kind, (int)gx8, (int)gyc, 1,           \
+                       h->gemm_sync, h->splitk_spin_limit, h->splitk_publish);                 \
+    return hipGetLastError();                                                                  \
+  } while (0)
+    if (one_round(8)) SBN_GEMM8(8);
+    if (one_round(6)) SBN_GEMM8(6);
+    if (one_round(4)) SBN_GEMM8(4);
+    if (one_round(3)) SBN_GEMM8(3);
+#undef SBN_GEMM8
     if (w8) {
       SBN_GEMM(8, 8, gx8);
       return hipGetLastError();

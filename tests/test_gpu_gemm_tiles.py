@@ -1,5 +1,7 @@
-"""GPU parity of the GEMM's tile shapes (T > 16). Launches whose 128-token tiles number more
-than 256 use them (on 512 rows with 8 waves when those tiles number at least 200); smaller
+"""GPU parity of the GEMM's tile shapes (T > 16). A launch that fits one round of 8-wave
+workgroups on 512 rows (200 to 256 tiles of 128, 96, 64 or 48 tokens) takes the widest such
+tile. Otherwise launches whose 128-token tiles number more than 256 use them (on 512 rows with 8
+waves when those tiles number at least 200); smaller
 launches use 64-token tiles (split over K as well while they still number at most 256). Integer
 accumulators equal the oracle's exactly; fp32 outputs follow it within the forward's tolerance;
 the fp32 scale of each token comes from the tile's LDS copy of a'_t."""
@@ -49,6 +51,29 @@ def test_512_row_tiles(n, m):
     T, N, K = 2900, 4352, 1040 - 1040 % m
     assert tiles512(T, N) >= 200
     x, w = _case(7 * n + m, T, K, N)
+    g = gu.gpu_forward(x, w, n, m)
+    gu.check_stages(g, x, w, n, m)
+
+
+def one_round_cf(T, N):
+    """Token-tile width (in 16-token fragments) of the one-round 8-wave launch, or None."""
+    for cf in (8, 6, 4, 3):
+        tiles = -(-N // 512) * -(-T // (16 * cf))
+        if 200 <= tiles <= 256:
+            return cf
+    return None
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 16)])
+@pytest.mark.parametrize("T,K,cf", [(4091, 528, 6), (2059, 1040, 3)])
+def test_one_round_512_row_tiles(n, m, T, K, cf):
+    """One round of 8-wave workgroups on 512 rows where 128-token tiles would leave CUs idle:
+    96-token tiles (T = 4091: 43 token tiles, a 59-token tail) and 48-token tiles (T = 2059: 43,
+    a 43-token tail; the step's 12 activation loads spread over 8 waves, the last two issue
+    none). N = 2304 makes the last row tile half empty."""
+    N = 2304
+    assert one_round_cf(T, N) == cf
+    x, w = _case(T + 13 * n + m, T, K - K % m, N)
     g = gu.gpu_forward(x, w, n, m)
     gu.check_stages(g, x, w, n, m)
 
