@@ -82,11 +82,8 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
   constexpr int kGemmCF = CF;                             // 16-token fragments per tile
   constexpr int kGemmTok = CF * 16;                       // tokens per tile
   constexpr int kTileBytes = kGemmTok * kQuadK;           // one step's activation tile
-  // A step's activation tile is 4 CF wave loads of 1 KB (16 tokens x 64 bytes each), spread over
-  // the W waves; when W does not divide them (CF = 3 on 8 waves) the last waves issue fewer.
-  constexpr int kXInstr = 4 * CF;
-  constexpr int kXLoads = (kXInstr + W - 1) / W;          // wave loads per wave and step
-  constexpr bool kXRagged = kXInstr % W != 0;
+  constexpr int kXLoads = kGemmTok * 16 / (W * 64);       // 16-byte pieces per thread per step
+  static_assert(kXLoads * W * 64 == kGemmTok * 16, "the waves share a step's loads evenly");
   constexpr size_t kRing = (size_t)kXBufs * kTileBytes;
   constexpr bool POS = FORM != kFormKept;  // 16 code bytes per lane and quad
   constexpr bool SP = FORM == kFormSparse24;
@@ -157,7 +154,6 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i) {
         const int ii = wave * kXLoads + i, cf = ii >> 2, c0 = (ii & 3) * 4;
-        if (kXRagged && ii >= kXInstr) break;  // wave-uniform
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(dst + i * 1024), 16,
                                                  xlane + cf * 16 * ldq + c0 * 16, 0, 0, 0);
       }
@@ -165,7 +161,6 @@ void bitlinear_gemm(const uint8_t* __restrict__ mask_plane, const uint8_t* __res
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i) {
         const int ii = wave * kXLoads + i, cf = ii >> 2, c0 = (ii & 3) * 4;
-        if (kXRagged && ii >= kXInstr) break;  // wave-uniform
         const int tok = cf * 16 + (lane & 15), c = c0 + (lane >> 4);
         const int8_t* row = xq + min<int64_t>(t0 + tok, T - 1) * ld_q;
         *reinterpret_cast<v4i*>(dst + i * 1024 + lane * 16) = load_x16<false>(row, kq + c * 16, K);
@@ -623,10 +618,12 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
   } while (0)
   if constexpr (XVEC && FORM != kFormKept) {  // positional bricks through a bounded resource
     // One round of 512-row tiles that fills at least kWideMinTiles of the CUs: the widest token
-    // tile (128, 96, 64 or 48 tokens) whose tile count lies in [kWideMinTiles, kOneRoundTiles].
+    // tile (128, 96 or 64 tokens) whose tile count lies in [kWideMinTiles, kOneRoundTiles].
     // Same-box A/B at T = 4096: 2560 -> 2560 38.8 -> 28.2 us and 6912 -> 2560 81.5 -> 60.4 us
     // with 96-token tiles (215 tiles) against 128-token tiles of 256 rows (320 tiles, two per CU
-    // on 64 CUs); 2560 -> 6912 at T = 2048 keeps 128-token tiles (224).
+    // on 64 CUs); 2560 -> 6912 at T = 2048 keeps 128-token tiles (224). 48-token tiles (215 on
+    // 6912 -> 2560 at T = 2048) ran in the time of the 320 64-token tiles of 256 rows there
+    // (39.0 against 39.7 us) and fetched 16% more (58.3 against 50.4 MB), so they are not used.
     auto one_round = [&](int cf) {
       const int64_t tiles = gx8 * ((T + 16 * cf - 1) / (16 * cf));
       return tiles >= kWideMinTiles && tiles <= kOneRoundTiles;
@@ -645,7 +642,6 @@ hipError_t launch_pattern(const sbn_packed* h, const int8_t* xq, int64_t ld_q,
     if (one_round(8)) SBN_GEMM8(8);
     if (one_round(6)) SBN_GEMM8(6);
     if (one_round(4)) SBN_GEMM8(4);
-    if (one_round(3)) SBN_GEMM8(3);
 #undef SBN_GEMM8
     if (w8) {
       SBN_GEMM(8, 8, gx8);

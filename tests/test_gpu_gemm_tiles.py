@@ -1,5 +1,5 @@
 """GPU parity of the GEMM's tile shapes (T > 16). A launch that fits one round of 8-wave
-workgroups on 512 rows (200 to 256 tiles of 128, 96, 64 or 48 tokens) takes the widest such
+workgroups on 512 rows (200 to 256 tiles of 128, 96 or 64 tokens) takes the widest such
 tile. Otherwise launches whose 128-token tiles number more than 256 use them (on 512 rows with 8
 waves when those tiles number at least 200); smaller
 launches use 64-token tiles (split over K as well while they still number at most 256). Integer
@@ -57,7 +57,7 @@ def test_512_row_tiles(n, m):
 
 def one_round_cf(T, N):
     """Token-tile width (in 16-token fragments) of the one-round 8-wave launch, or None."""
-    for cf in (8, 6, 4, 3):
+    for cf in (8, 6, 4):
         tiles = -(-N // 512) * -(-T // (16 * cf))
         if 200 <= tiles <= 256:
             return cf
@@ -65,12 +65,11 @@ def one_round_cf(T, N):
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 16)])
-@pytest.mark.parametrize("T,K,cf", [(4091, 528, 6), (2059, 1040, 3)])
+@pytest.mark.parametrize("T,K,cf", [(4091, 528, 6), (2600, 1040, 4)])
 def test_one_round_512_row_tiles(n, m, T, K, cf):
     """One round of 8-wave workgroups on 512 rows where 128-token tiles would leave CUs idle:
-    96-token tiles (T = 4091: 43 token tiles, a 59-token tail) and 48-token tiles (T = 2059: 43,
-    a 43-token tail; the step's 12 activation loads spread over 8 waves, the last two issue
-    none). N = 2304 makes the last row tile half empty."""
+    96-token tiles (T = 4091: 43 token tiles, a 59-token tail) and 64-token tiles (T = 2600: 41,
+    a 40-token tail). N = 2304 makes the last row tile half empty."""
     N = 2304
     assert one_round_cf(T, N) == cf
     x, w = _case(T + 13 * n + m, T, K - K % m, N)
