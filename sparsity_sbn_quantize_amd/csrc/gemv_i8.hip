@@ -414,6 +414,9 @@ void bitlinear_gemv_i8_kx(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (lds_ptr)(xs + (real ? tt * kRow + hb * 1024 : 16 * kRow)), 16, lane * 16, 0, 0, 0);
   }
+  // the token's a' with the pieces, so the last arrival's epilogue waits for no load of its own
+  float a_t = 0.0f;
+  if (out_kind == SBN_OUT_F32) a_t = absmax[tok_ok ? t : 0];
   __builtin_amdgcn_sched_barrier(0);  // the pieces go out before the bricks
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(code_plane + rb * nq * 1024), (short)0, nq * 1024, kBufDword3);
@@ -469,14 +472,27 @@ void bitlinear_gemv_i8_kx(
   constexpr int kGlc = 1;  // buffer cache-policy bit sc0: read past L1
   const __amdgpu_buffer_rsrc_t pr =
       __builtin_amdgcn_make_buffer_rsrc(pg, (short)0, C * 16384, kBufDword3);
-  for (int cc = 0; cc < C; ++cc)
-    if (cc != c) acc += __builtin_amdgcn_raw_buffer_load_b128(pr, wave * 1024 + lane * 16,
-                                                              cc * 16384, kGlc);
+  const float gamma = gamma_p[0];
+  // The other chunks' partial sums, kPB loads in flight per wait (their own chunk and chunks past
+  // C take an offset past the range and read zero). One wait per load made the last arrival's
+  // C - 1 L2 round trips serial.
+  constexpr int kPB = 8;
+  for (int c0 = 0; c0 < C; c0 += kPB) {
+    v4i pv[kPB];
+#pragma unroll
+    for (int u = 0; u < kPB; ++u) {
+      const int cc = c0 + u;
+      pv[u] = __builtin_amdgcn_raw_buffer_load_b128(pr, wave * 1024 + lane * 16,
+                                                    cc < C && cc != c ? cc * 16384 : C * 16384,
+                                                    kGlc);
+    }
+#pragma unroll
+    for (int u = 0; u < kPB; ++u) acc += pv[u];
+  }
   if (threadIdx.x == 0)
     __hip_atomic_store(count + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!tok_ok) return;
-  const float gamma = gamma_p[0];
-  const float step = out_kind == SBN_OUT_F32 ? absmax[t] / 127.0f : 0.0f;
+  const float step = out_kind == SBN_OUT_F32 ? a_t / 127.0f : 0.0f;
   const int64_t row0 = rb * 16 + 4 * g;
   const bool vec = ((uintptr_t)y % 16 == 0) && (ld_y % 4 == 0) && row0 + 3 < n_out;
   if (vec) {
