@@ -39,7 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["sparsity_sbn_quantize_amd/csrc/bitlinear.hip",
                   "sparsity_sbn_quantize_amd/csrc/sbn_common.hpp",
                   "sparsity_sbn_quantize_amd/csrc/gemv.hpp",
-                  "sparsity_sbn_quantize_amd/csrc/gemv_i8.hip"]
+                  "sparsity_sbn_quantize_amd/csrc/gemv_i8.hip",
+                  "sparsity_sbn_quantize_amd/csrc/gemv_bf16.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -822,7 +823,7 @@ def profile_copy(gpu, args):
 # `--pmc WRITE_SIZE`; the tag "copy" is `bench.py --profile-copy`.
 TRAFFIC_RUNS = {
     # positional codes (form 0) only: the compact variant's GEMV runs in the same workload
-    "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv<0, true, \w+, \d+, false, \w+>"),
+    "decode": ("gemv_fused_6of8_T1", r"bitlinear_gemv_bf16_one<0,"),
     "decode16": ("gemv_6of8_T16", r"bitlinear_gemv_i8_deep<0,"),
     "prefill_up": ("gemm_8of16_ffn_up", r"bitlinear_gemm<"),
     "prefill_down": ("gemm_8of16_ffn_down", r"bitlinear_gemm<"),

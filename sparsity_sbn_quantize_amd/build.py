@@ -15,11 +15,12 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsbn.so")
 
 SOURCES = ["api.hip", "quantize_act.hip", "pack.hip", "bitlinear.hip", "backward.hip",
-           "outliers.hip", "gemv_i8.hip", "ceilings.hip", "static_ws.hip"]
+           "outliers.hip", "gemv_i8.hip", "gemv_bf16.hip", "ceilings.hip", "static_ws.hip"]
 HEADERS = ["sbn_common.hpp", "sbn_internal.hpp", "gemv.hpp"]
-# The int8-input GEMV entry takes its first loads' operands as leading scalar arguments, which
-# the firmware preloads into registers with this option.
-EXTRA_FLAGS = {"gemv_i8.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+# The int8-input GEMV entries and the one-token bf16 entry take their first loads' operands as
+# leading scalar arguments, which the firmware preloads into registers with this option.
+_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+EXTRA_FLAGS = {"gemv_i8.hip": _PRELOAD, "gemv_bf16.hip": _PRELOAD}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -741,6 +741,9 @@ hipError_t launch_bitlinear_bf16_plain(const sbn_packed* h, const uint16_t* x, i
                                        void* y, int64_t ld_y, int out_kind, float ln_eps,
                                        hipStream_t s) {
   const Layout& L = h->L;
+  // one token, no LayerNorm: the entry with preloaded arguments (gemv_bf16.hip)
+  if (gemv_bf16_one_fits(h, x, T, ln_eps))
+    return launch_gemv_bf16_one(h, x, xq, ld_q, absmax, y, ld_y, out_kind, s);
   if (L.n_out > 0 && T <= kFusedMaxT && L.quads <= (int64_t)kGemvMaxWaves * kGemvMaxQ) {
     const bool xvec = ((uintptr_t)x % 8 == 0) && (ld_x % 4 == 0) && (L.K % 4 == 0);
 #define SBN_FUSED(FF)                                                                          \

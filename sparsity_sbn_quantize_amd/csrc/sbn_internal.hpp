@@ -143,6 +143,12 @@ hipError_t launch_sum_flips(const sbn_packed* h, uint64_t* out, hipStream_t s);
 hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s);
 hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,
                          float* dx, int64_t ld_dx, hipStream_t s);
+// The one-token quantize-and-multiply step without a LayerNorm (gemv_bf16.hip), and whether a
+// call fits it (T = 1, no compact plane, x 8-byte aligned, K % 4 == 0, one batch of quads).
+bool gemv_bf16_one_fits(const sbn_packed* h, const uint16_t* x, int64_t T, float ln_eps);
+hipError_t launch_gemv_bf16_one(const sbn_packed* h, const uint16_t* x, int8_t* xq, int64_t ld_q,
+                                float* absmax, void* y, int64_t ld_y, int out_kind,
+                                hipStream_t s);
 // ln_eps > 0: parameter-free LayerNorm (with that epsilon) before the quantization.
 hipError_t launch_bitlinear_bf16(const sbn_packed* h, const uint16_t* x, int64_t ld_x, int64_t T,
                                  int8_t* xq, int64_t ld_q, float* absmax, void* y, int64_t ld_y,
