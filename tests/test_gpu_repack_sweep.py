@@ -5,7 +5,8 @@ operation 3).
 Each case packs random latent weights once and then re-packs the same handle eight times, every
 step applying an update drawn at random: gamma scaled by up to 1% either way (inside or past the
 2^-7 bracket of the single-read re-pack), additive noise of four magnitudes, a row block replaced
-by a fresh draw, a row block set to exact magnitude ties, or rows set to zero. After every pack
+by a fresh draw, a row block set to exact magnitude ties, rows set to zero, or whole m-groups
+permuted along K (the masks move, gamma stays). After every pack
 gamma, the keep mask and the codes must equal the oracle's for the current weights (codes at the
 gamma the kernels used, which equals the oracle's except at an fp32 rounding midpoint of the mean);
 at the end a forward on the handle must match the oracle. Mostly the lean patterns (single-read
@@ -63,7 +64,7 @@ def _update(rng, w, m):
         w[rows] = 0.0
         what = "rows zeroed"
     else:
-        w = w[:, rng.permutation(K // m) .repeat(m) * m + np.tile(np.arange(m), K // m)]
+        w = w[:, rng.permutation(K // m).repeat(m) * m + np.tile(np.arange(m), K // m)]
         w = np.ascontiguousarray(w)
         what = "groups permuted"
     return w.astype(np.float32), what
