@@ -281,7 +281,9 @@ sbn_status sbn_bitlinear_fwd_latent_static(const float* w_latent, int64_t n_out,
  *             accumulated in fp32 (every product is exact; the order of the fp32 additions is
  *             unspecified, so |S - exact| <= (n_out - 1) * 2^-24 * sum_r |dy[t][r] * code[r][k]|).
  * The first call after a pack rebuilds the handle's transposed code plane (one extra kernel);
- * later calls reuse it. n_out == 0 gives dx = 0.
+ * later calls reuse it (the kernel still launches and exits at once). Whether a pack has run since
+ * is tracked in device memory, so packs and data gradients may be replayed from captured HIP
+ * graphs in any mix. n_out == 0 gives dx = 0.
  * Requires T >= 0, n_out <= ld_dy <= 2^25, ld_dx >= K, n_out <= 2^27; T == 0 is a no-op.
  */
 sbn_status sbn_bitlinear_bwd_dx(const sbn_packed* w, const uint16_t* dy_bf16, int64_t ld_dy,

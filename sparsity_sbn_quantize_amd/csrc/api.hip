@@ -74,7 +74,8 @@ sbn_status make_plan(int64_t n_out, int64_t K, int n, int m, Plan& p) {
   p.kx_chunks = kx ? (int)((L.quads + kKxQuads - 1) / kKxQuads) : 0;
   const int64_t kx_groups = kx ? kx_row_groups(L.row_blocks) : 0;
   p.off_sync = off;
-  off = align_up(off + sizeof(uint32_t) * (kGemmSyncInts + 1 + kx_groups), 256);
+  p.gen_index = kGemmSyncInts + 1 + (int)kx_groups;
+  off = align_up(off + sizeof(uint32_t) * (p.gen_index + 2), 256);
   p.off_flips = off;
   off = align_up(off + sizeof(uint32_t) * slots / 16, 256);  // 4 waves per fragment
   p.off_vc = off;
@@ -127,6 +128,7 @@ void bind_planes(sbn_packed& h, const Plan& p, uint8_t* base) {
   h.partials = reinterpret_cast<double*>(base + p.off_part);
   h.gemm_sync = reinterpret_cast<uint32_t*>(base + p.off_sync);
   h.kx_count = h.gemm_sync + kGemmSyncInts + 1;
+  h.pack_gen = h.gemm_sync + p.gen_index;
   h.kx_part = base + p.off_kx;
   h.kx_chunks = p.kx_chunks;
   h.flip_parts = reinterpret_cast<uint32_t*>(base + p.off_flips);
@@ -465,7 +467,6 @@ sbn_status sbn_pack_nm_ternary_ex(const float* w_latent, int64_t n_out, int64_t 
   }
   sbn::splitk_settings(h->splitk_spin_limit, h->splitk_publish);
   h->last_stream = s;
-  h->tplane_valid = false;  // rebuilt from the new codes by the next data-gradient call
   h->vc = (flags & SBN_PACK_VARIANCE_CORRECTION) != 0;
   h->compact = (flags & SBN_PACK_COMPACT) != 0;
   h->outlier_k = outlier_k;

@@ -63,8 +63,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t n_out, int64_t K,
                       const float* __restrict__ gamma_p, const uint16_t* __restrict__ dy,
                       int64_t ld_dy, int64_t T, float* __restrict__ dx, int64_t ld_dx,
-                      int tiles_c, int tiles_t) {
+                      int tiles_c, int tiles_t, uint32_t* __restrict__ pack_gen) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // The transposed plane this launch reads was built from the handle's last pack (the transpose
+  // kernel ran just before, in stream order); record that pack count for the next call.
+  if (blockIdx.x == 0 && threadIdx.x == 0) pack_gen[1] = pack_gen[0];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int lin = xcd_order((int)gridDim.x, (int)blockIdx.x);
@@ -253,11 +256,13 @@ void bitlinear_bwd_dx(const uint32_t* __restrict__ tplane, int rq_count, int64_t
 hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy, int64_t T,
                          float* dx, int64_t ld_dx, hipStream_t s) {
   const Layout& L = h->L;
-  if (!h->tplane_valid && h->rq_count > 0) {
+  // The transposed plane is rebuilt when a pack has run since it was last built; the check is
+  // made on the device (pack counts in the handle), so it holds when packs or data gradients are
+  // replayed from captured graphs. An up-to-date plane costs one launch whose workgroups exit.
+  if (h->rq_count > 0) {
     hipError_t e = launch_transpose_codes(h, s);
     if (e != hipSuccess) return e;
   }
-  const_cast<sbn_packed*>(h)->tplane_valid = true;
   const int64_t tiles_t = (T + kBwTok - 1) / kBwTok;
   const bool xvec = ((uintptr_t)dy % 16 == 0) && (ld_dy % 8 == 0) && (L.n_out % 8 == 0) &&
                     (double)T * (double)ld_dy * 2.0 < (double)kMaxBufExtent;
@@ -272,7 +277,8 @@ hipError_t launch_bwd_dx(const sbn_packed* h, const uint16_t* dy, int64_t ld_dy,
     if (e != hipSuccess) return e;                                                             \
     hipLaunchKernelGGL((bitlinear_bwd_dx<XV, WW>), dim3((unsigned)(tiles_c * tiles_t)),          \
                        dim3(WW * 64), kBwSmem, s, h->tplane, (int)h->rq_count, L.n_out, L.K,     \
-                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t);    \
+                       h->gamma_out(), dy, ld_dy, T, dx, ld_dx, (int)tiles_c, (int)tiles_t,     \
+                       h->pack_gen);                                                           \
   } while (0)
   if (w8) {
     SBN_BWD(true, 8);

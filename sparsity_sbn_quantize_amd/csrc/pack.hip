@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_partial(const float* 
 // taken off, so gamma is the absmean of the weights the ternary path sees.
 __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
     const double* __restrict__ partials, int num, double count, float* __restrict__ gamma,
-    const double* __restrict__ osum, int64_t nos) {
+    const double* __restrict__ osum, int64_t nos, uint32_t* __restrict__ pack_gen) {
   __shared__ double red[kAbsmeanThreads / 64];
   __shared__ double red2[kAbsmeanThreads / 64];
   double acc = 0.0;
@@ -100,7 +100,10 @@ __global__ __launch_bounds__(kAbsmeanThreads) void absmean_finalize(
     for (int64_t i = threadIdx.x; i < nos; i += kAbsmeanThreads) acc2 += osum[i];
     s -= block_sum_f64(acc2, red2);
   }
-  if (threadIdx.x == 0) gamma[0] = count > 0.0 ? (float)(s / count) : 0.0f;
+  if (threadIdx.x == 0) {
+    gamma[0] = count > 0.0 ? (float)(s / count) : 0.0f;
+    pack_gen[0] += 1u;  // one more pack of the handle (the transposed plane is now stale)
+  }
 }
 
 // Keep mask of one m-group a[0..M) by rank counting (used for M = 4): i is kept iff fewer than n
@@ -776,7 +779,8 @@ __global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, in
                                                  int vec4, Layout L, float* __restrict__ gamma_out,
                                                  uint8_t* __restrict__ mask_plane,
                                                  uint8_t* __restrict__ code_plane, BandWs band,
-                                                 int64_t frags, double count) {
+                                                 int64_t frags, double count,
+                                                 uint32_t* __restrict__ pack_gen) {
   constexpr int kWords = kBandRecBytes / 4;
   __shared__ uint32_t rec[kFixFrags][kWords];
   __shared__ uint32_t start[kFixFrags + 1];
@@ -834,7 +838,10 @@ __global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, in
   }
   __syncthreads();
   if (tid == 0) {
-    if (blockIdx.x == 0) gamma_out[0] = gsh;
+    if (blockIdx.x == 0) {
+      gamma_out[0] = gsh;
+      pack_gen[0] += 1u;  // one more pack of the handle (the transposed plane is now stale)
+    }
     // the last workgroup to have read the counters clears them for the next pass
     // Relaxed: a workgroup's counter loads have returned before its arrival (their sum is
     // computed above), and the clearing stores need only be visible to the next launch. (A
@@ -1192,7 +1199,13 @@ __device__ __forceinline__ int tc_ow_at(int cbl, int i) {
 __global__ __launch_bounds__(256) void transpose_codes(Layout L, const uint8_t* mask_plane,
                                                        const uint8_t* code_plane,
                                                        int64_t rq_count,
-                                                       uint32_t* __restrict__ tplane) {
+                                                       uint32_t* __restrict__ tplane,
+                                                       const uint32_t* __restrict__ pack_gen) {
+  // Nothing to do when the plane was built from the handle's last pack (the data-gradient kernel
+  // records that pack count once it has run on the plane).
+  if (__builtin_amdgcn_readfirstlane((int)pack_gen[1]) ==
+      __builtin_amdgcn_readfirstlane((int)pack_gen[0]))
+    return;
   __shared__ __attribute__((aligned(16))) uint32_t cw[128 * 16 + 7 * 16];
   __shared__ __attribute__((aligned(16))) uint32_t ow[16 * 128];
   const int64_t rq = blockIdx.x / L.quads, q = blockIdx.x % L.quads;
@@ -1370,7 +1383,8 @@ hipError_t launch_pack(const float* w, int64_t ld_w, sbn_packed* h, hipStream_t 
                                                    (frags + kFixFrags - 1) / kFixFrags);
       hipLaunchKernelGGL((pack_fix<decltype(MM)::value, decltype(NN)::value, decltype(FF)::value>),
                          dim3((unsigned)fix_blocks), dim3(1024), 0, s, w, ld_w, vec4, L, h->gamma,
-                         h->mask, h->codes, band, frags, (double)L.n_out * (double)L.K);
+                         h->mask, h->codes, band, frags, (double)L.n_out * (double)L.K,
+                         h->pack_gen);
     });
   } else {
     if (L.n_out > 0) {
@@ -1384,7 +1398,7 @@ hipError_t launch_pack(const float* w, int64_t ld_w, sbn_packed* h, hipStream_t 
     hipLaunchKernelGGL(absmean_finalize, dim3(1), dim3(kAbsmeanThreads), 0, s, h->partials,
                        L.n_out > 0 ? h->num_partials : 0, (double)L.n_out * (double)L.K, h->gamma,
                        outl ? h->osum : nullptr,
-                       outl ? (L.n_out * (L.K >> 8) + 255) / 256 : (int64_t)0);
+                       outl ? (L.n_out * (L.K >> 8) + 255) / 256 : (int64_t)0, h->pack_gen);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || L.n_out == 0) return e;
     uint32_t* const vc = h->vc ? h->vc_parts : nullptr;
@@ -1553,7 +1567,7 @@ hipError_t launch_transpose_codes(const sbn_packed* h, hipStream_t s) {
   const Layout& L = h->L;
   if (h->rq_count == 0) return hipSuccess;
   hipLaunchKernelGGL(transpose_codes, dim3((unsigned)(h->rq_count * L.quads)), dim3(256), 0, s, L,
-                     h->mask, h->codes, h->rq_count, h->tplane);
+                     h->mask, h->codes, h->rq_count, h->tplane, h->pack_gen);
   return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ struct sbn_packed {
   bool vc;              // the last pack applied the variance correction (host-side state)
   uint32_t* tplane;     // transposed code plane (data-gradient matmul), 2 bits per weight
   int64_t rq_count;     // 128-row groups of the transposed plane
-  bool tplane_valid;    // the transposed plane matches the last pack (host-side state)
+  uint32_t* pack_gen;   // device words: [0] packs of this handle, [1] the pack count the
+                        // transposed plane was built from (graph replays of a pack keep it right)
   uint8_t* cplane;      // compact plane (nonzero masks + sign slots), read by the GEMV
   size_t cplane_bytes;  // its size, the slack included
   size_t compact_row_bytes;  // per-row bytes of the compact export stream
@@ -95,6 +96,7 @@ struct Plan {
   size_t off_mask, off_codes, off_gamma, off_part, off_sync, off_flips, off_vc, off_gamma_vc,
       off_tplane, off_cplane, off_opos, off_oval, off_omask, off_osum, off_kx, off_band;
   int kx_chunks;
+  int gen_index;  // the pack-generation words, in the split-K words' region
   size_t forward_bytes, total_bytes;
 };
 size_t align_up(size_t v, size_t a);

@@ -195,3 +195,67 @@ def test_bwd_dx_row_stride_near_2_22(ld_dx):
     pw.free()
     assert np.all(canary == 7.0)
     _check(dx, dy, codes, gamma)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (3, 8)])
+def test_bwd_dx_after_graph_replayed_packs(n, m):
+    """Whether the transposed plane matches the last pack is tracked on the device: a re-pack
+    replayed from a captured graph (new weights copied into its input between replays) followed
+    by an eager data gradient, and a captured data gradient replayed after eager and replayed
+    packs, all give the data gradient of the weights the handle holds at that moment. Eager work
+    runs between the replays; every result is checked against the oracle."""
+    import torch
+    rng = np.random.default_rng(500 + 10 * n + m)
+    T, N, K = 130, 300, 1040
+    K += (-K) % m
+    ws = [(rng.standard_normal((N, K)) * 0.02).astype(np.float32) for _ in range(6)]
+    dy = inputs.f32_to_bf16_bits((rng.standard_normal((T, N)) * 0.5).astype(np.float32))
+    dyd = gu.to_dev_bf16(dy)
+    wbuf = gu.to_dev_f32(ws[0])
+    pw = binding.PackedWeight(wbuf, n, m)
+    dxbuf = torch.empty((T, K), dtype=torch.float32, device="cuda")
+
+    def check(w, what):
+        codes, _, gamma = pw.export()
+        torch.cuda.synchronize()
+        codes_h, g = codes.cpu().numpy(), np.float32(gamma.cpu().numpy()[0])
+        assert gu.gamma_matches(g, w), f"{what}: gamma"
+        # the oracle's codes at the gamma the kernels used (they differ from the oracle's own
+        # gamma only at an fp32 rounding midpoint of the mean)
+        ref = oracle.ternary_codes(w, oracle.nm_keep_mask(w, n, m), g)
+        assert np.array_equal(codes_h, ref), f"{what}: codes"
+        _check(dxbuf.cpu().numpy(), dy, codes_h, g)
+
+    binding.bitlinear_bwd_dx(dyd, pw, dx=dxbuf)
+    check(ws[0], "eager")
+    g_pack = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_pack):
+        pw.pack(wbuf)
+    for i in (1, 2):
+        wbuf.copy_(gu.to_dev_f32(ws[i]))
+        torch.cuda.synchronize()
+        g_pack.replay()
+        binding.bitlinear_bwd_dx(dyd, pw, dx=dxbuf)
+        check(ws[i], f"replayed pack {i}, eager data gradient")
+    g_bwd = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_bwd):
+        binding.bitlinear_bwd_dx(dyd, pw, dx=dxbuf)
+    wbuf.copy_(gu.to_dev_f32(ws[3]))
+    torch.cuda.synchronize()
+    g_pack.replay()
+    dxbuf.zero_()
+    g_bwd.replay()
+    check(ws[3], "replayed pack, replayed data gradient")
+    dxbuf.zero_()
+    g_bwd.replay()
+    check(ws[3], "replayed data gradient again (plane reused)")
+    pw.pack(gu.to_dev_f32(ws[4]))
+    dxbuf.zero_()
+    g_bwd.replay()
+    check(ws[4], "eager pack, replayed data gradient")
+    wbuf.copy_(gu.to_dev_f32(ws[5]))
+    torch.cuda.synchronize()
+    g_pack.replay()
+    binding.bitlinear_bwd_dx(dyd, pw, dx=dxbuf)
+    check(ws[5], "replayed pack after the eager one, eager data gradient")
+    pw.free()
