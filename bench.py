@@ -961,8 +961,10 @@ def main():
                              cpu_seconds=min(args.cpu_seconds, 5.0))
             sec.append({k: rp[k] for k in ("value", "unit", "ms_per_step", "config", "roofline",
                                            "activation_kernels", "cpu_baseline") if k in rp})
-        for li, pat in ((0, (2, 4)), (1, (8, 16))):
-            sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
+        # both 7B FFN shapes at both patterns of the training-step workload
+        for pat in ((2, 4), (8, 16)):
+            for li in (0, 1):
+                sec.append({"train_step": run_train(gpu, args, li, pat, 5)})
         sec.append({"decode_large_k": run_decode_large(gpu, args)})
         from sparsity_sbn_quantize_amd import inputs
         gpu.block_weights = [gpu.f32(inputs.latent_weights(inputs.W_BLOCK, i))
