@@ -633,9 +633,10 @@ struct BandWs {
 // where 2^e > the previous pack's total sum |w| (so the new total is about 2^50 units) and
 // rounded to an integer, to one of kBandSlots counters. Integer sums do not depend on the order
 // of the additions, so gamma is the same on every run; its rounding error (half a unit per
-// fragment) is below 2^-36 of the total. A fragment above 2^62 / frags units (the total could
-// overflow), or a previous sum of 0 or not finite, sets the overflow flag, and the fix-up kernel
-// then adds the fp64 partials in a fixed order instead.
+// fragment) is below 2^-36 of the total, which the fix-up kernel checks (a total under frags * 2^35
+// units). A fragment above 2^62 / frags units (the total could overflow), or a previous sum of 0 or
+// not finite, sets the overflow flag. In either case the fix-up kernel adds the fp64 partials in a
+// fixed order instead.
 __device__ __forceinline__ double band_scale(float gamma_prev, double count) {
   const double tot = (double)gamma_prev * count;
   if (!(tot > 0.0) || !isfinite(tot)) return 0.0;
@@ -801,21 +802,27 @@ __global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, in
     *reinterpret_cast<uint4*>(&rec[k][4 * q]) = reinterpret_cast<const uint4*>(
         band.seg + (blockIdx.x + (int64_t)k * G) * kBandRecBytes)[q];
   }
-  // gamma: the fixed-point counters, or the fp64 partials if the pass flagged an overflow
-  const bool fixed = band.lim[2] == 0u;
-  if (fixed) {
-    if (wave == 0) {
-      const unsigned long long v = band.slots[16 * lane];
-      // the 64 counters add up below 2^63
-      unsigned long long sum = v;
+  // gamma: the fixed-point counters, or the fp64 partials if the pass flagged an overflow or the
+  // counters' total is below frags * 2^35 units (the weights shrank by more than about 2^(14 -
+  // log2 frags) since the previous pack: the half unit each fragment rounds off would then exceed
+  // 2^-36 of the total)
+  __shared__ bool use_fixed;
+  if (tid == 0) use_fixed = false;
+  __syncthreads();
+  if (band.lim[2] == 0u && wave == 0) {
+    const unsigned long long v = band.slots[16 * lane];
+    // the 64 counters add up below 2^63
+    unsigned long long sum = v;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
-      if (lane == 0) {
-        const double sc = *reinterpret_cast<const double*>(band.lim + 4);  // the pass's scale
-        gsh = count > 0.0 ? (float)(((double)sum / sc) / count) : 0.0f;
-      }
+    for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0 && (double)sum >= (double)frags * 0x1p35) {
+      const double sc = *reinterpret_cast<const double*>(band.lim + 4);  // the pass's scale
+      gsh = count > 0.0 ? (float)(((double)sum / sc) / count) : 0.0f;
+      use_fixed = true;
     }
-  } else {
+  }
+  __syncthreads();
+  if (!use_fixed) {
     double acc = 0.0;
     for (int64_t i0 = 0; i0 < frags; i0 += 16 * 1024) {
       double v[16];
