@@ -11,7 +11,12 @@ operation 2).
 - Re-packs of one handle across scale jumps: x1e6 (outside the single-read re-pack's bracket, and
   its fixed-point gamma sum overflows), x1.001 at that scale (inside the bracket), x1e-6, all-zero
   weights (gamma 0), a re-pack from that zero gamma, and rows of 1e30 mixed with rows of 1e-30.
-  After every pack gamma, the keep mask and the codes must equal the oracle's."""
+  After every pack gamma, the keep mask and the codes must equal the oracle's.
+- The parameter-free LayerNorm ("The BitLinear Layer", operation 1) on rows of large, subnormal,
+  zero, constant and one-hot activations: x_q and a' exactly the oracle's.
+- Structured k:256 outliers ("From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights
+  with Variance Correction", summary) of huge and of subnormal weights: positions and bf16 values
+  exactly the oracle's, the ternary codes and accumulators exact, y within the fp32 bound."""
 
 import numpy as np
 import pytest
@@ -141,4 +146,91 @@ def test_repack_scale_jumps(case):
     p = oracle.pack_nm_ternary(w0, n, m)
     y_ref = oracle.dequantize(oracle.int_matmul(xq, p["codes"]), p["gamma"], a)
     gu.assert_y_close(y.cpu().numpy(), y_ref, "y after the walk")
+    pw.free()
+
+
+def _ln_rows(rng, T, K):
+    """T rows cycling through: large magnitudes (up to 8.5e37, random signs, so that fp32 x - mu
+    stays finite), bf16 subnormals, all zeros, one constant, one nonzero element, Student-t."""
+    rows = []
+    for t in range(T):
+        kind = t % 6
+        sign = np.where(rng.random(K) < 0.5, 0x8000, 0).astype(np.uint16)
+        if kind == 0:
+            row = rng.integers(0x7E00, 0x7E80, K).astype(np.uint16) | sign
+        elif kind == 1:
+            row = rng.integers(1, 0x80, K).astype(np.uint16) | sign
+        elif kind == 2:
+            row = np.zeros(K, np.uint16)
+        elif kind == 3:
+            row = np.full(K, inputs.f32_to_bf16_bits(np.float32([rng.uniform(-50, 50)]))[0],
+                          np.uint16)
+        elif kind == 4:
+            row = np.zeros(K, np.uint16)
+            row[int(rng.integers(0, K))] = 0x4120  # 10.0
+        else:
+            row = inputs.f32_to_bf16_bits(rng.standard_t(4, K).astype(np.float32))
+        rows.append(row)
+    return np.stack(rows).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_extreme_layernorm(case):
+    import torch
+    n, m = PATTERNS[case % len(PATTERNS)]
+    rng = np.random.default_rng(98_000 + case)
+    T = [1, 3, 4, 5, 12, 40][case % 6]
+    K = int(rng.integers(1, 2000 // m + 1)) * m
+    N = int(rng.integers(1, 400))
+    eps = float(rng.choice([1e-5, 1e-6]))
+    x = _ln_rows(rng, T, K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xd = gu.to_dev_bf16(x)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m)
+    y, q, a = binding.bitlinear_bf16(xd, pw, out="f32", ln_eps=eps)
+    acc, _, _ = binding.bitlinear_bf16(xd, pw, out="i32", ln_eps=eps)
+    codes, _, gamma = pw.export()
+    torch.cuda.synchronize()
+    q_ref, a_ref = oracle.layernorm_quantize_act(x, eps)
+    assert np.array_equal(q.cpu().numpy(), q_ref), "x_q after the LayerNorm"
+    assert np.array_equal(a.cpu().numpy(), a_ref), "a' after the LayerNorm"
+    acc_ref = oracle.int_matmul(q_ref, codes.cpu().numpy())
+    assert np.array_equal(acc.cpu().numpy(), acc_ref), "int32 accumulators"
+    gu.assert_y_close(y.cpu().numpy(),
+                      oracle.dequantize(acc_ref, np.float32(gamma.cpu().numpy()[0]), a_ref))
+    pw.free()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_extreme_outliers(case):
+    import torch
+    n, m = [(2, 4), (8, 16), (6, 8), (4, 8)][case % 4]
+    scale = [1e30, 4e-39][case % 2]  # huge weights, or mostly fp32 subnormals
+    rng = np.random.default_rng(99_000 + case)
+    k = int(rng.choice([4, 16]))
+    K = int(rng.integers(1, 7)) * 256
+    N = int(rng.integers(1, 300))
+    T = [1, 5, 40, 3][case % 4]
+    w = (rng.standard_normal((N, K)) * scale).astype(np.float32)
+    x = inputs.f32_to_bf16_bits(rng.standard_t(4, (T, K)).astype(np.float32))
+    q, a = binding.quantize_act(gu.to_dev_bf16(x))
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m, outliers=k)
+    y = binding.bitlinear(q, a, pw, out="f32")
+    acc = binding.bitlinear(q, a, pw, out="i32")
+    codes, _, g = pw.export()
+    pos, val = pw.export_outliers()
+    torch.cuda.synchronize()
+    ref = oracle.pack_with_outliers(w, n, m, k)
+    codes_h = codes.cpu().numpy()
+    assert np.array_equal(codes_h, ref["codes"]), "ternary codes of the remaining weights"
+    assert np.array_equal(pos.cpu().numpy(), ref["opos"]), "outlier positions"
+    assert np.array_equal(val.cpu().numpy().view(np.uint16), ref["oval"]), "bf16 outlier values"
+    qh, ah = q.cpu().numpy(), a.cpu().numpy()
+    f = oracle.forward_with_outliers(qh, ah, codes_h, np.float32(g.cpu().numpy()[0]),
+                                     pos.cpu().numpy(), val.cpu().numpy().view(np.uint16))
+    assert np.array_equal(acc.cpu().numpy(), f["acc"]), "int32 accumulators (ternary part)"
+    # relative fp32 rounding, plus an absolute 2^-150 per operation whose result is subnormal
+    bound = ((K // 256) * k + 8) * (2.0 ** -24 * f["mag"] + 2.0 ** -150)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - f["y"])
+    assert np.all(err <= bound), f"y: max err/bound {np.max(err / bound):.3g}"
     pw.free()
