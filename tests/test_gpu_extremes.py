@@ -11,7 +11,10 @@ operation 2).
 - Re-packs of one handle across scale jumps: x1e6 (outside the single-read re-pack's bracket, and
   its fixed-point gamma sum overflows), x1.001 at that scale (inside the bracket), x1e-6, all-zero
   weights (gamma 0), a re-pack from that zero gamma, and rows of 1e30 mixed with rows of 1e-30.
-  After every pack gamma, the keep mask and the codes must equal the oracle's.
+  After every pack gamma, the keep mask and the codes must equal the oracle's. Also walks whose
+  previous gamma is subnormal (the single-read pass's bracket in the subnormal range), and the
+  jumps with variance correction, the compact plane or k:256 outliers on, where gamma_out, the
+  compact bytes, the outlier positions and values and the mask flip count are checked as well.
 - The parameter-free LayerNorm ("The BitLinear Layer", operation 1) on rows of large, subnormal,
   zero, constant and one-hot activations: x_q and a' exactly the oracle's.
 - Structured k:256 outliers ("From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights
@@ -233,4 +236,102 @@ def test_extreme_outliers(case):
     bound = ((K // 256) * k + 8) * (2.0 ** -24 * f["mag"] + 2.0 ** -150)
     err = np.abs(y.cpu().numpy().astype(np.float64) - f["y"])
     assert np.all(err <= bound), f"y: max err/bound {np.max(err / bound):.3g}"
+    pw.free()
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_repack_subnormal_walk(case):
+    """Re-packs whose previous gamma is subnormal: the single-read pass brackets a subnormal
+    gamma / 2, and its fixed-point scale comes from a total near 1e-33."""
+    n, m = PATTERNS[case % len(PATTERNS)]
+    rng = np.random.default_rng(97_500 + case)
+    N = int(rng.integers(1, 600))
+    K = int(rng.integers(1, 3000 // m + 1)) * m
+    w0 = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    sub = (w0 * np.float32(3e-37)).astype(np.float32)  # mostly below 2^-126; gamma too
+    ulps = rng.integers(-3, 4, (N, K)).astype(np.float32) * TINY
+    flip = ulps.copy()
+    idx = rng.choice(N * K, size=max(1, N * K // 50), replace=False)
+    flip.flat[idx] = -flip.flat[idx]
+    steps = [("to subnormal", sub),
+             ("subnormal x1.001", (sub * np.float32(1.001)).astype(np.float32)),
+             ("subnormal + noise", (sub + np.float32(1e-40) * rng.standard_normal((N, K)))
+              .astype(np.float32)),
+             ("multiples of 2^-149", ulps),
+             ("signs flipped", flip),
+             ("back", w0)]
+    pw = binding.PackedWeight(gu.to_dev_f32(w0), n, m)
+    _check(pw, w0, n, m, "first pack")
+    for what, w in steps:
+        pw.pack(gu.to_dev_f32(w))
+        _check(pw, w, n, m, what)
+    pw.free()
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_repack_options_scale_jumps(case):
+    """The same scale jumps with a pack option on: variance correction (the exported scale is
+    gamma_out, the codes use gamma), the compact plane (its bytes), or k:256 outliers (positions,
+    values and the codes of the other weights). The mask flip count of every pack is checked too."""
+    import torch
+    option = ["vc", "compact", "outliers"][case % 3]
+    n, m = [(2, 4), (8, 16), (6, 8), (4, 8)][case % 4]
+    rng = np.random.default_rng(97_800 + case)
+    N = int(rng.integers(1, 400))
+    K = int(rng.integers(1, 9)) * 256
+    k = int(rng.choice([4, 8, 16]))
+    w0 = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    mixed = w0 * np.where(rng.random((N, 1)) < 0.3, np.float32(1e30), np.float32(1e-30))
+    steps = [("first pack", w0),
+             ("x1e6", w0 * np.float32(1e6)),
+             ("x1e6 then x1.001", w0 * np.float32(1e6) * np.float32(1.001)),
+             ("x1e-6", w0 * np.float32(1e-6)),
+             ("zeros", np.zeros_like(w0)),
+             ("back from zero gamma", w0),
+             ("subnormal", (w0 * np.float32(3e-37)).astype(np.float32)),
+             ("rows of 1e30 and 1e-30", mixed.astype(np.float32)),
+             ("back", w0)]
+    kw = {"vc": dict(variance_correction=True), "compact": dict(compact=True),
+          "outliers": dict(outliers=k)}[option]
+    pw = None
+    keep_prev = None
+    for what, w in steps:
+        if pw is None:
+            pw = binding.PackedWeight(gu.to_dev_f32(w), n, m, **kw)
+        else:
+            pw.pack(gu.to_dev_f32(w))
+        codes_d, keep_d, gamma_d = pw.export()
+        flips = pw.mask_flips()
+        extra = pw.export_compact() if option == "compact" else (
+            pw.export_outliers() if option == "outliers" else None)
+        torch.cuda.synchronize()
+        g = np.float32(gamma_d.cpu().numpy()[0])
+        keep = keep_d.cpu().numpy().astype(bool)
+        codes = codes_d.cpu().numpy()
+        if option == "outliers":
+            ref = oracle.pack_with_outliers(w, n, m, k)
+            assert gu.gamma_matches(g, ref["w_rest"]), f"{what}: gamma {g} vs {ref['gamma']}"
+            assert np.array_equal(keep, ref["keep"]), f"{what}: keep mask"
+            assert np.array_equal(codes, oracle.ternary_codes(ref["w_rest"], ref["keep"], g)), \
+                f"{what}: codes"
+            pos, val = extra
+            assert np.array_equal(pos.cpu().numpy(), ref["opos"]), f"{what}: outlier positions"
+            assert np.array_equal(val.cpu().numpy().view(np.uint16), ref["oval"]), \
+                f"{what}: outlier values"
+        else:
+            keep_ref = oracle.nm_keep_mask(w, n, m)
+            assert np.array_equal(keep, keep_ref), f"{what}: keep mask"
+            if option == "vc":
+                ref = oracle.variance_correction(w, n, m)
+                assert g == ref["gamma_out"], f"{what}: gamma_out {g} vs {ref['gamma_out']}"
+                assert np.array_equal(codes, oracle.ternary_codes(w, keep_ref, ref["gamma"])), \
+                    f"{what}: codes"
+            else:
+                assert gu.gamma_matches(g, w), f"{what}: gamma {g} vs {oracle.absmean_gamma(w)}"
+                assert np.array_equal(codes, oracle.ternary_codes(w, keep_ref, g)), f"{what}: codes"
+                assert np.array_equal(extra.cpu().numpy(), oracle.compact_pack(codes, n, m)), \
+                    f"{what}: compact bytes"
+        assert int(flips.cpu().numpy()[0]) == oracle.mask_flips(keep_prev, keep), \
+            f"{what}: mask flips"
+        keep_prev = keep
     pw.free()
