@@ -2,8 +2,9 @@
 weights and the forward, with the packed planes in the library's fixed device workspace. Its
 outputs must equal those of sbn_pack_nm_ternary followed by sbn_bitlinear_fwd bit for bit (int32
 accumulators and fp32 outputs), on calls in a row whose later inputs are smaller (the workspace
-keeps the earlier call's contents), through the GEMV, the GEMM and the split-K GEMM, and inside a
-captured graph replayed several times. Sizes beyond the workspace are rejected on the host."""
+keeps the earlier call's contents) or whose weights differ in scale by up to 1e69 (each call packs
+afresh), through the GEMV, the GEMM and the split-K GEMM, and inside a captured graph replayed
+several times. Sizes beyond the workspace are rejected on the host."""
 
 import ctypes
 
@@ -65,6 +66,34 @@ def test_static_equals_handle_path_on_calls_in_a_row():
             pw, yh = _handle_path(wd, n, m, q, a, kind)
             torch.cuda.synchronize()
             assert np.array_equal(ys.cpu().numpy(), yh.cpu().numpy()), (i, kind)
+            pw.free()
+
+
+@pytest.mark.gpu
+def test_static_calls_across_weight_scales():
+    """Calls in a row on weights of very different scales (1e30, 0.02, mostly fp32 subnormals, all
+    zero, 0.02 again): each call packs afresh from its own weights, so every call equals the
+    handle path bit for bit, and the handle's gamma, keep mask and codes equal the oracle's."""
+    import torch
+    import oracle
+    T, K, N, n, m = 40, 1024, 300, 6, 8
+    for i, scale in enumerate([1e30, 0.02, 4e-39, 0.0, 0.02]):
+        x, w = _case(60 + i, T, K, N)
+        w = (w * np.float32(scale / 0.02)).astype(np.float32)
+        xd, wd = gu.to_dev_bf16(x), gu.to_dev_f32(w)
+        q, a = binding.quantize_act(xd)
+        print(f"[static] scale {scale:g}", flush=True)
+        for kind in ("i32", "f32"):
+            ys = binding.bitlinear_latent_static(wd, n, m, q, a, out=kind)
+            pw, yh = _handle_path(wd, n, m, q, a, kind)
+            codes, keep, gamma = pw.export()
+            torch.cuda.synchronize()
+            assert np.array_equal(ys.cpu().numpy(), yh.cpu().numpy()), (scale, kind)
+            g = np.float32(gamma.cpu().numpy()[0])
+            assert gu.gamma_matches(g, w), (scale, g, oracle.absmean_gamma(w))
+            keep_ref = oracle.nm_keep_mask(w, n, m)
+            assert np.array_equal(keep.cpu().numpy().astype(bool), keep_ref), scale
+            assert np.array_equal(codes.cpu().numpy(), oracle.ternary_codes(w, keep_ref, g)), scale
             pw.free()
 
 
