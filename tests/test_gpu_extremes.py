@@ -19,7 +19,10 @@ operation 2).
   zero, constant and one-hot activations: x_q and a' exactly the oracle's.
 - Structured k:256 outliers ("From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights
   with Variance Correction", summary) of huge and of subnormal weights: positions and bf16 values
-  exactly the oracle's, the ternary codes and accumulators exact, y within the fp32 bound."""
+  exactly the oracle's, the ternary codes and accumulators exact, y within the fp32 bound.
+- The straight-through data gradient with gamma near 1e30, or dY near 1e34, within the fp32
+  summation bound; grouped forwards whose members range from 1e30 to subnormal and all-zero
+  weights, each member equal to its own forward."""
 
 import numpy as np
 import pytest
@@ -335,3 +338,69 @@ def test_repack_options_scale_jumps(case):
             f"{what}: mask flips"
         keep_prev = keep
     pw.free()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_extreme_bwd_dx(case):
+    """The straight-through data gradient dX = gamma dY codes with huge weights (gamma near 1e30)
+    or with dY rows near 1e34 (small enough that no fp32 partial sum overflows), against the
+    oracle within the fp32 summation bound."""
+    import torch
+    n, m = [(2, 4), (8, 16), (6, 8), (4, 8)][case % 4]
+    rng = np.random.default_rng(99_500 + case)
+    T = int(rng.integers(1, 300))
+    N = int(rng.integers(1, 500))
+    K = int(rng.integers(1, 2000 // m + 1)) * m
+    if case % 2 == 0:
+        w = (rng.standard_normal((N, K)) * 1e30).astype(np.float32)
+        dy32 = rng.standard_normal((T, N)).astype(np.float32)
+    else:
+        w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        dy32 = (rng.standard_normal((T, N)) * 1e34 / max(N, 1)).astype(np.float32)
+        dy32[::3] *= np.float32(1e-30)  # and rows near 1e4 / N
+    dy = inputs.f32_to_bf16_bits(dy32)
+    pw = binding.PackedWeight(gu.to_dev_f32(w), n, m)
+    dx = binding.bitlinear_bwd_dx(gu.to_dev_bf16(dy), pw)
+    codes, _, gamma = pw.export()
+    torch.cuda.synchronize()
+    codes, gamma, got = codes.cpu().numpy(), np.float32(gamma.cpu().numpy()[0]), dx.cpu().numpy()
+    pw.free()
+    ref = oracle.ste_dx(dy, codes, gamma).astype(np.float64)
+    bound = (N + 2) * 2.0 ** -24 * oracle.ste_dx_abs(dy, codes, gamma) + 2.0 ** -149
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(np.isfinite(got)), "non-finite dX"
+    assert np.all(err <= bound), f"max err/bound {np.max(err / bound):.3g}"
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_extreme_group_members(case):
+    """A grouped forward whose members' weights differ in scale (1e30, 0.02, mostly subnormal, all
+    zero): every member equals its own forward bit for bit, and its accumulators the oracle's."""
+    import torch
+    n, m = [(2, 4), (8, 16), (6, 8)][case % 3]
+    rng = np.random.default_rng(99_700 + case)
+    T = [1, 3, 12, 40, 200, 2][case]
+    K = int(rng.integers(1, 2000 // m + 1)) * m
+    scales = [1e30, 0.02, 4e-39, 0.0]
+    ws = [(rng.standard_normal((int(rng.integers(1, 600)), K)) * s).astype(np.float32)
+          for s in scales]
+    x = inputs.f32_to_bf16_bits(rng.standard_t(4, (T, K)).astype(np.float32))
+    xd = gu.to_dev_bf16(x)
+    pws = [binding.PackedWeight(gu.to_dev_f32(w), n, m) for w in ws]
+    ys_b, q, a = binding.bitlinear_group_bf16(xd, pws, out="f32")
+    acc_g = binding.bitlinear_group(q, a, pws, out="i32")
+    torch.cuda.synchronize()
+    qh = q.cpu().numpy()
+    for s, w, pw, yb, ag in zip(scales, ws, pws, ys_b, acc_g):
+        ys = binding.bitlinear(q, a, pw, out="f32")
+        codes, keep, gamma = pw.export()
+        torch.cuda.synchronize()
+        g = np.float32(gamma.cpu().numpy()[0])
+        assert gu.gamma_matches(g, w), (s, g)
+        keep_ref = oracle.nm_keep_mask(w, n, m)
+        assert np.array_equal(keep.cpu().numpy().astype(bool), keep_ref), s
+        assert np.array_equal(codes.cpu().numpy(), oracle.ternary_codes(w, keep_ref, g)), s
+        assert np.array_equal(yb.cpu().numpy(), ys.cpu().numpy()), f"grouped y vs single, {s}"
+        assert np.array_equal(ag.cpu().numpy(), oracle.int_matmul(qh, codes.cpu().numpy())), s
+    for pw in pws:
+        pw.free()
