@@ -404,3 +404,38 @@ def test_extreme_group_members(case):
         assert np.array_equal(ag.cpu().numpy(), oracle.int_matmul(qh, codes.cpu().numpy())), s
     for pw in pws:
         pw.free()
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (8, 16), (6, 8)])
+def test_graph_replayed_repack_scale_jumps(n, m):
+    """A re-pack captured once in a graph and replayed across the scale jumps (new weights copied
+    into its input between replays, eager forwards in between): whether the fixed-point gamma sum
+    is used or the fp64 partials is decided on the device, so every replay gives the oracle's gamma,
+    keep mask and codes, and a forward after it matches the oracle."""
+    import torch
+    rng = np.random.default_rng(99_900 + 10 * n + m)
+    N, K = 333, 1536
+    w0 = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    steps = [w0 * np.float32(1e6), w0 * np.float32(1e6) * np.float32(1.001),
+             w0 * np.float32(1e-6), np.zeros_like(w0), w0, w0 * np.float32(3e-37),
+             w0 * np.float32(1.002), w0]
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((5, K)).astype(np.float32))
+    xd = gu.to_dev_bf16(x)
+    xq, a = oracle.quantize_act(x)
+    wbuf = gu.to_dev_f32(w0)
+    pw = binding.PackedWeight(wbuf, n, m)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pw.pack(wbuf)
+    for i, w in enumerate(steps):
+        w = np.asarray(w, np.float32)
+        wbuf.copy_(gu.to_dev_f32(w))
+        torch.cuda.synchronize()
+        graph.replay()
+        _check(pw, w, n, m, f"replay {i}")
+        y, _, _ = binding.bitlinear_bf16(xd, pw)
+        acc = oracle.int_matmul(xq, oracle.ternary_codes(w, oracle.nm_keep_mask(w, n, m),
+                                                          oracle.absmean_gamma(w)))
+        y_ref = oracle.dequantize(acc, oracle.absmean_gamma(w), a)
+        gu.assert_y_close(y.cpu().numpy(), y_ref, f"y after replay {i}")
+    pw.free()
