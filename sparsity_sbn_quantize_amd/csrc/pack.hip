@@ -633,10 +633,10 @@ struct BandWs {
 // where 2^e > the previous pack's total sum |w| (so the new total is about 2^50 units) and
 // rounded to an integer, to one of kBandSlots counters. Integer sums do not depend on the order
 // of the additions, so gamma is the same on every run; its rounding error (half a unit per
-// fragment) is below 2^-36 of the total, which the fix-up kernel checks (a total under frags * 2^35
-// units). A fragment above 2^62 / frags units (the total could overflow), or a previous sum of 0 or
-// not finite, sets the overflow flag. In either case the fix-up kernel adds the fp64 partials in a
-// fixed order instead.
+// fragment) is below 2^-33 of the total (1.2e-10), which the fix-up kernel checks (a total under
+// frags * 2^32 units). A fragment above 2^62 / frags units (the total could overflow), or a previous
+// sum of 0 or not finite, sets the overflow flag. In either case the fix-up kernel adds the fp64
+// partials in a fixed order instead.
 __device__ __forceinline__ double band_scale(float gamma_prev, double count) {
   const double tot = (double)gamma_prev * count;
   if (!(tot > 0.0) || !isfinite(tot)) return 0.0;
@@ -803,9 +803,9 @@ __global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, in
         band.seg + (blockIdx.x + (int64_t)k * G) * kBandRecBytes)[q];
   }
   // gamma: the fixed-point counters, or the fp64 partials if the pass flagged an overflow or the
-  // counters' total is below frags * 2^35 units (the weights shrank by more than about 2^(14 -
+  // counters' total is below frags * 2^32 units (the weights shrank by more than about 2^(17 -
   // log2 frags) since the previous pack: the half unit each fragment rounds off would then exceed
-  // 2^-36 of the total)
+  // 2^-33 of the total)
   __shared__ bool use_fixed;
   if (tid == 0) use_fixed = false;
   __syncthreads();
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(1024) void pack_fix(const float* __restrict__ w, in
     unsigned long long sum = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (lane == 0 && (double)sum >= (double)frags * 0x1p35) {
+    if (lane == 0 && (double)sum >= (double)frags * 0x1p32) {
       const double sc = *reinterpret_cast<const double*>(band.lim + 4);  // the pass's scale
       gsh = count > 0.0 ? (float)(((double)sum / sc) / count) : 0.0f;
       use_fixed = true;

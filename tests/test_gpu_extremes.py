@@ -439,3 +439,30 @@ def test_graph_replayed_repack_scale_jumps(n, m):
         y_ref = oracle.dequantize(acc, oracle.absmean_gamma(w), a)
         gu.assert_y_close(y.cpu().numpy(), y_ref, f"y after replay {i}")
     pw.free()
+
+
+def test_repack_near_the_fixed_point_threshold():
+    """8192 fragments (4096 x 8192 weights, 2:4): re-packs after the weights shrink by 10x (the
+    fixed-point sum stays in use, at about 2^45.7 units against the 2^45 floor), 20x (either side
+    of the floor) and 50x (the fp64 partials), then grow back. Every gamma matches the oracle's;
+    keep mask and codes of sampled rows too."""
+    import torch
+    n, m, N, K = 2, 4, 4096, 8192
+    rng = np.random.default_rng(99_990)
+    w0 = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    rows = np.sort(rng.choice(N, size=48, replace=False))
+    wbuf = gu.to_dev_f32(w0)
+    pw = binding.PackedWeight(wbuf, n, m)
+    for f in (0.1, 0.05, 0.02, 1.0, 0.999):
+        w = (w0 * np.float32(f)).astype(np.float32)
+        wbuf.copy_(torch.from_numpy(w))
+        pw.pack(wbuf)
+        codes_d, keep_d, gamma_d = pw.export()
+        torch.cuda.synchronize()
+        g = np.float32(gamma_d.cpu().numpy()[0])
+        assert gu.gamma_matches(g, w), f"x{f}: gamma {g} vs {oracle.absmean_gamma(w)}"
+        keep_ref = oracle.nm_keep_mask(w[rows], n, m)
+        assert np.array_equal(keep_d.cpu().numpy()[rows].astype(bool), keep_ref), f"x{f}: keep"
+        assert np.array_equal(codes_d.cpu().numpy()[rows],
+                              oracle.ternary_codes(w[rows], keep_ref, g)), f"x{f}: codes"
+    pw.free()
