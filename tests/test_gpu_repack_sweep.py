@@ -10,7 +10,8 @@ permuted along K (the masks move, gamma stays). After every pack
 gamma, the keep mask and the codes must equal the oracle's for the current weights (codes at the
 gamma the kernels used, which equals the oracle's except at an fp32 rounding midpoint of the mean);
 at the end a forward on the handle must match the oracle. Mostly the lean patterns (single-read
-re-pack), also patterns outside that set and 2:4 on both MFMA forms."""
+re-pack), also patterns outside that set and 2:4 on both MFMA forms. Also walks on padded rows
+(NaN canaries past K) and on a base address 4 bytes off 16 (element-wise loads)."""
 
 import numpy as np
 import pytest
@@ -91,4 +92,35 @@ def test_random_repack_walk(case, monkeypatch):
     p = oracle.pack_nm_ternary(w, n, m)
     y_ref = oracle.dequantize(oracle.int_matmul(xq, p["codes"]), p["gamma"], a)
     gu.assert_y_close(y.cpu().numpy(), y_ref, "y after the walk")
+    pw.free()
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_repack_walk_padded(case):
+    """The same walks on weights whose rows are padded (NaN canaries past K: a read beyond the row
+    would make gamma NaN) or whose base address is 4 bytes off 16: the single-read pass and its
+    fix-up on element-wise loads, and on 16-byte loads over padded rows."""
+    import torch
+    n, m, _ = PATTERNS[case % len(PATTERNS)]
+    rng = np.random.default_rng(71_000 + case)
+    N = int(rng.integers(1, 500))
+    K = int(rng.integers(1, 2500 // m + 1)) * m
+    layout = ["pad1", "pad4", "offset"][case % 3]
+
+    def dev(w):
+        if layout == "pad1":
+            return gu.to_dev_f32(w, ld=K + 1)
+        if layout == "pad4":
+            return gu.to_dev_f32(w, ld=K + 4)
+        flat = torch.full((N * K + 1,), float("nan"), dtype=torch.float32, device="cuda")
+        flat[1:].copy_(torch.from_numpy(np.ascontiguousarray(w)).reshape(-1))
+        return flat[1:].view(N, K)
+
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    pw = binding.PackedWeight(dev(w), n, m)
+    _check(pw, w, n, m, f"{layout}: first pack")
+    for step in range(6):
+        w, what = _update(rng, w, m)
+        pw.pack(dev(w))
+        _check(pw, w, n, m, f"{layout} step {step}: {what}")
     pw.free()
